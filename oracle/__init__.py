@@ -1,0 +1,169 @@
+"""fp64 CPU oracle of the differential-attention forward pass (ctypes binding).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the
+benchmark's CPU-baseline leg are the only users.  The product path (the
+``differential_attention_amd`` package and its HIP library) never imports
+this package, and this package never imports that one; the only module both
+sides share is the seeded input generator ``workloads``.
+
+The arithmetic lives in ``diffattn_ref.c`` (plain C, IEEE double, OpenMP over
+output rows); see its header for the formula and the pages it follows.
+``build()`` compiles it with gcc into ``libdiffattn_ref.so`` beside it.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "diffattn_ref.c")
+LIBRARY = os.path.join(_HERE, "libdiffattn_ref.so")
+
+
+def build(source: str = SOURCE, output: str = LIBRARY, extra=()) -> str:
+    """Compile the oracle with gcc (IEEE semantics: no fast-math)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+           "-Wall", "-Werror", *extra, source, "-o", output + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(output + ".tmp", output)
+    return output
+
+
+_lib_cache = {}
+
+
+def load(path: str = LIBRARY) -> ctypes.CDLL:
+    """Load (building first if absent) the oracle library at ``path``."""
+    if path in _lib_cache:
+        return _lib_cache[path]
+    if path == LIBRARY and not os.path.exists(path):
+        build()
+    lib = ctypes.CDLL(path)
+    f32p = ctypes.POINTER(ctypes.c_float)
+    f64p = ctypes.POINTER(ctypes.c_double)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    lib.diffattn_ref_lambda_init.argtypes = [ctypes.c_int]
+    lib.diffattn_ref_lambda_init.restype = ctypes.c_double
+    lib.diffattn_ref_lambda.argtypes = [f32p, f32p, f32p, f32p, ctypes.c_int,
+                                        ctypes.c_double]
+    lib.diffattn_ref_lambda.restype = ctypes.c_double
+    common = [f32p, f32p, f32p, f32p, f32p, f32p, f32p, ctypes.c_double, f32p,
+              ctypes.c_double, ctypes.c_int, i32p, ctypes.c_int, ctypes.c_int64,
+              ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.diffattn_ref_fwd.argtypes = common + [f64p, ctypes.c_int]
+    lib.diffattn_ref_fwd.restype = ctypes.c_int
+    lib.diffattn_ref_rows.argtypes = common + [i64p, i32p, ctypes.c_int64, f64p,
+                                               ctypes.c_int]
+    lib.diffattn_ref_rows.restype = ctypes.c_int
+    lib.diffattn_ref_max_threads.argtypes = []
+    lib.diffattn_ref_max_threads.restype = ctypes.c_int
+    _lib_cache[path] = lib
+    return lib
+
+
+def _f32(x) -> np.ndarray:
+    """Any array-like (numpy, torch CPU tensor of fp32 or bf16) as a
+    contiguous fp32 numpy array; bf16 -> fp32 is exact."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().to("cpu", torch.float32).contiguous().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+
+
+def _ptr(a: np.ndarray, ct):
+    return a.ctypes.data_as(ctypes.POINTER(ct))
+
+
+def lambda_init(depth: int, lib: Optional[ctypes.CDLL] = None) -> float:
+    return (lib or load()).diffattn_ref_lambda_init(int(depth))
+
+
+def lam(lq1, lk1, lq2, lk2, lambda_init_value: float,
+        lib: Optional[ctypes.CDLL] = None) -> float:
+    a = [_f32(x).reshape(-1) for x in (lq1, lk1, lq2, lk2)]
+    d = a[0].size
+    assert all(x.size == d for x in a)
+    return (lib or load()).diffattn_ref_lambda(
+        *[_ptr(x, ctypes.c_float) for x in a], d, float(lambda_init_value))
+
+
+def _common(q, k, v, lq1, lk1, lq2, lk2, lambda_init_value, w, eps, causal,
+            cu_seqlens):
+    qa, ka, va = _f32(q), _f32(k), _f32(v)
+    T, H, two, d = qa.shape
+    assert two == 2
+    Hkv = ka.shape[1]
+    assert ka.shape == (T, Hkv, 2, d) and va.shape == (T, Hkv, 2 * d)
+    lv = [_f32(x).reshape(-1) for x in (lq1, lk1, lq2, lk2)]
+    assert all(x.size == d for x in lv)
+    wa = None if w is None else _f32(w).reshape(-1)
+    if wa is not None:
+        assert wa.size == 2 * d
+    if cu_seqlens is None:
+        cu = np.array([0, T], dtype=np.int32)
+    else:
+        try:
+            import torch
+            if isinstance(cu_seqlens, torch.Tensor):
+                cu_seqlens = cu_seqlens.cpu().numpy()
+        except ImportError:  # pragma: no cover
+            pass
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+    keep = (qa, ka, va, lv, wa, cu)
+    args = [_ptr(qa, ctypes.c_float), _ptr(ka, ctypes.c_float),
+            _ptr(va, ctypes.c_float)] + [_ptr(x, ctypes.c_float) for x in lv]
+    args += [float(lambda_init_value),
+             None if wa is None else _ptr(wa, ctypes.c_float),
+             float(eps), int(bool(causal)), _ptr(cu, ctypes.c_int32),
+             int(cu.size - 1), int(T), int(H), int(Hkv), int(d)]
+    return keep, args, (T, H, d)
+
+
+def fwd(q, k, v, lq1, lk1, lq2, lk2, lambda_init_value: float, w=None,
+        eps: float = 1e-5, causal: bool = True, cu_seqlens=None,
+        nthreads: int = 0, lib: Optional[ctypes.CDLL] = None) -> np.ndarray:
+    """Whole output ``[T, H, 2d]`` in fp64.  Layouts as in ``workloads``."""
+    keep, args, (T, H, d) = _common(q, k, v, lq1, lk1, lq2, lk2,
+                                    lambda_init_value, w, eps, causal,
+                                    cu_seqlens)
+    out = np.empty((T, H, 2 * d), dtype=np.float64)
+    rc = (lib or load()).diffattn_ref_fwd(*args, _ptr(out, ctypes.c_double),
+                                          int(nthreads))
+    del keep
+    if rc != 0:
+        raise ValueError(f"diffattn_ref_fwd failed with status {rc}")
+    return out
+
+
+def rows(q, k, v, lq1, lk1, lq2, lk2, lambda_init_value: float,
+         tokens: Sequence[int], heads: Sequence[int], w=None, eps: float = 1e-5,
+         causal: bool = True, cu_seqlens=None, nthreads: int = 0,
+         lib: Optional[ctypes.CDLL] = None) -> np.ndarray:
+    """Output rows ``[len(tokens), 2d]`` in fp64 for (token, head) pairs."""
+    keep, args, (T, H, d) = _common(q, k, v, lq1, lk1, lq2, lk2,
+                                    lambda_init_value, w, eps, causal,
+                                    cu_seqlens)
+    tok = np.ascontiguousarray(np.asarray(tokens, dtype=np.int64))
+    hd = np.ascontiguousarray(np.asarray(heads, dtype=np.int32))
+    assert tok.shape == hd.shape and tok.ndim == 1
+    out = np.empty((tok.size, 2 * d), dtype=np.float64)
+    rc = (lib or load()).diffattn_ref_rows(
+        *args, _ptr(tok, ctypes.c_int64), _ptr(hd, ctypes.c_int32),
+        int(tok.size), _ptr(out, ctypes.c_double), int(nthreads))
+    del keep
+    if rc != 0:
+        raise ValueError(f"diffattn_ref_rows failed with status {rc}")
+    return out
+
+
+def max_threads(lib: Optional[ctypes.CDLL] = None) -> int:
+    return (lib or load()).diffattn_ref_max_threads()

@@ -1,0 +1,259 @@
+/*
+ * diffattn_ref.c -- fp64 CPU oracle of the differential-attention forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link,
+ * load or call this file or the library built from it.  Only the test suite,
+ * the smoke check and the benchmark's CPU-baseline leg use it.  It shares no
+ * code, header or constant with the HIP library.
+ *
+ * What it computes (sources: the DiffTransformer.py page of
+ * Differential-Transformer-PyTorch, MultiHeadDifferentialAttention.forward and
+ * RMSNorm.forward; the LlamaDiffSdpaAttention.py gist, forward; the unilm pull
+ * request "Add an isolated implementation of FlashDiffAttention",
+ * alternative_forward):
+ *
+ *   lambda  = exp(sum_c lq1[c]*lk1[c]) - exp(sum_c lq2[c]*lk2[c]) + lambda_init
+ *   for every packed sequence s (tokens a .. a+n-1), head h, row i:
+ *     g      = h / (H / Hkv)                  (GQA: contiguous head groups)
+ *     map m in {1,2}: x_j = <Qm[a+i,h], Km[a+j,g]> / sqrt(d), j in J(i)
+ *                     J(i) = {0..i} when causal, else {0..n-1}
+ *                     A_m  = softmax_j(x_j)
+ *     pre    = sum_j (A_1[j] - lambda * A_2[j]) * V[a+j, g, :]     (2d wide)
+ *     out    = pre / sqrt(mean_c pre[c]^2 + eps) * w * (1 - lambda_init)
+ *
+ * Each softmax is taken the plain two-pass way (maximum, then exponentials
+ * and their sum), every operation in IEEE double.  Inputs arrive as fp32
+ * arrays: every bf16 or fp32 input value is exactly representable there, and
+ * each is widened to double before use.
+ *
+ * Parity of every function here is pinned by the CPU tests against an mpmath
+ * brute force of the materialised form, torch's scaled_dot_product_attention
+ * and rms_norm on special inputs, and closed forms (row 0, uniform attention,
+ * identical maps, lambda = 0).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* The decaying initial value of lambda for a layer at 1-based depth, as the
+ * DiffTransformer model builds its layers (DiffTransformer.__init__). */
+double diffattn_ref_lambda_init(int depth)
+{
+    return 0.8 - 0.6 * exp(-0.3 * (double)(depth - 1));
+}
+
+/* The re-parameterised lambda (MultiHeadDifferentialAttention.forward):
+ * one scalar shared by every head, as in the Llama gist and the pull
+ * request's alternative_forward, where the four vectors have length d. */
+double diffattn_ref_lambda(const float *lq1, const float *lk1,
+                           const float *lq2, const float *lk2, int d,
+                           double lambda_init)
+{
+    double dot1 = 0.0, dot2 = 0.0;
+    for (int c = 0; c < d; ++c) {
+        dot1 += (double)lq1[c] * (double)lk1[c];
+        dot2 += (double)lq2[c] * (double)lk2[c];
+    }
+    return exp(dot1) - exp(dot2) + lambda_init;
+}
+
+/* Softmax of one attention map over the keys j in [0, nkeys) of the sequence
+ * starting at token a, for query token a+i of head h: writes the
+ * probabilities into p[0..nkeys). */
+static void softmax_map(const float *q, const float *k, int64_t a, int64_t i,
+                        int64_t nkeys, int h, int g, int map, int H, int Hkv,
+                        int d, double *p)
+{
+    const float *qrow = q + (((a + i) * H + h) * 2 + map) * (int64_t)d;
+    const double scale = 1.0 / sqrt((double)d);
+    double mx = -INFINITY;
+    for (int64_t j = 0; j < nkeys; ++j) {
+        const float *krow = k + (((a + j) * Hkv + g) * 2 + map) * (int64_t)d;
+        double x = 0.0;
+        for (int c = 0; c < d; ++c)
+            x += (double)qrow[c] * (double)krow[c];
+        x *= scale;
+        p[j] = x;
+        if (x > mx)
+            mx = x;
+    }
+    double z = 0.0;
+    for (int64_t j = 0; j < nkeys; ++j) {
+        p[j] = exp(p[j] - mx);
+        z += p[j];
+    }
+    for (int64_t j = 0; j < nkeys; ++j)
+        p[j] /= z;
+}
+
+/* One output row (token a+i, head h) into o[0..2d). p1, p2 and pre are
+ * caller-provided scratch of n, n and 2d doubles. */
+static void diff_row(const float *q, const float *k, const float *v,
+                     double lam, double lambda_init, const float *w, double eps,
+                     int causal, int64_t a, int64_t n, int64_t i, int h, int H,
+                     int Hkv, int d, double *p1, double *p2, double *pre,
+                     double *o)
+{
+    const int g = h / (H / Hkv);
+    const int64_t nkeys = causal ? i + 1 : n;
+    const int dv = 2 * d;
+    softmax_map(q, k, a, i, nkeys, h, g, 0, H, Hkv, d, p1);
+    softmax_map(q, k, a, i, nkeys, h, g, 1, H, Hkv, d, p2);
+    for (int c = 0; c < dv; ++c)
+        pre[c] = 0.0;
+    for (int64_t j = 0; j < nkeys; ++j) {
+        const double coef = p1[j] - lam * p2[j];
+        const float *vrow = v + ((a + j) * Hkv + g) * (int64_t)dv;
+        for (int c = 0; c < dv; ++c)
+            pre[c] += coef * (double)vrow[c];
+    }
+    double ss = 0.0;
+    for (int c = 0; c < dv; ++c)
+        ss += pre[c] * pre[c];
+    const double rms = sqrt(ss / (double)dv + eps);
+    for (int c = 0; c < dv; ++c) {
+        const double wc = w ? (double)w[c] : 1.0;
+        o[c] = pre[c] / rms * wc * (1.0 - lambda_init);
+    }
+}
+
+static int check_args(const int32_t *cu, int nseq, int64_t T, int H, int Hkv,
+                      int d)
+{
+    if (nseq < 0 || T < 0 || H < 1 || Hkv < 1 || d < 1 || H % Hkv != 0)
+        return -1;
+    if (!cu)
+        return -1;
+    if (cu[0] != 0 || cu[nseq] != T)
+        return -1;
+    for (int s = 0; s < nseq; ++s)
+        if (cu[s + 1] < cu[s])
+            return -1;
+    return 0;
+}
+
+static int64_t max_len(const int32_t *cu, int nseq)
+{
+    int64_t m = 0;
+    for (int s = 0; s < nseq; ++s)
+        if (cu[s + 1] - cu[s] > m)
+            m = cu[s + 1] - cu[s];
+    return m;
+}
+
+/* Full forward pass: out[T, H, 2d] in double.  cu_seqlens[nseq+1] holds the
+ * packed sequence boundaries (host).  nthreads <= 0 uses the OpenMP default.
+ * Returns 0, or -1 on malformed arguments, -2 if scratch memory is short. */
+int diffattn_ref_fwd(const float *q, const float *k, const float *v,
+                     const float *lq1, const float *lk1, const float *lq2,
+                     const float *lk2, double lambda_init, const float *w,
+                     double eps, int causal, const int32_t *cu_seqlens,
+                     int nseq, int64_t T, int H, int Hkv, int d, double *out,
+                     int nthreads)
+{
+    if (check_args(cu_seqlens, nseq, T, H, Hkv, d))
+        return -1;
+    const double lam = diffattn_ref_lambda(lq1, lk1, lq2, lk2, d, lambda_init);
+    const int64_t nmax = max_len(cu_seqlens, nseq);
+    const int64_t nrows = T * H;
+    int err = 0;
+#ifdef _OPENMP
+    if (nthreads <= 0)
+        nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads)
+#endif
+    {
+        double *scratch = malloc(sizeof(double) * (size_t)(2 * nmax + 2 * d + 1));
+        if (!scratch) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+            err = -2;
+        }
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 8)
+#endif
+        for (int64_t r = 0; r < nrows; ++r) {
+            if (!scratch)
+                continue;
+            const int64_t t = r / H;
+            const int h = (int)(r % H);
+            int s = 0;
+            while (cu_seqlens[s + 1] <= t)
+                ++s;
+            const int64_t a = cu_seqlens[s];
+            const int64_t n = cu_seqlens[s + 1] - a;
+            diff_row(q, k, v, lam, lambda_init, w, eps, causal, a, n, t - a, h,
+                     H, Hkv, d, scratch, scratch + nmax, scratch + 2 * nmax,
+                     out + r * 2 * (int64_t)d);
+        }
+        free(scratch);
+    }
+    return err;
+}
+
+/* Selected rows only: row r is (token tok[r], head head[r]); writes
+ * out_rows[nrows, 2d].  Used to check full-size runs on a sample. */
+int diffattn_ref_rows(const float *q, const float *k, const float *v,
+                      const float *lq1, const float *lk1, const float *lq2,
+                      const float *lk2, double lambda_init, const float *w,
+                      double eps, int causal, const int32_t *cu_seqlens,
+                      int nseq, int64_t T, int H, int Hkv, int d,
+                      const int64_t *tok, const int32_t *head, int64_t nrows,
+                      double *out_rows, int nthreads)
+{
+    if (check_args(cu_seqlens, nseq, T, H, Hkv, d))
+        return -1;
+    for (int64_t r = 0; r < nrows; ++r)
+        if (tok[r] < 0 || tok[r] >= T || head[r] < 0 || head[r] >= H)
+            return -1;
+    const double lam = diffattn_ref_lambda(lq1, lk1, lq2, lk2, d, lambda_init);
+    const int64_t nmax = max_len(cu_seqlens, nseq);
+    int err = 0;
+#ifdef _OPENMP
+    if (nthreads <= 0)
+        nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads)
+#endif
+    {
+        double *scratch = malloc(sizeof(double) * (size_t)(2 * nmax + 2 * d + 1));
+        if (!scratch) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+            err = -2;
+        }
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+        for (int64_t r = 0; r < nrows; ++r) {
+            if (!scratch)
+                continue;
+            const int64_t t = tok[r];
+            int s = 0;
+            while (cu_seqlens[s + 1] <= t)
+                ++s;
+            const int64_t a = cu_seqlens[s];
+            const int64_t n = cu_seqlens[s + 1] - a;
+            diff_row(q, k, v, lam, lambda_init, w, eps, causal, a, n, t - a,
+                     head[r], H, Hkv, d, scratch, scratch + nmax,
+                     scratch + 2 * nmax, out_rows + r * 2 * (int64_t)d);
+        }
+        free(scratch);
+    }
+    return err;
+}
+
+/* Number of OpenMP threads a parallel region with nthreads <= 0 would use. */
+int diffattn_ref_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

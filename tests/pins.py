@@ -1,0 +1,347 @@
+"""Checks that pin the fp64 oracle to something other than itself.
+
+Each ``pin_*`` function takes a loaded oracle library (``oracle.load(path)``)
+and raises ``AssertionError`` when the oracle disagrees with:
+
+* an mpmath brute force of the materialised form of the DiffTransformer.py
+  page (MultiHeadDifferentialAttention.forward: two full masked score
+  matrices, two softmaxes, their lambda-weighted difference times V, then the
+  per-head RMSNorm and the (1 - lambda_init) scale), at 50 digits on tiny
+  inputs;
+* torch's ``scaled_dot_product_attention`` and ``rms_norm`` in fp64 (library
+  routines), composed the way the LlamaDiffSdpaAttention.py gist composes two
+  SDPA calls (attn1 - lambda * attn2, then subln, then the scale), with the
+  library's own GQA broadcast (``enable_gqa``: head h reads KV head h // G,
+  as ``repeat_kv`` does on that page);
+* closed forms: lambda at special vectors, row 0 of every sequence, uniform
+  attention (K = 0), identical maps with lambda = 1;
+* invariants: causality, packing, GQA = MHA with repeated K/V, odd symmetry
+  in V, the row-sampling entry point.
+
+The same pins run against deliberately broken copies of the oracle source
+(``tests/test_oracle_mutants.py``) to show that each plausible mistake fails
+at least one of them.
+"""
+
+from __future__ import annotations
+
+import math
+
+import mpmath
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+import oracle
+
+
+# --------------------------------------------------------------------------
+# tiny seeded inputs (fp32 values; the oracle widens them exactly)
+
+def tiny_inputs(seed, seqlens, H, Hkv, d, q_scale=1.0, v_scale=1.0):
+    rng = np.random.default_rng(seed)
+    T = int(sum(seqlens))
+    q = (rng.standard_normal((T, H, 2, d)) * q_scale).astype(np.float32)
+    k = rng.standard_normal((T, Hkv, 2, d)).astype(np.float32)
+    v = (rng.standard_normal((T, Hkv, 2 * d)) * v_scale).astype(np.float32)
+    lv = [(0.3 * rng.standard_normal(d)).astype(np.float32) for _ in range(4)]
+    w = (0.5 + rng.random(2 * d)).astype(np.float32)
+    cu = np.zeros(len(seqlens) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(seqlens)
+    return q, k, v, lv, w, cu
+
+
+def run(lib, q, k, v, lv, lam_init, w, eps, causal, cu):
+    return oracle.fwd(q, k, v, *lv, lam_init, w, eps, causal, cu, lib=lib)
+
+
+# --------------------------------------------------------------------------
+# mpmath brute force of the materialised two-map form
+
+def brute_mpmath(q, k, v, lv, lam_init, w, eps, causal, cu, dps=50):
+    mpmath.mp.dps = dps
+    T, H, _, d = q.shape
+    Hkv = k.shape[1]
+    G = H // Hkv
+    mpf = mpmath.mpf
+    lq1, lk1, lq2, lk2 = [[mpf(float(x)) for x in a] for a in lv]
+    lam = (mpmath.exp(mpmath.fsum(a * b for a, b in zip(lq1, lk1)))
+           - mpmath.exp(mpmath.fsum(a * b for a, b in zip(lq2, lk2)))
+           + mpf(lam_init))
+    scaling = 1 / mpmath.sqrt(d)
+    out = np.zeros((T, H, 2 * d))
+    for s in range(len(cu) - 1):
+        a, b = int(cu[s]), int(cu[s + 1])
+        n = b - a
+        for h in range(H):
+            g = h // G
+            A = []
+            for m in range(2):
+                Am = []
+                for i in range(n):
+                    row = []
+                    for j in range(n):
+                        if causal and j > i:
+                            row.append(mpmath.ninf)
+                            continue
+                        x = mpmath.fsum(mpf(float(q[a + i, h, m, c]))
+                                        * mpf(float(k[a + j, g, m, c]))
+                                        for c in range(d))
+                        row.append(x * scaling)
+                    mx = max(x for x in row if x != mpmath.ninf)
+                    e = [mpmath.exp(x - mx) if x != mpmath.ninf else mpf(0)
+                         for x in row]
+                    z = mpmath.fsum(e)
+                    Am.append([x / z for x in e])
+                A.append(Am)
+            for i in range(n):
+                pre = []
+                for c in range(2 * d):
+                    pre.append(mpmath.fsum((A[0][i][j] - lam * A[1][i][j])
+                                           * mpf(float(v[a + j, g, c]))
+                                           for j in range(n)))
+                rms = mpmath.sqrt(mpmath.fsum(x * x for x in pre) / (2 * d)
+                                  + mpf(eps))
+                for c in range(2 * d):
+                    wc = mpf(1) if w is None else mpf(float(w[c]))
+                    out[a + i, h, c] = float(pre[c] / rms * wc * (1 - mpf(lam_init)))
+    return out
+
+
+def pin_brute_force(lib):
+    cases = [
+        # seed, seqlens, H, Hkv, d, causal, q_scale
+        (1, (4, 6), 4, 2, 3, True, 1.0),
+        (2, (5,), 2, 2, 2, False, 1.0),
+        (3, (3, 1, 5), 2, 1, 4, True, 1.0),
+        (4, (6,), 2, 1, 2, True, 800.0),    # scores beyond exp()'s double range
+    ]
+    for seed, seqlens, H, Hkv, d, causal, qs in cases:
+        q, k, v, lv, w, cu = tiny_inputs(seed, seqlens, H, Hkv, d, q_scale=qs)
+        lam_init = 0.8 - 0.6 * math.exp(-0.3 * (seed + 2))
+        got = run(lib, q, k, v, lv, lam_init, w, 1e-5, causal, cu)
+        ref = brute_mpmath(q, k, v, lv, lam_init, w, 1e-5, causal, cu)
+        err = np.max(np.abs(got - ref))
+        assert np.all(np.isfinite(got)), f"non-finite oracle output, case {seed}"
+        assert err < 1e-12, f"brute force case {seed}: max-abs {err:.3e}"
+
+
+# --------------------------------------------------------------------------
+# library routines: torch SDPA + rms_norm in fp64
+
+def sdpa_diff(q, k, v, lam, lam_init, w, eps, causal, cu):
+    """The two-call composition with torch library routines, per sequence."""
+    qt = torch.from_numpy(q).double()
+    kt = torch.from_numpy(k).double()
+    vt = torch.from_numpy(v).double()
+    T, H, _, d = q.shape
+    out = torch.zeros(T, H, 2 * d, dtype=torch.float64)
+    wt = None if w is None else torch.from_numpy(w).double()
+    for s in range(len(cu) - 1):
+        a, b = int(cu[s]), int(cu[s + 1])
+        if b == a:
+            continue
+        # [1, heads, n, width]
+        q1 = qt[a:b, :, 0].permute(1, 0, 2).unsqueeze(0)
+        q2 = qt[a:b, :, 1].permute(1, 0, 2).unsqueeze(0)
+        k1 = kt[a:b, :, 0].permute(1, 0, 2).unsqueeze(0)
+        k2 = kt[a:b, :, 1].permute(1, 0, 2).unsqueeze(0)
+        vv = vt[a:b].permute(1, 0, 2).unsqueeze(0)
+        sc = 1.0 / math.sqrt(d)
+        o1 = F.scaled_dot_product_attention(q1, k1, vv, is_causal=causal,
+                                            scale=sc, enable_gqa=True)
+        o2 = F.scaled_dot_product_attention(q2, k2, vv, is_causal=causal,
+                                            scale=sc, enable_gqa=True)
+        o = o1 - lam * o2
+        o = F.rms_norm(o, (2 * d,), weight=wt, eps=eps) * (1.0 - lam_init)
+        out[a:b] = o[0].permute(1, 0, 2)
+    return out.numpy()
+
+
+def pin_sdpa_lambda_zero(lib):
+    """lambda = 0 (lambda_init = 0, equal vector pairs): plain causal softmax
+    attention of map 1 followed by RMSNorm."""
+    q, k, v, lv, w, cu = tiny_inputs(11, (37, 64, 9), 8, 2, 16)
+    lv = [lv[0], lv[1], lv[0], lv[1]]
+    got = run(lib, q, k, v, lv, 0.0, w, 1e-5, True, cu)
+    q2 = q.copy()
+    q2[:, :, 1] = 0.0  # map 2 is multiplied by lambda = 0
+    ref = sdpa_diff(q2, k, v, 0.0, 0.0, w, 1e-5, True, cu)
+    err = np.max(np.abs(got - ref))
+    assert err < 1e-10, f"lambda=0 vs SDPA: max-abs {err:.3e}"
+
+
+def pin_sdpa_two_maps(lib):
+    for causal in (True, False):
+        for H, Hkv in ((8, 2), (4, 4), (6, 1)):
+            q, k, v, lv, w, cu = tiny_inputs(12 + H, (33, 70), H, Hkv, 16)
+            lam_init = 0.8 - 0.6 * math.exp(-0.3 * 7)
+            lam = (math.exp(float(np.dot(lv[0].astype(np.float64), lv[1])))
+                   - math.exp(float(np.dot(lv[2].astype(np.float64), lv[3])))
+                   + lam_init)
+            got = run(lib, q, k, v, lv, lam_init, w, 1e-5, causal, cu)
+            ref = sdpa_diff(q, k, v, lam, lam_init, w, 1e-5, causal, cu)
+            err = np.max(np.abs(got - ref))
+            assert err < 1e-10, (f"two-map vs SDPA (H={H}, Hkv={Hkv}, "
+                                 f"causal={causal}): max-abs {err:.3e}")
+
+
+# --------------------------------------------------------------------------
+# closed forms
+
+def pin_lambda_closed_forms(lib):
+    assert oracle.lambda_init(1, lib=lib) == 0.8 - 0.6, "lambda_init(1)"
+    assert abs(oracle.lambda_init(1, lib=lib) - 0.2) < 1e-15
+    assert abs(oracle.lambda_init(10 ** 6, lib=lib) - 0.8) < 1e-15
+    # strictly increasing in depth
+    vals = [oracle.lambda_init(l, lib=lib) for l in range(1, 40)]
+    assert all(b > a for a, b in zip(vals, vals[1:]))
+    d = 8
+    z = np.zeros(d, np.float32)
+    e0 = np.zeros(d, np.float32)
+    e0[0] = 1.0
+    e1 = np.zeros(d, np.float32)
+    e1[1] = 1.0
+    # both dot products zero: exp(0) - exp(0) + lambda_init
+    assert oracle.lam(z, z, z, z, 0.3, lib=lib) == 0.3
+    assert oracle.lam(e0, e1, e1, e0, 0.3, lib=lib) == 0.3
+    # first dot product one, second zero: e - 1 + lambda_init
+    got = oracle.lam(e0, e0, z, z, 0.25, lib=lib)
+    assert abs(got - (math.e - 1.0 + 0.25)) < 1e-15, got
+    # second dot product two, first zero: 1 - e^2 + lambda_init
+    two = 2 * e1
+    got = oracle.lam(z, z, two, e1, 0.5, lib=lib)
+    assert abs(got - (1.0 - math.e ** 2 + 0.5)) < 1e-14, got
+
+
+def pin_row0_closed_form(lib):
+    """Causal row 0 of a sequence sees only key 0, so both maps put weight 1
+    on V[a]: pre = (1 - lambda) V[a]."""
+    for v_scale in (1.0, 3e-3):
+        q, k, v, lv, w, cu = tiny_inputs(21, (5, 17, 1, 40), 4, 2, 8,
+                                         v_scale=v_scale)
+        lam_init = 0.55
+        lam = (math.exp(float(np.dot(lv[0].astype(np.float64), lv[1])))
+               - math.exp(float(np.dot(lv[2].astype(np.float64), lv[3])))
+               + lam_init)
+        got = run(lib, q, k, v, lv, lam_init, w, 1e-5, True, cu)
+        for s in range(len(cu) - 1):
+            a = int(cu[s])
+            for h in range(4):
+                g = h // 2
+                pre = (1.0 - lam) * v[a, g].astype(np.float64)
+                ref = (pre / math.sqrt(np.mean(pre * pre) + 1e-5)
+                       * w.astype(np.float64) * (1.0 - lam_init))
+                err = np.max(np.abs(got[a, h] - ref))
+                assert err < 1e-12, f"row0 seq {s} head {h}: {err:.3e}"
+
+
+def pin_uniform_attention(lib):
+    """K = 0 makes every score zero, so each map is the uniform average over
+    the visible keys: pre_i = (1 - lambda) * mean_{j in J(i)} V_j."""
+    for causal in (True, False):
+        q, k, v, lv, w, cu = tiny_inputs(31, (50, 3, 77), 4, 1, 8)
+        k[:] = 0.0
+        lam_init = 0.7
+        lam = (math.exp(float(np.dot(lv[0].astype(np.float64), lv[1])))
+               - math.exp(float(np.dot(lv[2].astype(np.float64), lv[3])))
+               + lam_init)
+        got = run(lib, q, k, v, lv, lam_init, w, 1e-5, causal, cu)
+        for s in range(len(cu) - 1):
+            a, b = int(cu[s]), int(cu[s + 1])
+            vv = v[a:b, 0].astype(np.float64)
+            if causal:
+                mean = np.cumsum(vv, axis=0) / np.arange(1, b - a + 1)[:, None]
+            else:
+                mean = np.broadcast_to(vv.mean(axis=0), vv.shape)
+            pre = (1.0 - lam) * mean
+            ref = (pre / np.sqrt(np.mean(pre * pre, axis=1, keepdims=True) + 1e-5)
+                   * w.astype(np.float64) * (1.0 - lam_init))
+            for h in range(4):
+                err = np.max(np.abs(got[a:b, h] - ref))
+                assert err < 1e-12, f"uniform seq {s} head {h}: {err:.3e}"
+
+
+def pin_identical_maps(lib):
+    """Q2 = Q1, K2 = K1 and lambda = 1 cancel the two maps exactly."""
+    q, k, v, lv, w, cu = tiny_inputs(41, (20, 13), 4, 2, 8)
+    q[:, :, 1] = q[:, :, 0]
+    k[:, :, 1] = k[:, :, 0]
+    lv = [lv[0], lv[1], lv[0], lv[1]]
+    got = run(lib, q, k, v, lv, 1.0, w, 1e-5, True, cu)
+    assert np.all(got == 0.0), "identical maps with lambda = 1 must give 0"
+    # and with lambda != 1 they give RMSNorm((1 - lambda) * attention), whose
+    # sign is that of (1 - lambda): flip it and the output flips
+    a = run(lib, q, k, v, lv, 0.5, w, 1e-5, True, cu)
+    b = run(lib, q, k, v, lv, 1.5, w, 1e-5, True, cu)
+    assert np.max(np.abs(a / (1 - 0.5) + b / (1 - 1.5))) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# invariants
+
+def pin_causality(lib):
+    q, k, v, lv, w, cu = tiny_inputs(51, (30,), 2, 1, 4)
+    base = run(lib, q, k, v, lv, 0.4, w, 1e-5, True, cu)
+    for cut in (0, 7, 29):
+        q2, k2, v2 = q.copy(), k.copy(), v.copy()
+        q2[cut + 1:] += 3.0
+        k2[cut + 1:] -= 2.0
+        v2[cut + 1:] *= -5.0
+        got = run(lib, q2, k2, v2, lv, 0.4, w, 1e-5, True, cu)
+        assert np.array_equal(got[:cut + 1], base[:cut + 1]), f"cut {cut}"
+        if cut + 1 < 30:
+            assert not np.allclose(got[cut + 1:], base[cut + 1:])
+
+
+def pin_packing(lib):
+    seqlens = (9, 1, 25, 4)
+    q, k, v, lv, w, cu = tiny_inputs(61, seqlens, 4, 2, 4)
+    for causal in (True, False):
+        packed = run(lib, q, k, v, lv, 0.3, w, 1e-5, causal, cu)
+        for s in range(len(seqlens)):
+            a, b = int(cu[s]), int(cu[s + 1])
+            one = run(lib, q[a:b], k[a:b], v[a:b], lv, 0.3, w, 1e-5, causal,
+                      np.array([0, b - a], np.int32))
+            assert np.array_equal(one, packed[a:b]), f"seq {s}"
+
+
+def pin_gqa_equals_repeated(lib):
+    q, k, v, lv, w, cu = tiny_inputs(71, (19, 8), 6, 2, 4)
+    got = run(lib, q, k, v, lv, 0.3, w, 1e-5, True, cu)
+    kr = np.repeat(k, 3, axis=1)   # KV head g serves heads 3g .. 3g+2
+    vr = np.repeat(v, 3, axis=1)
+    ref = run(lib, q, kr, vr, lv, 0.3, w, 1e-5, True, cu)
+    assert np.array_equal(got, ref)
+
+
+def pin_odd_in_v(lib):
+    q, k, v, lv, w, cu = tiny_inputs(81, (12, 12), 2, 2, 4)
+    a = run(lib, q, k, v, lv, 0.3, w, 1e-5, True, cu)
+    b = run(lib, q, k, -v, lv, 0.3, w, 1e-5, True, cu)
+    assert np.array_equal(a, -b)
+
+
+def pin_rows_entry(lib):
+    q, k, v, lv, w, cu = tiny_inputs(91, (10, 23), 4, 2, 4)
+    full = run(lib, q, k, v, lv, 0.3, w, 1e-5, True, cu)
+    toks = np.array([0, 9, 10, 11, 32, 5, 20], np.int64)
+    heads = np.array([0, 3, 1, 2, 3, 0, 1], np.int32)
+    got = oracle.rows(q, k, v, *lv, 0.3, toks, heads, w, 1e-5, True, cu, lib=lib)
+    assert np.array_equal(got, full[toks, heads])
+
+
+ALL_PINS = [
+    pin_lambda_closed_forms,
+    pin_brute_force,
+    pin_sdpa_lambda_zero,
+    pin_sdpa_two_maps,
+    pin_row0_closed_form,
+    pin_uniform_attention,
+    pin_identical_maps,
+    pin_causality,
+    pin_packing,
+    pin_gqa_equals_repeated,
+    pin_odd_in_v,
+    pin_rows_entry,
+]

@@ -1,0 +1,55 @@
+"""Each plausible mistake planted in a copy of the oracle fails a pin.
+
+The copy is compiled on the CPU into a temporary directory; the real oracle
+source is never modified.
+"""
+
+import os
+
+import pytest
+
+import oracle
+import pins
+
+MUTANTS = {
+    "lambda_sign": ("p1[j] - lam * p2[j]", "p1[j] + lam * p2[j]"),
+    "lambda_drop_init": ("exp(dot1) - exp(dot2) + lambda_init", "exp(dot1) - exp(dot2)"),
+    "lambda_swap_terms": ("exp(dot1) - exp(dot2)", "exp(dot2) - exp(dot1)"),
+    "lambda_init_schedule": ("-0.3 * (double)(depth - 1)", "-0.3 * (double)depth"),
+    "causal_ignored": ("causal ? i + 1 : n", "causal ? n : n"),
+    "causal_strict": ("causal ? i + 1 : n", "causal ? (i > 0 ? i : 1) : n"),
+    "gqa_modulo": ("h / (H / Hkv)", "h % Hkv"),
+    "scale_full_width": ("1.0 / sqrt((double)d)", "1.0 / sqrt(2.0 * d)"),
+    "scale_squared": ("1.0 / sqrt((double)d)", "1.0 / (double)d"),
+    "eps_dropped": ("ss / (double)dv + eps", "ss / (double)dv"),
+    "rms_sum_not_mean": ("ss / (double)dv + eps", "ss + eps"),
+    "final_scale_dropped": ("* wc * (1.0 - lambda_init)", "* wc"),
+    "weight_ignored": ("w ? (double)w[c] : 1.0", "1.0"),
+    "k_map_swapped": ("+ g) * 2 + map) * (int64_t)d", "+ g) * 2 + (1 - map)) * (int64_t)d"),
+    "q_map_swapped": ("+ h) * 2 + map) * (int64_t)d", "+ h) * 2 + (1 - map)) * (int64_t)d"),
+    "key_row_is_query_row": ("k + (((a + j) * Hkv", "k + (((a + i) * Hkv"),
+    "v_uses_query_head": ("((a + j) * Hkv + g) * (int64_t)dv", "((a + j) * Hkv + h % Hkv) * (int64_t)dv"),
+    "softmax_no_max_shift": ("exp(p[j] - mx)", "exp(p[j])"),
+    "softmax_wrong_normaliser": ("p[j] /= z;", "p[j] /= (double)nkeys;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(tmp_path, name):
+    old, new = MUTANTS[name]
+    src = open(oracle.SOURCE).read()
+    assert src.count(old) >= 1, f"mutation anchor for {name} not found"
+    mutated = src.replace(old, new)
+    path = os.path.join(tmp_path, "mut.c")
+    with open(path, "w") as f:
+        f.write(mutated)
+    lib_path = oracle.build(path, os.path.join(tmp_path, f"libmut_{name}.so"))
+    lib = oracle.load(lib_path)
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(lib)
+        except (AssertionError, ValueError, FloatingPointError):
+            caught.append(pin.__name__)
+            break
+    assert caught, f"mutant {name} passed every pin"

@@ -1,0 +1,173 @@
+"""Seeded synthetic inputs for the differential-attention forward pass.
+
+This module holds no arithmetic of the method itself: it only draws random
+tensors, fixes the packed memory layout and names the five workload shapes.
+Both the fp64 oracle (through the tests) and the HIP library (through the
+tests and the benchmark) consume exactly what it returns, so the two sides see
+bit-identical inputs.
+
+Layout (token-major, contiguous), with T tokens, H differential heads, Hkv
+key/value heads and half-head width d:
+
+    q   [T, H,   2, d]   q[:, h, 0] is Q1 of head h, q[:, h, 1] is Q2
+    k   [T, Hkv, 2, d]   k[:, g, 0] is K1 of KV head g, k[:, g, 1] is K2
+    v   [T, Hkv, 2d]     one V shared by both maps
+    out [T, H,   2d]
+
+This is the head-major split of the DiffTransformer page
+("MultiHeadDifferentialAttention.forward": each head's 2d-wide projection is
+chunked into a first half for map 1 and a second half for map 2) laid out the
+way the FlashDiffAttention pull request packs it (2H half-heads of width d,
+"new_impl" / "alternative_forward").
+
+Draw order (one ``torch.Generator`` seeded with ``seed``): q, k, v from a
+standard normal in fp32, then the four lambda vectors lambda_q1, lambda_k1,
+lambda_q2, lambda_k2 from N(0, 0.1^2) in fp32 (the Llama diff-attention gist
+initialises them with ``normal_(mean=0, std=0.1)``). bf16 workloads round q, k
+and v to bf16 after drawing; the lambda vectors stay fp32.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: str              # "f32" or "bf16": storage type of q, k, v, out
+    seqlens: tuple          # one entry per packed sequence
+    H: int
+    Hkv: int
+    d: int
+    depth: int
+    causal: bool = True
+    eps: float = 1e-5
+    seed: int = 0
+    description: str = ""
+
+    @property
+    def T(self) -> int:
+        return int(sum(self.seqlens))
+
+    @property
+    def nseq(self) -> int:
+        return len(self.seqlens)
+
+    @property
+    def max_seqlen(self) -> int:
+        return int(max(self.seqlens)) if self.seqlens else 0
+
+    def cu_seqlens(self) -> np.ndarray:
+        cu = np.zeros(self.nseq + 1, dtype=np.int32)
+        cu[1:] = np.cumsum(np.asarray(self.seqlens, dtype=np.int64))
+        return cu
+
+    def flops(self) -> float:
+        """FLOP count under the stated convention: per unmasked (query, key)
+        pair and head, two QK^T maps of 2d FLOP each plus two PV
+        accumulations of 2*2d FLOP each, i.e. 12*d; a causal sequence of
+        length n contributes n^2/2 pairs, a full one n^2."""
+        pairs = sum((n * n) / 2.0 if self.causal else float(n * n) for n in self.seqlens)
+        return 12.0 * self.d * self.H * pairs
+
+
+def varlen_lengths(total: int, lo: int, hi: int, seed: int = 0) -> List[int]:
+    """Sequence lengths drawn uniformly from [lo, hi] with
+    ``numpy.random.default_rng(seed)`` until their sum reaches ``total``; the
+    last length is cut so that the sum is exactly ``total``."""
+    rng = np.random.default_rng(seed)
+    out: List[int] = []
+    s = 0
+    while s < total:
+        n = int(rng.integers(lo, hi + 1))
+        n = min(n, total - s)
+        out.append(n)
+        s += n
+    return out
+
+
+WORKLOADS = {
+    "tiny_f32": Workload(
+        "tiny_f32", "f32", (64,), H=2, Hkv=2, d=16, depth=1,
+        description="fp32, B=1, N=64, 2 diff heads (no GQA), d=16, depth 1"),
+    "embed2048_b2_n512": Workload(
+        "embed2048_b2_n512", "bf16", (512, 512), H=16, Hkv=4, d=64, depth=12,
+        description="bf16, B=2, N=512, 16 diff heads, 4 KV heads, d=64, depth 12"),
+    "llama1b_b8_n4096": Workload(
+        "llama1b_b8_n4096", "bf16", (4096,) * 8, H=16, Hkv=4, d=64, depth=8,
+        description="bf16, B=8, N=4096, 16 diff heads, 4 KV heads, d=64, depth 8"),
+    "long_b1_n32768": Workload(
+        "long_b1_n32768", "bf16", (32768,), H=16, Hkv=4, d=64, depth=16,
+        description="bf16, B=1, N=32768, 16 diff heads, 4 KV heads, d=64, depth 16"),
+    "varlen_t65536": Workload(
+        "varlen_t65536", "bf16", tuple(varlen_lengths(65536, 128, 4096, 0)),
+        H=16, Hkv=4, d=64, depth=24,
+        description="bf16 varlen, 65536 tokens, lengths uniform in [128,4096], "
+                    "16 diff heads, 4 KV heads, d=64, depth 24"),
+}
+
+HEADLINE = "llama1b_b8_n4096"
+
+
+def _randn(gen: torch.Generator, *shape) -> torch.Tensor:
+    return torch.randn(*shape, generator=gen, dtype=torch.float32)
+
+
+@dataclasses.dataclass
+class Inputs:
+    """Host tensors of one workload; q/k/v in the storage dtype, everything
+    else fp32 (cu_seqlens int32). ``depth`` is the 1-based layer depth from
+    which each side derives lambda_init itself."""
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    lq1: torch.Tensor
+    lk1: torch.Tensor
+    lq2: torch.Tensor
+    lk2: torch.Tensor
+    w: torch.Tensor
+    cu_seqlens: torch.Tensor
+    depth: int
+    eps: float
+    causal: bool
+    max_seqlen: int
+
+
+def torch_dtype(name: str) -> torch.dtype:
+    return {"f32": torch.float32, "bf16": torch.bfloat16}[name]
+
+
+def make_inputs(wl: Workload, seed: Optional[int] = None,
+                q_scale: float = 1.0) -> Inputs:
+    """Draw the inputs of ``wl`` on the CPU in the fixed order."""
+    gen = torch.Generator("cpu")
+    gen.manual_seed(wl.seed if seed is None else seed)
+    T, H, Hkv, d = wl.T, wl.H, wl.Hkv, wl.d
+    dt = torch_dtype(wl.dtype)
+    q = _randn(gen, T, H, 2, d)
+    if q_scale != 1.0:
+        q = q * q_scale
+    q = q.to(dt)
+    k = _randn(gen, T, Hkv, 2, d).to(dt)
+    v = _randn(gen, T, Hkv, 2 * d).to(dt)
+    lq1 = 0.1 * _randn(gen, d)
+    lk1 = 0.1 * _randn(gen, d)
+    lq2 = 0.1 * _randn(gen, d)
+    lk2 = 0.1 * _randn(gen, d)
+    w = torch.ones(2 * d, dtype=torch.float32)
+    cu = torch.from_numpy(wl.cu_seqlens())
+    return Inputs(q, k, v, lq1, lk1, lq2, lk2, w, cu,
+                  wl.depth, wl.eps, wl.causal, wl.max_seqlen)
+
+
+def custom(name: str, dtype: str, seqlens, H: int, Hkv: int, d: int,
+           depth: int = 1, causal: bool = True, eps: float = 1e-5,
+           seed: int = 0) -> Workload:
+    """An ad-hoc workload for edge-case tests."""
+    return Workload(name, dtype, tuple(int(n) for n in seqlens), H=H, Hkv=Hkv,
+                    d=d, depth=depth, causal=causal, eps=eps, seed=seed)
