@@ -1,0 +1,185 @@
+#!/usr/bin/env python3
+"""Throughput of the differential-attention forward on one MI355X.
+
+One step = one pass of the whole forward path (lambda, the two causal
+softmax maps over GQA/varlen-packed K/V, the combine, the per-head RMSNorm
+and the scale: one launch of the fused kernel) over one batch of synthetic
+input already resident in HBM.  The default workload is the 4096-token
+causal GQA shape (B=8, N=4096, 16 differential heads, 4 KV heads, d=64 per
+half, bf16).
+
+Prints ONE JSON line.  ``value`` is TFLOP/s under the convention 12*d*H
+FLOP per unmasked (query, key) pair with n^2/2 pairs per causal sequence;
+``roofline`` relates the measured kernel time to MI355X's dense bf16 MFMA
+peak; ``cpu_baseline`` times the fp64 oracle on the host cores on a bounded
+sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+if HERE not in sys.path:
+    sys.path.insert(0, HERE)
+
+# MI355X dense bf16 MFMA peak: 256 CUs x 2.4 GHz x 4096 FLOP/clk/CU
+# (AMD's published figure is 2.5 PFLOP/s dense; this is its unrounded form).
+PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12
+# fp32 MFMA (matrix) peak, for fp32-storage workloads.
+PEAK_F32_TFLOPS = 157.3
+METRIC = "diff-attention fwd TFLOP/s & % bf16 MFMA peak, 1 MI355X, N=4096 causal"
+KERNEL_SOURCES = [os.path.join(HERE, "differential_attention_amd", "csrc",
+                               "diffattn_fwd.hip"),
+                  os.path.join(HERE, "include", "diffattn.h")]
+
+
+def kernel_digest() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(HERE, "profiles", f"hbm_traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"kernel_digest:\s*([0-9a-f]+)", text)
+    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != kernel_digest():
+        return None
+    return float(t.group(1))
+
+
+def cpu_baseline(wl, inp):
+    """The fp64 oracle on every query row of the first sequence, all heads
+    (1/nseq of the workload)."""
+    import numpy as np
+    import oracle
+    n0 = int(wl.seqlens[0])
+    toks = np.repeat(np.arange(n0, dtype=np.int64), wl.H)
+    heads = np.tile(np.arange(wl.H, dtype=np.int32), n0)
+    arrs = [oracle._f32(x) for x in (inp.q, inp.k, inp.v, inp.lq1, inp.lk1,
+                                     inp.lq2, inp.lk2, inp.w)]
+    lam0 = oracle.lambda_init(wl.depth)
+    oracle.load()
+    t0 = time.perf_counter()
+    oracle.rows(*arrs[:7], lam0, toks, heads, arrs[7], wl.eps, wl.causal,
+                inp.cu_seqlens)
+    dt = time.perf_counter() - t0
+    pairs = float(np.sum(toks + 1)) if wl.causal else float(toks.size * n0)
+    flops = 12.0 * wl.d * pairs
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s",
+            "cores": oracle.max_threads(), "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": (f"every query row of sequence 0 ({n0} tokens) x all "
+                       f"{wl.H} heads = 1/{wl.nseq} of the workload; fp64 C "
+                       "oracle, OpenMP over rows")}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only (the forward kernel "
+              "on one GPU's share); --gpus above 1 is not supported",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import workloads
+    import differential_attention_amd as da
+
+    name = args.workload or workloads.HEADLINE
+    wl = workloads.WORKLOADS[name]
+    inp = workloads.make_inputs(wl)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    c = lambda t: t.to(dev).contiguous()
+    q, k, v = c(inp.q), c(inp.k), c(inp.v)
+    lv = [c(x) for x in (inp.lq1, inp.lk1, inp.lq2, inp.lk2)]
+    w = c(inp.w)
+    cu = c(inp.cu_seqlens)
+    out = torch.empty((wl.T, wl.H, 2 * wl.d), dtype=q.dtype, device=dev)
+    lam0 = da.lambda_init(wl.depth)
+    stream = torch.cuda.Stream(dev)
+    dtype_code = da.BF16 if wl.dtype == "bf16" else da.F32
+    ptrs = (dtype_code, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+            *[x.data_ptr() for x in lv], lam0, w.data_ptr(), wl.eps,
+            int(wl.causal), cu.data_ptr(), wl.nseq, wl.max_seqlen, wl.T, wl.H,
+            wl.Hkv, wl.d, out.data_ptr(), stream.cuda_stream)
+
+    def step():
+        st = da.fwd_ptr(*ptrs)
+        if st != 0:
+            raise da.DiffAttnError(st, "diffattn_fwd")
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            step()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    flops = wl.flops()
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
+    traffic = traffic_from_profiles(name)
+
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded N(0,1) q/k/v, N(0,0.1^2) lambda vectors)",
+        "config": {"workload": name, "T": wl.T, "nseq": wl.nseq,
+                   "max_seqlen": wl.max_seqlen, "H": wl.H, "Hkv": wl.Hkv,
+                   "d": wl.d, "depth": wl.depth, "causal": wl.causal,
+                   "flops_per_step": flops,
+                   "pct_of_bf16_peak": round(100 * tflops / peak, 2),
+                   "wall_s_timed": round(wall, 4),
+                   "kernel_digest": kernel_digest()},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
+                     "peak": round(peak, 1), "unit": "TFLOP/s",
+                     "frac": round(tflops / peak, 4), "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, inp)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

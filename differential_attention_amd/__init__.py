@@ -1,0 +1,187 @@
+"""Python binding of libdiffattn, the MI355X differential-attention forward.
+
+Argument marshalling only: tensors become device pointers and sizes, the
+stream comes from torch, and every step of the computation runs in the HIP
+kernels of ``libdiffattn.so`` behind the C ABI declared in
+``include/diffattn.h``.  PyTorch is used for device memory and streams.
+
+There is no fallback: if the library is missing, or the call fails, this
+module raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = ["fwd", "fwd_ptr", "lambda_init", "supported", "check_cu_seqlens",
+           "library", "LIBRARY", "DiffAttnError", "BF16", "F32"]
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(HERE, "libdiffattn.so")
+
+OK, EINVAL, EUNSUPPORTED, EHIP = 0, -1, -2, -3
+BF16, F32 = 0, 1
+_DTYPES = {torch.bfloat16: BF16, torch.float32: F32}
+
+
+class DiffAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {strerror(status)} (status {status})")
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def library() -> ctypes.CDLL:
+    """The loaded C library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIBRARY):
+        raise RuntimeError(
+            f"{LIBRARY} is missing: build it with "
+            "`python differential_attention_amd/build.py` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIBRARY)
+    vp, f32p, i32p = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
+    i32 = ctypes.c_int32
+    lib.diffattn_fwd.argtypes = [
+        ctypes.c_int, vp, vp, vp, f32p, f32p, f32p, f32p, ctypes.c_float, f32p,
+        ctypes.c_float, ctypes.c_int, i32p, i32, i32, i32, i32, i32, i32, vp, vp]
+    lib.diffattn_fwd.restype = ctypes.c_int
+    lib.diffattn_lambda_init.argtypes = [ctypes.c_int]
+    lib.diffattn_lambda_init.restype = ctypes.c_double
+    lib.diffattn_supported.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.diffattn_supported.restype = ctypes.c_int
+    lib.diffattn_check_cu_seqlens.argtypes = [ctypes.POINTER(ctypes.c_int32),
+                                              i32, i32, i32]
+    lib.diffattn_check_cu_seqlens.restype = ctypes.c_int
+    lib.diffattn_strerror.argtypes = [ctypes.c_int]
+    lib.diffattn_strerror.restype = ctypes.c_char_p
+    lib.diffattn_abi_version.argtypes = []
+    lib.diffattn_abi_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def strerror(status: int) -> str:
+    return library().diffattn_strerror(int(status)).decode()
+
+
+def lambda_init(depth: int) -> float:
+    """Initial lambda of a layer at 1-based ``depth`` (computed by the
+    library)."""
+    return float(library().diffattn_lambda_init(int(depth)))
+
+
+def supported(dtype: torch.dtype, d: int) -> bool:
+    return bool(library().diffattn_supported(_DTYPES[dtype], int(d)))
+
+
+def check_cu_seqlens(cu_host, T: int, max_seqlen: int) -> bool:
+    """Host-side precondition check of a CPU copy of cu_seqlens."""
+    cu = torch.as_tensor(cu_host, dtype=torch.int32).contiguous().cpu()
+    ptr = ctypes.cast(cu.data_ptr(), ctypes.POINTER(ctypes.c_int32))
+    return library().diffattn_check_cu_seqlens(ptr, cu.numel() - 1, int(T),
+                                               int(max_seqlen)) == OK
+
+
+def fwd_ptr(dtype: int, q: int, k: int, v: int, lq1: int, lk1: int, lq2: int,
+            lk2: int, lambda_init_value: float, subln_weight: int, eps: float,
+            causal: int, cu_seqlens: int, nseq: int, max_seqlen: int, T: int,
+            H: int, Hkv: int, d: int, out: int, stream: int) -> int:
+    """The raw C entry point on integer device addresses; returns the
+    status."""
+    return library().diffattn_fwd(
+        int(dtype), q or None, k or None, v or None, lq1 or None, lk1 or None,
+        lq2 or None, lk2 or None, float(lambda_init_value),
+        subln_weight or None, float(eps), int(causal), cu_seqlens or None,
+        int(nseq), int(max_seqlen), int(T), int(H), int(Hkv), int(d),
+        out or None, stream or None)
+
+
+def _dev(t: torch.Tensor, name: str, device, dtype=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+        lambda_q1: torch.Tensor, lambda_k1: torch.Tensor,
+        lambda_q2: torch.Tensor, lambda_k2: torch.Tensor,
+        lambda_init: float, subln_weight: Optional[torch.Tensor] = None,
+        eps: float = 1e-5, causal: bool = True,
+        cu_seqlens: Optional[torch.Tensor] = None,
+        max_seqlen: Optional[int] = None, nseq: Optional[int] = None,
+        out: Optional[torch.Tensor] = None,
+        stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Differential-attention forward on the GPU.
+
+    q [T, H, 2, d], k [T, Hkv, 2, d], v [T, Hkv, 2d] (bf16 or fp32, one
+    device); lambda vectors fp32 [d]; subln_weight fp32 [2d] or None;
+    cu_seqlens int32 [nseq + 1] on the device, or None for ``nseq`` (default
+    1) sequences of equal length.  ``max_seqlen`` bounds every sequence
+    length; when cu_seqlens is given without it, it is read back from the
+    device (a synchronising copy).  Returns ``out`` [T, H, 2d].
+    """
+    if q.dim() != 4 or q.shape[2] != 2:
+        raise ValueError("q must be [T, H, 2, d]")
+    T, H, _, d = q.shape
+    if k.dim() != 4 or k.shape[0] != T or k.shape[2:] != (2, d):
+        raise ValueError("k must be [T, Hkv, 2, d]")
+    Hkv = k.shape[1]
+    if tuple(v.shape) != (T, Hkv, 2 * d):
+        raise ValueError("v must be [T, Hkv, 2d]")
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("q must be a GPU tensor")
+    args = [_dev(q, "q", dev), _dev(k, "k", dev, q.dtype),
+            _dev(v, "v", dev, q.dtype)]
+    for name, lv in (("lambda_q1", lambda_q1), ("lambda_k1", lambda_k1),
+                     ("lambda_q2", lambda_q2), ("lambda_k2", lambda_k2)):
+        if lv.numel() != d:
+            raise ValueError(f"{name} must have d = {d} elements")
+        args.append(_dev(lv, name, dev, torch.float32))
+    w_ptr = 0
+    if subln_weight is not None:
+        if subln_weight.numel() != 2 * d:
+            raise ValueError("subln_weight must have 2d elements")
+        w_ptr = _dev(subln_weight, "subln_weight", dev, torch.float32)
+    cu_ptr = 0
+    if cu_seqlens is not None:
+        cu_ptr = _dev(cu_seqlens, "cu_seqlens", dev, torch.int32)
+        nseq = cu_seqlens.numel() - 1
+        if max_seqlen is None:
+            cu_host = cu_seqlens.cpu()
+            max_seqlen = int((cu_host[1:] - cu_host[:-1]).max()) if nseq > 0 else 0
+    else:
+        nseq = 1 if nseq is None else int(nseq)
+        if max_seqlen is None:
+            max_seqlen = T // nseq if nseq > 0 else 0
+    if out is None:
+        out = torch.empty((T, H, 2 * d), dtype=q.dtype, device=dev)
+    elif tuple(out.shape) != (T, H, 2 * d):
+        raise ValueError("out must be [T, H, 2d]")
+    out_ptr = _dev(out, "out", dev, q.dtype)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        st = fwd_ptr(_DTYPES[q.dtype], args[0], args[1], args[2], args[3],
+                     args[4], args[5], args[6], lambda_init, w_ptr, eps,
+                     int(bool(causal)), cu_ptr, nseq, max_seqlen, T, H, Hkv, d,
+                     out_ptr, stream.cuda_stream)
+    if st != OK:
+        raise DiffAttnError(st, "diffattn_fwd")
+    return out

@@ -1,0 +1,41 @@
+"""Build step of the HIP library: hipcc for gfx950 into libdiffattn.so,
+in-tree beside this file."""
+
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+SOURCES = [os.path.join(HERE, "csrc", "diffattn_fwd.hip")]
+LIBRARY = os.path.join(HERE, "libdiffattn.so")
+ARCH = "gfx950"
+
+HIPCC_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-Wall", "-Werror",
+    # no packed-fp32 VALU instructions anywhere in the device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", os.path.join(ROOT, "include"),
+]
+
+
+def build(output: str = LIBRARY, extra=(), verbose: bool = False) -> str:
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    cmd = [hipcc, *HIPCC_FLAGS, *extra, *SOURCES, "-o", output + ".tmp"]
+    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                         text=True)
+    msg = "\n".join(l for l in res.stdout.splitlines()
+                    if "packed-fp32-ops' is not a recognized feature" not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{msg}")
+    if verbose and msg.strip():
+        print(msg, file=sys.stderr)
+    os.replace(output + ".tmp", output)
+    return output
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

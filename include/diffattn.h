@@ -1,0 +1,122 @@
+/*
+ * diffattn.h -- C ABI of the MI355X (gfx950) differential-attention forward.
+ *
+ * The operation (DiffTransformer.py of Differential-Transformer-PyTorch,
+ * MultiHeadDifferentialAttention.forward; LlamaDiffSdpaAttention.py, forward;
+ * unilm pull request "Add an isolated implementation of FlashDiffAttention",
+ * FlashDiffAttention and alternative_forward):
+ *
+ *   lambda = exp(<lambda_q1, lambda_k1>) - exp(<lambda_q2, lambda_k2>) + lambda_init
+ *   for each packed sequence, head h (KV head g = h / (H / Hkv)), query i:
+ *     A_m[i, j] = softmax_j( <Qm[i, h], Km[j, g]> / sqrt(d) ),  m = 1, 2,
+ *                 over keys j <= i of the same sequence (all of its keys
+ *                 when causal == 0)
+ *     pre[i]    = sum_j (A_1[i, j] - lambda * A_2[i, j]) * V[j, g]   (2d wide)
+ *     out[i, h] = pre[i] / sqrt(mean(pre[i]^2) + eps) * w * (1 - lambda_init)
+ *
+ * Memory layout (all device memory, contiguous, token-major; T tokens, H
+ * differential heads, Hkv key/value heads, half-head width d):
+ *   q   [T, H,   2, d]   q[t, h, 0, :] = Q1, q[t, h, 1, :] = Q2 of head h
+ *   k   [T, Hkv, 2, d]   k[t, g, 0, :] = K1, k[t, g, 1, :] = K2 of KV head g
+ *   v   [T, Hkv, 2d]
+ *   out [T, H,   2d]     equal to [T, H * 2d], the heads concatenated
+ * q, k, v and out share one element type (DIFFATTN_BF16 or DIFFATTN_F32)
+ * and must be 16-byte aligned.
+ *
+ * Ownership: the caller owns every buffer.  The library allocates no device
+ * or host memory, keeps no state between calls, never synchronises, and is
+ * safe to call from several threads.  out must not overlap any input.
+ *
+ * Errors: every entry point returns a status (DIFFATTN_OK or a negative
+ * code) and never aborts or throws.  Argument errors are detected on the host
+ * before anything is launched.  Launch errors return DIFFATTN_EHIP; a fault
+ * inside the kernel surfaces at the caller's next synchronisation on the
+ * stream.
+ */
+#ifndef DIFFATTN_H
+#define DIFFATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DIFFATTN_ABI_VERSION 1
+
+enum diffattn_status {
+    DIFFATTN_OK = 0,
+    DIFFATTN_EINVAL = -1,       /* malformed arguments; nothing launched    */
+    DIFFATTN_EUNSUPPORTED = -2, /* (dtype, d) pair not compiled in          */
+    DIFFATTN_EHIP = -3          /* HIP runtime error: no device, bad launch */
+};
+
+enum diffattn_dtype {
+    DIFFATTN_BF16 = 0, /* bfloat16 storage, fp32 accumulation */
+    DIFFATTN_F32 = 1   /* fp32 storage, fp32 arithmetic       */
+};
+
+/*
+ * Differential-attention forward pass, asynchronous on `stream`.
+ *
+ *   dtype        DIFFATTN_BF16 or DIFFATTN_F32: element type of q, k, v, out.
+ *   q, k, v      device inputs in the layout above.
+ *   lambda_q1, lambda_k1, lambda_q2, lambda_k2
+ *                device fp32 vectors of length d, one set shared by all heads
+ *                (the Llama gist and alternative_forward share it; the
+ *                DiffTransformer page keeps one set per head).
+ *   lambda_init  the layer's initial lambda (see diffattn_lambda_init).
+ *   subln_weight device fp32 [2d] RMSNorm weight, or NULL for all ones.
+ *   eps          RMSNorm epsilon (1e-5 on the DiffTransformer page); >= 0.
+ *   causal       1: query i sees keys j <= i of its sequence; 0: all keys of
+ *                its sequence.
+ *   cu_seqlens   device int32 [nseq + 1] sequence boundaries: cu[0] = 0,
+ *                non-decreasing, cu[nseq] = T.  Zero-length sequences are
+ *                allowed.  NULL means nseq sequences of T / nseq tokens each.
+ *                The contents are a precondition, not checked here (see
+ *                diffattn_check_cu_seqlens).
+ *   nseq         number of sequences (>= 1 when T > 0).
+ *   max_seqlen   an upper bound on every sequence length (>= 1 when T > 0);
+ *                sizes the launch grid.  With cu_seqlens == NULL it must be
+ *                T / nseq, or <= 0 to let the library take that value.
+ *   T, H, Hkv, d sizes; H % Hkv == 0.  Compiled (dtype, d) pairs: see
+ *                diffattn_supported.
+ *   out          device output [T, H, 2d], same element type as q.
+ *   stream       a hipStream_t, or NULL for the null stream.
+ *
+ * Returns DIFFATTN_OK (also for T == 0, which launches nothing),
+ * DIFFATTN_EINVAL, DIFFATTN_EUNSUPPORTED or DIFFATTN_EHIP.
+ */
+int diffattn_fwd(int dtype, const void *q, const void *k, const void *v,
+                 const float *lambda_q1, const float *lambda_k1,
+                 const float *lambda_q2, const float *lambda_k2,
+                 float lambda_init, const float *subln_weight, float eps,
+                 int causal, const int32_t *cu_seqlens, int32_t nseq,
+                 int32_t max_seqlen, int32_t T, int32_t H, int32_t Hkv,
+                 int32_t d, void *out, void *stream);
+
+/* Initial lambda of a layer at 1-based depth: 0.8 - 0.6 * exp(-0.3 *
+ * (depth - 1)), the decaying schedule with which DiffTransformer.__init__
+ * builds its layers.  Host function; no device work. */
+double diffattn_lambda_init(int depth);
+
+/* 1 if the kernel is compiled for (dtype, d), else 0.  Host function. */
+int diffattn_supported(int dtype, int d);
+
+/* Host-side check of a host copy of cu_seqlens against the preconditions of
+ * diffattn_fwd (cu[0] == 0, non-decreasing, cu[nseq] == T, every length
+ * <= max_seqlen).  Returns DIFFATTN_OK or DIFFATTN_EINVAL. */
+int diffattn_check_cu_seqlens(const int32_t *host_cu, int32_t nseq, int32_t T,
+                              int32_t max_seqlen);
+
+/* Static text for a status code; never NULL. */
+const char *diffattn_strerror(int status);
+
+/* DIFFATTN_ABI_VERSION of the built library. */
+int diffattn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIFFATTN_H */

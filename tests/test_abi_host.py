@@ -1,0 +1,97 @@
+"""The C-ABI library on the host: it loads, exports every declared symbol
+and rejects malformed arguments before touching a device (CPU only)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import differential_attention_amd as da
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "diffattn.h")
+FAKE = 0x1000   # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(diffattn_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return da.library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert "diffattn_fwd" in names and len(names) >= 6
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in diffattn.h but not exported"
+
+
+def test_abi_version_matches_header(lib):
+    m = re.search(r"#define DIFFATTN_ABI_VERSION (\d+)", open(HEADER).read())
+    assert lib.diffattn_abi_version() == int(m.group(1))
+
+
+def test_strerror(lib):
+    for st in (0, -1, -2, -3, 12345):
+        assert isinstance(da.strerror(st), str) and da.strerror(st)
+
+
+def test_lambda_init_schedule():
+    assert abs(da.lambda_init(1) - 0.2) < 1e-15
+    assert abs(da.lambda_init(10 ** 6) - 0.8) < 1e-15
+
+
+def test_supported():
+    import torch
+    assert da.supported(torch.bfloat16, 64)
+    assert da.supported(torch.float32, 16)
+    assert not da.supported(torch.bfloat16, 48)
+
+
+def test_check_cu_seqlens():
+    assert da.check_cu_seqlens([0, 3, 3, 10], 10, 7)
+    assert not da.check_cu_seqlens([0, 3, 3, 10], 10, 6)     # length 7 > max
+    assert not da.check_cu_seqlens([0, 5, 4, 10], 10, 10)    # decreasing
+    assert not da.check_cu_seqlens([1, 5, 10], 10, 10)       # cu[0] != 0
+    assert not da.check_cu_seqlens([0, 5, 9], 10, 10)        # cu[nseq] != T
+
+
+def call(**over):
+    a = dict(dtype=da.BF16, q=FAKE, k=FAKE, v=FAKE, lq1=FAKE, lk1=FAKE,
+             lq2=FAKE, lk2=FAKE, lambda_init_value=0.2, subln_weight=0,
+             eps=1e-5, causal=1, cu_seqlens=0, nseq=2, max_seqlen=0, T=64,
+             H=16, Hkv=4, d=64, out=FAKE, stream=0)
+    a.update(over)
+    return da.fwd_ptr(**a)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(dtype=7), da.EINVAL),
+    (dict(H=6, Hkv=4), da.EINVAL),
+    (dict(Hkv=0), da.EINVAL),
+    (dict(T=-1), da.EINVAL),
+    (dict(causal=2), da.EINVAL),
+    (dict(eps=-1.0), da.EINVAL),
+    (dict(eps=float("nan")), da.EINVAL),
+    (dict(lambda_init_value=float("inf")), da.EINVAL),
+    (dict(d=48), da.EUNSUPPORTED),
+    (dict(dtype=da.F32, d=32), da.EUNSUPPORTED),
+    (dict(q=0), da.EINVAL),
+    (dict(out=0), da.EINVAL),
+    (dict(lk2=0), da.EINVAL),
+    (dict(q=FAKE + 8), da.EINVAL),             # not 16-byte aligned
+    (dict(nseq=0), da.EINVAL),
+    (dict(nseq=3), da.EINVAL),                 # T % nseq != 0 without cu
+    (dict(max_seqlen=31), da.EINVAL),          # must equal T / nseq
+    (dict(cu_seqlens=FAKE, max_seqlen=0), da.EINVAL),
+    (dict(cu_seqlens=FAKE, max_seqlen=65), da.EINVAL),
+    (dict(T=0, q=0, k=0, v=0, out=0), da.OK),  # empty: nothing launched
+])
+def test_validation_before_any_device_work(over, status):
+    assert call(**over) == status
