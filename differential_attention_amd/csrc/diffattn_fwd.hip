@@ -13,27 +13,33 @@
 //   otherwise  : 1 head   x 128 queries
 // Every wave owns 32 query rows of one head and keeps, for both maps, the
 // running row maximum, the running sum and a 32 x 2d fp32 accumulator, so
-// the two softmax recurrences are fully independent.
+// the two softmax recurrences are fully independent.  The register budget
+// is 256 per lane, so two workgroups share a CU: while one wave of a SIMD
+// runs its MFMAs the other runs its softmax.
 //
 // The workgroup streams the KV range of its sequence in tiles of 64 keys.
-// Each tile's K (both halves, 64 x 2d) and V (transposed, 2d x 64) is staged
-// once in LDS and read by all four waves: K/V of a GQA group enter the chip
-// once per 32..128 query rows and are never copied per head.  Tiles are
-// double-buffered: global loads of tile t+1 are in flight (in registers)
-// while tile t is computed, then written to the other LDS buffer; one
-// barrier per tile.
+// K (both halves) and V of a tile are copied global -> LDS directly
+// (global_load_lds, 16 bytes per lane, no registers), row-major with an XOR
+// swizzle of the 16-byte chunks, double-buffered: the copy of tile t+1 is in
+// flight while tile t is computed; one barrier per tile.  K/V of a GQA group
+// enter LDS once per 32..128 query rows and are never copied per head.
 //
 // All four contractions run on MFMA (v_mfma_f32_32x32x16_bf16 for bf16,
 // v_mfma_f32_32x32x2_f32 for fp32), in transposed form:
 //   S_m^T [keys x queries] = K_m [keys x d] * Q_m^T      (m = 1, 2)
 //   O_m^T [2d  x queries] += V^T [2d x keys] * P_m^T
-// With S^T, each lane owns one query column and 16 keys of every 32-key
-// block, so row maxima and sums need one cross-half exchange only, and the
-// accumulator layout of S^T is directly the B-operand layout of the PV
-// product.  The key order inside a 32-key block is permuted (K rows are
-// gathered in order sigma) so that the 8 keys one lane contributes to a PV
-// step are consecutive, which makes every V^T operand a single 16-byte LDS
-// read.
+// With S^T each lane owns one query column and 16 keys of every 32-key
+// block: row maxima and sums are in-lane plus one cross-half exchange, and
+// the accumulator layout of S^T is directly the B-operand layout of the PV
+// product.  V^T operands come from the row-major V tile through the
+// transposing LDS read ds_read_b64_tr_b16 (bf16) or plain 4-byte reads
+// (fp32).
+//
+// Softmax uses a lazily updated running maximum: probabilities are taken
+// against the stored maximum as long as no score of the tile exceeds it by
+// more than 2^8 in probability; only then (in practice on the first tile)
+// the maximum, the sums and the accumulators are rescaled.  The result O/l
+// does not depend on which maximum was used.
 //
 // The epilogue is fused: lambda (computed per wave from the four vectors),
 // O_1/l_1 - lambda O_2/l_2, the RMSNorm over 2d (in-lane sums plus one
@@ -52,19 +58,54 @@
 namespace {
 
 typedef __bf16 bf16;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void gbl_void;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBN = 64;   // keys per KV tile
 constexpr int kQW = 32;   // query rows per wave
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescaleLog2 = 8.0f;   // lazy-max threshold, log2 units
 
+// ---------------------------------------------------------------------------
+// LDS tile geometry.  A K tile is [64 keys][2d] (K1 then K2 of each key), a
+// V tile [64 keys][2d]; both row-major with padded rows so that every
+// operand read is a per-lane base plus a compile-time offset and hits
+// distinct banks:
+//   K rows are ROWB + 16 bytes apart: the 16 rows one 16-lane group reads at
+//     one column start 16 bytes apart modulo 256;
+//   V rows (bf16) are ROWB + 64 bytes apart: the 4 rows x 64 bytes one
+//     half-wave of a transposing read touches tile all 256 bytes of banks.
+// The tiles are filled by direct global->LDS copies of 64 lanes x 16 bytes
+// (1 KiB contiguous per copy); padding slots receive a harmless duplicate.
+template <typename E, int D> struct Geo {
+    static constexpr int ES = (int)sizeof(E);
+    static constexpr int ROWB = 2 * D * ES;                 // data bytes per row
+    static constexpr int CPR = ROWB / 16;                   // data chunks per row
+    static constexpr int KROWB = ROWB + 16;
+    static constexpr int VROWB = ROWB + (ES == 2 ? 64 : 16);
+    static constexpr int KSPR = KROWB / 16;                 // slots per K row
+    static constexpr int VSPR = VROWB / 16;
+    static constexpr int KTILEB = kBN * KROWB;
+    static constexpr int VTILEB = kBN * VROWB;
+    static constexpr int KCOPIES = KTILEB / 1024;           // 1 KiB copies
+    static constexpr int VCOPIES = VTILEB / 1024;
+    static constexpr int STAGEB = KTILEB + VTILEB;
+    static constexpr int MAXC = (KCOPIES > VCOPIES ? KCOPIES : VCOPIES);
+    static constexpr int CPW = (MAXC + kWaves - 1) / kWaves; // copies per wave
+    static_assert(KCOPIES * 1024 == KTILEB && VCOPIES * 1024 == VTILEB, "copy tiling");
+};
+
+// ---------------------------------------------------------------------------
+// MFMA flavours.  VEC = operand elements per lane; one MFMA contracts 2*VEC.
 template <typename E> struct Mfma;
 
 template <> struct Mfma<bf16> {
-    static constexpr int VEC = 8;   // operand elements per lane
+    static constexpr int VEC = 8;
     typedef bf16x8 Frag;
     __device__ static inline f32x16 mma(Frag a, Frag b, f32x16 c)
     {
@@ -90,6 +131,72 @@ template <> struct Mfma<float> {
     __device__ static inline Frag pack(const f32x16 &s, int a0) { return s[a0]; }
 };
 
+// Row (key offset inside a 32-key block) of accumulator element a of a lane
+// in half h of a 32x32 MFMA result.
+__device__ __host__ constexpr int acc_row(int a, int h) { return 8 * (a / 4) + 4 * h + (a % 4); }
+
+// Value of x in the lane 32 apart, and the two combined (lower lane first,
+// so both halves compute bitwise the same result).
+__device__ inline float pair_max(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float pair_sum(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// V^T operand of the PV product for one 16-key step (keys base .. base+15
+// of the tile, in MFMA k order) and one 32-dim block.
+template <typename E, int D> struct VOperand;
+
+template <int D> struct VOperand<bf16, D> {
+    // lane l: group G = l/16, j = l%16; for the transposing read, lane j of
+    // the group addresses key row (4*(l/32) + j/4) and dims 4*(j%4)..+3 of
+    // the group's 16 dims; the hardware hands lane j dim (16*(G%2) + j) of
+    // all four rows.  Two reads (t = 0, 1) give keys 8t + 4h + 0..3 of the
+    // 16-key step, i.e. MFMA k = 8h + 4t + e.
+    __device__ static inline int lane_base(int lane)
+    {
+        typedef Geo<bf16, D> G;
+        const int j = lane & 15;
+        return (4 * (lane >> 5) + (j >> 2)) * G::VROWB + 32 * ((lane >> 4) & 1) + 8 * (j & 3);
+    }
+    __device__ static inline bf16x8 load(const char *vt, int step_row, int db)
+    {
+        typedef Geo<bf16, D> G;
+        bf16x8 f;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const char *addr = vt + (step_row + 8 * t) * G::VROWB + 64 * db;
+            const bf16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (__attribute__((address_space(3))) bf16x4 *)addr);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                f[4 * t + e] = x[e];
+        }
+        return f;
+    }
+};
+
+template <int D> struct VOperand<float, D> {
+    // lane (m = l%32, h = l/32) reads dim 32*db + m of key row step_row + 4h
+    __device__ static inline int lane_base(int lane)
+    {
+        typedef Geo<float, D> G;
+        return 4 * (lane >> 5) * G::VROWB + 4 * (lane & 31);
+    }
+    __device__ static inline float load(const char *vt, int step_row, int db)
+    {
+        typedef Geo<float, D> G;
+        return *(const float *)(vt + step_row * G::VROWB + 128 * db);
+    }
+};
+
 struct Params {
     const void *q;
     const void *k;
@@ -107,124 +214,36 @@ struct Params {
     int32_t hblocks;   // head blocks per KV group: G / hpw
 };
 
-// Key offset, inside a 32-key block, of accumulator element a of a lane in
-// half h (= lane / 32).  The 32x32 MFMA accumulator puts element a of lane
-// (n, h) at row 8*(a/4) + 4*h + a%4; K rows are gathered so that this row
-// holds key 16*(a/8) + 8*h + a%8.
-__device__ __host__ constexpr int key_of_acc(int a, int h)
-{
-    return 16 * (a / 8) + 8 * h + (a % 8);
-}
-
-// The K row that MFMA row m (= lane % 32 of the A operand) must hold.
-__device__ __host__ constexpr int key_of_row(int m)
-{
-    return key_of_acc(4 * (m / 8) + (m % 4), (m / 4) % 2);
-}
-
-__device__ inline float xor32(float x) { return __shfl_xor(x, 32, 64); }
-
-template <typename E, int D> struct Layout {
-    static constexpr int CH = 16 / (int)sizeof(E);        // elements per 16 B
-    static constexpr int KROW = 2 * D + CH;               // K row stride
-    static constexpr int VROW = kBN + CH;                 // V^T row stride
-    static constexpr int K_ELEMS = kBN * KROW;
-    static constexpr int V_ELEMS = 2 * D * VROW;
-    static constexpr int STAGE = K_ELEMS + V_ELEMS;
-    static constexpr int CPR = 2 * D / CH;                // 16 B chunks per row
-    static constexpr int KC = kBN * CPR / kThreads;       // K chunks per thread
-    static constexpr int KG = kThreads / CPR;             // V key groups
-    static constexpr int R = kBN / KG;                    // keys per V group
-    static_assert(KC * kThreads == kBN * CPR, "K staging must tile evenly");
-    static_assert(KG * R == kBN && KG * CPR == kThreads, "V staging tiling");
-    static_assert(D % (2 * Mfma<E>::VEC) == 0, "d must be a multiple of the MFMA depth");
-    static_assert((2 * D) % 32 == 0, "2d must be a multiple of 32");
-};
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// Global -> registers part of staging one KV tile (keys [k0, k0 + 64) of KV
-// head g).  Keys at or beyond `kend` are replaced by zeros.
-template <typename E, int D> struct Stage {
-    typedef Layout<E, D> L;
-    u32x4 kr[L::KC];
-    u32x4 vr[L::R];
-
-    __device__ inline void load(const E *__restrict__ k, const E *__restrict__ v,
-                                int Hkv, int g, int k0, int kend, int tid)
-    {
-#pragma unroll
-        for (int c = 0; c < L::KC; ++c) {
-            const int idx = tid + c * kThreads;
-            const int row = idx / L::CPR, col = idx % L::CPR;
-            const int key = k0 + row;
-            if (key < kend) {
-                const E *src = k + ((int64_t)key * Hkv + g) * (2 * D) + col * L::CH;
-                kr[c] = *(const u32x4 *)src;
-            } else {
-                kr[c] = u32x4{0, 0, 0, 0};
-            }
-        }
-        const int kg = tid % L::KG, dc = tid / L::KG;
-#pragma unroll
-        for (int r = 0; r < L::R; ++r) {
-            const int key = k0 + kg * L::R + r;
-            if (key < kend) {
-                const E *src = v + ((int64_t)key * Hkv + g) * (2 * D) + dc * L::CH;
-                vr[r] = *(const u32x4 *)src;
-            } else {
-                vr[r] = u32x4{0, 0, 0, 0};
-            }
-        }
-    }
-
-    __device__ inline void store(E *__restrict__ ks, E *__restrict__ vts, int tid) const
-    {
-#pragma unroll
-        for (int c = 0; c < L::KC; ++c) {
-            const int idx = tid + c * kThreads;
-            const int row = idx / L::CPR, col = idx % L::CPR;
-            *(u32x4 *)(ks + row * L::KROW + col * L::CH) = kr[c];
-        }
-        // transpose: V rows (keys) -> V^T rows (dims)
-        const int kg = tid % L::KG, dc = tid / L::KG;
-        E vals[L::R][L::CH];
-#pragma unroll
-        for (int r = 0; r < L::R; ++r)
-            __builtin_memcpy(&vals[r][0], &vr[r], 16);
-#pragma unroll
-        for (int e = 0; e < L::CH; ++e) {
-            E col[L::R];
-#pragma unroll
-            for (int r = 0; r < L::R; ++r)
-                col[r] = vals[r][e];
-            __builtin_memcpy(vts + (dc * L::CH + e) * L::VROW + kg * L::R, col,
-                             sizeof(col));
-        }
-    }
+// Waves per SIMD the register budget is cut for: two (two workgroups per CU)
+// wherever the double-buffered tiles leave room for a second workgroup in LDS.
+template <typename E, int D> struct Occupancy {
+    static constexpr int value = 2 * Geo<E, D>::STAGEB * 2 <= 160 * 1024 ? 2 : 1;
 };
 
 template <typename E, int D>
-__global__ __launch_bounds__(kThreads, 1) void diffattn_fwd_kernel(Params p)
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(Occupancy<E, D>::value, Occupancy<E, D>::value)))
+void diffattn_fwd_kernel(Params p)
 {
-    typedef Layout<E, D> L;
+    typedef Geo<E, D> GEO;
     typedef Mfma<E> M;
     typedef typename M::Frag Frag;
     constexpr int VEC = M::VEC;
-    constexpr int KSTEP = 2 * VEC;         // contraction depth of one MFMA
-    constexpr int NKS = D / KSTEP;         // MFMAs per 32x32 score block
-    constexpr int NDB = 2 * D / 32;        // 32-wide blocks of the output
-    constexpr int NPS = 32 / KSTEP;        // PV steps per 32-key block
+    constexpr int KSTEP = 2 * VEC;      // contraction depth of one MFMA
+    constexpr int NKS = D / KSTEP;      // MFMAs per 32x32 score block
+    constexpr int NDB = 2 * D / 32;     // 32-wide blocks of the output
+    constexpr int NPS = 32 / KSTEP;     // PV steps per 32-key block
+    static_assert(D % KSTEP == 0 && (2 * D) % 32 == 0, "unsupported d");
 
-    __shared__ __attribute__((aligned(16))) E smem[2 * L::STAGE];
+    __shared__ __attribute__((aligned(1024))) char smem[2 * GEO::STAGEB];
 
     const int tid = threadIdx.x;
-    const int wave = tid / 64;
-    const int lane = tid % 64;
-    const int n = lane % 32;   // query column owned by this lane
-    const int h = lane / 32;   // lane half
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int n = lane & 31;   // query column owned by this lane
+    const int h = lane >> 5;   // lane half
 
-    // ---- tile scheduler: longest query tiles first ----------------------
+    // ---- tile scheduler: longest query tiles first ------------------------
     const int pairs = p.nseq * p.Hkv * p.hblocks;
     const int id = blockIdx.x;
     const int t = p.ntile_q - 1 - id / pairs;
@@ -242,23 +261,21 @@ __global__ __launch_bounds__(kThreads, 1) void diffattn_fwd_kernel(Params p)
         s0 = seq * p.seqlen_uniform;
         s1 = s0 + p.seqlen_uniform;
     }
-    const int qpw = kWaves / p.hpw;           // query blocks per workgroup
-    const int bm = kQW * qpw;                 // query rows per workgroup
+    const int qpw = kWaves / p.hpw;     // query blocks per workgroup
+    const int bm = kQW * qpw;           // query rows per workgroup
     const int q0 = s0 + t * bm;
     if (q0 >= s1)
         return;
     const int qhi = min(s1, q0 + bm);
 
     const int head = g * (p.H / p.Hkv) + hb * p.hpw + wave / qpw;
-    const int wq0 = q0 + (wave % qpw) * kQW;  // first query row of this wave
+    const int wq0 = q0 + (wave % qpw) * kQW;   // first query row of this wave
     const int wq_last = min(wq0 + kQW, s1) - 1;
-    const int tq = wq0 + n;                   // this lane's query token
+    const int tq = wq0 + n;                    // this lane's query token
 
     const E *__restrict__ qg = (const E *)p.q;
-    const E *__restrict__ kg = (const E *)p.k;
-    const E *__restrict__ vg = (const E *)p.v;
 
-    // ---- lambda (every wave computes the same scalar) --------------------
+    // ---- lambda (every wave computes the same scalar) ---------------------
     float lam;
     {
         float a = 0.f, b = 0.f;
@@ -288,10 +305,62 @@ __global__ __launch_bounds__(kThreads, 1) void diffattn_fwd_kernel(Params p)
             }
         }
 
-    // ---- running state ---------------------------------------------------
+    // ---- KV tile copies: per-lane source offsets (bytes) -------------------
+    // Copy i fills LDS slots [64 i, 64 i + 64) of 16 bytes of a tile; slot s
+    // holds chunk s % SPR of row s / SPR (chunks past the row's data are
+    // padding and get chunk 0 again).  Wave w issues copies w, w + 4, ...
+    const int rowstride = p.Hkv * GEO::ROWB;   // bytes between keys
+    // slot -> (row, byte offset inside the row's data); padding slots take
+    // chunk 0 of their row
+    auto slot_row = [&](int slot, int spr) { return slot / spr; };
+    auto slot_col = [&](int slot, int spr) {
+        const int ch = slot % spr;
+        return (ch < GEO::CPR ? ch : 0) * 16 + g * GEO::ROWB;
+    };
+    int kc_off[GEO::CPW], vc_off[GEO::CPW];   // source offsets of full tiles
+#pragma unroll
+    for (int j = 0; j < GEO::CPW; ++j) {
+        const int slot = (wave + kWaves * j) * 64 + lane;
+        kc_off[j] = slot_row(slot, GEO::KSPR) * rowstride + slot_col(slot, GEO::KSPR);
+        vc_off[j] = slot_row(slot, GEO::VSPR) * rowstride + slot_col(slot, GEO::VSPR);
+    }
+    const char *kbytes = (const char *)p.k;
+    const char *vbytes = (const char *)p.v;
+    auto issue_copy = [&](int k0, char *stage) {
+        // rows past the end of the sequence are clamped to its last row
+        const bool tail = k0 + kBN > s1;
+        const char *kb = kbytes + (int64_t)k0 * rowstride;
+        const char *vb = vbytes + (int64_t)k0 * rowstride;
+#pragma unroll
+        for (int j = 0; j < GEO::CPW; ++j) {
+            const int i = wave + kWaves * j;
+            const int slot = i * 64 + lane;
+            if (i < GEO::KCOPIES) {
+                int off = kc_off[j];
+                if (tail)
+                    off = min(slot_row(slot, GEO::KSPR), s1 - 1 - k0) * rowstride +
+                          slot_col(slot, GEO::KSPR);
+                __builtin_amdgcn_global_load_lds((gbl_void *)(kb + off),
+                                                 (lds_void *)(stage + 1024 * i), 16, 0, 0);
+            }
+            if (i < GEO::VCOPIES) {
+                int off = vc_off[j];
+                if (tail)
+                    off = min(slot_row(slot, GEO::VSPR), s1 - 1 - k0) * rowstride +
+                          slot_col(slot, GEO::VSPR);
+                __builtin_amdgcn_global_load_lds((gbl_void *)(vb + off),
+                                                 (lds_void *)(stage + GEO::KTILEB + 1024 * i),
+                                                 16, 0, 0);
+            }
+        }
+    };
+    const int k_lane = n * GEO::KROWB + h * VEC * (int)sizeof(E);
+    const int v_lane = VOperand<E, D>::lane_base(lane);
+
+    // ---- running state ----------------------------------------------------
     const float c = kLog2e / sqrtf((float)D);   // softmax scale in log2 units
-    float m_run[2] = {-INFINITY, -INFINITY};
-    float l_run[2] = {0.f, 0.f};
+    float m_run[2] = {-INFINITY, -INFINITY};    // raw-score units
+    float l_run[2] = {0.f, 0.f};                // this lane's partial sums
     f32x16 o[2][NDB];
 #pragma unroll
     for (int mp = 0; mp < 2; ++mp)
@@ -302,116 +371,112 @@ __global__ __launch_bounds__(kThreads, 1) void diffattn_fwd_kernel(Params p)
     const int kv_end = p.causal ? qhi : s1;
     const int ntiles = (kv_end - s0 + kBN - 1) / kBN;
 
-    Stage<E, D> st;
-    st.load(kg, vg, p.Hkv, g, s0, s1, tid);
-    st.store(smem, smem + L::K_ELEMS, tid);
+    issue_copy(s0, smem);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
     for (int it = 0; it < ntiles; ++it) {
         const int k0 = s0 + it * kBN;
-        E *ks_lds = smem + (it & 1) * L::STAGE;
-        E *vt_lds = ks_lds + L::K_ELEMS;
+        const char *kt = smem + (it & 1) * GEO::STAGEB + k_lane;
+        const char *vt = smem + (it & 1) * GEO::STAGEB + GEO::KTILEB + v_lane;
         if (it + 1 < ntiles)
-            st.load(kg, vg, p.Hkv, g, k0 + kBN, s1, tid);
+            issue_copy(k0 + kBN, smem + ((it + 1) & 1) * GEO::STAGEB);
 
-        // ---- S^T = K Q^T for both maps and both 32-key blocks -------------
-        f32x16 s[2][2];
-        bool live[2];
+        // The tile is consumed one 32-key block at a time: both maps' scores
+        // of the block, their softmax update, then both PV products sharing
+        // each V operand read.
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
             const int kb0 = k0 + 32 * b;
-            live[b] = kb0 < s1 && (!p.causal || kb0 <= wq_last);
+            // wave-uniform: can this wave see any key of the block, and does
+            // any key need the index mask?
+            if (kb0 >= s1 || (p.causal && kb0 > wq_last))
+                continue;
+            const bool masked = kb0 + 32 > s1 || (p.causal && kb0 + 31 > wq0);
+
+            // ---- S^T = K Q^T for both maps -------------------------------
+            f32x16 s[2];
 #pragma unroll
             for (int mp = 0; mp < 2; ++mp) {
-                s[mp][b] = f32x16{};
-                if (live[b]) {
-                    const E *arow = ks_lds + (32 * b + key_of_row(n)) * L::KROW + mp * D + h * VEC;
+                s[mp] = f32x16{};
 #pragma unroll
-                    for (int ks = 0; ks < NKS; ++ks) {
-                        Frag a = *(const Frag *)(arow + ks * KSTEP);
-                        s[mp][b] = M::mma(a, qf[mp][ks], s[mp][b]);
-                    }
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const int off = 32 * b * GEO::KROWB + (mp * D + ks * KSTEP) * (int)sizeof(E);
+                    const Frag a = *(const Frag *)(kt + off);
+                    s[mp] = M::mma(a, qf[mp][ks], s[mp]);
                 }
             }
-        }
 
-        // ---- mask: keys beyond the sequence, or after the query ----------
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const int kb0 = k0 + 32 * b;
-            const bool need = !live[b] || kb0 + 31 >= s1 || (p.causal && kb0 + 31 > wq0);
-            if (need) {
+            if (masked) {
 #pragma unroll
                 for (int a = 0; a < 16; ++a) {
-                    const int key = kb0 + key_of_acc(a, h);
-                    const bool ok = live[b] && key < s1 && (!p.causal || key <= tq);
-                    if (!ok) {
-                        s[0][b][a] = -INFINITY;
-                        s[1][b][a] = -INFINITY;
+                    const int key = kb0 + acc_row(a, h);
+                    if (key >= s1 || (p.causal && key > tq)) {
+                        s[0][a] = -INFINITY;
+                        s[1][a] = -INFINITY;
                     }
                 }
             }
-        }
 
-        // ---- two independent online-softmax updates ----------------------
+            // ---- two independent online-softmax updates (lazy maximum) ----
 #pragma unroll
-        for (int mp = 0; mp < 2; ++mp) {
-            float mt = -INFINITY;
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
+            for (int mp = 0; mp < 2; ++mp) {
+                float pm = -INFINITY;
 #pragma unroll
                 for (int a = 0; a < 16; ++a)
-                    mt = fmaxf(mt, s[mp][b][a]);
-            mt = fmaxf(mt, xor32(mt));
-            const float mnew = fmaxf(m_run[mp], mt);
-            const bool fin = mnew != -INFINITY;
-            const float alpha = fin ? __builtin_amdgcn_exp2f((m_run[mp] - mnew) * c) : 1.f;
-            const float mc = fin ? mnew * c : 0.f;
-            m_run[mp] = mnew;
-            float rs = 0.f;
+                    pm = fmaxf(pm, s[mp][a]);
+                const bool grow = (pm - m_run[mp]) * c > kRescaleLog2;
+                if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+                    const float mold = m_run[mp];
+                    const float mnew = fmaxf(mold, pair_max(pm));
+                    float alpha;
+                    if (mold == -INFINITY)
+                        alpha = 0.f;          // nothing accumulated yet
+                    else
+                        alpha = __builtin_amdgcn_exp2f((mold - mnew) * c);
+                    m_run[mp] = mnew;
+                    l_run[mp] *= alpha;
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
+                    for (int db = 0; db < NDB; ++db)
+                        o[mp][db] *= alpha;
+                }
+                // every row has a visible key in its first block, so m_run is
+                // finite from here on
+                const float mc = m_run[mp] * c;
+                float rs = 0.f;
 #pragma unroll
                 for (int a = 0; a < 16; ++a) {
-                    const float pv = __builtin_amdgcn_exp2f(s[mp][b][a] * c - mc);
-                    s[mp][b][a] = pv;
+                    const float pv = __builtin_amdgcn_exp2f(fmaf(s[mp][a], c, -mc));
+                    s[mp][a] = pv;
                     rs += pv;
                 }
-            l_run[mp] = l_run[mp] * alpha + rs;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-                o[mp][db] *= alpha;
-        }
+                l_run[mp] += rs;
+            }
 
-        // ---- O^T += V^T P^T ---------------------------------------------
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            if (!live[b])
-                continue;
+            // ---- O^T += V^T P^T ------------------------------------------
 #pragma unroll
             for (int ps = 0; ps < NPS; ++ps) {
-                const int a0 = ps * VEC;
-                const Frag p1 = M::pack(s[0][b], a0);
-                const Frag p2 = M::pack(s[1][b], a0);
-                const E *vcol = vt_lds + 32 * b + key_of_acc(a0, h);
+                const Frag p1 = M::pack(s[0], ps * VEC);
+                const Frag p2 = M::pack(s[1], ps * VEC);
+                // first key row of this step (the lane part is in v_lane)
+                const int row = VEC == 8 ? 32 * b + 16 * ps
+                                         : 32 * b + 8 * (ps / 4) + (ps % 4);
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
-                    const Frag vf = *(const Frag *)(vcol + (32 * db + n) * L::VROW);
+                    const Frag vf = VOperand<E, D>::load(vt, row, db);
                     o[0][db] = M::mma(vf, p1, o[0][db]);
                     o[1][db] = M::mma(vf, p2, o[1][db]);
                 }
             }
         }
 
-        if (it + 1 < ntiles)
-            st.store(smem + ((it + 1) & 1) * L::STAGE,
-                     smem + ((it + 1) & 1) * L::STAGE + L::K_ELEMS, tid);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     }
 
-    // ---- epilogue: combine, RMSNorm, scale, store -------------------------
-    const float l1 = l_run[0] + xor32(l_run[0]);
-    const float l2 = l_run[1] + xor32(l_run[1]);
+    // ---- epilogue: combine, RMSNorm, scale, store --------------------------
+    const float l1 = pair_sum(l_run[0]);
+    const float l2 = pair_sum(l_run[1]);
     const float i1 = 1.f / l1;
     const float i2 = lam / l2;
     float ss = 0.f;
@@ -423,10 +488,29 @@ __global__ __launch_bounds__(kThreads, 1) void diffattn_fwd_kernel(Params p)
             o[0][db][a] = pre;
             ss += pre * pre;
         }
-    ss += xor32(ss);
+    ss = pair_sum(ss);
     const float r = (1.f - p.lambda_init) / sqrtf(ss / (float)(2 * D) + p.eps);
     if (tq < s1) {
         E *dst = (E *)p.out + ((int64_t)tq * p.H + head) * (2 * D);
+        // weight: one wave-uniform branch, not one per element
+        float wv[NDB][16];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int a = 0; a < 16; ++a)
+                wv[db][a] = r;
+        if (p.w) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float4 w4 = *(const float4 *)(p.w + 32 * db + 8 * i + 4 * h);
+                    wv[db][4 * i + 0] *= w4.x;
+                    wv[db][4 * i + 1] *= w4.y;
+                    wv[db][4 * i + 2] *= w4.z;
+                    wv[db][4 * i + 3] *= w4.w;
+                }
+        }
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -434,10 +518,8 @@ __global__ __launch_bounds__(kThreads, 1) void diffattn_fwd_kernel(Params p)
                 const int dim = 32 * db + 8 * i + 4 * h;
                 E vals[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float wv = p.w ? p.w[dim + j] : 1.f;
-                    vals[j] = (E)(o[0][db][4 * i + j] * r * wv);
-                }
+                for (int j = 0; j < 4; ++j)
+                    vals[j] = (E)(o[0][db][4 * i + j] * wv[db][4 * i + j]);
                 __builtin_memcpy(dst + dim, vals, sizeof(vals));
             }
     }
@@ -526,7 +608,8 @@ int diffattn_fwd(int dtype, const void *q, const void *k, const void *v,
     if (!q || !k || !v || !out || !lambda_q1 || !lambda_k1 || !lambda_q2 || !lambda_k2)
         return DIFFATTN_EINVAL;
     // q, k, v and out are read and written in 16-byte vectors
-    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) % 16 != 0)
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out |
+         (uintptr_t)subln_weight) % 16 != 0)
         return DIFFATTN_EINVAL;
     if (nseq < 1)
         return DIFFATTN_EINVAL;
@@ -542,7 +625,7 @@ int diffattn_fwd(int dtype, const void *q, const void *k, const void *v,
     } else if (max_seqlen < 1 || max_seqlen > T) {
         return DIFFATTN_EINVAL;
     }
-    // element offsets of q/out rows stay within int64; the grid within int32
+    // byte offsets of K/V rows are formed in 64 bits; the grid in 32 bits
     const int G = H / Hkv;
     const int hpw = (G % 4 == 0) ? 4 : (G % 2 == 0 ? 2 : 1);
     const int bm = kQW * (kWaves / hpw);

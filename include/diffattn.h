@@ -66,7 +66,8 @@ enum diffattn_dtype {
  *                (the Llama gist and alternative_forward share it; the
  *                DiffTransformer page keeps one set per head).
  *   lambda_init  the layer's initial lambda (see diffattn_lambda_init).
- *   subln_weight device fp32 [2d] RMSNorm weight, or NULL for all ones.
+ *   subln_weight device fp32 [2d] RMSNorm weight (16-byte aligned), or NULL
+ *                for all ones.
  *   eps          RMSNorm epsilon (1e-5 on the DiffTransformer page); >= 0.
  *   causal       1: query i sees keys j <= i of its sequence; 0: all keys of
  *                its sequence.
