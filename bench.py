@@ -88,13 +88,40 @@ def cpu_baseline(wl, inp):
                        "oracle, OpenMP over rows")}
 
 
+def copy_calibration(args) -> int:
+    """A plain device-to-device copy of known size, for scaling the HBM byte
+    counters (FETCH_SIZE, WRITE_SIZE) of the kernel under a profiler."""
+    import torch
+    dev = torch.device("cuda:0")
+    a = torch.ones(args.copy_bytes, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(args.warmup):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(args.steps):
+        b.copy_(a)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    print(json.dumps({"copy_bytes": args.copy_bytes, "ms_per_copy": round(ms, 4),
+                      "GB_per_s_read_plus_write": round(2 * args.copy_bytes / ms / 1e6, 1)}),
+          flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="instead of the workload, time a plain device copy of "
+                         "this many bytes (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only (the forward kernel "
@@ -103,6 +130,8 @@ def main() -> int:
         return 2
 
     import torch
+    if args.copy_bytes > 0:
+        return copy_calibration(args)
     import workloads
     import differential_attention_amd as da
 

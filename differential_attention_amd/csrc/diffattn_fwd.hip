@@ -6,27 +6,34 @@
 //
 // Kernel design
 // -------------
-// One workgroup = 4 waves (one per SIMD) = one KV head g, a block of heads of
-// that group and a block of query tokens of one packed sequence:
-//   G % 4 == 0 : 4 heads  x 32 queries (each wave one head)
-//   G % 2 == 0 : 2 heads  x 64 queries
-//   otherwise  : 1 head   x 128 queries
-// Every wave owns 32 query rows of one head and keeps, for both maps, the
-// running row maximum, the running sum and a 32 x 2d fp32 accumulator, so
-// the two softmax recurrences are fully independent.  The register budget
-// is 256 per lane, so two workgroups share a CU: while one wave of a SIMD
-// runs its MFMAs the other runs its softmax.
+// One workgroup = 8 waves = one KV head g, a block of heads of that group
+// and a block of query tokens of one packed sequence.  The four "slots" of
+// a workgroup are (head, 64 queries) pairs:
+//   G % 4 == 0 : 4 heads  x  64 queries
+//   G % 2 == 0 : 2 heads  x 128 queries
+//   otherwise  : 1 head   x 256 queries
+// and every slot is served by two waves, one per attention map: wave w
+// computes map (w / 4) of slot (w % 4) for its 64 queries, as two 32-query
+// sub-blocks.  Each K operand read and each V operand read of a wave feeds
+// two MFMAs (one per sub-block), and each K/V tile staged in LDS serves
+// 256 query rows of the GQA group: LDS traffic per MFMA is what bounds this
+// kernel on gfx950 (the transposing V read runs at half the LDS rate).  A
+// wave keeps, per sub-block, one running row maximum, one running sum and a
+// 32 x 2d fp32 accumulator of its map; the combine O_1/l_1 - lambda O_2/l_2
+// happens once, in the epilogue, through LDS.  Two waves per SIMD (256
+// registers each) interleave their MFMA and softmax phases.
 //
-// The workgroup streams the KV range of its sequence in tiles of 64 keys.
-// K (both halves) and V of a tile are copied global -> LDS directly
-// (global_load_lds, 16 bytes per lane, no registers), row-major with an XOR
-// swizzle of the 16-byte chunks, double-buffered: the copy of tile t+1 is in
-// flight while tile t is computed; one barrier per tile.  K/V of a GQA group
-// enter LDS once per 32..128 query rows and are never copied per head.
+// The workgroup streams the KV range of its sequence in tiles of 128 keys
+// (64 where two stages of 128 would not fit LDS).  K (both halves) and V of
+// a tile are staged into padded row-major LDS tiles, double-buffered: tile
+// t+1 moves global -> registers -> LDS in slices, one per 32-key block of
+// tile t, so its loads are in flight while tile t is computed; one barrier
+// per tile.  (Direct global -> LDS copies were measured slower on this part:
+// their transfer path costs more than 16-byte LDS writes.)
 //
-// All four contractions run on MFMA (v_mfma_f32_32x32x16_bf16 for bf16,
+// All contractions run on MFMA (v_mfma_f32_32x32x16_bf16 for bf16,
 // v_mfma_f32_32x32x2_f32 for fp32), in transposed form:
-//   S_m^T [keys x queries] = K_m [keys x d] * Q_m^T      (m = 1, 2)
+//   S_m^T [keys x queries] = K_m [keys x d] * Q_m^T
 //   O_m^T [2d  x queries] += V^T [2d x keys] * P_m^T
 // With S^T each lane owns one query column and 16 keys of every 32-key
 // block: row maxima and sums are in-lane plus one cross-half exchange, and
@@ -36,15 +43,15 @@
 // (fp32).
 //
 // Softmax uses a lazily updated running maximum: probabilities are taken
-// against the stored maximum as long as no score of the tile exceeds it by
-// more than 2^8 in probability; only then (in practice on the first tile)
-// the maximum, the sums and the accumulators are rescaled.  The result O/l
+// against the stored maximum as long as no score of the block exceeds it by
+// more than 2^8 in probability; only then (in practice on the first block)
+// the maximum, the sum and the accumulator are rescaled.  The result O/l
 // does not depend on which maximum was used.
 //
-// The epilogue is fused: lambda (computed per wave from the four vectors),
-// O_1/l_1 - lambda O_2/l_2, the RMSNorm over 2d (in-lane sums plus one
-// cross-half exchange), the weight, the (1 - lambda_init) scale and the
-// rounding store.  Causal tiles above the diagonal are never visited; on the
+// The epilogue is fused: lambda (from the four vectors), O_1/l_1 -
+// lambda O_2/l_2, the RMSNorm over 2d (in-lane sums plus one cross-half
+// exchange), the weight, the (1 - lambda_init) scale and the rounding
+// store.  Causal tiles above the diagonal are never visited; on the
 // diagonal, 32-key blocks a wave cannot see are skipped and the rest are
 // masked by index.  Workgroups are numbered longest-first (largest query
 // tile index first) so the causal tail is short.
@@ -61,13 +68,13 @@ typedef __bf16 bf16;
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) const void gbl_void;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;    // two maps x four slots
+constexpr int kSlots = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBN = 64;   // keys per KV tile
-constexpr int kQW = 32;   // query rows per wave
+constexpr int kSub = 2;   // 32-query sub-blocks per wave
+constexpr int kQB = 32 * kSub;   // query rows per slot
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleLog2 = 8.0f;   // lazy-max threshold, log2 units
 
@@ -80,24 +87,20 @@ constexpr float kRescaleLog2 = 8.0f;   // lazy-max threshold, log2 units
 //     one column start 16 bytes apart modulo 256;
 //   V rows (bf16) are ROWB + 64 bytes apart: the 4 rows x 64 bytes one
 //     half-wave of a transposing read touches tile all 256 bytes of banks.
-// The tiles are filled by direct global->LDS copies of 64 lanes x 16 bytes
-// (1 KiB contiguous per copy); padding slots receive a harmless duplicate.
+// The tiles are filled through registers (16-byte global loads, 16-byte LDS
+// writes), so the padding is never transferred.
 template <typename E, int D> struct Geo {
     static constexpr int ES = (int)sizeof(E);
     static constexpr int ROWB = 2 * D * ES;                 // data bytes per row
     static constexpr int CPR = ROWB / 16;                   // data chunks per row
     static constexpr int KROWB = ROWB + 16;
     static constexpr int VROWB = ROWB + (ES == 2 ? 64 : 16);
-    static constexpr int KSPR = KROWB / 16;                 // slots per K row
-    static constexpr int VSPR = VROWB / 16;
-    static constexpr int KTILEB = kBN * KROWB;
-    static constexpr int VTILEB = kBN * VROWB;
-    static constexpr int KCOPIES = KTILEB / 1024;           // 1 KiB copies
-    static constexpr int VCOPIES = VTILEB / 1024;
-    static constexpr int STAGEB = KTILEB + VTILEB;
-    static constexpr int MAXC = (KCOPIES > VCOPIES ? KCOPIES : VCOPIES);
-    static constexpr int CPW = (MAXC + kWaves - 1) / kWaves; // copies per wave
-    static_assert(KCOPIES * 1024 == KTILEB && VCOPIES * 1024 == VTILEB, "copy tiling");
+    // keys per tile: 128 when two stages of that size fit the 160 KiB LDS
+    static constexpr int BN = 2 * 128 * (KROWB + VROWB) <= 160 * 1024 ? 128 : 64;
+    static constexpr int NB = BN / 32;                      // 32-key blocks per tile
+    static constexpr int KTILEB = BN * KROWB;
+    static constexpr int VTILEB = BN * VROWB;
+    static constexpr int STAGEB = KTILEB + VTILEB;          // K tile, then V tile
 };
 
 // ---------------------------------------------------------------------------
@@ -214,15 +217,10 @@ struct Params {
     int32_t hblocks;   // head blocks per KV group: G / hpw
 };
 
-// Waves per SIMD the register budget is cut for: two (two workgroups per CU)
-// wherever the double-buffered tiles leave room for a second workgroup in LDS.
-template <typename E, int D> struct Occupancy {
-    static constexpr int value = 2 * Geo<E, D>::STAGEB * 2 <= 160 * 1024 ? 2 : 1;
-};
-
+// Every CU runs one workgroup of 8 waves (two per SIMD); the register
+// budget per lane is the 256 that two waves per SIMD leave.
 template <typename E, int D>
-__global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(Occupancy<E, D>::value, Occupancy<E, D>::value)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void diffattn_fwd_kernel(Params p)
 {
     typedef Geo<E, D> GEO;
@@ -234,14 +232,23 @@ void diffattn_fwd_kernel(Params p)
     constexpr int NDB = 2 * D / 32;     // 32-wide blocks of the output
     constexpr int NPS = 32 / KSTEP;     // PV steps per 32-key block
     static_assert(D % KSTEP == 0 && (2 * D) % 32 == 0, "unsupported d");
+    // epilogue exchange: two slots per stage object, NSUB x NDB x 16 x 64
+    // floats each
+    constexpr int XCH = kSub * NDB * 16 * 64;
+    static_assert(2 * XCH * 4 <= GEO::STAGEB, "exchange must fit a stage");
 
-    __shared__ __attribute__((aligned(1024))) char smem[2 * GEO::STAGEB];
+    // two distinct LDS objects for the two stages, so the compiler can see
+    // that reads of one never alias writes into the other
+    __shared__ __attribute__((aligned(1024))) char stage0[GEO::STAGEB];
+    __shared__ __attribute__((aligned(1024))) char stage1[GEO::STAGEB];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
-    const int n = lane & 31;   // query column owned by this lane
-    const int h = lane >> 5;   // lane half
+    const int n = lane & 31;           // query column owned by this lane
+    const int h = lane >> 5;           // lane half
+    const int slot = wave % kSlots;    // (head, query block) served
+    const int map = wave / kSlots;     // 0: map 1 (Q1, K1), 1: map 2 (Q2, K2)
 
     // ---- tile scheduler: longest query tiles first ------------------------
     const int pairs = p.nseq * p.Hkv * p.hblocks;
@@ -261,132 +268,123 @@ void diffattn_fwd_kernel(Params p)
         s0 = seq * p.seqlen_uniform;
         s1 = s0 + p.seqlen_uniform;
     }
-    const int qpw = kWaves / p.hpw;     // query blocks per workgroup
-    const int bm = kQW * qpw;           // query rows per workgroup
+    const int qpw = kSlots / p.hpw;     // query blocks per workgroup
+    const int bm = kQB * qpw;           // query rows per workgroup
     const int q0 = s0 + t * bm;
     if (q0 >= s1)
         return;
     const int qhi = min(s1, q0 + bm);
 
-    const int head = g * (p.H / p.Hkv) + hb * p.hpw + wave / qpw;
-    const int wq0 = q0 + (wave % qpw) * kQW;   // first query row of this wave
-    const int wq_last = min(wq0 + kQW, s1) - 1;
-    const int tq = wq0 + n;                    // this lane's query token
+    const int head = g * (p.H / p.Hkv) + hb * p.hpw + slot / qpw;
+    const int wq0 = q0 + (slot % qpw) * kQB;   // first query row of this slot
+    const int wq_last = min(wq0 + kQB, s1) - 1;
 
-    const E *__restrict__ qg = (const E *)p.q;
-
-    // ---- lambda (every wave computes the same scalar) ---------------------
-    float lam;
+    // ---- Q fragments of this wave's map (B operand of S^T = K Q^T) --------
+    // sub-block u holds queries wq0 + 32 u + n
+    Frag qf[kSub][NKS];
     {
-        float a = 0.f, b = 0.f;
-        for (int c = lane; c < D; c += 64) {
-            a += p.lq1[c] * p.lk1[c];
-            b += p.lq2[c] * p.lk2[c];
-        }
+        const E *__restrict__ qg = (const E *)p.q;
 #pragma unroll
-        for (int off = 32; off >= 1; off /= 2) {
-            a += __shfl_xor(a, off, 64);
-            b += __shfl_xor(b, off, 64);
-        }
-        lam = expf(a) - expf(b) + p.lambda_init;
+        for (int u = 0; u < kSub; ++u)
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const int tq = wq0 + 32 * u + n;
+                if (tq < s1) {
+                    const E *src = qg + (((int64_t)tq * p.H + head) * 2 + map) * D + ks * KSTEP + h * VEC;
+                    qf[u][ks] = *(const Frag *)src;
+                } else {
+                    qf[u][ks] = Frag{};
+                }
+            }
     }
 
-    // ---- Q fragments (B operand of S^T = K Q^T), kept in registers --------
-    Frag qf[2][NKS];
+    // ---- KV tile staging ---------------------------------------------------
+    // A tile's K rows (and V rows) move in loads of 64 lanes x 16 bytes = RPL
+    // consecutive rows: load L covers rows [L RPL, L RPL + RPL), lane l row
+    // L RPL + l / CPR and 16-byte chunk l % CPR.  Wave w moves loads w,
+    // w + 8, ...: LPW per tensor and tile.  While 32-key block b of tile t is
+    // computed, the slice of loads assigned to block b of tile t + 1 travels
+    // global -> registers; it is written registers -> LDS (into the padded
+    // rows) during block b + 1, so each load has a block's time to arrive.
+    constexpr int RPL = 1024 / GEO::ROWB;          // rows per load
+    constexpr int NLT = GEO::BN / RPL;             // loads per tensor per tile
+    constexpr int LPW = NLT / kWaves;              // loads per wave
+    constexpr int MAXL = (LPW + GEO::NB - 1) / GEO::NB;
+    static_assert(RPL * GEO::ROWB == 1024 && LPW * kWaves == NLT, "staging tiling");
+    const int rowstride = p.Hkv * GEO::ROWB;       // bytes between keys
+    const int lrow = wave * RPL + lane / GEO::CPR; // row of load 0
+    const int lcol = (lane % GEO::CPR) * 16;
+    const char *kbytes = (const char *)p.k + g * GEO::ROWB + lcol;
+    const char *vbytes = (const char *)p.v + g * GEO::ROWB + lcol;
+    const int kdst = lrow * GEO::KROWB + lcol;
+    const int vdst = GEO::KTILEB + lrow * GEO::VROWB + lcol;
+    u32x4 kst[MAXL], vst[MAXL];
+    // global -> registers: this wave's loads of block slice b of the tile at k0
+    auto stage_load = [&](int k0, int b) __attribute__((always_inline)) {
+        const bool tail = k0 + GEO::BN > s1;
 #pragma unroll
-    for (int mp = 0; mp < 2; ++mp)
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            if (tq < s1) {
-                const E *src = qg + (((int64_t)tq * p.H + head) * 2 + mp) * D + ks * KSTEP + h * VEC;
-                qf[mp][ks] = *(const Frag *)src;
-            } else {
-                qf[mp][ks] = Frag{};
-            }
-        }
-
-    // ---- KV tile copies: per-lane source offsets (bytes) -------------------
-    // Copy i fills LDS slots [64 i, 64 i + 64) of 16 bytes of a tile; slot s
-    // holds chunk s % SPR of row s / SPR (chunks past the row's data are
-    // padding and get chunk 0 again).  Wave w issues copies w, w + 4, ...
-    const int rowstride = p.Hkv * GEO::ROWB;   // bytes between keys
-    // slot -> (row, byte offset inside the row's data); padding slots take
-    // chunk 0 of their row
-    auto slot_row = [&](int slot, int spr) { return slot / spr; };
-    auto slot_col = [&](int slot, int spr) {
-        const int ch = slot % spr;
-        return (ch < GEO::CPR ? ch : 0) * 16 + g * GEO::ROWB;
-    };
-    int kc_off[GEO::CPW], vc_off[GEO::CPW];   // source offsets of full tiles
-#pragma unroll
-    for (int j = 0; j < GEO::CPW; ++j) {
-        const int slot = (wave + kWaves * j) * 64 + lane;
-        kc_off[j] = slot_row(slot, GEO::KSPR) * rowstride + slot_col(slot, GEO::KSPR);
-        vc_off[j] = slot_row(slot, GEO::VSPR) * rowstride + slot_col(slot, GEO::VSPR);
-    }
-    const char *kbytes = (const char *)p.k;
-    const char *vbytes = (const char *)p.v;
-    auto issue_copy = [&](int k0, char *stage) {
-        // rows past the end of the sequence are clamped to its last row
-        const bool tail = k0 + kBN > s1;
-        const char *kb = kbytes + (int64_t)k0 * rowstride;
-        const char *vb = vbytes + (int64_t)k0 * rowstride;
-#pragma unroll
-        for (int j = 0; j < GEO::CPW; ++j) {
-            const int i = wave + kWaves * j;
-            const int slot = i * 64 + lane;
-            if (i < GEO::KCOPIES) {
-                int off = kc_off[j];
-                if (tail)
-                    off = min(slot_row(slot, GEO::KSPR), s1 - 1 - k0) * rowstride +
-                          slot_col(slot, GEO::KSPR);
-                __builtin_amdgcn_global_load_lds((gbl_void *)(kb + off),
-                                                 (lds_void *)(stage + 1024 * i), 16, 0, 0);
-            }
-            if (i < GEO::VCOPIES) {
-                int off = vc_off[j];
-                if (tail)
-                    off = min(slot_row(slot, GEO::VSPR), s1 - 1 - k0) * rowstride +
-                          slot_col(slot, GEO::VSPR);
-                __builtin_amdgcn_global_load_lds((gbl_void *)(vb + off),
-                                                 (lds_void *)(stage + GEO::KTILEB + 1024 * i),
-                                                 16, 0, 0);
-            }
+        for (int i = b * LPW / GEO::NB; i < (b + 1) * LPW / GEO::NB; ++i) {
+            int key = k0 + lrow + i * kWaves * RPL;
+            if (tail)   // rows past the sequence repeat its last row
+                key = min(key, s1 - 1);
+            const int64_t off = (int64_t)key * rowstride;
+            kst[i - b * LPW / GEO::NB] = *(const u32x4 *)(kbytes + off);
+            vst[i - b * LPW / GEO::NB] = *(const u32x4 *)(vbytes + off);
         }
     };
-    const int k_lane = n * GEO::KROWB + h * VEC * (int)sizeof(E);
+    // registers -> LDS stage
+    auto stage_store = [&](char *stage, int b) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = b * LPW / GEO::NB; i < (b + 1) * LPW / GEO::NB; ++i) {
+            *(u32x4 *)(stage + kdst + i * kWaves * RPL * GEO::KROWB) = kst[i - b * LPW / GEO::NB];
+            *(u32x4 *)(stage + vdst + i * kWaves * RPL * GEO::VROWB) = vst[i - b * LPW / GEO::NB];
+        }
+    };
+    // this lane's part of its K operand address (row n, map half, lane half)
+    const int k_lane = n * GEO::KROWB + (map * D + h * VEC) * (int)sizeof(E);
     const int v_lane = VOperand<E, D>::lane_base(lane);
 
-    // ---- running state ----------------------------------------------------
+    // ---- running state of this wave's map, per query sub-block ------------
     const float c = kLog2e / sqrtf((float)D);   // softmax scale in log2 units
-    float m_run[2] = {-INFINITY, -INFINITY};    // raw-score units
-    float l_run[2] = {0.f, 0.f};                // this lane's partial sums
-    f32x16 o[2][NDB];
+    float m_run[kSub], l_run[kSub];             // raw-score units; partial sums
+    f32x16 o[kSub][NDB];
 #pragma unroll
-    for (int mp = 0; mp < 2; ++mp)
+    for (int u = 0; u < kSub; ++u) {
+        m_run[u] = -INFINITY;
+        l_run[u] = 0.f;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
-            o[mp][db] = f32x16{};
+            o[u][db] = f32x16{};
+    }
 
     const int kv_end = p.causal ? qhi : s1;
-    const int ntiles = (kv_end - s0 + kBN - 1) / kBN;
+    const int ntiles = (kv_end - s0 + GEO::BN - 1) / GEO::BN;
 
-    issue_copy(s0, smem);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int b = 0; b < GEO::NB; ++b) {
+        stage_load(s0, b);
+        stage_store(stage0, b);
+    }
     __syncthreads();
 
-    for (int it = 0; it < ntiles; ++it) {
-        const int k0 = s0 + it * kBN;
-        const char *kt = smem + (it & 1) * GEO::STAGEB + k_lane;
-        const char *vt = smem + (it & 1) * GEO::STAGEB + GEO::KTILEB + v_lane;
-        if (it + 1 < ntiles)
-            issue_copy(k0 + kBN, smem + ((it + 1) & 1) * GEO::STAGEB);
+    // One tile: compute from `cur` while the next tile is staged into `nxt`.
+    auto tile = [&](int it, const char *cur, char *nxt) __attribute__((always_inline)) {
+        const int k0 = s0 + it * GEO::BN;
+        const char *kt = cur + k_lane;
+        const char *vt = cur + GEO::KTILEB + v_lane;
+        const bool more = it + 1 < ntiles;
 
-        // The tile is consumed one 32-key block at a time: both maps' scores
-        // of the block, their softmax update, then both PV products sharing
-        // each V operand read.
+        // The tile is consumed one 32-key block at a time: the block's
+        // scores for both query sub-blocks, their softmax updates, then the
+        // PV products, each V operand read serving both sub-blocks.
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
+        for (int b = 0; b < GEO::NB; ++b) {
+            // staging of the next tile, one slice per block
+            if (more) {
+                if (b > 0)
+                    stage_store(nxt, b - 1);
+                stage_load(k0 + GEO::BN, b);
+            }
             const int kb0 = k0 + 32 * b;
             // wave-uniform: can this wave see any key of the block, and does
             // any key need the index mask?
@@ -394,134 +392,179 @@ void diffattn_fwd_kernel(Params p)
                 continue;
             const bool masked = kb0 + 32 > s1 || (p.causal && kb0 + 31 > wq0);
 
-            // ---- S^T = K Q^T for both maps -------------------------------
-            f32x16 s[2];
+            // ---- S^T = K Q^T ------------------------------------------------
+            Frag ka[NKS];
 #pragma unroll
-            for (int mp = 0; mp < 2; ++mp) {
-                s[mp] = f32x16{};
+            for (int ks = 0; ks < NKS; ++ks)
+                ka[ks] = *(const Frag *)(kt + 32 * b * GEO::KROWB + ks * KSTEP * (int)sizeof(E));
+            f32x16 sc[kSub];
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    const int off = 32 * b * GEO::KROWB + (mp * D + ks * KSTEP) * (int)sizeof(E);
-                    const Frag a = *(const Frag *)(kt + off);
-                    s[mp] = M::mma(a, qf[mp][ks], s[mp]);
-                }
+            for (int u = 0; u < kSub; ++u) {
+                sc[u] = f32x16{};
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+                    sc[u] = M::mma(ka[ks], qf[u][ks], sc[u]);
             }
 
             if (masked) {
 #pragma unroll
-                for (int a = 0; a < 16; ++a) {
-                    const int key = kb0 + acc_row(a, h);
-                    if (key >= s1 || (p.causal && key > tq)) {
-                        s[0][a] = -INFINITY;
-                        s[1][a] = -INFINITY;
+                for (int u = 0; u < kSub; ++u) {
+                    const int tq = wq0 + 32 * u + n;
+#pragma unroll
+                    for (int a = 0; a < 16; ++a) {
+                        const int key = kb0 + acc_row(a, h);
+                        if (key >= s1 || (p.causal && key > tq))
+                            sc[u][a] = -INFINITY;
                     }
                 }
             }
 
-            // ---- two independent online-softmax updates (lazy maximum) ----
+            // ---- online softmax with a lazily raised maximum ---------------
+            // (a query row whose keys of this block are all masked keeps its
+            // maximum: its first block always has a visible key)
+            Frag pf[kSub][NPS];
 #pragma unroll
-            for (int mp = 0; mp < 2; ++mp) {
+            for (int u = 0; u < kSub; ++u) {
                 float pm = -INFINITY;
 #pragma unroll
                 for (int a = 0; a < 16; ++a)
-                    pm = fmaxf(pm, s[mp][a]);
-                const bool grow = (pm - m_run[mp]) * c > kRescaleLog2;
+                    pm = fmaxf(pm, sc[u][a]);
+                const bool grow = (pm - m_run[u]) * c > kRescaleLog2;
                 if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-                    const float mold = m_run[mp];
-                    const float mnew = fmaxf(mold, pair_max(pm));
-                    float alpha;
-                    if (mold == -INFINITY)
-                        alpha = 0.f;          // nothing accumulated yet
-                    else
-                        alpha = __builtin_amdgcn_exp2f((mold - mnew) * c);
-                    m_run[mp] = mnew;
-                    l_run[mp] *= alpha;
+                    const float mnew = fmaxf(m_run[u], pair_max(pm));
+                    // nothing accumulated yet when m_run is still -inf
+                    const float alpha = m_run[u] == -INFINITY
+                                            ? 0.f
+                                            : __builtin_amdgcn_exp2f((m_run[u] - mnew) * c);
+                    m_run[u] = mnew;
+                    l_run[u] *= alpha;
 #pragma unroll
                     for (int db = 0; db < NDB; ++db)
-                        o[mp][db] *= alpha;
+                        o[u][db] *= alpha;
                 }
-                // every row has a visible key in its first block, so m_run is
-                // finite from here on
-                const float mc = m_run[mp] * c;
-                float rs = 0.f;
+                const float mc = m_run[u] * c;
+                float ps_sum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int a = 0; a < 16; ++a) {
-                    const float pv = __builtin_amdgcn_exp2f(fmaf(s[mp][a], c, -mc));
-                    s[mp][a] = pv;
-                    rs += pv;
+                    const float pv = __builtin_amdgcn_exp2f(fmaf(sc[u][a], c, -mc));
+                    sc[u][a] = pv;
+                    ps_sum[a & 3] += pv;
                 }
-                l_run[mp] += rs;
+                l_run[u] += (ps_sum[0] + ps_sum[1]) + (ps_sum[2] + ps_sum[3]);
+#pragma unroll
+                for (int ps = 0; ps < NPS; ++ps)
+                    pf[u][ps] = M::pack(sc[u], ps * VEC);
             }
 
-            // ---- O^T += V^T P^T ------------------------------------------
+            // ---- O^T += V^T P^T ---------------------------------------------
 #pragma unroll
             for (int ps = 0; ps < NPS; ++ps) {
-                const Frag p1 = M::pack(s[0], ps * VEC);
-                const Frag p2 = M::pack(s[1], ps * VEC);
                 // first key row of this step (the lane part is in v_lane)
                 const int row = VEC == 8 ? 32 * b + 16 * ps
                                          : 32 * b + 8 * (ps / 4) + (ps % 4);
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
                     const Frag vf = VOperand<E, D>::load(vt, row, db);
-                    o[0][db] = M::mma(vf, p1, o[0][db]);
-                    o[1][db] = M::mma(vf, p2, o[1][db]);
+#pragma unroll
+                    for (int u = 0; u < kSub; ++u)
+                        o[u][db] = M::mma(vf, pf[u][ps], o[u][db]);
                 }
             }
         }
 
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (more)
+            stage_store(nxt, GEO::NB - 1);
         __syncthreads();
+    };
+    for (int it = 0; it < ntiles; it += 2) {
+        tile(it, stage0, stage1);
+        if (it + 1 < ntiles)
+            tile(it + 1, stage1, stage0);
     }
 
-    // ---- epilogue: combine, RMSNorm, scale, store --------------------------
-    const float l1 = pair_sum(l_run[0]);
-    const float l2 = pair_sum(l_run[1]);
-    const float i1 = 1.f / l1;
-    const float i2 = lam / l2;
-    float ss = 0.f;
+    // ---- epilogue: combine through LDS, RMSNorm, scale, store -------------
+    // Map-2 waves publish lambda * O_2 / l_2 in their own accumulator layout;
+    // the map-1 wave of the same slot, whose lanes hold the same (query, dim)
+    // elements, subtracts it from O_1 / l_1.
+    float *xch = (float *)((slot < 2 ? stage0 : stage1)) + (slot & 1) * XCH;
+    float lsum[kSub];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int a = 0; a < 16; ++a) {
-            const float pre = o[0][db][a] * i1 - o[1][db][a] * i2;
-            o[0][db][a] = pre;
-            ss += pre * pre;
+    for (int u = 0; u < kSub; ++u)
+        lsum[u] = pair_sum(l_run[u]);
+    if (map == 1) {
+        float a = 0.f, b = 0.f;
+        for (int cc = lane; cc < D; cc += 64) {
+            a += p.lq1[cc] * p.lk1[cc];
+            b += p.lq2[cc] * p.lk2[cc];
         }
-    ss = pair_sum(ss);
-    const float r = (1.f - p.lambda_init) / sqrtf(ss / (float)(2 * D) + p.eps);
-    if (tq < s1) {
-        E *dst = (E *)p.out + ((int64_t)tq * p.H + head) * (2 * D);
-        // weight: one wave-uniform branch, not one per element
-        float wv[NDB][16];
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+        for (int off = 32; off >= 1; off /= 2) {
+            a += __shfl_xor(a, off, 64);
+            b += __shfl_xor(b, off, 64);
+        }
+        const float lam = expf(a) - expf(b) + p.lambda_init;
 #pragma unroll
-            for (int a = 0; a < 16; ++a)
-                wv[db][a] = r;
-        if (p.w) {
+        for (int u = 0; u < kSub; ++u) {
+            const float c2 = lam / lsum[u];
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float4 w4 = *(const float4 *)(p.w + 32 * db + 8 * i + 4 * h);
-                    wv[db][4 * i + 0] *= w4.x;
-                    wv[db][4 * i + 1] *= w4.y;
-                    wv[db][4 * i + 2] *= w4.z;
-                    wv[db][4 * i + 3] *= w4.w;
-                }
+                for (int a2 = 0; a2 < 16; ++a2)
+                    xch[((u * NDB + db) * 16 + a2) * 64 + lane] = o[u][db][a2] * c2;
         }
+    }
+    __syncthreads();
+    if (map == 1)
+        return;
+
+    // weights of this lane's output dims
+    float wv[NDB][16];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int a = 0; a < 16; ++a)
+            wv[db][a] = 1.f;
+    if (p.w) {   // one wave-uniform branch, not one per element
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int dim = 32 * db + 8 * i + 4 * h;
-                E vals[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    vals[j] = (E)(o[0][db][4 * i + j] * wv[db][4 * i + j]);
-                __builtin_memcpy(dst + dim, vals, sizeof(vals));
+                const float4 w4 = *(const float4 *)(p.w + 32 * db + 8 * i + 4 * h);
+                wv[db][4 * i + 0] = w4.x;
+                wv[db][4 * i + 1] = w4.y;
+                wv[db][4 * i + 2] = w4.z;
+                wv[db][4 * i + 3] = w4.w;
             }
+    }
+#pragma unroll
+    for (int u = 0; u < kSub; ++u) {
+        const int tq = wq0 + 32 * u + n;
+        const float i1 = 1.f / lsum[u];
+        float ss = 0.f;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int a = 0; a < 16; ++a) {
+                const float pre = o[u][db][a] * i1 - xch[((u * NDB + db) * 16 + a) * 64 + lane];
+                o[u][db][a] = pre;
+                ss += pre * pre;
+            }
+        ss = pair_sum(ss);
+        const float r = (1.f - p.lambda_init) / sqrtf(ss / (float)(2 * D) + p.eps);
+        if (tq < s1) {
+            E *dst = (E *)p.out + ((int64_t)tq * p.H + head) * (2 * D);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int dim = 32 * db + 8 * i + 4 * h;
+                    E vals[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        vals[j] = (E)(o[u][db][4 * i + j] * r * wv[db][4 * i + j]);
+                    __builtin_memcpy(dst + dim, vals, sizeof(vals));
+                }
+        }
     }
 }
 
@@ -628,7 +671,7 @@ int diffattn_fwd(int dtype, const void *q, const void *k, const void *v,
     // byte offsets of K/V rows are formed in 64 bits; the grid in 32 bits
     const int G = H / Hkv;
     const int hpw = (G % 4 == 0) ? 4 : (G % 2 == 0 ? 2 : 1);
-    const int bm = kQW * (kWaves / hpw);
+    const int bm = kQB * (kSlots / hpw);
     const int64_t ntile_q = ((int64_t)max_seqlen + bm - 1) / bm;
     const int64_t nblocks = ntile_q * nseq * Hkv * (G / hpw);
     if (nblocks > INT32_MAX)
