@@ -409,12 +409,19 @@ void diffattn_fwd_kernel(Params p)
             if (masked) {
 #pragma unroll
                 for (int u = 0; u < kSub; ++u) {
-                    const int tq = wq0 + 32 * u + n;
+                    // wave-uniform: does this sub-block straddle the diagonal
+                    // or the end of the sequence?
+                    if (kb0 + 32 > s1 || (p.causal && kb0 + 31 > wq0 + 32 * u)) {
+                        // key kb0 + acc_row(a, h) is visible iff its offset
+                        // acc_row(a, 0) is at most lim (one compare per key)
+                        int lim = s1 - 1 - kb0;
+                        if (p.causal)
+                            lim = min(lim, wq0 + 32 * u + n - kb0);
+                        lim -= 4 * h;
 #pragma unroll
-                    for (int a = 0; a < 16; ++a) {
-                        const int key = kb0 + acc_row(a, h);
-                        if (key >= s1 || (p.causal && key > tq))
-                            sc[u][a] = -INFINITY;
+                        for (int a = 0; a < 16; ++a)
+                            if (acc_row(a, 0) > lim)
+                                sc[u][a] = -INFINITY;
                     }
                 }
             }
