@@ -159,7 +159,7 @@ def main() -> int:
     stream = torch.cuda.Stream(dev)
     dtype_code = da.BF16 if wl.dtype == "bf16" else da.F32
     ptrs = (dtype_code, q.data_ptr(), k.data_ptr(), v.data_ptr(),
-            *[x.data_ptr() for x in lv], lam0, w.data_ptr(), wl.eps,
+            *[x.data_ptr() for x in lv], 0, lam0, w.data_ptr(), wl.eps,
             int(wl.causal), cu.data_ptr(), wl.nseq, wl.max_seqlen, wl.T, wl.H,
             wl.Hkv, wl.d, out.data_ptr(), stream.cuda_stream)
 

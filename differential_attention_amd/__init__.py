@@ -50,8 +50,9 @@ def library() -> ctypes.CDLL:
     vp, f32p, i32p = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
     i32 = ctypes.c_int32
     lib.diffattn_fwd.argtypes = [
-        ctypes.c_int, vp, vp, vp, f32p, f32p, f32p, f32p, ctypes.c_float, f32p,
-        ctypes.c_float, ctypes.c_int, i32p, i32, i32, i32, i32, i32, i32, vp, vp]
+        ctypes.c_int, vp, vp, vp, f32p, f32p, f32p, f32p, i32, ctypes.c_float,
+        f32p, ctypes.c_float, ctypes.c_int, i32p, i32, i32, i32, i32, i32, i32,
+        vp, vp]
     lib.diffattn_fwd.restype = ctypes.c_int
     lib.diffattn_lambda_init.argtypes = [ctypes.c_int]
     lib.diffattn_lambda_init.restype = ctypes.c_double
@@ -91,14 +92,15 @@ def check_cu_seqlens(cu_host, T: int, max_seqlen: int) -> bool:
 
 
 def fwd_ptr(dtype: int, q: int, k: int, v: int, lq1: int, lk1: int, lq2: int,
-            lk2: int, lambda_init_value: float, subln_weight: int, eps: float,
-            causal: int, cu_seqlens: int, nseq: int, max_seqlen: int, T: int,
-            H: int, Hkv: int, d: int, out: int, stream: int) -> int:
+            lk2: int, lambda_stride: int, lambda_init_value: float,
+            subln_weight: int, eps: float, causal: int, cu_seqlens: int,
+            nseq: int, max_seqlen: int, T: int, H: int, Hkv: int, d: int,
+            out: int, stream: int) -> int:
     """The raw C entry point on integer device addresses; returns the
     status."""
     return library().diffattn_fwd(
         int(dtype), q or None, k or None, v or None, lq1 or None, lk1 or None,
-        lq2 or None, lk2 or None, float(lambda_init_value),
+        lq2 or None, lk2 or None, int(lambda_stride), float(lambda_init_value),
         subln_weight or None, float(eps), int(causal), cu_seqlens or None,
         int(nseq), int(max_seqlen), int(T), int(H), int(Hkv), int(d),
         out or None, stream or None)
@@ -128,7 +130,8 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     """Differential-attention forward on the GPU.
 
     q [T, H, 2, d], k [T, Hkv, 2, d], v [T, Hkv, 2d] (bf16 or fp32, one
-    device); lambda vectors fp32 [d]; subln_weight fp32 [2d] or None;
+    device); lambda vectors fp32 [d] (one set for all heads) or [H, d] (one
+    set per head); subln_weight fp32 [2d] or None;
     cu_seqlens int32 [nseq + 1] on the device, or None for ``nseq`` (default
     1) sequences of equal length.  ``max_seqlen`` bounds every sequence
     length; when cu_seqlens is given without it, it is read back from the
@@ -149,11 +152,14 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         raise ValueError("q must be a GPU tensor")
     args = [_dev(q, "q", dev), _dev(k, "k", dev, q.dtype),
             _dev(v, "v", dev, q.dtype)]
+    per_head = lambda_q1.dim() == 2
     for name, lv in (("lambda_q1", lambda_q1), ("lambda_k1", lambda_k1),
                      ("lambda_q2", lambda_q2), ("lambda_k2", lambda_k2)):
-        if lv.numel() != d:
-            raise ValueError(f"{name} must have d = {d} elements")
+        want = (H, d) if per_head else (d,)
+        if tuple(lv.shape) != want:
+            raise ValueError(f"{name} must be {list(want)}")
         args.append(_dev(lv, name, dev, torch.float32))
+    lambda_stride = d if per_head else 0
     w_ptr = 0
     if subln_weight is not None:
         if subln_weight.numel() != 2 * d:
@@ -179,7 +185,8 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         stream = torch.cuda.current_stream(dev)
     with torch.cuda.device(dev):
         st = fwd_ptr(_DTYPES[q.dtype], args[0], args[1], args[2], args[3],
-                     args[4], args[5], args[6], lambda_init, w_ptr, eps,
+                     args[4], args[5], args[6], lambda_stride, lambda_init,
+                     w_ptr, eps,
                      int(bool(causal)), cu_ptr, nseq, max_seqlen, T, H, Hkv, d,
                      out_ptr, stream.cuda_stream)
     if st != OK:

@@ -206,6 +206,7 @@ struct Params {
     const void *v;
     void *out;
     const float *lq1, *lk1, *lq2, *lk2;
+    int64_t lstride;   // elements between heads' lambda vectors (0: shared)
     const float *w;
     const int32_t *cu;
     float lambda_init;
@@ -500,9 +501,10 @@ void diffattn_fwd_kernel(Params p)
         lsum[u] = pair_sum(l_run[u]);
     if (map == 1) {
         float a = 0.f, b = 0.f;
+        const int64_t lo = head * p.lstride;   // this head's lambda vectors
         for (int cc = lane; cc < D; cc += 64) {
-            a += p.lq1[cc] * p.lk1[cc];
-            b += p.lq2[cc] * p.lk2[cc];
+            a += p.lq1[lo + cc] * p.lk1[lo + cc];
+            b += p.lq2[lo + cc] * p.lk2[lo + cc];
         }
 #pragma unroll
         for (int off = 32; off >= 1; off /= 2) {
@@ -637,7 +639,8 @@ int diffattn_check_cu_seqlens(const int32_t *host_cu, int32_t nseq, int32_t T,
 int diffattn_fwd(int dtype, const void *q, const void *k, const void *v,
                  const float *lambda_q1, const float *lambda_k1,
                  const float *lambda_q2, const float *lambda_k2,
-                 float lambda_init, const float *subln_weight, float eps,
+                 int32_t lambda_stride, float lambda_init,
+                 const float *subln_weight, float eps,
                  int causal, const int32_t *cu_seqlens, int32_t nseq,
                  int32_t max_seqlen, int32_t T, int32_t H, int32_t Hkv,
                  int32_t d, void *out, void *stream)
@@ -649,6 +652,8 @@ int diffattn_fwd(int dtype, const void *q, const void *k, const void *v,
     if (causal != 0 && causal != 1)
         return DIFFATTN_EINVAL;
     if (!(eps >= 0.f) || isinf(eps) || !isfinite(lambda_init))
+        return DIFFATTN_EINVAL;
+    if (lambda_stride != 0 && lambda_stride < d)
         return DIFFATTN_EINVAL;
     const launch_fn fn = find_launcher(dtype, d);
     if (!fn)
@@ -693,6 +698,7 @@ int diffattn_fwd(int dtype, const void *q, const void *k, const void *v,
     p.lk1 = lambda_k1;
     p.lq2 = lambda_q2;
     p.lk2 = lambda_k2;
+    p.lstride = lambda_stride;
     p.w = subln_weight;
     p.cu = cu_seqlens;
     p.lambda_init = lambda_init;

@@ -6,12 +6,13 @@
  * unilm pull request "Add an isolated implementation of FlashDiffAttention",
  * FlashDiffAttention and alternative_forward):
  *
- *   lambda = exp(<lambda_q1, lambda_k1>) - exp(<lambda_q2, lambda_k2>) + lambda_init
+ *   lambda_h = exp(<lambda_q1_h, lambda_k1_h>) - exp(<lambda_q2_h, lambda_k2_h>)
+ *              + lambda_init
  *   for each packed sequence, head h (KV head g = h / (H / Hkv)), query i:
  *     A_m[i, j] = softmax_j( <Qm[i, h], Km[j, g]> / sqrt(d) ),  m = 1, 2,
  *                 over keys j <= i of the same sequence (all of its keys
  *                 when causal == 0)
- *     pre[i]    = sum_j (A_1[i, j] - lambda * A_2[i, j]) * V[j, g]   (2d wide)
+ *     pre[i]    = sum_j (A_1[i, j] - lambda_h * A_2[i, j]) * V[j, g] (2d wide)
  *     out[i, h] = pre[i] / sqrt(mean(pre[i]^2) + eps) * w * (1 - lambda_init)
  *
  * Memory layout (all device memory, contiguous, token-major; T tokens, H
@@ -42,7 +43,7 @@
 extern "C" {
 #endif
 
-#define DIFFATTN_ABI_VERSION 1
+#define DIFFATTN_ABI_VERSION 2
 
 enum diffattn_status {
     DIFFATTN_OK = 0,
@@ -62,9 +63,12 @@ enum diffattn_dtype {
  *   dtype        DIFFATTN_BF16 or DIFFATTN_F32: element type of q, k, v, out.
  *   q, k, v      device inputs in the layout above.
  *   lambda_q1, lambda_k1, lambda_q2, lambda_k2
- *                device fp32 vectors of length d, one set shared by all heads
- *                (the Llama gist and alternative_forward share it; the
- *                DiffTransformer page keeps one set per head).
+ *                device fp32 vectors of length d: one set shared by all
+ *                heads (the Llama gist and alternative_forward share it), or
+ *                one set per head (the DiffTransformer page keeps them so),
+ *                head h's vectors starting lambda_stride elements after head
+ *                h-1's.
+ *   lambda_stride 0 for one shared set, else >= d (e.g. d for [H, d]).
  *   lambda_init  the layer's initial lambda (see diffattn_lambda_init).
  *   subln_weight device fp32 [2d] RMSNorm weight (16-byte aligned), or NULL
  *                for all ones.
@@ -91,7 +95,8 @@ enum diffattn_dtype {
 int diffattn_fwd(int dtype, const void *q, const void *k, const void *v,
                  const float *lambda_q1, const float *lambda_k1,
                  const float *lambda_q2, const float *lambda_k2,
-                 float lambda_init, const float *subln_weight, float eps,
+                 int32_t lambda_stride, float lambda_init,
+                 const float *subln_weight, float eps,
                  int causal, const int32_t *cu_seqlens, int32_t nseq,
                  int32_t max_seqlen, int32_t T, int32_t H, int32_t Hkv,
                  int32_t d, void *out, void *stream);

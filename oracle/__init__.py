@@ -53,9 +53,10 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.diffattn_ref_lambda.argtypes = [f32p, f32p, f32p, f32p, ctypes.c_int,
                                         ctypes.c_double]
     lib.diffattn_ref_lambda.restype = ctypes.c_double
-    common = [f32p, f32p, f32p, f32p, f32p, f32p, f32p, ctypes.c_double, f32p,
-              ctypes.c_double, ctypes.c_int, i32p, ctypes.c_int, ctypes.c_int64,
-              ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    common = [f32p, f32p, f32p, f32p, f32p, f32p, f32p, ctypes.c_int64,
+              ctypes.c_double, f32p, ctypes.c_double, ctypes.c_int, i32p,
+              ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+              ctypes.c_int]
     lib.diffattn_ref_fwd.argtypes = common + [f64p, ctypes.c_int]
     lib.diffattn_ref_fwd.restype = ctypes.c_int
     lib.diffattn_ref_rows.argtypes = common + [i64p, i32p, ctypes.c_int64, f64p,
@@ -103,8 +104,11 @@ def _common(q, k, v, lq1, lk1, lq2, lk2, lambda_init_value, w, eps, causal,
     assert two == 2
     Hkv = ka.shape[1]
     assert ka.shape == (T, Hkv, 2, d) and va.shape == (T, Hkv, 2 * d)
-    lv = [_f32(x).reshape(-1) for x in (lq1, lk1, lq2, lk2)]
-    assert all(x.size == d for x in lv)
+    # lambda vectors: [d] shared by all heads, or [H, d] one set per head
+    lv = [_f32(x) for x in (lq1, lk1, lq2, lk2)]
+    per_head = lv[0].ndim == 2
+    assert all(x.shape == ((H, d) if per_head else (d,)) for x in lv)
+    lstride = d if per_head else 0
     wa = None if w is None else _f32(w).reshape(-1)
     if wa is not None:
         assert wa.size == 2 * d
@@ -121,7 +125,7 @@ def _common(q, k, v, lq1, lk1, lq2, lk2, lambda_init_value, w, eps, causal,
     keep = (qa, ka, va, lv, wa, cu)
     args = [_ptr(qa, ctypes.c_float), _ptr(ka, ctypes.c_float),
             _ptr(va, ctypes.c_float)] + [_ptr(x, ctypes.c_float) for x in lv]
-    args += [float(lambda_init_value),
+    args += [int(lstride), float(lambda_init_value),
              None if wa is None else _ptr(wa, ctypes.c_float),
              float(eps), int(bool(causal)), _ptr(cu, ctypes.c_int32),
              int(cu.size - 1), int(T), int(H), int(Hkv), int(d)]
@@ -131,7 +135,8 @@ def _common(q, k, v, lq1, lk1, lq2, lk2, lambda_init_value, w, eps, causal,
 def fwd(q, k, v, lq1, lk1, lq2, lk2, lambda_init_value: float, w=None,
         eps: float = 1e-5, causal: bool = True, cu_seqlens=None,
         nthreads: int = 0, lib: Optional[ctypes.CDLL] = None) -> np.ndarray:
-    """Whole output ``[T, H, 2d]`` in fp64.  Layouts as in ``workloads``."""
+    """Whole output ``[T, H, 2d]`` in fp64.  Layouts as in ``workloads``;
+    the lambda vectors are ``[d]`` (shared) or ``[H, d]`` (per head)."""
     keep, args, (T, H, d) = _common(q, k, v, lq1, lk1, lq2, lk2,
                                     lambda_init_value, w, eps, causal,
                                     cu_seqlens)

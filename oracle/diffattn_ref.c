@@ -12,13 +12,16 @@
  * request "Add an isolated implementation of FlashDiffAttention",
  * alternative_forward):
  *
- *   lambda  = exp(sum_c lq1[c]*lk1[c]) - exp(sum_c lq2[c]*lk2[c]) + lambda_init
+ *   lambda_h = exp(sum_c lq1_h[c]*lk1_h[c]) - exp(sum_c lq2_h[c]*lk2_h[c])
+ *              + lambda_init
+ *              (one set of vectors shared by all heads, or one per head as
+ *              the DiffTransformer page keeps them: lq1_h = lq1 + h*stride)
  *   for every packed sequence s (tokens a .. a+n-1), head h, row i:
  *     g      = h / (H / Hkv)                  (GQA: contiguous head groups)
  *     map m in {1,2}: x_j = <Qm[a+i,h], Km[a+j,g]> / sqrt(d), j in J(i)
  *                     J(i) = {0..i} when causal, else {0..n-1}
  *                     A_m  = softmax_j(x_j)
- *     pre    = sum_j (A_1[j] - lambda * A_2[j]) * V[a+j, g, :]     (2d wide)
+ *     pre    = sum_j (A_1[j] - lambda_h * A_2[j]) * V[a+j, g, :]   (2d wide)
  *     out    = pre / sqrt(mean_c pre[c]^2 + eps) * w * (1 - lambda_init)
  *
  * Each softmax is taken the plain two-pass way (maximum, then exponentials
@@ -46,9 +49,10 @@ double diffattn_ref_lambda_init(int depth)
     return 0.8 - 0.6 * exp(-0.3 * (double)(depth - 1));
 }
 
-/* The re-parameterised lambda (MultiHeadDifferentialAttention.forward):
- * one scalar shared by every head, as in the Llama gist and the pull
- * request's alternative_forward, where the four vectors have length d. */
+/* The re-parameterised lambda (MultiHeadDifferentialAttention.forward) of
+ * one set of four length-d vectors.  The Llama gist and the pull request's
+ * alternative_forward share one set among all heads; the DiffTransformer page
+ * keeps one set per head. */
 double diffattn_ref_lambda(const float *lq1, const float *lk1,
                            const float *lq2, const float *lk2, int d,
                            double lambda_init)
@@ -59,6 +63,19 @@ double diffattn_ref_lambda(const float *lq1, const float *lk1,
         dot2 += (double)lq2[c] * (double)lk2[c];
     }
     return exp(dot1) - exp(dot2) + lambda_init;
+}
+
+/* lambda of every head: lam[h] from the vectors at offset h * stride
+ * (stride 0: the same vectors for every head). */
+static void lambda_per_head(const float *lq1, const float *lk1,
+                            const float *lq2, const float *lk2, int64_t stride,
+                            int H, int d, double lambda_init, double *lam)
+{
+    for (int h = 0; h < H; ++h) {
+        const int64_t o = (int64_t)h * stride;
+        lam[h] = diffattn_ref_lambda(lq1 + o, lk1 + o, lq2 + o, lk2 + o, d,
+                                     lambda_init);
+    }
 }
 
 /* Softmax of one attention map over the keys j in [0, nkeys) of the sequence
@@ -150,14 +167,17 @@ static int64_t max_len(const int32_t *cu, int nseq)
  * Returns 0, or -1 on malformed arguments, -2 if scratch memory is short. */
 int diffattn_ref_fwd(const float *q, const float *k, const float *v,
                      const float *lq1, const float *lk1, const float *lq2,
-                     const float *lk2, double lambda_init, const float *w,
-                     double eps, int causal, const int32_t *cu_seqlens,
-                     int nseq, int64_t T, int H, int Hkv, int d, double *out,
-                     int nthreads)
+                     const float *lk2, int64_t lambda_stride,
+                     double lambda_init, const float *w, double eps, int causal,
+                     const int32_t *cu_seqlens, int nseq, int64_t T, int H,
+                     int Hkv, int d, double *out, int nthreads)
 {
-    if (check_args(cu_seqlens, nseq, T, H, Hkv, d))
+    if (check_args(cu_seqlens, nseq, T, H, Hkv, d) || lambda_stride < 0)
         return -1;
-    const double lam = diffattn_ref_lambda(lq1, lk1, lq2, lk2, d, lambda_init);
+    double *lam = malloc(sizeof(double) * (size_t)H);
+    if (!lam)
+        return -2;
+    lambda_per_head(lq1, lk1, lq2, lk2, lambda_stride, H, d, lambda_init, lam);
     const int64_t nmax = max_len(cu_seqlens, nseq);
     const int64_t nrows = T * H;
     int err = 0;
@@ -187,12 +207,13 @@ int diffattn_ref_fwd(const float *q, const float *k, const float *v,
                 ++s;
             const int64_t a = cu_seqlens[s];
             const int64_t n = cu_seqlens[s + 1] - a;
-            diff_row(q, k, v, lam, lambda_init, w, eps, causal, a, n, t - a, h,
-                     H, Hkv, d, scratch, scratch + nmax, scratch + 2 * nmax,
+            diff_row(q, k, v, lam[h], lambda_init, w, eps, causal, a, n, t - a,
+                     h, H, Hkv, d, scratch, scratch + nmax, scratch + 2 * nmax,
                      out + r * 2 * (int64_t)d);
         }
         free(scratch);
     }
+    free(lam);
     return err;
 }
 
@@ -200,18 +221,22 @@ int diffattn_ref_fwd(const float *q, const float *k, const float *v,
  * out_rows[nrows, 2d].  Used to check full-size runs on a sample. */
 int diffattn_ref_rows(const float *q, const float *k, const float *v,
                       const float *lq1, const float *lk1, const float *lq2,
-                      const float *lk2, double lambda_init, const float *w,
-                      double eps, int causal, const int32_t *cu_seqlens,
-                      int nseq, int64_t T, int H, int Hkv, int d,
-                      const int64_t *tok, const int32_t *head, int64_t nrows,
-                      double *out_rows, int nthreads)
+                      const float *lk2, int64_t lambda_stride,
+                      double lambda_init, const float *w, double eps,
+                      int causal, const int32_t *cu_seqlens, int nseq,
+                      int64_t T, int H, int Hkv, int d, const int64_t *tok,
+                      const int32_t *head, int64_t nrows, double *out_rows,
+                      int nthreads)
 {
-    if (check_args(cu_seqlens, nseq, T, H, Hkv, d))
+    if (check_args(cu_seqlens, nseq, T, H, Hkv, d) || lambda_stride < 0)
         return -1;
     for (int64_t r = 0; r < nrows; ++r)
         if (tok[r] < 0 || tok[r] >= T || head[r] < 0 || head[r] >= H)
             return -1;
-    const double lam = diffattn_ref_lambda(lq1, lk1, lq2, lk2, d, lambda_init);
+    double *lam = malloc(sizeof(double) * (size_t)H);
+    if (!lam)
+        return -2;
+    lambda_per_head(lq1, lk1, lq2, lk2, lambda_stride, H, d, lambda_init, lam);
     const int64_t nmax = max_len(cu_seqlens, nseq);
     int err = 0;
 #ifdef _OPENMP
@@ -239,12 +264,13 @@ int diffattn_ref_rows(const float *q, const float *k, const float *v,
                 ++s;
             const int64_t a = cu_seqlens[s];
             const int64_t n = cu_seqlens[s + 1] - a;
-            diff_row(q, k, v, lam, lambda_init, w, eps, causal, a, n, t - a,
-                     head[r], H, Hkv, d, scratch, scratch + nmax,
+            diff_row(q, k, v, lam[head[r]], lambda_init, w, eps, causal, a, n,
+                     t - a, head[r], H, Hkv, d, scratch, scratch + nmax,
                      scratch + 2 * nmax, out_rows + r * 2 * (int64_t)d);
         }
         free(scratch);
     }
+    free(lam);
     return err;
 }
 

@@ -64,10 +64,16 @@ def brute_mpmath(q, k, v, lv, lam_init, w, eps, causal, cu, dps=50):
     Hkv = k.shape[1]
     G = H // Hkv
     mpf = mpmath.mpf
-    lq1, lk1, lq2, lk2 = [[mpf(float(x)) for x in a] for a in lv]
-    lam = (mpmath.exp(mpmath.fsum(a * b for a, b in zip(lq1, lk1)))
-           - mpmath.exp(mpmath.fsum(a * b for a, b in zip(lq2, lk2)))
-           + mpf(lam_init))
+
+    def lam_of(vecs):
+        lq1, lk1, lq2, lk2 = [[mpf(float(x)) for x in a] for a in vecs]
+        return (mpmath.exp(mpmath.fsum(a * b for a, b in zip(lq1, lk1)))
+                - mpmath.exp(mpmath.fsum(a * b for a, b in zip(lq2, lk2)))
+                + mpf(lam_init))
+    if np.asarray(lv[0]).ndim == 2:     # one set of vectors per head
+        lams = [lam_of([a[h] for a in lv]) for h in range(H)]
+    else:
+        lams = [lam_of(lv)] * H
     scaling = 1 / mpmath.sqrt(d)
     out = np.zeros((T, H, 2 * d))
     for s in range(len(cu) - 1):
@@ -75,6 +81,7 @@ def brute_mpmath(q, k, v, lv, lam_init, w, eps, causal, cu, dps=50):
         n = b - a
         for h in range(H):
             g = h // G
+            lam = lams[h]
             A = []
             for m in range(2):
                 Am = []
@@ -115,9 +122,14 @@ def pin_brute_force(lib):
         (2, (5,), 2, 2, 2, False, 1.0),
         (3, (3, 1, 5), 2, 1, 4, True, 1.0),
         (4, (6,), 2, 1, 2, True, 800.0),    # scores beyond exp()'s double range
+        (5, (4, 5), 4, 2, 3, True, 1.0),    # one set of lambda vectors per head
     ]
     for seed, seqlens, H, Hkv, d, causal, qs in cases:
         q, k, v, lv, w, cu = tiny_inputs(seed, seqlens, H, Hkv, d, q_scale=qs)
+        if seed == 5:
+            rng = np.random.default_rng(55)
+            lv = [(0.4 * rng.standard_normal((H, d))).astype(np.float32)
+                  for _ in range(4)]
         lam_init = 0.8 - 0.6 * math.exp(-0.3 * (seed + 2))
         got = run(lib, q, k, v, lv, lam_init, w, 1e-5, causal, cu)
         ref = brute_mpmath(q, k, v, lv, lam_init, w, 1e-5, causal, cu)
@@ -152,7 +164,8 @@ def sdpa_diff(q, k, v, lam, lam_init, w, eps, causal, cu):
                                             scale=sc, enable_gqa=True)
         o2 = F.scaled_dot_product_attention(q2, k2, vv, is_causal=causal,
                                             scale=sc, enable_gqa=True)
-        o = o1 - lam * o2
+        lam_t = torch.as_tensor(np.asarray(lam, dtype=np.float64)).reshape(-1, 1, 1)
+        o = o1 - lam_t * o2
         o = F.rms_norm(o, (2 * d,), weight=wt, eps=eps) * (1.0 - lam_init)
         out[a:b] = o[0].permute(1, 0, 2)
     return out.numpy()
@@ -169,6 +182,29 @@ def pin_sdpa_lambda_zero(lib):
     ref = sdpa_diff(q2, k, v, 0.0, 0.0, w, 1e-5, True, cu)
     err = np.max(np.abs(got - ref))
     assert err < 1e-10, f"lambda=0 vs SDPA: max-abs {err:.3e}"
+
+
+def pin_sdpa_per_head_lambda(lib):
+    """One set of lambda vectors per head (the DiffTransformer page's
+    parameter shape), against the library composition with a per-head
+    lambda."""
+    H, Hkv, d = 8, 2, 16
+    q, k, v, lv, w, cu = tiny_inputs(17, (41, 30), H, Hkv, d)
+    rng = np.random.default_rng(170)
+    lv = [(0.3 * rng.standard_normal((H, d))).astype(np.float32) for _ in range(4)]
+    lam_init = 0.8 - 0.6 * math.exp(-0.3 * 4)
+    lam = np.array([math.exp(float(np.dot(lv[0][h].astype(np.float64), lv[1][h])))
+                    - math.exp(float(np.dot(lv[2][h].astype(np.float64), lv[3][h])))
+                    + lam_init for h in range(H)])
+    got = run(lib, q, k, v, lv, lam_init, w, 1e-5, True, cu)
+    ref = sdpa_diff(q, k, v, lam, lam_init, w, 1e-5, True, cu)
+    err = np.max(np.abs(got - ref))
+    assert err < 1e-10, f"per-head lambda vs SDPA: max-abs {err:.3e}"
+    # identical per-head sets equal the shared set, bitwise
+    shared = [x[3] for x in lv]
+    rep = [np.repeat(x[None, :], H, axis=0) for x in shared]
+    assert np.array_equal(run(lib, q, k, v, rep, lam_init, w, 1e-5, True, cu),
+                          run(lib, q, k, v, shared, lam_init, w, 1e-5, True, cu))
 
 
 def pin_sdpa_two_maps(lib):
@@ -336,6 +372,7 @@ ALL_PINS = [
     pin_brute_force,
     pin_sdpa_lambda_zero,
     pin_sdpa_two_maps,
+    pin_sdpa_per_head_lambda,
     pin_row0_closed_form,
     pin_uniform_attention,
     pin_identical_maps,

@@ -64,7 +64,8 @@ def test_check_cu_seqlens():
 
 def call(**over):
     a = dict(dtype=da.BF16, q=FAKE, k=FAKE, v=FAKE, lq1=FAKE, lk1=FAKE,
-             lq2=FAKE, lk2=FAKE, lambda_init_value=0.2, subln_weight=0,
+             lq2=FAKE, lk2=FAKE, lambda_stride=0, lambda_init_value=0.2,
+             subln_weight=0,
              eps=1e-5, causal=1, cu_seqlens=0, nseq=2, max_seqlen=0, T=64,
              H=16, Hkv=4, d=64, out=FAKE, stream=0)
     a.update(over)
@@ -80,6 +81,8 @@ def call(**over):
     (dict(eps=-1.0), da.EINVAL),
     (dict(eps=float("nan")), da.EINVAL),
     (dict(lambda_init_value=float("inf")), da.EINVAL),
+    (dict(lambda_stride=-1), da.EINVAL),
+    (dict(lambda_stride=63), da.EINVAL),        # stride below d
     (dict(d=48), da.EUNSUPPORTED),
     (dict(dtype=da.F32, d=32), da.EUNSUPPORTED),
     (dict(q=0), da.EINVAL),

@@ -31,6 +31,8 @@ MUTANTS = {
     "v_uses_query_head": ("((a + j) * Hkv + g) * (int64_t)dv", "((a + j) * Hkv + h % Hkv) * (int64_t)dv"),
     "softmax_no_max_shift": ("exp(p[j] - mx)", "exp(p[j])"),
     "softmax_wrong_normaliser": ("p[j] /= z;", "p[j] /= (double)nkeys;"),
+    "per_head_lambda_offset": ("const int64_t o = (int64_t)h * stride;", "const int64_t o = 0 * stride;"),
+    "per_head_lambda_index": ("diff_row(q, k, v, lam[h],", "diff_row(q, k, v, lam[0],"),
 }
 
 

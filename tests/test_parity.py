@@ -276,3 +276,19 @@ def test_stream_argument():
         out = gpu_run(inp, stream=s)
     s.synchronize()
     assert torch.equal(out, gpu_run(inp))
+
+
+@pytest.mark.parametrize("dtype,d,H,Hkv", [("bf16", 64, 16, 4), ("f32", 16, 4, 2),
+                                           ("bf16", 32, 6, 3)])
+def test_per_head_lambda(dtype, d, H, Hkv):
+    """One set of lambda vectors per head, as the DiffTransformer page keeps
+    them ([H, d], lambda_stride = d)."""
+    wl = custom("per_head", dtype, (200, 77, 130), H, Hkv, d, depth=9, seed=d)
+    inp = make_inputs(wl)
+    g = torch.Generator().manual_seed(1234 + d)
+    inp.lq1, inp.lk1, inp.lq2, inp.lk2 = [
+        0.3 * torch.randn(H, d, generator=g) for _ in range(4)]
+    announce(f"per-head lambda {dtype} d={d} H={H} Hkv={Hkv}")
+    err = max_abs(gpu_run(inp), oracle_full(inp))
+    announce(f"per-head lambda max-abs {err:.3e}")
+    assert err <= TOL[dtype]
