@@ -62,6 +62,12 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.diffattn_ref_rows.argtypes = common + [i64p, i32p, ctypes.c_int64, f64p,
                                                ctypes.c_int]
     lib.diffattn_ref_rows.restype = ctypes.c_int
+    lib.diffattn_ref_fwd_kv.argtypes = (
+        [f32p] * 7 + [ctypes.c_int64, ctypes.c_double, f32p, ctypes.c_double,
+                      ctypes.c_int, i32p, i32p, ctypes.c_int, ctypes.c_int64,
+                      ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                      f64p, ctypes.c_int])
+    lib.diffattn_ref_fwd_kv.restype = ctypes.c_int
     lib.diffattn_ref_max_threads.argtypes = []
     lib.diffattn_ref_max_threads.restype = ctypes.c_int
     _lib_cache[path] = lib
@@ -167,6 +173,52 @@ def rows(q, k, v, lq1, lk1, lq2, lk2, lambda_init_value: float,
     del keep
     if rc != 0:
         raise ValueError(f"diffattn_ref_rows failed with status {rc}")
+    return out
+
+
+def _cu(x) -> np.ndarray:
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.cpu().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+
+def fwd_kv(q, k, v, lq1, lk1, lq2, lk2, lambda_init_value: float, w=None,
+           eps: float = 1e-5, causal: bool = True, cu_seqlens_q=None,
+           cu_seqlens_k=None, nthreads: int = 0,
+           lib: Optional[ctypes.CDLL] = None) -> np.ndarray:
+    """New queries against a key/value cache, in fp64: q ``[Tq, H, 2, d]``,
+    k ``[Tk, Hkv, 2, d]``, v ``[Tk, Hkv, 2d]``; sequence s owns query tokens
+    ``cu_seqlens_q[s] ..`` and key tokens ``cu_seqlens_k[s] ..`` (one
+    sequence of all tokens when both are None).  Causal rows are aligned
+    bottom-right.  Returns ``[Tq, H, 2d]``."""
+    qa, ka, va = _f32(q), _f32(k), _f32(v)
+    Tq, H, two, d = qa.shape
+    Tk, Hkv = ka.shape[0], ka.shape[1]
+    assert two == 2 and ka.shape == (Tk, Hkv, 2, d)
+    assert va.shape == (Tk, Hkv, 2 * d)
+    lv = [_f32(x) for x in (lq1, lk1, lq2, lk2)]
+    per_head = lv[0].ndim == 2
+    assert all(x.shape == ((H, d) if per_head else (d,)) for x in lv)
+    wa = None if w is None else _f32(w).reshape(-1)
+    cq = _cu([0, Tq] if cu_seqlens_q is None else cu_seqlens_q)
+    ck = _cu([0, Tk] if cu_seqlens_k is None else cu_seqlens_k)
+    if cq.size != ck.size:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k differ in length")
+    out = np.empty((Tq, H, 2 * d), dtype=np.float64)
+    rc = (lib or load()).diffattn_ref_fwd_kv(
+        _ptr(qa, ctypes.c_float), _ptr(ka, ctypes.c_float),
+        _ptr(va, ctypes.c_float), *[_ptr(x, ctypes.c_float) for x in lv],
+        int(d if per_head else 0), float(lambda_init_value),
+        None if wa is None else _ptr(wa, ctypes.c_float), float(eps),
+        int(bool(causal)), _ptr(cq, ctypes.c_int32), _ptr(ck, ctypes.c_int32),
+        int(cq.size - 1), int(Tq), int(Tk), int(H), int(Hkv), int(d),
+        _ptr(out, ctypes.c_double), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"diffattn_ref_fwd_kv failed with status {rc}")
     return out
 
 

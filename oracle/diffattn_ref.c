@@ -24,6 +24,13 @@
  *     pre    = sum_j (A_1[j] - lambda_h * A_2[j]) * V[a+j, g, :]   (2d wide)
  *     out    = pre / sqrt(mean_c pre[c]^2 + eps) * w * (1 - lambda_init)
  *
+ * Against a key/value cache (diffattn_ref_fwd_kv; the Llama gist's forward
+ * appends the new keys and values to the cache before attending), sequence s
+ * has nq new queries and nk >= nq keys, the queries' own keys last; causal
+ * row i sees keys {0 .. nk - nq + i}, the bottom-right alignment of the pull
+ * request's mask (upper triangle above diagonal 1 + src_len - tgt_len).
+ * With nq = nk this is the prefill above.
+ *
  * Each softmax is taken the plain two-pass way (maximum, then exponentials
  * and their sum), every operation in IEEE double.  Inputs arrive as fp32
  * arrays: every bf16 or fp32 input value is exactly representable there, and
@@ -78,18 +85,18 @@ static void lambda_per_head(const float *lq1, const float *lk1,
     }
 }
 
-/* Softmax of one attention map over the keys j in [0, nkeys) of the sequence
- * starting at token a, for query token a+i of head h: writes the
- * probabilities into p[0..nkeys). */
-static void softmax_map(const float *q, const float *k, int64_t a, int64_t i,
+/* Softmax of one attention map over the keys j in [0, nkeys) that start at
+ * key token ka, for query token qt of head h: writes the probabilities into
+ * p[0..nkeys). */
+static void softmax_map(const float *q, const float *k, int64_t qt, int64_t ka,
                         int64_t nkeys, int h, int g, int map, int H, int Hkv,
                         int d, double *p)
 {
-    const float *qrow = q + (((a + i) * H + h) * 2 + map) * (int64_t)d;
+    const float *qrow = q + ((qt * H + h) * 2 + map) * (int64_t)d;
     const double scale = 1.0 / sqrt((double)d);
     double mx = -INFINITY;
     for (int64_t j = 0; j < nkeys; ++j) {
-        const float *krow = k + (((a + j) * Hkv + g) * 2 + map) * (int64_t)d;
+        const float *krow = k + (((ka + j) * Hkv + g) * 2 + map) * (int64_t)d;
         double x = 0.0;
         for (int c = 0; c < d; ++c)
             x += (double)qrow[c] * (double)krow[c];
@@ -107,24 +114,24 @@ static void softmax_map(const float *q, const float *k, int64_t a, int64_t i,
         p[j] /= z;
 }
 
-/* One output row (token a+i, head h) into o[0..2d). p1, p2 and pre are
- * caller-provided scratch of n, n and 2d doubles. */
+/* One output row (query token qt, head h) over the nkeys keys that start at
+ * key token ka, into o[0..2d).  p1, p2 and pre are caller-provided scratch
+ * of nkeys, nkeys and 2d doubles. */
 static void diff_row(const float *q, const float *k, const float *v,
                      double lam, double lambda_init, const float *w, double eps,
-                     int causal, int64_t a, int64_t n, int64_t i, int h, int H,
+                     int64_t qt, int64_t ka, int64_t nkeys, int h, int H,
                      int Hkv, int d, double *p1, double *p2, double *pre,
                      double *o)
 {
     const int g = h / (H / Hkv);
-    const int64_t nkeys = causal ? i + 1 : n;
     const int dv = 2 * d;
-    softmax_map(q, k, a, i, nkeys, h, g, 0, H, Hkv, d, p1);
-    softmax_map(q, k, a, i, nkeys, h, g, 1, H, Hkv, d, p2);
+    softmax_map(q, k, qt, ka, nkeys, h, g, 0, H, Hkv, d, p1);
+    softmax_map(q, k, qt, ka, nkeys, h, g, 1, H, Hkv, d, p2);
     for (int c = 0; c < dv; ++c)
         pre[c] = 0.0;
     for (int64_t j = 0; j < nkeys; ++j) {
         const double coef = p1[j] - lam * p2[j];
-        const float *vrow = v + ((a + j) * Hkv + g) * (int64_t)dv;
+        const float *vrow = v + ((ka + j) * Hkv + g) * (int64_t)dv;
         for (int c = 0; c < dv; ++c)
             pre[c] += coef * (double)vrow[c];
     }
@@ -136,6 +143,13 @@ static void diff_row(const float *q, const float *k, const float *v,
         const double wc = w ? (double)w[c] : 1.0;
         o[c] = pre[c] / rms * wc * (1.0 - lambda_init);
     }
+}
+
+/* Keys visible to row i (0-based) of a sequence of n tokens attending to
+ * itself: its prefix when causal, the whole sequence otherwise. */
+static int64_t prefill_keys(int causal, int64_t i, int64_t n)
+{
+    return causal ? i + 1 : n;
 }
 
 static int check_args(const int32_t *cu, int nseq, int64_t T, int H, int Hkv,
@@ -207,8 +221,9 @@ int diffattn_ref_fwd(const float *q, const float *k, const float *v,
                 ++s;
             const int64_t a = cu_seqlens[s];
             const int64_t n = cu_seqlens[s + 1] - a;
-            diff_row(q, k, v, lam[h], lambda_init, w, eps, causal, a, n, t - a,
-                     h, H, Hkv, d, scratch, scratch + nmax, scratch + 2 * nmax,
+            diff_row(q, k, v, lam[h], lambda_init, w, eps, t, a,
+                     prefill_keys(causal, t - a, n), h, H, Hkv, d, scratch,
+                     scratch + nmax, scratch + 2 * nmax,
                      out + r * 2 * (int64_t)d);
         }
         free(scratch);
@@ -264,9 +279,78 @@ int diffattn_ref_rows(const float *q, const float *k, const float *v,
                 ++s;
             const int64_t a = cu_seqlens[s];
             const int64_t n = cu_seqlens[s + 1] - a;
-            diff_row(q, k, v, lam[head[r]], lambda_init, w, eps, causal, a, n,
-                     t - a, head[r], H, Hkv, d, scratch, scratch + nmax,
-                     scratch + 2 * nmax, out_rows + r * 2 * (int64_t)d);
+            diff_row(q, k, v, lam[head[r]], lambda_init, w, eps, t, a,
+                     prefill_keys(causal, t - a, n), head[r], H, Hkv, d,
+                     scratch, scratch + nmax, scratch + 2 * nmax,
+                     out_rows + r * 2 * (int64_t)d);
+        }
+        free(scratch);
+    }
+    free(lam);
+    return err;
+}
+
+/* New queries against a key/value cache: sequence s has nq = cu_q[s+1] -
+ * cu_q[s] query tokens (in q) and nk = cu_k[s+1] - cu_k[s] key tokens (in k,
+ * v; the queries' own keys are the last nq of them).  Causal alignment is
+ * bottom-right, as the pull request's alternative_forward builds its mask
+ * with triu(-inf, 1 + src_len - tgt_len): query i sees keys j <= nk - nq + i.
+ * Not causal: every key of the sequence.  out[Tq, H, 2d].  Returns 0, -1 on
+ * malformed arguments (including causal with nq > nk), -2 without memory. */
+int diffattn_ref_fwd_kv(const float *q, const float *k, const float *v,
+                        const float *lq1, const float *lk1, const float *lq2,
+                        const float *lk2, int64_t lambda_stride,
+                        double lambda_init, const float *w, double eps,
+                        int causal, const int32_t *cu_q, const int32_t *cu_k,
+                        int nseq, int64_t Tq, int64_t Tk, int H, int Hkv, int d,
+                        double *out, int nthreads)
+{
+    if (check_args(cu_q, nseq, Tq, H, Hkv, d) || check_args(cu_k, nseq, Tk, H, Hkv, d) ||
+        lambda_stride < 0)
+        return -1;
+    for (int s = 0; s < nseq; ++s) {
+        const int64_t nq = cu_q[s + 1] - cu_q[s], nk = cu_k[s + 1] - cu_k[s];
+        if ((causal && nq > nk) || (nq > 0 && nk == 0))
+            return -1;
+    }
+    double *lam = malloc(sizeof(double) * (size_t)H);
+    if (!lam)
+        return -2;
+    lambda_per_head(lq1, lk1, lq2, lk2, lambda_stride, H, d, lambda_init, lam);
+    const int64_t nmax = max_len(cu_k, nseq);
+    const int64_t nrows = Tq * H;
+    int err = 0;
+#ifdef _OPENMP
+    if (nthreads <= 0)
+        nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads)
+#endif
+    {
+        double *scratch = malloc(sizeof(double) * (size_t)(2 * nmax + 2 * d + 1));
+        if (!scratch) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+            err = -2;
+        }
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 8)
+#endif
+        for (int64_t r = 0; r < nrows; ++r) {
+            if (!scratch)
+                continue;
+            const int64_t t = r / H;
+            const int h = (int)(r % H);
+            int s = 0;
+            while (cu_q[s + 1] <= t)
+                ++s;
+            const int64_t nq = cu_q[s + 1] - cu_q[s];
+            const int64_t nk = cu_k[s + 1] - cu_k[s];
+            const int64_t i = t - cu_q[s];
+            const int64_t nkeys = causal ? nk - nq + i + 1 : nk;
+            diff_row(q, k, v, lam[h], lambda_init, w, eps, t, cu_k[s], nkeys,
+                     h, H, Hkv, d, scratch, scratch + nmax, scratch + 2 * nmax,
+                     out + r * 2 * (int64_t)d);
         }
         free(scratch);
     }

@@ -58,8 +58,14 @@ def run(lib, q, k, v, lv, lam_init, w, eps, causal, cu):
 # --------------------------------------------------------------------------
 # mpmath brute force of the materialised two-map form
 
-def brute_mpmath(q, k, v, lv, lam_init, w, eps, causal, cu, dps=50):
+def brute_mpmath(q, k, v, lv, lam_init, w, eps, causal, cu, dps=50, cu_k=None):
+    """With ``cu_k``, sequence s has its queries at ``cu[s]..`` and its keys
+    at ``cu_k[s]..`` and a causal row i sees keys j <= i + nk - nq: the
+    lower triangle of the pull request's mask, which puts -inf above
+    diagonal 1 + src_len - tgt_len."""
     mpmath.mp.dps = dps
+    if cu_k is None:
+        cu_k = cu
     T, H, _, d = q.shape
     Hkv = k.shape[1]
     G = H // Hkv
@@ -79,6 +85,8 @@ def brute_mpmath(q, k, v, lv, lam_init, w, eps, causal, cu, dps=50):
     for s in range(len(cu) - 1):
         a, b = int(cu[s]), int(cu[s + 1])
         n = b - a
+        ka = int(cu_k[s])
+        nk = int(cu_k[s + 1]) - ka
         for h in range(H):
             g = h // G
             lam = lams[h]
@@ -87,12 +95,12 @@ def brute_mpmath(q, k, v, lv, lam_init, w, eps, causal, cu, dps=50):
                 Am = []
                 for i in range(n):
                     row = []
-                    for j in range(n):
-                        if causal and j > i:
+                    for j in range(nk):
+                        if causal and j > i + nk - n:
                             row.append(mpmath.ninf)
                             continue
                         x = mpmath.fsum(mpf(float(q[a + i, h, m, c]))
-                                        * mpf(float(k[a + j, g, m, c]))
+                                        * mpf(float(k[ka + j, g, m, c]))
                                         for c in range(d))
                         row.append(x * scaling)
                     mx = max(x for x in row if x != mpmath.ninf)
@@ -105,8 +113,8 @@ def brute_mpmath(q, k, v, lv, lam_init, w, eps, causal, cu, dps=50):
                 pre = []
                 for c in range(2 * d):
                     pre.append(mpmath.fsum((A[0][i][j] - lam * A[1][i][j])
-                                           * mpf(float(v[a + j, g, c]))
-                                           for j in range(n)))
+                                           * mpf(float(v[ka + j, g, c]))
+                                           for j in range(nk)))
                 rms = mpmath.sqrt(mpmath.fsum(x * x for x in pre) / (2 * d)
                                   + mpf(eps))
                 for c in range(2 * d):
@@ -141,8 +149,13 @@ def pin_brute_force(lib):
 # --------------------------------------------------------------------------
 # library routines: torch SDPA + rms_norm in fp64
 
-def sdpa_diff(q, k, v, lam, lam_init, w, eps, causal, cu):
-    """The two-call composition with torch library routines, per sequence."""
+def sdpa_diff(q, k, v, lam, lam_init, w, eps, causal, cu, cu_k=None):
+    """The two-call composition with torch library routines, per sequence.
+    With ``cu_k`` the keys of sequence s are ``cu_k[s]..`` and the causal
+    mask is an explicit bottom-right lower triangle (torch.tril at offset
+    nk - nq)."""
+    if cu_k is None:
+        cu_k = cu
     qt = torch.from_numpy(q).double()
     kt = torch.from_numpy(k).double()
     vt = torch.from_numpy(v).double()
@@ -151,19 +164,25 @@ def sdpa_diff(q, k, v, lam, lam_init, w, eps, causal, cu):
     wt = None if w is None else torch.from_numpy(w).double()
     for s in range(len(cu) - 1):
         a, b = int(cu[s]), int(cu[s + 1])
+        ka, kb = int(cu_k[s]), int(cu_k[s + 1])
         if b == a:
             continue
         # [1, heads, n, width]
         q1 = qt[a:b, :, 0].permute(1, 0, 2).unsqueeze(0)
         q2 = qt[a:b, :, 1].permute(1, 0, 2).unsqueeze(0)
-        k1 = kt[a:b, :, 0].permute(1, 0, 2).unsqueeze(0)
-        k2 = kt[a:b, :, 1].permute(1, 0, 2).unsqueeze(0)
-        vv = vt[a:b].permute(1, 0, 2).unsqueeze(0)
+        k1 = kt[ka:kb, :, 0].permute(1, 0, 2).unsqueeze(0)
+        k2 = kt[ka:kb, :, 1].permute(1, 0, 2).unsqueeze(0)
+        vv = vt[ka:kb].permute(1, 0, 2).unsqueeze(0)
         sc = 1.0 / math.sqrt(d)
-        o1 = F.scaled_dot_product_attention(q1, k1, vv, is_causal=causal,
-                                            scale=sc, enable_gqa=True)
-        o2 = F.scaled_dot_product_attention(q2, k2, vv, is_causal=causal,
-                                            scale=sc, enable_gqa=True)
+        if kb - ka == b - a:
+            kw = dict(is_causal=causal)
+        else:
+            mask = torch.ones(b - a, kb - ka, dtype=torch.bool)
+            kw = dict(attn_mask=mask.tril((kb - ka) - (b - a)) if causal else None)
+        o1 = F.scaled_dot_product_attention(q1, k1, vv, scale=sc,
+                                            enable_gqa=True, **kw)
+        o2 = F.scaled_dot_product_attention(q2, k2, vv, scale=sc,
+                                            enable_gqa=True, **kw)
         lam_t = torch.as_tensor(np.asarray(lam, dtype=np.float64)).reshape(-1, 1, 1)
         o = o1 - lam_t * o2
         o = F.rms_norm(o, (2 * d,), weight=wt, eps=eps) * (1.0 - lam_init)
@@ -367,6 +386,96 @@ def pin_rows_entry(lib):
     assert np.array_equal(got, full[toks, heads])
 
 
+# --------------------------------------------------------------------------
+# new queries against a key/value cache
+
+def kv_inputs(seed, nq, nk, H, Hkv, d, q_scale=1.0):
+    """Queries of ``sum(nq)`` tokens, keys/values of ``sum(nk)`` tokens."""
+    rng = np.random.default_rng(seed)
+    Tq, Tk = int(sum(nq)), int(sum(nk))
+    q = (rng.standard_normal((Tq, H, 2, d)) * q_scale).astype(np.float32)
+    k = rng.standard_normal((Tk, Hkv, 2, d)).astype(np.float32)
+    v = rng.standard_normal((Tk, Hkv, 2 * d)).astype(np.float32)
+    lv = [(0.3 * rng.standard_normal(d)).astype(np.float32) for _ in range(4)]
+    w = (0.5 + rng.random(2 * d)).astype(np.float32)
+    cq = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    ck = np.concatenate([[0], np.cumsum(nk)]).astype(np.int32)
+    return q, k, v, lv, w, cq, ck
+
+
+def run_kv(lib, q, k, v, lv, lam_init, w, eps, causal, cq, ck):
+    return oracle.fwd_kv(q, k, v, *lv, lam_init, w, eps, causal, cq, ck, lib=lib)
+
+
+def pin_kv_brute_force(lib):
+    cases = [
+        # seed, query lengths, key lengths, H, Hkv, d, causal
+        (101, (1, 3), (5, 7), 4, 2, 3, True),
+        (102, (2, 4), (6, 3), 2, 1, 2, False),   # more queries than keys
+        (103, (1, 1, 2), (1, 4, 2), 2, 2, 4, True),
+        (104, (3,), (9,), 4, 1, 2, True),
+    ]
+    for seed, nq, nk, H, Hkv, d, causal in cases:
+        q, k, v, lv, w, cq, ck = kv_inputs(seed, nq, nk, H, Hkv, d)
+        if seed == 104:                        # one set of vectors per head
+            rng = np.random.default_rng(1040)
+            lv = [(0.4 * rng.standard_normal((H, d))).astype(np.float32)
+                  for _ in range(4)]
+        lam_init = 0.8 - 0.6 * math.exp(-0.3 * (seed - 100))
+        got = run_kv(lib, q, k, v, lv, lam_init, w, 1e-5, causal, cq, ck)
+        ref = brute_mpmath(q, k, v, lv, lam_init, w, 1e-5, causal, cq, cu_k=ck)
+        err = np.max(np.abs(got - ref))
+        assert np.all(np.isfinite(got)), f"non-finite oracle output, case {seed}"
+        assert err < 1e-12, f"kv brute force case {seed}: max-abs {err:.3e}"
+
+
+def pin_kv_sdpa(lib):
+    for causal in (True, False):
+        q, k, v, lv, w, cq, ck = kv_inputs(110, (1, 5, 16, 2), (40, 5, 100, 77),
+                                           8, 2, 16)
+        lam_init = 0.8 - 0.6 * math.exp(-0.3 * 11)
+        lam = (math.exp(float(np.dot(lv[0].astype(np.float64), lv[1])))
+               - math.exp(float(np.dot(lv[2].astype(np.float64), lv[3])))
+               + lam_init)
+        got = run_kv(lib, q, k, v, lv, lam_init, w, 1e-5, causal, cq, ck)
+        ref = sdpa_diff(q, k, v, lam, lam_init, w, 1e-5, causal, cq, cu_k=ck)
+        err = np.max(np.abs(got - ref))
+        assert err < 1e-10, f"kv vs SDPA (causal={causal}): max-abs {err:.3e}"
+
+
+def pin_kv_prefill_tail(lib):
+    """The last nq rows of a causal prefill are nq new queries against the
+    whole sequence as their cache (same arithmetic, so bitwise)."""
+    seqlens = (12, 1, 30)
+    tails = (4, 1, 7)
+    q, k, v, lv, w, cu = tiny_inputs(120, seqlens, 4, 2, 4)
+    full = run(lib, q, k, v, lv, 0.35, w, 1e-5, True, cu)
+    rows = np.concatenate([np.arange(int(cu[s + 1]) - tails[s], int(cu[s + 1]))
+                           for s in range(len(seqlens))])
+    cq = np.concatenate([[0], np.cumsum(tails)]).astype(np.int32)
+    got = run_kv(lib, q[rows], k, v, lv, 0.35, w, 1e-5, True, cq, cu)
+    assert np.array_equal(got, full[rows])
+    # nq = nk is the prefill itself, causal or not
+    for causal in (True, False):
+        assert np.array_equal(run_kv(lib, q, k, v, lv, 0.35, w, 1e-5, causal, cu, cu),
+                              run(lib, q, k, v, lv, 0.35, w, 1e-5, causal, cu))
+
+
+def pin_kv_single_key(lib):
+    """One query against a one-key cache (or the cache's first key only,
+    causal with nq = nk): pre = (1 - lambda) V[key]."""
+    q, k, v, lv, w, cq, ck = kv_inputs(130, (1, 1), (1, 1), 2, 1, 4)
+    lam_init = 0.45
+    lam = (math.exp(float(np.dot(lv[0].astype(np.float64), lv[1])))
+           - math.exp(float(np.dot(lv[2].astype(np.float64), lv[3])))
+           + lam_init)
+    got = run_kv(lib, q, k, v, lv, lam_init, w, 1e-5, True, cq, ck)
+    for s in range(2):
+        pre = (1.0 - lam) * v[s, 0].astype(np.float64)
+        ref = pre / math.sqrt(np.mean(pre * pre) + 1e-5) * w * (1.0 - lam_init)
+        assert np.max(np.abs(got[s] - ref)) < 1e-12
+
+
 ALL_PINS = [
     pin_lambda_closed_forms,
     pin_brute_force,
@@ -381,4 +490,8 @@ ALL_PINS = [
     pin_gqa_equals_repeated,
     pin_odd_in_v,
     pin_rows_entry,
+    pin_kv_brute_force,
+    pin_kv_sdpa,
+    pin_kv_prefill_tail,
+    pin_kv_single_key,
 ]

@@ -26,3 +26,12 @@ def test_rejects_malformed_arguments(lib):
         oracle.fwd(q, k, v, *lv, 0.2, w, 1e-5, True, np.array([0, 5, 4, 8], np.int32), lib=lib)
     with pytest.raises(ValueError):     # token out of range
         oracle.rows(q, k, v, *lv, 0.2, [8], [0], w, 1e-5, True, cu, lib=lib)
+
+
+def test_kv_rejects_malformed_arguments(lib):
+    q, k, v, lv, w, cq, ck = pins.kv_inputs(0, (3, 1), (2, 4), 2, 1, 2)
+    with pytest.raises(ValueError):     # causal: 3 queries, 2 keys
+        pins.run_kv(lib, q, k, v, lv, 0.2, w, 1e-5, True, cq, ck)
+    q, k, v, lv, w, cq, ck = pins.kv_inputs(0, (1, 1), (0, 4), 2, 1, 2)
+    with pytest.raises(ValueError):     # a query with no keys at all
+        pins.run_kv(lib, q, k, v, lv, 0.2, w, 1e-5, False, cq, ck)

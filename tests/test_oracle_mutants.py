@@ -16,8 +16,11 @@ MUTANTS = {
     "lambda_drop_init": ("exp(dot1) - exp(dot2) + lambda_init", "exp(dot1) - exp(dot2)"),
     "lambda_swap_terms": ("exp(dot1) - exp(dot2)", "exp(dot2) - exp(dot1)"),
     "lambda_init_schedule": ("-0.3 * (double)(depth - 1)", "-0.3 * (double)depth"),
-    "causal_ignored": ("causal ? i + 1 : n", "causal ? n : n"),
-    "causal_strict": ("causal ? i + 1 : n", "causal ? (i > 0 ? i : 1) : n"),
+    "causal_ignored": ("return causal ? i + 1 : n;", "return causal ? n : n;"),
+    "causal_strict": ("return causal ? i + 1 : n;", "return causal ? (i > 0 ? i : 1) : n;"),
+    "decode_alignment_top_left": ("causal ? nk - nq + i + 1 : nk", "causal ? nq - nq + i + 1 : nk"),
+    "decode_alignment_off_by_one": ("causal ? nk - nq + i + 1 : nk", "causal ? nk - nq + i : nk"),
+    "decode_keys_from_query_offsets": ("t, cu_k[s], nkeys", "t, cu_q[s], nkeys"),
     "gqa_modulo": ("h / (H / Hkv)", "h % Hkv"),
     "scale_full_width": ("1.0 / sqrt((double)d)", "1.0 / sqrt(2.0 * d)"),
     "scale_squared": ("1.0 / sqrt((double)d)", "1.0 / (double)d"),
@@ -26,9 +29,9 @@ MUTANTS = {
     "final_scale_dropped": ("* wc * (1.0 - lambda_init)", "* wc"),
     "weight_ignored": ("w ? (double)w[c] : 1.0", "1.0"),
     "k_map_swapped": ("+ g) * 2 + map) * (int64_t)d", "+ g) * 2 + (1 - map)) * (int64_t)d"),
-    "q_map_swapped": ("+ h) * 2 + map) * (int64_t)d", "+ h) * 2 + (1 - map)) * (int64_t)d"),
-    "key_row_is_query_row": ("k + (((a + j) * Hkv", "k + (((a + i) * Hkv"),
-    "v_uses_query_head": ("((a + j) * Hkv + g) * (int64_t)dv", "((a + j) * Hkv + h % Hkv) * (int64_t)dv"),
+    "q_map_swapped": ("((qt * H + h) * 2 + map)", "((qt * H + h) * 2 + (1 - map))"),
+    "key_row_is_query_row": ("k + (((ka + j) * Hkv", "k + (((qt) * Hkv"),
+    "v_uses_query_head": ("((ka + j) * Hkv + g) * (int64_t)dv", "((ka + j) * Hkv + h % Hkv) * (int64_t)dv"),
     "softmax_no_max_shift": ("exp(p[j] - mx)", "exp(p[j])"),
     "softmax_wrong_normaliser": ("p[j] /= z;", "p[j] /= (double)nkeys;"),
     "per_head_lambda_offset": ("const int64_t o = (int64_t)h * stride;", "const int64_t o = 0 * stride;"),
