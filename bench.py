@@ -13,6 +13,11 @@ FLOP per unmasked (query, key) pair with n^2/2 pairs per causal sequence;
 ``roofline`` relates the measured kernel time to MI355X's dense bf16 MFMA
 peak; ``cpu_baseline`` times the fp64 oracle on the host cores on a bounded
 sample of the same workload.
+
+``--workload decode_...`` measures the key/value-cache path instead (one
+step = one diffattn_fwd_kv call: the split-KV partial kernel and the
+combine kernel); its ``value`` is GB/s of the bytes the step must move (q,
+k, v read once, out written once) against MI355X's 8 TB/s HBM peak.
 """
 
 from __future__ import annotations
@@ -34,21 +39,25 @@ if HERE not in sys.path:
 PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12
 # fp32 MFMA (matrix) peak, for fp32-storage workloads.
 PEAK_F32_TFLOPS = 157.3
+# MI355X HBM3E peak bandwidth
+PEAK_HBM_GBS = 8000.0
 METRIC = "diff-attention fwd TFLOP/s & % bf16 MFMA peak, 1 MI355X, N=4096 causal"
-KERNEL_SOURCES = [os.path.join(HERE, "differential_attention_amd", "csrc",
-                               "diffattn_fwd.hip"),
-                  os.path.join(HERE, "include", "diffattn.h")]
+METRIC_KV = "diff-attention KV-cache decode GB/s & % HBM peak, 1 MI355X"
+_CSRC = os.path.join(HERE, "differential_attention_amd", "csrc")
+_HEADER = os.path.join(HERE, "include", "diffattn.h")
+KERNEL_SOURCES = [os.path.join(_CSRC, "diffattn_fwd.hip"), _HEADER]
+KV_KERNEL_SOURCES = [os.path.join(_CSRC, "diffattn_kv.hip"), _HEADER]
 
 
-def kernel_digest() -> str:
+def kernel_digest(sources=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in sources:
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(workload: str):
+def traffic_from_profiles(workload: str, sources=KERNEL_SOURCES):
     """HBM bytes per launch from the committed counter summary, if it was
     taken on the current kernel source; else None."""
     path = os.path.join(HERE, "profiles", f"hbm_traffic_{workload}.md")
@@ -57,7 +66,7 @@ def traffic_from_profiles(workload: str):
     text = open(path).read()
     m = re.search(r"kernel_digest:\s*([0-9a-f]+)", text)
     t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m or not t or m.group(1) != kernel_digest():
+    if not m or not t or m.group(1) != kernel_digest(sources):
         return None
     return float(t.group(1))
 
@@ -95,6 +104,118 @@ def cpu_baseline(wl, inp, flop_budget: float = 1.0e12):
             "sample": (f"{what} x all {wl.H} heads ({toks.size * wl.H} output "
                        f"rows, {flops / 1e9:.1f} GFLOP under the counting "
                        "convention); fp64 C oracle, OpenMP over rows")}
+
+
+def cpu_baseline_kv(wl, inp, byte_budget: float = 4.0e8):
+    """The fp64 oracle on every s-th sequence of a cache workload (all its
+    queries and heads), s >= 1 chosen so that the sample's cache holds at
+    most ``byte_budget`` bytes; reported in GB/s of the sample's bytes."""
+    import numpy as np
+    import oracle
+    es = 2 if wl.dtype == "bf16" else 4
+    per_seq = [es * (2 * nq * wl.H * 2 * wl.d + 2 * nk * wl.Hkv * 2 * wl.d)
+               for nq, nk in zip(wl.q_lens, wl.k_lens)]
+    stride = max(1, int(np.ceil(sum(per_seq) / byte_budget)))
+    seqs = list(range(0, wl.nseq, stride))
+    cq, ck = wl.cu_q(), wl.cu_k()
+    qi = np.concatenate([np.arange(cq[s], cq[s + 1]) for s in seqs])
+    ki = np.concatenate([np.arange(ck[s], ck[s + 1]) for s in seqs])
+    q, k, v = (oracle._f32(x) for x in (inp.q[qi], inp.k[ki], inp.v[ki]))
+    lv = [oracle._f32(x) for x in (inp.lq1, inp.lk1, inp.lq2, inp.lk2)]
+    cqs = np.concatenate([[0], np.cumsum([wl.q_lens[s] for s in seqs])])
+    cks = np.concatenate([[0], np.cumsum([wl.k_lens[s] for s in seqs])])
+    oracle.load()
+    t0 = time.perf_counter()
+    oracle.fwd_kv(q, k, v, *lv, oracle.lambda_init(wl.depth),
+                  oracle._f32(inp.w), wl.eps, wl.causal, cqs, cks)
+    dt = time.perf_counter() - t0
+    nbytes = float(sum(per_seq[s] for s in seqs))
+    what = ("every sequence" if stride == 1 else
+            f"one sequence in {stride} ({len(seqs)} of {wl.nseq})")
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": oracle.max_threads(),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": (f"{what}, all queries and heads ({nbytes / 1e6:.1f} MB of "
+                       "q/k/v/out in the storage type); fp64 C oracle, OpenMP "
+                       "over output rows")}
+
+
+def bench_kv(args, name) -> int:
+    import torch
+    import workloads
+    import differential_attention_amd as da
+
+    wl = workloads.KV_WORKLOADS[name]
+    inp = workloads.make_kv_inputs(wl)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    c = lambda t: t.to(dev).contiguous()
+    q, k, v = c(inp.q), c(inp.k), c(inp.v)
+    lv = [c(x) for x in (inp.lq1, inp.lk1, inp.lq2, inp.lk2)]
+    w, cq, ck = c(inp.w), c(inp.cu_q), c(inp.cu_k)
+    out = torch.empty((wl.Tq, wl.H, 2 * wl.d), dtype=q.dtype, device=dev)
+    need = da.kv_workspace_size(wl.nseq, wl.max_q, wl.max_k, wl.H, wl.Hkv, wl.d)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream(dev)
+    ptrs = (da.BF16, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+            *[x.data_ptr() for x in lv], 0, da.lambda_init(wl.depth),
+            w.data_ptr(), wl.eps, int(wl.causal), cq.data_ptr(), ck.data_ptr(),
+            wl.nseq, wl.max_q, wl.max_k, wl.Tq, wl.Tk, wl.H, wl.Hkv, wl.d,
+            ws.data_ptr(), need, out.data_ptr(), stream.cuda_stream)
+
+    def step():
+        st = da.fwd_kv_ptr(*ptrs)
+        if st != 0:
+            raise da.DiffAttnError(st, "diffattn_fwd_kv")
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            step()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    nbytes = wl.bytes()
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC_KV,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded N(0,1) q/k/v, N(0,0.1^2) lambda vectors)",
+        "config": {"workload": name, "nseq": wl.nseq, "Tq": wl.Tq, "Tk": wl.Tk,
+                   "max_q": wl.max_q, "max_k": wl.max_k, "H": wl.H,
+                   "Hkv": wl.Hkv, "d": wl.d, "depth": wl.depth,
+                   "causal": wl.causal, "bytes_per_step": nbytes,
+                   "tokens_per_s": round(wl.Tq / (ms * 1e-3), 1),
+                   "tflops": round(wl.flops() / (ms * 1e-3) / 1e12, 2),
+                   "workspace_bytes": need,
+                   "wall_s_timed": round(wall, 4),
+                   "kernel_digest": kernel_digest(KV_KERNEL_SOURCES)},
+        # both kernels of the step are in the timed duration, so this is a
+        # lower bound on the partial kernel's own rate
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": traffic_from_profiles(name, KV_KERNEL_SOURCES)},
+    }
+    result["cpu_baseline"] = (None if args.no_cpu_baseline
+                              else cpu_baseline_kv(wl, inp))
+    print(json.dumps(result), flush=True)
+    return 0
 
 
 def copy_calibration(args) -> int:
@@ -145,6 +266,8 @@ def main() -> int:
     import differential_attention_amd as da
 
     name = args.workload or workloads.HEADLINE
+    if name in workloads.KV_WORKLOADS:
+        return bench_kv(args, name)
     wl = workloads.WORKLOADS[name]
     inp = workloads.make_inputs(wl)
     dev = torch.device("cuda:0")

@@ -17,8 +17,10 @@ from typing import Optional
 
 import torch
 
-__all__ = ["fwd", "fwd_ptr", "lambda_init", "supported", "check_cu_seqlens",
-           "library", "LIBRARY", "DiffAttnError", "BF16", "F32"]
+__all__ = ["fwd", "fwd_ptr", "fwd_kv", "fwd_kv_ptr", "kv_workspace_size",
+           "lambda_init", "supported", "supported_kv", "check_cu_seqlens",
+           "check_cu_seqlens_kv", "library", "LIBRARY", "DiffAttnError",
+           "BF16", "F32"]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "libdiffattn.so")
@@ -54,6 +56,19 @@ def library() -> ctypes.CDLL:
         f32p, ctypes.c_float, ctypes.c_int, i32p, i32, i32, i32, i32, i32, i32,
         vp, vp]
     lib.diffattn_fwd.restype = ctypes.c_int
+    lib.diffattn_fwd_kv.argtypes = [
+        ctypes.c_int, vp, vp, vp, f32p, f32p, f32p, f32p, i32, ctypes.c_float,
+        f32p, ctypes.c_float, ctypes.c_int, i32p, i32p, i32, i32, i32, i32,
+        i32, i32, i32, i32, vp, ctypes.c_size_t, vp, vp]
+    lib.diffattn_fwd_kv.restype = ctypes.c_int
+    lib.diffattn_fwd_kv_workspace_size.argtypes = [i32] * 6
+    lib.diffattn_fwd_kv_workspace_size.restype = ctypes.c_size_t
+    lib.diffattn_supported_kv.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.diffattn_supported_kv.restype = ctypes.c_int
+    lib.diffattn_check_cu_seqlens_kv.argtypes = [
+        ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32), i32,
+        i32, i32, i32, i32, ctypes.c_int]
+    lib.diffattn_check_cu_seqlens_kv.restype = ctypes.c_int
     lib.diffattn_lambda_init.argtypes = [ctypes.c_int]
     lib.diffattn_lambda_init.restype = ctypes.c_double
     lib.diffattn_supported.argtypes = [ctypes.c_int, ctypes.c_int]
@@ -89,6 +104,51 @@ def check_cu_seqlens(cu_host, T: int, max_seqlen: int) -> bool:
     ptr = ctypes.cast(cu.data_ptr(), ctypes.POINTER(ctypes.c_int32))
     return library().diffattn_check_cu_seqlens(ptr, cu.numel() - 1, int(T),
                                                int(max_seqlen)) == OK
+
+
+def supported_kv(dtype: torch.dtype, d: int) -> bool:
+    return bool(library().diffattn_supported_kv(_DTYPES[dtype], int(d)))
+
+
+def check_cu_seqlens_kv(cu_q_host, cu_k_host, Tq: int, Tk: int,
+                        max_seqlen_q: int, max_seqlen_k: int,
+                        causal: bool = True) -> bool:
+    """Host-side precondition check of CPU copies of both boundaries."""
+    cq = torch.as_tensor(cu_q_host, dtype=torch.int32).contiguous().cpu()
+    ck = torch.as_tensor(cu_k_host, dtype=torch.int32).contiguous().cpu()
+    if cq.numel() != ck.numel():
+        return False
+    P = ctypes.POINTER(ctypes.c_int32)
+    return library().diffattn_check_cu_seqlens_kv(
+        ctypes.cast(cq.data_ptr(), P), ctypes.cast(ck.data_ptr(), P),
+        cq.numel() - 1, int(Tq), int(Tk), int(max_seqlen_q),
+        int(max_seqlen_k), int(bool(causal))) == OK
+
+
+def kv_workspace_size(nseq: int, max_seqlen_q: int, max_seqlen_k: int,
+                      H: int, Hkv: int, d: int) -> int:
+    """Bytes of device workspace ``fwd_kv`` needs (0: sizes rejected)."""
+    return int(library().diffattn_fwd_kv_workspace_size(
+        int(nseq), int(max_seqlen_q), int(max_seqlen_k), int(H), int(Hkv),
+        int(d)))
+
+
+def fwd_kv_ptr(dtype: int, q: int, k: int, v: int, lq1: int, lk1: int,
+               lq2: int, lk2: int, lambda_stride: int,
+               lambda_init_value: float, subln_weight: int, eps: float,
+               causal: int, cu_seqlens_q: int, cu_seqlens_k: int, nseq: int,
+               max_seqlen_q: int, max_seqlen_k: int, Tq: int, Tk: int, H: int,
+               Hkv: int, d: int, workspace: int, workspace_bytes: int,
+               out: int, stream: int) -> int:
+    """The raw cache entry point on integer device addresses; returns the
+    status."""
+    return library().diffattn_fwd_kv(
+        int(dtype), q or None, k or None, v or None, lq1 or None, lk1 or None,
+        lq2 or None, lk2 or None, int(lambda_stride), float(lambda_init_value),
+        subln_weight or None, float(eps), int(causal), cu_seqlens_q or None,
+        cu_seqlens_k or None, int(nseq), int(max_seqlen_q), int(max_seqlen_k),
+        int(Tq), int(Tk), int(H), int(Hkv), int(d), workspace or None,
+        int(workspace_bytes), out or None, stream or None)
 
 
 def fwd_ptr(dtype: int, q: int, k: int, v: int, lq1: int, lk1: int, lq2: int,
@@ -191,4 +251,101 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                      out_ptr, stream.cuda_stream)
     if st != OK:
         raise DiffAttnError(st, "diffattn_fwd")
+    return out
+
+
+def _lambda_args(lvs, H, d, dev):
+    per_head = lvs[0].dim() == 2
+    ptrs = []
+    for name, lv in zip(("lambda_q1", "lambda_k1", "lambda_q2", "lambda_k2"), lvs):
+        want = (H, d) if per_head else (d,)
+        if tuple(lv.shape) != want:
+            raise ValueError(f"{name} must be {list(want)}")
+        ptrs.append(_dev(lv, name, dev, torch.float32))
+    return ptrs, (d if per_head else 0)
+
+
+def fwd_kv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+           lambda_q1: torch.Tensor, lambda_k1: torch.Tensor,
+           lambda_q2: torch.Tensor, lambda_k2: torch.Tensor,
+           lambda_init: float, subln_weight: Optional[torch.Tensor] = None,
+           eps: float = 1e-5, causal: bool = True,
+           cu_seqlens_q: Optional[torch.Tensor] = None,
+           cu_seqlens_k: Optional[torch.Tensor] = None,
+           max_seqlen_q: Optional[int] = None,
+           max_seqlen_k: Optional[int] = None, nseq: Optional[int] = None,
+           workspace: Optional[torch.Tensor] = None,
+           out: Optional[torch.Tensor] = None,
+           stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """New queries against a key/value cache on the GPU (bottom-right causal).
+
+    q [Tq, H, 2, d]; k [Tk, Hkv, 2, d], v [Tk, Hkv, 2d] (bf16); lambda
+    vectors fp32 [d] or [H, d]; cu_seqlens_q / cu_seqlens_k int32
+    [nseq + 1] on the device, both or neither (neither: ``nseq`` equal
+    sequences).  When the bounds are not given they are read back from the
+    device (a synchronising copy).  ``workspace`` is a device uint8 tensor of
+    at least ``kv_workspace_size(...)`` bytes; one is allocated through
+    torch when it is None.  Returns ``out`` [Tq, H, 2d].
+    """
+    if q.dim() != 4 or q.shape[2] != 2:
+        raise ValueError("q must be [Tq, H, 2, d]")
+    Tq, H, _, d = q.shape
+    if k.dim() != 4 or k.shape[2:] != (2, d):
+        raise ValueError("k must be [Tk, Hkv, 2, d]")
+    Tk, Hkv = k.shape[0], k.shape[1]
+    if tuple(v.shape) != (Tk, Hkv, 2 * d):
+        raise ValueError("v must be [Tk, Hkv, 2d]")
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("q must be a GPU tensor")
+    qp, kp, vp_ = (_dev(q, "q", dev), _dev(k, "k", dev, q.dtype),
+                   _dev(v, "v", dev, q.dtype))
+    lptrs, lambda_stride = _lambda_args(
+        (lambda_q1, lambda_k1, lambda_q2, lambda_k2), H, d, dev)
+    w_ptr = 0
+    if subln_weight is not None:
+        if subln_weight.numel() != 2 * d:
+            raise ValueError("subln_weight must have 2d elements")
+        w_ptr = _dev(subln_weight, "subln_weight", dev, torch.float32)
+    if (cu_seqlens_q is None) != (cu_seqlens_k is None):
+        raise ValueError("give both cu_seqlens_q and cu_seqlens_k, or neither")
+    cq_ptr = ck_ptr = 0
+    if cu_seqlens_q is not None:
+        if cu_seqlens_q.numel() != cu_seqlens_k.numel():
+            raise ValueError("cu_seqlens_q and cu_seqlens_k differ in length")
+        cq_ptr = _dev(cu_seqlens_q, "cu_seqlens_q", dev, torch.int32)
+        ck_ptr = _dev(cu_seqlens_k, "cu_seqlens_k", dev, torch.int32)
+        nseq = cu_seqlens_q.numel() - 1
+        if max_seqlen_q is None:
+            c = cu_seqlens_q.cpu()
+            max_seqlen_q = int((c[1:] - c[:-1]).max()) if nseq > 0 else 0
+        if max_seqlen_k is None:
+            c = cu_seqlens_k.cpu()
+            max_seqlen_k = int((c[1:] - c[:-1]).max()) if nseq > 0 else 0
+    else:
+        nseq = 1 if nseq is None else int(nseq)
+        max_seqlen_q = Tq // nseq if nseq > 0 else 0
+        max_seqlen_k = Tk // nseq if nseq > 0 else 0
+    need = kv_workspace_size(nseq, max(max_seqlen_q, 1), max(max_seqlen_k, 1),
+                             H, Hkv, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    ws_ptr = _dev(workspace, "workspace", dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if out is None:
+        out = torch.empty((Tq, H, 2 * d), dtype=q.dtype, device=dev)
+    elif tuple(out.shape) != (Tq, H, 2 * d):
+        raise ValueError("out must be [Tq, H, 2d]")
+    out_ptr = _dev(out, "out", dev, q.dtype)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        st = fwd_kv_ptr(_DTYPES[q.dtype], qp, kp, vp_, *lptrs, lambda_stride,
+                        lambda_init, w_ptr, eps, int(bool(causal)), cq_ptr,
+                        ck_ptr, nseq, max_seqlen_q, max_seqlen_k, Tq, Tk, H,
+                        Hkv, d, ws_ptr, ws_bytes, out_ptr, stream.cuda_stream)
+    if st != OK:
+        raise DiffAttnError(st, "diffattn_fwd_kv")
     return out

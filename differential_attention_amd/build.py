@@ -9,7 +9,8 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = [os.path.join(HERE, "csrc", "diffattn_fwd.hip")]
+SOURCES = [os.path.join(HERE, "csrc", "diffattn_fwd.hip"),
+           os.path.join(HERE, "csrc", "diffattn_kv.hip")]
 LIBRARY = os.path.join(HERE, "libdiffattn.so")
 ARCH = "gfx950"
 

@@ -1,0 +1,672 @@
+// diffattn_kv.hip -- differential attention of new queries against a
+// key/value cache, for CDNA4 (gfx950).
+//
+// The operation is the one defined for diffattn_fwd_kv in include/diffattn.h:
+// the LlamaDiffSdpaAttention.py gist's forward appends the step's keys and
+// values to the cache and then attends with both maps; the causal mask is
+// aligned bottom-right, as the FlashDiffAttention pull request's
+// alternative_forward builds it (-inf above diagonal 1 + src_len - tgt_len),
+// so query i of nq sees cache keys 0 .. nk - nq + i.
+//
+// Why a second kernel
+// -------------------
+// A decode step has a handful of query rows per KV head (G heads x nq
+// queries) against thousands of keys: every K/V byte feeds only G * nq rows,
+// so the work is bound by reading the cache from HBM, not by MFMA.  The
+// design goal is to stream K and V once, with enough bytes in flight on
+// every CU, and to keep the GQA sharing (one K/V read serves all G heads of
+// a group).
+//
+// Split-KV partial kernel
+// -----------------------
+// One wave = (sequence s, KV head g, block of 16 query rows, split of Ck
+// keys).  A row is (query i, head gh of the group), row r = i * G + gh.
+// Waves are independent: each has a private LDS slice for its V tile and no
+// barrier is ever taken.  Per 32-key block:
+//   * K of both maps goes global -> registers directly in the A-operand
+//     layout of v_mfma_f32_16x16x32_bf16 (lane (key n, quarter q) holds
+//     8 consecutive dims), one block ahead of use;
+//   * V goes global -> registers one block ahead, then into the wave's
+//     padded LDS tile, and comes back through the transposing read
+//     ds_read_b64_tr_b16 as the V^T operand;
+//   * S^T [16 keys x 16 rows] = K Q^T per map and 16-key half: each lane
+//     owns one row and 4 keys of each half, so the accumulator is directly
+//     the P^T operand of the PV product when the contraction runs over keys
+//     {4q..4q+3} U {16+4q..16+4q+3} -- the order the transposing read
+//     produces;
+//   * O_m^T [2d x 16 rows] += V^T P_m^T; one V^T operand feeds both maps.
+// The softmax keeps, per map and row, a lazily raised maximum (log2 units)
+// and a running sum; the partial (m, l, O) of the split is written to the
+// caller's workspace in fp32.
+//
+// Combine kernel
+// --------------
+// One wave per output row (token, head): merges the splits' partials of
+// both maps by log-sum-exp, then applies the epilogue that the prefill
+// kernel fuses -- lambda from the four vectors, O_1/l_1 - lambda O_2/l_2,
+// RMSNorm over 2d, the weight and the (1 - lambda_init) scale -- and stores
+// in the input dtype.  Partial outputs cannot simply be summed: the
+// combination is nonlinear in the two maps' normalisers.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "diffattn.h"
+
+namespace {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWavesPerBlock = 4;
+constexpr int kThreads = 64 * kWavesPerBlock;
+constexpr int kRows = 16;      // query rows per wave
+constexpr int kBlockKeys = 32; // keys per inner block
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescaleLog2 = 8.0f;
+
+struct KvParams {
+    const void *q;
+    const void *k;
+    const void *v;
+    void *out;
+    const float *lq1, *lk1, *lq2, *lk2;
+    int64_t lstride;
+    const float *w;
+    const int32_t *cuq;   // NULL: uniform lengths qlen_uniform
+    const int32_t *cuk;   // NULL: uniform lengths klen_uniform
+    float *ws_o;          // [nseq][Hkv][nsplit][rmax][2][2d]
+    float *ws_ml;         // [nseq][Hkv][nsplit][rmax][4]: m, l of map 1, m, l of map 2
+    float lambda_init;
+    float eps;
+    int32_t H, Hkv, G, nseq, causal;
+    int32_t qlen_uniform, klen_uniform;
+    int32_t max_q;        // queries per sequence at most
+    int32_t rmax;         // G * max_q rows per (sequence, group)
+    int32_t nrb;          // 16-row blocks per (sequence, group)
+    int32_t nsplit;       // key splits per (sequence, group)
+    int32_t ck;           // keys per split (multiple of 32)
+};
+
+__device__ inline void seq_bounds(const int32_t *cu, int uniform, int s, int &a, int &n)
+{
+    if (cu) {
+        a = cu[s];
+        n = cu[s + 1] - a;
+    } else {
+        a = s * uniform;
+        n = uniform;
+    }
+}
+
+// Combined value over the four lanes l, l^16, l^32, l^48 (the quarter-waves
+// of one row); the order of combination is fixed, so all four lanes get
+// bitwise the same result.
+__device__ inline float quad_max(float x)
+{
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y),
+                                                    false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ inline float quad_sum(float x)
+{
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y),
+                                                    false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+__device__ inline f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void diffattn_kv_partial(KvParams p)
+{
+    constexpr int NKS = D / 32;              // QK MFMAs per map and 16-key half
+    constexpr int NDT = 2 * D / 16;          // 16-wide tiles of the 2d output
+    constexpr int ROWB = 2 * D * 2;          // bytes of one K (or V) row
+    constexpr int CPR = ROWB / 16;           // 16-byte chunks per row
+    constexpr int RPL = 64 / CPR;            // rows per 64-lane V load
+    constexpr int NVL = kBlockKeys / RPL;    // V loads per lane per block
+    // padded V row: the 8 rows one half-wave reads per transposing read
+    // start 32 bytes apart modulo 256 and cover all banks once
+    constexpr int VROWB = ROWB + 32;
+    static_assert(D % 32 == 0 && NVL * RPL == kBlockKeys, "unsupported d");
+
+    __shared__ __attribute__((aligned(16))) char vlds[kWavesPerBlock][kBlockKeys * VROWB];
+
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15;      // row (S^T column) owned by this lane; key row for K loads
+    const int qq = lane >> 4;     // quarter of the wave
+
+    // ---- work item ---------------------------------------------------------
+    // KV head fastest: the waves of a workgroup (and neighbouring
+    // workgroups) read the other heads' slices of the same key rows at the
+    // same time, so every DRAM page they open is read whole
+    int64_t wid = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+    const int g = (int)(wid % p.Hkv);
+    wid /= p.Hkv;
+    const int rb = (int)(wid % p.nrb);
+    wid /= p.nrb;
+    const int split = (int)(wid % p.nsplit);
+    const int s = (int)(wid / p.nsplit);
+    if (s >= p.nseq)
+        return;
+    int qa, nq, ka, nk;
+    seq_bounds(p.cuq, p.qlen_uniform, s, qa, nq);
+    seq_bounds(p.cuk, p.klen_uniform, s, ka, nk);
+    const int nrows = p.G * min(nq, p.max_q);   // rows of this (sequence, group)
+    const int r0 = rb * kRows;
+    const int kstart = split * p.ck;
+    if (r0 >= nrows || kstart >= nk)
+        return;   // nothing to compute; the combine reads no partial here
+
+    // rows of this wave: r = r0 + n (valid if r < nrows), query i = r / G
+    const int r = r0 + n;
+    const bool row_ok = r < nrows;
+    const int qi = r / p.G;
+    const int i_lo = r0 / p.G;
+    const int i_hi = min(nrows - 1, r0 + kRows - 1) / p.G;
+    // keys this wave can see: [kstart, kend)
+    int kend = min(nk, kstart + p.ck);
+    if (p.causal)
+        kend = min(kend, nk - nq + i_hi + 1);
+    // keys below kvis are visible to every row of the wave
+    const int kvis = p.causal ? min(nk, nk - nq + i_lo + 1) : nk;
+    const int row_lim = p.causal ? min(nk - 1, nk - nq + qi) : nk - 1;
+
+    // ---- Q fragments (B operand of S^T = K Q^T) ----------------------------
+    bf16x8 qf[2][NKS];
+    {
+        const bf16 *qg = (const bf16 *)p.q;
+        const int head = g * p.G + r % p.G;
+        const int64_t tok = (int64_t)qa + qi;
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                if (row_ok)
+                    qf[m][ks] = *(const bf16x8 *)(qg + ((tok * p.H + head) * 2 + m) * D + 32 * ks + 8 * qq);
+                else
+                    qf[m][ks] = bf16x8{};
+            }
+    }
+
+    // ---- accumulators --------------------------------------------------------
+    f32x4 o[2][NDT];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int t = 0; t < NDT; ++t)
+            o[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float mrun[2] = {-INFINITY, -INFINITY};
+    float lsum[2] = {0.f, 0.f};
+    const float c = kLog2e * rsqrtf((float)D);
+
+    // ---- K/V streaming -------------------------------------------------------
+    const int64_t rowstride = (int64_t)p.Hkv * ROWB;    // bytes between keys
+    const char *kbase = (const char *)p.k + (int64_t)ka * rowstride + (int64_t)g * ROWB;
+    const char *vbase = (const char *)p.v + (int64_t)ka * rowstride + (int64_t)g * ROWB;
+    char *vl = vlds[wave];
+    // K register tile: kf[half][map][ks], lane (key n, quarter qq) holds dims
+    // 32 ks + 8 qq .. + 7 of key 16 half + n
+    u32x4 kf[2][2][NKS], kn[2][2][NKS];
+    u32x4 vn[NVL];
+    const int vrow = lane / CPR;
+    const int vcol = (lane % CPR) * 16;
+    auto load_block = [&](int kb) __attribute__((always_inline)) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const int key = min(kb + 16 * hf + n, nk - 1);
+            const char *src = kbase + key * rowstride + 16 * qq;
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+                    kn[hf][m][ks] = *(const u32x4 *)(src + m * (ROWB / 2) + 64 * ks);
+        }
+#pragma unroll
+        for (int i = 0; i < NVL; ++i) {
+            const int key = min(kb + vrow + RPL * i, nk - 1);
+            vn[i] = *(const u32x4 *)(vbase + key * rowstride + vcol);
+        }
+    };
+    auto store_v = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < NVL; ++i)
+            *(u32x4 *)(vl + (vrow + RPL * i) * VROWB + vcol) = vn[i];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+                    kf[hf][m][ks] = kn[hf][m][ks];
+    };
+    // transposing-read base of this lane: row 4 qq + (n / 4), dims 4 (n % 4)
+    const int trbase = (4 * qq + (n >> 2)) * VROWB + 8 * (n & 3);
+
+    if (kstart < kend) {
+        load_block(kstart);
+        store_v();
+    }
+    for (int kb = kstart; kb < kend; kb += kBlockKeys) {
+        const bool more = kb + kBlockKeys < kend;
+        if (more)
+            load_block(kb + kBlockKeys);
+
+        // S^T for both maps and both 16-key halves, in log2 units
+        f32x4 sc[2][2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+                    acc = mma(__builtin_bit_cast(bf16x8, kf[hf][m][ks]), qf[m][ks], acc);
+                sc[m][hf] = acc * c;
+            }
+        // keys past the sequence end or above the row's causal limit
+        if (kb + kBlockKeys > kvis) {
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (kb + 16 * hf + 4 * qq + e > row_lim) {
+                        sc[0][hf][e] = -INFINITY;
+                        sc[1][hf][e] = -INFINITY;
+                    }
+        }
+        // lazily raised maximum; rescale only when a score outgrows it by 2^8
+        float bmax[2];
+        bool grow = false;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            float x = fmaxf(fmaxf(sc[m][0][0], sc[m][0][1]), fmaxf(sc[m][0][2], sc[m][0][3]));
+            x = fmaxf(x, fmaxf(fmaxf(sc[m][1][0], sc[m][1][1]), fmaxf(sc[m][1][2], sc[m][1][3])));
+            bmax[m] = quad_max(x);
+            grow |= bmax[m] > mrun[m] + kRescaleLog2;
+        }
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const float mn = fmaxf(mrun[m], bmax[m]);
+                const float a = mn == -INFINITY ? 1.f : exp2f(mrun[m] - mn);
+                lsum[m] *= a;
+#pragma unroll
+                for (int t = 0; t < NDT; ++t)
+                    o[m][t] *= a;
+                mrun[m] = mn;
+            }
+        }
+        // probabilities, packed as the P^T operand: k = 8 qq + 4 hf + e
+        bf16x8 pf[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const float mref = mrun[m] == -INFINITY ? 0.f : mrun[m];
+            float ps = 0.f;
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float pv = exp2f(sc[m][hf][e] - mref);
+                    ps += pv;
+                    pf[m][4 * hf + e] = (bf16)pv;
+                }
+            lsum[m] += ps;
+        }
+        // O^T += V^T P^T, one V^T operand per 16-wide tile for both maps
+#pragma unroll
+        for (int t = 0; t < NDT; ++t) {
+            bf16x8 va;
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const bf16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (__attribute__((address_space(3))) bf16x4 *)(vl + trbase + 16 * hf * VROWB + 32 * t));
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    va[4 * hf + e] = x[e];
+            }
+            o[0][t] = mma(va, pf[0], o[0][t]);
+            o[1][t] = mma(va, pf[1], o[1][t]);
+        }
+        if (more)
+            store_v();
+    }
+
+    // ---- partial of this split -------------------------------------------
+    if (!row_ok)
+        return;
+    const int64_t slot = (((int64_t)s * p.Hkv + g) * p.nsplit + split) * p.rmax + r;
+    const float l0 = quad_sum(lsum[0]);
+    const float l1 = quad_sum(lsum[1]);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        float *dst = p.ws_o + (slot * 2 + m) * (2 * D);
+#pragma unroll
+        for (int t = 0; t < NDT; ++t)
+            *(f32x4 *)(dst + 16 * t + 4 * qq) = o[m][t];
+    }
+    if (qq == 0)
+        *(f32x4 *)(p.ws_ml + slot * 4) = f32x4{mrun[0], l0, mrun[1], l1};
+}
+
+__device__ inline float wave_sum(float x)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        x += __shfl_xor(x, off, 64);
+    return x;
+}
+__device__ inline float wave_max(float x)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        x = fmaxf(x, __shfl_xor(x, off, 64));
+    return x;
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads)
+void diffattn_kv_combine(KvParams p)
+{
+    constexpr int CPL = 2 * D / 64;   // output columns per lane
+    static_assert(CPL == 1 || CPL == 2, "unsupported d");
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    int64_t wid = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+    const int h = (int)(wid % p.H);
+    wid /= p.H;
+    const int i = (int)(wid % p.max_q);
+    const int s = (int)(wid / p.max_q);
+    if (s >= p.nseq)
+        return;
+    int qa, nq, ka, nk;
+    seq_bounds(p.cuq, p.qlen_uniform, s, qa, nq);
+    seq_bounds(p.cuk, p.klen_uniform, s, ka, nk);
+    if (i >= nq)
+        return;
+    const int g = h / p.G;
+    const int r = i * p.G + h % p.G;
+    const int nsp = min(p.nsplit, (nk + p.ck - 1) / p.ck);
+
+    // lambda of this head
+    float lam;
+    {
+        const int64_t lo = (int64_t)h * p.lstride;
+        float d1 = 0.f, d2 = 0.f;
+        for (int cc = lane; cc < D; cc += 64) {
+            d1 += p.lq1[lo + cc] * p.lk1[lo + cc];
+            d2 += p.lq2[lo + cc] * p.lk2[lo + cc];
+        }
+        d1 = wave_sum(d1);
+        d2 = wave_sum(d2);
+        lam = expf(d1) - expf(d2) + p.lambda_init;
+    }
+
+    // merge the splits of both maps (log-sum-exp in log2 units).  Splits
+    // are taken 64 at a time, one per lane: lane j loads split j's (m, l)
+    // of both maps in one 16-byte read, the wave reduces the maximum and the
+    // weighted sum, and every lane then accumulates its columns of all
+    // splits' O with independent loads.
+    float acc[2][CPL];
+    float M[2] = {-INFINITY, -INFINITY};
+    float L[2] = {0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc)
+            acc[m][cc] = 0.f;
+    const int64_t slot0 = ((int64_t)s * p.Hkv + g) * p.nsplit * p.rmax + r;
+    for (int j0 = 0; j0 < nsp; j0 += 64) {
+        const int j = j0 + lane;
+        f32x4 ml = f32x4{-INFINITY, 0.f, -INFINITY, 0.f};
+        if (j < nsp)
+            ml = *(const f32x4 *)(p.ws_ml + (slot0 + (int64_t)j * p.rmax) * 4);
+        float wgt[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const float mj = ml[2 * m];
+            const float cm = wave_max(mj);
+            const float mn = fmaxf(M[m], cm);
+            // rescale what earlier chunks accumulated (1 on the first chunk)
+            const float fa = M[m] == -INFINITY ? 0.f : exp2f(M[m] - mn);
+            wgt[m] = mj == -INFINITY ? 0.f : exp2f(mj - mn);
+            L[m] = L[m] * fa + wave_sum(ml[2 * m + 1] * wgt[m]);
+#pragma unroll
+            for (int cc = 0; cc < CPL; ++cc)
+                acc[m][cc] *= fa;
+            M[m] = mn;
+        }
+        // four splits per step with independent loads; past the last split
+        // the step re-reads the last one with weight 0
+        const int nj = min(64, nsp - j0);
+        for (int jj = 0; jj < nj; jj += 4) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int jc = min(jj + u, nj - 1);
+                const float keep = jj + u < nj ? 1.f : 0.f;
+                const float *op = p.ws_o + (slot0 + (int64_t)(j0 + jc) * p.rmax) * 2 * (2 * D) + CPL * lane;
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    const float wj = keep * __int_as_float(
+                        __builtin_amdgcn_readlane(__float_as_int(wgt[m]), jc));
+#pragma unroll
+                    for (int cc = 0; cc < CPL; ++cc)
+                        acc[m][cc] += wj * op[m * 2 * D + cc];
+                }
+            }
+        }
+    }
+
+    // epilogue: combine the maps, RMSNorm over 2d, weight, scale, store
+    float pre[CPL];
+    float ss = 0.f;
+    const float i1 = 1.f / L[0], i2 = lam / L[1];
+#pragma unroll
+    for (int cc = 0; cc < CPL; ++cc) {
+        pre[cc] = acc[0][cc] * i1 - acc[1][cc] * i2;
+        ss += pre[cc] * pre[cc];
+    }
+    ss = wave_sum(ss);
+    const float scale = rsqrtf(ss / (float)(2 * D) + p.eps) * (1.f - p.lambda_init);
+    bf16 *dst = (bf16 *)p.out + ((int64_t)(qa + i) * p.H + h) * (2 * D) + CPL * lane;
+#pragma unroll
+    for (int cc = 0; cc < CPL; ++cc) {
+        const float wc = p.w ? p.w[CPL * lane + cc] : 1.f;
+        dst[cc] = (bf16)(pre[cc] * scale * wc);
+    }
+}
+
+// Split policy: enough waves to keep every CU streaming (about 16 per CU),
+// but at least 128 keys per split so the partial traffic stays small
+// against the cache bytes each wave reads.
+struct KvPlan {
+    int nrb, nsplit, ck, rmax;
+    size_t ws_o_bytes, ws_ml_bytes;
+};
+
+bool make_plan(int nseq, int max_q, int max_k, int G, int Hkv, int d, KvPlan &pl)
+{
+    if (nseq < 1 || max_q < 1 || max_k < 1 || G < 1 || Hkv < 1)
+        return false;
+    const int64_t rmax = (int64_t)G * max_q;
+    if (rmax > (1 << 24))
+        return false;
+    pl.rmax = (int)rmax;
+    pl.nrb = (int)((rmax + kRows - 1) / kRows);
+    const int64_t units = (int64_t)nseq * Hkv * pl.nrb;
+    const int64_t target = 4096;
+    int64_t nsplit = (target + units - 1) / units;
+    const int64_t max_splits = (max_k + 127) / 128;
+    if (nsplit > max_splits)
+        nsplit = max_splits;
+    if (nsplit < 1)
+        nsplit = 1;
+    int64_t ck = (max_k + nsplit - 1) / nsplit;
+    ck = (ck + kBlockKeys - 1) / kBlockKeys * kBlockKeys;
+    nsplit = (max_k + ck - 1) / ck;
+    pl.ck = (int)ck;
+    pl.nsplit = (int)nsplit;
+    const int64_t slots = (int64_t)nseq * Hkv * nsplit * rmax * 2;
+    pl.ws_o_bytes = (size_t)(slots * 2 * d * 4);
+    pl.ws_ml_bytes = (size_t)(slots * 2 * 4);
+    return true;
+}
+
+bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+} // namespace
+
+extern "C" int diffattn_supported_kv(int dtype, int d)
+{
+    return dtype == DIFFATTN_BF16 && (d == 32 || d == 64);
+}
+
+extern "C" int diffattn_check_cu_seqlens_kv(const int32_t *host_cu_q, const int32_t *host_cu_k,
+                                            int32_t nseq, int32_t Tq, int32_t Tk,
+                                            int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                            int causal)
+{
+    if (!host_cu_q || !host_cu_k || nseq < 0 || Tq < 0 || Tk < 0)
+        return DIFFATTN_EINVAL;
+    if (host_cu_q[0] != 0 || host_cu_k[0] != 0 || host_cu_q[nseq] != Tq ||
+        host_cu_k[nseq] != Tk)
+        return DIFFATTN_EINVAL;
+    for (int32_t s = 0; s < nseq; ++s) {
+        const int64_t nq = (int64_t)host_cu_q[s + 1] - host_cu_q[s];
+        const int64_t nk = (int64_t)host_cu_k[s + 1] - host_cu_k[s];
+        if (nq < 0 || nk < 0 || nq > max_seqlen_q || nk > max_seqlen_k)
+            return DIFFATTN_EINVAL;
+        if ((nq > 0 && nk == 0) || (causal && nq > nk))
+            return DIFFATTN_EINVAL;
+    }
+    return DIFFATTN_OK;
+}
+
+extern "C" size_t diffattn_fwd_kv_workspace_size(int32_t nseq, int32_t max_seqlen_q,
+                                                 int32_t max_seqlen_k, int32_t H, int32_t Hkv,
+                                                 int32_t d)
+{
+    if (H < 1 || Hkv < 1 || H % Hkv != 0 || d < 1)
+        return 0;
+    KvPlan pl;
+    if (!make_plan(nseq, max_seqlen_q, max_seqlen_k, H / Hkv, Hkv, d, pl))
+        return 0;
+    return pl.ws_o_bytes + pl.ws_ml_bytes;
+}
+
+extern "C" int diffattn_fwd_kv(int dtype, const void *q, const void *k, const void *v,
+                               const float *lambda_q1, const float *lambda_k1,
+                               const float *lambda_q2, const float *lambda_k2,
+                               int32_t lambda_stride, float lambda_init,
+                               const float *subln_weight, float eps, int causal,
+                               const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                               int32_t nseq, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                               int32_t Tq, int32_t Tk, int32_t H, int32_t Hkv, int32_t d,
+                               void *workspace, size_t workspace_bytes, void *out,
+                               void *stream)
+{
+    if (dtype != DIFFATTN_BF16 && dtype != DIFFATTN_F32)
+        return DIFFATTN_EINVAL;
+    if (Tq < 0 || Tk < 0 || H < 1 || Hkv < 1 || d < 1 || H % Hkv != 0 || nseq < 1)
+        return DIFFATTN_EINVAL;
+    if (causal != 0 && causal != 1)
+        return DIFFATTN_EINVAL;
+    if (!(eps >= 0.f) || !isfinite(eps) || !isfinite(lambda_init))
+        return DIFFATTN_EINVAL;
+    if (lambda_stride != 0 && lambda_stride < d)
+        return DIFFATTN_EINVAL;
+    if ((cu_seqlens_q == nullptr) != (cu_seqlens_k == nullptr))
+        return DIFFATTN_EINVAL;
+    if (!cu_seqlens_q) {
+        if (Tq % nseq != 0 || Tk % nseq != 0)
+            return DIFFATTN_EINVAL;
+        max_seqlen_q = Tq / nseq;
+        max_seqlen_k = Tk / nseq;
+        if (causal && max_seqlen_q > max_seqlen_k)
+            return DIFFATTN_EINVAL;
+        if (max_seqlen_q > 0 && max_seqlen_k == 0)
+            return DIFFATTN_EINVAL;
+    } else if (max_seqlen_q < 0 || max_seqlen_k < 0 || max_seqlen_q > Tq || max_seqlen_k > Tk) {
+        return DIFFATTN_EINVAL;
+    }
+    if (!diffattn_supported_kv(dtype, d))
+        return DIFFATTN_EUNSUPPORTED;
+    if (Tq == 0 || max_seqlen_q == 0)
+        return DIFFATTN_OK;   // no query rows: nothing to write
+    if (max_seqlen_k == 0)
+        return DIFFATTN_EINVAL;   // queries with no key at all
+    if (!q || !k || !v || !out || !lambda_q1 || !lambda_k1 || !lambda_q2 || !lambda_k2 ||
+        !workspace)
+        return DIFFATTN_EINVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+        !aligned16(workspace) || (subln_weight && !aligned16(subln_weight)))
+        return DIFFATTN_EINVAL;
+    const int G = H / Hkv;
+    KvPlan pl;
+    if (!make_plan(nseq, max_seqlen_q, max_seqlen_k, G, Hkv, d, pl))
+        return DIFFATTN_EINVAL;
+    if (workspace_bytes < pl.ws_o_bytes + pl.ws_ml_bytes)
+        return DIFFATTN_EINVAL;
+
+    KvParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.out = out;
+    p.lq1 = lambda_q1;
+    p.lk1 = lambda_k1;
+    p.lq2 = lambda_q2;
+    p.lk2 = lambda_k2;
+    p.lstride = lambda_stride;
+    p.w = subln_weight;
+    p.cuq = cu_seqlens_q;
+    p.cuk = cu_seqlens_k;
+    p.ws_o = (float *)workspace;
+    p.ws_ml = (float *)((char *)workspace + pl.ws_o_bytes);
+    p.lambda_init = lambda_init;
+    p.eps = eps;
+    p.H = H;
+    p.Hkv = Hkv;
+    p.G = G;
+    p.nseq = nseq;
+    p.causal = causal;
+    p.qlen_uniform = cu_seqlens_q ? 0 : Tq / nseq;
+    p.klen_uniform = cu_seqlens_q ? 0 : Tk / nseq;
+    p.max_q = max_seqlen_q;
+    p.rmax = pl.rmax;
+    p.nrb = pl.nrb;
+    p.nsplit = pl.nsplit;
+    p.ck = pl.ck;
+
+    hipStream_t st = (hipStream_t)stream;
+    const int64_t waves1 = (int64_t)nseq * Hkv * pl.nsplit * pl.nrb;
+    const int64_t waves2 = (int64_t)nseq * max_seqlen_q * H;
+    const int64_t blocks1 = (waves1 + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int64_t blocks2 = (waves2 + kWavesPerBlock - 1) / kWavesPerBlock;
+    if (blocks1 > 0x7fffffff || blocks2 > 0x7fffffff)
+        return DIFFATTN_EINVAL;
+    if (d == 64) {
+        hipLaunchKernelGGL(diffattn_kv_partial<64>, dim3((unsigned)blocks1), dim3(kThreads), 0, st, p);
+        hipLaunchKernelGGL(diffattn_kv_combine<64>, dim3((unsigned)blocks2), dim3(kThreads), 0, st, p);
+    } else {
+        hipLaunchKernelGGL(diffattn_kv_partial<32>, dim3((unsigned)blocks1), dim3(kThreads), 0, st, p);
+        hipLaunchKernelGGL(diffattn_kv_combine<32>, dim3((unsigned)blocks2), dim3(kThreads), 0, st, p);
+    }
+    return hipGetLastError() == hipSuccess ? DIFFATTN_OK : DIFFATTN_EHIP;
+}

@@ -37,13 +37,14 @@
 #ifndef DIFFATTN_H
 #define DIFFATTN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-#define DIFFATTN_ABI_VERSION 2
+#define DIFFATTN_ABI_VERSION 3
 
 enum diffattn_status {
     DIFFATTN_OK = 0,
@@ -100,6 +101,82 @@ int diffattn_fwd(int dtype, const void *q, const void *k, const void *v,
                  int causal, const int32_t *cu_seqlens, int32_t nseq,
                  int32_t max_seqlen, int32_t T, int32_t H, int32_t Hkv,
                  int32_t d, void *out, void *stream);
+
+/*
+ * New queries against a key/value cache (decoding), asynchronous on
+ * `stream`.  The LlamaDiffSdpaAttention.py gist's forward appends the step's
+ * keys and values to the layer's cache and then attends from the new
+ * queries to the whole cache; the FlashDiffAttention pull request's
+ * alternative_forward aligns the causal mask bottom-right (-inf above
+ * diagonal 1 + src_len - tgt_len).  So, per sequence s with nq new queries
+ * and nk cached keys (the new tokens' own keys being the last nq of them),
+ * query i (0-based) sees keys j <= nk - nq + i when causal == 1 and all nk
+ * keys when causal == 0; everything else is as in diffattn_fwd.  With
+ * nq == nk this is diffattn_fwd's causal prefill.
+ *
+ *   q            device [Tq, H, 2, d]: the new queries, packed by
+ *                cu_seqlens_q.
+ *   k, v         device [Tk, Hkv, 2, d] and [Tk, Hkv, 2d]: the caches,
+ *                packed by cu_seqlens_k (sequence s owns rows
+ *                cu_seqlens_k[s] .. cu_seqlens_k[s+1]-1).
+ *   lambda_*, lambda_stride, lambda_init, subln_weight, eps
+ *                as for diffattn_fwd.
+ *   causal       1: bottom-right causal as above; 0: every cached key.
+ *   cu_seqlens_q, cu_seqlens_k
+ *                device int32 [nseq + 1] boundaries (cu[0] = 0,
+ *                non-decreasing, cu_q[nseq] = Tq, cu_k[nseq] = Tk), both
+ *                given or both NULL (NULL: nseq sequences of Tq / nseq
+ *                queries and Tk / nseq keys).  Preconditions, not read here:
+ *                every sequence with nq > 0 has nk >= 1, and nk >= nq when
+ *                causal (see diffattn_check_cu_seqlens_kv).
+ *   max_seqlen_q, max_seqlen_k
+ *                upper bounds on every nq and nk (ignored when the
+ *                boundaries are NULL); they size the grid and the workspace.
+ *   Tq, Tk, H, Hkv, d
+ *                sizes; H % Hkv == 0.  Compiled (dtype, d) pairs: see
+ *                diffattn_supported_kv.
+ *   workspace    device scratch of at least workspace_bytes =
+ *                diffattn_fwd_kv_workspace_size(nseq, max_seqlen_q,
+ *                max_seqlen_k, H, Hkv, d) bytes, 16-byte aligned, owned by
+ *                the caller.  It holds fp32 partial results between the two
+ *                kernels of one call; its contents need no initialisation
+ *                and are meaningless afterwards.  Two calls in flight at
+ *                once (on different streams) need different workspaces.
+ *   out          device [Tq, H, 2d], same element type as q.
+ *
+ * Returns DIFFATTN_OK (also when there is no query row, which launches
+ * nothing), DIFFATTN_EINVAL (including a workspace smaller than required),
+ * DIFFATTN_EUNSUPPORTED or DIFFATTN_EHIP.
+ */
+int diffattn_fwd_kv(int dtype, const void *q, const void *k, const void *v,
+                    const float *lambda_q1, const float *lambda_k1,
+                    const float *lambda_q2, const float *lambda_k2,
+                    int32_t lambda_stride, float lambda_init,
+                    const float *subln_weight, float eps, int causal,
+                    const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                    int32_t nseq, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                    int32_t Tq, int32_t Tk, int32_t H, int32_t Hkv, int32_t d,
+                    void *workspace, size_t workspace_bytes, void *out,
+                    void *stream);
+
+/* Bytes of workspace diffattn_fwd_kv needs for these sizes (the same split
+ * plan the call makes); 0 for sizes it rejects.  Host function. */
+size_t diffattn_fwd_kv_workspace_size(int32_t nseq, int32_t max_seqlen_q,
+                                      int32_t max_seqlen_k, int32_t H,
+                                      int32_t Hkv, int32_t d);
+
+/* 1 if the cache kernel is compiled for (dtype, d), else 0.  Host
+ * function. */
+int diffattn_supported_kv(int dtype, int d);
+
+/* Host-side check of host copies of cu_seqlens_q and cu_seqlens_k against
+ * the preconditions of diffattn_fwd_kv (both well-formed for Tq and Tk,
+ * lengths within the bounds, nk >= 1 where nq >= 1, nk >= nq when causal).
+ * Returns DIFFATTN_OK or DIFFATTN_EINVAL. */
+int diffattn_check_cu_seqlens_kv(const int32_t *host_cu_q,
+                                 const int32_t *host_cu_k, int32_t nseq,
+                                 int32_t Tq, int32_t Tk, int32_t max_seqlen_q,
+                                 int32_t max_seqlen_k, int causal);
 
 /* Initial lambda of a layer at 1-based depth: 0.8 - 0.6 * exp(-0.3 *
  * (depth - 1)), the decaying schedule with which DiffTransformer.__init__

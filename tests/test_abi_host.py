@@ -98,3 +98,73 @@ def call(**over):
 ])
 def test_validation_before_any_device_work(over, status):
     assert call(**over) == status
+
+
+# --------------------------------------------------------------------------
+# the key/value-cache entry point
+
+def test_supported_kv():
+    import torch
+    assert da.supported_kv(torch.bfloat16, 64)
+    assert da.supported_kv(torch.bfloat16, 32)
+    assert not da.supported_kv(torch.bfloat16, 16)
+    assert not da.supported_kv(torch.float32, 64)
+
+
+def test_kv_workspace_size():
+    small = da.kv_workspace_size(8, 1, 4097, 16, 4, 64)
+    big = da.kv_workspace_size(64, 1, 8192, 16, 4, 64)
+    assert 0 < small < big
+    assert da.kv_workspace_size(8, 1, 4097, 16, 5, 64) == 0   # H % Hkv
+    assert da.kv_workspace_size(0, 1, 4097, 16, 4, 64) == 0
+    # more queries need more partial rows
+    assert da.kv_workspace_size(8, 4, 4097, 16, 4, 64) > small
+
+
+def test_check_cu_seqlens_kv():
+    ok = da.check_cu_seqlens_kv
+    assert ok([0, 1, 3], [0, 10, 12], 3, 12, 2, 10)
+    assert not ok([0, 1, 3], [0, 10, 12], 3, 12, 1, 10)     # nq 2 > max
+    assert not ok([0, 1, 3], [0, 10, 11], 3, 11, 2, 10)     # causal nq > nk
+    assert ok([0, 1, 3], [0, 10, 11], 3, 11, 2, 10, causal=False)
+    assert not ok([0, 1, 3], [0, 0, 12], 3, 12, 2, 12, causal=False)  # nk = 0
+    assert not ok([0, 1, 3], [0, 10, 12], 3, 13, 2, 10)     # cu_k[nseq] != Tk
+
+
+def call_kv(**over):
+    a = dict(dtype=da.BF16, q=FAKE, k=FAKE, v=FAKE, lq1=FAKE, lk1=FAKE,
+             lq2=FAKE, lk2=FAKE, lambda_stride=0, lambda_init_value=0.7,
+             subln_weight=0, eps=1e-5, causal=1, cu_seqlens_q=0,
+             cu_seqlens_k=0, nseq=8, max_seqlen_q=0, max_seqlen_k=0, Tq=8,
+             Tk=8 * 4097, H=16, Hkv=4, d=64, workspace=FAKE,
+             workspace_bytes=1 << 30, out=FAKE, stream=0)
+    a.update(over)
+    return da.fwd_kv_ptr(**a)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(dtype=7), da.EINVAL),
+    (dict(H=6, Hkv=4), da.EINVAL),
+    (dict(Tq=-1), da.EINVAL),
+    (dict(causal=2), da.EINVAL),
+    (dict(eps=-1.0), da.EINVAL),
+    (dict(lambda_init_value=float("nan")), da.EINVAL),
+    (dict(lambda_stride=63), da.EINVAL),
+    (dict(dtype=da.F32), da.EUNSUPPORTED),
+    (dict(d=16), da.EUNSUPPORTED),
+    (dict(cu_seqlens_q=FAKE), da.EINVAL),          # one boundary array only
+    (dict(Tq=12), da.EINVAL),                      # Tq % nseq
+    (dict(Tk=8 * 4097 + 1), da.EINVAL),            # Tk % nseq
+    (dict(Tq=8 * 5000), da.EINVAL),                # causal: nq > nk
+    (dict(Tk=0), da.EINVAL),                       # queries without keys
+    (dict(q=0), da.EINVAL),
+    (dict(workspace=0), da.EINVAL),
+    (dict(workspace=FAKE + 4), da.EINVAL),         # not 16-byte aligned
+    (dict(workspace_bytes=1024), da.EINVAL),       # smaller than required
+    (dict(cu_seqlens_q=FAKE, cu_seqlens_k=FAKE, max_seqlen_q=9), da.EINVAL),
+    (dict(cu_seqlens_q=FAKE, cu_seqlens_k=FAKE, max_seqlen_q=1,
+          max_seqlen_k=8 * 4097 + 1), da.EINVAL),  # bound beyond Tk
+    (dict(Tq=0, q=0, out=0), da.OK),               # no query rows
+])
+def test_kv_validation_before_any_device_work(over, status):
+    assert call_kv(**over) == status

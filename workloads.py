@@ -165,6 +165,150 @@ def make_inputs(wl: Workload, seed: Optional[int] = None,
                   wl.depth, wl.eps, wl.causal, wl.max_seqlen)
 
 
+# --------------------------------------------------------------------------
+# new queries against a key/value cache (decoding)
+
+@dataclasses.dataclass(frozen=True)
+class KvWorkload:
+    """Sequence s has ``q_lens[s]`` new queries and ``k_lens[s]`` cached keys
+    (the new tokens' own keys being the last ``q_lens[s]`` of them).  Queries
+    are packed ``[Tq, H, 2, d]``, the caches ``[Tk, Hkv, 2, d]`` and
+    ``[Tk, Hkv, 2d]``, each by its own cu_seqlens."""
+    name: str
+    dtype: str
+    q_lens: tuple
+    k_lens: tuple
+    H: int
+    Hkv: int
+    d: int
+    depth: int
+    causal: bool = True
+    eps: float = 1e-5
+    seed: int = 0
+    description: str = ""
+
+    @property
+    def nseq(self) -> int:
+        return len(self.q_lens)
+
+    @property
+    def Tq(self) -> int:
+        return int(sum(self.q_lens))
+
+    @property
+    def Tk(self) -> int:
+        return int(sum(self.k_lens))
+
+    @property
+    def max_q(self) -> int:
+        return int(max(self.q_lens)) if self.q_lens else 0
+
+    @property
+    def max_k(self) -> int:
+        return int(max(self.k_lens)) if self.k_lens else 0
+
+    def cu_q(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.q_lens)]).astype(np.int32)
+
+    def cu_k(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.k_lens)]).astype(np.int32)
+
+    def bytes(self) -> float:
+        """Bytes a call must move at least: read q, k, v once, write out."""
+        es = 2 if self.dtype == "bf16" else 4
+        return float(es * (2 * self.Tq * self.H * 2 * self.d
+                           + 2 * self.Tk * self.Hkv * 2 * self.d))
+
+    def flops(self) -> float:
+        """12*d FLOP per visible (query, key) pair and head, as for the
+        prefill."""
+        pairs = 0
+        for nq, nk in zip(self.q_lens, self.k_lens):
+            if self.causal:
+                pairs += sum(nk - nq + i + 1 for i in range(nq))
+            else:
+                pairs += nq * nk
+        return 12.0 * self.d * self.H * pairs
+
+
+KV_WORKLOADS = {
+    "decode_b8_kv4097": KvWorkload(
+        "decode_b8_kv4097", "bf16", (1,) * 8, (4097,) * 8, H=16, Hkv=4, d=64,
+        depth=8,
+        description="bf16 decode step after the B=8, N=4096 prefill: one new "
+                    "query per sequence against 4097 cached keys, 16 diff "
+                    "heads, 4 KV heads, d=64"),
+    "decode_b64_kv8192": KvWorkload(
+        "decode_b64_kv8192", "bf16", (1,) * 64, (8192,) * 64, H=16, Hkv=4,
+        d=64, depth=8,
+        description="bf16 decode step, 64 sequences x 8192 cached keys "
+                    "(1 GiB of K/V), one new query each, 16 diff heads, "
+                    "4 KV heads, d=64"),
+    "decode_varlen_b32_q4": KvWorkload(
+        "decode_varlen_b32_q4", "bf16", (4,) * 32,
+        tuple(int(x) for x in np.random.default_rng(1).integers(1024, 32769, 32)),
+        H=16, Hkv=4, d=64, depth=8,
+        description="bf16 multi-token decode: 32 sequences, 4 new queries "
+                    "each, cache lengths uniform in [1024, 32768], 16 diff "
+                    "heads, 4 KV heads, d=64"),
+}
+
+KV_HEADLINE = "decode_b64_kv8192"
+
+
+@dataclasses.dataclass
+class KvInputs:
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    lq1: torch.Tensor
+    lk1: torch.Tensor
+    lq2: torch.Tensor
+    lk2: torch.Tensor
+    w: torch.Tensor
+    cu_q: torch.Tensor
+    cu_k: torch.Tensor
+    depth: int
+    eps: float
+    causal: bool
+    max_q: int
+    max_k: int
+
+
+def make_kv_inputs(wl: KvWorkload, seed: Optional[int] = None,
+                   q_scale: float = 1.0) -> KvInputs:
+    """Draw the inputs of ``wl`` on the CPU: q, k, v (standard normal, fp32
+    then rounded to the storage type), then the four lambda vectors
+    (N(0, 0.1^2)), from one generator seeded with ``seed``."""
+    gen = torch.Generator("cpu")
+    gen.manual_seed(wl.seed if seed is None else seed)
+    H, Hkv, d = wl.H, wl.Hkv, wl.d
+    dt = torch_dtype(wl.dtype)
+    q = _randn(gen, wl.Tq, H, 2, d)
+    if q_scale != 1.0:
+        q = q * q_scale
+    q = q.to(dt)
+    k = _randn(gen, wl.Tk, Hkv, 2, d).to(dt)
+    v = _randn(gen, wl.Tk, Hkv, 2 * d).to(dt)
+    lq1 = 0.1 * _randn(gen, d)
+    lk1 = 0.1 * _randn(gen, d)
+    lq2 = 0.1 * _randn(gen, d)
+    lk2 = 0.1 * _randn(gen, d)
+    w = torch.ones(2 * d, dtype=torch.float32)
+    return KvInputs(q, k, v, lq1, lk1, lq2, lk2, w,
+                    torch.from_numpy(wl.cu_q()), torch.from_numpy(wl.cu_k()),
+                    wl.depth, wl.eps, wl.causal, wl.max_q, wl.max_k)
+
+
+def custom_kv(name: str, dtype: str, q_lens, k_lens, H: int, Hkv: int, d: int,
+              depth: int = 1, causal: bool = True, eps: float = 1e-5,
+              seed: int = 0) -> KvWorkload:
+    """An ad-hoc cache workload for edge-case tests."""
+    return KvWorkload(name, dtype, tuple(int(n) for n in q_lens),
+                      tuple(int(n) for n in k_lens), H=H, Hkv=Hkv, d=d,
+                      depth=depth, causal=causal, eps=eps, seed=seed)
+
+
 def custom(name: str, dtype: str, seqlens, H: int, Hkv: int, d: int,
            depth: int = 1, causal: bool = True, eps: float = 1e-5,
            seed: int = 0) -> Workload:
