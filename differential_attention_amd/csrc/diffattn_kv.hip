@@ -418,11 +418,12 @@ void diffattn_kv_combine(KvParams p)
         lam = expf(d1) - expf(d2) + p.lambda_init;
     }
 
-    // merge the splits of both maps (log-sum-exp in log2 units).  Splits
-    // are taken 64 at a time, one per lane: lane j loads split j's (m, l)
-    // of both maps in one 16-byte read, the wave reduces the maximum and the
-    // weighted sum, and every lane then accumulates its columns of all
-    // splits' O with independent loads.
+    // merge the splits of both maps (log-sum-exp in log2 units), up to 16
+    // splits per round: lane j loads split j's (m, l) of both maps in one
+    // 16-byte read while every lane loads its columns of all 16 splits' O
+    // (independent loads, one memory round trip per round); the wave then
+    // reduces the maximum and the weighted sums.
+    constexpr int kChunk = 16;
     float acc[2][CPL];
     float M[2] = {-INFINITY, -INFINITY};
     float L[2] = {0.f, 0.f};
@@ -432,44 +433,44 @@ void diffattn_kv_combine(KvParams p)
         for (int cc = 0; cc < CPL; ++cc)
             acc[m][cc] = 0.f;
     const int64_t slot0 = ((int64_t)s * p.Hkv + g) * p.nsplit * p.rmax + r;
-    for (int j0 = 0; j0 < nsp; j0 += 64) {
-        const int j = j0 + lane;
+    for (int j0 = 0; j0 < nsp; j0 += kChunk) {
+        const int nj = min(kChunk, nsp - j0);
         f32x4 ml = f32x4{-INFINITY, 0.f, -INFINITY, 0.f};
-        if (j < nsp)
-            ml = *(const f32x4 *)(p.ws_ml + (slot0 + (int64_t)j * p.rmax) * 4);
-        float wgt[2];
+        if (lane < nj)
+            ml = *(const f32x4 *)(p.ws_ml + (slot0 + (int64_t)(j0 + lane) * p.rmax) * 4);
+        // past the last split the round re-reads the last one (weight 0)
+        float ob[kChunk][2][CPL];
+#pragma unroll
+        for (int u = 0; u < kChunk; ++u) {
+            const int jc = j0 + min(u, nj - 1);
+            const float *op = p.ws_o + (slot0 + (int64_t)jc * p.rmax) * 2 * (2 * D) + CPL * lane;
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int cc = 0; cc < CPL; ++cc)
+                    ob[u][m][cc] = op[m * 2 * D + cc];
+        }
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             const float mj = ml[2 * m];
-            const float cm = wave_max(mj);
-            const float mn = fmaxf(M[m], cm);
-            // rescale what earlier chunks accumulated (1 on the first chunk)
+            const float mn = fmaxf(M[m], wave_max(mj));
+            // rescale what earlier rounds accumulated (0 before any)
             const float fa = M[m] == -INFINITY ? 0.f : exp2f(M[m] - mn);
-            wgt[m] = mj == -INFINITY ? 0.f : exp2f(mj - mn);
-            L[m] = L[m] * fa + wave_sum(ml[2 * m + 1] * wgt[m]);
+            const float wgt = mj == -INFINITY ? 0.f : exp2f(mj - mn);
+            L[m] = L[m] * fa + wave_sum(ml[2 * m + 1] * wgt);
 #pragma unroll
             for (int cc = 0; cc < CPL; ++cc)
                 acc[m][cc] *= fa;
-            M[m] = mn;
-        }
-        // four splits per step with independent loads; past the last split
-        // the step re-reads the last one with weight 0
-        const int nj = min(64, nsp - j0);
-        for (int jj = 0; jj < nj; jj += 4) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int jc = min(jj + u, nj - 1);
-                const float keep = jj + u < nj ? 1.f : 0.f;
-                const float *op = p.ws_o + (slot0 + (int64_t)(j0 + jc) * p.rmax) * 2 * (2 * D) + CPL * lane;
+            for (int u = 0; u < kChunk; ++u) {
+                const float wj = u < nj ? __int_as_float(__builtin_amdgcn_readlane(
+                                              __float_as_int(wgt), u))
+                                        : 0.f;
 #pragma unroll
-                for (int m = 0; m < 2; ++m) {
-                    const float wj = keep * __int_as_float(
-                        __builtin_amdgcn_readlane(__float_as_int(wgt[m]), jc));
-#pragma unroll
-                    for (int cc = 0; cc < CPL; ++cc)
-                        acc[m][cc] += wj * op[m * 2 * D + cc];
-                }
+                for (int cc = 0; cc < CPL; ++cc)
+                    acc[m][cc] += wj * ob[u][m][cc];
             }
+            M[m] = mn;
         }
     }
 
