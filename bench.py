@@ -106,37 +106,35 @@ def cpu_baseline(wl, inp, flop_budget: float = 1.0e12):
                        "convention); fp64 C oracle, OpenMP over rows")}
 
 
-def cpu_baseline_kv(wl, inp, byte_budget: float = 4.0e8):
-    """The fp64 oracle on every s-th sequence of a cache workload (all its
-    queries and heads), s >= 1 chosen so that the sample's cache holds at
-    most ``byte_budget`` bytes; reported in GB/s of the sample's bytes."""
+def cpu_baseline_kv(wl, inp, min_seconds: float = 2.0):
+    """The fp64 oracle on the whole cache workload (every sequence, query
+    and head), repeated until ``min_seconds`` of host time have passed;
+    reported in GB/s of the bytes a step must move (q, k, v, out in the
+    storage type)."""
     import numpy as np
     import oracle
-    es = 2 if wl.dtype == "bf16" else 4
-    per_seq = [es * (2 * nq * wl.H * 2 * wl.d + 2 * nk * wl.Hkv * 2 * wl.d)
-               for nq, nk in zip(wl.q_lens, wl.k_lens)]
-    stride = max(1, int(np.ceil(sum(per_seq) / byte_budget)))
-    seqs = list(range(0, wl.nseq, stride))
-    cq, ck = wl.cu_q(), wl.cu_k()
-    qi = np.concatenate([np.arange(cq[s], cq[s + 1]) for s in seqs])
-    ki = np.concatenate([np.arange(ck[s], ck[s + 1]) for s in seqs])
-    q, k, v = (oracle._f32(x) for x in (inp.q[qi], inp.k[ki], inp.v[ki]))
+    q, k, v = (oracle._f32(x) for x in (inp.q, inp.k, inp.v))
     lv = [oracle._f32(x) for x in (inp.lq1, inp.lk1, inp.lq2, inp.lk2)]
-    cqs = np.concatenate([[0], np.cumsum([wl.q_lens[s] for s in seqs])])
-    cks = np.concatenate([[0], np.cumsum([wl.k_lens[s] for s in seqs])])
+    w = oracle._f32(inp.w)
+    cq, ck = wl.cu_q(), wl.cu_k()
+    lam0 = oracle.lambda_init(wl.depth)
     oracle.load()
+    runs = 0
     t0 = time.perf_counter()
-    oracle.fwd_kv(q, k, v, *lv, oracle.lambda_init(wl.depth),
-                  oracle._f32(inp.w), wl.eps, wl.causal, cqs, cks)
-    dt = time.perf_counter() - t0
-    nbytes = float(sum(per_seq[s] for s in seqs))
-    what = ("every sequence" if stride == 1 else
-            f"one sequence in {stride} ({len(seqs)} of {wl.nseq})")
-    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": oracle.max_threads(),
-            "kind": "oracle", "seconds": round(dt, 3),
-            "sample": (f"{what}, all queries and heads ({nbytes / 1e6:.1f} MB of "
-                       "q/k/v/out in the storage type); fp64 C oracle, OpenMP "
-                       "over output rows")}
+    while True:
+        oracle.fwd_kv(q, k, v, *lv, lam0, w, wl.eps, wl.causal, cq, ck)
+        runs += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    nbytes = wl.bytes()
+    return {"value": nbytes * runs / dt / 1e9, "unit": "GB/s",
+            "cores": oracle.max_threads(), "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": (f"the whole workload ({wl.Tq} queries x {wl.H} heads "
+                       f"against {wl.Tk} cached keys, {nbytes / 1e6:.1f} MB of "
+                       f"q/k/v/out in the storage type), {runs} run(s); fp64 C "
+                       "oracle, OpenMP over output rows")}
 
 
 def bench_kv(args, name) -> int:
