@@ -16,6 +16,10 @@
  *              + lambda_init
  *              (one set of vectors shared by all heads, or one per head as
  *              the DiffTransformer page keeps them: lq1_h = lq1 + h*stride)
+ *   optional rotary prologue (the pull request's apply_rotary_emb with
+ *   interleaved=True on every d-wide half-head of q and k): the pair
+ *   (x[2j], x[2j+1]) of a row at sequence position p is turned by the angle
+ *   of table row p, column j;
  *   for every packed sequence s (tokens a .. a+n-1), head h, row i:
  *     g      = h / (H / Hkv)                  (GQA: contiguous head groups)
  *     map m in {1,2}: x_j = <Qm[a+i,h], Km[a+j,g]> / sqrt(d), j in J(i)
@@ -85,21 +89,55 @@ static void lambda_per_head(const float *lq1, const float *lk1,
     }
 }
 
-/* Softmax of one attention map over the keys j in [0, nkeys) that start at
- * key token ka, for query token qt of head h: writes the probabilities into
- * p[0..nkeys). */
-static void softmax_map(const float *q, const float *k, int64_t qt, int64_t ka,
-                        int64_t nkeys, int h, int g, int map, int H, int Hkv,
-                        int d, double *p)
+/* Rotary position tables (the pull request passes them as rel_pos, built by
+ * RotaryEmbedding(head_dim, base, interleaved=True)): row p holds
+ * cos(p * theta_j) and sin(p * theta_j), j < d/2.  cos == NULL: no rotation
+ * (the inputs are already rotated). */
+typedef struct {
+    const float *cos;
+    const float *sin;
+    int64_t len;
+} rope_t;
+
+/* One d-wide half-head row x at sequence position pos, rotated the
+ * interleaved way: the pair (x[2j], x[2j+1]) is turned by the angle whose
+ * cosine and sine are row pos, column j of the tables (the complex number
+ * x[2j] + i x[2j+1] times exp(i angle)).  Widened to double. */
+static void row_rot(const float *x, int d, const rope_t *rp, int64_t pos,
+                    double *out)
 {
-    const float *qrow = q + ((qt * H + h) * 2 + map) * (int64_t)d;
+    if (!rp->cos) {
+        for (int c = 0; c < d; ++c)
+            out[c] = (double)x[c];
+        return;
+    }
+    const float *cr = rp->cos + pos * (int64_t)(d / 2);
+    const float *sr = rp->sin + pos * (int64_t)(d / 2);
+    for (int j = 0; j < d / 2; ++j) {
+        const double x0 = (double)x[2 * j], x1 = (double)x[2 * j + 1];
+        const double c = (double)cr[j], sn = (double)sr[j];
+        out[2 * j] = x0 * c - x1 * sn;
+        out[2 * j + 1] = x0 * sn + x1 * c;
+    }
+}
+
+/* Softmax of one attention map over the keys j in [0, nkeys) that start at
+ * key token ka, for query token qt (sequence position qpos; key j sits at
+ * position j) of head h: writes the probabilities into p[0..nkeys).
+ * qd and kd are scratch of d doubles. */
+static void softmax_map(const float *q, const float *k, int64_t qt, int64_t qpos,
+                        int64_t ka, int64_t nkeys, int h, int g, int map, int H,
+                        int Hkv, int d, const rope_t *rp, double *qd,
+                        double *kd, double *p)
+{
+    row_rot(q + ((qt * H + h) * 2 + map) * (int64_t)d, d, rp, qpos, qd);
     const double scale = 1.0 / sqrt((double)d);
     double mx = -INFINITY;
     for (int64_t j = 0; j < nkeys; ++j) {
-        const float *krow = k + (((ka + j) * Hkv + g) * 2 + map) * (int64_t)d;
+        row_rot(k + (((ka + j) * Hkv + g) * 2 + map) * (int64_t)d, d, rp, j, kd);
         double x = 0.0;
         for (int c = 0; c < d; ++c)
-            x += (double)qrow[c] * (double)krow[c];
+            x += qd[c] * kd[c];
         x *= scale;
         p[j] = x;
         if (x > mx)
@@ -114,19 +152,21 @@ static void softmax_map(const float *q, const float *k, int64_t qt, int64_t ka,
         p[j] /= z;
 }
 
-/* One output row (query token qt, head h) over the nkeys keys that start at
- * key token ka, into o[0..2d).  p1, p2 and pre are caller-provided scratch
- * of nkeys, nkeys and 2d doubles. */
+/* One output row (query token qt at sequence position qpos, head h) over
+ * the nkeys keys that start at key token ka, into o[0..2d).  sc is
+ * caller-provided scratch of 2 nkeys + 4d doubles. */
 static void diff_row(const float *q, const float *k, const float *v,
                      double lam, double lambda_init, const float *w, double eps,
-                     int64_t qt, int64_t ka, int64_t nkeys, int h, int H,
-                     int Hkv, int d, double *p1, double *p2, double *pre,
+                     int64_t qt, int64_t qpos, int64_t ka, int64_t nkeys, int h,
+                     int H, int Hkv, int d, const rope_t *rp, double *sc,
                      double *o)
 {
     const int g = h / (H / Hkv);
     const int dv = 2 * d;
-    softmax_map(q, k, qt, ka, nkeys, h, g, 0, H, Hkv, d, p1);
-    softmax_map(q, k, qt, ka, nkeys, h, g, 1, H, Hkv, d, p2);
+    double *p1 = sc, *p2 = sc + nkeys, *pre = sc + 2 * nkeys;
+    double *qd = pre + dv, *kd = qd + d;
+    softmax_map(q, k, qt, qpos, ka, nkeys, h, g, 0, H, Hkv, d, rp, qd, kd, p1);
+    softmax_map(q, k, qt, qpos, ka, nkeys, h, g, 1, H, Hkv, d, rp, qd, kd, p2);
     for (int c = 0; c < dv; ++c)
         pre[c] = 0.0;
     for (int64_t j = 0; j < nkeys; ++j) {
@@ -177,16 +217,23 @@ static int64_t max_len(const int32_t *cu, int nseq)
 }
 
 /* Full forward pass: out[T, H, 2d] in double.  cu_seqlens[nseq+1] holds the
- * packed sequence boundaries (host).  nthreads <= 0 uses the OpenMP default.
+ * packed sequence boundaries (host).  rope_cos / rope_sin: rotary tables
+ * [rope_len, d/2] (rope_len >= the longest sequence) or NULL for inputs that
+ * are already rotated.  nthreads <= 0 uses the OpenMP default.
  * Returns 0, or -1 on malformed arguments, -2 if scratch memory is short. */
 int diffattn_ref_fwd(const float *q, const float *k, const float *v,
                      const float *lq1, const float *lk1, const float *lq2,
                      const float *lk2, int64_t lambda_stride,
                      double lambda_init, const float *w, double eps, int causal,
                      const int32_t *cu_seqlens, int nseq, int64_t T, int H,
-                     int Hkv, int d, double *out, int nthreads)
+                     int Hkv, int d, const float *rope_cos,
+                     const float *rope_sin, int64_t rope_len, double *out,
+                     int nthreads)
 {
     if (check_args(cu_seqlens, nseq, T, H, Hkv, d) || lambda_stride < 0)
+        return -1;
+    const rope_t rp = {rope_cos, rope_sin, rope_len};
+    if (rope_cos && (!rope_sin || d % 2 || rope_len < max_len(cu_seqlens, nseq)))
         return -1;
     double *lam = malloc(sizeof(double) * (size_t)H);
     if (!lam)
@@ -201,7 +248,7 @@ int diffattn_ref_fwd(const float *q, const float *k, const float *v,
 #pragma omp parallel num_threads(nthreads)
 #endif
     {
-        double *scratch = malloc(sizeof(double) * (size_t)(2 * nmax + 2 * d + 1));
+        double *scratch = malloc(sizeof(double) * (size_t)(2 * nmax + 4 * d + 1));
         if (!scratch) {
 #ifdef _OPENMP
 #pragma omp atomic write
@@ -221,10 +268,9 @@ int diffattn_ref_fwd(const float *q, const float *k, const float *v,
                 ++s;
             const int64_t a = cu_seqlens[s];
             const int64_t n = cu_seqlens[s + 1] - a;
-            diff_row(q, k, v, lam[h], lambda_init, w, eps, t, a,
-                     prefill_keys(causal, t - a, n), h, H, Hkv, d, scratch,
-                     scratch + nmax, scratch + 2 * nmax,
-                     out + r * 2 * (int64_t)d);
+            diff_row(q, k, v, lam[h], lambda_init, w, eps, t, t - a, a,
+                     prefill_keys(causal, t - a, n), h, H, Hkv, d, &rp,
+                     scratch, out + r * 2 * (int64_t)d);
         }
         free(scratch);
     }
@@ -239,11 +285,15 @@ int diffattn_ref_rows(const float *q, const float *k, const float *v,
                       const float *lk2, int64_t lambda_stride,
                       double lambda_init, const float *w, double eps,
                       int causal, const int32_t *cu_seqlens, int nseq,
-                      int64_t T, int H, int Hkv, int d, const int64_t *tok,
-                      const int32_t *head, int64_t nrows, double *out_rows,
-                      int nthreads)
+                      int64_t T, int H, int Hkv, int d, const float *rope_cos,
+                      const float *rope_sin, int64_t rope_len,
+                      const int64_t *tok, const int32_t *head, int64_t nrows,
+                      double *out_rows, int nthreads)
 {
     if (check_args(cu_seqlens, nseq, T, H, Hkv, d) || lambda_stride < 0)
+        return -1;
+    const rope_t rp = {rope_cos, rope_sin, rope_len};
+    if (rope_cos && (!rope_sin || d % 2 || rope_len < max_len(cu_seqlens, nseq)))
         return -1;
     for (int64_t r = 0; r < nrows; ++r)
         if (tok[r] < 0 || tok[r] >= T || head[r] < 0 || head[r] >= H)
@@ -260,7 +310,7 @@ int diffattn_ref_rows(const float *q, const float *k, const float *v,
 #pragma omp parallel num_threads(nthreads)
 #endif
     {
-        double *scratch = malloc(sizeof(double) * (size_t)(2 * nmax + 2 * d + 1));
+        double *scratch = malloc(sizeof(double) * (size_t)(2 * nmax + 4 * d + 1));
         if (!scratch) {
 #ifdef _OPENMP
 #pragma omp atomic write
@@ -279,10 +329,9 @@ int diffattn_ref_rows(const float *q, const float *k, const float *v,
                 ++s;
             const int64_t a = cu_seqlens[s];
             const int64_t n = cu_seqlens[s + 1] - a;
-            diff_row(q, k, v, lam[head[r]], lambda_init, w, eps, t, a,
-                     prefill_keys(causal, t - a, n), head[r], H, Hkv, d,
-                     scratch, scratch + nmax, scratch + 2 * nmax,
-                     out_rows + r * 2 * (int64_t)d);
+            diff_row(q, k, v, lam[head[r]], lambda_init, w, eps, t, t - a, a,
+                     prefill_keys(causal, t - a, n), head[r], H, Hkv, d, &rp,
+                     scratch, out_rows + r * 2 * (int64_t)d);
         }
         free(scratch);
     }
@@ -318,6 +367,7 @@ int diffattn_ref_fwd_kv(const float *q, const float *k, const float *v,
         return -2;
     lambda_per_head(lq1, lk1, lq2, lk2, lambda_stride, H, d, lambda_init, lam);
     const int64_t nmax = max_len(cu_k, nseq);
+    const rope_t no_rope = {NULL, NULL, 0};
     const int64_t nrows = Tq * H;
     int err = 0;
 #ifdef _OPENMP
@@ -326,7 +376,7 @@ int diffattn_ref_fwd_kv(const float *q, const float *k, const float *v,
 #pragma omp parallel num_threads(nthreads)
 #endif
     {
-        double *scratch = malloc(sizeof(double) * (size_t)(2 * nmax + 2 * d + 1));
+        double *scratch = malloc(sizeof(double) * (size_t)(2 * nmax + 4 * d + 1));
         if (!scratch) {
 #ifdef _OPENMP
 #pragma omp atomic write
@@ -348,8 +398,8 @@ int diffattn_ref_fwd_kv(const float *q, const float *k, const float *v,
             const int64_t nk = cu_k[s + 1] - cu_k[s];
             const int64_t i = t - cu_q[s];
             const int64_t nkeys = causal ? nk - nq + i + 1 : nk;
-            diff_row(q, k, v, lam[h], lambda_init, w, eps, t, cu_k[s], nkeys,
-                     h, H, Hkv, d, scratch, scratch + nmax, scratch + 2 * nmax,
+            diff_row(q, k, v, lam[h], lambda_init, w, eps, t, nk - nq + i,
+                     cu_k[s], nkeys, h, H, Hkv, d, &no_rope, scratch,
                      out + r * 2 * (int64_t)d);
         }
         free(scratch);

@@ -58,14 +58,19 @@ def run(lib, q, k, v, lv, lam_init, w, eps, causal, cu):
 # --------------------------------------------------------------------------
 # mpmath brute force of the materialised two-map form
 
-def brute_mpmath(q, k, v, lv, lam_init, w, eps, causal, cu, dps=50, cu_k=None):
+def brute_mpmath(q, k, v, lv, lam_init, w, eps, causal, cu, dps=50, cu_k=None,
+                 rope=None):
     """With ``cu_k``, sequence s has its queries at ``cu[s]..`` and its keys
     at ``cu_k[s]..`` and a causal row i sees keys j <= i + nk - nq: the
     lower triangle of the pull request's mask, which puts -inf above
-    diagonal 1 + src_len - tgt_len."""
+    diagonal 1 + src_len - tgt_len.  With ``rope`` = (cos, sin) tables, q and
+    k rows at sequence position p are first multiplied, as complex numbers
+    x[2j] + i x[2j+1], by cos[p, j] + i sin[p, j]."""
     mpmath.mp.dps = dps
     if cu_k is None:
         cu_k = cu
+    if rope is not None:
+        q, k = _rotate_mp(q, cu, rope), _rotate_mp(k, cu_k, rope)
     T, H, _, d = q.shape
     Hkv = k.shape[1]
     G = H // Hkv
@@ -99,8 +104,8 @@ def brute_mpmath(q, k, v, lv, lam_init, w, eps, causal, cu, dps=50, cu_k=None):
                         if causal and j > i + nk - n:
                             row.append(mpmath.ninf)
                             continue
-                        x = mpmath.fsum(mpf(float(q[a + i, h, m, c]))
-                                        * mpf(float(k[ka + j, g, m, c]))
+                        x = mpmath.fsum(_mp(q[a + i, h, m, c])
+                                        * _mp(k[ka + j, g, m, c])
                                         for c in range(d))
                         row.append(x * scaling)
                     mx = max(x for x in row if x != mpmath.ninf)
@@ -120,6 +125,28 @@ def brute_mpmath(q, k, v, lv, lam_init, w, eps, causal, cu, dps=50, cu_k=None):
                 for c in range(2 * d):
                     wc = mpf(1) if w is None else mpf(float(w[c]))
                     out[a + i, h, c] = float(pre[c] / rms * wc * (1 - mpf(lam_init)))
+    return out
+
+
+def _mp(x):
+    return x if isinstance(x, mpmath.mpf) else mpmath.mpf(float(x))
+
+
+def _rotate_mp(x, cu, rope):
+    """Rotated copy of x [T, heads, 2, d] as an object array of mpf."""
+    cos, sin = (np.asarray(t, dtype=np.float64) for t in rope)
+    T, nh, two, d = x.shape
+    out = np.empty(x.shape, dtype=object)
+    for s in range(len(cu) - 1):
+        for t in range(int(cu[s]), int(cu[s + 1])):
+            p = t - int(cu[s])
+            for hh in range(nh):
+                for m in range(two):
+                    for j in range(d // 2):
+                        z = (mpmath.mpc(float(x[t, hh, m, 2 * j]), float(x[t, hh, m, 2 * j + 1]))
+                             * mpmath.mpc(cos[p, j], sin[p, j]))
+                        out[t, hh, m, 2 * j] = z.real
+                        out[t, hh, m, 2 * j + 1] = z.imag
     return out
 
 
@@ -387,6 +414,93 @@ def pin_rows_entry(lib):
 
 
 # --------------------------------------------------------------------------
+# rotary prologue (the pull request's interleaved apply_rotary_emb)
+
+def rope_tables(length, d, base=10000.0, offset=0):
+    import workloads
+    c, s_ = workloads.rope_tables(length, d, base, offset)
+    return c.numpy(), s_.numpy()
+
+
+def rotate_torch(x, cu, rope):
+    """q or k [T, heads, 2, d] rotated with torch complex arithmetic
+    (view_as_complex on consecutive pairs times cos + i sin of the row's
+    sequence position), fp64."""
+    cos, sin = (torch.from_numpy(np.asarray(t, dtype=np.float64)) for t in rope)
+    xt = torch.from_numpy(np.asarray(x, dtype=np.float64))
+    T, nh, two, d = xt.shape
+    pos = torch.cat([torch.arange(int(cu[s + 1] - cu[s])) for s in range(len(cu) - 1)])
+    z = torch.view_as_complex(xt.reshape(T, nh, two, d // 2, 2).contiguous())
+    rot = torch.complex(cos, sin)[pos]                             # [T, d/2]
+    out = torch.view_as_real(z * rot[:, None, None, :]).reshape(T, nh, two, d)
+    return out.numpy()
+
+
+def pin_rope_brute_force(lib):
+    cases = [
+        # seed, seqlens, H, Hkv, d, causal
+        (201, (4, 6), 4, 2, 4, True),
+        (202, (5,), 2, 1, 6, False),
+    ]
+    for seed, seqlens, H, Hkv, d, causal in cases:
+        q, k, v, lv, w, cu = tiny_inputs(seed, seqlens, H, Hkv, d)
+        rope = rope_tables(max(seqlens), d, base=3.0)
+        got = oracle.fwd(q, k, v, *lv, 0.45, w, 1e-5, causal, cu, lib=lib, rope=rope)
+        ref = brute_mpmath(q, k, v, lv, 0.45, w, 1e-5, causal, cu, rope=rope)
+        err = np.max(np.abs(got - ref))
+        assert err < 1e-12, f"rope brute force case {seed}: max-abs {err:.3e}"
+
+
+def pin_rope_sdpa(lib):
+    """Rotation by torch complex arithmetic, then the library composition of
+    two SDPA calls, against the oracle's fused rotary prologue (varlen, GQA,
+    positions restart in every sequence)."""
+    H, Hkv, d = 8, 2, 16
+    q, k, v, lv, w, cu = tiny_inputs(210, (45, 1, 70), H, Hkv, d)
+    rope = rope_tables(80, d)
+    lam_init = 0.8 - 0.6 * math.exp(-0.3 * 5)
+    lam = (math.exp(float(np.dot(lv[0].astype(np.float64), lv[1])))
+           - math.exp(float(np.dot(lv[2].astype(np.float64), lv[3])))
+           + lam_init)
+    for causal in (True, False):
+        got = oracle.fwd(q, k, v, *lv, lam_init, w, 1e-5, causal, cu, lib=lib,
+                         rope=rope)
+        ref = sdpa_diff(rotate_torch(q, cu, rope), rotate_torch(k, cu, rope), v,
+                        lam, lam_init, w, 1e-5, causal, cu)
+        err = np.max(np.abs(got - ref))
+        assert err < 1e-10, f"rope vs SDPA (causal={causal}): max-abs {err:.3e}"
+    # rows entry point with the same prologue
+    toks = np.array([0, 44, 45, 46, 115], np.int64)
+    heads = np.array([0, 7, 3, 1, 5], np.int32)
+    full = oracle.fwd(q, k, v, *lv, lam_init, w, 1e-5, True, cu, lib=lib, rope=rope)
+    got = oracle.rows(q, k, v, *lv, lam_init, toks, heads, w, 1e-5, True, cu,
+                      lib=lib, rope=rope)
+    assert np.array_equal(got, full[toks, heads])
+
+
+def pin_rope_identity_and_shift(lib):
+    """cos = 1, sin = 0 rotates nothing (bitwise equal to no prologue); and
+    rotating every position by the same extra angle leaves every score, so
+    every output, unchanged (scores depend on position differences only)."""
+    H, Hkv, d = 4, 2, 8
+    q, k, v, lv, w, cu = tiny_inputs(220, (17, 30), H, Hkv, d)
+    ones = np.ones((30, d // 2), np.float32)
+    zeros = np.zeros((30, d // 2), np.float32)
+    plain = run(lib, q, k, v, lv, 0.3, w, 1e-5, True, cu)
+    ident = oracle.fwd(q, k, v, *lv, 0.3, w, 1e-5, True, cu, lib=lib,
+                       rope=(ones, zeros))
+    assert np.array_equal(plain, ident)
+    a = oracle.fwd(q, k, v, *lv, 0.3, w, 1e-5, True, cu, lib=lib,
+                   rope=rope_tables(30, d, base=7.0))
+    b = oracle.fwd(q, k, v, *lv, 0.3, w, 1e-5, True, cu, lib=lib,
+                   rope=rope_tables(30, d, base=7.0, offset=1000))
+    # the tables are rounded to fp32 at different angles: ~1e-7 apart
+    err = np.max(np.abs(a - b))
+    assert err < 1e-5, f"rope shift invariance: {err:.3e}"
+    assert np.max(np.abs(a - plain)) > 1e-3, "rotation had no effect"
+
+
+# --------------------------------------------------------------------------
 # new queries against a key/value cache
 
 def kv_inputs(seed, nq, nk, H, Hkv, d, q_scale=1.0):
@@ -490,6 +604,9 @@ ALL_PINS = [
     pin_gqa_equals_repeated,
     pin_odd_in_v,
     pin_rows_entry,
+    pin_rope_brute_force,
+    pin_rope_sdpa,
+    pin_rope_identity_and_shift,
     pin_kv_brute_force,
     pin_kv_sdpa,
     pin_kv_prefill_tail,

@@ -20,7 +20,14 @@ MUTANTS = {
     "causal_strict": ("return causal ? i + 1 : n;", "return causal ? (i > 0 ? i : 1) : n;"),
     "decode_alignment_top_left": ("causal ? nk - nq + i + 1 : nk", "causal ? nq - nq + i + 1 : nk"),
     "decode_alignment_off_by_one": ("causal ? nk - nq + i + 1 : nk", "causal ? nk - nq + i : nk"),
-    "decode_keys_from_query_offsets": ("t, cu_k[s], nkeys", "t, cu_q[s], nkeys"),
+    "decode_keys_from_query_offsets": ("cu_k[s], nkeys, h, H, Hkv", "cu_q[s], nkeys, h, H, Hkv"),
+    "rope_sign": ("out[2 * j] = x0 * c - x1 * sn;", "out[2 * j] = x0 * c + x1 * sn;"),
+    "rope_pairs_half_apart": ("const double x0 = (double)x[2 * j], x1 = (double)x[2 * j + 1];",
+                              "const double x0 = (double)x[j], x1 = (double)x[j + d / 2];"),
+    "rope_global_positions": ("t, t - a, a,", "t, t, a,"),
+    "rope_key_position_zero": ("row_rot(k + (((ka + j) * Hkv + g) * 2 + map) * (int64_t)d, d, rp, j, kd);",
+                               "row_rot(k + (((ka + j) * Hkv + g) * 2 + map) * (int64_t)d, d, rp, 0, kd);"),
+    "rope_table_row_stride": ("rp->cos + pos * (int64_t)(d / 2)", "rp->cos + pos * (int64_t)d"),
     "gqa_modulo": ("h / (H / Hkv)", "h % Hkv"),
     "scale_full_width": ("1.0 / sqrt((double)d)", "1.0 / sqrt(2.0 * d)"),
     "scale_squared": ("1.0 / sqrt((double)d)", "1.0 / (double)d"),

@@ -165,6 +165,18 @@ def make_inputs(wl: Workload, seed: Optional[int] = None,
                   wl.depth, wl.eps, wl.causal, wl.max_seqlen)
 
 
+def rope_tables(length: int, d: int, base: float = 10000.0, offset: int = 0):
+    """Rotary tables ``(cos, sin)``, each fp32 ``[length, d/2]``: row p,
+    column j holds cos / sin of (p + offset) * base^(-2j/d), the frequencies
+    RotaryEmbedding(head_dim=d, base) uses in the pull request's test
+    (computed in float64, rounded once to fp32)."""
+    j = np.arange(d // 2, dtype=np.float64)
+    inv_freq = base ** (-2.0 * j / d)
+    ang = np.outer(np.arange(length, dtype=np.float64) + offset, inv_freq)
+    return (torch.from_numpy(np.cos(ang).astype(np.float32)),
+            torch.from_numpy(np.sin(ang).astype(np.float32)))
+
+
 # --------------------------------------------------------------------------
 # new queries against a key/value cache (decoding)
 
