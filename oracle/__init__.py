@@ -56,7 +56,7 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     common = [f32p, f32p, f32p, f32p, f32p, f32p, f32p, ctypes.c_int64,
               ctypes.c_double, f32p, ctypes.c_double, ctypes.c_int, i32p,
               ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
-              ctypes.c_int, f32p, f32p, ctypes.c_int64]
+              ctypes.c_int, f32p, f32p, ctypes.c_int64, ctypes.c_int]
     lib.diffattn_ref_fwd.argtypes = common + [f64p, ctypes.c_int]
     lib.diffattn_ref_fwd.restype = ctypes.c_int
     lib.diffattn_ref_rows.argtypes = common + [i64p, i32p, ctypes.c_int64, f64p,
@@ -104,7 +104,7 @@ def lam(lq1, lk1, lq2, lk2, lambda_init_value: float,
 
 
 def _common(q, k, v, lq1, lk1, lq2, lk2, lambda_init_value, w, eps, causal,
-            cu_seqlens, rope=None):
+            cu_seqlens, rope=None, rope_round_bf16=False):
     qa, ka, va = _f32(q), _f32(k), _f32(v)
     T, H, two, d = qa.shape
     assert two == 2
@@ -143,20 +143,23 @@ def _common(q, k, v, lq1, lk1, lq2, lk2, lambda_init_value, w, eps, causal,
              float(eps), int(bool(causal)), _ptr(cu, ctypes.c_int32),
              int(cu.size - 1), int(T), int(H), int(Hkv), int(d),
              None if rc is None else _ptr(rc, ctypes.c_float),
-             None if rs is None else _ptr(rs, ctypes.c_float), int(rope_len)]
+             None if rs is None else _ptr(rs, ctypes.c_float), int(rope_len),
+             int(bool(rope_round_bf16))]
     return keep, args, (T, H, d)
 
 
 def fwd(q, k, v, lq1, lk1, lq2, lk2, lambda_init_value: float, w=None,
         eps: float = 1e-5, causal: bool = True, cu_seqlens=None,
         nthreads: int = 0, lib: Optional[ctypes.CDLL] = None,
-        rope=None) -> np.ndarray:
+        rope=None, rope_round_bf16: bool = False) -> np.ndarray:
     """Whole output ``[T, H, 2d]`` in fp64.  Layouts as in ``workloads``;
     the lambda vectors are ``[d]`` (shared) or ``[H, d]`` (per head);
-    ``rope`` = (cos, sin) tables ``[len, d/2]`` rotates q and k first."""
+    ``rope`` = (cos, sin) tables ``[len, d/2]`` rotates q and k first
+    (``rope_round_bf16``: and stores the rotated rows as bf16, as a bf16
+    pipeline does)."""
     keep, args, (T, H, d) = _common(q, k, v, lq1, lk1, lq2, lk2,
                                     lambda_init_value, w, eps, causal,
-                                    cu_seqlens, rope)
+                                    cu_seqlens, rope, rope_round_bf16)
     out = np.empty((T, H, 2 * d), dtype=np.float64)
     rc = (lib or load()).diffattn_ref_fwd(*args, _ptr(out, ctypes.c_double),
                                           int(nthreads))
@@ -169,11 +172,12 @@ def fwd(q, k, v, lq1, lk1, lq2, lk2, lambda_init_value: float, w=None,
 def rows(q, k, v, lq1, lk1, lq2, lk2, lambda_init_value: float,
          tokens: Sequence[int], heads: Sequence[int], w=None, eps: float = 1e-5,
          causal: bool = True, cu_seqlens=None, nthreads: int = 0,
-         lib: Optional[ctypes.CDLL] = None, rope=None) -> np.ndarray:
+         lib: Optional[ctypes.CDLL] = None, rope=None,
+         rope_round_bf16: bool = False) -> np.ndarray:
     """Output rows ``[len(tokens), 2d]`` in fp64 for (token, head) pairs."""
     keep, args, (T, H, d) = _common(q, k, v, lq1, lk1, lq2, lk2,
                                     lambda_init_value, w, eps, causal,
-                                    cu_seqlens, rope)
+                                    cu_seqlens, rope, rope_round_bf16)
     tok = np.ascontiguousarray(np.asarray(tokens, dtype=np.int64))
     hd = np.ascontiguousarray(np.asarray(heads, dtype=np.int32))
     assert tok.shape == hd.shape and tok.ndim == 1

@@ -97,12 +97,29 @@ typedef struct {
     const float *cos;
     const float *sin;
     int64_t len;
+    int round_bf16;   /* store rotated rows as bf16, as a bf16 pipeline does */
 } rope_t;
+
+/* x rounded to the nearest bfloat16 (ties to even), by way of the nearest
+ * float: the value a bf16 tensor holds after a float result is stored. */
+static double to_bf16(double x)
+{
+    float f = (float)x;
+    uint32_t u;
+    memcpy(&u, &f, sizeof(u));
+    u += 0x7fffu + ((u >> 16) & 1u);
+    u &= 0xffff0000u;
+    memcpy(&f, &u, sizeof(f));
+    return (double)f;
+}
 
 /* One d-wide half-head row x at sequence position pos, rotated the
  * interleaved way: the pair (x[2j], x[2j+1]) is turned by the angle whose
  * cosine and sine are row pos, column j of the tables (the complex number
- * x[2j] + i x[2j+1] times exp(i angle)).  Widened to double. */
+ * x[2j] + i x[2j+1] times exp(i angle)).  Widened to double; with
+ * round_bf16 the rotated values are then rounded to bfloat16, since the
+ * pull request's pipeline stores the rotated q and k in its bf16 storage
+ * type before the attention reads them. */
 static void row_rot(const float *x, int d, const rope_t *rp, int64_t pos,
                     double *out)
 {
@@ -119,6 +136,9 @@ static void row_rot(const float *x, int d, const rope_t *rp, int64_t pos,
         out[2 * j] = x0 * c - x1 * sn;
         out[2 * j + 1] = x0 * sn + x1 * c;
     }
+    if (rp->round_bf16)
+        for (int c = 0; c < d; ++c)
+            out[c] = to_bf16(out[c]);
 }
 
 /* Softmax of one attention map over the keys j in [0, nkeys) that start at
@@ -219,7 +239,8 @@ static int64_t max_len(const int32_t *cu, int nseq)
 /* Full forward pass: out[T, H, 2d] in double.  cu_seqlens[nseq+1] holds the
  * packed sequence boundaries (host).  rope_cos / rope_sin: rotary tables
  * [rope_len, d/2] (rope_len >= the longest sequence) or NULL for inputs that
- * are already rotated.  nthreads <= 0 uses the OpenMP default.
+ * are already rotated; rope_round_bf16 rounds the rotated rows to bf16.
+ * nthreads <= 0 uses the OpenMP default.
  * Returns 0, or -1 on malformed arguments, -2 if scratch memory is short. */
 int diffattn_ref_fwd(const float *q, const float *k, const float *v,
                      const float *lq1, const float *lk1, const float *lq2,
@@ -227,12 +248,12 @@ int diffattn_ref_fwd(const float *q, const float *k, const float *v,
                      double lambda_init, const float *w, double eps, int causal,
                      const int32_t *cu_seqlens, int nseq, int64_t T, int H,
                      int Hkv, int d, const float *rope_cos,
-                     const float *rope_sin, int64_t rope_len, double *out,
-                     int nthreads)
+                     const float *rope_sin, int64_t rope_len, int rope_round_bf16,
+                     double *out, int nthreads)
 {
     if (check_args(cu_seqlens, nseq, T, H, Hkv, d) || lambda_stride < 0)
         return -1;
-    const rope_t rp = {rope_cos, rope_sin, rope_len};
+    const rope_t rp = {rope_cos, rope_sin, rope_len, rope_round_bf16};
     if (rope_cos && (!rope_sin || d % 2 || rope_len < max_len(cu_seqlens, nseq)))
         return -1;
     double *lam = malloc(sizeof(double) * (size_t)H);
@@ -287,12 +308,13 @@ int diffattn_ref_rows(const float *q, const float *k, const float *v,
                       int causal, const int32_t *cu_seqlens, int nseq,
                       int64_t T, int H, int Hkv, int d, const float *rope_cos,
                       const float *rope_sin, int64_t rope_len,
-                      const int64_t *tok, const int32_t *head, int64_t nrows,
-                      double *out_rows, int nthreads)
+                      int rope_round_bf16, const int64_t *tok,
+                      const int32_t *head, int64_t nrows, double *out_rows,
+                      int nthreads)
 {
     if (check_args(cu_seqlens, nseq, T, H, Hkv, d) || lambda_stride < 0)
         return -1;
-    const rope_t rp = {rope_cos, rope_sin, rope_len};
+    const rope_t rp = {rope_cos, rope_sin, rope_len, rope_round_bf16};
     if (rope_cos && (!rope_sin || d % 2 || rope_len < max_len(cu_seqlens, nseq)))
         return -1;
     for (int64_t r = 0; r < nrows; ++r)
@@ -367,7 +389,7 @@ int diffattn_ref_fwd_kv(const float *q, const float *k, const float *v,
         return -2;
     lambda_per_head(lq1, lk1, lq2, lk2, lambda_stride, H, d, lambda_init, lam);
     const int64_t nmax = max_len(cu_k, nseq);
-    const rope_t no_rope = {NULL, NULL, 0};
+    const rope_t no_rope = {NULL, NULL, 0, 0};
     const int64_t nrows = Tq * H;
     int err = 0;
 #ifdef _OPENMP

@@ -500,6 +500,34 @@ def pin_rope_identity_and_shift(lib):
     assert np.max(np.abs(a - plain)) > 1e-3, "rotation had no effect"
 
 
+def pin_rope_bf16_storage(lib):
+    """With rope_round_bf16 the oracle equals, bitwise, the plain oracle on
+    q and k rotated in fp64 (same products, same order) and stored as bf16
+    by torch's own conversion (a library routine)."""
+    H, Hkv, d = 4, 2, 16
+    q, k, v, lv, w, cu = tiny_inputs(230, (40, 9), H, Hkv, d)
+    rope = rope_tables(40, d, base=20.0)
+    got = oracle.fwd(q, k, v, *lv, 0.5, w, 1e-5, True, cu, lib=lib, rope=rope,
+                     rope_round_bf16=True)
+
+    def rot_bf16(x):
+        cos, sin = (np.asarray(t, dtype=np.float64) for t in rope)
+        pos = np.concatenate([np.arange(int(cu[s + 1] - cu[s])) for s in range(len(cu) - 1)])
+        x0 = x[..., 0::2].astype(np.float64)
+        x1 = x[..., 1::2].astype(np.float64)
+        c = cos[pos][:, None, None, :]
+        s_ = sin[pos][:, None, None, :]
+        out = np.empty(x.shape, np.float64)
+        out[..., 0::2] = x0 * c - x1 * s_
+        out[..., 1::2] = x0 * s_ + x1 * c
+        return torch.from_numpy(out).to(torch.bfloat16).float().numpy()
+
+    ref = run(lib, rot_bf16(q), rot_bf16(k), v, lv, 0.5, w, 1e-5, True, cu)
+    assert np.array_equal(got, ref)
+    plain = oracle.fwd(q, k, v, *lv, 0.5, w, 1e-5, True, cu, lib=lib, rope=rope)
+    assert np.max(np.abs(plain - got)) > 1e-6, "rounding had no effect"
+
+
 # --------------------------------------------------------------------------
 # new queries against a key/value cache
 
@@ -607,6 +635,7 @@ ALL_PINS = [
     pin_rope_brute_force,
     pin_rope_sdpa,
     pin_rope_identity_and_shift,
+    pin_rope_bf16_storage,
     pin_kv_brute_force,
     pin_kv_sdpa,
     pin_kv_prefill_tail,

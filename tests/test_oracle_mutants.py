@@ -28,6 +28,7 @@ MUTANTS = {
     "rope_key_position_zero": ("row_rot(k + (((ka + j) * Hkv + g) * 2 + map) * (int64_t)d, d, rp, j, kd);",
                                "row_rot(k + (((ka + j) * Hkv + g) * 2 + map) * (int64_t)d, d, rp, 0, kd);"),
     "rope_table_row_stride": ("rp->cos + pos * (int64_t)(d / 2)", "rp->cos + pos * (int64_t)d"),
+    "rope_bf16_rounding_dropped": ("    if (rp->round_bf16)\n", "    if (0)\n"),
     "gqa_modulo": ("h / (H / Hkv)", "h % Hkv"),
     "scale_full_width": ("1.0 / sqrt((double)d)", "1.0 / sqrt(2.0 * d)"),
     "scale_squared": ("1.0 / sqrt((double)d)", "1.0 / (double)d"),
