@@ -71,7 +71,8 @@ def traffic_from_profiles(workload: str, sources=KERNEL_SOURCES):
     return float(t.group(1))
 
 
-def cpu_baseline(wl, inp, flop_budget: float = 1.0e12):
+def cpu_baseline(wl, inp, flop_budget: float = 1.0e12, rope=None):
+    # (with rope, rotated rows are stored in the workload's storage type)
     """The fp64 oracle on every s-th query token of the workload, all heads,
     with the stride s >= 1 chosen so that the sample holds at most
     ``flop_budget`` FLOP under the counting convention (the whole headline
@@ -93,7 +94,8 @@ def cpu_baseline(wl, inp, flop_budget: float = 1.0e12):
     oracle.load()
     t0 = time.perf_counter()
     oracle.rows(*arrs[:7], lam0, rows_t, rows_h, arrs[7], wl.eps, wl.causal,
-                cu.astype(np.int32))
+                cu.astype(np.int32), rope=rope,
+                rope_round_bf16=wl.dtype == "bf16")
     dt = time.perf_counter() - t0
     flops = 12.0 * wl.d * wl.H * float(pairs_per_token[toks].sum())
     what = ("every query row of the workload" if stride == 1 else
@@ -247,6 +249,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rope", action="store_true",
+                    help="prefill with the fused rotary prologue (q and k "
+                         "given unrotated, tables of base 10000)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of the workload, time a plain device copy of "
                          "this many bytes (calibrates HBM byte counters)")
@@ -279,10 +284,14 @@ def main() -> int:
     lam0 = da.lambda_init(wl.depth)
     stream = torch.cuda.Stream(dev)
     dtype_code = da.BF16 if wl.dtype == "bf16" else da.F32
+    rope_args = (0, 0, 0)
+    if args.rope:
+        rc, rs = (c(t) for t in workloads.rope_tables(wl.max_seqlen, wl.d))
+        rope_args = (rc.data_ptr(), rs.data_ptr(), wl.max_seqlen)
     ptrs = (dtype_code, q.data_ptr(), k.data_ptr(), v.data_ptr(),
             *[x.data_ptr() for x in lv], 0, lam0, w.data_ptr(), wl.eps,
             int(wl.causal), cu.data_ptr(), wl.nseq, wl.max_seqlen, wl.T, wl.H,
-            wl.Hkv, wl.d, out.data_ptr(), stream.cuda_stream)
+            wl.Hkv, wl.d, *rope_args, out.data_ptr(), stream.cuda_stream)
 
     def step():
         st = da.fwd_ptr(*ptrs)
@@ -321,7 +330,8 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic (seeded N(0,1) q/k/v, N(0,0.1^2) lambda vectors)",
-        "config": {"workload": name, "T": wl.T, "nseq": wl.nseq,
+        "config": {"workload": name + ("+rope" if args.rope else ""),
+                   "T": wl.T, "nseq": wl.nseq, "rope": bool(args.rope),
                    "max_seqlen": wl.max_seqlen, "H": wl.H, "Hkv": wl.Hkv,
                    "d": wl.d, "depth": wl.depth, "causal": wl.causal,
                    "flops_per_step": flops,
@@ -333,7 +343,8 @@ def main() -> int:
                      "frac": round(tflops / peak, 4), "traffic": traffic},
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, inp)
+        result["cpu_baseline"] = cpu_baseline(
+            wl, inp, rope=workloads.rope_tables(wl.max_seqlen, wl.d) if args.rope else None)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

@@ -54,7 +54,7 @@ def library() -> ctypes.CDLL:
     lib.diffattn_fwd.argtypes = [
         ctypes.c_int, vp, vp, vp, f32p, f32p, f32p, f32p, i32, ctypes.c_float,
         f32p, ctypes.c_float, ctypes.c_int, i32p, i32, i32, i32, i32, i32, i32,
-        vp, vp]
+        f32p, f32p, i32, vp, vp]
     lib.diffattn_fwd.restype = ctypes.c_int
     lib.diffattn_fwd_kv.argtypes = [
         ctypes.c_int, vp, vp, vp, f32p, f32p, f32p, f32p, i32, ctypes.c_float,
@@ -155,7 +155,8 @@ def fwd_ptr(dtype: int, q: int, k: int, v: int, lq1: int, lk1: int, lq2: int,
             lk2: int, lambda_stride: int, lambda_init_value: float,
             subln_weight: int, eps: float, causal: int, cu_seqlens: int,
             nseq: int, max_seqlen: int, T: int, H: int, Hkv: int, d: int,
-            out: int, stream: int) -> int:
+            rope_cos: int, rope_sin: int, rope_len: int, out: int,
+            stream: int) -> int:
     """The raw C entry point on integer device addresses; returns the
     status."""
     return library().diffattn_fwd(
@@ -163,7 +164,8 @@ def fwd_ptr(dtype: int, q: int, k: int, v: int, lq1: int, lk1: int, lq2: int,
         lq2 or None, lk2 or None, int(lambda_stride), float(lambda_init_value),
         subln_weight or None, float(eps), int(causal), cu_seqlens or None,
         int(nseq), int(max_seqlen), int(T), int(H), int(Hkv), int(d),
-        out or None, stream or None)
+        rope_cos or None, rope_sin or None, int(rope_len), out or None,
+        stream or None)
 
 
 def _dev(t: torch.Tensor, name: str, device, dtype=None) -> int:
@@ -186,7 +188,8 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         cu_seqlens: Optional[torch.Tensor] = None,
         max_seqlen: Optional[int] = None, nseq: Optional[int] = None,
         out: Optional[torch.Tensor] = None,
-        stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+        stream: Optional[torch.cuda.Stream] = None,
+        rope: Optional[tuple] = None) -> torch.Tensor:
     """Differential-attention forward on the GPU.
 
     q [T, H, 2, d], k [T, Hkv, 2, d], v [T, Hkv, 2d] (bf16 or fp32, one
@@ -195,7 +198,9 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     cu_seqlens int32 [nseq + 1] on the device, or None for ``nseq`` (default
     1) sequences of equal length.  ``max_seqlen`` bounds every sequence
     length; when cu_seqlens is given without it, it is read back from the
-    device (a synchronising copy).  Returns ``out`` [T, H, 2d].
+    device (a synchronising copy).  ``rope`` = (cos, sin) fp32 device tables
+    [len, d/2] applies the interleaved rotary prologue to q and k in the
+    kernel (positions restart in every sequence).  Returns ``out`` [T, H, 2d].
     """
     if q.dim() != 4 or q.shape[2] != 2:
         raise ValueError("q must be [T, H, 2, d]")
@@ -236,6 +241,14 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         nseq = 1 if nseq is None else int(nseq)
         if max_seqlen is None:
             max_seqlen = T // nseq if nseq > 0 else 0
+    rc_ptr = rs_ptr = rope_len = 0
+    if rope is not None:
+        rc, rs = rope
+        if rc.dim() != 2 or rc.shape[1] != d // 2 or tuple(rs.shape) != tuple(rc.shape):
+            raise ValueError("rope tables must be two [len, d/2] tensors")
+        rc_ptr = _dev(rc, "rope cos", dev, torch.float32)
+        rs_ptr = _dev(rs, "rope sin", dev, torch.float32)
+        rope_len = rc.shape[0]
     if out is None:
         out = torch.empty((T, H, 2 * d), dtype=q.dtype, device=dev)
     elif tuple(out.shape) != (T, H, 2 * d):
@@ -248,7 +261,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                      args[4], args[5], args[6], lambda_stride, lambda_init,
                      w_ptr, eps,
                      int(bool(causal)), cu_ptr, nseq, max_seqlen, T, H, Hkv, d,
-                     out_ptr, stream.cuda_stream)
+                     rc_ptr, rs_ptr, rope_len, out_ptr, stream.cuda_stream)
     if st != OK:
         raise DiffAttnError(st, "diffattn_fwd")
     return out

@@ -200,6 +200,75 @@ template <int D> struct VOperand<float, D> {
     }
 };
 
+// ---------------------------------------------------------------------------
+// Rotary prologue (the pull request's apply_rotary_emb with interleaved=True
+// on every d-wide half-head): the pair (x[2j], x[2j+1]) of a row at
+// sequence position pos becomes (x0 c - x1 s, x0 s + x1 c) with c, s the
+// table entries at row pos, column j.  Tables are fp32 [len][d/2]; the
+// rotation runs in fp32 and rounds once to the storage type.  A 16-byte
+// chunk of a row holds whole pairs (4 for bf16, 2 for fp32), so K chunks
+// are rotated in the lane that stages them.
+template <typename E> struct Rope;
+
+template <> struct Rope<bf16> {
+    struct Coef { float4 c, s; };
+    __device__ static inline Coef coef(const float *rc, const float *rs, int pos, int j, int D)
+    {
+        const int64_t o = (int64_t)pos * (D / 2) + j;
+        return Coef{*(const float4 *)(rc + o), *(const float4 *)(rs + o)};
+    }
+    __device__ static inline u32x4 rotate(u32x4 x, const Coef &k)
+    {
+        const bf16x8 v = __builtin_bit_cast(bf16x8, x);
+        const float cc[4] = {k.c.x, k.c.y, k.c.z, k.c.w};
+        const float ss[4] = {k.s.x, k.s.y, k.s.z, k.s.w};
+        bf16x8 r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float x0 = (float)v[2 * i], x1 = (float)v[2 * i + 1];
+            r[2 * i] = (bf16)(x0 * cc[i] - x1 * ss[i]);
+            r[2 * i + 1] = (bf16)(x0 * ss[i] + x1 * cc[i]);
+        }
+        return __builtin_bit_cast(u32x4, r);
+    }
+    // B-operand fragment of dims d0 .. d0+7 of a query row, rotated
+    __device__ static inline bf16x8 q_frag(const bf16 *row, int d0, int, const float *rc,
+                                           const float *rs, int pos, int D)
+    {
+        const u32x4 x = *(const u32x4 *)(row + d0);
+        return __builtin_bit_cast(bf16x8, rotate(x, coef(rc, rs, pos, d0 / 2, D)));
+    }
+};
+
+template <> struct Rope<float> {
+    struct Coef { float2 c, s; };
+    __device__ static inline Coef coef(const float *rc, const float *rs, int pos, int j, int D)
+    {
+        const int64_t o = (int64_t)pos * (D / 2) + j;
+        return Coef{*(const float2 *)(rc + o), *(const float2 *)(rs + o)};
+    }
+    __device__ static inline u32x4 rotate(u32x4 x, const Coef &k)
+    {
+        const float4 v = __builtin_bit_cast(float4, x);
+        float4 r;
+        r.x = v.x * k.c.x - v.y * k.s.x;
+        r.y = v.x * k.s.x + v.y * k.c.x;
+        r.z = v.z * k.c.y - v.w * k.s.y;
+        r.w = v.z * k.s.y + v.w * k.c.y;
+        return __builtin_bit_cast(u32x4, r);
+    }
+    // B-operand element of dim d0 (= 2j + half) of a query row, rotated: the
+    // lane reads both elements of its pair
+    __device__ static inline float q_frag(const float *row, int d0, int half, const float *rc,
+                                          const float *rs, int pos, int D)
+    {
+        const float2 x = *(const float2 *)(row + (d0 & ~1));
+        const int64_t o = (int64_t)pos * (D / 2) + d0 / 2;
+        const float c = rc[o], sn = rs[o];
+        return half ? x.x * sn + x.y * c : x.x * c - x.y * sn;
+    }
+};
+
 struct Params {
     const void *q;
     const void *k;
@@ -209,6 +278,7 @@ struct Params {
     int64_t lstride;   // elements between heads' lambda vectors (0: shared)
     const float *w;
     const int32_t *cu;
+    const float *rcos, *rsin;   // rotary tables [len][d/2], or NULL
     float lambda_init;
     float eps;
     int32_t T, H, Hkv, nseq, seqlen_uniform;
@@ -220,7 +290,7 @@ struct Params {
 
 // Every CU runs one workgroup of 8 waves (two per SIMD); the register
 // budget per lane is the 256 that two waves per SIMD leave.
-template <typename E, int D>
+template <typename E, int D, bool ROPE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void diffattn_fwd_kernel(Params p)
 {
@@ -291,8 +361,12 @@ void diffattn_fwd_kernel(Params p)
             for (int ks = 0; ks < NKS; ++ks) {
                 const int tq = wq0 + 32 * u + n;
                 if (tq < s1) {
-                    const E *src = qg + (((int64_t)tq * p.H + head) * 2 + map) * D + ks * KSTEP + h * VEC;
-                    qf[u][ks] = *(const Frag *)src;
+                    const E *row = qg + (((int64_t)tq * p.H + head) * 2 + map) * D;
+                    if constexpr (ROPE)
+                        qf[u][ks] = Rope<E>::q_frag(row, ks * KSTEP + h * VEC, h,
+                                                    p.rcos, p.rsin, tq - s0, D);
+                    else
+                        qf[u][ks] = *(const Frag *)(row + ks * KSTEP + h * VEC);
                 } else {
                     qf[u][ks] = Frag{};
                 }
@@ -320,6 +394,10 @@ void diffattn_fwd_kernel(Params p)
     const int kdst = lrow * GEO::KROWB + lcol;
     const int vdst = GEO::KTILEB + lrow * GEO::VROWB + lcol;
     u32x4 kst[MAXL], vst[MAXL];
+    // rotary: the cos / sin of the pairs in this lane's K chunk (ROPE only)
+    typename Rope<E>::Coef kcs[MAXL];
+    // rotary pair index of this lane's chunk start within its half-head
+    const int kpair = ((lcol / (int)sizeof(E)) % D) / 2;
     // global -> registers: this wave's loads of block slice b of the tile at k0
     auto stage_load = [&](int k0, int b) __attribute__((always_inline)) {
         const bool tail = k0 + GEO::BN > s1;
@@ -331,13 +409,18 @@ void diffattn_fwd_kernel(Params p)
             const int64_t off = (int64_t)key * rowstride;
             kst[i - b * LPW / GEO::NB] = *(const u32x4 *)(kbytes + off);
             vst[i - b * LPW / GEO::NB] = *(const u32x4 *)(vbytes + off);
+            if constexpr (ROPE)
+                kcs[i - b * LPW / GEO::NB] = Rope<E>::coef(p.rcos, p.rsin, key - s0, kpair, D);
         }
     };
-    // registers -> LDS stage
+    // registers -> LDS stage (rotating K on the way when ROPE)
     auto stage_store = [&](char *stage, int b) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = b * LPW / GEO::NB; i < (b + 1) * LPW / GEO::NB; ++i) {
-            *(u32x4 *)(stage + kdst + i * kWaves * RPL * GEO::KROWB) = kst[i - b * LPW / GEO::NB];
+            u32x4 kv = kst[i - b * LPW / GEO::NB];
+            if constexpr (ROPE)
+                kv = Rope<E>::rotate(kv, kcs[i - b * LPW / GEO::NB]);
+            *(u32x4 *)(stage + kdst + i * kWaves * RPL * GEO::KROWB) = kv;
             *(u32x4 *)(stage + vdst + i * kWaves * RPL * GEO::VROWB) = vst[i - b * LPW / GEO::NB];
         }
     };
@@ -580,8 +663,12 @@ void diffattn_fwd_kernel(Params p)
 template <typename E, int D>
 int launch(const Params &p, int nblocks, hipStream_t stream)
 {
-    hipLaunchKernelGGL((diffattn_fwd_kernel<E, D>), dim3(nblocks), dim3(kThreads), 0,
-                       stream, p);
+    if (p.rcos)
+        hipLaunchKernelGGL((diffattn_fwd_kernel<E, D, true>), dim3(nblocks), dim3(kThreads), 0,
+                           stream, p);
+    else
+        hipLaunchKernelGGL((diffattn_fwd_kernel<E, D, false>), dim3(nblocks), dim3(kThreads), 0,
+                           stream, p);
     return hipGetLastError() == hipSuccess ? DIFFATTN_OK : DIFFATTN_EHIP;
 }
 
@@ -643,7 +730,8 @@ int diffattn_fwd(int dtype, const void *q, const void *k, const void *v,
                  const float *subln_weight, float eps,
                  int causal, const int32_t *cu_seqlens, int32_t nseq,
                  int32_t max_seqlen, int32_t T, int32_t H, int32_t Hkv,
-                 int32_t d, void *out, void *stream)
+                 int32_t d, const float *rope_cos, const float *rope_sin,
+                 int32_t rope_len, void *out, void *stream)
 {
     if (dtype != DIFFATTN_BF16 && dtype != DIFFATTN_F32)
         return DIFFATTN_EINVAL;
@@ -654,6 +742,8 @@ int diffattn_fwd(int dtype, const void *q, const void *k, const void *v,
     if (!(eps >= 0.f) || isinf(eps) || !isfinite(lambda_init))
         return DIFFATTN_EINVAL;
     if (lambda_stride != 0 && lambda_stride < d)
+        return DIFFATTN_EINVAL;
+    if ((rope_cos == nullptr) != (rope_sin == nullptr))
         return DIFFATTN_EINVAL;
     const launch_fn fn = find_launcher(dtype, d);
     if (!fn)
@@ -680,6 +770,10 @@ int diffattn_fwd(int dtype, const void *q, const void *k, const void *v,
     } else if (max_seqlen < 1 || max_seqlen > T) {
         return DIFFATTN_EINVAL;
     }
+    // rotary tables cover every position and are read in 16-byte vectors
+    if (rope_cos && (rope_len < max_seqlen ||
+                     ((uintptr_t)rope_cos | (uintptr_t)rope_sin) % 16 != 0))
+        return DIFFATTN_EINVAL;
     // byte offsets of K/V rows are formed in 64 bits; the grid in 32 bits
     const int G = H / Hkv;
     const int hpw = (G % 4 == 0) ? 4 : (G % 2 == 0 ? 2 : 1);
@@ -701,6 +795,8 @@ int diffattn_fwd(int dtype, const void *q, const void *k, const void *v,
     p.lstride = lambda_stride;
     p.w = subln_weight;
     p.cu = cu_seqlens;
+    p.rcos = rope_cos;
+    p.rsin = rope_sin;
     p.lambda_init = lambda_init;
     p.eps = eps;
     p.T = T;

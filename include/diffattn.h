@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define DIFFATTN_ABI_VERSION 3
+#define DIFFATTN_ABI_VERSION 4
 
 enum diffattn_status {
     DIFFATTN_OK = 0,
@@ -87,6 +87,18 @@ enum diffattn_dtype {
  *                T / nseq, or <= 0 to let the library take that value.
  *   T, H, Hkv, d sizes; H % Hkv == 0.  Compiled (dtype, d) pairs: see
  *                diffattn_supported.
+ *   rope_cos, rope_sin
+ *                NULL (both) when q and k are already rotated; otherwise
+ *                device fp32 tables [rope_len, d/2] (16-byte aligned), and
+ *                the kernel applies the rotary prologue of the
+ *                FlashDiffAttention pull request's test (apply_rotary_emb
+ *                with interleaved=True on every d-wide half-head of q and k):
+ *                the pair (x[2j], x[2j+1]) of a row at position p of its
+ *                sequence (0-based, restarting in every packed sequence)
+ *                becomes (x0 c - x1 s, x0 s + x1 c) with c = rope_cos[p, j],
+ *                s = rope_sin[p, j]; computed in fp32, rounded once to the
+ *                storage type.  V is not rotated.
+ *   rope_len     rows of the tables; >= max_seqlen when they are given.
  *   out          device output [T, H, 2d], same element type as q.
  *   stream       a hipStream_t, or NULL for the null stream.
  *
@@ -100,7 +112,8 @@ int diffattn_fwd(int dtype, const void *q, const void *k, const void *v,
                  const float *subln_weight, float eps,
                  int causal, const int32_t *cu_seqlens, int32_t nseq,
                  int32_t max_seqlen, int32_t T, int32_t H, int32_t Hkv,
-                 int32_t d, void *out, void *stream);
+                 int32_t d, const float *rope_cos, const float *rope_sin,
+                 int32_t rope_len, void *out, void *stream);
 
 /*
  * New queries against a key/value cache (decoding), asynchronous on
