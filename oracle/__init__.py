@@ -68,6 +68,12 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
                       ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                       f64p, ctypes.c_int])
     lib.diffattn_ref_fwd_kv.restype = ctypes.c_int
+    lib.diffattn_ref_bwd.argtypes = (
+        [f32p] * 7 + [ctypes.c_int64, ctypes.c_double, f32p, ctypes.c_double,
+                      ctypes.c_int, i32p, ctypes.c_int, ctypes.c_int64,
+                      ctypes.c_int, ctypes.c_int, ctypes.c_int, f32p]
+        + [f64p] * 8 + [ctypes.c_int])
+    lib.diffattn_ref_bwd.restype = ctypes.c_int
     lib.diffattn_ref_max_threads.argtypes = []
     lib.diffattn_ref_max_threads.restype = ctypes.c_int
     _lib_cache[path] = lib
@@ -234,6 +240,34 @@ def fwd_kv(q, k, v, lq1, lk1, lq2, lk2, lambda_init_value: float, w=None,
         _ptr(out, ctypes.c_double), int(nthreads))
     if rc != 0:
         raise ValueError(f"diffattn_ref_fwd_kv failed with status {rc}")
+    return out
+
+
+def bwd(q, k, v, lq1, lk1, lq2, lk2, lambda_init_value: float, dy, w=None,
+        eps: float = 1e-5, causal: bool = True, cu_seqlens=None,
+        nthreads: int = 0, lib: Optional[ctypes.CDLL] = None) -> dict:
+    """Gradients of <dy, fwd(...)> in fp64: ``dq``, ``dk``, ``dv`` in the
+    input layouts, ``dlq1``.. ``dlk2`` shaped like the lambda vectors and
+    ``dw`` [2d] (the RMSNorm weight; of ones when ``w`` is None)."""
+    keep, args, (T, H, d) = _common(q, k, v, lq1, lk1, lq2, lk2,
+                                    lambda_init_value, w, eps, causal,
+                                    cu_seqlens)
+    Hkv = _f32(k).shape[1]
+    dya = _f32(dy)
+    assert dya.shape == (T, H, 2 * d)
+    lshape = _f32(lq1).shape
+    out = {"dq": np.empty((T, H, 2, d)), "dk": np.empty((T, Hkv, 2, d)),
+           "dv": np.empty((T, Hkv, 2 * d)), "dlq1": np.zeros(lshape),
+           "dlk1": np.zeros(lshape), "dlq2": np.zeros(lshape),
+           "dlk2": np.zeros(lshape), "dw": np.empty(2 * d)}
+    order = ["dq", "dk", "dv", "dlq1", "dlk1", "dlq2", "dlk2", "dw"]
+    # the rotary arguments of the forward entry points are not part of this one
+    rc = (lib or load()).diffattn_ref_bwd(
+        *args[:-4], _ptr(dya, ctypes.c_float),
+        *[_ptr(out[kk], ctypes.c_double) for kk in order], int(nthreads))
+    del keep
+    if rc != 0:
+        raise ValueError(f"diffattn_ref_bwd failed with status {rc}")
     return out
 
 

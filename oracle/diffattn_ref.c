@@ -430,6 +430,199 @@ int diffattn_ref_fwd_kv(const float *q, const float *k, const float *v,
     return err;
 }
 
+/* Backward of the prefill (inputs already rotated; no rotary prologue).
+ * Given the output gradient dy[T, H, 2d], writes in double:
+ *   dq[T, H, 2, d], dk[T, Hkv, 2, d], dv[T, Hkv, 2d];
+ *   dlq1, dlk1, dlq2, dlk2: gradients of the lambda vectors, laid out like
+ *     them (lambda_stride 0: one set of d; else H sets, stride apart);
+ *   dw[2d]: gradient of the RMSNorm weight (of a weight of ones when w is
+ *     NULL).
+ * The chain, per row (token i, head h) of the forward above:
+ *   g = dy * w * (1 - lambda_init);  r = 1 / sqrt(mean(pre^2) + eps)
+ *   dpre = r g - r^3 pre <g, pre> / (2d);   dw += dy * pre * r * (1 - lambda_init)
+ *   dO_1 = dpre;  dO_2 = -lambda dpre;  dlambda_h += -<dpre, O_2>
+ *   per map m: D_m = <dO_m, O_m>;  dS_m[j] = P_m[j] (<dO_m, V_j> - D_m)
+ *     dQ_m[i] += scale sum_j dS_m[j] K_m[j];  dK_m[j] += scale dS_m[j] Q_m[i]
+ *     dV[j] += P_m[j] dO_m
+ *   lambda = exp(a) - exp(b) + lambda_init with a = <lq1, lk1>, b = <lq2, lk2>:
+ *     dlq1 = dlambda e^a lk1, dlk1 = dlambda e^a lq1,
+ *     dlq2 = -dlambda e^b lk2, dlk2 = -dlambda e^b lq2
+ * Work is split by (sequence, KV head), so every dk/dv element has one
+ * writer; dlambda and dw are summed per task and reduced in task order.
+ * Returns 0, -1 on malformed arguments, -2 without memory. */
+int diffattn_ref_bwd(const float *q, const float *k, const float *v,
+                     const float *lq1, const float *lk1, const float *lq2,
+                     const float *lk2, int64_t lambda_stride, double lambda_init,
+                     const float *w, double eps, int causal,
+                     const int32_t *cu_seqlens, int nseq, int64_t T, int H,
+                     int Hkv, int d, const float *dy, double *dq, double *dk,
+                     double *dv, double *dlq1, double *dlk1, double *dlq2,
+                     double *dlk2, double *dw, int nthreads)
+{
+    if (check_args(cu_seqlens, nseq, T, H, Hkv, d) || lambda_stride < 0)
+        return -1;
+    const int G = H / Hkv, dv2 = 2 * d;
+    const int64_t ntask = (int64_t)nseq * Hkv;
+    double *lam = malloc(sizeof(double) * (size_t)H);
+    double *tdl = calloc((size_t)(ntask * H), sizeof(double));   /* dlambda per task, head */
+    double *tdw = calloc((size_t)(ntask * dv2), sizeof(double)); /* dw per task */
+    if (!lam || !tdl || !tdw) {
+        free(lam);
+        free(tdl);
+        free(tdw);
+        return -2;
+    }
+    lambda_per_head(lq1, lk1, lq2, lk2, lambda_stride, H, d, lambda_init, lam);
+    memset(dq, 0, sizeof(double) * (size_t)(T * H * 2 * d));
+    memset(dk, 0, sizeof(double) * (size_t)(T * Hkv * 2 * d));
+    memset(dv, 0, sizeof(double) * (size_t)(T * Hkv * dv2));
+    const int64_t nmax = max_len(cu_seqlens, nseq);
+    const double scale = 1.0 / sqrt((double)d);
+    int err = 0;
+#ifdef _OPENMP
+    if (nthreads <= 0)
+        nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads)
+#endif
+    {
+        /* p1, p2 [nmax]; o1, o2, pre, do1, do2 [2d] */
+        double *sc = malloc(sizeof(double) * (size_t)(2 * nmax + 5 * dv2 + 1));
+        if (!sc) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+            err = -2;
+        }
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+        for (int64_t task = 0; task < ntask; ++task) {
+            if (!sc)
+                continue;
+            const int s = (int)(task / Hkv), g = (int)(task % Hkv);
+            const int64_t a = cu_seqlens[s], n = cu_seqlens[s + 1] - a;
+            double *p[2] = {sc, sc + nmax};
+            double *o[2] = {sc + 2 * nmax, sc + 2 * nmax + dv2};
+            double *pre = o[1] + dv2, *dO[2] = {pre + dv2, pre + 2 * dv2};
+            for (int h = g * G; h < (g + 1) * G; ++h) {
+                for (int64_t i = 0; i < n; ++i) {
+                    const int64_t t = a + i, nk = prefill_keys(causal, i, n);
+                    /* forward of the row: both maps, O_m normalised */
+                    for (int m = 0; m < 2; ++m) {
+                        const float *qr = q + ((t * H + h) * 2 + m) * (int64_t)d;
+                        double mx = -INFINITY;
+                        for (int64_t j = 0; j < nk; ++j) {
+                            const float *kr = k + (((a + j) * Hkv + g) * 2 + m) * (int64_t)d;
+                            double x = 0.0;
+                            for (int c = 0; c < d; ++c)
+                                x += (double)qr[c] * (double)kr[c];
+                            p[m][j] = x * scale;
+                            if (p[m][j] > mx)
+                                mx = p[m][j];
+                        }
+                        double z = 0.0;
+                        for (int64_t j = 0; j < nk; ++j) {
+                            p[m][j] = exp(p[m][j] - mx);
+                            z += p[m][j];
+                        }
+                        for (int c = 0; c < dv2; ++c)
+                            o[m][c] = 0.0;
+                        for (int64_t j = 0; j < nk; ++j) {
+                            p[m][j] /= z;
+                            const float *vr = v + ((a + j) * Hkv + g) * (int64_t)dv2;
+                            for (int c = 0; c < dv2; ++c)
+                                o[m][c] += p[m][j] * (double)vr[c];
+                        }
+                    }
+                    double ss = 0.0;
+                    for (int c = 0; c < dv2; ++c) {
+                        pre[c] = o[0][c] - lam[h] * o[1][c];
+                        ss += pre[c] * pre[c];
+                    }
+                    const double r = 1.0 / sqrt(ss / (double)dv2 + eps);
+                    /* RMSNorm, weight and scale backward */
+                    const float *dyr = dy + (t * H + h) * (int64_t)dv2;
+                    double gp = 0.0;
+                    for (int c = 0; c < dv2; ++c) {
+                        const double wc = w ? (double)w[c] : 1.0;
+                        gp += (double)dyr[c] * wc * (1.0 - lambda_init) * pre[c];
+                        tdw[task * dv2 + c] += (double)dyr[c] * pre[c] * r * (1.0 - lambda_init);
+                    }
+                    double dl = 0.0;
+                    for (int c = 0; c < dv2; ++c) {
+                        const double wc = w ? (double)w[c] : 1.0;
+                        const double gc = (double)dyr[c] * wc * (1.0 - lambda_init);
+                        const double dp = r * gc - r * r * r * pre[c] * gp / (double)dv2;
+                        dO[0][c] = dp;
+                        dO[1][c] = -lam[h] * dp;
+                        dl -= dp * o[1][c];
+                    }
+                    tdl[task * H + h] += dl;
+                    /* both softmax maps */
+                    for (int m = 0; m < 2; ++m) {
+                        double D = 0.0;
+                        for (int c = 0; c < dv2; ++c)
+                            D += dO[m][c] * o[m][c];
+                        const float *qr = q + ((t * H + h) * 2 + m) * (int64_t)d;
+                        double *dqr = dq + ((t * H + h) * 2 + m) * (int64_t)d;
+                        for (int64_t j = 0; j < nk; ++j) {
+                            const float *vr = v + ((a + j) * Hkv + g) * (int64_t)dv2;
+                            double dpj = 0.0;
+                            for (int c = 0; c < dv2; ++c)
+                                dpj += dO[m][c] * (double)vr[c];
+                            const double ds = p[m][j] * (dpj - D);
+                            const float *kr = k + (((a + j) * Hkv + g) * 2 + m) * (int64_t)d;
+                            double *dkr = dk + (((a + j) * Hkv + g) * 2 + m) * (int64_t)d;
+                            for (int c = 0; c < d; ++c) {
+                                dqr[c] += scale * ds * (double)kr[c];
+                                dkr[c] += scale * ds * (double)qr[c];
+                            }
+                            double *dvr = dv + ((a + j) * Hkv + g) * (int64_t)dv2;
+                            for (int c = 0; c < dv2; ++c)
+                                dvr[c] += p[m][j] * dO[m][c];
+                        }
+                    }
+                }
+            }
+        }
+        free(sc);
+    }
+    if (!err) {
+        /* reduce in task order; lambda-vector gradients by the chain rule */
+        for (int c = 0; c < dv2; ++c) {
+            double acc = 0.0;
+            for (int64_t t2 = 0; t2 < ntask; ++t2)
+                acc += tdw[t2 * dv2 + c];
+            dw[c] = acc;
+        }
+        const int nsets = lambda_stride ? H : 1;
+        for (int st = 0; st < nsets; ++st) {
+            double dlam = 0.0;
+            for (int h = 0; h < H; ++h)
+                if (!lambda_stride || h == st)
+                    for (int64_t t2 = 0; t2 < ntask; ++t2)
+                        dlam += tdl[t2 * H + h];
+            const int64_t off = (int64_t)st * lambda_stride;
+            double a1 = 0.0, b1 = 0.0;
+            for (int c = 0; c < d; ++c) {
+                a1 += (double)lq1[off + c] * (double)lk1[off + c];
+                b1 += (double)lq2[off + c] * (double)lk2[off + c];
+            }
+            const double ea = exp(a1), eb = exp(b1);
+            for (int c = 0; c < d; ++c) {
+                dlq1[off + c] = dlam * ea * (double)lk1[off + c];
+                dlk1[off + c] = dlam * ea * (double)lq1[off + c];
+                dlq2[off + c] = -dlam * eb * (double)lk2[off + c];
+                dlk2[off + c] = -dlam * eb * (double)lq2[off + c];
+            }
+        }
+    }
+    free(lam);
+    free(tdl);
+    free(tdw);
+    return err;
+}
+
 /* Number of OpenMP threads a parallel region with nthreads <= 0 would use. */
 int diffattn_ref_max_threads(void)
 {

@@ -529,6 +529,96 @@ def pin_rope_bf16_storage(lib):
 
 
 # --------------------------------------------------------------------------
+# backward
+
+def autograd_composition(q, k, v, lv, lam_init, w, eps, causal, cu, dy):
+    """Gradients of <dy, out> by torch autograd in fp64 through the library
+    composition: lambda from the vectors, two SDPA calls per sequence (GQA
+    through enable_gqa), their difference, rms_norm with the weight, the
+    (1 - lambda_init) scale."""
+    f = lambda x: torch.tensor(np.asarray(x, dtype=np.float64), requires_grad=True)
+    qt, kt, vt, wt = f(q), f(k), f(v), f(w)
+    lt = [f(x) for x in lv]
+    a = (lt[0] * lt[1]).sum(-1)
+    b = (lt[2] * lt[3]).sum(-1)
+    lam = torch.exp(a) - torch.exp(b) + lam_init
+    T, H, _, d = q.shape
+    sc = 1.0 / math.sqrt(d)
+    outs = []
+    for s in range(len(cu) - 1):
+        a0, b0 = int(cu[s]), int(cu[s + 1])
+        if b0 == a0:
+            continue
+        seg = lambda x, m: x[a0:b0, :, m].permute(1, 0, 2).unsqueeze(0)
+        vv = vt[a0:b0].permute(1, 0, 2).unsqueeze(0)
+        o1 = F.scaled_dot_product_attention(seg(qt, 0), seg(kt, 0), vv,
+                                            is_causal=causal, scale=sc, enable_gqa=True)
+        o2 = F.scaled_dot_product_attention(seg(qt, 1), seg(kt, 1), vv,
+                                            is_causal=causal, scale=sc, enable_gqa=True)
+        o = o1 - lam.reshape(-1, 1, 1) * o2
+        o = F.rms_norm(o, (2 * d,), weight=wt, eps=eps) * (1.0 - lam_init)
+        outs.append(o[0].permute(1, 0, 2))
+    y = torch.cat(outs, 0)
+    (y * torch.from_numpy(np.asarray(dy, dtype=np.float64))).sum().backward()
+    g = {"dq": qt.grad, "dk": kt.grad, "dv": vt.grad, "dw": wt.grad}
+    for name, t in zip(("dlq1", "dlk1", "dlq2", "dlk2"), lt):
+        g[name] = t.grad
+    return {kk: x.numpy() for kk, x in g.items()}
+
+
+def pin_bwd_autograd(lib):
+    cases = [
+        # seed, seqlens, H, Hkv, d, causal, per-head lambda
+        (301, (9, 1, 14), 4, 2, 8, True, False),
+        (302, (11, 6), 6, 2, 4, False, False),
+        (303, (7, 12), 4, 1, 8, True, True),
+    ]
+    for seed, seqlens, H, Hkv, d, causal, per_head in cases:
+        q, k, v, lv, w, cu = tiny_inputs(seed, seqlens, H, Hkv, d)
+        if per_head:
+            rng = np.random.default_rng(seed + 1)
+            lv = [(0.3 * rng.standard_normal((H, d))).astype(np.float32) for _ in range(4)]
+        dy = np.random.default_rng(seed + 2).standard_normal((q.shape[0], H, 2 * d)).astype(np.float32)
+        lam_init = 0.8 - 0.6 * math.exp(-0.3 * (seed - 300))
+        got = oracle.bwd(q, k, v, *lv, lam_init, dy, w, 1e-5, causal, cu, lib=lib)
+        ref = autograd_composition(q, k, v, lv, lam_init, w, 1e-5, causal, cu, dy)
+        for name in ref:
+            err = np.max(np.abs(got[name] - ref[name]))
+            assert err < 1e-9, f"bwd vs autograd case {seed} {name}: max-abs {err:.3e}"
+
+
+def pin_bwd_finite_differences(lib):
+    """Central differences of <dy, oracle forward> along +-1 directions
+    scaled by 2^-10 (exact in fp32 for these inputs) against <grad, u>."""
+    H, Hkv, d = 4, 2, 4
+    for causal in (True, False):
+        q, k, v, lv, w, cu = tiny_inputs(310 + causal, (7, 5), H, Hkv, d)
+        dy = np.random.default_rng(311).standard_normal((12, H, 2 * d)).astype(np.float32)
+        lam_init = 0.35
+        g = oracle.bwd(q, k, v, *lv, lam_init, dy, w, 1e-5, causal, cu, lib=lib)
+        base = dict(q=q, k=k, v=v, lq1=lv[0], lk1=lv[1], lq2=lv[2], lk2=lv[3], w=w)
+        eps = 2.0 ** -10
+
+        def loss(x):
+            out = oracle.fwd(x["q"], x["k"], x["v"], x["lq1"], x["lk1"], x["lq2"],
+                             x["lk2"], lam_init, x["w"], 1e-5, causal, cu, lib=lib)
+            return float(np.sum(out * dy.astype(np.float64)))
+
+        rng = np.random.default_rng(312)
+        for name, gname in (("q", "dq"), ("k", "dk"), ("v", "dv"), ("w", "dw"),
+                            ("lq1", "dlq1"), ("lk1", "dlk1"), ("lq2", "dlq2"),
+                            ("lk2", "dlk2")):
+            u = rng.choice([-1.0, 1.0], size=base[name].shape).astype(np.float32)
+            xp, xm = dict(base), dict(base)
+            xp[name] = (base[name] + np.float32(eps) * u).astype(np.float32)
+            xm[name] = (base[name] - np.float32(eps) * u).astype(np.float32)
+            fd = (loss(xp) - loss(xm)) / (2 * eps)
+            an = float(np.sum(g[gname] * u))
+            assert abs(fd - an) <= 1e-4 * max(1.0, abs(an)), \
+                f"finite differences {name} causal={causal}: {fd:.8f} vs {an:.8f}"
+
+
+# --------------------------------------------------------------------------
 # new queries against a key/value cache
 
 def kv_inputs(seed, nq, nk, H, Hkv, d, q_scale=1.0):
@@ -636,6 +726,8 @@ ALL_PINS = [
     pin_rope_sdpa,
     pin_rope_identity_and_shift,
     pin_rope_bf16_storage,
+    pin_bwd_autograd,
+    pin_bwd_finite_differences,
     pin_kv_brute_force,
     pin_kv_sdpa,
     pin_kv_prefill_tail,

@@ -29,6 +29,20 @@ MUTANTS = {
                                "row_rot(k + (((ka + j) * Hkv + g) * 2 + map) * (int64_t)d, d, rp, 0, kd);"),
     "rope_table_row_stride": ("rp->cos + pos * (int64_t)(d / 2)", "rp->cos + pos * (int64_t)d"),
     "rope_bf16_rounding_dropped": ("    if (rp->round_bf16)\n", "    if (0)\n"),
+    "bwd_softmax_no_D": ("const double ds = p[m][j] * (dpj - D);", "const double ds = p[m][j] * dpj;"),
+    "bwd_map2_lambda_sign": ("dO[1][c] = -lam[h] * dp;", "dO[1][c] = lam[h] * dp;"),
+    "bwd_rmsnorm_no_r3_term": ("const double dp = r * gc - r * r * r * pre[c] * gp / (double)dv2;",
+                               "const double dp = r * gc;"),
+    "bwd_dv_from_map1_only": ("dvr[c] += p[m][j] * dO[m][c];", "dvr[c] += p[0][j] * dO[0][c];"),
+    "bwd_dq_from_q": ("dqr[c] += scale * ds * (double)kr[c];", "dqr[c] += scale * ds * (double)qr[c] + 0.0 * kr[c];"),
+    "bwd_dk_unscaled": ("dkr[c] += scale * ds * (double)qr[c];", "dkr[c] += ds * (double)qr[c];"),
+    "bwd_dw_without_r": ("tdw[task * dv2 + c] += (double)dyr[c] * pre[c] * r * (1.0 - lambda_init);",
+                         "tdw[task * dv2 + c] += (double)dyr[c] * pre[c] * (1.0 - lambda_init);"),
+    "bwd_dlambda_sign": ("dl -= dp * o[1][c];", "dl += dp * o[1][c];"),
+    "bwd_dlq1_wrong_vector": ("dlq1[off + c] = dlam * ea * (double)lk1[off + c];",
+                              "dlq1[off + c] = dlam * ea * (double)lq1[off + c];"),
+    "bwd_dlk2_sign": ("dlk2[off + c] = -dlam * eb * (double)lq2[off + c];",
+                      "dlk2[off + c] = dlam * eb * (double)lq2[off + c];"),
     "gqa_modulo": ("h / (H / Hkv)", "h % Hkv"),
     "scale_full_width": ("1.0 / sqrt((double)d)", "1.0 / sqrt(2.0 * d)"),
     "scale_squared": ("1.0 / sqrt((double)d)", "1.0 / (double)d"),
