@@ -18,6 +18,7 @@ from typing import Optional
 import torch
 
 __all__ = ["fwd", "fwd_ptr", "fwd_kv", "fwd_kv_ptr", "kv_workspace_size",
+           "fwd_train", "bwd", "bwd_workspace_size", "supported_bwd",
            "lambda_init", "supported", "supported_kv", "check_cu_seqlens",
            "check_cu_seqlens_kv", "library", "LIBRARY", "DiffAttnError",
            "BF16", "F32"]
@@ -69,6 +70,20 @@ def library() -> ctypes.CDLL:
         ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32), i32,
         i32, i32, i32, i32, ctypes.c_int]
     lib.diffattn_check_cu_seqlens_kv.restype = ctypes.c_int
+    lib.diffattn_fwd_train.argtypes = [
+        ctypes.c_int, vp, vp, vp, f32p, f32p, f32p, f32p, i32, ctypes.c_float,
+        f32p, ctypes.c_float, ctypes.c_int, i32p, i32, i32, i32, i32, i32, i32,
+        vp, vp, vp, vp]
+    lib.diffattn_fwd_train.restype = ctypes.c_int
+    lib.diffattn_bwd.argtypes = [
+        ctypes.c_int, vp, vp, vp, f32p, f32p, f32p, f32p, i32, ctypes.c_float,
+        f32p, ctypes.c_float, ctypes.c_int, i32p, i32, i32, i32, i32, i32, i32,
+        vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.diffattn_bwd.restype = ctypes.c_int
+    lib.diffattn_bwd_workspace_size.argtypes = [i32, i32, i32]
+    lib.diffattn_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.diffattn_supported_bwd.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.diffattn_supported_bwd.restype = ctypes.c_int
     lib.diffattn_lambda_init.argtypes = [ctypes.c_int]
     lib.diffattn_lambda_init.restype = ctypes.c_double
     lib.diffattn_supported.argtypes = [ctypes.c_int, ctypes.c_int]
@@ -362,3 +377,93 @@ def fwd_kv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if st != OK:
         raise DiffAttnError(st, "diffattn_fwd_kv")
     return out
+
+
+def supported_bwd(dtype: torch.dtype, d: int) -> bool:
+    return bool(library().diffattn_supported_bwd(_DTYPES[dtype], int(d)))
+
+
+def bwd_workspace_size(T: int, H: int, d: int) -> int:
+    return int(library().diffattn_bwd_workspace_size(int(T), int(H), int(d)))
+
+
+def _seq_args(T, cu_seqlens, max_seqlen, nseq, dev):
+    if cu_seqlens is not None:
+        cu_ptr = _dev(cu_seqlens, "cu_seqlens", dev, torch.int32)
+        nseq = cu_seqlens.numel() - 1
+        if max_seqlen is None:
+            c = cu_seqlens.cpu()
+            max_seqlen = int((c[1:] - c[:-1]).max()) if nseq > 0 else 0
+        return cu_ptr, nseq, max_seqlen
+    nseq = 1 if nseq is None else int(nseq)
+    return 0, nseq, (T // nseq if nseq > 0 else 0)
+
+
+def fwd_train(q, k, v, lambda_q1, lambda_k1, lambda_q2, lambda_k2,
+              lambda_init: float, subln_weight=None, eps: float = 1e-5,
+              causal: bool = True, cu_seqlens=None, max_seqlen=None, nseq=None,
+              stream=None):
+    """Training forward: returns ``(out, lse, o12)`` where ``lse``
+    [T, H, 2] and ``o12`` [T, H, 2, 2d] (fp32) are what ``bwd`` needs."""
+    T, H, _, d = q.shape
+    Hkv = k.shape[1]
+    dev = q.device
+    lptrs, lstride = _lambda_args((lambda_q1, lambda_k1, lambda_q2, lambda_k2), H, d, dev)
+    w_ptr = 0 if subln_weight is None else _dev(subln_weight, "subln_weight", dev, torch.float32)
+    cu_ptr, nseq, max_seqlen = _seq_args(T, cu_seqlens, max_seqlen, nseq, dev)
+    out = torch.empty((T, H, 2 * d), dtype=q.dtype, device=dev)
+    lse = torch.empty((T, H, 2), dtype=torch.float32, device=dev)
+    o12 = torch.empty((T, H, 2, 2 * d), dtype=torch.float32, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        st = library().diffattn_fwd_train(
+            _DTYPES[q.dtype], _dev(q, "q", dev), _dev(k, "k", dev, q.dtype),
+            _dev(v, "v", dev, q.dtype), *lptrs, lstride, float(lambda_init),
+            w_ptr or None, float(eps), int(bool(causal)), cu_ptr or None, nseq,
+            max_seqlen, T, H, Hkv, d, out.data_ptr() or None,
+            lse.data_ptr() or None, o12.data_ptr() or None, stream.cuda_stream)
+    if st != OK:
+        raise DiffAttnError(st, "diffattn_fwd_train")
+    return out, lse, o12
+
+
+def bwd(q, k, v, lambda_q1, lambda_k1, lambda_q2, lambda_k2,
+        lambda_init: float, dout, lse, o12, subln_weight=None,
+        eps: float = 1e-5, causal: bool = True, cu_seqlens=None,
+        max_seqlen=None, nseq=None, workspace=None, stream=None) -> dict:
+    """Backward of the prefill: gradients of sum(dout * out) as a dict with
+    ``dq``, ``dk``, ``dv`` (storage type), ``dlq1`` .. ``dlk2`` (fp32, shaped
+    like the lambda vectors) and ``dw`` (fp32 [2d])."""
+    T, H, _, d = q.shape
+    Hkv = k.shape[1]
+    dev = q.device
+    lvs = (lambda_q1, lambda_k1, lambda_q2, lambda_k2)
+    lptrs, lstride = _lambda_args(lvs, H, d, dev)
+    w_ptr = 0 if subln_weight is None else _dev(subln_weight, "subln_weight", dev, torch.float32)
+    cu_ptr, nseq, max_seqlen = _seq_args(T, cu_seqlens, max_seqlen, nseq, dev)
+    g = {"dq": torch.empty_like(q), "dk": torch.empty_like(k),
+         "dv": torch.empty_like(v)}
+    for name, lv in zip(("dlq1", "dlk1", "dlq2", "dlk2"), lvs):
+        g[name] = torch.zeros_like(lv)
+    g["dw"] = torch.zeros(2 * d, dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(bwd_workspace_size(T, H, d), 16),
+                                dtype=torch.uint8, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    ptr = lambda t: t.data_ptr() or None
+    with torch.cuda.device(dev):
+        st = library().diffattn_bwd(
+            _DTYPES[q.dtype], _dev(q, "q", dev), _dev(k, "k", dev, q.dtype),
+            _dev(v, "v", dev, q.dtype), *lptrs, lstride, float(lambda_init),
+            w_ptr or None, float(eps), int(bool(causal)), cu_ptr or None, nseq,
+            max_seqlen, T, H, Hkv, d, _dev(dout, "dout", dev, q.dtype),
+            _dev(lse, "lse", dev, torch.float32), _dev(o12, "o12", dev, torch.float32),
+            ptr(g["dq"]), ptr(g["dk"]), ptr(g["dv"]), ptr(g["dlq1"]),
+            ptr(g["dlk1"]), ptr(g["dlq2"]), ptr(g["dlk2"]), ptr(g["dw"]),
+            _dev(workspace, "workspace", dev), workspace.numel(),
+            stream.cuda_stream)
+    if st != OK:
+        raise DiffAttnError(st, "diffattn_bwd")
+    return g

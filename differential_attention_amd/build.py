@@ -10,7 +10,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SOURCES = [os.path.join(HERE, "csrc", "diffattn_fwd.hip"),
-           os.path.join(HERE, "csrc", "diffattn_kv.hip")]
+           os.path.join(HERE, "csrc", "diffattn_kv.hip"),
+           os.path.join(HERE, "csrc", "diffattn_bwd.hip")]
 LIBRARY = os.path.join(HERE, "libdiffattn.so")
 ARCH = "gfx950"
 

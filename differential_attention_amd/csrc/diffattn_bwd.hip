@@ -1,0 +1,716 @@
+// diffattn_bwd.hip -- backward pass of the differential-attention prefill
+// for CDNA4 (gfx950).
+//
+// The gradients are those of diffattn_bwd in include/diffattn.h: the
+// DiffTransformer page's MultiHeadDifferentialAttention.forward (and the
+// gist's two-SDPA form) differentiated through the RMSNorm, the
+// lambda-weighted difference of the two softmax maps and the lambda
+// re-parameterisation.  The training forward (diffattn_fwd_train) saved,
+// per row and map, the log2-sum-exp of the scaled scores and the
+// normalised output O_m.
+//
+// Four kernels, no atomics (the result is bitwise reproducible):
+//
+//  prep     one wave per (head, token stride): pre = O_1 - lambda O_2 and
+//           its RMSNorm backward, dO_1 = dpre, dO_2 = -lambda dpre (stored
+//           bf16 as MFMA operands), D_m = <dO_m, O_m> (from the rounded
+//           dO_m, so that the softmax gradients of a row sum to zero),
+//           and per-wave partial sums of the weight and lambda gradients.
+//  reduce   one workgroup: the partial sums in a fixed order, and the
+//           lambda-vector gradients by the chain rule.
+//  dq       query-outer, as the forward: one workgroup = (sequence, head,
+//           128 queries), wave = (map, 32 queries).  Over K/V tiles staged
+//           in LDS: S^T = K Q^T, P^T = exp2(S^T c - lse), dP^T = V dO^T,
+//           dS^T = P^T (dP^T - D), dQ^T += K^T dS^T (K^T through the
+//           transposing LDS read, dS^T straight from the accumulator).
+//  dkdv     key-outer: one workgroup = (sequence, KV head, 128 keys), wave
+//           = (map, 32 keys) with its K and V rows in registers.  Over the
+//           group's heads and the query tiles that can see the keys (Q, dO,
+//           lse, D staged in LDS): S = Q K^T, P, dP = dO V^T, dS, then
+//           dV^T += dO^T P and dK^T += Q^T dS (dO^T and Q^T through the
+//           transposing read, P and dS straight from the accumulator).  The
+//           two maps' dV are summed through LDS at the end.
+//
+// All contractions run on v_mfma_f32_32x32x16_bf16 with fp32 accumulators;
+// P and dS are rounded to bf16 as operands, as are dO_m.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "diffattn.h"
+
+namespace {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kThreads = 512;   // 8 waves: 2 maps x 4 blocks of 32 rows
+constexpr int kTile = 128;      // queries (dq) or keys (dkdv) per workgroup
+constexpr int kInner = 64;      // keys (dq) or queries (dkdv) per staged tile
+constexpr int kPrepPerHead = 64;   // prep waves per head
+
+__device__ inline f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Row (offset inside a 32-row block) of accumulator element a of a lane in
+// half h of a 32x32 MFMA result.
+__device__ constexpr int acc_row(int a, int h) { return 8 * (a / 4) + 4 * h + (a % 4); }
+
+// Accumulator elements a0 .. a0+7 as a bf16 operand: rows 16 (a0/8) + 8t +
+// 4h + e (t = 0, 1), the contraction order of tr_operand below.
+__device__ inline bf16x8 pack8(const f32x16 &s, int a0)
+{
+    bf16x8 f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        f[e] = (bf16)s[a0 + e];
+    return f;
+}
+
+// A operand X^T for a contraction over 16 rows of a row-major bf16 LDS tile
+// X: lane (column i, half h) gets X[step_row + 8t + 4h + e][i] for t, e in
+// 0..3 (two transposing reads).  col_byte selects the 32 columns.
+struct TrOperand {
+    int base;
+    __device__ TrOperand(int lane, int rowb)
+    {
+        const int j = lane & 15;
+        base = (4 * (lane >> 5) + (j >> 2)) * rowb + 32 * ((lane >> 4) & 1) + 8 * (j & 3);
+    }
+    __device__ inline bf16x8 load(const char *tile, int rowb, int step_row, int col_byte) const
+    {
+        bf16x8 f;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const char *addr = tile + base + (step_row + 8 * t) * rowb + col_byte;
+            const bf16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (__attribute__((address_space(3))) bf16x4 *)addr);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                f[4 * t + e] = x[e];
+        }
+        return f;
+    }
+};
+
+__device__ inline float wave_sum(float x)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+struct BwdParams {
+    const bf16 *q, *k, *v, *dy;
+    const float *lse;    // [T][H][2]
+    const float *o12;    // [T][H][2][2d]
+    const float *lq1, *lk1, *lq2, *lk2;
+    int64_t lstride;
+    const float *w;
+    const int32_t *cu;
+    bf16 *dq, *dk, *dv;
+    float *dlq1, *dlk1, *dlq2, *dlk2, *dw;
+    // workspace
+    bf16 *do12;          // [T][H][2][2d]
+    float *dd;           // [T][H][2]
+    float *part_dw;      // [nprep][2d]
+    float *part_dl;      // [nprep]
+    float lambda_init, eps;
+    int32_t T, H, Hkv, G, nseq, seqlen_uniform, causal, ntile;
+};
+
+__device__ inline void seq_bounds(const BwdParams &p, int s, int &s0, int &s1)
+{
+    if (p.cu) {
+        s0 = p.cu[s];
+        s1 = p.cu[s + 1];
+    } else {
+        s0 = s * p.seqlen_uniform;
+        s1 = s0 + p.seqlen_uniform;
+    }
+}
+
+__device__ inline float head_lambda(const BwdParams &p, int h, int lane, int D)
+{
+    const int64_t lo = (int64_t)h * p.lstride;
+    float a = 0.f, b = 0.f;
+    for (int cc = lane; cc < D; cc += 64) {
+        a += p.lq1[lo + cc] * p.lk1[lo + cc];
+        b += p.lq2[lo + cc] * p.lk2[lo + cc];
+    }
+    return expf(wave_sum(a)) - expf(wave_sum(b)) + p.lambda_init;
+}
+
+// ---------------------------------------------------------------------------
+// prep: RMSNorm / combine backward per row, D_m, partial weight and lambda
+// gradients.  Wave w serves head w % H and tokens w / H, w / H + nper, ...
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep(BwdParams p)
+{
+    constexpr int CPL = 2 * D / 64;   // columns per lane
+    const int lane = threadIdx.x & 63;
+    const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (wid >= p.H * kPrepPerHead)
+        return;
+    const int h = wid % p.H;
+    const float lam = head_lambda(p, h, lane, D);
+    const float sc = 1.f - p.lambda_init;
+    float wv[CPL], dwp[CPL];
+#pragma unroll
+    for (int cc = 0; cc < CPL; ++cc) {
+        wv[cc] = p.w ? p.w[CPL * lane + cc] : 1.f;
+        dwp[cc] = 0.f;
+    }
+    float dlp = 0.f;
+    for (int t = wid / p.H; t < p.T; t += kPrepPerHead) {
+        const int64_t row = (int64_t)t * p.H + h;
+        const float *o1 = p.o12 + row * 2 * (2 * D) + CPL * lane;
+        const float *o2 = o1 + 2 * D;
+        const bf16 *dyr = p.dy + row * (2 * D) + CPL * lane;
+        float pre[CPL], g[CPL], a1[CPL], a2[CPL];
+        float ss = 0.f, gp = 0.f;
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) {
+            a1[cc] = o1[cc];
+            a2[cc] = o2[cc];
+            pre[cc] = a1[cc] - lam * a2[cc];
+            ss += pre[cc] * pre[cc];
+            g[cc] = (float)dyr[cc] * wv[cc] * sc;
+            gp += g[cc] * pre[cc];
+        }
+        ss = wave_sum(ss);
+        gp = wave_sum(gp);
+        const float r = rsqrtf(ss / (float)(2 * D) + p.eps);
+        const float r3 = r * r * r * gp / (float)(2 * D);
+        float d1 = 0.f, d2 = 0.f;
+        bf16 *do1 = p.do12 + row * 2 * (2 * D) + CPL * lane;
+        bf16 *do2 = do1 + 2 * D;
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) {
+            const float dpre = r * g[cc] - r3 * pre[cc];
+            const bf16 b1 = (bf16)dpre, b2 = (bf16)(-lam * dpre);
+            do1[cc] = b1;
+            do2[cc] = b2;
+            d1 += (float)b1 * a1[cc];
+            d2 += (float)b2 * a2[cc];
+            dlp -= dpre * a2[cc];
+            dwp[cc] += (float)dyr[cc] * pre[cc] * r * sc;
+        }
+        d1 = wave_sum(d1);
+        d2 = wave_sum(d2);
+        if (lane == 0) {
+            p.dd[row * 2] = d1;
+            p.dd[row * 2 + 1] = d2;
+        }
+    }
+#pragma unroll
+    for (int cc = 0; cc < CPL; ++cc)
+        p.part_dw[(int64_t)wid * 2 * D + CPL * lane + cc] = dwp[cc];
+    dlp = wave_sum(dlp);
+    if (lane == 0)
+        p.part_dl[wid] = dlp;
+}
+
+// ---------------------------------------------------------------------------
+// reduce: fixed-order sums of the partials, lambda-vector gradients.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_reduce(BwdParams p)
+{
+    __shared__ float dlh[256];   // per head (H <= 256)
+    const int tid = threadIdx.x;
+    const int nprep = p.H * kPrepPerHead;
+    if (p.dw) {
+        for (int c = tid; c < 2 * D; c += 256) {
+            float acc = 0.f;
+            for (int w = 0; w < nprep; ++w)
+                acc += p.part_dw[(int64_t)w * 2 * D + c];
+            p.dw[c] = acc;
+        }
+    }
+    for (int h = tid; h < p.H; h += 256) {
+        float acc = 0.f;
+        for (int k = 0; k < kPrepPerHead; ++k)
+            acc += p.part_dl[k * p.H + h];
+        dlh[h] = acc;
+    }
+    __syncthreads();
+    const int nsets = p.lstride ? p.H : 1;
+    for (int idx = tid; idx < nsets * D; idx += 256) {
+        const int st = idx / D, c = idx % D;
+        float dlam = 0.f;
+        if (p.lstride) {
+            dlam = dlh[st];
+        } else {
+            for (int h = 0; h < p.H; ++h)
+                dlam += dlh[h];
+        }
+        const int64_t off = (int64_t)st * p.lstride;
+        float a = 0.f, b = 0.f;
+        for (int j = 0; j < D; ++j) {
+            a += p.lq1[off + j] * p.lk1[off + j];
+            b += p.lq2[off + j] * p.lk2[off + j];
+        }
+        const float ea = expf(a), eb = expf(b);
+        p.dlq1[off + c] = dlam * ea * p.lk1[off + c];
+        p.dlk1[off + c] = dlam * ea * p.lq1[off + c];
+        p.dlq2[off + c] = -dlam * eb * p.lk2[off + c];
+        p.dlk2[off + c] = -dlam * eb * p.lq2[off + c];
+    }
+}
+
+// Cooperative copy of `rows` rows of `rowbytes` bytes (rows past `valid` are
+// zero) from global rows `stride` bytes apart into an LDS tile with rows
+// `ldsrow` bytes apart, in 16-byte pieces.
+__device__ inline void stage_rows(char *lds, int ldsrow, const char *src, int64_t stride,
+                                  int rowbytes, int rows, int valid)
+{
+    const int cpr = rowbytes / 16;
+    for (int i = threadIdx.x; i < rows * cpr; i += kThreads) {
+        const int r = i / cpr, c = (i % cpr) * 16;
+        u32x4 x = u32x4{0u, 0u, 0u, 0u};
+        if (r < valid)
+            x = *(const u32x4 *)(src + r * stride + c);
+        *(u32x4 *)(lds + r * ldsrow + c) = x;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dq: query-outer.
+template <int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq(BwdParams p)
+{
+    constexpr int ROWB = 2 * D * 2;        // K or V row bytes
+    constexpr int LROW = ROWB + 16;        // padded LDS row
+    constexpr int NKS = D / 16;            // QK contraction steps
+    constexpr int NVS = 2 * D / 16;        // dO V contraction steps
+    constexpr int NDB = D / 32;            // 32-dim blocks of dQ
+    __shared__ __attribute__((aligned(16))) char kt[kInner * LROW];
+    __shared__ __attribute__((aligned(16))) char vt[kInner * LROW];
+
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int n = lane & 31, h = lane >> 5;
+    const int map = wave >> 2, sub = wave & 3;
+
+    // longest query tiles first
+    const int pairs = p.nseq * p.H;
+    const int tile = p.ntile - 1 - blockIdx.x / pairs;
+    const int rem = blockIdx.x % pairs;
+    const int s = rem / p.H, head = rem % p.H;
+    const int g = head / p.G;
+    int s0, s1;
+    seq_bounds(p, s, s0, s1);
+    const int q0 = s0 + tile * kTile;
+    if (q0 >= s1)
+        return;
+    const int wq = q0 + 32 * sub + n;      // this lane's query
+    const bool qok = wq < s1;
+    const int64_t qrow = (int64_t)wq * p.H + head;
+
+    bf16x8 qf[NKS], df[NVS];
+    float lse = INFINITY, dval = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+        qf[ks] = qok ? *(const bf16x8 *)(p.q + (qrow * 2 + map) * D + 16 * ks + 8 * h) : bf16x8{};
+#pragma unroll
+    for (int ks = 0; ks < NVS; ++ks)
+        df[ks] = qok ? *(const bf16x8 *)(p.do12 + (qrow * 2 + map) * (2 * D) + 16 * ks + 8 * h)
+                     : bf16x8{};
+    if (qok) {
+        lse = p.lse[qrow * 2 + map];
+        dval = p.dd[qrow * 2 + map];
+    }
+    f32x16 dqa[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+        dqa[db] = f32x16{};
+    const float c = kLog2e * rsqrtf((float)D);
+    const TrOperand tr(lane, LROW);
+    const int qhi = min(s1, q0 + kTile);
+    const int kend = p.causal ? qhi : s1;
+    const int64_t kstride = (int64_t)p.Hkv * ROWB;
+
+    for (int k0 = s0; k0 < kend; k0 += kInner) {
+        __syncthreads();
+        stage_rows(kt, LROW, (const char *)p.k + (int64_t)k0 * kstride + (int64_t)g * ROWB,
+                   kstride, ROWB, kInner, min(kInner, s1 - k0));
+        stage_rows(vt, LROW, (const char *)p.v + (int64_t)k0 * kstride + (int64_t)g * ROWB,
+                   kstride, ROWB, kInner, min(kInner, s1 - k0));
+        __syncthreads();
+#pragma unroll
+        for (int b = 0; b < kInner / 32; ++b) {
+            const int kb0 = k0 + 32 * b;
+            // wave-uniform: keys of the block this wave's queries can see
+            if (kb0 >= s1 || (p.causal && kb0 > q0 + 32 * sub + 31))
+                continue;
+            // S^T = K Q^T (keys x queries)
+            f32x16 st = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const bf16x8 ka = *(const bf16x8 *)(kt + (32 * b + n) * LROW +
+                                                    (map * D + 16 * ks + 8 * h) * 2);
+                st = mma(ka, qf[ks], st);
+            }
+            // dP^T = V dO^T
+            f32x16 dp = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < NVS; ++ks) {
+                const bf16x8 va = *(const bf16x8 *)(vt + (32 * b + n) * LROW + (16 * ks + 8 * h) * 2);
+                dp = mma(va, df[ks], dp);
+            }
+            // P^T and dS^T; lane owns query wq, element a is key kb0 + acc_row(a, h)
+#pragma unroll
+            for (int a = 0; a < 16; ++a) {
+                const int key = kb0 + acc_row(a, h);
+                const bool vis = key < s1 && (!p.causal || key <= wq);
+                const float pv = vis ? exp2f(st[a] * c - lse) : 0.f;
+                st[a] = pv * (dp[a] - dval);
+            }
+            // dQ^T += K^T dS^T
+#pragma unroll
+            for (int ps = 0; ps < 2; ++ps) {
+                const bf16x8 bs = pack8(st, 8 * ps);
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    dqa[db] = mma(tr.load(kt, LROW, 32 * b + 16 * ps, (map * D + 32 * db) * 2),
+                                  bs, dqa[db]);
+            }
+        }
+    }
+    if (!qok)
+        return;
+    const float scale = rsqrtf((float)D);
+    bf16 *dst = p.dq + (qrow * 2 + map) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            bf16 vals[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                vals[e] = (bf16)(dqa[db][4 * i + e] * scale);
+            __builtin_memcpy(dst + 32 * db + 8 * i + 4 * h, vals, sizeof(vals));
+        }
+}
+
+// ---------------------------------------------------------------------------
+// dkdv: key-outer.
+template <int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dkdv(BwdParams p)
+{
+    constexpr int ROWB = 2 * D * 2;          // K, V or Q row bytes (both maps of q)
+    constexpr int QROW = ROWB + 16;
+    constexpr int DROWB = 4 * D * 2;         // dO row bytes (both maps)
+    constexpr int DROW = DROWB + 16;
+    constexpr int NKS = D / 16;
+    constexpr int NVS = 2 * D / 16;
+    constexpr int NKB = D / 32;              // 32-dim blocks of dK
+    constexpr int NVB = 2 * D / 32;          // 32-dim blocks of dV
+    // Q and dO tiles during the loop; the dV exchange of the epilogue after it
+    constexpr int QT_BYTES = kInner * QROW;
+    constexpr int DT_BYTES = kInner * DROW;
+    constexpr int XCH_BYTES = 4 * NVB * 16 * 64 * 4;
+    constexpr int SMEM = QT_BYTES + DT_BYTES > XCH_BYTES ? QT_BYTES + DT_BYTES : XCH_BYTES;
+    __shared__ __attribute__((aligned(16))) char smem[SMEM];
+    __shared__ float lt[kInner * 2], ddt[kInner * 2];
+    char *qt = smem;
+    char *dt = smem + QT_BYTES;
+
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int n = lane & 31, h = lane >> 5;
+    const int map = wave >> 2, sub = wave & 3;
+
+    const int pairs = p.nseq * p.Hkv;
+    const int tile = blockIdx.x / pairs;
+    const int rem = blockIdx.x % pairs;
+    const int s = rem / p.Hkv, g = rem % p.Hkv;
+    int s0, s1;
+    seq_bounds(p, s, s0, s1);
+    const int k0 = s0 + tile * kTile;
+    if (k0 >= s1)
+        return;
+    const int wk = k0 + 32 * sub + n;   // this lane's key
+    const int wkc = min(wk, s1 - 1);
+
+    bf16x8 kf[NKS], vf[NVS];
+    {
+        const bf16 *kr = p.k + ((int64_t)wkc * p.Hkv + g) * (2 * D) + map * D;
+        const bf16 *vr = p.v + ((int64_t)wkc * p.Hkv + g) * (2 * D);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+            kf[ks] = *(const bf16x8 *)(kr + 16 * ks + 8 * h);
+#pragma unroll
+        for (int ks = 0; ks < NVS; ++ks)
+            vf[ks] = *(const bf16x8 *)(vr + 16 * ks + 8 * h);
+    }
+    f32x16 dka[NKB], dva[NVB];
+#pragma unroll
+    for (int db = 0; db < NKB; ++db)
+        dka[db] = f32x16{};
+#pragma unroll
+    for (int db = 0; db < NVB; ++db)
+        dva[db] = f32x16{};
+    const float c = kLog2e * rsqrtf((float)D);
+    const TrOperand trq(lane, QROW), trd(lane, DROW);
+    const int wk_first = k0 + 32 * sub;   // first key of this wave
+    // queries before the tile's first key cannot see any of its keys
+    const int qstart = p.causal ? s0 + ((k0 - s0) / kInner) * kInner : s0;
+
+    for (int hh = 0; hh < p.G; ++hh) {
+        const int head = g * p.G + hh;
+        for (int q0 = qstart; q0 < s1; q0 += kInner) {
+            __syncthreads();
+            const int valid = min(kInner, s1 - q0);
+            const int64_t qrow0 = (int64_t)q0 * p.H + head;
+            stage_rows(qt, QROW, (const char *)(p.q + qrow0 * 2 * D), (int64_t)p.H * ROWB, ROWB,
+                       kInner, valid);
+            stage_rows(dt, DROW, (const char *)(p.do12 + qrow0 * 4 * D), (int64_t)p.H * DROWB,
+                       DROWB, kInner, valid);
+            for (int i = threadIdx.x; i < kInner * 2; i += kThreads) {
+                const int r = i >> 1;
+                lt[i] = r < valid ? p.lse[(qrow0 + (int64_t)r * p.H) * 2 + (i & 1)] : INFINITY;
+                ddt[i] = r < valid ? p.dd[(qrow0 + (int64_t)r * p.H) * 2 + (i & 1)] : 0.f;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int b = 0; b < kInner / 32; ++b) {
+                const int qb0 = q0 + 32 * b;
+                // wave-uniform: can any query of the block see a key of the wave?
+                if (qb0 >= s1 || (p.causal && qb0 + 31 < wk_first))
+                    continue;
+                // S = Q K^T (queries x keys); lane owns key wk
+                f32x16 st = f32x16{};
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const bf16x8 qa = *(const bf16x8 *)(qt + (32 * b + n) * QROW +
+                                                        (map * D + 16 * ks + 8 * h) * 2);
+                    st = mma(qa, kf[ks], st);
+                }
+                // dP = dO V^T
+                f32x16 dp = f32x16{};
+#pragma unroll
+                for (int ks = 0; ks < NVS; ++ks) {
+                    const bf16x8 da = *(const bf16x8 *)(dt + (32 * b + n) * DROW +
+                                                        (map * 2 * D + 16 * ks + 8 * h) * 2);
+                    dp = mma(da, vf[ks], dp);
+                }
+                bf16x8 bpk[2];   // P as the B operand of dV^T, packed at once
+#pragma unroll
+                for (int a = 0; a < 16; ++a) {
+                    const int qi = 32 * b + acc_row(a, h);          // row in the tile
+                    const bool vis = !p.causal || wk <= q0 + qi;
+                    const float pv = vis ? exp2f(st[a] * c - lt[qi * 2 + map]) : 0.f;
+                    bpk[a / 8][a % 8] = (bf16)pv;
+                    st[a] = pv * (dp[a] - ddt[qi * 2 + map]);
+                }
+                // dV^T += dO^T P, dK^T += Q^T dS
+#pragma unroll
+                for (int ps = 0; ps < 2; ++ps) {
+                    const bf16x8 bp = bpk[ps];
+                    const bf16x8 bs = pack8(st, 8 * ps);
+#pragma unroll
+                    for (int db = 0; db < NVB; ++db)
+                        dva[db] = mma(trd.load(dt, DROW, 32 * b + 16 * ps,
+                                               (map * 2 * D + 32 * db) * 2),
+                                      bp, dva[db]);
+#pragma unroll
+                    for (int db = 0; db < NKB; ++db)
+                        dka[db] = mma(trq.load(qt, QROW, 32 * b + 16 * ps, (map * D + 32 * db) * 2),
+                                      bs, dka[db]);
+                }
+            }
+        }
+    }
+
+    // dK of this map; dV summed over the two maps through LDS
+    const float scale = rsqrtf((float)D);
+    const bool kok = wk < s1;
+    if (kok) {
+        bf16 *dst = p.dk + (((int64_t)wk * p.Hkv + g) * 2 + map) * D;
+#pragma unroll
+        for (int db = 0; db < NKB; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                bf16 vals[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    vals[e] = (bf16)(dka[db][4 * i + e] * scale);
+                __builtin_memcpy(dst + 32 * db + 8 * i + 4 * h, vals, sizeof(vals));
+            }
+    }
+    __syncthreads();
+    // map-2 waves publish dV^T (fp32) in their accumulator layout; the map-1
+    // wave of the same keys adds it and stores
+    float *xch = (float *)smem;
+    if (map == 1) {
+#pragma unroll
+        for (int db = 0; db < NVB; ++db)
+#pragma unroll
+            for (int a = 0; a < 16; ++a)
+                xch[((sub * NVB + db) * 16 + a) * 64 + lane] = dva[db][a];
+    }
+    __syncthreads();
+    if (map == 1 || !kok)
+        return;
+    bf16 *dst = p.dv + ((int64_t)wk * p.Hkv + g) * (2 * D);
+#pragma unroll
+    for (int db = 0; db < NVB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            bf16 vals[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                vals[e] = (bf16)(dva[db][4 * i + e] +
+                                 xch[((sub * NVB + db) * 16 + 4 * i + e) * 64 + lane]);
+            __builtin_memcpy(dst + 32 * db + 8 * i + 4 * h, vals, sizeof(vals));
+        }
+}
+
+struct BwdPlan {
+    size_t do12, dd, part_dw, part_dl, total;
+};
+
+BwdPlan bwd_plan(int64_t T, int H, int d)
+{
+    BwdPlan pl;
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    pl.do12 = up((size_t)T * H * 2 * (2 * d) * 2);
+    pl.dd = up((size_t)T * H * 2 * 4);
+    pl.part_dw = up((size_t)H * kPrepPerHead * 2 * d * 4);
+    pl.part_dl = up((size_t)H * kPrepPerHead * 4);
+    pl.total = pl.do12 + pl.dd + pl.part_dw + pl.part_dl;
+    return pl;
+}
+
+template <int D>
+void launch_bwd(const BwdParams &p, int nseq, int Hkv, hipStream_t st)
+{
+    const int nprep = p.H * kPrepPerHead;
+    hipLaunchKernelGGL(bwd_prep<D>, dim3((nprep + 3) / 4), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(bwd_reduce<D>, dim3(1), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(bwd_dq<D>, dim3(p.ntile * nseq * p.H), dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL(bwd_dkdv<D>, dim3(p.ntile * nseq * Hkv), dim3(kThreads), 0, st, p);
+}
+
+bool a16(const void *x) { return ((uintptr_t)x & 15u) == 0; }
+
+} // namespace
+
+extern "C" int diffattn_supported_bwd(int dtype, int d)
+{
+    return dtype == DIFFATTN_BF16 && (d == 32 || d == 64);
+}
+
+extern "C" size_t diffattn_bwd_workspace_size(int32_t T, int32_t H, int32_t d)
+{
+    if (T < 0 || H < 1 || d < 1)
+        return 0;
+    return bwd_plan(T, H, d).total;
+}
+
+extern "C" int diffattn_bwd(int dtype, const void *q, const void *k, const void *v,
+                            const float *lambda_q1, const float *lambda_k1,
+                            const float *lambda_q2, const float *lambda_k2,
+                            int32_t lambda_stride, float lambda_init,
+                            const float *subln_weight, float eps, int causal,
+                            const int32_t *cu_seqlens, int32_t nseq, int32_t max_seqlen,
+                            int32_t T, int32_t H, int32_t Hkv, int32_t d, const void *dout,
+                            const float *lse, const float *o12, void *dq, void *dk, void *dv,
+                            float *dlambda_q1, float *dlambda_k1, float *dlambda_q2,
+                            float *dlambda_k2, float *dsubln_weight, void *workspace,
+                            size_t workspace_bytes, void *stream)
+{
+    if (dtype != DIFFATTN_BF16 && dtype != DIFFATTN_F32)
+        return DIFFATTN_EINVAL;
+    if (T < 0 || H < 1 || Hkv < 1 || H % Hkv != 0 || d < 1 || nseq < 1 || H > 256)
+        return DIFFATTN_EINVAL;
+    if (causal != 0 && causal != 1)
+        return DIFFATTN_EINVAL;
+    if (!(eps >= 0.f) || !isfinite(eps) || !isfinite(lambda_init))
+        return DIFFATTN_EINVAL;
+    if (lambda_stride != 0 && lambda_stride < d)
+        return DIFFATTN_EINVAL;
+    if (!diffattn_supported_bwd(dtype, d))
+        return DIFFATTN_EUNSUPPORTED;
+    if (!lambda_q1 || !lambda_k1 || !lambda_q2 || !lambda_k2 || !dlambda_q1 || !dlambda_k1 ||
+        !dlambda_q2 || !dlambda_k2)
+        return DIFFATTN_EINVAL;
+    int32_t uniform = 0;
+    if (!cu_seqlens) {
+        if (T % nseq != 0)
+            return DIFFATTN_EINVAL;
+        uniform = T / nseq;
+        max_seqlen = uniform;
+    } else if (max_seqlen < 0 || max_seqlen > T) {
+        return DIFFATTN_EINVAL;
+    }
+    const BwdPlan pl = bwd_plan(T, H, d);
+    if (T > 0) {
+        if (!q || !k || !v || !dout || !lse || !o12 || !dq || !dk || !dv || !workspace)
+            return DIFFATTN_EINVAL;
+        if (!a16(q) || !a16(k) || !a16(v) || !a16(dout) || !a16(o12) || !a16(dq) || !a16(dk) ||
+            !a16(dv) || !a16(workspace) || (subln_weight && !a16(subln_weight)))
+            return DIFFATTN_EINVAL;
+        if (workspace_bytes < pl.total)
+            return DIFFATTN_EINVAL;
+        if (max_seqlen < 1)
+            return DIFFATTN_EINVAL;
+    }
+    BwdParams p;
+    p.q = (const bf16 *)q;
+    p.k = (const bf16 *)k;
+    p.v = (const bf16 *)v;
+    p.dy = (const bf16 *)dout;
+    p.lse = lse;
+    p.o12 = o12;
+    p.lq1 = lambda_q1;
+    p.lk1 = lambda_k1;
+    p.lq2 = lambda_q2;
+    p.lk2 = lambda_k2;
+    p.lstride = lambda_stride;
+    p.w = subln_weight;
+    p.cu = cu_seqlens;
+    p.dq = (bf16 *)dq;
+    p.dk = (bf16 *)dk;
+    p.dv = (bf16 *)dv;
+    p.dlq1 = dlambda_q1;
+    p.dlk1 = dlambda_k1;
+    p.dlq2 = dlambda_q2;
+    p.dlk2 = dlambda_k2;
+    p.dw = dsubln_weight;
+    char *ws = (char *)workspace;
+    p.do12 = (bf16 *)ws;
+    p.dd = (float *)(ws + pl.do12);
+    p.part_dw = (float *)(ws + pl.do12 + pl.dd);
+    p.part_dl = (float *)(ws + pl.do12 + pl.dd + pl.part_dw);
+    p.lambda_init = lambda_init;
+    p.eps = eps;
+    p.T = T;
+    p.H = H;
+    p.Hkv = Hkv;
+    p.G = H / Hkv;
+    p.nseq = nseq;
+    p.seqlen_uniform = uniform;
+    p.causal = causal;
+    p.ntile = T > 0 ? (max_seqlen + kTile - 1) / kTile : 0;
+    const int64_t blocks = (int64_t)p.ntile * nseq * H;
+    if (blocks > INT32_MAX)
+        return DIFFATTN_EINVAL;
+    hipStream_t st = (hipStream_t)stream;
+    if (T == 0)
+        return DIFFATTN_OK;   // no rows: nothing is launched or written
+    if (d == 64)
+        launch_bwd<64>(p, nseq, Hkv, st);
+    else
+        launch_bwd<32>(p, nseq, Hkv, st);
+    return hipGetLastError() == hipSuccess ? DIFFATTN_OK : DIFFATTN_EHIP;
+}

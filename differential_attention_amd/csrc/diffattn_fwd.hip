@@ -279,6 +279,8 @@ struct Params {
     const float *w;
     const int32_t *cu;
     const float *rcos, *rsin;   // rotary tables [len][d/2], or NULL
+    float *lse;                 // training forward: [T][H][2] log2-sum-exp, or NULL
+    float *o12;                 // training forward: [T][H][2][2d] normalised O_m
     float lambda_init;
     float eps;
     int32_t T, H, Hkv, nseq, seqlen_uniform;
@@ -582,6 +584,28 @@ void diffattn_fwd_kernel(Params p)
 #pragma unroll
     for (int u = 0; u < kSub; ++u)
         lsum[u] = pair_sum(l_run[u]);
+    if (p.lse) {
+        // training forward: each map's log2-sum-exp of the scaled scores and
+        // its normalised output, for the backward pass
+#pragma unroll
+        for (int u = 0; u < kSub; ++u) {
+            const int tq = wq0 + 32 * u + n;
+            if (tq >= s1)
+                continue;
+            const int64_t row = (int64_t)tq * p.H + head;
+            if (h == 0)
+                p.lse[row * 2 + map] = m_run[u] * c + log2f(lsum[u]);
+            float *dst = p.o12 + (row * 2 + map) * (2 * D);
+            const float il = 1.f / lsum[u];
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    *(float4 *)(dst + 32 * db + 8 * i + 4 * h) =
+                        make_float4(o[u][db][4 * i] * il, o[u][db][4 * i + 1] * il,
+                                    o[u][db][4 * i + 2] * il, o[u][db][4 * i + 3] * il);
+        }
+    }
     if (map == 1) {
         float a = 0.f, b = 0.f;
         const int64_t lo = head * p.lstride;   // this head's lambda vectors
@@ -723,15 +747,19 @@ int diffattn_check_cu_seqlens(const int32_t *host_cu, int32_t nseq, int32_t T,
     return DIFFATTN_OK;
 }
 
-int diffattn_fwd(int dtype, const void *q, const void *k, const void *v,
-                 const float *lambda_q1, const float *lambda_k1,
-                 const float *lambda_q2, const float *lambda_k2,
-                 int32_t lambda_stride, float lambda_init,
-                 const float *subln_weight, float eps,
-                 int causal, const int32_t *cu_seqlens, int32_t nseq,
-                 int32_t max_seqlen, int32_t T, int32_t H, int32_t Hkv,
-                 int32_t d, const float *rope_cos, const float *rope_sin,
-                 int32_t rope_len, void *out, void *stream)
+} // extern "C"
+
+namespace {
+
+int fwd_impl(int dtype, const void *q, const void *k, const void *v,
+             const float *lambda_q1, const float *lambda_k1,
+             const float *lambda_q2, const float *lambda_k2,
+             int32_t lambda_stride, float lambda_init,
+             const float *subln_weight, float eps,
+             int causal, const int32_t *cu_seqlens, int32_t nseq,
+             int32_t max_seqlen, int32_t T, int32_t H, int32_t Hkv,
+             int32_t d, const float *rope_cos, const float *rope_sin,
+             int32_t rope_len, float *lse, float *o12, void *out, void *stream)
 {
     if (dtype != DIFFATTN_BF16 && dtype != DIFFATTN_F32)
         return DIFFATTN_EINVAL;
@@ -797,6 +825,8 @@ int diffattn_fwd(int dtype, const void *q, const void *k, const void *v,
     p.cu = cu_seqlens;
     p.rcos = rope_cos;
     p.rsin = rope_sin;
+    p.lse = lse;
+    p.o12 = o12;
     p.lambda_init = lambda_init;
     p.eps = eps;
     p.T = T;
@@ -813,6 +843,43 @@ int diffattn_fwd(int dtype, const void *q, const void *k, const void *v,
     if (hipGetDevice(&dev) != hipSuccess)
         return DIFFATTN_EHIP;
     return fn(p, (int)nblocks, (hipStream_t)stream);
+}
+
+} // namespace
+
+extern "C" {
+
+int diffattn_fwd(int dtype, const void *q, const void *k, const void *v,
+                 const float *lambda_q1, const float *lambda_k1,
+                 const float *lambda_q2, const float *lambda_k2,
+                 int32_t lambda_stride, float lambda_init,
+                 const float *subln_weight, float eps,
+                 int causal, const int32_t *cu_seqlens, int32_t nseq,
+                 int32_t max_seqlen, int32_t T, int32_t H, int32_t Hkv,
+                 int32_t d, const float *rope_cos, const float *rope_sin,
+                 int32_t rope_len, void *out, void *stream)
+{
+    return fwd_impl(dtype, q, k, v, lambda_q1, lambda_k1, lambda_q2, lambda_k2,
+                    lambda_stride, lambda_init, subln_weight, eps, causal, cu_seqlens,
+                    nseq, max_seqlen, T, H, Hkv, d, rope_cos, rope_sin, rope_len,
+                    nullptr, nullptr, out, stream);
+}
+
+int diffattn_fwd_train(int dtype, const void *q, const void *k, const void *v,
+                       const float *lambda_q1, const float *lambda_k1,
+                       const float *lambda_q2, const float *lambda_k2,
+                       int32_t lambda_stride, float lambda_init,
+                       const float *subln_weight, float eps, int causal,
+                       const int32_t *cu_seqlens, int32_t nseq, int32_t max_seqlen,
+                       int32_t T, int32_t H, int32_t Hkv, int32_t d, void *out,
+                       float *lse, float *o12, void *stream)
+{
+    if (T > 0 && (!lse || !o12 || ((uintptr_t)o12 % 16) != 0 || ((uintptr_t)lse % 4) != 0))
+        return DIFFATTN_EINVAL;
+    return fwd_impl(dtype, q, k, v, lambda_q1, lambda_k1, lambda_q2, lambda_k2,
+                    lambda_stride, lambda_init, subln_weight, eps, causal, cu_seqlens,
+                    nseq, max_seqlen, T, H, Hkv, d, nullptr, nullptr, 0, lse, o12, out,
+                    stream);
 }
 
 } // extern "C"

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define DIFFATTN_ABI_VERSION 4
+#define DIFFATTN_ABI_VERSION 5
 
 enum diffattn_status {
     DIFFATTN_OK = 0,
@@ -190,6 +190,87 @@ int diffattn_check_cu_seqlens_kv(const int32_t *host_cu_q,
                                  const int32_t *host_cu_k, int32_t nseq,
                                  int32_t Tq, int32_t Tk, int32_t max_seqlen_q,
                                  int32_t max_seqlen_k, int causal);
+
+/*
+ * Training forward: diffattn_fwd (without the rotary prologue) that also
+ * saves what diffattn_bwd needs.  Extra outputs, device fp32, written for
+ * every row:
+ *   lse  [T, H, 2]      per map m, log2 of the sum over the row's visible
+ *                       keys of 2^(<Qm, Km[j]> log2(e) / sqrt(d)) (4-byte
+ *                       aligned);
+ *   o12  [T, H, 2, 2d]  the normalised outputs O_1 and O_2 of the two maps
+ *                       (16-byte aligned).  They are kept in fp32 because the
+ *                       backward forms O_1 - lambda O_2, which can cancel.
+ * Other arguments, return values and errors as for diffattn_fwd.
+ */
+int diffattn_fwd_train(int dtype, const void *q, const void *k, const void *v,
+                       const float *lambda_q1, const float *lambda_k1,
+                       const float *lambda_q2, const float *lambda_k2,
+                       int32_t lambda_stride, float lambda_init,
+                       const float *subln_weight, float eps, int causal,
+                       const int32_t *cu_seqlens, int32_t nseq,
+                       int32_t max_seqlen, int32_t T, int32_t H, int32_t Hkv,
+                       int32_t d, void *out, float *lse, float *o12,
+                       void *stream);
+
+/*
+ * Backward pass of the prefill (inputs already rotated), asynchronous on
+ * `stream`: the gradients of sum(dout * out) for the output `out` of
+ * diffattn_fwd_train with the same arguments.  The chain (DiffTransformer
+ * page, MultiHeadDifferentialAttention.forward, differentiated), per row
+ * (token i, head h) with g = dout * w * (1 - lambda_init) and
+ * r = 1 / sqrt(mean(pre^2) + eps):
+ *   dpre  = r g - r^3 pre <g, pre> / (2d)
+ *   dO_1  = dpre,  dO_2 = -lambda_h dpre,  dlambda_h += -<dpre, O_2>
+ *   per map m: dS_m = P_m (dO_m V^T - <dO_m, O_m>)
+ *              dQ_m = dS_m K_m / sqrt(d),  dK_m = dS_m^T Q_m / sqrt(d)
+ *   dV    = P_1^T dO_1 + P_2^T dO_2
+ *   dw    = sum over rows of dout * pre * r * (1 - lambda_init)
+ *   lambda = exp(a) - exp(b) + lambda_init, a = <lq1, lk1>, b = <lq2, lk2>:
+ *   dlq1 = dlambda e^a lk1, dlk1 = dlambda e^a lq1,
+ *   dlq2 = -dlambda e^b lk2, dlk2 = -dlambda e^b lq2
+ * (dlambda summed over all heads when the vectors are shared).
+ *
+ *   dtype        DIFFATTN_BF16 (see diffattn_supported_bwd).
+ *   q .. max_seqlen, T, H, Hkv, d
+ *                exactly as given to diffattn_fwd_train (H <= 256).
+ *   dout         device [T, H, 2d], storage type.
+ *   lse, o12     device, as written by diffattn_fwd_train.
+ *   dq, dk, dv   device outputs in the layouts and storage type of q, k, v
+ *                (overwritten, not accumulated).
+ *   dlambda_q1 .. dlambda_k2
+ *                device fp32 outputs laid out like the lambda vectors
+ *                (d elements, or H sets lambda_stride apart).
+ *   dsubln_weight device fp32 [2d] output, or NULL to skip it.
+ *   workspace    device scratch of diffattn_bwd_workspace_size(T, H, d)
+ *                bytes, 16-byte aligned, owned by the caller; no
+ *                initialisation needed; calls in flight at once need
+ *                separate workspaces.
+ * Every output is a pure function of the inputs: there are no atomics, and
+ * repeated calls give bitwise equal results.  Returns DIFFATTN_OK (T == 0
+ * launches nothing and writes nothing), DIFFATTN_EINVAL,
+ * DIFFATTN_EUNSUPPORTED or DIFFATTN_EHIP.
+ */
+int diffattn_bwd(int dtype, const void *q, const void *k, const void *v,
+                 const float *lambda_q1, const float *lambda_k1,
+                 const float *lambda_q2, const float *lambda_k2,
+                 int32_t lambda_stride, float lambda_init,
+                 const float *subln_weight, float eps, int causal,
+                 const int32_t *cu_seqlens, int32_t nseq, int32_t max_seqlen,
+                 int32_t T, int32_t H, int32_t Hkv, int32_t d,
+                 const void *dout, const float *lse, const float *o12,
+                 void *dq, void *dk, void *dv, float *dlambda_q1,
+                 float *dlambda_k1, float *dlambda_q2, float *dlambda_k2,
+                 float *dsubln_weight, void *workspace, size_t workspace_bytes,
+                 void *stream);
+
+/* Bytes of workspace diffattn_bwd needs; 0 for sizes it rejects.  Host
+ * function. */
+size_t diffattn_bwd_workspace_size(int32_t T, int32_t H, int32_t d);
+
+/* 1 if the backward kernels are compiled for (dtype, d), else 0.  Host
+ * function. */
+int diffattn_supported_bwd(int dtype, int d);
 
 /* Initial lambda of a layer at 1-based depth: 0.8 - 0.6 * exp(-0.3 *
  * (depth - 1)), the decaying schedule with which DiffTransformer.__init__

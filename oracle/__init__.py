@@ -72,7 +72,7 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
         [f32p] * 7 + [ctypes.c_int64, ctypes.c_double, f32p, ctypes.c_double,
                       ctypes.c_int, i32p, ctypes.c_int, ctypes.c_int64,
                       ctypes.c_int, ctypes.c_int, ctypes.c_int, f32p]
-        + [f64p] * 8 + [ctypes.c_int])
+        + [f64p] * 10 + [ctypes.c_int])
     lib.diffattn_ref_bwd.restype = ctypes.c_int
     lib.diffattn_ref_max_threads.argtypes = []
     lib.diffattn_ref_max_threads.restype = ctypes.c_int
@@ -248,7 +248,10 @@ def bwd(q, k, v, lq1, lk1, lq2, lk2, lambda_init_value: float, dy, w=None,
         nthreads: int = 0, lib: Optional[ctypes.CDLL] = None) -> dict:
     """Gradients of <dy, fwd(...)> in fp64: ``dq``, ``dk``, ``dv`` in the
     input layouts, ``dlq1``.. ``dlk2`` shaped like the lambda vectors and
-    ``dw`` [2d] (the RMSNorm weight; of ones when ``w`` is None)."""
+    ``dw`` [2d] (the RMSNorm weight; of ones when ``w`` is None); plus, under
+    ``aux``, ``dlam_head`` [H] (dlambda per head) and ``dlam_scale`` [H]
+    (sum over the head's rows of |dpre| |O_2|, the size a relative error in
+    those factors can move dlambda by)."""
     keep, args, (T, H, d) = _common(q, k, v, lq1, lk1, lq2, lk2,
                                     lambda_init_value, w, eps, causal,
                                     cu_seqlens)
@@ -260,14 +263,18 @@ def bwd(q, k, v, lq1, lk1, lq2, lk2, lambda_init_value: float, dy, w=None,
            "dv": np.empty((T, Hkv, 2 * d)), "dlq1": np.zeros(lshape),
            "dlk1": np.zeros(lshape), "dlq2": np.zeros(lshape),
            "dlk2": np.zeros(lshape), "dw": np.empty(2 * d)}
+    aux = {"dlam_head": np.empty(H), "dlam_scale": np.empty(H)}
     order = ["dq", "dk", "dv", "dlq1", "dlk1", "dlq2", "dlk2", "dw"]
     # the rotary arguments of the forward entry points are not part of this one
     rc = (lib or load()).diffattn_ref_bwd(
         *args[:-4], _ptr(dya, ctypes.c_float),
-        *[_ptr(out[kk], ctypes.c_double) for kk in order], int(nthreads))
+        *[_ptr(out[kk], ctypes.c_double) for kk in order],
+        _ptr(aux["dlam_head"], ctypes.c_double),
+        _ptr(aux["dlam_scale"], ctypes.c_double), int(nthreads))
     del keep
     if rc != 0:
         raise ValueError(f"diffattn_ref_bwd failed with status {rc}")
+    out["aux"] = aux
     return out
 
 

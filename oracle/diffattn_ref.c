@@ -436,7 +436,10 @@ int diffattn_ref_fwd_kv(const float *q, const float *k, const float *v,
  *   dlq1, dlk1, dlq2, dlk2: gradients of the lambda vectors, laid out like
  *     them (lambda_stride 0: one set of d; else H sets, stride apart);
  *   dw[2d]: gradient of the RMSNorm weight (of a weight of ones when w is
- *     NULL).
+ *     NULL);
+ *   dlam_head[H]: dlambda_h, and dlam_scale[H]: the sum over the head's rows
+ *     of |dpre| |O_2| (Euclidean norms), which bounds how much a relative
+ *     error in O_2 or dpre can move dlambda_h (the sum can cancel).
  * The chain, per row (token i, head h) of the forward above:
  *   g = dy * w * (1 - lambda_init);  r = 1 / sqrt(mean(pre^2) + eps)
  *   dpre = r g - r^3 pre <g, pre> / (2d);   dw += dy * pre * r * (1 - lambda_init)
@@ -457,7 +460,8 @@ int diffattn_ref_bwd(const float *q, const float *k, const float *v,
                      const int32_t *cu_seqlens, int nseq, int64_t T, int H,
                      int Hkv, int d, const float *dy, double *dq, double *dk,
                      double *dv, double *dlq1, double *dlk1, double *dlq2,
-                     double *dlk2, double *dw, int nthreads)
+                     double *dlk2, double *dw, double *dlam_head,
+                     double *dlam_scale, int nthreads)
 {
     if (check_args(cu_seqlens, nseq, T, H, Hkv, d) || lambda_stride < 0)
         return -1;
@@ -465,11 +469,13 @@ int diffattn_ref_bwd(const float *q, const float *k, const float *v,
     const int64_t ntask = (int64_t)nseq * Hkv;
     double *lam = malloc(sizeof(double) * (size_t)H);
     double *tdl = calloc((size_t)(ntask * H), sizeof(double));   /* dlambda per task, head */
+    double *tds = calloc((size_t)(ntask * H), sizeof(double));   /* its scale */
     double *tdw = calloc((size_t)(ntask * dv2), sizeof(double)); /* dw per task */
-    if (!lam || !tdl || !tdw) {
+    if (!lam || !tdl || !tdw || !tds) {
         free(lam);
         free(tdl);
         free(tdw);
+        free(tds);
         return -2;
     }
     lambda_per_head(lq1, lk1, lq2, lk2, lambda_stride, H, d, lambda_init, lam);
@@ -548,7 +554,7 @@ int diffattn_ref_bwd(const float *q, const float *k, const float *v,
                         gp += (double)dyr[c] * wc * (1.0 - lambda_init) * pre[c];
                         tdw[task * dv2 + c] += (double)dyr[c] * pre[c] * r * (1.0 - lambda_init);
                     }
-                    double dl = 0.0;
+                    double dl = 0.0, nd = 0.0, no = 0.0;
                     for (int c = 0; c < dv2; ++c) {
                         const double wc = w ? (double)w[c] : 1.0;
                         const double gc = (double)dyr[c] * wc * (1.0 - lambda_init);
@@ -556,8 +562,11 @@ int diffattn_ref_bwd(const float *q, const float *k, const float *v,
                         dO[0][c] = dp;
                         dO[1][c] = -lam[h] * dp;
                         dl -= dp * o[1][c];
+                        nd += dp * dp;
+                        no += o[1][c] * o[1][c];
                     }
                     tdl[task * H + h] += dl;
+                    tds[task * H + h] += sqrt(nd) * sqrt(no);
                     /* both softmax maps */
                     for (int m = 0; m < 2; ++m) {
                         double D = 0.0;
@@ -595,6 +604,15 @@ int diffattn_ref_bwd(const float *q, const float *k, const float *v,
                 acc += tdw[t2 * dv2 + c];
             dw[c] = acc;
         }
+        for (int h = 0; h < H; ++h) {
+            double a2 = 0.0, s2 = 0.0;
+            for (int64_t t2 = 0; t2 < ntask; ++t2) {
+                a2 += tdl[t2 * H + h];
+                s2 += tds[t2 * H + h];
+            }
+            dlam_head[h] = a2;
+            dlam_scale[h] = s2;
+        }
         const int nsets = lambda_stride ? H : 1;
         for (int st = 0; st < nsets; ++st) {
             double dlam = 0.0;
@@ -620,6 +638,7 @@ int diffattn_ref_bwd(const float *q, const float *k, const float *v,
     free(lam);
     free(tdl);
     free(tdw);
+    free(tds);
     return err;
 }
 

@@ -582,6 +582,14 @@ def pin_bwd_autograd(lib):
         lam_init = 0.8 - 0.6 * math.exp(-0.3 * (seed - 300))
         got = oracle.bwd(q, k, v, *lv, lam_init, dy, w, 1e-5, causal, cu, lib=lib)
         ref = autograd_composition(q, k, v, lv, lam_init, w, 1e-5, causal, cu, dy)
+        # dlambda per head reproduces the vector gradients by the chain rule
+        aux = got["aux"]
+        for hh in range(H if per_head else 1):
+            sel = (lambda x: x[hh]) if per_head else (lambda x: x)
+            dl = aux["dlam_head"][hh] if per_head else aux["dlam_head"].sum()
+            ea = math.exp(float(np.dot(sel(lv[0]).astype(np.float64), sel(lv[1]))))
+            assert np.max(np.abs(dl * ea * sel(lv[1]) - sel(ref["dlq1"]))) < 1e-9
+            assert np.all(aux["dlam_scale"] >= np.abs(aux["dlam_head"]) - 1e-12)
         for name in ref:
             err = np.max(np.abs(got[name] - ref[name]))
             assert err < 1e-9, f"bwd vs autograd case {seed} {name}: max-abs {err:.3e}"

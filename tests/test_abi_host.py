@@ -172,3 +172,57 @@ def call_kv(**over):
 ])
 def test_kv_validation_before_any_device_work(over, status):
     assert call_kv(**over) == status
+
+
+# --------------------------------------------------------------------------
+# training forward and backward
+
+def test_supported_bwd_and_workspace():
+    import torch
+    assert da.supported_bwd(torch.bfloat16, 64)
+    assert da.supported_bwd(torch.bfloat16, 32)
+    assert not da.supported_bwd(torch.float32, 64)
+    assert da.bwd_workspace_size(4096, 16, 64) > da.bwd_workspace_size(1024, 16, 64) > 0
+    assert da.bwd_workspace_size(-1, 16, 64) == 0
+
+
+def call_bwd(**over):
+    a = [da.BF16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0.3, None, 1e-5, 1,
+         None, 2, 0, 64, 16, 4, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+         FAKE, FAKE, None, FAKE, 1 << 30, None]
+    names = ["dtype", "q", "k", "v", "lq1", "lk1", "lq2", "lk2", "lstride",
+             "lam", "w", "eps", "causal", "cu", "nseq", "max_seqlen", "T", "H",
+             "Hkv", "d", "dout", "lse", "o12", "dq", "dk", "dv", "dlq1", "dlk1",
+             "dlq2", "dlk2", "dw", "ws", "ws_bytes", "stream"]
+    for k2, v2 in over.items():
+        a[names.index(k2)] = v2
+    return da.library().diffattn_bwd(*a)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(dtype=9), da.EINVAL),
+    (dict(dtype=da.F32), da.EUNSUPPORTED),
+    (dict(d=16), da.EUNSUPPORTED),
+    (dict(H=6), da.EINVAL),
+    (dict(H=512, Hkv=4), da.EINVAL),            # more heads than supported
+    (dict(causal=3), da.EINVAL),
+    (dict(lstride=10), da.EINVAL),
+    (dict(T=63), da.EINVAL),                    # T % nseq
+    (dict(dq=None), da.EINVAL),
+    (dict(dlk2=None), da.EINVAL),
+    (dict(o12=FAKE + 4), da.EINVAL),            # alignment
+    (dict(ws_bytes=100), da.EINVAL),
+    (dict(T=0, q=None, k=None, v=None), da.OK),  # nothing to do
+])
+def test_bwd_validation_before_any_device_work(over, status):
+    assert call_bwd(**over) == status
+
+
+def test_fwd_train_validation():
+    lib = da.library()
+    args = [da.BF16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0.3, None, 1e-5, 1,
+            None, 2, 0, 64, 16, 4, 64, FAKE, None, FAKE, None]
+    assert lib.diffattn_fwd_train(*args) == da.EINVAL           # lse missing
+    args[21] = FAKE
+    args[22] = FAKE + 4
+    assert lib.diffattn_fwd_train(*args) == da.EINVAL           # o12 misaligned

@@ -1,0 +1,181 @@
+"""Parity of the backward pass (diffattn_fwd_train + diffattn_bwd, through
+the C ABI) with the fp64 oracle's ``bwd``.
+
+Gradients have very different scales from tensor to tensor, so the bar is
+relative: max|got - ref| <= 2e-2 * max|ref| for dq, dk, dv and dw -- the
+forward's 2e-2 on O(1) outputs; dq, dk and dv come from contractions with
+bf16 operands (P, dS, dO_m) and are stored in bf16.  The lambda-vector
+gradients are dlambda times a vector, and dlambda = -sum over rows of
+<dpre, O_2> can cancel to far below its terms, each of which carries the
+forward's bf16 rounding of P; their error is bounded instead by 2^-7 (two
+bf16 roundings) times the oracle's sum over rows of |dpre| |O_2|, times the
+vector factor.  All tests need an MI355X.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import WORKLOADS, custom, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+REL = {"dq": 2e-2, "dk": 2e-2, "dv": 2e-2, "dlq1": 2.0 ** -7, "dlk1": 2.0 ** -7,
+       "dlq2": 2.0 ** -7, "dlk2": 2.0 ** -7, "dw": 2e-2}
+
+
+def announce(msg):
+    print(f"[parity-bwd] {msg}", flush=True)
+
+
+def dout_for(inp, seed):
+    g = torch.Generator().manual_seed(seed)
+    T, H, _, d = inp.q.shape
+    return torch.randn(T, H, 2 * d, generator=g).to(inp.q.dtype)
+
+
+def gpu_grads(inp, dy, w=True, repeat=1):
+    import differential_attention_amd as da
+    dev = torch.device("cuda:0")
+    c = lambda t: t.to(dev).contiguous()
+    lv = [c(x) for x in (inp.lq1, inp.lk1, inp.lq2, inp.lk2)]
+    wt = c(inp.w) if w else None
+    kw = dict(subln_weight=wt, eps=inp.eps, causal=inp.causal,
+              cu_seqlens=c(inp.cu_seqlens), max_seqlen=inp.max_seqlen)
+    q, k, v = c(inp.q), c(inp.k), c(inp.v)
+    lam0 = da.lambda_init(inp.depth)
+    out, lse, o12 = da.fwd_train(q, k, v, *lv, lam0, **kw)
+    res = [da.bwd(q, k, v, *lv, lam0, c(dy), lse, o12, **kw) for _ in range(repeat)]
+    torch.cuda.synchronize()
+    return out, res
+
+
+def oracle_grads(inp, dy, w=True):
+    return oracle.bwd(inp.q, inp.k, inp.v, inp.lq1, inp.lk1, inp.lq2, inp.lk2,
+                      oracle.lambda_init(inp.depth), dy, inp.w if w else None,
+                      inp.eps, inp.causal, inp.cu_seqlens)
+
+
+def compare(got, ref, tag):
+    """dq, dk, dv, dw: max-abs relative to the tensor's largest magnitude.
+    The lambda-vector gradients all carry the factor dlambda (a sum over
+    rows that can cancel), so their error is measured against the oracle's
+    dlambda_scale instead: the sum over rows of |dpre| |O_2|, times the
+    vector factor (e^a |lk1| for dlq1, and so on)."""
+    errs = {}
+    aux = ref["aux"]
+    for name, r in ref.items():
+        if name == "aux":
+            continue
+        gv = got[name].float().cpu().double().numpy()
+        assert np.all(np.isfinite(gv)), f"{tag}: non-finite {name}"
+        if name.startswith("dl"):
+            # |d vector| = |dlambda| * |factor|: bound it by scale * |factor|
+            dl = aux["dlam_head"].sum() if r.ndim == 1 else aux["dlam_head"][:, None]
+            sc = aux["dlam_scale"].sum() if r.ndim == 1 else aux["dlam_scale"][:, None]
+            factor = np.abs(r) / np.maximum(np.abs(dl), 1e-300)
+            bound = sc * factor + 1e-30
+            errs[name] = float(np.max(np.abs(gv - r) / bound))
+        else:
+            scale = max(float(np.max(np.abs(r))), 1e-30)
+            errs[name] = float(np.max(np.abs(gv - r))) / scale
+    announce(f"{tag}: " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    for name, err in errs.items():
+        assert err <= REL[name], f"{tag}: {name} relative max-abs {err:.3e}"
+    return max(errs[n] / REL[n] for n in errs)
+
+
+RAGGED = (1, 0, 31, 32, 33, 63, 64, 65, 127, 200, 7)
+
+
+@pytest.mark.parametrize("d", [64, 32])
+@pytest.mark.parametrize("H,Hkv", [(4, 2), (8, 2), (3, 1), (16, 4)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_bwd_ragged(d, H, Hkv, causal):
+    wl = custom("bwd", "bf16", RAGGED, H, Hkv, d, depth=6, causal=causal,
+                seed=H * 10 + d)
+    inp = make_inputs(wl)
+    inp.w = torch.linspace(0.5, 1.5, 2 * d)
+    dy = dout_for(inp, 7)
+    _, (got,) = gpu_grads(inp, dy)
+    worst = compare(got, oracle_grads(inp, dy), f"d={d} H={H} Hkv={Hkv} causal={causal}")
+    announce(f"ragged d={d} H={H} Hkv={Hkv} causal={causal}: worst err / bar {worst:.3f}")
+
+
+def test_bwd_embed2048_full():
+    """The pull request's test shape (B=2, N=512, 16 heads, 4 KV heads) in
+    full: several query and key tiles per sequence."""
+    inp = make_inputs(WORKLOADS["embed2048_b2_n512"])
+    dy = dout_for(inp, 11)
+    out, (got,) = gpu_grads(inp, dy)
+    worst = compare(got, oracle_grads(inp, dy), "embed2048")
+    announce(f"embed2048: worst err / bar {worst:.3f}")
+
+
+def test_bwd_long_sequences():
+    """8 sequences of 1024 tokens (8 tiles each way), GQA 4."""
+    wl = custom("bwd_long", "bf16", (1024,) * 8, 16, 4, 64, depth=8, seed=12)
+    inp = make_inputs(wl)
+    dy = dout_for(inp, 13)
+    _, (got,) = gpu_grads(inp, dy)
+    worst = compare(got, oracle_grads(inp, dy), "8 x 1024")
+    announce(f"8 x 1024: worst err / bar {worst:.3f}")
+
+
+def test_bwd_per_head_lambda_no_weight():
+    wl = custom("bwd_ph", "bf16", (150, 90), 8, 2, 64, depth=4, seed=14)
+    inp = make_inputs(wl)
+    g = torch.Generator().manual_seed(15)
+    inp.lq1, inp.lk1, inp.lq2, inp.lk2 = [0.3 * torch.randn(8, 64, generator=g)
+                                          for _ in range(4)]
+    dy = dout_for(inp, 16)
+    _, (got,) = gpu_grads(inp, dy, w=False)
+    worst = compare(got, oracle_grads(inp, dy, w=False), "per-head lambda")
+    announce(f"per-head lambda, no weight: worst err / bar {worst:.3f}")
+
+
+def test_training_forward_matches_forward():
+    """The training forward's output equals the plain forward bitwise, and
+    its saved state reproduces the output: RMSNorm(O_1 - lambda O_2)."""
+    import differential_attention_amd as da
+    wl = custom("train", "bf16", (300, 41), 16, 4, 64, depth=8, seed=17)
+    inp = make_inputs(wl)
+    dev = torch.device("cuda:0")
+    c = lambda t: t.to(dev).contiguous()
+    lv = [c(x) for x in (inp.lq1, inp.lk1, inp.lq2, inp.lk2)]
+    lam0 = da.lambda_init(8)
+    out, lse, o12 = da.fwd_train(c(inp.q), c(inp.k), c(inp.v), *lv, lam0, c(inp.w),
+                                 1e-5, True, c(inp.cu_seqlens), max_seqlen=300)
+    plain = da.fwd(c(inp.q), c(inp.k), c(inp.v), *lv, lam0, c(inp.w), 1e-5, True,
+                   c(inp.cu_seqlens), max_seqlen=300)
+    torch.cuda.synchronize()
+    assert torch.equal(out, plain)
+    lam = oracle.lam(inp.lq1, inp.lk1, inp.lq2, inp.lk2, lam0)
+    o = o12.double().cpu()
+    pre = o[:, :, 0] - lam * o[:, :, 1]
+    y = pre / torch.sqrt((pre * pre).mean(-1, keepdim=True) + 1e-5) * (1 - lam0)
+    assert float((y - out.double().cpu()).abs().max()) < 2e-2
+    assert torch.all(torch.isfinite(lse))
+
+
+def test_bwd_deterministic():
+    wl = custom("bwd_det", "bf16", (333, 128, 5), 16, 4, 64, depth=3, seed=18)
+    inp = make_inputs(wl)
+    dy = dout_for(inp, 19)
+    _, (a, b) = gpu_grads(inp, dy, repeat=2)
+    for name in a:
+        assert torch.equal(a[name], b[name]), name
+
+
+def test_bwd_small_workspace_rejected():
+    import differential_attention_amd as da
+    wl = custom("bwd_ws", "bf16", (64,), 4, 2, 64, seed=20)
+    inp = make_inputs(wl)
+    dev = torch.device("cuda:0")
+    c = lambda t: t.to(dev).contiguous()
+    lv = [c(x) for x in (inp.lq1, inp.lk1, inp.lq2, inp.lk2)]
+    out, lse, o12 = da.fwd_train(c(inp.q), c(inp.k), c(inp.v), *lv, 0.3)
+    with pytest.raises(da.DiffAttnError):
+        da.bwd(c(inp.q), c(inp.k), c(inp.v), *lv, 0.3, torch.zeros_like(out), lse,
+               o12, workspace=torch.empty(256, dtype=torch.uint8, device=dev))
