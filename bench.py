@@ -47,6 +47,8 @@ _CSRC = os.path.join(HERE, "differential_attention_amd", "csrc")
 _HEADER = os.path.join(HERE, "include", "diffattn.h")
 KERNEL_SOURCES = [os.path.join(_CSRC, "diffattn_fwd.hip"), _HEADER]
 KV_KERNEL_SOURCES = [os.path.join(_CSRC, "diffattn_kv.hip"), _HEADER]
+BWD_KERNEL_SOURCES = [os.path.join(_CSRC, "diffattn_fwd.hip"),
+                      os.path.join(_CSRC, "diffattn_bwd.hip"), _HEADER]
 
 
 def kernel_digest(sources=KERNEL_SOURCES) -> str:
@@ -218,6 +220,92 @@ def bench_kv(args, name) -> int:
     return 0
 
 
+METRIC_BWD = "diff-attention fwd+bwd (training step) TFLOP/s & % bf16 MFMA peak, 1 MI355X"
+
+
+def bench_bwd(args, name) -> int:
+    """One step = diffattn_fwd_train + diffattn_bwd on resident inputs."""
+    import torch
+    import workloads
+    import differential_attention_amd as da
+
+    wl = workloads.WORKLOADS[name]
+    inp = workloads.make_inputs(wl)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    c = lambda t: t.to(dev).contiguous()
+    q, k, v = c(inp.q), c(inp.k), c(inp.v)
+    lv = [c(x) for x in (inp.lq1, inp.lk1, inp.lq2, inp.lk2)]
+    w, cu = c(inp.w), c(inp.cu_seqlens)
+    gen = torch.Generator().manual_seed(1)
+    dout = c(torch.randn(wl.T, wl.H, 2 * wl.d, generator=gen).to(q.dtype))
+    out = torch.empty_like(dout)
+    lse = torch.empty(wl.T, wl.H, 2, dtype=torch.float32, device=dev)
+    o12 = torch.empty(wl.T, wl.H, 2, 2 * wl.d, dtype=torch.float32, device=dev)
+    grads = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)] + \
+            [torch.empty_like(x) for x in lv] + [torch.empty(2 * wl.d, device=dev)]
+    need = da.bwd_workspace_size(wl.T, wl.H, wl.d)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream(dev)
+    lam0 = da.lambda_init(wl.depth)
+    lib = da.library()
+    common = (da.BF16, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+              *[x.data_ptr() for x in lv], 0, lam0, w.data_ptr(), wl.eps,
+              int(wl.causal), cu.data_ptr(), wl.nseq, wl.max_seqlen, wl.T, wl.H,
+              wl.Hkv, wl.d)
+
+    def step():
+        st = lib.diffattn_fwd_train(*common, out.data_ptr(), lse.data_ptr(),
+                                    o12.data_ptr(), stream.cuda_stream)
+        if st != 0:
+            raise da.DiffAttnError(st, "diffattn_fwd_train")
+        st = lib.diffattn_bwd(*common, dout.data_ptr(), lse.data_ptr(), o12.data_ptr(),
+                              *[g.data_ptr() for g in grads], ws.data_ptr(), need,
+                              stream.cuda_stream)
+        if st != 0:
+            raise da.DiffAttnError(st, "diffattn_bwd")
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            step()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    fwd_flops = wl.flops()
+    bwd_flops = fwd_flops * 28.0 / 12.0
+    tflops = (fwd_flops + bwd_flops) / (ms * 1e-3) / 1e12
+    result = {
+        "metric": METRIC_BWD,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded N(0,1) q/k/v/dout, N(0,0.1^2) lambda vectors)",
+        "config": {"workload": name + "+bwd", "T": wl.T, "nseq": wl.nseq,
+                   "H": wl.H, "Hkv": wl.Hkv, "d": wl.d, "causal": wl.causal,
+                   "flops_fwd": fwd_flops, "flops_bwd": bwd_flops,
+                   "workspace_bytes": need, "wall_s_timed": round(wall, 4),
+                   "kernel_digest": kernel_digest(BWD_KERNEL_SOURCES)},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
+                     "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_from_profiles(name + "_bwd", BWD_KERNEL_SOURCES)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def copy_calibration(args) -> int:
     """A plain device-to-device copy of known size, for scaling the HBM byte
     counters (FETCH_SIZE, WRITE_SIZE) of the kernel under a profiler."""
@@ -249,6 +337,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--bwd", action="store_true",
+                    help="a training step instead: the training forward and "
+                         "the backward pass (bf16, no rotary prologue)")
     ap.add_argument("--rope", action="store_true",
                     help="prefill with the fused rotary prologue (q and k "
                          "given unrotated, tables of base 10000)")
@@ -271,6 +362,8 @@ def main() -> int:
     name = args.workload or workloads.HEADLINE
     if name in workloads.KV_WORKLOADS:
         return bench_kv(args, name)
+    if args.bwd:
+        return bench_bwd(args, name)
     wl = workloads.WORKLOADS[name]
     inp = workloads.make_inputs(wl)
     dev = torch.device("cuda:0")

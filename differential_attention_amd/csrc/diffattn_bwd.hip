@@ -11,11 +11,13 @@
 //
 // Four kernels, no atomics (the result is bitwise reproducible):
 //
-//  prep     one wave per (head, token stride): pre = O_1 - lambda O_2 and
+//  prep     workgroups of four waves per head, each wave striding over the
+//           tokens: pre = O_1 - lambda O_2 and
 //           its RMSNorm backward, dO_1 = dpre, dO_2 = -lambda dpre (stored
 //           bf16 as MFMA operands), D_m = <dO_m, O_m> (from the rounded
 //           dO_m, so that the softmax gradients of a row sum to zero),
-//           and per-wave partial sums of the weight and lambda gradients.
+//           and per-workgroup partial sums of the weight and lambda
+//           gradients.
 //  reduce   one workgroup: the partial sums in a fixed order, and the
 //           lambda-vector gradients by the chain rule.
 //  dq       query-outer, as the forward: one workgroup = (sequence, head,
@@ -50,9 +52,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kThreads = 512;   // 8 waves: 2 maps x 4 blocks of 32 rows
-constexpr int kTile = 128;      // queries (dq) or keys (dkdv) per workgroup
+constexpr int kSubs = 4;        // blocks of 32 rows per map
+constexpr int kTile = 32 * kSubs;   // queries (dq) or keys (dkdv) per workgroup
 constexpr int kInner = 64;      // keys (dq) or queries (dkdv) per staged tile
-constexpr int kPrepPerHead = 64;   // prep waves per head
+constexpr int kPrepPerHead = 256;  // prep waves per head (4 per workgroup)
 
 __device__ inline f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c)
 {
@@ -156,11 +159,13 @@ template <int D>
 __global__ __launch_bounds__(256) void bwd_prep(BwdParams p)
 {
     constexpr int CPL = 2 * D / 64;   // columns per lane
-    const int lane = threadIdx.x & 63;
-    const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (wid >= p.H * kPrepPerHead)
-        return;
-    const int h = wid % p.H;
+    __shared__ float red_dw[4][2 * D];
+    __shared__ float red_dl[4];
+    const int lane = threadIdx.x & 63, wv4 = threadIdx.x >> 6;
+    // the four waves of a workgroup serve one head: wave w of the head takes
+    // tokens w, w + kPrepPerHead, ...
+    const int h = blockIdx.x % p.H;
+    const int wid = (blockIdx.x / p.H) * 4 + wv4;   // wave index within the head
     const float lam = head_lambda(p, h, lane, D);
     const float sc = 1.f - p.lambda_init;
     float wv[CPL], dwp[CPL];
@@ -170,7 +175,7 @@ __global__ __launch_bounds__(256) void bwd_prep(BwdParams p)
         dwp[cc] = 0.f;
     }
     float dlp = 0.f;
-    for (int t = wid / p.H; t < p.T; t += kPrepPerHead) {
+    for (int t = wid; t < p.T; t += kPrepPerHead) {
         const int64_t row = (int64_t)t * p.H + h;
         const float *o1 = p.o12 + row * 2 * (2 * D) + CPL * lane;
         const float *o2 = o1 + 2 * D;
@@ -211,39 +216,63 @@ __global__ __launch_bounds__(256) void bwd_prep(BwdParams p)
             p.dd[row * 2 + 1] = d2;
         }
     }
+    // the workgroup's four waves summed in a fixed order, one partial per
+    // workgroup: part[blockIdx.x] (head h = blockIdx.x % H)
 #pragma unroll
     for (int cc = 0; cc < CPL; ++cc)
-        p.part_dw[(int64_t)wid * 2 * D + CPL * lane + cc] = dwp[cc];
+        red_dw[wv4][CPL * lane + cc] = dwp[cc];
     dlp = wave_sum(dlp);
     if (lane == 0)
-        p.part_dl[wid] = dlp;
+        red_dl[wv4] = dlp;
+    __syncthreads();
+    for (int c = threadIdx.x; c < 2 * D; c += 256)
+        p.part_dw[(int64_t)blockIdx.x * 2 * D + c] =
+            (red_dw[0][c] + red_dw[1][c]) + (red_dw[2][c] + red_dw[3][c]);
+    if (threadIdx.x == 0)
+        p.part_dl[blockIdx.x] = (red_dl[0] + red_dl[1]) + (red_dl[2] + red_dl[3]);
 }
 
 // ---------------------------------------------------------------------------
 // reduce: fixed-order sums of the partials, lambda-vector gradients.
+constexpr int kPrepBlocksPerHead = kPrepPerHead / 4;
+
 template <int D>
-__global__ __launch_bounds__(256) void bwd_reduce(BwdParams p)
+__global__ __launch_bounds__(1024) void bwd_reduce(BwdParams p)
 {
+    // 1024 threads: (column c, part j) sums partials j, j + 8, ... of its
+    // column, then the 8 parts are added in a fixed order
+    constexpr int NPART = 1024 / (2 * D);
+    __shared__ float red[1024];
     __shared__ float dlh[256];   // per head (H <= 256)
     const int tid = threadIdx.x;
-    const int nprep = p.H * kPrepPerHead;
-    if (p.dw) {
-        for (int c = tid; c < 2 * D; c += 256) {
-            float acc = 0.f;
-            for (int w = 0; w < nprep; ++w)
-                acc += p.part_dw[(int64_t)w * 2 * D + c];
-            p.dw[c] = acc;
-        }
+    const int nblk = p.H * kPrepBlocksPerHead;
+    {
+        const int c = tid % (2 * D), j = tid / (2 * D);
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        int w = j;
+        for (; w + 3 * NPART < nblk; w += 4 * NPART)
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                acc[u] += p.part_dw[(int64_t)(w + u * NPART) * 2 * D + c];
+        for (; w < nblk; w += NPART)
+            acc[0] += p.part_dw[(int64_t)w * 2 * D + c];
+        red[tid] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     }
-    for (int h = tid; h < p.H; h += 256) {
+    for (int h = tid; h < p.H; h += 1024) {
         float acc = 0.f;
-        for (int k = 0; k < kPrepPerHead; ++k)
+        for (int k = 0; k < kPrepBlocksPerHead; ++k)
             acc += p.part_dl[k * p.H + h];
         dlh[h] = acc;
     }
     __syncthreads();
+    if (p.dw && tid < 2 * D) {
+        float acc = 0.f;
+        for (int j = 0; j < NPART; ++j)
+            acc += red[j * 2 * D + tid];
+        p.dw[tid] = acc;
+    }
     const int nsets = p.lstride ? p.H : 1;
-    for (int idx = tid; idx < nsets * D; idx += 256) {
+    for (int idx = tid; idx < nsets * D; idx += 1024) {
         const int st = idx / D, c = idx % D;
         float dlam = 0.f;
         if (p.lstride) {
@@ -298,7 +327,7 @@ void bwd_dq(BwdParams p)
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int n = lane & 31, h = lane >> 5;
-    const int map = wave >> 2, sub = wave & 3;
+    const int map = wave / kSubs, sub = wave % kSubs;
 
     // longest query tiles first
     const int pairs = p.nseq * p.H;
@@ -418,7 +447,7 @@ void bwd_dkdv(BwdParams p)
     // Q and dO tiles during the loop; the dV exchange of the epilogue after it
     constexpr int QT_BYTES = kInner * QROW;
     constexpr int DT_BYTES = kInner * DROW;
-    constexpr int XCH_BYTES = 4 * NVB * 16 * 64 * 4;
+    constexpr int XCH_BYTES = kSubs * NVB * 16 * 64 * 4;
     constexpr int SMEM = QT_BYTES + DT_BYTES > XCH_BYTES ? QT_BYTES + DT_BYTES : XCH_BYTES;
     __shared__ __attribute__((aligned(16))) char smem[SMEM];
     __shared__ float lt[kInner * 2], ddt[kInner * 2];
@@ -427,7 +456,7 @@ void bwd_dkdv(BwdParams p)
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int n = lane & 31, h = lane >> 5;
-    const int map = wave >> 2, sub = wave & 3;
+    const int map = wave / kSubs, sub = wave % kSubs;
 
     const int pairs = p.nseq * p.Hkv;
     const int tile = blockIdx.x / pairs;
@@ -585,8 +614,8 @@ BwdPlan bwd_plan(int64_t T, int H, int d)
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     pl.do12 = up((size_t)T * H * 2 * (2 * d) * 2);
     pl.dd = up((size_t)T * H * 2 * 4);
-    pl.part_dw = up((size_t)H * kPrepPerHead * 2 * d * 4);
-    pl.part_dl = up((size_t)H * kPrepPerHead * 4);
+    pl.part_dw = up((size_t)H * (kPrepPerHead / 4) * 2 * d * 4);
+    pl.part_dl = up((size_t)H * (kPrepPerHead / 4) * 4);
     pl.total = pl.do12 + pl.dd + pl.part_dw + pl.part_dl;
     return pl;
 }
@@ -594,9 +623,8 @@ BwdPlan bwd_plan(int64_t T, int H, int d)
 template <int D>
 void launch_bwd(const BwdParams &p, int nseq, int Hkv, hipStream_t st)
 {
-    const int nprep = p.H * kPrepPerHead;
-    hipLaunchKernelGGL(bwd_prep<D>, dim3((nprep + 3) / 4), dim3(256), 0, st, p);
-    hipLaunchKernelGGL(bwd_reduce<D>, dim3(1), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(bwd_prep<D>, dim3(p.H * kPrepBlocksPerHead), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(bwd_reduce<D>, dim3(1), dim3(1024), 0, st, p);
     hipLaunchKernelGGL(bwd_dq<D>, dim3(p.ntile * nseq * p.H), dim3(kThreads), 0, st, p);
     hipLaunchKernelGGL(bwd_dkdv<D>, dim3(p.ntile * nseq * Hkv), dim3(kThreads), 0, st, p);
 }
