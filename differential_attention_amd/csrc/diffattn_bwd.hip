@@ -21,14 +21,17 @@
 //  reduce   one workgroup: the partial sums in a fixed order, and the
 //           lambda-vector gradients by the chain rule.
 //  dq       query-outer, as the forward: one workgroup = (sequence, head,
-//           128 queries), wave = (map, 32 queries).  Over K/V tiles staged
-//           in LDS: S^T = K Q^T, P^T = exp2(S^T c - lse), dP^T = V dO^T,
+//           128 queries), wave = (map, 32 queries).  Over K/V tiles
+//           double-buffered in LDS (the next tile travels through registers
+//           while the current one is used): S^T = K Q^T,
+//           P^T = exp2(S^T c - lse), dP^T = V dO^T,
 //           dS^T = P^T (dP^T - D), dQ^T += K^T dS^T (K^T through the
 //           transposing LDS read, dS^T straight from the accumulator).
 //  dkdv     key-outer: one workgroup = (sequence, KV head, 128 keys), wave
-//           = (map, 32 keys) with its K and V rows in registers.  Over the
-//           group's heads and the query tiles that can see the keys (Q, dO,
-//           lse, D staged in LDS): S = Q K^T, P, dP = dO V^T, dS, then
+//           = (map, 32 keys); the K and V rows stay in LDS.  Over the
+//           group's heads and the 32-row query tiles that can see the keys
+//           (Q, dO, lse, D double-buffered in LDS as for dq): S = Q K^T, P,
+//           dP = dO V^T, dS, then
 //           dV^T += dO^T P and dK^T += Q^T dS (dO^T and Q^T through the
 //           transposing read, P and dS straight from the accumulator).  The
 //           two maps' dV are summed through LDS at the end.
@@ -295,24 +298,42 @@ __global__ __launch_bounds__(1024) void bwd_reduce(BwdParams p)
     }
 }
 
-// Cooperative copy of `rows` rows of `rowbytes` bytes (rows past `valid` are
-// zero) from global rows `stride` bytes apart into an LDS tile with rows
-// `ldsrow` bytes apart, in 16-byte pieces.
-__device__ inline void stage_rows(char *lds, int ldsrow, const char *src, int64_t stride,
-                                  int rowbytes, int rows, int valid)
-{
-    const int cpr = rowbytes / 16;
-    for (int i = threadIdx.x; i < rows * cpr; i += kThreads) {
-        const int r = i / cpr, c = (i % cpr) * 16;
-        u32x4 x = u32x4{0u, 0u, 0u, 0u};
-        if (r < valid)
-            x = *(const u32x4 *)(src + r * stride + c);
-        *(u32x4 *)(lds + r * ldsrow + c) = x;
+// ---------------------------------------------------------------------------
+// Staging of row tiles: `rows` rows of ROWB bytes from global rows `stride`
+// bytes apart into an LDS tile with rows LROW bytes apart, in 16-byte
+// chunks spread over the workgroup; rows at or past `valid` read as zero.
+// load() fills this thread's registers (the loads stay in flight), store()
+// writes them to LDS, so a tile can travel while the previous one is used.
+template <int ROWB, int LROW, int ROWS>
+struct Stager {
+    static constexpr int CPR = ROWB / 16;
+    static constexpr int N = (ROWS * CPR + kThreads - 1) / kThreads;   // chunks per thread
+    u32x4 r[N];
+    __device__ inline void load(const char *src, int64_t stride, int valid)
+    {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int idx = threadIdx.x + i * kThreads;
+            const int row = idx / CPR, c = (idx % CPR) * 16;
+            r[i] = u32x4{0u, 0u, 0u, 0u};
+            if (idx < ROWS * CPR && row < valid)
+                r[i] = *(const u32x4 *)(src + row * stride + c);
+        }
     }
-}
+    __device__ inline void store(char *lds) const
+    {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int idx = threadIdx.x + i * kThreads;
+            const int row = idx / CPR, c = (idx % CPR) * 16;
+            if (idx < ROWS * CPR)
+                *(u32x4 *)(lds + row * LROW + c) = r[i];
+        }
+    }
+};
 
 // ---------------------------------------------------------------------------
-// dq: query-outer.
+// dq: query-outer; K/V tiles of kInner keys double-buffered in LDS.
 template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq(BwdParams p)
@@ -322,8 +343,11 @@ void bwd_dq(BwdParams p)
     constexpr int NKS = D / 16;            // QK contraction steps
     constexpr int NVS = 2 * D / 16;        // dO V contraction steps
     constexpr int NDB = D / 32;            // 32-dim blocks of dQ
-    __shared__ __attribute__((aligned(16))) char kt[kInner * LROW];
-    __shared__ __attribute__((aligned(16))) char vt[kInner * LROW];
+    constexpr int TILEB = kInner * LROW;
+    // two stages, each a K tile then a V tile; separate objects so that the
+    // compiler can see stores to one never alias loads from the other
+    __shared__ __attribute__((aligned(16))) char st0[2 * TILEB];
+    __shared__ __attribute__((aligned(16))) char st1[2 * TILEB];
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int n = lane & 31, h = lane >> 5;
@@ -365,15 +389,24 @@ void bwd_dq(BwdParams p)
     const TrOperand tr(lane, LROW);
     const int qhi = min(s1, q0 + kTile);
     const int kend = p.causal ? qhi : s1;
+    const int ntiles = (kend - s0 + kInner - 1) / kInner;
     const int64_t kstride = (int64_t)p.Hkv * ROWB;
+    const char *kg = (const char *)p.k + (int64_t)g * ROWB;
+    const char *vg = (const char *)p.v + (int64_t)g * ROWB;
+    Stager<ROWB, LROW, kInner> sk, sv;
+    auto fetch = [&](int it) __attribute__((always_inline)) {
+        const int k0 = s0 + it * kInner;
+        sk.load(kg + (int64_t)k0 * kstride, kstride, min(kInner, s1 - k0));
+        sv.load(vg + (int64_t)k0 * kstride, kstride, min(kInner, s1 - k0));
+    };
+    auto put = [&](char *stage) __attribute__((always_inline)) {
+        sk.store(stage);
+        sv.store(stage + TILEB);
+    };
 
-    for (int k0 = s0; k0 < kend; k0 += kInner) {
-        __syncthreads();
-        stage_rows(kt, LROW, (const char *)p.k + (int64_t)k0 * kstride + (int64_t)g * ROWB,
-                   kstride, ROWB, kInner, min(kInner, s1 - k0));
-        stage_rows(vt, LROW, (const char *)p.v + (int64_t)k0 * kstride + (int64_t)g * ROWB,
-                   kstride, ROWB, kInner, min(kInner, s1 - k0));
-        __syncthreads();
+    auto compute = [&](int it, const char *stage) __attribute__((always_inline)) {
+        const char *kt = stage, *vt = stage + TILEB;
+        const int k0 = s0 + it * kInner;
 #pragma unroll
         for (int b = 0; b < kInner / 32; ++b) {
             const int kb0 = k0 + 32 * b;
@@ -381,12 +414,12 @@ void bwd_dq(BwdParams p)
             if (kb0 >= s1 || (p.causal && kb0 > q0 + 32 * sub + 31))
                 continue;
             // S^T = K Q^T (keys x queries)
-            f32x16 st = f32x16{};
+            f32x16 sa = f32x16{};
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
                 const bf16x8 ka = *(const bf16x8 *)(kt + (32 * b + n) * LROW +
                                                     (map * D + 16 * ks + 8 * h) * 2);
-                st = mma(ka, qf[ks], st);
+                sa = mma(ka, qf[ks], sa);
             }
             // dP^T = V dO^T
             f32x16 dp = f32x16{};
@@ -400,19 +433,37 @@ void bwd_dq(BwdParams p)
             for (int a = 0; a < 16; ++a) {
                 const int key = kb0 + acc_row(a, h);
                 const bool vis = key < s1 && (!p.causal || key <= wq);
-                const float pv = vis ? exp2f(st[a] * c - lse) : 0.f;
-                st[a] = pv * (dp[a] - dval);
+                const float pv = vis ? exp2f(sa[a] * c - lse) : 0.f;
+                sa[a] = pv * (dp[a] - dval);
             }
             // dQ^T += K^T dS^T
 #pragma unroll
             for (int ps = 0; ps < 2; ++ps) {
-                const bf16x8 bs = pack8(st, 8 * ps);
+                const bf16x8 bs = pack8(sa, 8 * ps);
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)
                     dqa[db] = mma(tr.load(kt, LROW, 32 * b + 16 * ps, (map * D + 32 * db) * 2),
                                   bs, dqa[db]);
             }
         }
+    };
+    auto step = [&](int it, const char *cur, char *nxt) __attribute__((always_inline)) {
+        const bool more = it + 1 < ntiles;
+        if (more)
+            fetch(it + 1);
+        compute(it, cur);
+        if (more)
+            put(nxt);
+        __syncthreads();
+    };
+
+    fetch(0);
+    put(st0);
+    __syncthreads();
+    for (int it = 0; it < ntiles; it += 2) {
+        step(it, st0, st1);
+        if (it + 1 < ntiles)
+            step(it + 1, st1, st0);
     }
     if (!qok)
         return;
@@ -431,28 +482,31 @@ void bwd_dq(BwdParams p)
 }
 
 // ---------------------------------------------------------------------------
-// dkdv: key-outer.
+// dkdv: key-outer.  The workgroup's K and V rows sit in LDS for the whole
+// kernel; query tiles of kQT rows (Q, dO, lse, D) are double-buffered.
+constexpr int kQT = 32;
+
 template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv(BwdParams p)
 {
     constexpr int ROWB = 2 * D * 2;          // K, V or Q row bytes (both maps of q)
-    constexpr int QROW = ROWB + 16;
+    constexpr int LROW = ROWB + 16;
     constexpr int DROWB = 4 * D * 2;         // dO row bytes (both maps)
     constexpr int DROW = DROWB + 16;
     constexpr int NKS = D / 16;
     constexpr int NVS = 2 * D / 16;
     constexpr int NKB = D / 32;              // 32-dim blocks of dK
     constexpr int NVB = 2 * D / 32;          // 32-dim blocks of dV
-    // Q and dO tiles during the loop; the dV exchange of the epilogue after it
-    constexpr int QT_BYTES = kInner * QROW;
-    constexpr int DT_BYTES = kInner * DROW;
+    constexpr int KVB = kTile * LROW;        // K (or V) tile bytes
+    constexpr int QB = kQT * LROW;           // Q tile bytes
+    constexpr int DB = kQT * DROW;           // dO tile bytes
+    constexpr int STB = QB + DB + kQT * 4 * 4;   // one stage: Q, dO, lse[2], D[2]
     constexpr int XCH_BYTES = kSubs * NVB * 16 * 64 * 4;
-    constexpr int SMEM = QT_BYTES + DT_BYTES > XCH_BYTES ? QT_BYTES + DT_BYTES : XCH_BYTES;
-    __shared__ __attribute__((aligned(16))) char smem[SMEM];
-    __shared__ float lt[kInner * 2], ddt[kInner * 2];
-    char *qt = smem;
-    char *dt = smem + QT_BYTES;
+    static_assert(XCH_BYTES <= 2 * KVB, "dV exchange fits the K/V tiles");
+    __shared__ __attribute__((aligned(16))) char kvt[2 * KVB];   // K tile, then V tile
+    __shared__ __attribute__((aligned(16))) char st0[STB];
+    __shared__ __attribute__((aligned(16))) char st1[STB];
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int n = lane & 31, h = lane >> 5;
@@ -468,18 +522,15 @@ void bwd_dkdv(BwdParams p)
     if (k0 >= s1)
         return;
     const int wk = k0 + 32 * sub + n;   // this lane's key
-    const int wkc = min(wk, s1 - 1);
-
-    bf16x8 kf[NKS], vf[NVS];
+    const int64_t kstride = (int64_t)p.Hkv * ROWB;
     {
-        const bf16 *kr = p.k + ((int64_t)wkc * p.Hkv + g) * (2 * D) + map * D;
-        const bf16 *vr = p.v + ((int64_t)wkc * p.Hkv + g) * (2 * D);
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-            kf[ks] = *(const bf16x8 *)(kr + 16 * ks + 8 * h);
-#pragma unroll
-        for (int ks = 0; ks < NVS; ++ks)
-            vf[ks] = *(const bf16x8 *)(vr + 16 * ks + 8 * h);
+        Stager<ROWB, LROW, kTile> sk, sv;
+        sk.load((const char *)p.k + (int64_t)k0 * kstride + (int64_t)g * ROWB, kstride,
+                min(kTile, s1 - k0));
+        sv.load((const char *)p.v + (int64_t)k0 * kstride + (int64_t)g * ROWB, kstride,
+                min(kTile, s1 - k0));
+        sk.store(kvt);
+        sv.store(kvt + KVB);
     }
     f32x16 dka[NKB], dva[NVB];
 #pragma unroll
@@ -489,78 +540,104 @@ void bwd_dkdv(BwdParams p)
     for (int db = 0; db < NVB; ++db)
         dva[db] = f32x16{};
     const float c = kLog2e * rsqrtf((float)D);
-    const TrOperand trq(lane, QROW), trd(lane, DROW);
+    const TrOperand trq(lane, LROW), trd(lane, DROW);
     const int wk_first = k0 + 32 * sub;   // first key of this wave
     // queries before the tile's first key cannot see any of its keys
-    const int qstart = p.causal ? s0 + ((k0 - s0) / kInner) * kInner : s0;
+    const int qstart = p.causal ? k0 : s0;
+    const int nqt = (s1 - qstart + kQT - 1) / kQT;   // query tiles per head
+    const int total = p.G * nqt;                     // (head, query tile) steps
+    const char *krow = kvt + (32 * sub + n) * LROW + map * D * 2;
+    const char *vrow = kvt + KVB + (32 * sub + n) * LROW;
 
-    for (int hh = 0; hh < p.G; ++hh) {
-        const int head = g * p.G + hh;
-        for (int q0 = qstart; q0 < s1; q0 += kInner) {
-            __syncthreads();
-            const int valid = min(kInner, s1 - q0);
-            const int64_t qrow0 = (int64_t)q0 * p.H + head;
-            stage_rows(qt, QROW, (const char *)(p.q + qrow0 * 2 * D), (int64_t)p.H * ROWB, ROWB,
-                       kInner, valid);
-            stage_rows(dt, DROW, (const char *)(p.do12 + qrow0 * 4 * D), (int64_t)p.H * DROWB,
-                       DROWB, kInner, valid);
-            for (int i = threadIdx.x; i < kInner * 2; i += kThreads) {
-                const int r = i >> 1;
-                lt[i] = r < valid ? p.lse[(qrow0 + (int64_t)r * p.H) * 2 + (i & 1)] : INFINITY;
-                ddt[i] = r < valid ? p.dd[(qrow0 + (int64_t)r * p.H) * 2 + (i & 1)] : 0.f;
-            }
-            __syncthreads();
-#pragma unroll
-            for (int b = 0; b < kInner / 32; ++b) {
-                const int qb0 = q0 + 32 * b;
-                // wave-uniform: can any query of the block see a key of the wave?
-                if (qb0 >= s1 || (p.causal && qb0 + 31 < wk_first))
-                    continue;
-                // S = Q K^T (queries x keys); lane owns key wk
-                f32x16 st = f32x16{};
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    const bf16x8 qa = *(const bf16x8 *)(qt + (32 * b + n) * QROW +
-                                                        (map * D + 16 * ks + 8 * h) * 2);
-                    st = mma(qa, kf[ks], st);
-                }
-                // dP = dO V^T
-                f32x16 dp = f32x16{};
-#pragma unroll
-                for (int ks = 0; ks < NVS; ++ks) {
-                    const bf16x8 da = *(const bf16x8 *)(dt + (32 * b + n) * DROW +
-                                                        (map * 2 * D + 16 * ks + 8 * h) * 2);
-                    dp = mma(da, vf[ks], dp);
-                }
-                bf16x8 bpk[2];   // P as the B operand of dV^T, packed at once
-#pragma unroll
-                for (int a = 0; a < 16; ++a) {
-                    const int qi = 32 * b + acc_row(a, h);          // row in the tile
-                    const bool vis = !p.causal || wk <= q0 + qi;
-                    const float pv = vis ? exp2f(st[a] * c - lt[qi * 2 + map]) : 0.f;
-                    bpk[a / 8][a % 8] = (bf16)pv;
-                    st[a] = pv * (dp[a] - ddt[qi * 2 + map]);
-                }
-                // dV^T += dO^T P, dK^T += Q^T dS
-#pragma unroll
-                for (int ps = 0; ps < 2; ++ps) {
-                    const bf16x8 bp = bpk[ps];
-                    const bf16x8 bs = pack8(st, 8 * ps);
-#pragma unroll
-                    for (int db = 0; db < NVB; ++db)
-                        dva[db] = mma(trd.load(dt, DROW, 32 * b + 16 * ps,
-                                               (map * 2 * D + 32 * db) * 2),
-                                      bp, dva[db]);
-#pragma unroll
-                    for (int db = 0; db < NKB; ++db)
-                        dka[db] = mma(trq.load(qt, QROW, 32 * b + 16 * ps, (map * D + 32 * db) * 2),
-                                      bs, dka[db]);
-                }
-            }
+    Stager<ROWB, LROW, kQT> sq;
+    Stager<DROWB, DROW, kQT> sd;
+    float lv = 0.f;   // one lse or D value per thread of the first 4 kQT
+    auto fetch = [&](int stp) __attribute__((always_inline)) {
+        const int head = g * p.G + stp / nqt;
+        const int q0 = qstart + (stp % nqt) * kQT;
+        const int valid = min(kQT, s1 - q0);
+        const int64_t qrow0 = (int64_t)q0 * p.H + head;
+        sq.load((const char *)(p.q + qrow0 * 2 * D), (int64_t)p.H * ROWB, valid);
+        sd.load((const char *)(p.do12 + qrow0 * 4 * D), (int64_t)p.H * DROWB, valid);
+        const int i = threadIdx.x;
+        if (i < kQT * 4) {
+            // i = 2 * row + map for lse, kQT * 2 + that for D
+            const int which = i / (kQT * 2), j = i % (kQT * 2), r = j >> 1;
+            const float *src = which ? p.dd : p.lse;
+            lv = r < valid ? src[(qrow0 + (int64_t)r * p.H) * 2 + (j & 1)]
+                           : (which ? 0.f : INFINITY);
         }
+    };
+    auto put = [&](char *stage) __attribute__((always_inline)) {
+        sq.store(stage);
+        sd.store(stage + QB);
+        if (threadIdx.x < kQT * 4)
+            ((float *)(stage + QB + DB))[threadIdx.x] = lv;
+    };
+    auto compute = [&](int stp, const char *stage) __attribute__((always_inline)) {
+        const char *qt = stage, *dt = stage + QB;
+        const float *lt = (const float *)(stage + QB + DB), *ddt = lt + kQT * 2;
+        const int q0 = qstart + (stp % nqt) * kQT;
+        // wave-uniform: can any query of the tile see a key of the wave?
+        if (q0 >= s1 || (p.causal && q0 + kQT - 1 < wk_first))
+            return;
+        // S = Q K^T (queries x keys); lane owns key wk
+        f32x16 sa = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            const bf16x8 qa = *(const bf16x8 *)(qt + n * LROW + (map * D + 16 * ks + 8 * h) * 2);
+            sa = mma(qa, *(const bf16x8 *)(krow + (16 * ks + 8 * h) * 2), sa);
+        }
+        // dP = dO V^T
+        f32x16 dp = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < NVS; ++ks) {
+            const bf16x8 da = *(const bf16x8 *)(dt + n * DROW + (map * 2 * D + 16 * ks + 8 * h) * 2);
+            dp = mma(da, *(const bf16x8 *)(vrow + (16 * ks + 8 * h) * 2), dp);
+        }
+        bf16x8 bpk[2];   // P as the B operand of dV^T, packed at once
+#pragma unroll
+        for (int a = 0; a < 16; ++a) {
+            const int qi = acc_row(a, h);          // row in the tile
+            const bool vis = !p.causal || wk <= q0 + qi;
+            const float pv = vis ? exp2f(sa[a] * c - lt[qi * 2 + map]) : 0.f;
+            bpk[a / 8][a % 8] = (bf16)pv;
+            sa[a] = pv * (dp[a] - ddt[qi * 2 + map]);
+        }
+        // dV^T += dO^T P, dK^T += Q^T dS
+#pragma unroll
+        for (int ps = 0; ps < 2; ++ps) {
+            const bf16x8 bs = pack8(sa, 8 * ps);
+#pragma unroll
+            for (int db = 0; db < NVB; ++db)
+                dva[db] = mma(trd.load(dt, DROW, 16 * ps, (map * 2 * D + 32 * db) * 2), bpk[ps],
+                              dva[db]);
+#pragma unroll
+            for (int db = 0; db < NKB; ++db)
+                dka[db] = mma(trq.load(qt, LROW, 16 * ps, (map * D + 32 * db) * 2), bs, dka[db]);
+        }
+    };
+    auto step = [&](int stp, const char *cur, char *nxt) __attribute__((always_inline)) {
+        const bool more = stp + 1 < total;
+        if (more)
+            fetch(stp + 1);
+        compute(stp, cur);
+        if (more)
+            put(nxt);
+        __syncthreads();
+    };
+
+    fetch(0);
+    put(st0);
+    __syncthreads();
+    for (int stp = 0; stp < total; stp += 2) {
+        step(stp, st0, st1);
+        if (stp + 1 < total)
+            step(stp + 1, st1, st0);
     }
 
-    // dK of this map; dV summed over the two maps through LDS
+    // dK of this map; dV summed over the two maps through LDS (the K/V
+    // tiles are no longer read: every wave passed the last barrier)
     const float scale = rsqrtf((float)D);
     const bool kok = wk < s1;
     if (kok) {
@@ -576,10 +653,7 @@ void bwd_dkdv(BwdParams p)
                 __builtin_memcpy(dst + 32 * db + 8 * i + 4 * h, vals, sizeof(vals));
             }
     }
-    __syncthreads();
-    // map-2 waves publish dV^T (fp32) in their accumulator layout; the map-1
-    // wave of the same keys adds it and stores
-    float *xch = (float *)smem;
+    float *xch = (float *)kvt;
     if (map == 1) {
 #pragma unroll
         for (int db = 0; db < NVB; ++db)
