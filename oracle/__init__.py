@@ -74,6 +74,13 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
                       ctypes.c_int, ctypes.c_int, ctypes.c_int, f32p]
         + [f64p] * 10 + [ctypes.c_int])
     lib.diffattn_ref_bwd.restype = ctypes.c_int
+    lib.diffattn_ref_bwd_sample.argtypes = (
+        [f32p] * 7 + [ctypes.c_int64, ctypes.c_double, f32p, ctypes.c_double,
+                      ctypes.c_int, i32p, ctypes.c_int, ctypes.c_int64,
+                      ctypes.c_int, ctypes.c_int, ctypes.c_int, f32p,
+                      ctypes.c_int64, i64p, i32p, f64p,
+                      ctypes.c_int64, i64p, i32p, f64p, f64p, ctypes.c_int])
+    lib.diffattn_ref_bwd_sample.restype = ctypes.c_int
     lib.diffattn_ref_max_threads.argtypes = []
     lib.diffattn_ref_max_threads.restype = ctypes.c_int
     _lib_cache[path] = lib
@@ -275,6 +282,36 @@ def bwd(q, k, v, lq1, lk1, lq2, lk2, lambda_init_value: float, dy, w=None,
     if rc != 0:
         raise ValueError(f"diffattn_ref_bwd failed with status {rc}")
     out["aux"] = aux
+    return out
+
+
+def bwd_sample(q, k, v, lq1, lk1, lq2, lk2, lambda_init_value: float, dy,
+               rows_q, rows_k, w=None, eps: float = 1e-5, causal: bool = True,
+               cu_seqlens=None, nthreads: int = 0,
+               lib: Optional[ctypes.CDLL] = None) -> dict:
+    """Backward on a sample: ``dq`` [len(rows_q), 2, d] for rows_q = (tokens,
+    heads) and ``dk`` [len(rows_k), 2, d], ``dv`` [len(rows_k), 2d] for
+    rows_k = (key tokens, KV heads), as ``bwd`` defines them."""
+    keep, args, (T, H, d) = _common(q, k, v, lq1, lk1, lq2, lk2,
+                                    lambda_init_value, w, eps, causal,
+                                    cu_seqlens)
+    dya = _f32(dy)
+    tq = np.ascontiguousarray(np.asarray(rows_q[0], dtype=np.int64))
+    hq = np.ascontiguousarray(np.asarray(rows_q[1], dtype=np.int32))
+    tk = np.ascontiguousarray(np.asarray(rows_k[0], dtype=np.int64))
+    gk = np.ascontiguousarray(np.asarray(rows_k[1], dtype=np.int32))
+    out = {"dq": np.empty((tq.size, 2, d)), "dk": np.empty((tk.size, 2, d)),
+           "dv": np.empty((tk.size, 2 * d))}
+    rc = (lib or load()).diffattn_ref_bwd_sample(
+        *args[:-4], _ptr(dya, ctypes.c_float),
+        int(tq.size), _ptr(tq, ctypes.c_int64), _ptr(hq, ctypes.c_int32),
+        _ptr(out["dq"], ctypes.c_double),
+        int(tk.size), _ptr(tk, ctypes.c_int64), _ptr(gk, ctypes.c_int32),
+        _ptr(out["dk"], ctypes.c_double), _ptr(out["dv"], ctypes.c_double),
+        int(nthreads))
+    del keep
+    if rc != 0:
+        raise ValueError(f"diffattn_ref_bwd_sample failed with status {rc}")
     return out
 
 

@@ -642,6 +642,234 @@ int diffattn_ref_bwd(const float *q, const float *k, const float *v,
     return err;
 }
 
+/* The backward quantities of one row (token t at sequence position i of a
+ * sequence starting at token a, head h, KV head g): for both maps the
+ * natural log-sum-exp of the scaled scores over the nk visible keys, dO_m
+ * (2d each) and D_m = <dO_m, O_m>.  p is scratch of nk doubles, o of 4d. */
+static void bwd_row_stats(const float *q, const float *k, const float *v,
+                          double lam, double lambda_init, const float *w,
+                          double eps, const float *dy, int64_t t, int64_t a,
+                          int64_t nk, int h, int g, int H, int Hkv, int d,
+                          double *p, double *o, double lse[2],
+                          double *dO /* [2][2d] */, double D[2])
+{
+    const int dv2 = 2 * d;
+    const double scale = 1.0 / sqrt((double)d);
+    for (int m = 0; m < 2; ++m) {
+        const float *qr = q + ((t * H + h) * 2 + m) * (int64_t)d;
+        double mx = -INFINITY;
+        for (int64_t j = 0; j < nk; ++j) {
+            const float *kr = k + (((a + j) * Hkv + g) * 2 + m) * (int64_t)d;
+            double x = 0.0;
+            for (int c = 0; c < d; ++c)
+                x += (double)qr[c] * (double)kr[c];
+            p[j] = x * scale;
+            if (p[j] > mx)
+                mx = p[j];
+        }
+        double z = 0.0;
+        for (int64_t j = 0; j < nk; ++j)
+            z += exp(p[j] - mx);
+        lse[m] = mx + log(z);
+        double *om = o + m * dv2;
+        for (int c = 0; c < dv2; ++c)
+            om[c] = 0.0;
+        for (int64_t j = 0; j < nk; ++j) {
+            const double pj = exp(p[j] - lse[m]);
+            const float *vr = v + ((a + j) * Hkv + g) * (int64_t)dv2;
+            for (int c = 0; c < dv2; ++c)
+                om[c] += pj * (double)vr[c];
+        }
+    }
+    double ss = 0.0, gp = 0.0;
+    const float *dyr = dy + (t * H + h) * (int64_t)dv2;
+    for (int c = 0; c < dv2; ++c) {
+        const double pre = o[c] - lam * o[dv2 + c];
+        ss += pre * pre;
+    }
+    const double r = 1.0 / sqrt(ss / (double)dv2 + eps);
+    for (int c = 0; c < dv2; ++c) {
+        const double pre = o[c] - lam * o[dv2 + c];
+        gp += (double)dyr[c] * (w ? (double)w[c] : 1.0) * (1.0 - lambda_init) * pre;
+    }
+    D[0] = D[1] = 0.0;
+    for (int c = 0; c < dv2; ++c) {
+        const double pre = o[c] - lam * o[dv2 + c];
+        const double gc = (double)dyr[c] * (w ? (double)w[c] : 1.0) * (1.0 - lambda_init);
+        const double dp = r * gc - r * r * r * pre * gp / (double)dv2;
+        dO[c] = dp;
+        dO[dv2 + c] = -lam * dp;
+        D[0] += dO[c] * o[c];
+        D[1] += dO[dv2 + c] * o[dv2 + c];
+    }
+}
+
+/* Gradients on a sample, for checking full-size runs: dq of the rows
+ * (tok_q[r], head_q[r]) into dq_out[nq][2][d], and dk, dv of the key rows
+ * (tok_k[r], kvhead_k[r]) into dk_out[nk][2][d], dv_out[nk][2d]; same
+ * inputs and definitions as diffattn_ref_bwd.  A sampled key needs every
+ * row of its sequence and group that can see it; each such row's
+ * statistics are computed once and applied to all sampled keys of that
+ * (sequence, KV head).  Returns 0, -1 on malformed arguments, -2 without
+ * memory. */
+int diffattn_ref_bwd_sample(const float *q, const float *k, const float *v,
+                            const float *lq1, const float *lk1,
+                            const float *lq2, const float *lk2,
+                            int64_t lambda_stride, double lambda_init,
+                            const float *w, double eps, int causal,
+                            const int32_t *cu_seqlens, int nseq, int64_t T,
+                            int H, int Hkv, int d, const float *dy,
+                            int64_t nrq, const int64_t *tok_q,
+                            const int32_t *head_q, double *dq_out,
+                            int64_t nrk, const int64_t *tok_k,
+                            const int32_t *kvhead_k, double *dk_out,
+                            double *dv_out, int nthreads)
+{
+    if (check_args(cu_seqlens, nseq, T, H, Hkv, d) || lambda_stride < 0)
+        return -1;
+    for (int64_t r = 0; r < nrq; ++r)
+        if (tok_q[r] < 0 || tok_q[r] >= T || head_q[r] < 0 || head_q[r] >= H)
+            return -1;
+    for (int64_t r = 0; r < nrk; ++r)
+        if (tok_k[r] < 0 || tok_k[r] >= T || kvhead_k[r] < 0 || kvhead_k[r] >= Hkv)
+            return -1;
+    const int G = H / Hkv, dv2 = 2 * d;
+    const double scale = 1.0 / sqrt((double)d);
+    double *lam = malloc(sizeof(double) * (size_t)H);
+    if (!lam)
+        return -2;
+    lambda_per_head(lq1, lk1, lq2, lk2, lambda_stride, H, d, lambda_init, lam);
+    const int64_t nmax = max_len(cu_seqlens, nseq);
+#ifdef _OPENMP
+    if (nthreads <= 0)
+        nthreads = omp_get_max_threads();
+#else
+    nthreads = 1;
+#endif
+    /* per-thread accumulators of the sampled keys' dk and dv */
+    const int64_t per = nrk * (2 * d + dv2);
+    double *acc = calloc((size_t)(nthreads * per + 1), sizeof(double));
+    int err = acc ? 0 : -2;
+    /* work items: sampled query rows, then (row token, head) pairs that some
+     * sampled key needs */
+    const int64_t nitems = nrq + T * H;
+#ifdef _OPENMP
+#pragma omp parallel num_threads(nthreads)
+#endif
+    {
+#ifdef _OPENMP
+        const int tid = omp_get_thread_num();
+#else
+        const int tid = 0;
+#endif
+        double *sc = malloc(sizeof(double) * (size_t)(nmax + 4 * dv2 + 8));
+        if (!sc || !acc) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+            err = -2;
+        }
+#ifdef _OPENMP
+#pragma omp for schedule(static, 1)
+#endif
+        for (int64_t it = 0; it < nitems; ++it) {
+            if (!sc || !acc)
+                continue;
+            int64_t t;
+            int h;
+            if (it < nrq) {
+                t = tok_q[it];
+                h = head_q[it];
+            } else {
+                t = (it - nrq) / H;
+                h = (int)((it - nrq) % H);
+            }
+            const int g = h / G;
+            int s = 0;
+            while (cu_seqlens[s + 1] <= t)
+                ++s;
+            const int64_t a = cu_seqlens[s], n = cu_seqlens[s + 1] - a, i = t - a;
+            const int64_t nk = prefill_keys(causal, i, n);
+            if (it >= nrq) {
+                /* does any sampled key of this sequence and group see row i? */
+                int need = 0;
+                for (int64_t r = 0; r < nrk && !need; ++r)
+                    need = kvhead_k[r] == g && tok_k[r] >= a && tok_k[r] - a < nk;
+                if (!need)
+                    continue;
+            }
+            double *p = sc, *o = sc + nmax, *dO = o + 2 * dv2;
+            double lse[2], D[2];
+            bwd_row_stats(q, k, v, lam[h], lambda_init, w, eps, dy, t, a, nk, h, g,
+                          H, Hkv, d, p, o, lse, dO, D);
+            if (it < nrq) {
+                double *dqr = dq_out + it * 2 * (int64_t)d;
+                for (int m = 0; m < 2; ++m) {
+                    for (int c = 0; c < d; ++c)
+                        dqr[m * d + c] = 0.0;
+                    const float *qr = q + ((t * H + h) * 2 + m) * (int64_t)d;
+                    for (int64_t j = 0; j < nk; ++j) {
+                        const float *kr = k + (((a + j) * Hkv + g) * 2 + m) * (int64_t)d;
+                        const float *vr = v + ((a + j) * Hkv + g) * (int64_t)dv2;
+                        double x = 0.0, dp = 0.0;
+                        for (int c = 0; c < d; ++c)
+                            x += (double)qr[c] * (double)kr[c];
+                        for (int c = 0; c < dv2; ++c)
+                            dp += dO[m * dv2 + c] * (double)vr[c];
+                        const double ds = exp(x * scale - lse[m]) * (dp - D[m]);
+                        for (int c = 0; c < d; ++c)
+                            dqr[m * d + c] += scale * ds * (double)kr[c];
+                    }
+                }
+                continue;
+            }
+            double *my = acc + tid * per;
+            for (int64_t r = 0; r < nrk; ++r) {
+                if (kvhead_k[r] != g || tok_k[r] < a || tok_k[r] - a >= nk)
+                    continue;
+                const int64_t j = tok_k[r];
+                const float *vr = v + (j * Hkv + g) * (int64_t)dv2;
+                double *dkr = my + r * (2 * d + dv2), *dvr = dkr + 2 * d;
+                for (int m = 0; m < 2; ++m) {
+                    const float *qr = q + ((t * H + h) * 2 + m) * (int64_t)d;
+                    const float *kr = k + ((j * Hkv + g) * 2 + m) * (int64_t)d;
+                    double x = 0.0, dp = 0.0;
+                    for (int c = 0; c < d; ++c)
+                        x += (double)qr[c] * (double)kr[c];
+                    for (int c = 0; c < dv2; ++c)
+                        dp += dO[m * dv2 + c] * (double)vr[c];
+                    const double pj = exp(x * scale - lse[m]);
+                    const double ds = pj * (dp - D[m]);
+                    for (int c = 0; c < d; ++c)
+                        dkr[m * d + c] += scale * ds * (double)qr[c];
+                    for (int c = 0; c < dv2; ++c)
+                        dvr[c] += pj * dO[m * dv2 + c];
+                }
+            }
+        }
+        free(sc);
+    }
+    if (!err) {
+        for (int64_t r = 0; r < nrk; ++r) {
+            for (int c = 0; c < 2 * d; ++c) {
+                double x = 0.0;
+                for (int th = 0; th < nthreads; ++th)
+                    x += acc[th * per + r * (2 * d + dv2) + c];
+                dk_out[r * 2 * d + c] = x;
+            }
+            for (int c = 0; c < dv2; ++c) {
+                double x = 0.0;
+                for (int th = 0; th < nthreads; ++th)
+                    x += acc[th * per + r * (2 * d + dv2) + 2 * d + c];
+                dv_out[r * dv2 + c] = x;
+            }
+        }
+    }
+    free(acc);
+    free(lam);
+    return err;
+}
+
 /* Number of OpenMP threads a parallel region with nthreads <= 0 would use. */
 int diffattn_ref_max_threads(void)
 {

@@ -626,6 +626,24 @@ def pin_bwd_finite_differences(lib):
                 f"finite differences {name} causal={causal}: {fd:.8f} vs {an:.8f}"
 
 
+def pin_bwd_sample(lib):
+    """The sampling entry point equals the full backward on the sampled
+    rows and keys (only the summation order of dk, dv differs)."""
+    for causal in (True, False):
+        q, k, v, lv, w, cu = tiny_inputs(320 + causal, (13, 1, 20), 6, 2, 4)
+        dy = np.random.default_rng(321).standard_normal((34, 6, 8)).astype(np.float32)
+        full = oracle.bwd(q, k, v, *lv, 0.4, dy, w, 1e-5, causal, cu, lib=lib)
+        tq = np.array([0, 12, 13, 14, 33, 20], np.int64)
+        hq = np.array([0, 5, 3, 2, 1, 4], np.int32)
+        tk = np.array([0, 5, 12, 13, 14, 20, 33], np.int64)
+        gk = np.array([0, 1, 1, 0, 1, 0, 1], np.int32)
+        got = oracle.bwd_sample(q, k, v, *lv, 0.4, dy, (tq, hq), (tk, gk), w, 1e-5,
+                                causal, cu, lib=lib)
+        assert np.max(np.abs(got["dq"] - full["dq"][tq, hq])) < 1e-12
+        assert np.max(np.abs(got["dk"] - full["dk"][tk, gk])) < 1e-12
+        assert np.max(np.abs(got["dv"] - full["dv"][tk, gk])) < 1e-12
+
+
 # --------------------------------------------------------------------------
 # new queries against a key/value cache
 
@@ -736,6 +754,7 @@ ALL_PINS = [
     pin_rope_bf16_storage,
     pin_bwd_autograd,
     pin_bwd_finite_differences,
+    pin_bwd_sample,
     pin_kv_brute_force,
     pin_kv_sdpa,
     pin_kv_prefill_tail,

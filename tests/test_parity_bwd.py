@@ -179,3 +179,43 @@ def test_bwd_small_workspace_rejected():
     with pytest.raises(da.DiffAttnError):
         da.bwd(c(inp.q), c(inp.k), c(inp.v), *lv, 0.3, torch.zeros_like(out), lse,
                o12, workspace=torch.empty(256, dtype=torch.uint8, device=dev))
+
+
+@pytest.mark.parametrize("name", ["llama1b_b8_n4096", "long_b1_n32768"])
+def test_bwd_full_size_sampled(name):
+    """The benchmark's training-step configuration at full size: dq of
+    sampled rows and dk, dv of sampled keys against the oracle's sampling
+    entry (which recomputes every row that can see a sampled key).  Bar:
+    2e-2 of the sample's largest magnitude per tensor."""
+    import differential_attention_amd as da
+    wl = WORKLOADS[name]
+    inp = make_inputs(wl)
+    gen = torch.Generator().manual_seed(1)
+    dy = torch.randn(wl.T, wl.H, 2 * wl.d, generator=gen).to(torch.bfloat16)
+    _, (got,) = gpu_grads(inp, dy)
+    n = wl.max_seqlen
+    if wl.nseq > 1:
+        tq = np.array([0, 1, 63, 64, n - 1, n + 2047, 3 * n + 100, 7 * n + n - 1], np.int64)
+        tk = np.array([0, 1, 2047, n - 1, 7 * n, 7 * n + 3000, 7 * n + n - 1], np.int64)
+        gk = np.array([0, 0, 0, 0, 3, 3, 3], np.int32)
+    else:   # one 32768-token sequence: late keys keep the oracle's work small
+        tq = np.array([0, 127, 128, 16383, 32000, n - 1], np.int64)
+        tk = np.array([n - 700, n - 129, n - 128, n - 1], np.int64)
+        gk = np.array([1, 2, 2, 3], np.int32)
+    hq = ((np.arange(tq.size) * 5 + 3) % wl.H).astype(np.int32)
+    announce(f"{name}: full-size backward, {tq.size} dq rows, {tk.size} dk/dv keys")
+    ref = oracle.bwd_sample(inp.q, inp.k, inp.v, inp.lq1, inp.lk1, inp.lq2, inp.lk2,
+                            oracle.lambda_init(wl.depth), dy, (tq, hq), (tk, gk),
+                            inp.w, inp.eps, inp.causal, inp.cu_seqlens)
+    dev_idx = lambda a: torch.from_numpy(np.asarray(a, np.int64)).cuda()
+    sel = {"dq": got["dq"][dev_idx(tq), dev_idx(hq)],
+           "dk": got["dk"][dev_idx(tk), dev_idx(gk)],
+           "dv": got["dv"][dev_idx(tk), dev_idx(gk)]}
+    errs = {}
+    for key in ("dq", "dk", "dv"):
+        gv = sel[key].float().cpu().double().numpy()
+        assert np.all(np.isfinite(gv))
+        errs[key] = float(np.max(np.abs(gv - ref[key]))) / float(np.max(np.abs(ref[key])))
+    announce(f"{name}: " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    for key, e in errs.items():
+        assert e <= 2e-2, f"{name}: {key} relative max-abs {e:.3e}"
