@@ -57,7 +57,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kThreads = 512;   // 8 waves: 2 maps x 4 blocks of 32 rows
 constexpr int kSubs = 4;        // blocks of 32 rows per map
 constexpr int kTile = 32 * kSubs;   // queries (dq) or keys (dkdv) per workgroup
-constexpr int kInner = 64;      // keys (dq) or queries (dkdv) per staged tile
+constexpr int kInner = 64;      // keys per staged K/V tile of dq
 constexpr int kPrepPerHead = 256;  // prep waves per head (4 per workgroup)
 
 __device__ inline f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c)
