@@ -377,10 +377,12 @@ def main() -> int:
     lam0 = da.lambda_init(wl.depth)
     stream = torch.cuda.Stream(dev)
     dtype_code = da.BF16 if wl.dtype == "bf16" else da.F32
-    rope_args = (0, 0, 0)
+    rope_args = (0, 0, 0, 0, 0)
     if args.rope:
         rc, rs = (c(t) for t in workloads.rope_tables(wl.max_seqlen, wl.d))
-        rope_args = (rc.data_ptr(), rs.data_ptr(), wl.max_seqlen)
+        need = da.fwd_workspace_size(q.dtype, wl.T, wl.Hkv, wl.d, True)
+        rws = torch.empty(need, dtype=torch.uint8, device=dev)
+        rope_args = (rc.data_ptr(), rs.data_ptr(), wl.max_seqlen, rws.data_ptr(), need)
     ptrs = (dtype_code, q.data_ptr(), k.data_ptr(), v.data_ptr(),
             *[x.data_ptr() for x in lv], 0, lam0, w.data_ptr(), wl.eps,
             int(wl.causal), cu.data_ptr(), wl.nseq, wl.max_seqlen, wl.T, wl.H,

@@ -17,7 +17,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["fwd", "fwd_ptr", "fwd_kv", "fwd_kv_ptr", "kv_workspace_size",
+__all__ = ["fwd", "fwd_ptr", "fwd_workspace_size", "fwd_kv", "fwd_kv_ptr", "kv_workspace_size",
            "fwd_train", "bwd", "bwd_workspace_size", "supported_bwd",
            "lambda_init", "supported", "supported_kv", "check_cu_seqlens",
            "check_cu_seqlens_kv", "library", "LIBRARY", "DiffAttnError",
@@ -55,7 +55,9 @@ def library() -> ctypes.CDLL:
     lib.diffattn_fwd.argtypes = [
         ctypes.c_int, vp, vp, vp, f32p, f32p, f32p, f32p, i32, ctypes.c_float,
         f32p, ctypes.c_float, ctypes.c_int, i32p, i32, i32, i32, i32, i32, i32,
-        f32p, f32p, i32, vp, vp]
+        f32p, f32p, i32, vp, ctypes.c_size_t, vp, vp]
+    lib.diffattn_fwd_workspace_size.argtypes = [ctypes.c_int, i32, i32, i32, ctypes.c_int]
+    lib.diffattn_fwd_workspace_size.restype = ctypes.c_size_t
     lib.diffattn_fwd.restype = ctypes.c_int
     lib.diffattn_fwd_kv.argtypes = [
         ctypes.c_int, vp, vp, vp, f32p, f32p, f32p, f32p, i32, ctypes.c_float,
@@ -170,8 +172,8 @@ def fwd_ptr(dtype: int, q: int, k: int, v: int, lq1: int, lk1: int, lq2: int,
             lk2: int, lambda_stride: int, lambda_init_value: float,
             subln_weight: int, eps: float, causal: int, cu_seqlens: int,
             nseq: int, max_seqlen: int, T: int, H: int, Hkv: int, d: int,
-            rope_cos: int, rope_sin: int, rope_len: int, out: int,
-            stream: int) -> int:
+            rope_cos: int, rope_sin: int, rope_len: int, workspace: int,
+            workspace_bytes: int, out: int, stream: int) -> int:
     """The raw C entry point on integer device addresses; returns the
     status."""
     return library().diffattn_fwd(
@@ -179,8 +181,15 @@ def fwd_ptr(dtype: int, q: int, k: int, v: int, lq1: int, lk1: int, lq2: int,
         lq2 or None, lk2 or None, int(lambda_stride), float(lambda_init_value),
         subln_weight or None, float(eps), int(causal), cu_seqlens or None,
         int(nseq), int(max_seqlen), int(T), int(H), int(Hkv), int(d),
-        rope_cos or None, rope_sin or None, int(rope_len), out or None,
-        stream or None)
+        rope_cos or None, rope_sin or None, int(rope_len), workspace or None,
+        int(workspace_bytes), out or None, stream or None)
+
+
+def fwd_workspace_size(dtype: torch.dtype, T: int, Hkv: int, d: int,
+                       rope: bool) -> int:
+    """Bytes of workspace ``fwd`` needs (the rotated K when ``rope``)."""
+    return int(library().diffattn_fwd_workspace_size(
+        _DTYPES[dtype], int(T), int(Hkv), int(d), int(bool(rope))))
 
 
 def _dev(t: torch.Tensor, name: str, device, dtype=None) -> int:
@@ -204,7 +213,8 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         max_seqlen: Optional[int] = None, nseq: Optional[int] = None,
         out: Optional[torch.Tensor] = None,
         stream: Optional[torch.cuda.Stream] = None,
-        rope: Optional[tuple] = None) -> torch.Tensor:
+        rope: Optional[tuple] = None,
+        workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Differential-attention forward on the GPU.
 
     q [T, H, 2, d], k [T, Hkv, 2, d], v [T, Hkv, 2d] (bf16 or fp32, one
@@ -215,7 +225,9 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     length; when cu_seqlens is given without it, it is read back from the
     device (a synchronising copy).  ``rope`` = (cos, sin) fp32 device tables
     [len, d/2] applies the interleaved rotary prologue to q and k in the
-    kernel (positions restart in every sequence).  Returns ``out`` [T, H, 2d].
+    kernel (positions restart in every sequence); it needs a device uint8
+    ``workspace`` of ``fwd_workspace_size(...)`` bytes for the rotated K,
+    allocated through torch when None.  Returns ``out`` [T, H, 2d].
     """
     if q.dim() != 4 or q.shape[2] != 2:
         raise ValueError("q must be [T, H, 2, d]")
@@ -256,7 +268,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         nseq = 1 if nseq is None else int(nseq)
         if max_seqlen is None:
             max_seqlen = T // nseq if nseq > 0 else 0
-    rc_ptr = rs_ptr = rope_len = 0
+    rc_ptr = rs_ptr = rope_len = ws_ptr = ws_bytes = 0
     if rope is not None:
         rc, rs = rope
         if rc.dim() != 2 or rc.shape[1] != d // 2 or tuple(rs.shape) != tuple(rc.shape):
@@ -264,6 +276,11 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         rc_ptr = _dev(rc, "rope cos", dev, torch.float32)
         rs_ptr = _dev(rs, "rope sin", dev, torch.float32)
         rope_len = rc.shape[0]
+        if workspace is None:
+            workspace = torch.empty(max(fwd_workspace_size(q.dtype, T, Hkv, d, True), 16),
+                                    dtype=torch.uint8, device=dev)
+        ws_ptr = _dev(workspace, "workspace", dev)
+        ws_bytes = workspace.numel()
     if out is None:
         out = torch.empty((T, H, 2 * d), dtype=q.dtype, device=dev)
     elif tuple(out.shape) != (T, H, 2 * d):
@@ -276,7 +293,8 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                      args[4], args[5], args[6], lambda_stride, lambda_init,
                      w_ptr, eps,
                      int(bool(causal)), cu_ptr, nseq, max_seqlen, T, H, Hkv, d,
-                     rc_ptr, rs_ptr, rope_len, out_ptr, stream.cuda_stream)
+                     rc_ptr, rs_ptr, rope_len, ws_ptr, ws_bytes, out_ptr,
+                     stream.cuda_stream)
     if st != OK:
         raise DiffAttnError(st, "diffattn_fwd")
     return out

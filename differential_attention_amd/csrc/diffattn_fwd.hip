@@ -206,8 +206,10 @@ template <int D> struct VOperand<float, D> {
 // sequence position pos becomes (x0 c - x1 s, x0 s + x1 c) with c, s the
 // table entries at row pos, column j.  Tables are fp32 [len][d/2]; the
 // rotation runs in fp32 and rounds once to the storage type.  A 16-byte
-// chunk of a row holds whole pairs (4 for bf16, 2 for fp32), so K chunks
-// are rotated in the lane that stages them.
+// chunk of a row holds whole pairs (4 for bf16, 2 for fp32).  K is rotated
+// once per call into the caller's workspace (every query tile of a group
+// reads each K row, so rotating it while staging would repeat the work
+// per tile); Q fragments are rotated when each wave loads them.
 template <typename E> struct Rope;
 
 template <> struct Rope<bf16> {
@@ -269,6 +271,43 @@ template <> struct Rope<float> {
     }
 };
 
+// Rotates every K row once, into a copy: thread = one 16-byte chunk of a
+// (token, KV head) row (whole pairs); the token's position is its offset in
+// its sequence, found by binary search over cu_seqlens.  The prefill kernel
+// then stages the rotated copy.
+template <typename E, int D>
+__global__ __launch_bounds__(256) void rope_rotate_k(const char *k, char *kr, const int32_t *cu,
+                                                     int32_t nseq, int32_t uniform, int32_t T,
+                                                     int32_t Hkv, const float *rc, const float *rs)
+{
+    constexpr int CPR = 2 * D * (int)sizeof(E) / 16;    // chunks per (token, KV head) row
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t per_tok = (int64_t)Hkv * CPR;
+    const int t = (int)(idx / per_tok);
+    if (t >= T)
+        return;
+    int s0;
+    if (cu) {
+        int lo = 0, hi = nseq;   // last sequence with cu[s] <= t
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (cu[mid] <= t)
+                lo = mid;
+            else
+                hi = mid;
+        }
+        s0 = cu[lo];
+    } else {
+        s0 = (t / uniform) * uniform;
+    }
+    const int c = (int)(idx % CPR);
+    // pair index of the chunk's first element within its d-wide half-head
+    const int j = ((c * 16 / (int)sizeof(E)) % D) / 2;
+    const int64_t off = idx * 16;
+    const u32x4 x = *(const u32x4 *)(k + off);
+    *(u32x4 *)(kr + off) = Rope<E>::rotate(x, Rope<E>::coef(rc, rs, t - s0, j, D));
+}
+
 struct Params {
     const void *q;
     const void *k;
@@ -279,6 +318,8 @@ struct Params {
     const float *w;
     const int32_t *cu;
     const float *rcos, *rsin;   // rotary tables [len][d/2], or NULL
+    const void *k_orig;         // unrotated K when rcos is set (k is then its rotated copy)
+    int32_t max_seqlen;
     float *lse;                 // training forward: [T][H][2] log2-sum-exp, or NULL
     float *o12;                 // training forward: [T][H][2][2d] normalised O_m
     float lambda_init;
@@ -396,10 +437,6 @@ void diffattn_fwd_kernel(Params p)
     const int kdst = lrow * GEO::KROWB + lcol;
     const int vdst = GEO::KTILEB + lrow * GEO::VROWB + lcol;
     u32x4 kst[MAXL], vst[MAXL];
-    // rotary: the cos / sin of the pairs in this lane's K chunk (ROPE only)
-    typename Rope<E>::Coef kcs[MAXL];
-    // rotary pair index of this lane's chunk start within its half-head
-    const int kpair = ((lcol / (int)sizeof(E)) % D) / 2;
     // global -> registers: this wave's loads of block slice b of the tile at k0
     auto stage_load = [&](int k0, int b) __attribute__((always_inline)) {
         const bool tail = k0 + GEO::BN > s1;
@@ -411,18 +448,13 @@ void diffattn_fwd_kernel(Params p)
             const int64_t off = (int64_t)key * rowstride;
             kst[i - b * LPW / GEO::NB] = *(const u32x4 *)(kbytes + off);
             vst[i - b * LPW / GEO::NB] = *(const u32x4 *)(vbytes + off);
-            if constexpr (ROPE)
-                kcs[i - b * LPW / GEO::NB] = Rope<E>::coef(p.rcos, p.rsin, key - s0, kpair, D);
         }
     };
-    // registers -> LDS stage (rotating K on the way when ROPE)
+    // registers -> LDS stage
     auto stage_store = [&](char *stage, int b) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = b * LPW / GEO::NB; i < (b + 1) * LPW / GEO::NB; ++i) {
-            u32x4 kv = kst[i - b * LPW / GEO::NB];
-            if constexpr (ROPE)
-                kv = Rope<E>::rotate(kv, kcs[i - b * LPW / GEO::NB]);
-            *(u32x4 *)(stage + kdst + i * kWaves * RPL * GEO::KROWB) = kv;
+            *(u32x4 *)(stage + kdst + i * kWaves * RPL * GEO::KROWB) = kst[i - b * LPW / GEO::NB];
             *(u32x4 *)(stage + vdst + i * kWaves * RPL * GEO::VROWB) = vst[i - b * LPW / GEO::NB];
         }
     };
@@ -687,6 +719,13 @@ void diffattn_fwd_kernel(Params p)
 template <typename E, int D>
 int launch(const Params &p, int nblocks, hipStream_t stream)
 {
+    if (p.rcos) {
+        // K rotated once into the workspace, which the kernel then reads as K
+        const int64_t chunks = (int64_t)p.T * p.Hkv * (2 * D * (int)sizeof(E) / 16);
+        hipLaunchKernelGGL((rope_rotate_k<E, D>), dim3((unsigned)((chunks + 255) / 256)),
+                           dim3(256), 0, stream, (const char *)p.k_orig, (char *)p.k, p.cu,
+                           p.nseq, p.seqlen_uniform, p.T, p.Hkv, p.rcos, p.rsin);
+    }
     if (p.rcos)
         hipLaunchKernelGGL((diffattn_fwd_kernel<E, D, true>), dim3(nblocks), dim3(kThreads), 0,
                            stream, p);
@@ -759,7 +798,8 @@ int fwd_impl(int dtype, const void *q, const void *k, const void *v,
              int causal, const int32_t *cu_seqlens, int32_t nseq,
              int32_t max_seqlen, int32_t T, int32_t H, int32_t Hkv,
              int32_t d, const float *rope_cos, const float *rope_sin,
-             int32_t rope_len, float *lse, float *o12, void *out, void *stream)
+             int32_t rope_len, void *workspace, size_t workspace_bytes, float *lse,
+             float *o12, void *out, void *stream)
 {
     if (dtype != DIFFATTN_BF16 && dtype != DIFFATTN_F32)
         return DIFFATTN_EINVAL;
@@ -798,9 +838,13 @@ int fwd_impl(int dtype, const void *q, const void *k, const void *v,
     } else if (max_seqlen < 1 || max_seqlen > T) {
         return DIFFATTN_EINVAL;
     }
-    // rotary tables cover every position and are read in 16-byte vectors
+    // rotary tables cover every position and are read in 16-byte vectors;
+    // the workspace holds the rotated copy of K
     if (rope_cos && (rope_len < max_seqlen ||
                      ((uintptr_t)rope_cos | (uintptr_t)rope_sin) % 16 != 0))
+        return DIFFATTN_EINVAL;
+    if (rope_cos && (!workspace || (uintptr_t)workspace % 16 != 0 ||
+                     workspace_bytes < diffattn_fwd_workspace_size(dtype, T, Hkv, d, 1)))
         return DIFFATTN_EINVAL;
     // byte offsets of K/V rows are formed in 64 bits; the grid in 32 bits
     const int G = H / Hkv;
@@ -813,7 +857,8 @@ int fwd_impl(int dtype, const void *q, const void *k, const void *v,
 
     Params p;
     p.q = q;
-    p.k = k;
+    p.k = rope_cos ? workspace : k;
+    p.k_orig = k;
     p.v = v;
     p.out = out;
     p.lq1 = lambda_q1;
@@ -836,6 +881,7 @@ int fwd_impl(int dtype, const void *q, const void *k, const void *v,
     p.seqlen_uniform = uniform;
     p.causal = causal;
     p.ntile_q = (int32_t)ntile_q;
+    p.max_seqlen = max_seqlen;
     p.hpw = hpw;
     p.hblocks = G / hpw;
 
@@ -857,12 +903,21 @@ int diffattn_fwd(int dtype, const void *q, const void *k, const void *v,
                  int causal, const int32_t *cu_seqlens, int32_t nseq,
                  int32_t max_seqlen, int32_t T, int32_t H, int32_t Hkv,
                  int32_t d, const float *rope_cos, const float *rope_sin,
-                 int32_t rope_len, void *out, void *stream)
+                 int32_t rope_len, void *workspace, size_t workspace_bytes,
+                 void *out, void *stream)
 {
     return fwd_impl(dtype, q, k, v, lambda_q1, lambda_k1, lambda_q2, lambda_k2,
                     lambda_stride, lambda_init, subln_weight, eps, causal, cu_seqlens,
                     nseq, max_seqlen, T, H, Hkv, d, rope_cos, rope_sin, rope_len,
-                    nullptr, nullptr, out, stream);
+                    workspace, workspace_bytes, nullptr, nullptr, out, stream);
+}
+
+size_t diffattn_fwd_workspace_size(int dtype, int32_t T, int32_t Hkv, int32_t d, int rope)
+{
+    if (!rope || T <= 0 || Hkv < 1 || d < 1)
+        return 0;
+    const size_t es = dtype == DIFFATTN_F32 ? 4 : 2;
+    return ((size_t)T * Hkv * 2 * d * es + 255) & ~(size_t)255;
 }
 
 int diffattn_fwd_train(int dtype, const void *q, const void *k, const void *v,
@@ -878,8 +933,8 @@ int diffattn_fwd_train(int dtype, const void *q, const void *k, const void *v,
         return DIFFATTN_EINVAL;
     return fwd_impl(dtype, q, k, v, lambda_q1, lambda_k1, lambda_q2, lambda_k2,
                     lambda_stride, lambda_init, subln_weight, eps, causal, cu_seqlens,
-                    nseq, max_seqlen, T, H, Hkv, d, nullptr, nullptr, 0, lse, o12, out,
-                    stream);
+                    nseq, max_seqlen, T, H, Hkv, d, nullptr, nullptr, 0, nullptr, 0, lse,
+                    o12, out, stream);
 }
 
 } // extern "C"

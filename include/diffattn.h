@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define DIFFATTN_ABI_VERSION 5
+#define DIFFATTN_ABI_VERSION 6
 
 enum diffattn_status {
     DIFFATTN_OK = 0,
@@ -99,6 +99,13 @@ enum diffattn_dtype {
  *                s = rope_sin[p, j]; computed in fp32, rounded once to the
  *                storage type.  V is not rotated.
  *   rope_len     rows of the tables; >= max_seqlen when they are given.
+ *   workspace, workspace_bytes
+ *                with rotary tables: device scratch of at least
+ *                diffattn_fwd_workspace_size(dtype, T, Hkv, d, 1) bytes,
+ *                16-byte aligned, owned by the caller, holding the rotated
+ *                copy of k during the call (no initialisation needed; calls
+ *                in flight at once need separate workspaces).  Without
+ *                tables it is not used (NULL, 0).
  *   out          device output [T, H, 2d], same element type as q.
  *   stream       a hipStream_t, or NULL for the null stream.
  *
@@ -113,7 +120,13 @@ int diffattn_fwd(int dtype, const void *q, const void *k, const void *v,
                  int causal, const int32_t *cu_seqlens, int32_t nseq,
                  int32_t max_seqlen, int32_t T, int32_t H, int32_t Hkv,
                  int32_t d, const float *rope_cos, const float *rope_sin,
-                 int32_t rope_len, void *out, void *stream);
+                 int32_t rope_len, void *workspace, size_t workspace_bytes,
+                 void *out, void *stream);
+
+/* Bytes of workspace diffattn_fwd needs: the rotated copy of k when rope
+ * (rotary tables given) is nonzero, else 0.  Host function. */
+size_t diffattn_fwd_workspace_size(int dtype, int32_t T, int32_t Hkv, int32_t d,
+                                   int rope);
 
 /*
  * New queries against a key/value cache (decoding), asynchronous on

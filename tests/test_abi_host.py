@@ -47,6 +47,13 @@ def test_lambda_init_schedule():
     assert abs(da.lambda_init(10 ** 6) - 0.8) < 1e-15
 
 
+def test_fwd_workspace_size():
+    import torch
+    assert da.fwd_workspace_size(torch.bfloat16, 64, 4, 64, False) == 0
+    assert da.fwd_workspace_size(torch.bfloat16, 64, 4, 64, True) >= 64 * 4 * 128 * 2
+    assert da.fwd_workspace_size(torch.float32, 64, 4, 64, True) >= 64 * 4 * 128 * 4
+
+
 def test_supported():
     import torch
     assert da.supported(torch.bfloat16, 64)
@@ -67,8 +74,8 @@ def call(**over):
              lq2=FAKE, lk2=FAKE, lambda_stride=0, lambda_init_value=0.2,
              subln_weight=0,
              eps=1e-5, causal=1, cu_seqlens=0, nseq=2, max_seqlen=0, T=64,
-             H=16, Hkv=4, d=64, rope_cos=0, rope_sin=0, rope_len=0, out=FAKE,
-             stream=0)
+             H=16, Hkv=4, d=64, rope_cos=0, rope_sin=0, rope_len=0,
+             workspace=0, workspace_bytes=0, out=FAKE, stream=0)
     a.update(over)
     return da.fwd_ptr(**a)
 
@@ -96,8 +103,13 @@ def call(**over):
     (dict(cu_seqlens=FAKE, max_seqlen=0), da.EINVAL),
     (dict(cu_seqlens=FAKE, max_seqlen=65), da.EINVAL),
     (dict(rope_cos=FAKE, rope_len=32), da.EINVAL),               # sin missing
-    (dict(rope_cos=FAKE, rope_sin=FAKE, rope_len=31), da.EINVAL),  # < max_seqlen
-    (dict(rope_cos=FAKE + 8, rope_sin=FAKE, rope_len=32), da.EINVAL),  # alignment
+    (dict(rope_cos=FAKE, rope_sin=FAKE, rope_len=31, workspace=FAKE,
+          workspace_bytes=1 << 20), da.EINVAL),                     # < max_seqlen
+    (dict(rope_cos=FAKE + 8, rope_sin=FAKE, rope_len=32, workspace=FAKE,
+          workspace_bytes=1 << 20), da.EINVAL),                     # alignment
+    (dict(rope_cos=FAKE, rope_sin=FAKE, rope_len=32), da.EINVAL),   # no workspace
+    (dict(rope_cos=FAKE, rope_sin=FAKE, rope_len=32, workspace=FAKE,
+          workspace_bytes=100), da.EINVAL),                         # workspace too small
     (dict(T=0, q=0, k=0, v=0, out=0), da.OK),  # empty: nothing launched
 ])
 def test_validation_before_any_device_work(over, status):
