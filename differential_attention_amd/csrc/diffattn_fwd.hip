@@ -43,10 +43,13 @@
 // (fp32).
 //
 // Softmax uses a lazily updated running maximum: probabilities are taken
-// against the stored maximum as long as no score of the block exceeds it by
-// more than 2^8 in probability; only then (in practice on the first block)
-// the maximum, the sum and the accumulator are rescaled.  The result O/l
-// does not depend on which maximum was used.
+// against the stored maximum as long as none of the block exceeds 2^8; only
+// then (in practice on the first block) the maximum, the sum and the
+// accumulator are rescaled.  The result O/l does not depend on which maximum
+// was used.  For bf16 the block's probabilities are computed first and their
+// sum serves both as the row-sum update and as the test: every probability
+// is at most the sum, so no per-block row maximum is needed on the common
+// path.
 //
 // The epilogue is fused: lambda (from the four vectors), O_1/l_1 -
 // lambda O_2/l_2, the RMSNorm over 2d (in-lane sums plus one cross-half
@@ -77,6 +80,7 @@ constexpr int kSub = 2;   // 32-query sub-blocks per wave
 constexpr int kQB = 32 * kSub;   // query rows per slot
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleLog2 = 8.0f;   // lazy-max threshold, log2 units
+constexpr float kRescaleSum = 256.0f;  // the same threshold as a probability
 
 // ---------------------------------------------------------------------------
 // LDS tile geometry.  A K tile is [64 keys][2d] (K1 then K2 of each key), a
@@ -122,6 +126,14 @@ template <> struct Mfma<bf16> {
             f[e] = (bf16)s[a0 + e];
         return f;
     }
+    __device__ static inline Frag pack(const float *s, int a0)
+    {
+        Frag f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            f[e] = (bf16)s[a0 + e];
+        return f;
+    }
 };
 
 template <> struct Mfma<float> {
@@ -132,6 +144,7 @@ template <> struct Mfma<float> {
         return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
     }
     __device__ static inline Frag pack(const f32x16 &s, int a0) { return s[a0]; }
+    __device__ static inline Frag pack(const float *s, int a0) { return s[a0]; }
 };
 
 // Row (key offset inside a 32-key block) of accumulator element a of a lane
@@ -550,12 +563,13 @@ void diffattn_fwd_kernel(Params p)
             Frag pf[kSub][NPS];
 #pragma unroll
             for (int u = 0; u < kSub; ++u) {
-                float pm = -INFINITY;
+                // the row maximum of the block, then a raised running maximum
+                // with the sum and accumulator rescaled to it
+                auto raise = [&]() __attribute__((always_inline)) {
+                    float pm = -INFINITY;
 #pragma unroll
-                for (int a = 0; a < 16; ++a)
-                    pm = fmaxf(pm, sc[u][a]);
-                const bool grow = (pm - m_run[u]) * c > kRescaleLog2;
-                if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+                    for (int a = 0; a < 16; ++a)
+                        pm = fmaxf(pm, sc[u][a]);
                     const float mnew = fmaxf(m_run[u], pair_max(pm));
                     // nothing accumulated yet when m_run is still -inf
                     const float alpha = m_run[u] == -INFINITY
@@ -566,19 +580,59 @@ void diffattn_fwd_kernel(Params p)
 #pragma unroll
                     for (int db = 0; db < NDB; ++db)
                         o[u][db] *= alpha;
-                }
-                const float mc = m_run[u] * c;
-                float ps_sum[4] = {0.f, 0.f, 0.f, 0.f};
+                };
+                // probabilities against the stored maximum, packed as the
+                // B operand of the PV product; returns their fp32 sum
+                auto probs = [&]() __attribute__((always_inline)) {
+                    const float mc = m_run[u] * c;
+                    float pv[16];
 #pragma unroll
-                for (int a = 0; a < 16; ++a) {
-                    const float pv = __builtin_amdgcn_exp2f(fmaf(sc[u][a], c, -mc));
-                    sc[u][a] = pv;
-                    ps_sum[a & 3] += pv;
-                }
-                l_run[u] += (ps_sum[0] + ps_sum[1]) + (ps_sum[2] + ps_sum[3]);
+                    for (int a = 0; a < 16; ++a)
+                        pv[a] = __builtin_amdgcn_exp2f(fmaf(sc[u][a], c, -mc));
 #pragma unroll
-                for (int ps = 0; ps < NPS; ++ps)
-                    pf[u][ps] = M::pack(sc[u], ps * VEC);
+                    for (int ps = 0; ps < NPS; ++ps)
+                        pf[u][ps] = M::pack(pv, ps * VEC);
+                    float s4[4] = {pv[0], pv[1], pv[2], pv[3]};
+#pragma unroll
+                    for (int a = 4; a < 16; ++a)
+                        s4[a & 3] += pv[a];
+                    return (s4[0] + s4[1]) + (s4[2] + s4[3]);
+                };
+                if constexpr (VEC == 8) {
+                    // Probabilities against the stored maximum first; their
+                    // sum bounds each of them, so a sum within 2^8 means none
+                    // exceeded the lazy threshold.  A larger, infinite or NaN
+                    // sum (a raised maximum, or the first block against -inf)
+                    // takes the slow path: raise the maximum and recompute.
+                    // (The sum is of the fp32 probabilities: a row sum of
+                    // their bf16 roundings is measurably less accurate.)
+                    float bsum = probs();
+                    if (__builtin_amdgcn_ballot_w64(!(bsum <= kRescaleSum)) != 0) {
+                        raise();
+                        bsum = probs();
+                    }
+                    l_run[u] += bsum;
+                } else {
+                    float pm = -INFINITY;
+#pragma unroll
+                    for (int a = 0; a < 16; ++a)
+                        pm = fmaxf(pm, sc[u][a]);
+                    const bool grow = (pm - m_run[u]) * c > kRescaleLog2;
+                    if (__builtin_amdgcn_ballot_w64(grow) != 0)
+                        raise();
+                    const float mc = m_run[u] * c;
+                    float ps_sum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int a = 0; a < 16; ++a) {
+                        const float pv = __builtin_amdgcn_exp2f(fmaf(sc[u][a], c, -mc));
+                        sc[u][a] = pv;
+                        ps_sum[a & 3] += pv;
+                    }
+                    l_run[u] += (ps_sum[0] + ps_sum[1]) + (ps_sum[2] + ps_sum[3]);
+#pragma unroll
+                    for (int ps = 0; ps < NPS; ++ps)
+                        pf[u][ps] = M::pack(sc[u], ps * VEC);
+                }
             }
 
             // ---- O^T += V^T P^T ---------------------------------------------
