@@ -428,12 +428,21 @@ void bwd_dq(BwdParams p)
                 const bf16x8 va = *(const bf16x8 *)(vt + (32 * b + n) * LROW + (16 * ks + 8 * h) * 2);
                 dp = mma(va, df[ks], dp);
             }
-            // P^T and dS^T; lane owns query wq, element a is key kb0 + acc_row(a, h)
+            // P^T and dS^T; lane owns query wq, element a is key kb0 + acc_row(a, h).
+            // Keys past the sequence or after the query get a score of -inf
+            // (probability 0); wave-uniform: only blocks that reach the end of
+            // the sequence or the diagonal need the test.
+            if (kb0 + 32 > s1 || (p.causal && kb0 + 31 > q0 + 32 * sub)) {
+#pragma unroll
+                for (int a = 0; a < 16; ++a) {
+                    const int key = kb0 + acc_row(a, h);
+                    if (!(key < s1 && (!p.causal || key <= wq)))
+                        sa[a] = -INFINITY;
+                }
+            }
 #pragma unroll
             for (int a = 0; a < 16; ++a) {
-                const int key = kb0 + acc_row(a, h);
-                const bool vis = key < s1 && (!p.causal || key <= wq);
-                const float pv = vis ? exp2f(sa[a] * c - lse) : 0.f;
+                const float pv = __builtin_amdgcn_exp2f(fmaf(sa[a], c, -lse));
                 sa[a] = pv * (dp[a] - dval);
             }
             // dQ^T += K^T dS^T
@@ -557,6 +566,8 @@ void bwd_dkdv(BwdParams p)
 
     Stager<ROWB, LQROW, kQT> sq;
     Stager<DROWB, DROW, kQT> sd;
+    // lse and D of the tile as [lse, D][map][row], so that the four rows
+    // a lane's accumulator elements cover are one 16-byte read
     float lv = 0.f;   // one lse or D value per thread of the first 4 kQT
     auto fetch = [&](int stp) __attribute__((always_inline)) {
         const int head = g * p.G + stp / nqt;
@@ -567,10 +578,10 @@ void bwd_dkdv(BwdParams p)
         sd.load((const char *)(p.do12 + qrow0 * 4 * D), (int64_t)p.H * DROWB, valid);
         const int i = threadIdx.x;
         if (i < kQT * 4) {
-            // i = 2 * row + map for lse, kQT * 2 + that for D
-            const int which = i / (kQT * 2), j = i % (kQT * 2), r = j >> 1;
+            // i = (which * 2 + map) * kQT + row; which 0: lse, 1: D
+            const int which = i / (kQT * 2), mp = (i / kQT) & 1, r = i % kQT;
             const float *src = which ? p.dd : p.lse;
-            lv = r < valid ? src[(qrow0 + (int64_t)r * p.H) * 2 + (j & 1)]
+            lv = r < valid ? src[(qrow0 + (int64_t)r * p.H) * 2 + mp]
                            : (which ? 0.f : INFINITY);
         }
     };
@@ -582,7 +593,8 @@ void bwd_dkdv(BwdParams p)
     };
     auto compute = [&](int stp, const char *stage) __attribute__((always_inline)) {
         const char *qt = stage, *dt = stage + QB;
-        const float *lt = (const float *)(stage + QB + DB), *ddt = lt + kQT * 2;
+        const float *lt = (const float *)(stage + QB + DB) + map * kQT;
+        const float *ddt = lt + kQT * 2;
         const int q0 = qstart + (stp % nqt) * kQT;
         // wave-uniform: can any query of the tile see a key of the wave?
         if (q0 >= s1 || (p.causal && q0 + kQT - 1 < wk_first))
@@ -602,13 +614,28 @@ void bwd_dkdv(BwdParams p)
             dp = mma(da, *(const bf16x8 *)(vrow + (16 * ks + 8 * h) * 2), dp);
         }
         bf16x8 bpk[2];   // P as the B operand of dV^T, packed at once
+        // queries before the wave's key get a score of -inf (probability 0);
+        // wave-uniform: only tiles that reach the diagonal need the test
+        if (p.causal && q0 < wk_first + 31) {
 #pragma unroll
-        for (int a = 0; a < 16; ++a) {
-            const int qi = acc_row(a, h);          // row in the tile
-            const bool vis = !p.causal || wk <= q0 + qi;
-            const float pv = vis ? exp2f(sa[a] * c - lt[qi * 2 + map]) : 0.f;
-            bpk[a / 8][a % 8] = (bf16)pv;
-            sa[a] = pv * (dp[a] - ddt[qi * 2 + map]);
+            for (int a = 0; a < 16; ++a)
+                if (wk > q0 + acc_row(a, h))
+                    sa[a] = -INFINITY;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            // rows 8 j + 4 h .. + 3 of the tile
+            const float4 l4 = *(const float4 *)(lt + 8 * j + 4 * h);
+            const float4 d4 = *(const float4 *)(ddt + 8 * j + 4 * h);
+            const float lr[4] = {l4.x, l4.y, l4.z, l4.w};
+            const float dr[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int a = 4 * j + e;
+                const float pv = __builtin_amdgcn_exp2f(fmaf(sa[a], c, -lr[e]));
+                bpk[a / 8][a % 8] = (bf16)pv;
+                sa[a] = pv * (dp[a] - dr[e]);
+            }
         }
         // dV^T += dO^T P, dK^T += Q^T dS
 #pragma unroll

@@ -370,7 +370,7 @@ void diffattn_fwd_kernel(Params p)
     __shared__ __attribute__((aligned(1024))) char stage1[GEO::STAGEB];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int lane = tid & 63;
     const int n = lane & 31;           // query column owned by this lane
     const int h = lane >> 5;           // lane half
