@@ -158,15 +158,63 @@ __device__ inline float head_lambda(const BwdParams &p, int h, int lane, int D)
 // ---------------------------------------------------------------------------
 // prep: RMSNorm / combine backward per row, D_m, partial weight and lambda
 // gradients.  Wave w serves head w % H and tokens w / H, w / H + nper, ...
+// Sum over the 16 lanes of a row group (lanes 16 r .. 16 r + 15).
+__device__ inline float seg16_sum(float x)
+{
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1)
+        x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+// N consecutive floats / bf16 values of a row, in 16-, 8- or 4-byte pieces.
+template <int N> __device__ inline void load_f32(float (&x)[N], const float *src)
+{
+    if constexpr (N % 4 == 0) {
+#pragma unroll
+        for (int k = 0; k < N / 4; ++k) {
+            const float4 v = *(const float4 *)(src + 4 * k);
+            x[4 * k] = v.x, x[4 * k + 1] = v.y, x[4 * k + 2] = v.z, x[4 * k + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < N / 2; ++k) {
+            const float2 v = *(const float2 *)(src + 2 * k);
+            x[2 * k] = v.x, x[2 * k + 1] = v.y;
+        }
+    }
+}
+template <int N> __device__ inline void load_bf16(float (&x)[N], const bf16 *src)
+{
+    typedef __bf16 bv __attribute__((ext_vector_type(N)));
+    const bv v = *(const bv *)src;
+#pragma unroll
+    for (int k = 0; k < N; ++k)
+        x[k] = (float)v[k];
+}
+template <int N> __device__ inline void store_bf16(bf16 *dst, const bf16 (&x)[N])
+{
+    typedef __bf16 bv __attribute__((ext_vector_type(N)));
+    bv v;
+#pragma unroll
+    for (int k = 0; k < N; ++k)
+        v[k] = x[k];
+    *(bv *)dst = v;
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep(BwdParams p)
 {
-    constexpr int CPL = 2 * D / 64;   // columns per lane
+    // a wave takes four (token, head) rows at a time, 16 lanes per row and
+    // CPL consecutive columns per lane, so every load and store is 8 to 32
+    // bytes wide and the row sums are 16-lane reductions
+    constexpr int CPL = 2 * D / 16;   // columns per lane
     __shared__ float red_dw[4][2 * D];
     __shared__ float red_dl[4];
     const int lane = threadIdx.x & 63, wv4 = threadIdx.x >> 6;
+    const int sub = lane >> 4, l16 = lane & 15;
     // the four waves of a workgroup serve one head: wave w of the head takes
-    // tokens w, w + kPrepPerHead, ...
+    // the row groups w, w + kPrepPerHead, ... (tokens 4 g .. 4 g + 3)
     const int h = blockIdx.x % p.H;
     const int wid = (blockIdx.x / p.H) * 4 + wv4;   // wave index within the head
     const float lam = head_lambda(p, h, lane, D);
@@ -174,56 +222,75 @@ __global__ __launch_bounds__(256) void bwd_prep(BwdParams p)
     float wv[CPL], dwp[CPL];
 #pragma unroll
     for (int cc = 0; cc < CPL; ++cc) {
-        wv[cc] = p.w ? p.w[CPL * lane + cc] : 1.f;
+        wv[cc] = p.w ? p.w[CPL * l16 + cc] : 1.f;
         dwp[cc] = 0.f;
     }
     float dlp = 0.f;
-    for (int t = wid; t < p.T; t += kPrepPerHead) {
-        const int64_t row = (int64_t)t * p.H + h;
-        const float *o1 = p.o12 + row * 2 * (2 * D) + CPL * lane;
-        const float *o2 = o1 + 2 * D;
-        const bf16 *dyr = p.dy + row * (2 * D) + CPL * lane;
-        float pre[CPL], g[CPL], a1[CPL], a2[CPL];
+    for (int g0 = 4 * wid; g0 < p.T; g0 += 4 * kPrepPerHead) {
+        const int t = g0 + sub;
+        const bool ok = t < p.T;
+        const int64_t row = (int64_t)(ok ? t : 0) * p.H + h;
+        float a1[CPL], a2[CPL], dyv[CPL];
+        if (ok) {
+            const float *o1 = p.o12 + row * 2 * (2 * D) + CPL * l16;
+            load_f32(a1, o1);
+            load_f32(a2, o1 + 2 * D);
+            load_bf16(dyv, p.dy + row * (2 * D) + CPL * l16);
+        } else {
+#pragma unroll
+            for (int cc = 0; cc < CPL; ++cc)
+                a1[cc] = a2[cc] = dyv[cc] = 0.f;
+        }
+        float pre[CPL], g[CPL];
         float ss = 0.f, gp = 0.f;
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc) {
-            a1[cc] = o1[cc];
-            a2[cc] = o2[cc];
             pre[cc] = a1[cc] - lam * a2[cc];
             ss += pre[cc] * pre[cc];
-            g[cc] = (float)dyr[cc] * wv[cc] * sc;
+            g[cc] = dyv[cc] * wv[cc] * sc;
             gp += g[cc] * pre[cc];
         }
-        ss = wave_sum(ss);
-        gp = wave_sum(gp);
+        ss = seg16_sum(ss);
+        gp = seg16_sum(gp);
         const float r = rsqrtf(ss / (float)(2 * D) + p.eps);
         const float r3 = r * r * r * gp / (float)(2 * D);
         float d1 = 0.f, d2 = 0.f;
-        bf16 *do1 = p.do12 + row * 2 * (2 * D) + CPL * lane;
-        bf16 *do2 = do1 + 2 * D;
+        bf16 b1[CPL], b2[CPL];
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc) {
             const float dpre = r * g[cc] - r3 * pre[cc];
-            const bf16 b1 = (bf16)dpre, b2 = (bf16)(-lam * dpre);
-            do1[cc] = b1;
-            do2[cc] = b2;
-            d1 += (float)b1 * a1[cc];
-            d2 += (float)b2 * a2[cc];
+            b1[cc] = (bf16)dpre;
+            b2[cc] = (bf16)(-lam * dpre);
+            d1 += (float)b1[cc] * a1[cc];
+            d2 += (float)b2[cc] * a2[cc];
             dlp -= dpre * a2[cc];
-            dwp[cc] += (float)dyr[cc] * pre[cc] * r * sc;
+            dwp[cc] += dyv[cc] * pre[cc] * r * sc;
         }
-        d1 = wave_sum(d1);
-        d2 = wave_sum(d2);
-        if (lane == 0) {
-            p.dd[row * 2] = d1;
-            p.dd[row * 2 + 1] = d2;
+        d1 = seg16_sum(d1);
+        d2 = seg16_sum(d2);
+        if (ok) {
+            bf16 *do1 = p.do12 + row * 2 * (2 * D) + CPL * l16;
+            store_bf16(do1, b1);
+            store_bf16(do1 + 2 * D, b2);
+            if (l16 == 0) {
+                p.dd[row * 2] = d1;
+                p.dd[row * 2 + 1] = d2;
+            }
         }
     }
-    // the workgroup's four waves summed in a fixed order, one partial per
-    // workgroup: part[blockIdx.x] (head h = blockIdx.x % H)
+    // the wave's four row groups, then the workgroup's four waves, summed in
+    // a fixed order: one partial per workgroup, part[blockIdx.x] (head h =
+    // blockIdx.x % H)
 #pragma unroll
-    for (int cc = 0; cc < CPL; ++cc)
-        red_dw[wv4][CPL * lane + cc] = dwp[cc];
+    for (int cc = 0; cc < CPL; ++cc) {
+        dwp[cc] += __shfl_xor(dwp[cc], 16, 64);
+        dwp[cc] += __shfl_xor(dwp[cc], 32, 64);
+    }
+    if (sub == 0) {
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc)
+            red_dw[wv4][CPL * l16 + cc] = dwp[cc];
+    }
     dlp = wave_sum(dlp);
     if (lane == 0)
         red_dl[wv4] = dlp;
@@ -562,6 +629,9 @@ void bwd_dkdv(BwdParams p)
     const int nqt = (s1 - qstart + kQT - 1) / kQT;   // query tiles per head
     const int total = p.G * nqt;                     // (head, query tile) steps
     const char *krow = kvt + (32 * sub + n) * LROW + map * D * 2;
+    // this wave's K rows (B operand of S = Q K^T), read into registers once
+    // the tile is in LDS
+    bf16x8 kf[NKS];
     const char *vrow = kvt + KVB + (32 * sub + n) * LROW;
 
     Stager<ROWB, LQROW, kQT> sq;
@@ -604,7 +674,7 @@ void bwd_dkdv(BwdParams p)
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             const bf16x8 qa = *(const bf16x8 *)(qt + n * LQROW + (map * D + 16 * ks + 8 * h) * 2);
-            sa = mma(qa, *(const bf16x8 *)(krow + (16 * ks + 8 * h) * 2), sa);
+            sa = mma(qa, kf[ks], sa);
         }
         // dP = dO V^T
         f32x16 dp = f32x16{};
@@ -663,6 +733,9 @@ void bwd_dkdv(BwdParams p)
     fetch(0);
     put(st0);
     __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+        kf[ks] = *(const bf16x8 *)(krow + (16 * ks + 8 * h) * 2);
     for (int stp = 0; stp < total; stp += 2) {
         step(stp, st0, st1);
         if (stp + 1 < total)
