@@ -54,7 +54,8 @@
 // The epilogue is fused: lambda (from the four vectors), O_1/l_1 -
 // lambda O_2/l_2, the RMSNorm over 2d (in-lane sums plus one cross-half
 // exchange), the weight, the (1 - lambda_init) scale and the rounding
-// store.  Causal tiles above the diagonal are never visited; on the
+// store.  The two waves of a slot share it, one 32-query sub-block each,
+// and bf16 rows leave through LDS as whole 256-byte rows.  Causal tiles above the diagonal are never visited; on the
 // diagonal, 32-key blocks a wave cannot see are skipped and the rest are
 // masked by index.  Workgroups are numbered longest-first (largest query
 // tile index first) so the causal tail is short.
@@ -491,10 +492,45 @@ void diffattn_fwd_kernel(Params p)
     const int kv_end = p.causal ? qhi : s1;
     const int ntiles = (kv_end - s0 + GEO::BN - 1) / GEO::BN;
 
+    // lambda of this head (needed by the map-2 waves in the epilogue); its
+    // loads travel with the first tile's.  The butterfly leaves every lane
+    // with the same bits, so the value is kept in a scalar register.
+    float lam = 0.f;
+    if (map == 1) {
+        float a = 0.f, b = 0.f;
+        const int64_t lo = head * p.lstride;   // this head's lambda vectors
+        for (int cc = lane; cc < D; cc += 64) {
+            a += p.lq1[lo + cc] * p.lk1[lo + cc];
+            b += p.lq2[lo + cc] * p.lk2[lo + cc];
+        }
 #pragma unroll
-    for (int b = 0; b < GEO::NB; ++b) {
-        stage_load(s0, b);
-        stage_store(stage0, b);
+        for (int off = 32; off >= 1; off /= 2) {
+            a += __shfl_xor(a, off, 64);
+            b += __shfl_xor(b, off, 64);
+        }
+        lam = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                             __builtin_bit_cast(int, expf(a) - expf(b) + p.lambda_init)));
+    }
+
+    // first tile: every load of this wave in flight before the first LDS
+    // write (slice by slice, each write would wait for its own load)
+    {
+        u32x4 k0v[LPW], v0v[LPW];
+        const bool tail = s0 + GEO::BN > s1;
+#pragma unroll
+        for (int i = 0; i < LPW; ++i) {
+            int key = s0 + lrow + i * kWaves * RPL;
+            if (tail)   // rows past the sequence repeat its last row
+                key = min(key, s1 - 1);
+            const int64_t off = (int64_t)key * rowstride;
+            k0v[i] = *(const u32x4 *)(kbytes + off);
+            v0v[i] = *(const u32x4 *)(vbytes + off);
+        }
+#pragma unroll
+        for (int i = 0; i < LPW; ++i) {
+            *(u32x4 *)(stage0 + kdst + i * kWaves * RPL * GEO::KROWB) = k0v[i];
+            *(u32x4 *)(stage0 + vdst + i * kWaves * RPL * GEO::VROWB) = v0v[i];
+        }
     }
     __syncthreads();
 
@@ -662,10 +698,15 @@ void diffattn_fwd_kernel(Params p)
     }
 
     // ---- epilogue: combine through LDS, RMSNorm, scale, store -------------
-    // Map-2 waves publish lambda * O_2 / l_2 in their own accumulator layout;
-    // the map-1 wave of the same slot, whose lanes hold the same (query, dim)
-    // elements, subtracts it from O_1 / l_1.
+    // The two waves of a slot split the epilogue by query sub-block: the
+    // map-1 wave finishes sub-block 0, the map-2 wave sub-block 1.  Each
+    // publishes the term the other needs (map 1: O_1/l_1 of sub-block 1;
+    // map 2: lambda O_2/l_2 of sub-block 0) in its accumulator layout (four
+    // consecutive elements of a lane as one 16-byte entry, lanes adjacent);
+    // the partner's lanes hold the same (query, dim) elements.
     float *xch = (float *)((slot < 2 ? stage0 : stage1)) + (slot & 1) * XCH;
+    constexpr int XHALF = XCH / kSub;   // floats per published sub-block
+    static_assert(kSub == 2, "one sub-block per map wave");
     float lsum[kSub];
 #pragma unroll
     for (int u = 0; u < kSub; ++u)
@@ -692,34 +733,28 @@ void diffattn_fwd_kernel(Params p)
                                     o[u][db][4 * i + 2] * il, o[u][db][4 * i + 3] * il);
         }
     }
-    if (map == 1) {
-        float a = 0.f, b = 0.f;
-        const int64_t lo = head * p.lstride;   // this head's lambda vectors
-        for (int cc = lane; cc < D; cc += 64) {
-            a += p.lq1[lo + cc] * p.lk1[lo + cc];
-            b += p.lq2[lo + cc] * p.lk2[lo + cc];
-        }
+    // this wave's scale of its own map (1/l_1, or lambda/l_2) per sub-block
+    float own[kSub];
 #pragma unroll
-        for (int off = 32; off >= 1; off /= 2) {
-            a += __shfl_xor(a, off, 64);
-            b += __shfl_xor(b, off, 64);
-        }
-        const float lam = expf(a) - expf(b) + p.lambda_init;
+    for (int u = 0; u < kSub; ++u)
+        own[u] = (map == 0 ? 1.f : lam) / lsum[u];
+    // (the accumulators are indexed by compile-time sub-block only: one
+    // branch per map, so they stay in registers)
+    auto publish = [&](const f32x16 (&acc)[NDB], float scale, float *dst)
+        __attribute__((always_inline)) {
 #pragma unroll
-        for (int u = 0; u < kSub; ++u) {
-            const float c2 = lam / lsum[u];
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int a2 = 0; a2 < 16; ++a2)
-                    xch[((u * NDB + db) * 16 + a2) * 64 + lane] = o[u][db][a2] * c2;
-        }
-    }
-    __syncthreads();
-    if (map == 1)
-        return;
-
-    // weights of this lane's output dims
+            for (int i = 0; i < 4; ++i)
+                *(float4 *)(dst + ((db * 4 + i) * 64 + lane) * 4) =
+                    make_float4(acc[db][4 * i] * scale, acc[db][4 * i + 1] * scale,
+                                acc[db][4 * i + 2] * scale, acc[db][4 * i + 3] * scale);
+    };
+    if (map == 0)
+        publish(o[1], own[1], xch + XHALF);
+    else
+        publish(o[0], own[0], xch);
+    // weights of this lane's output dims (loads in flight across the barrier)
     float wv[NDB][16];
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -738,36 +773,89 @@ void diffattn_fwd_kernel(Params p)
                 wv[db][4 * i + 3] = w4.w;
             }
     }
-#pragma unroll
-    for (int u = 0; u < kSub; ++u) {
-        const int tq = wq0 + 32 * u + n;
-        const float i1 = 1.f / lsum[u];
+    __syncthreads();
+
+    // pre = O_1/l_1 - lambda O_2/l_2 of this wave's sub-block u = map, its
+    // RMSNorm, weight, scale and store
+    auto finish = [&](const f32x16 (&acc)[NDB], float scale, int u) __attribute__((always_inline)) {
+        const float *src = xch + u * XHALF;
+        float pre[NDB][16];
         float ss = 0.f;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int a = 0; a < 16; ++a) {
-                const float pre = o[u][db][a] * i1 - xch[((u * NDB + db) * 16 + a) * 64 + lane];
-                o[u][db][a] = pre;
-                ss += pre * pre;
+            for (int i = 0; i < 4; ++i) {
+                const float4 x4 = *(const float4 *)(src + ((db * 4 + i) * 64 + lane) * 4);
+                const float xs[4] = {x4.x, x4.y, x4.z, x4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float mine = acc[db][4 * i + e] * scale;
+                    const float v = u == 0 ? mine - xs[e] : xs[e] - mine;
+                    pre[db][4 * i + e] = v;
+                    ss += v * v;
+                }
             }
         ss = pair_sum(ss);
         const float r = (1.f - p.lambda_init) / sqrtf(ss / (float)(2 * D) + p.eps);
-        if (tq < s1) {
-            E *dst = (E *)p.out + ((int64_t)tq * p.H + head) * (2 * D);
+        const int qbase = wq0 + 32 * u;   // query of row 0 of this sub-block
+        if constexpr (sizeof(E) == 2) {
+            // Rounded rows go through the wave's own LDS (the half of the
+            // exchange it has just read, so no other wave touches it) and out
+            // as whole rows: 16 bytes per lane, each store covers 64 / CPR
+            // consecutive rows instead of 32 scattered 16-byte pieces.
+            constexpr int ROW = 2 * D * 2;        // bytes per output row
+            constexpr int PITCH = ROW + 8;        // 8-byte writes of 32 rows hit distinct banks
+            constexpr int CPR = ROW / 16;         // 16-byte chunks per row
+            constexpr int RPS = 64 / CPR;         // rows per store
+            static_assert(32 * PITCH <= XHALF * 4, "staged rows must fit the read half");
+            char *stg = (char *)src;
+            // ordered after this wave's reads of the same bytes (LDS operations
+            // of one wave complete in order)
+            __builtin_amdgcn_wave_barrier();
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int dim = 32 * db + 8 * i + 4 * h;
-                    E vals[4];
+                    bf16x4 vals;
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
-                        vals[j] = (E)(o[u][db][4 * i + j] * r * wv[db][4 * i + j]);
-                    __builtin_memcpy(dst + dim, vals, sizeof(vals));
+                        vals[j] = (bf16)(pre[db][4 * i + j] * r * wv[db][4 * i + j]);
+                    *(bf16x4 *)(stg + n * PITCH + (32 * db + 8 * i + 4 * h) * 2) = vals;
                 }
+            __builtin_amdgcn_wave_barrier();
+            const int rr = lane / CPR, cc = (lane % CPR) * 16;
+#pragma unroll
+            for (int k = 0; k < 32 / RPS; ++k) {
+                const int row = k * RPS + rr;
+                const char *a = stg + row * PITCH + cc;
+                const uint2 lo = *(const uint2 *)a, hi = *(const uint2 *)(a + 8);
+                const int tq = qbase + row;
+                if (tq < s1)
+                    *(u32x4 *)((char *)p.out + ((int64_t)tq * p.H + head) * ROW + cc) =
+                        u32x4{lo.x, lo.y, hi.x, hi.y};
+            }
+        } else {
+            const int tq = qbase + n;
+            if (tq < s1) {
+                E *dst = (E *)p.out + ((int64_t)tq * p.H + head) * (2 * D);
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int dim = 32 * db + 8 * i + 4 * h;
+                        E vals[4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            vals[j] = (E)(pre[db][4 * i + j] * r * wv[db][4 * i + j]);
+                        __builtin_memcpy(dst + dim, vals, sizeof(vals));
+                    }
+            }
         }
-    }
+    };
+    if (map == 0)
+        finish(o[0], own[0], 0);
+    else
+        finish(o[1], own[1], 1);
 }
 
 template <typename E, int D>
