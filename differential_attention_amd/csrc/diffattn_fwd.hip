@@ -247,13 +247,6 @@ template <> struct Rope<bf16> {
         }
         return __builtin_bit_cast(u32x4, r);
     }
-    // B-operand fragment of dims d0 .. d0+7 of a query row, rotated
-    __device__ static inline bf16x8 q_frag(const bf16 *row, int d0, int, const float *rc,
-                                           const float *rs, int pos, int D)
-    {
-        const u32x4 x = *(const u32x4 *)(row + d0);
-        return __builtin_bit_cast(bf16x8, rotate(x, coef(rc, rs, pos, d0 / 2, D)));
-    }
 };
 
 template <> struct Rope<float> {
@@ -410,7 +403,44 @@ void diffattn_fwd_kernel(Params p)
     // ---- Q fragments of this wave's map (B operand of S^T = K Q^T) --------
     // sub-block u holds queries wq0 + 32 u + n
     Frag qf[kSub][NKS];
-    {
+    if constexpr (sizeof(E) == 2) {
+        // The wave's Q rows (its map's half) arrive as whole rows, CPQ lanes
+        // per row and 16 bytes per lane, pass through the wave's own region
+        // of stage 1 (idle until the first tile is computed) and are read
+        // back as fragments.  Loaded as fragments, every load instruction
+        // would touch 32 rows in 32-byte pieces.
+        constexpr int QROWB = D * 2 + 16;   // padded LDS row
+        constexpr int CPQ = D * 2 / 16;     // 16-byte chunks per row
+        constexpr int RPQ = 64 / CPQ;       // rows per load
+        static_assert(kWaves * kQB * QROWB <= GEO::STAGEB, "Q rows must fit a stage");
+        char *qst = stage1 + wave * kQB * QROWB;
+        const int qr = lane / CPQ, qc = lane % CPQ;
+        u32x4 qv[kQB / RPQ];
+#pragma unroll
+        for (int i = 0; i < kQB / RPQ; ++i) {
+            const int tq = wq0 + i * RPQ + qr;
+            if (tq < s1) {
+                const char *src = (const char *)p.q +
+                                  (((int64_t)tq * p.H + head) * 2 + map) * (D * 2) + qc * 16;
+                qv[i] = *(const u32x4 *)src;
+                if constexpr (ROPE)   // pairs 4 qc .. 4 qc + 3 of the half-head
+                    qv[i] = Rope<E>::rotate(qv[i], Rope<E>::coef(p.rcos, p.rsin, tq - s0,
+                                                                 4 * qc, D));
+            } else {
+                qv[i] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kQB / RPQ; ++i)
+            *(u32x4 *)(qst + (i * RPQ + qr) * QROWB + qc * 16) = qv[i];
+        // (same wave, same bytes: LDS operations of a wave complete in order)
+#pragma unroll
+        for (int u = 0; u < kSub; ++u)
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+                qf[u][ks] = *(const Frag *)(qst + (32 * u + n) * QROWB +
+                                            (ks * KSTEP + h * VEC) * 2);
+    } else {
         const E *__restrict__ qg = (const E *)p.q;
 #pragma unroll
         for (int u = 0; u < kSub; ++u)
