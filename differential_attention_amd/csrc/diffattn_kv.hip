@@ -79,8 +79,8 @@ struct KvParams {
     const float *w;
     const int32_t *cuq;   // NULL: uniform lengths qlen_uniform
     const int32_t *cuk;   // NULL: uniform lengths klen_uniform
-    float *ws_o;          // [nseq][Hkv][nsplit][rmax][2][2d]
-    float *ws_ml;         // [nseq][Hkv][nsplit][rmax][4]: m, l of map 1, m, l of map 2
+    float *ws_o;          // [split slot][Hkv][rmax][2][2d]
+    float *ws_ml;         // [split slot][Hkv][rmax][4]: m, l of map 1, m, l of map 2
     float lambda_init;
     float eps;
     int32_t H, Hkv, G, nseq, causal;
@@ -88,7 +88,7 @@ struct KvParams {
     int32_t max_q;        // queries per sequence at most
     int32_t rmax;         // G * max_q rows per (sequence, group)
     int32_t nrb;          // 16-row blocks per (sequence, group)
-    int32_t nsplit;       // key splits per (sequence, group)
+    int32_t nslots;       // split slots of the workspace (bound on all sequences' splits)
     int32_t ck;           // keys per split (multiple of 32)
 };
 
@@ -101,6 +101,63 @@ __device__ inline void seq_bounds(const int32_t *cu, int uniform, int s, int &a,
         a = s * uniform;
         n = uniform;
     }
+}
+
+// Splits of all sequences share one index space: sequence s owns the
+// ceil(nk_s / ck) consecutive slots starting at base(s) = the sum of the
+// earlier sequences' split counts.  Both kernels find them with a
+// wave-wide scan of cu_seqlens_k, 64 sequences per step (wave-uniform).
+__device__ inline int split_count(int nk, int ck) { return (nk + ck - 1) / ck; }
+
+// base(s) of sequence s
+__device__ inline int split_base(const KvParams &p, int s, int lane)
+{
+    if (!p.cuk)
+        return s * split_count(p.klen_uniform, p.ck);
+    int base = 0;
+    for (int s0 = 0; s0 < s; s0 += 64) {
+        const int si = s0 + lane;
+        int cnt = si < s ? split_count(p.cuk[si + 1] - p.cuk[si], p.ck) : 0;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1)
+            cnt += __shfl_xor(cnt, off, 64);
+        base += cnt;
+    }
+    return base;
+}
+
+// Sequence owning slot j and its base, or false past the last split.
+__device__ inline bool split_owner(const KvParams &p, int j, int lane, int &s, int &base)
+{
+    if (!p.cuk) {
+        const int cnt = split_count(p.klen_uniform, p.ck);
+        if (cnt == 0 || j >= cnt * p.nseq)
+            return false;
+        s = j / cnt;
+        base = s * cnt;
+        return true;
+    }
+    int run = 0;
+    for (int s0 = 0; s0 < p.nseq; s0 += 64) {
+        const int si = s0 + lane;
+        const int cnt = si < p.nseq ? split_count(p.cuk[si + 1] - p.cuk[si], p.ck) : 0;
+        int incl = cnt;   // inclusive prefix over the lanes
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int t = __shfl_up(incl, off, 64);
+            if (lane >= off)
+                incl += t;
+        }
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(j >= run + incl - cnt && j < run + incl);
+        if (hit) {
+            const int l = __builtin_ctzll(hit);
+            s = s0 + l;
+            base = run + __builtin_amdgcn_readlane(incl - cnt, l);
+            return true;
+        }
+        run += __builtin_amdgcn_readlane(incl, 63);
+    }
+    return false;
 }
 
 // Combined value over the four lanes l, l^16, l^32, l^48 (the quarter-waves
@@ -160,17 +217,18 @@ void diffattn_kv_partial(KvParams p)
     const int g = (int)(wid % p.Hkv);
     wid /= p.Hkv;
     const int rb = (int)(wid % p.nrb);
-    wid /= p.nrb;
-    const int split = (int)(wid % p.nsplit);
-    const int s = (int)(wid / p.nsplit);
-    if (s >= p.nseq)
+    const int j = (int)(wid / p.nrb);   // split slot
+    if (j >= p.nslots)
         return;
+    int s, sbase;
+    if (!split_owner(p, j, lane, s, sbase))
+        return;   // past the last split
     int qa, nq, ka, nk;
     seq_bounds(p.cuq, p.qlen_uniform, s, qa, nq);
     seq_bounds(p.cuk, p.klen_uniform, s, ka, nk);
     const int nrows = p.G * min(nq, p.max_q);   // rows of this (sequence, group)
     const int r0 = rb * kRows;
-    const int kstart = split * p.ck;
+    const int kstart = (j - sbase) * p.ck;
     if (r0 >= nrows || kstart >= nk)
         return;   // nothing to compute; the combine reads no partial here
 
@@ -351,7 +409,7 @@ void diffattn_kv_partial(KvParams p)
     // ---- partial of this split -------------------------------------------
     if (!row_ok)
         return;
-    const int64_t slot = (((int64_t)s * p.Hkv + g) * p.nsplit + split) * p.rmax + r;
+    const int64_t slot = ((int64_t)j * p.Hkv + g) * p.rmax + r;
     const float l0 = quad_sum(lsum[0]);
     const float l1 = quad_sum(lsum[1]);
 #pragma unroll
@@ -402,7 +460,10 @@ void diffattn_kv_combine(KvParams p)
         return;
     const int g = h / p.G;
     const int r = i * p.G + h % p.G;
-    const int nsp = min(p.nsplit, (nk + p.ck - 1) / p.ck);
+    const int sbase = split_base(p, s, lane);
+    // (the clamp only matters when cu_seqlens_k breaks its preconditions:
+    // no read past the workspace)
+    const int nsp = max(0, min(split_count(nk, p.ck), p.nslots - sbase));
 
     // lambda of this head
     float lam;
@@ -432,18 +493,19 @@ void diffattn_kv_combine(KvParams p)
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc)
             acc[m][cc] = 0.f;
-    const int64_t slot0 = ((int64_t)s * p.Hkv + g) * p.nsplit * p.rmax + r;
+    const int64_t slot0 = ((int64_t)sbase * p.Hkv + g) * p.rmax + r;
+    const int64_t sstride = (int64_t)p.Hkv * p.rmax;   // between a row's splits
     for (int j0 = 0; j0 < nsp; j0 += kChunk) {
         const int nj = min(kChunk, nsp - j0);
         f32x4 ml = f32x4{-INFINITY, 0.f, -INFINITY, 0.f};
         if (lane < nj)
-            ml = *(const f32x4 *)(p.ws_ml + (slot0 + (int64_t)(j0 + lane) * p.rmax) * 4);
+            ml = *(const f32x4 *)(p.ws_ml + (slot0 + (int64_t)(j0 + lane) * sstride) * 4);
         // past the last split the round re-reads the last one (weight 0)
         float ob[kChunk][2][CPL];
 #pragma unroll
         for (int u = 0; u < kChunk; ++u) {
             const int jc = j0 + min(u, nj - 1);
-            const float *op = p.ws_o + (slot0 + (int64_t)jc * p.rmax) * 2 * (2 * D) + CPL * lane;
+            const float *op = p.ws_o + (slot0 + (int64_t)jc * sstride) * 2 * (2 * D) + CPL * lane;
 #pragma unroll
             for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -493,15 +555,23 @@ void diffattn_kv_combine(KvParams p)
     }
 }
 
-// Split policy: enough waves to keep every CU streaming (about 16 per CU),
-// but at least 128 keys per split so the partial traffic stays small
-// against the cache bytes each wave reads.
+// Split policy: keys per split ck chosen from the total number of cache
+// keys Tk so that all sequences together have about 4096 busy waves (about
+// 16 per CU, every one with the same ck keys whatever the length mix), but
+// at least 128 keys per split so the partial traffic stays small against
+// the cache bytes each wave reads.  With ck >= Tk * U / target (U = waves
+// per split: KV heads x 16-row blocks), the splits of all sequences number
+// at most Tk / ck + nseq <= target / U + nseq, a bound that does not depend
+// on Tk: it sizes the workspace.
 struct KvPlan {
-    int nrb, nsplit, ck, rmax;
+    int nrb, nslots, ck, rmax;
     size_t ws_o_bytes, ws_ml_bytes;
 };
 
-bool make_plan(int nseq, int max_q, int max_k, int G, int Hkv, int d, KvPlan &pl)
+constexpr int64_t kTargetWaves = 4096;
+
+// Tk < 0: the workspace bound only (ck left 0)
+bool make_plan(int nseq, int max_q, int max_k, int G, int Hkv, int d, int64_t Tk, KvPlan &pl)
 {
     if (nseq < 1 || max_q < 1 || max_k < 1 || G < 1 || Hkv < 1)
         return false;
@@ -510,20 +580,22 @@ bool make_plan(int nseq, int max_q, int max_k, int G, int Hkv, int d, KvPlan &pl
         return false;
     pl.rmax = (int)rmax;
     pl.nrb = (int)((rmax + kRows - 1) / kRows);
-    const int64_t units = (int64_t)nseq * Hkv * pl.nrb;
-    const int64_t target = 4096;
-    int64_t nsplit = (target + units - 1) / units;
-    const int64_t max_splits = (max_k + 127) / 128;
-    if (nsplit > max_splits)
-        nsplit = max_splits;
-    if (nsplit < 1)
-        nsplit = 1;
-    int64_t ck = (max_k + nsplit - 1) / nsplit;
-    ck = (ck + kBlockKeys - 1) / kBlockKeys * kBlockKeys;
-    nsplit = (max_k + ck - 1) / ck;
-    pl.ck = (int)ck;
-    pl.nsplit = (int)nsplit;
-    const int64_t slots = (int64_t)nseq * Hkv * nsplit * rmax * 2;
+    const int64_t per_split = (int64_t)Hkv * pl.nrb;
+    const int64_t nslots = (kTargetWaves + per_split - 1) / per_split + nseq;
+    if (nslots > (1 << 30))
+        return false;
+    pl.nslots = (int)nslots;
+    pl.ck = 0;
+    if (Tk >= 0) {
+        int64_t ck = (Tk * per_split + kTargetWaves - 1) / kTargetWaves;
+        if (ck < 128)
+            ck = 128;
+        ck = (ck + kBlockKeys - 1) / kBlockKeys * kBlockKeys;
+        if (ck > (1 << 30))
+            return false;
+        pl.ck = (int)ck;
+    }
+    const int64_t slots = nslots * Hkv * rmax * 2;
     pl.ws_o_bytes = (size_t)(slots * 2 * d * 4);
     pl.ws_ml_bytes = (size_t)(slots * 2 * 4);
     return true;
@@ -566,7 +638,7 @@ extern "C" size_t diffattn_fwd_kv_workspace_size(int32_t nseq, int32_t max_seqle
     if (H < 1 || Hkv < 1 || H % Hkv != 0 || d < 1)
         return 0;
     KvPlan pl;
-    if (!make_plan(nseq, max_seqlen_q, max_seqlen_k, H / Hkv, Hkv, d, pl))
+    if (!make_plan(nseq, max_seqlen_q, max_seqlen_k, H / Hkv, Hkv, d, -1, pl))
         return 0;
     return pl.ws_o_bytes + pl.ws_ml_bytes;
 }
@@ -620,7 +692,7 @@ extern "C" int diffattn_fwd_kv(int dtype, const void *q, const void *k, const vo
         return DIFFATTN_EINVAL;
     const int G = H / Hkv;
     KvPlan pl;
-    if (!make_plan(nseq, max_seqlen_q, max_seqlen_k, G, Hkv, d, pl))
+    if (!make_plan(nseq, max_seqlen_q, max_seqlen_k, G, Hkv, d, Tk, pl))
         return DIFFATTN_EINVAL;
     if (workspace_bytes < pl.ws_o_bytes + pl.ws_ml_bytes)
         return DIFFATTN_EINVAL;
@@ -652,11 +724,11 @@ extern "C" int diffattn_fwd_kv(int dtype, const void *q, const void *k, const vo
     p.max_q = max_seqlen_q;
     p.rmax = pl.rmax;
     p.nrb = pl.nrb;
-    p.nsplit = pl.nsplit;
+    p.nslots = pl.nslots;
     p.ck = pl.ck;
 
     hipStream_t st = (hipStream_t)stream;
-    const int64_t waves1 = (int64_t)nseq * Hkv * pl.nsplit * pl.nrb;
+    const int64_t waves1 = (int64_t)pl.nslots * Hkv * pl.nrb;
     const int64_t waves2 = (int64_t)nseq * max_seqlen_q * H;
     const int64_t blocks1 = (waves1 + kWavesPerBlock - 1) / kWavesPerBlock;
     const int64_t blocks2 = (waves2 + kWavesPerBlock - 1) / kWavesPerBlock;

@@ -157,7 +157,9 @@ size_t diffattn_fwd_workspace_size(int dtype, int32_t T, int32_t Hkv, int32_t d,
  *                causal (see diffattn_check_cu_seqlens_kv).
  *   max_seqlen_q, max_seqlen_k
  *                upper bounds on every nq and nk (ignored when the
- *                boundaries are NULL); they size the grid and the workspace.
+ *                boundaries are NULL); max_seqlen_q sizes the grid and the
+ *                workspace.  Keys are split into chunks of one size for all
+ *                sequences, chosen from Tk.
  *   Tq, Tk, H, Hkv, d
  *                sizes; H % Hkv == 0.  Compiled (dtype, d) pairs: see
  *                diffattn_supported_kv.
