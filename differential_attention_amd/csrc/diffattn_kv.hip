@@ -49,6 +49,8 @@
 // combination is nonlinear in the two maps' normalisers.
 
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #include <math.h>
 #include <stdint.h>
 
@@ -562,7 +564,8 @@ void diffattn_kv_combine(KvParams p)
 // the cache bytes each wave reads.  With ck >= Tk * U / target (U = waves
 // per split: KV heads x 16-row blocks), the splits of all sequences number
 // at most Tk / ck + nseq <= target / U + nseq, a bound that does not depend
-// on Tk: it sizes the workspace.
+// on Tk: it sizes the workspace (with nseq * ceil(max_k / 128), whichever
+// is smaller).
 struct KvPlan {
     int nrb, nslots, ck, rmax;
     size_t ws_o_bytes, ws_ml_bytes;
@@ -581,7 +584,9 @@ bool make_plan(int nseq, int max_q, int max_k, int G, int Hkv, int d, int64_t Tk
     pl.rmax = (int)rmax;
     pl.nrb = (int)((rmax + kRows - 1) / kRows);
     const int64_t per_split = (int64_t)Hkv * pl.nrb;
-    const int64_t nslots = (kTargetWaves + per_split - 1) / per_split + nseq;
+    // (also at most ceil(max_k / 128) splits per sequence, as ck >= 128)
+    const int64_t nslots = std::min((kTargetWaves + per_split - 1) / per_split + nseq,
+                                    (int64_t)nseq * ((max_k + 127) / 128));
     if (nslots > (1 << 30))
         return false;
     pl.nslots = (int)nslots;
