@@ -158,6 +158,26 @@ def test_ragged_matrix(H, Hkv, d, causal, case):
     assert err <= TOL
 
 
+def test_many_sequences_split_scan():
+    """More than 64 sequences, with empty ones, uneven caches and a total
+    large enough for splits longer than the minimum: every sequence's
+    splits are found by the kernels' scan of cu_seqlens_k across several
+    64-sequence steps."""
+    rng = np.random.default_rng(21)
+    nseq = 150
+    kl = [int(x) for x in rng.integers(1, 6000, nseq)]
+    ql = [int(x) for x in rng.integers(1, 4, nseq)]
+    for s in (0, 63, 64, 100):       # empty sequences, on and off step edges
+        ql[s], kl[s] = 0, 0
+    ql[70] = 0                       # no query, keys only
+    wl = custom_kv("many", "bf16", tuple(ql), tuple(kl), H=8, Hkv=2, d=64,
+                   depth=4, seed=21)
+    inp = make_kv_inputs(wl)
+    err = max_abs(gpu_kv(inp), oracle_kv(inp))
+    announce(f"many sequences (Tk={sum(kl)}): max-abs {err:.3e}")
+    assert err <= TOL
+
+
 def test_long_cache_many_splits():
     """One long sequence with several new queries: many key splits per row
     block, and the causal limit inside the last split."""
