@@ -21,7 +21,10 @@
 // wave keeps, per sub-block, one running row maximum, one running sum and a
 // 32 x 2d fp32 accumulator of its map; the combine O_1/l_1 - lambda O_2/l_2
 // happens once, in the epilogue, through LDS.  Two waves per SIMD (256
-// registers each) interleave their MFMA and softmax phases.
+// registers each, waves s and s + 4: the two maps of a slot) interleave
+// their MFMA and softmax phases; the map-2 wave runs each block's PV
+// product at the start of the next block, which keeps the pair about half
+// a block apart.
 //
 // The workgroup streams the KV range of its sequence in tiles of 128 keys
 // (64 where two stages of 128 would not fit LDS).  K (both halves) and V of
@@ -353,7 +356,7 @@ void diffattn_fwd_kernel(Params p)
     constexpr int NDB = 2 * D / 32;     // 32-wide blocks of the output
     constexpr int NPS = 32 / KSTEP;     // PV steps per 32-key block
     static_assert(D % KSTEP == 0 && (2 * D) % 32 == 0, "unsupported d");
-    // epilogue exchange: two slots per stage object, NSUB x NDB x 16 x 64
+    // epilogue exchange: two slots per stage object, kSub x NDB x 16 x 64
     // floats each
     constexpr int XCH = kSub * NDB * 16 * 64;
     static_assert(2 * XCH * 4 <= GEO::STAGEB, "exchange must fit a stage");
@@ -564,16 +567,35 @@ void diffattn_fwd_kernel(Params p)
     }
     __syncthreads();
 
+    // Map-2 waves run the PV product of each block at the start of the next
+    // one (its probabilities wait in registers), so the two waves of a SIMD
+    // are offset by about half a block: one issues MFMAs while the other
+    // runs its exponentials.  A barrier after the first block of every tile
+    // keeps the previous tile's V in place until the late PV has read it.
+    const bool lag = map == 1;
+    Frag pf[kSub][NPS];
+    bool pend = false;   // lagging wave: PV of the previous block pending
+    auto pv_block = [&](const char *stage, int b) __attribute__((always_inline)) {
+        const char *vt = stage + GEO::KTILEB + v_lane;
+#pragma unroll
+            for (int ps = 0; ps < NPS; ++ps) {
+                // first key row of this step (the lane part is in v_lane)
+                const int row = VEC == 8 ? 32 * b + 16 * ps
+                                         : 32 * b + 8 * (ps / 4) + (ps % 4);
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    const Frag vf = VOperand<E, D>::load(vt, row, db);
+#pragma unroll
+                    for (int u = 0; u < kSub; ++u)
+                        o[u][db] = M::mma(vf, pf[u][ps], o[u][db]);
+                }
+            }
+    };
     // One tile: compute from `cur` while the next tile is staged into `nxt`.
     auto tile = [&](int it, const char *cur, char *nxt) __attribute__((always_inline)) {
         const int k0 = s0 + it * GEO::BN;
         const char *kt = cur + k_lane;
-        const char *vt = cur + GEO::KTILEB + v_lane;
         const bool more = it + 1 < ntiles;
-
-        // The tile is consumed one 32-key block at a time: the block's
-        // scores for both query sub-blocks, their softmax updates, then the
-        // PV products, each V operand read serving both sub-blocks.
 #pragma unroll
         for (int b = 0; b < GEO::NB; ++b) {
             // staging of the next tile, one slice per block
@@ -582,13 +604,15 @@ void diffattn_fwd_kernel(Params p)
                     stage_store(nxt, b - 1);
                 stage_load(k0 + GEO::BN, b);
             }
+            if (lag && pend) {
+                pv_block(b == 0 ? nxt : cur, (b + GEO::NB - 1) % GEO::NB);
+                pend = false;
+            }
             const int kb0 = k0 + 32 * b;
             // wave-uniform: can this wave see any key of the block, and does
             // any key need the index mask?
-            if (kb0 >= s1 || (p.causal && kb0 > wq_last))
-                continue;
+            if (!(kb0 >= s1 || (p.causal && kb0 > wq_last))) {
             const bool masked = kb0 + 32 > s1 || (p.causal && kb0 + 31 > wq0);
-
             // ---- S^T = K Q^T ------------------------------------------------
             Frag ka[NKS];
 #pragma unroll
@@ -626,7 +650,6 @@ void diffattn_fwd_kernel(Params p)
             // ---- online softmax with a lazily raised maximum ---------------
             // (a query row whose keys of this block are all masked keeps its
             // maximum: its first block always has a visible key)
-            Frag pf[kSub][NPS];
 #pragma unroll
             for (int u = 0; u < kSub; ++u) {
                 // the row maximum of the block, then a raised running maximum
@@ -701,20 +724,13 @@ void diffattn_fwd_kernel(Params p)
                 }
             }
 
-            // ---- O^T += V^T P^T ---------------------------------------------
-#pragma unroll
-            for (int ps = 0; ps < NPS; ++ps) {
-                // first key row of this step (the lane part is in v_lane)
-                const int row = VEC == 8 ? 32 * b + 16 * ps
-                                         : 32 * b + 8 * (ps / 4) + (ps % 4);
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    const Frag vf = VOperand<E, D>::load(vt, row, db);
-#pragma unroll
-                    for (int u = 0; u < kSub; ++u)
-                        o[u][db] = M::mma(vf, pf[u][ps], o[u][db]);
-                }
+            if (lag)
+                pend = true;
+            else
+                pv_block(cur, b);
             }
+            if (b == 0)
+                __syncthreads();
         }
 
         if (more)
@@ -726,6 +742,9 @@ void diffattn_fwd_kernel(Params p)
         if (it + 1 < ntiles)
             tile(it + 1, stage1, stage0);
     }
+    if (lag && pend)
+        pv_block((ntiles & 1) ? stage0 : stage1, GEO::NB - 1);
+    __syncthreads();
 
     // ---- epilogue: combine through LDS, RMSNorm, scale, store -------------
     // The two waves of a slot split the epilogue by query sub-block: the
