@@ -462,9 +462,12 @@ def bwd(q, k, v, lambda_q1, lambda_k1, lambda_q2, lambda_k2,
     cu_ptr, nseq, max_seqlen = _seq_args(T, cu_seqlens, max_seqlen, nseq, dev)
     g = {"dq": torch.empty_like(q), "dk": torch.empty_like(k),
          "dv": torch.empty_like(v)}
+    # (the library writes every element of these when T > 0; zeros only for
+    # T == 0, where it writes nothing -- so a captured call records no fill)
+    alloc = torch.zeros_like if T == 0 else torch.empty_like
     for name, lv in zip(("dlq1", "dlk1", "dlq2", "dlk2"), lvs):
-        g[name] = torch.zeros_like(lv)
-    g["dw"] = torch.zeros(2 * d, dtype=torch.float32, device=dev)
+        g[name] = alloc(lv)
+    g["dw"] = alloc(torch.empty(2 * d, dtype=torch.float32, device=dev))
     if workspace is None:
         workspace = torch.empty(max(bwd_workspace_size(T, H, d), 16),
                                 dtype=torch.uint8, device=dev)
