@@ -43,6 +43,7 @@ PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 METRIC = "diff-attention fwd TFLOP/s & % bf16 MFMA peak, 1 MI355X, N=4096 causal"
 METRIC_KV = "diff-attention KV-cache decode GB/s & % HBM peak, 1 MI355X"
+GRAPH_STEPS = 10   # decode steps per captured graph (--graph)
 _CSRC = os.path.join(HERE, "differential_attention_amd", "csrc")
 # the sources whose kernels a stored counter profile measured: a profile
 # counts only while their digest matches
@@ -170,6 +171,22 @@ def bench_kv(args, name) -> int:
         if st != 0:
             raise da.DiffAttnError(st, "diffattn_fwd_kv")
 
+    # --graph: the steps are replayed from a HIP graph of GRAPH_STEPS calls
+    # (what a serving loop that captures its decode step pays), not launched
+    # one by one from the host
+    graph = None
+    if args.graph:
+        if args.steps % GRAPH_STEPS:
+            raise SystemExit(f"--graph needs --steps divisible by {GRAPH_STEPS}")
+        with torch.cuda.stream(stream):
+            step()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for _ in range(GRAPH_STEPS):
+                step()
+        torch.cuda.synchronize()
+
     with torch.cuda.stream(stream):
         for _ in range(args.warmup):
             step()
@@ -178,8 +195,12 @@ def bench_kv(args, name) -> int:
         ev1 = torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
         ev0.record(stream)
-        for _ in range(args.steps):
-            step()
+        if graph is not None:
+            for _ in range(args.steps // GRAPH_STEPS):
+                graph.replay()
+        else:
+            for _ in range(args.steps):
+                step()
         ev1.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
@@ -206,6 +227,7 @@ def bench_kv(args, name) -> int:
                    "tokens_per_s": round(wl.Tq / (ms * 1e-3), 1),
                    "tflops": round(wl.flops() / (ms * 1e-3) / 1e12, 2),
                    "workspace_bytes": need,
+                   "launch": f"hip graph of {GRAPH_STEPS} steps" if graph is not None else "eager",
                    "wall_s_timed": round(wall, 4),
                    "kernel_digest": kernel_digest(KV_KERNEL_SOURCES)},
         # both kernels of the step are in the timed duration, so this is a
@@ -295,7 +317,8 @@ def bench_bwd(args, name) -> int:
         "config": {"workload": name + "+bwd", "T": wl.T, "nseq": wl.nseq,
                    "H": wl.H, "Hkv": wl.Hkv, "d": wl.d, "causal": wl.causal,
                    "flops_fwd": fwd_flops, "flops_bwd": bwd_flops,
-                   "workspace_bytes": need, "wall_s_timed": round(wall, 4),
+                   "workspace_bytes": need,
+                   "launch": f"hip graph of {GRAPH_STEPS} steps" if graph is not None else "eager", "wall_s_timed": round(wall, 4),
                    "kernel_digest": kernel_digest(BWD_KERNEL_SOURCES)},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
                      "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
@@ -338,6 +361,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="cache workloads: replay the timed steps from a HIP graph")
     ap.add_argument("--bwd", action="store_true",
                     help="a training step instead: the training forward and "
                          "the backward pass (bf16, no rotary prologue)")
