@@ -15,24 +15,25 @@
 // and every slot is served by two waves, one per attention map: wave w
 // computes map (w / 4) of slot (w % 4) for its 64 queries, as two 32-query
 // sub-blocks.  Each K operand read and each V operand read of a wave feeds
-// two MFMAs (one per sub-block), and each K/V tile staged in LDS serves
-// 256 query rows of the GQA group: LDS traffic per MFMA is what bounds this
-// kernel on gfx950 (the transposing V read runs at half the LDS rate).  A
-// wave keeps, per sub-block, one running row maximum, one running sum and a
-// 32 x 2d fp32 accumulator of its map; the combine O_1/l_1 - lambda O_2/l_2
-// happens once, in the epilogue, through LDS.  Two waves per SIMD (256
-// registers each, waves s and s + 4: the two maps of a slot) interleave
-// their MFMA and softmax phases; the map-2 wave runs each block's PV
-// product at the start of the next block, which keeps the pair about half
-// a block apart.
+// two MFMAs (one per sub-block), and each K/V tile staged in LDS serves 256
+// query rows of the GQA group, which keeps LDS traffic per MFMA low (the
+// transposing V read runs at half the LDS read rate, 16-byte LDS writes at a
+// third of it).  A wave keeps, per sub-block, one running row maximum, one
+// running sum and a 32 x 2d fp32 accumulator of its map; the combine
+// O_1/l_1 - lambda O_2/l_2 happens once, in the epilogue, through LDS.  Two
+// waves per SIMD (256 registers each, waves s and s + 4: the two maps of a
+// slot) interleave their MFMA and softmax phases; the map-2 wave runs each
+// block's PV product at the start of the next block, which keeps the pair
+// about half a block apart.
 //
 // The workgroup streams the KV range of its sequence in tiles of 128 keys
 // (64 where two stages of 128 would not fit LDS).  K (both halves) and V of
 // a tile are staged into padded row-major LDS tiles, double-buffered: tile
 // t+1 moves global -> registers -> LDS in slices, one per 32-key block of
-// tile t, so its loads are in flight while tile t is computed; one barrier
-// per tile.  (Direct global -> LDS copies were measured slower on this part:
-// their transfer path costs more than 16-byte LDS writes.)
+// tile t, so its loads are in flight while tile t is computed; two barriers
+// per tile (after its first block, for the late PV of the map-2 waves, and
+// at its end).  (Direct global -> LDS copies were measured slower on this
+// part: their transfer path costs more than 16-byte LDS writes.)
 //
 // All contractions run on MFMA (v_mfma_f32_32x32x16_bf16 for bf16,
 // v_mfma_f32_32x32x2_f32 for fp32), in transposed form:
@@ -58,10 +59,12 @@
 // lambda O_2/l_2, the RMSNorm over 2d (in-lane sums plus one cross-half
 // exchange), the weight, the (1 - lambda_init) scale and the rounding
 // store.  The two waves of a slot share it, one 32-query sub-block each,
-// and bf16 rows leave through LDS as whole 256-byte rows.  Causal tiles above the diagonal are never visited; on the
-// diagonal, 32-key blocks a wave cannot see are skipped and the rest are
-// masked by index.  Workgroups are numbered longest-first (largest query
-// tile index first) so the causal tail is short.
+// and bf16 rows leave through LDS as whole 256-byte rows.
+//
+// Causal tiles above the diagonal are never visited; on the diagonal,
+// 32-key blocks a wave cannot see are skipped and the rest are masked by
+// index.  Workgroups are numbered longest-first (largest query tile index
+// first) so the causal tail is short.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
