@@ -292,3 +292,36 @@ def test_per_head_lambda(dtype, d, H, Hkv):
     err = max_abs(gpu_run(inp), oracle_full(inp))
     announce(f"per-head lambda max-abs {err:.3e}")
     assert err <= TOL[dtype]
+
+
+# ---------------------------------------------------------------------------
+# seeded random shapes: sequence mixes whose tile counts are odd and even,
+# partial last tiles seen by some waves of a workgroup and not others, every
+# head-grouping, both maskings, with and without per-head lambda
+
+def random_case(i):
+    rng = np.random.default_rng(1000 + i)
+    dtype, d = [("bf16", 64), ("bf16", 64), ("bf16", 32), ("bf16", 16), ("f32", 16)][i % 5]
+    Hkv = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 2, 3, 4, 8]))
+    lens = tuple(int(x) for x in rng.integers(0, 700, int(rng.integers(1, 6))))
+    return dtype, d, Hkv * G, Hkv, lens, bool(rng.integers(0, 2)), bool(rng.integers(0, 2))
+
+
+@pytest.mark.parametrize("i", range(20))
+def test_random_shapes(i):
+    dtype, d, H, Hkv, lens, causal, per_head = random_case(i)
+    if sum(lens) == 0:
+        lens = lens + (5,)
+    wl = custom("random", dtype, lens, H, Hkv, d, depth=1 + i % 12, causal=causal,
+                seed=2000 + i)
+    announce(f"random case {i}: {dtype} d={d} H={H} Hkv={Hkv} lens={lens} "
+             f"causal={causal} per-head lambda={per_head}")
+    inp = make_inputs(wl)
+    if per_head:
+        g = torch.Generator().manual_seed(3000 + i)
+        inp.lq1, inp.lk1, inp.lq2, inp.lk2 = [0.2 * torch.randn(H, d, generator=g)
+                                              for _ in range(4)]
+    err = max_abs(gpu_run(inp), oracle_full(inp))
+    announce(f"random case {i}: max-abs {err:.3e}")
+    assert err <= TOL[dtype]
