@@ -318,7 +318,7 @@ def bench_bwd(args, name) -> int:
                    "H": wl.H, "Hkv": wl.Hkv, "d": wl.d, "causal": wl.causal,
                    "flops_fwd": fwd_flops, "flops_bwd": bwd_flops,
                    "workspace_bytes": need,
-                   "launch": f"hip graph of {GRAPH_STEPS} steps" if graph is not None else "eager", "wall_s_timed": round(wall, 4),
+                   "launch": "eager", "wall_s_timed": round(wall, 4),
                    "kernel_digest": kernel_digest(BWD_KERNEL_SOURCES)},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
                      "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",

@@ -12,32 +12,34 @@
 // Four kernels, no atomics (the result is bitwise reproducible):
 //
 //  prep     workgroups of four waves per head, each wave striding over the
-//           tokens: pre = O_1 - lambda O_2 and
-//           its RMSNorm backward, dO_1 = dpre, dO_2 = -lambda dpre (stored
-//           bf16 as MFMA operands), D_m = <dO_m, O_m> (from the rounded
-//           dO_m, so that the softmax gradients of a row sum to zero),
-//           and per-workgroup partial sums of the weight and lambda
-//           gradients.
+//           tokens: pre = O_1 - lambda O_2 and its RMSNorm backward dpre
+//           (stored bf16 as the MFMA operand; the maps' output gradients
+//           are dO_1 = dpre and dO_2 = -lambda dpre, and -lambda is applied
+//           in fp32 where map 2 uses it), D'_m = <dpre, O_m> from the
+//           rounded dpre (so that the softmax gradients of a row sum to
+//           zero), lambda per head, and per-workgroup partial sums of the
+//           weight and lambda gradients.
 //  reduce   one workgroup: the partial sums in a fixed order, and the
 //           lambda-vector gradients by the chain rule.
 //  dq       query-outer, as the forward: one workgroup = (sequence, head,
 //           128 queries), wave = (map, 32 queries).  Over K/V tiles
 //           double-buffered in LDS (the next tile travels through registers
 //           while the current one is used): S^T = K Q^T,
-//           P^T = exp2(S^T c - lse), dP^T = V dO^T,
-//           dS^T = P^T (dP^T - D), dQ^T += K^T dS^T (K^T through the
-//           transposing LDS read, dS^T straight from the accumulator).
-//  dkdv     key-outer: one workgroup = (sequence, KV head, 128 keys), wave
-//           = (map, 32 keys); the K and V rows stay in LDS.  Over the
-//           group's heads and the 32-row query tiles that can see the keys
-//           (Q, dO, lse, D double-buffered in LDS as for dq): S = Q K^T, P,
-//           dP = dO V^T, dS, then
-//           dV^T += dO^T P and dK^T += Q^T dS (dO^T and Q^T through the
-//           transposing read, P and dS straight from the accumulator).  The
-//           two maps' dV are summed through LDS at the end.
+//           P^T = exp2(S^T c - lse), dP'^T = V dpre^T,
+//           dS'^T = P^T (dP'^T - D'), dQ^T += K^T dS'^T (K^T through the
+//           transposing LDS read, dS'^T straight from the accumulator);
+//           map 2's dQ is scaled by -lambda at the end.
+//  dkdv     key-outer: one workgroup = (sequence, KV head, 128 keys).  Four
+//           waves (32 keys each, both maps) compute S_m = Q_m K_m^T, P_m,
+//           dP = dpre V^T once for both maps, dS_1 = P_1 (dP - D'_1),
+//           dS_2 = -lambda P_2 (dP - D'_2) and dK_m^T += Q_m^T dS_m, and
+//           pass W = P_1 - lambda P_2 (formed in fp32, then rounded) through
+//           LDS to the other four waves, which add dV^T += dpre^T W one
+//           query tile later.  Query tiles (Q, dpre, lse, D') of all G
+//           heads of the group rotate through three LDS stages.
 //
 // All contractions run on v_mfma_f32_32x32x16_bf16 with fp32 accumulators;
-// P and dS are rounded to bf16 as operands, as are dO_m.
+// P, W and dS are rounded to bf16 as operands, as is dpre.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -125,8 +127,9 @@ struct BwdParams {
     bf16 *dq, *dk, *dv;
     float *dlq1, *dlk1, *dlq2, *dlk2, *dw;
     // workspace
-    bf16 *do12;          // [T][H][2][2d]
-    float *dd;           // [T][H][2]
+    bf16 *dpre;          // [T][H][2d]: dO_1 = dpre, dO_2 = -lambda dpre
+    float *dd;           // [T][H][2]: <dpre, O_1>, <dpre, O_2>
+    float *lam;          // [H]
     float *part_dw;      // [nprep][2d]
     float *part_dl;      // [nprep]
     float lambda_init, eps;
@@ -218,6 +221,8 @@ __global__ __launch_bounds__(256) void bwd_prep(BwdParams p)
     const int h = blockIdx.x % p.H;
     const int wid = (blockIdx.x / p.H) * 4 + wv4;   // wave index within the head
     const float lam = head_lambda(p, h, lane, D);
+    if (blockIdx.x < p.H && threadIdx.x == 0)
+        p.lam[h] = lam;
     const float sc = 1.f - p.lambda_init;
     float wv[CPL], dwp[CPL];
 #pragma unroll
@@ -255,23 +260,20 @@ __global__ __launch_bounds__(256) void bwd_prep(BwdParams p)
         const float r = rsqrtf(ss / (float)(2 * D) + p.eps);
         const float r3 = r * r * r * gp / (float)(2 * D);
         float d1 = 0.f, d2 = 0.f;
-        bf16 b1[CPL], b2[CPL];
+        bf16 b1[CPL];
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc) {
             const float dpre = r * g[cc] - r3 * pre[cc];
             b1[cc] = (bf16)dpre;
-            b2[cc] = (bf16)(-lam * dpre);
             d1 += (float)b1[cc] * a1[cc];
-            d2 += (float)b2[cc] * a2[cc];
+            d2 += (float)b1[cc] * a2[cc];
             dlp -= dpre * a2[cc];
             dwp[cc] += dyv[cc] * pre[cc] * r * sc;
         }
         d1 = seg16_sum(d1);
         d2 = seg16_sum(d2);
         if (ok) {
-            bf16 *do1 = p.do12 + row * 2 * (2 * D) + CPL * l16;
-            store_bf16(do1, b1);
-            store_bf16(do1 + 2 * D, b2);
+            store_bf16(p.dpre + row * (2 * D) + CPL * l16, b1);
             if (l16 == 0) {
                 p.dd[row * 2] = d1;
                 p.dd[row * 2 + 1] = d2;
@@ -442,8 +444,7 @@ void bwd_dq(BwdParams p)
         qf[ks] = qok ? *(const bf16x8 *)(p.q + (qrow * 2 + map) * D + 16 * ks + 8 * h) : bf16x8{};
 #pragma unroll
     for (int ks = 0; ks < NVS; ++ks)
-        df[ks] = qok ? *(const bf16x8 *)(p.do12 + (qrow * 2 + map) * (2 * D) + 16 * ks + 8 * h)
-                     : bf16x8{};
+        df[ks] = qok ? *(const bf16x8 *)(p.dpre + qrow * (2 * D) + 16 * ks + 8 * h) : bf16x8{};
     if (qok) {
         lse = p.lse[qrow * 2 + map];
         dval = p.dd[qrow * 2 + map];
@@ -543,7 +544,9 @@ void bwd_dq(BwdParams p)
     }
     if (!qok)
         return;
-    const float scale = rsqrtf((float)D);
+    // map 2 ran on dO = dpre and D = <dpre, O_2>: its dS and dQ carry the
+    // factor -lambda, applied here in fp32
+    const float scale = rsqrtf((float)D) * (map ? -p.lam[head] : 1.f);
     bf16 *dst = p.dq + (qrow * 2 + map) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -558,41 +561,43 @@ void bwd_dq(BwdParams p)
 }
 
 // ---------------------------------------------------------------------------
-// dkdv: key-outer.  The workgroup's K and V rows sit in LDS for the whole
-// kernel; query tiles of kQT rows (Q, dO, lse, D) are double-buffered.
+// dkdv: key-outer.  Waves 0..3 (the S role) take 32 keys each and both
+// maps: S_m = Q_m K_m^T, P_m, dP = dpre V^T (once: dO_2 = -lambda dO_1, so
+// dP_2 = -lambda dP_1), dS_m, dK_m^T += Q_m^T dS_m, and W = P_1 - lambda P_2
+// rounded to bf16, which they hand to waves 4..7 (the V role, same keys)
+// through LDS.  The V-role waves add dV^T += dpre^T W one query tile
+// behind.  Forming P_1 - lambda P_2 in fp32 before rounding keeps dV
+// accurate where the two maps nearly cancel (the first key of a sequence
+// when lambda is near 1, where both maps put all weight on that key).
+// K and V rows of the S-role waves live in registers; 32-row query tiles
+// (Q, dpre, lse, D) rotate through three LDS stages: the S role computes on
+// tile i while the V role reads tile i - 1 and tile i + 1 is written.
 constexpr int kQT = 32;
 
 template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv(BwdParams p)
 {
-    constexpr int ROWB = 2 * D * 2;          // K, V or Q row bytes (both maps of q)
-    constexpr int LROW = ROWB + 16;          // K and V rows: plain 16-byte reads only
-    // Q and dO rows are read both ways: plain 16-byte reads of 16 rows and
+    constexpr int ROWB = 2 * D * 2;          // K, V, Q (both maps) or dpre row bytes
+    // Q and dpre rows are read both ways: plain 16-byte reads of 16 rows and
     // transposing reads of 4 consecutive rows x 64 bytes.  A pad of 48 keeps
     // the plain reads on distinct banks (48 r mod 256 differs for r < 16) and
-    // starts the 4 rows of a transposing read 48 bytes apart instead of 16;
-    // the dkdv kernel runs about 6% faster than with a 16-byte pad.
+    // starts the 4 rows of a transposing read 48 bytes apart instead of 16.
     constexpr int LQROW = ROWB + 48;
-    constexpr int DROWB = 4 * D * 2;         // dO row bytes (both maps)
-    constexpr int DROW = DROWB + 48;
     constexpr int NKS = D / 16;
     constexpr int NVS = 2 * D / 16;
-    constexpr int NKB = D / 32;              // 32-dim blocks of dK
+    constexpr int NKB = D / 32;              // 32-dim blocks of dK (per map)
     constexpr int NVB = 2 * D / 32;          // 32-dim blocks of dV
-    constexpr int KVB = kTile * LROW;        // K (or V) tile bytes
+    static_assert(2 * NKB == NVB, "both roles use the same accumulators");
     constexpr int QB = kQT * LQROW;          // Q tile bytes
-    constexpr int DB = kQT * DROW;           // dO tile bytes
-    constexpr int STB = QB + DB + kQT * 4 * 4;   // one stage: Q, dO, lse[2], D[2]
-    constexpr int XCH_BYTES = kSubs * NVB * 16 * 64 * 4;
-    static_assert(XCH_BYTES <= 2 * KVB, "dV exchange fits the K/V tiles");
-    __shared__ __attribute__((aligned(16))) char kvt[2 * KVB];   // K tile, then V tile
-    __shared__ __attribute__((aligned(16))) char st0[STB];
-    __shared__ __attribute__((aligned(16))) char st1[STB];
+    constexpr int STB = 2 * QB + kQT * 4 * 4;   // one stage: Q, dpre, lse[2], D[2]
+    constexpr int WXB = kSubs * 2 * 64 * 16; // one W hand-over buffer
+    __shared__ __attribute__((aligned(16))) char stg[3 * STB];
+    __shared__ __attribute__((aligned(16))) char wx[2 * WXB];
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int n = lane & 31, h = lane >> 5;
-    const int map = wave / kSubs, sub = wave % kSubs;
+    const int role = wave / kSubs, sub = wave % kSubs;   // role 0: S, 1: V
 
     const int pairs = p.nseq * p.Hkv;
     const int tile = blockIdx.x / pairs;
@@ -604,38 +609,36 @@ void bwd_dkdv(BwdParams p)
     if (k0 >= s1)
         return;
     const int wk = k0 + 32 * sub + n;   // this lane's key
-    const int64_t kstride = (int64_t)p.Hkv * ROWB;
-    {
-        Stager<ROWB, LROW, kTile> sk, sv;
-        sk.load((const char *)p.k + (int64_t)k0 * kstride + (int64_t)g * ROWB, kstride,
-                min(kTile, s1 - k0));
-        sv.load((const char *)p.v + (int64_t)k0 * kstride + (int64_t)g * ROWB, kstride,
-                min(kTile, s1 - k0));
-        sk.store(kvt);
-        sv.store(kvt + KVB);
-    }
-    f32x16 dka[NKB], dva[NVB];
+    const bool kok = wk < s1;
+    const int64_t kvrow = (int64_t)wk * p.Hkv + g;
+    // this wave's K rows (B operands of S_m = Q_m K_m^T) and V rows (B
+    // operand of dP = dpre V^T); the V role does not need them
+    bf16x8 kf[2][NKS], vf[NVS];
 #pragma unroll
-    for (int db = 0; db < NKB; ++db)
-        dka[db] = f32x16{};
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+            kf[m][ks] = (kok && role == 0)
+                            ? *(const bf16x8 *)(p.k + kvrow * 2 * D + m * D + 16 * ks + 8 * h)
+                            : bf16x8{};
+#pragma unroll
+    for (int ks = 0; ks < NVS; ++ks)
+        vf[ks] = (kok && role == 0) ? *(const bf16x8 *)(p.v + kvrow * 2 * D + 16 * ks + 8 * h)
+                                    : bf16x8{};
+    // S role: dK of map m in acc[m * NKB + db]; V role: dV in acc[db]
+    f32x16 acc[NVB];
 #pragma unroll
     for (int db = 0; db < NVB; ++db)
-        dva[db] = f32x16{};
+        acc[db] = f32x16{};
     const float c = kLog2e * rsqrtf((float)D);
-    const TrOperand trq(lane, LQROW), trd(lane, DROW);
+    const TrOperand tr(lane, LQROW);
     const int wk_first = k0 + 32 * sub;   // first key of this wave
     // queries before the tile's first key cannot see any of its keys
     const int qstart = p.causal ? k0 : s0;
     const int nqt = (s1 - qstart + kQT - 1) / kQT;   // query tiles per head
     const int total = p.G * nqt;                     // (head, query tile) steps
-    const char *krow = kvt + (32 * sub + n) * LROW + map * D * 2;
-    // this wave's K rows (B operand of S = Q K^T), read into registers once
-    // the tile is in LDS
-    bf16x8 kf[NKS];
-    const char *vrow = kvt + KVB + (32 * sub + n) * LROW;
 
-    Stager<ROWB, LQROW, kQT> sq;
-    Stager<DROWB, DROW, kQT> sd;
+    Stager<ROWB, LQROW, kQT> sq, sd;
     // lse and D of the tile as [lse, D][map][row], so that the four rows
     // a lane's accumulator elements cover are one 16-byte read
     float lv = 0.f;   // one lse or D value per thread of the first 4 kQT
@@ -645,7 +648,7 @@ void bwd_dkdv(BwdParams p)
         const int valid = min(kQT, s1 - q0);
         const int64_t qrow0 = (int64_t)q0 * p.H + head;
         sq.load((const char *)(p.q + qrow0 * 2 * D), (int64_t)p.H * ROWB, valid);
-        sd.load((const char *)(p.do12 + qrow0 * 4 * D), (int64_t)p.H * DROWB, valid);
+        sd.load((const char *)(p.dpre + qrow0 * 2 * D), (int64_t)p.H * ROWB, valid);
         const int i = threadIdx.x;
         if (i < kQT * 4) {
             // i = (which * 2 + map) * kQT + row; which 0: lse, 1: D
@@ -659,144 +662,166 @@ void bwd_dkdv(BwdParams p)
         sq.store(stage);
         sd.store(stage + QB);
         if (threadIdx.x < kQT * 4)
-            ((float *)(stage + QB + DB))[threadIdx.x] = lv;
+            ((float *)(stage + 2 * QB))[threadIdx.x] = lv;
     };
-    auto compute = [&](int stp, const char *stage) __attribute__((always_inline)) {
-        const char *qt = stage, *dt = stage + QB;
-        const float *lt = (const float *)(stage + QB + DB) + map * kQT;
-        const float *ddt = lt + kQT * 2;
+    // wave-uniform: can any query of step stp's tile see a key of the wave?
+    auto visible = [&](int stp) __attribute__((always_inline)) {
         const int q0 = qstart + (stp % nqt) * kQT;
-        // wave-uniform: can any query of the tile see a key of the wave?
-        if (q0 >= s1 || (p.causal && q0 + kQT - 1 < wk_first))
+        return !(q0 >= s1 || (p.causal && q0 + kQT - 1 < wk_first));
+    };
+    auto compute_s = [&](int stp, const char *stage, char *wout) __attribute__((always_inline)) {
+        if (!visible(stp))
             return;
-        // S = Q K^T (queries x keys); lane owns key wk
-        f32x16 sa = f32x16{};
+        const char *qt = stage, *dt = stage + QB;
+        const float *tab = (const float *)(stage + 2 * QB);
+        const int q0 = qstart + (stp % nqt) * kQT;
+        const float nlam = -p.lam[g * p.G + stp / nqt];
+        // S_m = Q_m K_m^T (queries x keys); lane owns key wk
+        f32x16 s1a = f32x16{}, s2a = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-            const bf16x8 qa = *(const bf16x8 *)(qt + n * LQROW + (map * D + 16 * ks + 8 * h) * 2);
-            sa = mma(qa, kf[ks], sa);
+            const char *qa = qt + n * LQROW + (16 * ks + 8 * h) * 2;
+            s1a = mma(*(const bf16x8 *)qa, kf[0][ks], s1a);
+            s2a = mma(*(const bf16x8 *)(qa + D * 2), kf[1][ks], s2a);
         }
-        // dP = dO V^T
+        // dP = dpre V^T
         f32x16 dp = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < NVS; ++ks) {
-            const bf16x8 da = *(const bf16x8 *)(dt + n * DROW + (map * 2 * D + 16 * ks + 8 * h) * 2);
-            dp = mma(da, *(const bf16x8 *)(vrow + (16 * ks + 8 * h) * 2), dp);
-        }
-        bf16x8 bpk[2];   // P as the B operand of dV^T, packed at once
+        for (int ks = 0; ks < NVS; ++ks)
+            dp = mma(*(const bf16x8 *)(dt + n * LQROW + (16 * ks + 8 * h) * 2), vf[ks], dp);
         // queries before the wave's key get a score of -inf (probability 0);
         // wave-uniform: only tiles that reach the diagonal need the test
         if (p.causal && q0 < wk_first + 31) {
 #pragma unroll
             for (int a = 0; a < 16; ++a)
-                if (wk > q0 + acc_row(a, h))
-                    sa[a] = -INFINITY;
+                if (wk > q0 + acc_row(a, h)) {
+                    s1a[a] = -INFINITY;
+                    s2a[a] = -INFINITY;
+                }
         }
+        bf16x8 wpk[2];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             // rows 8 j + 4 h .. + 3 of the tile
-            const float4 l4 = *(const float4 *)(lt + 8 * j + 4 * h);
-            const float4 d4 = *(const float4 *)(ddt + 8 * j + 4 * h);
-            const float lr[4] = {l4.x, l4.y, l4.z, l4.w};
-            const float dr[4] = {d4.x, d4.y, d4.z, d4.w};
+            const int r0 = 8 * j + 4 * h;
+            const float4 l1 = *(const float4 *)(tab + r0);
+            const float4 l2 = *(const float4 *)(tab + kQT + r0);
+            const float4 e1 = *(const float4 *)(tab + 2 * kQT + r0);
+            const float4 e2 = *(const float4 *)(tab + 3 * kQT + r0);
+            const float lr1[4] = {l1.x, l1.y, l1.z, l1.w}, lr2[4] = {l2.x, l2.y, l2.z, l2.w};
+            const float dr1[4] = {e1.x, e1.y, e1.z, e1.w}, dr2[4] = {e2.x, e2.y, e2.z, e2.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int a = 4 * j + e;
-                const float pv = __builtin_amdgcn_exp2f(fmaf(sa[a], c, -lr[e]));
-                bpk[a / 8][a % 8] = (bf16)pv;
-                sa[a] = pv * (dp[a] - dr[e]);
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(s1a[a], c, -lr1[e]));
+                // -lambda P_2: map 2's probability with its dO factor
+                const float p2 = nlam * __builtin_amdgcn_exp2f(fmaf(s2a[a], c, -lr2[e]));
+                wpk[a / 8][a % 8] = (bf16)(p1 + p2);
+                s1a[a] = p1 * (dp[a] - dr1[e]);
+                s2a[a] = p2 * (dp[a] - dr2[e]);
             }
         }
-        // dV^T += dO^T P, dK^T += Q^T dS
+#pragma unroll
+        for (int ps = 0; ps < 2; ++ps)
+            *(bf16x8 *)(wout + ((sub * 2 + ps) * 64 + lane) * 16) = wpk[ps];
+        // dK_m^T += Q_m^T dS_m
 #pragma unroll
         for (int ps = 0; ps < 2; ++ps) {
-            const bf16x8 bs = pack8(sa, 8 * ps);
+            const bf16x8 b1 = pack8(s1a, 8 * ps), b2 = pack8(s2a, 8 * ps);
 #pragma unroll
-            for (int db = 0; db < NVB; ++db)
-                dva[db] = mma(trd.load(dt, DROW, 16 * ps, (map * 2 * D + 32 * db) * 2), bpk[ps],
-                              dva[db]);
-#pragma unroll
-            for (int db = 0; db < NKB; ++db)
-                dka[db] = mma(trq.load(qt, LQROW, 16 * ps, (map * D + 32 * db) * 2), bs, dka[db]);
+            for (int db = 0; db < NKB; ++db) {
+                acc[db] = mma(tr.load(qt, LQROW, 16 * ps, 32 * db * 2), b1, acc[db]);
+                acc[NKB + db] =
+                    mma(tr.load(qt, LQROW, 16 * ps, (D + 32 * db) * 2), b2, acc[NKB + db]);
+            }
         }
     };
-    auto step = [&](int stp, const char *cur, char *nxt) __attribute__((always_inline)) {
+    auto compute_v = [&](int stp, const char *stage, const char *win) __attribute__((always_inline)) {
+        if (!visible(stp))
+            return;
+        const char *dt = stage + QB;
+        // dV^T += dpre^T W
+#pragma unroll
+        for (int ps = 0; ps < 2; ++ps) {
+            const bf16x8 w = *(const bf16x8 *)(win + ((sub * 2 + ps) * 64 + lane) * 16);
+#pragma unroll
+            for (int db = 0; db < NVB; ++db)
+                acc[db] = mma(tr.load(dt, LQROW, 16 * ps, 32 * db * 2), w, acc[db]);
+        }
+    };
+
+    char *prv = stg + 2 * STB, *cur = stg, *nxt = stg + STB;
+    fetch(0);
+    put(cur);
+    __syncthreads();
+    for (int stp = 0; stp < total; ++stp) {
         const bool more = stp + 1 < total;
         if (more)
             fetch(stp + 1);
-        compute(stp, cur);
+        if (role == 0)
+            compute_s(stp, cur, wx + (stp & 1) * WXB);
+        else if (stp > 0)
+            compute_v(stp - 1, prv, wx + ((stp - 1) & 1) * WXB);
+        // the stage written now held tile stp - 2, which no wave reads
+        // after the barrier that ended step stp - 1
         if (more)
             put(nxt);
         __syncthreads();
-    };
-
-    fetch(0);
-    put(st0);
-    __syncthreads();
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-        kf[ks] = *(const bf16x8 *)(krow + (16 * ks + 8 * h) * 2);
-    for (int stp = 0; stp < total; stp += 2) {
-        step(stp, st0, st1);
-        if (stp + 1 < total)
-            step(stp + 1, st1, st0);
+        char *t = prv;
+        prv = cur;
+        cur = nxt;
+        nxt = t;
     }
+    if (role == 1)
+        compute_v(total - 1, prv, wx + ((total - 1) & 1) * WXB);
 
-    // dK of this map; dV summed over the two maps through LDS (the K/V
-    // tiles are no longer read: every wave passed the last barrier)
-    const float scale = rsqrtf((float)D);
-    const bool kok = wk < s1;
-    if (kok) {
-        bf16 *dst = p.dk + (((int64_t)wk * p.Hkv + g) * 2 + map) * D;
+    if (!kok)
+        return;
+    if (role == 0) {
+        const float scale = rsqrtf((float)D);
 #pragma unroll
-        for (int db = 0; db < NKB; ++db)
+        for (int m = 0; m < 2; ++m) {
+            bf16 *dst = p.dk + (kvrow * 2 + m) * D;
+#pragma unroll
+            for (int db = 0; db < NKB; ++db)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    bf16 vals[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        vals[e] = (bf16)(acc[m * NKB + db][4 * i + e] * scale);
+                    __builtin_memcpy(dst + 32 * db + 8 * i + 4 * h, vals, sizeof(vals));
+                }
+        }
+    } else {
+        bf16 *dst = p.dv + kvrow * (2 * D);
+#pragma unroll
+        for (int db = 0; db < NVB; ++db)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 bf16 vals[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    vals[e] = (bf16)(dka[db][4 * i + e] * scale);
+                    vals[e] = (bf16)acc[db][4 * i + e];
                 __builtin_memcpy(dst + 32 * db + 8 * i + 4 * h, vals, sizeof(vals));
             }
     }
-    float *xch = (float *)kvt;
-    if (map == 1) {
-#pragma unroll
-        for (int db = 0; db < NVB; ++db)
-#pragma unroll
-            for (int a = 0; a < 16; ++a)
-                xch[((sub * NVB + db) * 16 + a) * 64 + lane] = dva[db][a];
-    }
-    __syncthreads();
-    if (map == 1 || !kok)
-        return;
-    bf16 *dst = p.dv + ((int64_t)wk * p.Hkv + g) * (2 * D);
-#pragma unroll
-    for (int db = 0; db < NVB; ++db)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            bf16 vals[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                vals[e] = (bf16)(dva[db][4 * i + e] +
-                                 xch[((sub * NVB + db) * 16 + 4 * i + e) * 64 + lane]);
-            __builtin_memcpy(dst + 32 * db + 8 * i + 4 * h, vals, sizeof(vals));
-        }
 }
 
 struct BwdPlan {
-    size_t do12, dd, part_dw, part_dl, total;
+    size_t dpre, dd, lam, part_dw, part_dl, total;
 };
 
 BwdPlan bwd_plan(int64_t T, int H, int d)
 {
     BwdPlan pl;
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-    pl.do12 = up((size_t)T * H * 2 * (2 * d) * 2);
+    pl.dpre = up((size_t)T * H * (2 * d) * 2);
     pl.dd = up((size_t)T * H * 2 * 4);
+    pl.lam = up((size_t)H * 4);
     pl.part_dw = up((size_t)H * (kPrepPerHead / 4) * 2 * d * 4);
     pl.part_dl = up((size_t)H * (kPrepPerHead / 4) * 4);
-    pl.total = pl.do12 + pl.dd + pl.part_dw + pl.part_dl;
+    pl.total = pl.dpre + pl.dd + pl.lam + pl.part_dw + pl.part_dl;
     return pl;
 }
 
@@ -896,10 +921,15 @@ extern "C" int diffattn_bwd(int dtype, const void *q, const void *k, const void 
     p.dlk2 = dlambda_k2;
     p.dw = dsubln_weight;
     char *ws = (char *)workspace;
-    p.do12 = (bf16 *)ws;
-    p.dd = (float *)(ws + pl.do12);
-    p.part_dw = (float *)(ws + pl.do12 + pl.dd);
-    p.part_dl = (float *)(ws + pl.do12 + pl.dd + pl.part_dw);
+    p.dpre = (bf16 *)ws;
+    ws += pl.dpre;
+    p.dd = (float *)ws;
+    ws += pl.dd;
+    p.lam = (float *)ws;
+    ws += pl.lam;
+    p.part_dw = (float *)ws;
+    ws += pl.part_dw;
+    p.part_dl = (float *)ws;
     p.lambda_init = lambda_init;
     p.eps = eps;
     p.T = T;

@@ -219,3 +219,32 @@ def test_bwd_full_size_sampled(name):
     announce(f"{name}: " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()))
     for key, e in errs.items():
         assert e <= 2e-2, f"{name}: {key} relative max-abs {e:.3e}"
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_bwd_random_shapes(i):
+    """Seeded random shapes for the backward: sequence mixes, head
+    groupings, d, masking, per-head lambda with or without the weight."""
+    rng = np.random.default_rng(7000 + i)
+    d = int(rng.choice([32, 64]))
+    Hkv = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 2, 3, 4]))
+    lens = tuple(int(x) for x in rng.integers(0, 400, int(rng.integers(1, 5))))
+    if sum(lens) == 0:
+        lens = lens + (9,)
+    causal = bool(rng.integers(0, 2))
+    wl = custom("bwd_random", "bf16", lens, Hkv * G, Hkv, d, depth=2 + i, causal=causal,
+                seed=8000 + i)
+    inp = make_inputs(wl)
+    use_w = bool(rng.integers(0, 2))
+    if use_w:
+        inp.w = torch.from_numpy(rng.uniform(0.5, 1.5, 2 * d)).float()
+    if rng.integers(0, 2):
+        g = torch.Generator().manual_seed(9000 + i)
+        inp.lq1, inp.lk1, inp.lq2, inp.lk2 = [0.3 * torch.randn(Hkv * G, d, generator=g)
+                                              for _ in range(4)]
+    dy = dout_for(inp, 10 + i)
+    _, (got,) = gpu_grads(inp, dy, w=use_w)
+    worst = compare(got, oracle_grads(inp, dy, w=use_w),
+                    f"random {i}: lens {lens} H={Hkv * G} Hkv={Hkv} d={d} causal={causal}")
+    announce(f"random case {i}: worst err / bar {worst:.3f}")

@@ -297,3 +297,32 @@ def test_more_queries_than_keys_noncausal():
     err = max_abs(gpu_kv(inp), oracle_kv(inp))
     announce(f"nq > nk, non-causal: max-abs {err:.3e}")
     assert err <= TOL
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_shapes(i):
+    """Seeded random cache shapes: sequence counts, query and cache lengths
+    (empty sequences included), head groupings, d, masking, shared or
+    per-head lambda."""
+    rng = np.random.default_rng(4000 + i)
+    nseq = int(rng.integers(1, 9))
+    d = int(rng.choice([32, 64]))
+    Hkv = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 2, 3, 4, 8]))
+    causal = bool(rng.integers(0, 2))
+    ql = [int(x) for x in rng.integers(0, 6, nseq)]
+    kl = [int(x) for x in rng.integers(1, 3000, nseq)]
+    kl = [max(k, q) if causal else k for q, k in zip(ql, kl)]
+    if sum(ql) == 0:
+        ql[0] = 1
+    wl = custom_kv("random", "bf16", tuple(ql), tuple(kl), H=Hkv * G, Hkv=Hkv, d=d,
+                   depth=1 + i, causal=causal, seed=5000 + i)
+    inp = make_kv_inputs(wl)
+    lam = None
+    if rng.integers(0, 2):
+        g = torch.Generator().manual_seed(6000 + i)
+        lam = [0.2 * torch.randn(Hkv * G, d, generator=g) for _ in range(4)]
+    err = max_abs(gpu_kv(inp, lam=lam), oracle_kv(inp, lam=lam))
+    announce(f"random case {i}: q {ql} k {kl} H={Hkv * G} Hkv={Hkv} d={d} "
+             f"causal={causal} per-head={lam is not None}: max-abs {err:.3e}")
+    assert err <= TOL
