@@ -408,7 +408,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 void bwd_dq(BwdParams p)
 {
     constexpr int ROWB = 2 * D * 2;        // K or V row bytes
-    constexpr int LROW = ROWB + 16;        // padded LDS row
+    // K rows are read both as plain 16-byte rows and through the transposing
+    // read (4 rows x 64 bytes); a 48-byte pad keeps the plain reads on
+    // distinct banks and starts the transposed rows 48 bytes apart
+    constexpr int LROW = ROWB + 48;
     constexpr int NKS = D / 16;            // QK contraction steps
     constexpr int NVS = 2 * D / 16;        // dO V contraction steps
     constexpr int NDB = D / 32;            // 32-dim blocks of dQ
@@ -562,16 +565,18 @@ void bwd_dq(BwdParams p)
 
 // ---------------------------------------------------------------------------
 // dkdv: key-outer.  Waves 0..3 (the S role) take 32 keys each and both
-// maps: S_m = Q_m K_m^T, P_m, dP = dpre V^T (once: dO_2 = -lambda dO_1, so
-// dP_2 = -lambda dP_1), dS_m, dK_m^T += Q_m^T dS_m, and W = P_1 - lambda P_2
-// rounded to bf16, which they hand to waves 4..7 (the V role, same keys)
-// through LDS.  The V-role waves add dV^T += dpre^T W one query tile
-// behind.  Forming P_1 - lambda P_2 in fp32 before rounding keeps dV
-// accurate where the two maps nearly cancel (the first key of a sequence
-// when lambda is near 1, where both maps put all weight on that key).
-// K and V rows of the S-role waves live in registers; 32-row query tiles
-// (Q, dpre, lse, D) rotate through three LDS stages: the S role computes on
-// tile i while the V role reads tile i - 1 and tile i + 1 is written.
+// maps: S_m = Q_m K_m^T, P_m, dS_1 = P_1 (dP - D'_1),
+// dS_2 = -lambda P_2 (dP - D'_2), dK_m^T += Q_m^T dS_m, and
+// W = P_1 - lambda P_2 rounded to bf16.  Waves 4..7 (the V role, same
+// keys) compute dP = dpre V^T one query tile ahead (one product serves
+// both maps: dO_2 = -lambda dO_1) and add dV^T += dpre^T W one query tile
+// behind; dP and W travel through LDS.  Forming P_1 - lambda P_2 in fp32
+// before rounding keeps dV accurate where the two maps nearly cancel (the
+// first key of a sequence when lambda is near 1, where both maps put all
+// weight on that key).  K rows (S role) and V rows (V role) live in
+// registers; 32-row query tiles (Q, dpre, lse, D') rotate through four LDS
+// stages: at step i the S role computes on tile i, the V role reads tiles
+// i + 1 and i - 1, and tile i + 2 is written.
 constexpr int kQT = 32;
 
 template <int D>
@@ -588,12 +593,14 @@ void bwd_dkdv(BwdParams p)
     constexpr int NVS = 2 * D / 16;
     constexpr int NKB = D / 32;              // 32-dim blocks of dK (per map)
     constexpr int NVB = 2 * D / 32;          // 32-dim blocks of dV
-    static_assert(2 * NKB == NVB, "both roles use the same accumulators");
+    static_assert(2 * NKB == NVB && 2 * NKS == NVS, "both roles share registers");
     constexpr int QB = kQT * LQROW;          // Q tile bytes
     constexpr int STB = 2 * QB + kQT * 4 * 4;   // one stage: Q, dpre, lse[2], D[2]
-    constexpr int WXB = kSubs * 2 * 64 * 16; // one W hand-over buffer
-    __shared__ __attribute__((aligned(16))) char stg[3 * STB];
+    constexpr int WXB = kSubs * 2 * 64 * 16;    // one W hand-over buffer (bf16)
+    constexpr int PXB = kSubs * 4 * 64 * 16;    // one dP hand-over buffer (fp32)
+    __shared__ __attribute__((aligned(16))) char stg[4 * STB];
     __shared__ __attribute__((aligned(16))) char wx[2 * WXB];
+    __shared__ __attribute__((aligned(16))) char px[2 * PXB];
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int n = lane & 31, h = lane >> 5;
@@ -611,20 +618,14 @@ void bwd_dkdv(BwdParams p)
     const int wk = k0 + 32 * sub + n;   // this lane's key
     const bool kok = wk < s1;
     const int64_t kvrow = (int64_t)wk * p.Hkv + g;
-    // this wave's K rows (B operands of S_m = Q_m K_m^T) and V rows (B
-    // operand of dP = dpre V^T); the V role does not need them
-    bf16x8 kf[2][NKS], vf[NVS];
+    // B operands from this wave's key rows: S role K_1, K_2 (of S_m =
+    // Q_m K_m^T), V role V (of dP = dpre V^T)
+    bf16x8 kv[NVS];
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-            kf[m][ks] = (kok && role == 0)
-                            ? *(const bf16x8 *)(p.k + kvrow * 2 * D + m * D + 16 * ks + 8 * h)
-                            : bf16x8{};
-#pragma unroll
-    for (int ks = 0; ks < NVS; ++ks)
-        vf[ks] = (kok && role == 0) ? *(const bf16x8 *)(p.v + kvrow * 2 * D + 16 * ks + 8 * h)
-                                    : bf16x8{};
+    for (int i = 0; i < NVS; ++i) {
+        const bf16 *src = role == 0 ? p.k : p.v;
+        kv[i] = kok ? *(const bf16x8 *)(src + kvrow * 2 * D + 16 * i + 8 * h) : bf16x8{};
+    }
     // S role: dK of map m in acc[m * NKB + db]; V role: dV in acc[db]
     f32x16 acc[NVB];
 #pragma unroll
@@ -639,9 +640,9 @@ void bwd_dkdv(BwdParams p)
     const int total = p.G * nqt;                     // (head, query tile) steps
 
     Stager<ROWB, LQROW, kQT> sq, sd;
-    // lse and D of the tile as [lse, D][map][row], so that the four rows
+    // lse and D' of the tile as [lse, D'][map][row], so that the four rows
     // a lane's accumulator elements cover are one 16-byte read
-    float lv = 0.f;   // one lse or D value per thread of the first 4 kQT
+    float lv = 0.f;   // one lse or D' value per thread of the first 4 kQT
     auto fetch = [&](int stp) __attribute__((always_inline)) {
         const int head = g * p.G + stp / nqt;
         const int q0 = qstart + (stp % nqt) * kQT;
@@ -651,7 +652,7 @@ void bwd_dkdv(BwdParams p)
         sd.load((const char *)(p.dpre + qrow0 * 2 * D), (int64_t)p.H * ROWB, valid);
         const int i = threadIdx.x;
         if (i < kQT * 4) {
-            // i = (which * 2 + map) * kQT + row; which 0: lse, 1: D
+            // i = (which * 2 + map) * kQT + row; which 0: lse, 1: D'
             const int which = i / (kQT * 2), mp = (i / kQT) & 1, r = i % kQT;
             const float *src = which ? p.dd : p.lse;
             lv = r < valid ? src[(qrow0 + (int64_t)r * p.H) * 2 + mp]
@@ -664,16 +665,33 @@ void bwd_dkdv(BwdParams p)
         if (threadIdx.x < kQT * 4)
             ((float *)(stage + 2 * QB))[threadIdx.x] = lv;
     };
+    auto stage_of = [&](int stp) __attribute__((always_inline)) { return stg + (stp & 3) * STB; };
     // wave-uniform: can any query of step stp's tile see a key of the wave?
     auto visible = [&](int stp) __attribute__((always_inline)) {
         const int q0 = qstart + (stp % nqt) * kQT;
         return !(q0 >= s1 || (p.causal && q0 + kQT - 1 < wk_first));
     };
-    auto compute_s = [&](int stp, const char *stage, char *wout) __attribute__((always_inline)) {
+    // V role: dP = dpre V^T of step stp (queries x keys; lane owns key wk),
+    // handed over as 16 floats per lane
+    auto compute_dp = [&](int stp) __attribute__((always_inline)) {
         if (!visible(stp))
             return;
-        const char *qt = stage, *dt = stage + QB;
-        const float *tab = (const float *)(stage + 2 * QB);
+        const char *dt = stage_of(stp) + QB;
+        f32x16 dp = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < NVS; ++ks)
+            dp = mma(*(const bf16x8 *)(dt + n * LQROW + (16 * ks + 8 * h) * 2), kv[ks], dp);
+        char *out = px + (stp & 1) * PXB + sub * 4 * 1024 + lane * 16;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            *(float4 *)(out + j * 1024) =
+                float4{dp[4 * j], dp[4 * j + 1], dp[4 * j + 2], dp[4 * j + 3]};
+    };
+    auto compute_s = [&](int stp) __attribute__((always_inline)) {
+        if (!visible(stp))
+            return;
+        const char *qt = stage_of(stp);
+        const float *tab = (const float *)(qt + 2 * QB);
         const int q0 = qstart + (stp % nqt) * kQT;
         const float nlam = -p.lam[g * p.G + stp / nqt];
         // S_m = Q_m K_m^T (queries x keys); lane owns key wk
@@ -681,14 +699,9 @@ void bwd_dkdv(BwdParams p)
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             const char *qa = qt + n * LQROW + (16 * ks + 8 * h) * 2;
-            s1a = mma(*(const bf16x8 *)qa, kf[0][ks], s1a);
-            s2a = mma(*(const bf16x8 *)(qa + D * 2), kf[1][ks], s2a);
+            s1a = mma(*(const bf16x8 *)qa, kv[ks], s1a);
+            s2a = mma(*(const bf16x8 *)(qa + D * 2), kv[NKS + ks], s2a);
         }
-        // dP = dpre V^T
-        f32x16 dp = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < NVS; ++ks)
-            dp = mma(*(const bf16x8 *)(dt + n * LQROW + (16 * ks + 8 * h) * 2), vf[ks], dp);
         // queries before the wave's key get a score of -inf (probability 0);
         // wave-uniform: only tiles that reach the diagonal need the test
         if (p.causal && q0 < wk_first + 31) {
@@ -699,6 +712,7 @@ void bwd_dkdv(BwdParams p)
                     s2a[a] = -INFINITY;
                 }
         }
+        const char *pin = px + (stp & 1) * PXB + sub * 4 * 1024 + lane * 16;
         bf16x8 wpk[2];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -708,8 +722,10 @@ void bwd_dkdv(BwdParams p)
             const float4 l2 = *(const float4 *)(tab + kQT + r0);
             const float4 e1 = *(const float4 *)(tab + 2 * kQT + r0);
             const float4 e2 = *(const float4 *)(tab + 3 * kQT + r0);
+            const float4 d4 = *(const float4 *)(pin + j * 1024);
             const float lr1[4] = {l1.x, l1.y, l1.z, l1.w}, lr2[4] = {l2.x, l2.y, l2.z, l2.w};
             const float dr1[4] = {e1.x, e1.y, e1.z, e1.w}, dr2[4] = {e2.x, e2.y, e2.z, e2.w};
+            const float dp[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int a = 4 * j + e;
@@ -717,10 +733,11 @@ void bwd_dkdv(BwdParams p)
                 // -lambda P_2: map 2's probability with its dO factor
                 const float p2 = nlam * __builtin_amdgcn_exp2f(fmaf(s2a[a], c, -lr2[e]));
                 wpk[a / 8][a % 8] = (bf16)(p1 + p2);
-                s1a[a] = p1 * (dp[a] - dr1[e]);
-                s2a[a] = p2 * (dp[a] - dr2[e]);
+                s1a[a] = p1 * (dp[e] - dr1[e]);
+                s2a[a] = p2 * (dp[e] - dr2[e]);
             }
         }
+        char *wout = wx + (stp & 1) * WXB;
 #pragma unroll
         for (int ps = 0; ps < 2; ++ps)
             *(bf16x8 *)(wout + ((sub * 2 + ps) * 64 + lane) * 16) = wpk[ps];
@@ -736,11 +753,12 @@ void bwd_dkdv(BwdParams p)
             }
         }
     };
-    auto compute_v = [&](int stp, const char *stage, const char *win) __attribute__((always_inline)) {
+    // V role: dV^T += dpre^T W of step stp
+    auto compute_v = [&](int stp) __attribute__((always_inline)) {
         if (!visible(stp))
             return;
-        const char *dt = stage + QB;
-        // dV^T += dpre^T W
+        const char *dt = stage_of(stp) + QB;
+        const char *win = wx + (stp & 1) * WXB;
 #pragma unroll
         for (int ps = 0; ps < 2; ++ps) {
             const bf16x8 w = *(const bf16x8 *)(win + ((sub * 2 + ps) * 64 + lane) * 16);
@@ -750,30 +768,39 @@ void bwd_dkdv(BwdParams p)
         }
     };
 
-    char *prv = stg + 2 * STB, *cur = stg, *nxt = stg + STB;
+    // prologue: tiles 0 and 1 staged, dP of tile 0 handed over
     fetch(0);
-    put(cur);
+    put(stage_of(0));
+    if (total > 1)
+        fetch(1);
     __syncthreads();
+    if (role == 1)
+        compute_dp(0);
+    if (total > 1)
+        put(stage_of(1));
+    __syncthreads();
+    // step i: the S role on tile i (dP from the V role's step i - 1); the V
+    // role's dP of tile i + 1 and dV of tile i - 1; tile i + 2 written into
+    // the stage of tile i - 2, which no wave reads after the barrier that
+    // ended step i - 1
     for (int stp = 0; stp < total; ++stp) {
-        const bool more = stp + 1 < total;
+        const bool more = stp + 2 < total;
         if (more)
-            fetch(stp + 1);
-        if (role == 0)
-            compute_s(stp, cur, wx + (stp & 1) * WXB);
-        else if (stp > 0)
-            compute_v(stp - 1, prv, wx + ((stp - 1) & 1) * WXB);
-        // the stage written now held tile stp - 2, which no wave reads
-        // after the barrier that ended step stp - 1
+            fetch(stp + 2);
+        if (role == 0) {
+            compute_s(stp);
+        } else {
+            if (stp + 1 < total)
+                compute_dp(stp + 1);
+            if (stp > 0)
+                compute_v(stp - 1);
+        }
         if (more)
-            put(nxt);
+            put(stage_of(stp + 2));
         __syncthreads();
-        char *t = prv;
-        prv = cur;
-        cur = nxt;
-        nxt = t;
     }
     if (role == 1)
-        compute_v(total - 1, prv, wx + ((total - 1) & 1) * WXB);
+        compute_v(total - 1);
 
     if (!kok)
         return;
