@@ -21,14 +21,17 @@
 // -----------------------
 // One wave = (sequence s, KV head g, block of 16 query rows, split of Ck
 // keys).  A row is (query i, head gh of the group), row r = i * G + gh.
-// Waves are independent: each has a private LDS slice for its V tile and no
-// barrier is ever taken.  Per 32-key block:
-//   * K of both maps goes global -> registers directly in the A-operand
-//     layout of v_mfma_f32_16x16x32_bf16 (lane (key n, quarter q) holds
-//     8 consecutive dims), one block ahead of use;
-//   * V goes global -> registers one block ahead, then into the wave's
-//     padded LDS tile, and comes back through the transposing read
-//     ds_read_b64_tr_b16 as the V^T operand;
+// Waves are independent: each has a private LDS slice for its K and V tiles
+// and no barrier is ever taken.  Per 32-key block:
+//   * K and V go global -> registers one block ahead of use, in whole rows
+//     (one load instruction covers consecutive rows) and with nontemporal
+//     loads, then into the wave's padded LDS tiles.  Loading K straight
+//     into the MFMA operand layout instead (16 keys x 64 bytes per load
+//     instruction) read the cache about 7% slower;
+//   * K comes back from LDS in the A-operand layout of
+//     v_mfma_f32_16x16x32_bf16 (lane (key n, quarter q) holds 8 consecutive
+//     dims), V through the transposing read ds_read_b64_tr_b16 as the V^T
+//     operand;
 //   * S^T [16 keys x 16 rows] = K Q^T per map and 16-key half: each lane
 //     owns one row and 4 keys of each half, so the accumulator is directly
 //     the P^T operand of the PV product when the contraction runs over keys
@@ -202,8 +205,12 @@ void diffattn_kv_partial(KvParams p)
     // padded V row: the 8 rows one half-wave reads per transposing read
     // start 32 bytes apart modulo 256 and cover all banks once
     constexpr int VROWB = ROWB + 32;
+    // padded K row: the 16 rows of one operand read start 16 bytes apart
+    // modulo 256 (d = 64; d = 32: distinct multiples of 16)
+    constexpr int KROWB = ROWB + 16;
     static_assert(D % 32 == 0 && NVL * RPL == kBlockKeys, "unsupported d");
 
+    __shared__ __attribute__((aligned(16))) char klds[kWavesPerBlock][kBlockKeys * KROWB];
     __shared__ __attribute__((aligned(16))) char vlds[kWavesPerBlock][kBlockKeys * VROWB];
 
     const int wave = threadIdx.x >> 6;
@@ -280,48 +287,38 @@ void diffattn_kv_partial(KvParams p)
     const int64_t rowstride = (int64_t)p.Hkv * ROWB;    // bytes between keys
     const char *kbase = (const char *)p.k + (int64_t)ka * rowstride + (int64_t)g * ROWB;
     const char *vbase = (const char *)p.v + (int64_t)ka * rowstride + (int64_t)g * ROWB;
+    char *kl = klds[wave];
     char *vl = vlds[wave];
-    // K register tile: kf[half][map][ks], lane (key n, quarter qq) holds dims
-    // 32 ks + 8 qq .. + 7 of key 16 half + n
-    u32x4 kf[2][2][NKS], kn[2][2][NKS];
-    u32x4 vn[NVL];
+    // K and V of the next block travel through registers in whole rows (a
+    // load instruction covers RPL consecutive rows), with nontemporal loads:
+    // the cache is read once
+    u32x4 kn[NVL], vn[NVL];
     const int vrow = lane / CPR;
     const int vcol = (lane % CPR) * 16;
     auto load_block = [&](int kb) __attribute__((always_inline)) {
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-            const int key = min(kb + 16 * hf + n, nk - 1);
-            const char *src = kbase + key * rowstride + 16 * qq;
-#pragma unroll
-            for (int m = 0; m < 2; ++m)
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks)
-                    kn[hf][m][ks] = *(const u32x4 *)(src + m * (ROWB / 2) + 64 * ks);
+        for (int i = 0; i < NVL; ++i) {
+            const int64_t off = (int64_t)min(kb + vrow + RPL * i, nk - 1) * rowstride + vcol;
+            kn[i] = __builtin_nontemporal_load((const u32x4 *)(kbase + off));
+            vn[i] = __builtin_nontemporal_load((const u32x4 *)(vbase + off));
         }
+    };
+    auto store_kv = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < NVL; ++i) {
-            const int key = min(kb + vrow + RPL * i, nk - 1);
-            vn[i] = *(const u32x4 *)(vbase + key * rowstride + vcol);
+            *(u32x4 *)(kl + (vrow + RPL * i) * KROWB + vcol) = kn[i];
+            *(u32x4 *)(vl + (vrow + RPL * i) * VROWB + vcol) = vn[i];
         }
     };
-    auto store_v = [&]() __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < NVL; ++i)
-            *(u32x4 *)(vl + (vrow + RPL * i) * VROWB + vcol) = vn[i];
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-            for (int m = 0; m < 2; ++m)
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks)
-                    kf[hf][m][ks] = kn[hf][m][ks];
-    };
+    // K operand read of this lane: key 16 half + n, dims 32 ks + 8 qq .. + 7
+    // of map m
+    const char *krd = kl + n * KROWB + 16 * qq;
     // transposing-read base of this lane: row 4 qq + (n / 4), dims 4 (n % 4)
     const int trbase = (4 * qq + (n >> 2)) * VROWB + 8 * (n & 3);
 
     if (kstart < kend) {
         load_block(kstart);
-        store_v();
+        store_kv();
     }
     for (int kb = kstart; kb < kend; kb += kBlockKeys) {
         const bool more = kb + kBlockKeys < kend;
@@ -337,7 +334,8 @@ void diffattn_kv_partial(KvParams p)
                 f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks)
-                    acc = mma(__builtin_bit_cast(bf16x8, kf[hf][m][ks]), qf[m][ks], acc);
+                    acc = mma(*(const bf16x8 *)(krd + 16 * hf * KROWB + m * (ROWB / 2) + 64 * ks),
+                              qf[m][ks], acc);
                 sc[m][hf] = acc * c;
             }
         // keys past the sequence end or above the row's causal limit
@@ -405,7 +403,7 @@ void diffattn_kv_partial(KvParams p)
             o[1][t] = mma(va, pf[1], o[1][t]);
         }
         if (more)
-            store_v();
+            store_kv();
     }
 
     // ---- partial of this split -------------------------------------------
@@ -558,20 +556,25 @@ void diffattn_kv_combine(KvParams p)
 }
 
 // Split policy: keys per split ck chosen from the total number of cache
-// keys Tk so that all sequences together have about 4096 busy waves (about
-// 16 per CU, every one with the same ck keys whatever the length mix), but
-// at least 128 keys per split so the partial traffic stays small against
-// the cache bytes each wave reads.  With ck >= Tk * U / target (U = waves
-// per split: KV heads x 16-row blocks), the splits of all sequences number
-// at most Tk / ck + nseq <= target / U + nseq, a bound that does not depend
-// on Tk: it sizes the workspace (with nseq * ceil(max_k / 128), whichever
-// is smaller).
+// keys Tk so that all sequences together have at most kTargetWaves busy
+// waves (one per SIMD), every one with the same ck keys whatever the length
+// mix: with U waves per split (KV heads x 16-row blocks) and
+// ck >= Tk / (kTargetWaves / U - nseq), the splits of all sequences number
+// at most Tk / ck + nseq <= kTargetWaves / U (each sequence's last split may
+// be short), so no launch spills a few waves into a second round.  When the
+// sequences alone exceed that, every sequence is one split.  At least 128
+// keys per split keep the partial traffic small against the cache bytes each
+// wave reads.  Measured on 64 x 8192, 32 x [1024, 32768] (4 queries) and
+// 8 x 4097 caches: this rule at 1024 waves beat 512, 768 and 2048 waves, and
+// the earlier rule ck = Tk U / W at W = 1024 ... 8192 waves.  The bound
+// nseq + kTargetWaves / U on the splits, which does not depend on Tk, sizes
+// the workspace (with nseq * ceil(max_k / 128), whichever is smaller).
 struct KvPlan {
     int nrb, nslots, ck, rmax;
     size_t ws_o_bytes, ws_ml_bytes;
 };
 
-constexpr int64_t kTargetWaves = 4096;
+constexpr int64_t kTargetWaves = 1024;
 
 // Tk < 0: the workspace bound only (ck left 0)
 bool make_plan(int nseq, int max_q, int max_k, int G, int Hkv, int d, int64_t Tk, KvPlan &pl)
@@ -592,7 +595,8 @@ bool make_plan(int nseq, int max_q, int max_k, int G, int Hkv, int d, int64_t Tk
     pl.nslots = (int)nslots;
     pl.ck = 0;
     if (Tk >= 0) {
-        int64_t ck = (Tk * per_split + kTargetWaves - 1) / kTargetWaves;
+        const int64_t fit = kTargetWaves / per_split - nseq;   // splits beyond one per sequence
+        int64_t ck = fit > 0 ? (Tk + fit - 1) / fit : max_k;
         if (ck < 128)
             ck = 128;
         ck = (ck + kBlockKeys - 1) / kBlockKeys * kBlockKeys;
