@@ -17,8 +17,8 @@
 //           are dO_1 = dpre and dO_2 = -lambda dpre, and -lambda is applied
 //           in fp32 where map 2 uses it), D'_m = <dpre, O_m> from the
 //           rounded dpre (so that the softmax gradients of a row sum to
-//           zero), lambda per head, and per-workgroup partial sums of the
-//           weight and lambda gradients.
+//           zero; stored as D'_1 and lambda D'_2), lambda per head, and
+//           per-workgroup partial sums of the weight and lambda gradients.
 //  reduce   one workgroup: the partial sums in a fixed order, and the
 //           lambda-vector gradients by the chain rule.
 //  dq       query-outer, as the forward: one workgroup = (sequence, head,
@@ -26,13 +26,14 @@
 //           double-buffered in LDS (the next tile travels through registers
 //           while the current one is used): S^T = K Q^T,
 //           P^T = exp2(S^T c - lse), dP'^T = V dpre^T,
-//           dS'^T = P^T (dP'^T - D'), dQ^T += K^T dS'^T (K^T through the
-//           transposing LDS read, dS'^T straight from the accumulator);
-//           map 2's dQ is scaled by -lambda at the end.
+//           dS_1^T = P_1^T (dP'^T - D'_1) or
+//           dS_2^T = P_2^T (-lambda dP'^T + lambda D'_2), dQ^T += K^T dS^T
+//           (K^T through the transposing LDS read, dS^T straight from the
+//           accumulator).
 //  dkdv     key-outer: one workgroup = (sequence, KV head, 128 keys).  Four
 //           waves (32 keys each, both maps) compute S_m = Q_m K_m^T, P_m,
 //           dP = dpre V^T once for both maps, dS_1 = P_1 (dP - D'_1),
-//           dS_2 = -lambda P_2 (dP - D'_2) and dK_m^T += Q_m^T dS_m, and
+//           dS_2 = P_2 (-lambda dP + lambda D'_2) and dK_m^T += Q_m^T dS_m, and
 //           pass W = P_1 - lambda P_2 (formed in fp32, then rounded) through
 //           LDS to the other four waves, which add dV^T += dpre^T W one
 //           query tile later.  Query tiles (Q, dpre, lse, D') of all G
@@ -128,7 +129,7 @@ struct BwdParams {
     float *dlq1, *dlk1, *dlq2, *dlk2, *dw;
     // workspace
     bf16 *dpre;          // [T][H][2d]: dO_1 = dpre, dO_2 = -lambda dpre
-    float *dd;           // [T][H][2]: <dpre, O_1>, <dpre, O_2>
+    float *dd;           // [T][H][2]: <dpre, O_1>, lambda <dpre, O_2>
     float *lam;          // [H]
     float *part_dw;      // [nprep][2d]
     float *part_dl;      // [nprep]
@@ -276,7 +277,7 @@ __global__ __launch_bounds__(256) void bwd_prep(BwdParams p)
             store_bf16(p.dpre + row * (2 * D) + CPL * l16, b1);
             if (l16 == 0) {
                 p.dd[row * 2] = d1;
-                p.dd[row * 2 + 1] = d2;
+                p.dd[row * 2 + 1] = lam * d2;
             }
         }
     }
@@ -441,6 +442,9 @@ void bwd_dq(BwdParams p)
     const int64_t qrow = (int64_t)wq * p.H + head;
 
     bf16x8 qf[NKS], df[NVS];
+    // dS = P (dpf dP' - dval) with dP' = dpre V^T: map 1 dpf = 1, dval = D'_1;
+    // map 2 dpf = -lambda, dval = -lambda D'_2 (dO_2 = -lambda dpre)
+    const float dpf = map ? -p.lam[head] : 1.f;
     float lse = INFINITY, dval = 0.f;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
@@ -450,7 +454,7 @@ void bwd_dq(BwdParams p)
         df[ks] = qok ? *(const bf16x8 *)(p.dpre + qrow * (2 * D) + 16 * ks + 8 * h) : bf16x8{};
     if (qok) {
         lse = p.lse[qrow * 2 + map];
-        dval = p.dd[qrow * 2 + map];
+        dval = map ? -p.dd[qrow * 2 + 1] : p.dd[qrow * 2];
     }
     f32x16 dqa[NDB];
 #pragma unroll
@@ -514,7 +518,7 @@ void bwd_dq(BwdParams p)
 #pragma unroll
             for (int a = 0; a < 16; ++a) {
                 const float pv = __builtin_amdgcn_exp2f(fmaf(sa[a], c, -lse));
-                sa[a] = pv * (dp[a] - dval);
+                sa[a] = pv * fmaf(dpf, dp[a], -dval);
             }
             // dQ^T += K^T dS^T
 #pragma unroll
@@ -547,9 +551,7 @@ void bwd_dq(BwdParams p)
     }
     if (!qok)
         return;
-    // map 2 ran on dO = dpre and D = <dpre, O_2>: its dS and dQ carry the
-    // factor -lambda, applied here in fp32
-    const float scale = rsqrtf((float)D) * (map ? -p.lam[head] : 1.f);
+    const float scale = rsqrtf((float)D);
     bf16 *dst = p.dq + (qrow * 2 + map) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -640,8 +642,9 @@ void bwd_dkdv(BwdParams p)
     const int total = p.G * nqt;                     // (head, query tile) steps
 
     Stager<ROWB, LQROW, kQT> sq, sd;
-    // lse and D' of the tile as [lse, D'][map][row], so that the four rows
-    // a lane's accumulator elements cover are one 16-byte read
+    // lse, and D'_1 or lambda D'_2, of the tile as [lse, D][map][row], so
+    // that the four rows a lane's accumulator elements cover are one 16-byte
+    // read
     float lv = 0.f;   // one lse or D' value per thread of the first 4 kQT
     auto fetch = [&](int stp) __attribute__((always_inline)) {
         const int head = g * p.G + stp / nqt;
@@ -730,11 +733,12 @@ void bwd_dkdv(BwdParams p)
             for (int e = 0; e < 4; ++e) {
                 const int a = 4 * j + e;
                 const float p1 = __builtin_amdgcn_exp2f(fmaf(s1a[a], c, -lr1[e]));
-                // -lambda P_2: map 2's probability with its dO factor
-                const float p2 = nlam * __builtin_amdgcn_exp2f(fmaf(s2a[a], c, -lr2[e]));
-                wpk[a / 8][a % 8] = (bf16)(p1 + p2);
+                const float p2 = __builtin_amdgcn_exp2f(fmaf(s2a[a], c, -lr2[e]));
+                // W = P_1 - lambda P_2; dS_2 = P_2 (-lambda dP + lambda D'_2),
+                // the table holding lambda D'_2
+                wpk[a / 8][a % 8] = (bf16)fmaf(nlam, p2, p1);
                 s1a[a] = p1 * (dp[e] - dr1[e]);
-                s2a[a] = p2 * (dp[e] - dr2[e]);
+                s2a[a] = p2 * fmaf(nlam, dp[e], dr2[e]);
             }
         }
         char *wout = wx + (stp & 1) * WXB;
