@@ -178,6 +178,24 @@ def test_many_sequences_split_scan():
     assert err <= TOL
 
 
+def test_one_split_per_sequence():
+    """More sequences x KV heads than the split plan's wave budget (300 x 4
+    against 1024): every sequence becomes a single split of the longest
+    cache's length, whatever its own length, including empty ones."""
+    rng = np.random.default_rng(31)
+    nseq = 300
+    kl = [int(x) for x in rng.integers(1, 400, nseq)]
+    ql = [int(x) for x in rng.integers(1, 3, nseq)]
+    for s in (5, 64, 299):
+        ql[s], kl[s] = 0, 0
+    wl = custom_kv("one_split", "bf16", tuple(ql), tuple(kl), H=8, Hkv=4, d=64,
+                   depth=5, seed=31)
+    inp = make_kv_inputs(wl)
+    err = max_abs(gpu_kv(inp), oracle_kv(inp))
+    announce(f"one split per sequence (Tk={sum(kl)}): max-abs {err:.3e}")
+    assert err <= TOL
+
+
 def test_long_cache_many_splits():
     """One long sequence with several new queries: many key splits per row
     block, and the causal limit inside the last split."""
