@@ -1,0 +1,24 @@
+"""The cancellation ratio used by the parity tests, pinned to its closed form
+on the CPU."""
+
+import torch
+
+import oracle
+from conditioning import cancellation_ratio
+from workloads import custom, make_inputs
+
+
+def test_cancellation_ratio_first_row_closed_form():
+    """At the first token of a causal sequence both maps put all weight on
+    V[0], so pre = (1 - lambda) V[0] and the ratio is |1 - lambda| exactly
+    (CPU only)."""
+    wl = custom("ratio", "bf16", (3, 5), 4, 2, 16, depth=3, seed=5)
+    inp = make_inputs(wl)
+    g = torch.Generator().manual_seed(6)
+    inp.lq1, inp.lk1, inp.lq2, inp.lk2 = [0.4 * torch.randn(4, 16, generator=g)
+                                          for _ in range(4)]
+    lam0 = oracle.lambda_init(inp.depth)
+    for t in (0, 3):
+        for h in range(4):
+            lam = oracle.lam(inp.lq1[h], inp.lk1[h], inp.lq2[h], inp.lk2[h], lam0)
+            assert abs(cancellation_ratio(inp, t, h) - abs(1 - lam)) < 1e-6 * max(1, abs(1 - lam))

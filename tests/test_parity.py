@@ -12,6 +12,7 @@ import torch
 
 import oracle
 import workloads
+from conditioning import cancellation_ratio
 from workloads import WORKLOADS, custom, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -297,7 +298,10 @@ def test_per_head_lambda(dtype, d, H, Hkv):
 # ---------------------------------------------------------------------------
 # seeded random shapes: sequence mixes whose tile counts are odd and even,
 # partial last tiles seen by some waves of a workgroup and not others, every
-# head-grouping, both maskings, with and without per-head lambda
+# head-grouping, both maskings, with and without per-head lambda (vectors at
+# 0.2 scale, so some heads get lambda near 1 and some rows nearly cancel:
+# case 65 has one such row, token 1 of a sequence in a head with lambda
+# 0.9885, where rms(pre) is 0.042 rms(O_1))
 
 def random_case(i):
     rng = np.random.default_rng(1000 + i)
@@ -308,7 +312,26 @@ def random_case(i):
     return dtype, d, Hkv * G, Hkv, lens, bool(rng.integers(0, 2)), bool(rng.integers(0, 2))
 
 
-@pytest.mark.parametrize("i", range(20))
+def check_rows(got, ref, dtype, inp):
+    """Every output row within the bar; for bf16, a row whose two maps cancel
+    (rms(pre) < 0.1 rms(O_1)) is held to the bar times 0.1 / that ratio
+    instead: the RMSNorm divides the fixed bf16 rounding of the
+    probabilities (the PV operand) by rms(pre)."""
+    g = got.float().cpu().double().numpy()
+    assert np.all(np.isfinite(g)), "non-finite GPU output"
+    if not ref.size:
+        return 0.0
+    row_err = np.abs(g - ref).max(axis=2)
+    for t, h in np.argwhere(row_err > TOL[dtype]):
+        assert dtype == "bf16", (t, h, row_err[t, h])
+        ratio = cancellation_ratio(inp, int(t), int(h))
+        announce(f"row (token {t}, head {h}): max-abs {row_err[t, h]:.3e}, "
+                 f"rms(pre)/rms(O_1) {ratio:.4f}")
+        assert ratio < 0.1 and row_err[t, h] <= TOL[dtype] * 0.1 / ratio
+    return float(row_err.max())
+
+
+@pytest.mark.parametrize("i", range(70))
 def test_random_shapes(i):
     dtype, d, H, Hkv, lens, causal, per_head = random_case(i)
     if sum(lens) == 0:
@@ -322,6 +345,5 @@ def test_random_shapes(i):
         g = torch.Generator().manual_seed(3000 + i)
         inp.lq1, inp.lk1, inp.lq2, inp.lk2 = [0.2 * torch.randn(H, d, generator=g)
                                               for _ in range(4)]
-    err = max_abs(gpu_run(inp), oracle_full(inp))
+    err = check_rows(gpu_run(inp), oracle_full(inp), dtype, inp)
     announce(f"random case {i}: max-abs {err:.3e}")
-    assert err <= TOL[dtype]
