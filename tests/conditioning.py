@@ -25,3 +25,38 @@ def cancellation_ratio(inp, t, h):
         o.append(pr @ v[J, g])
     pre = o[0] - lam * o[1]
     return float(pre.pow(2).mean().sqrt() / o[0].pow(2).mean().sqrt())
+
+
+def group_floor(inp):
+    """[nseq, Hkv]: the smallest rms(pre)/rms(O_1) over the rows (token,
+    head) of each (sequence, KV group), in fp64 from the definition (whole
+    score matrices: for the small shapes of the random tests)."""
+    cu = inp.cu_seqlens.tolist()
+    H, Hkv, d = inp.q.shape[1], inp.k.shape[1], inp.q.shape[3]
+    G = H // Hkv
+    lam0 = oracle.lambda_init(inp.depth)
+    q, k, v = inp.q.double(), inp.k.double(), inp.v.double()
+    out = torch.ones(len(cu) - 1, Hkv, dtype=torch.float64)
+    for s in range(len(cu) - 1):
+        a, b = cu[s], cu[s + 1]
+        n = b - a
+        if n == 0:
+            continue
+        mask = torch.ones(n, n, dtype=torch.bool)
+        if inp.causal:
+            mask = torch.tril(mask)
+        for g in range(Hkv):
+            worst = 1.0
+            for h in range(g * G, (g + 1) * G):
+                lv = [x if x.dim() == 1 else x[h] for x in (inp.lq1, inp.lk1, inp.lq2, inp.lk2)]
+                lam = oracle.lam(*lv, lam0)
+                o = []
+                for m in range(2):
+                    x = (q[a:b, h, m] @ k[a:b, g, m].T) / d ** 0.5
+                    pr = torch.softmax(x.masked_fill(~mask, float("-inf")), dim=1)
+                    o.append(pr @ v[a:b, g])
+                pre = o[0] - lam * o[1]
+                ratio = pre.pow(2).mean(1).sqrt() / o[0].pow(2).mean(1).sqrt()
+                worst = min(worst, float(ratio.min()))
+            out[s, g] = worst
+    return out.numpy()

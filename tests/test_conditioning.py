@@ -22,3 +22,24 @@ def test_cancellation_ratio_first_row_closed_form():
         for h in range(4):
             lam = oracle.lam(inp.lq1[h], inp.lk1[h], inp.lq2[h], inp.lk2[h], lam0)
             assert abs(cancellation_ratio(inp, t, h) - abs(1 - lam)) < 1e-6 * max(1, abs(1 - lam))
+
+
+def test_group_floor_equals_rowwise_minimum():
+    """The per-(sequence, KV group) minimum, from whole score matrices, equals
+    the minimum of the row-by-row ratio (CPU only)."""
+    import numpy as np
+    from conditioning import group_floor
+    for causal in (True, False):
+        wl = custom("floor", "bf16", (5, 9, 0, 4), 4, 2, 16, depth=3, causal=causal, seed=2)
+        inp = make_inputs(wl)
+        g = torch.Generator().manual_seed(1)
+        inp.lq1, inp.lk1, inp.lq2, inp.lk2 = [0.5 * torch.randn(4, 16, generator=g)
+                                              for _ in range(4)]
+        floor = group_floor(inp)
+        cu = inp.cu_seqlens.tolist()
+        brute = np.ones_like(floor)
+        for s in range(len(cu) - 1):
+            for t in range(cu[s], cu[s + 1]):
+                for h in range(4):
+                    brute[s, h // 2] = min(brute[s, h // 2], cancellation_ratio(inp, t, h))
+        assert np.abs(floor - brute).max() < 1e-12
