@@ -60,11 +60,11 @@ def oracle_grads(inp, dy, w=True):
 
 def conditioning_factors(inp):
     """Per-token and per-KV-head factors on the dq, dk and dv bars: rows whose
-    two maps cancel before the RMSNorm (rms(pre) < 0.2 rms(O_1)) amplify the
-    bf16 rounding of P that the training forward's saved O_m carry, once in
-    pre and again through the RMSNorm backward, by about rms(O_1)/rms(pre).
-    Every element of a (sequence, KV group) whose smallest ratio r is below
-    0.2 gets the factor 0.2 / r."""
+    two maps cancel before the RMSNorm (cancellation_ratio below 0.2)
+    amplify the bf16 rounding of P that the training forward's saved O_m
+    carry, once in pre and again through the RMSNorm backward, by about the
+    inverse ratio.  Every element of a (sequence, KV group) whose smallest
+    ratio r is below 0.2 gets the factor 0.2 / r."""
     floor = group_floor(inp)                       # [nseq, Hkv]
     cu = inp.cu_seqlens.numpy()
     seq_of = np.searchsorted(cu, np.arange(int(cu[-1])), side="right") - 1
@@ -243,9 +243,8 @@ def test_bwd_full_size_sampled(name):
         assert e <= 2e-2, f"{name}: {key} relative max-abs {e:.3e}"
 
 
-# 74, 83 and 156 each hold a row whose maps cancel (rms(pre) 0.085, 0.027 and
-# 0.039 of rms(O_1), the second or third token of a sequence), held to the
-# conditioning-scaled bar
+# 74, 83 and 156 each hold a row whose maps cancel (the second or third
+# token of a sequence), held to the conditioning-scaled bar
 @pytest.mark.parametrize("i", list(range(24)) + [74, 83, 156])
 def test_bwd_random_shapes(i):
     """Seeded random shapes for the backward: sequence mixes, head

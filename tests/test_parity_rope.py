@@ -15,6 +15,7 @@ import pytest
 import torch
 
 import oracle
+from conditioning import rotated, rows_within_bar
 from workloads import WORKLOADS, custom, make_inputs, rope_tables
 
 pytestmark = pytest.mark.gpu
@@ -137,3 +138,33 @@ def test_short_tables_rejected():
     inp = make_inputs(wl)
     with pytest.raises(da.DiffAttnError):
         gpu_run(inp, rope_tables(99, 64))
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_shapes_rope(i):
+    """Seeded random shapes through the rotary prologue: sequence mixes
+    (positions restart in every sequence), head groupings, the five (dtype,
+    d) instantiations, masking, table bases and lengths, shared or per-head
+    lambda; rows whose maps cancel held to the conditioning-scaled bar."""
+    rng = np.random.default_rng(5000 + i)
+    dtype, d = [("bf16", 64), ("bf16", 32), ("bf16", 16), ("f32", 16), ("f32", 64)][i % 5]
+    Hkv = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 2, 3, 4]))
+    lens = tuple(int(x) for x in rng.integers(0, 600, int(rng.integers(1, 6))))
+    if sum(lens) == 0:
+        lens = lens + (5,)
+    causal = bool(rng.integers(0, 2))
+    wl = custom("random_rope", dtype, lens, Hkv * G, Hkv, d, depth=1 + i % 10, causal=causal,
+                seed=6000 + i)
+    inp = make_inputs(wl)
+    if rng.integers(0, 2):
+        g = torch.Generator().manual_seed(7000 + i)
+        inp.lq1, inp.lk1, inp.lq2, inp.lk2 = [0.2 * torch.randn(Hkv * G, d, generator=g)
+                                              for _ in range(4)]
+    base = float(rng.choice([50.0, 500.0, 10000.0]))
+    rope = rope_tables(max(lens) + int(rng.integers(0, 50)), d, base=base)
+    announce(f"random case {i}: {dtype} d={d} H={Hkv * G} Hkv={Hkv} lens={lens} "
+             f"causal={causal} base={base}")
+    err = rows_within_bar(gpu_run(inp, rope), oracle_full(inp, rope), TOL[dtype],
+                          dtype == "bf16", rotated(inp, rope), announce)
+    announce(f"random case {i}: max-abs {err:.3e}")
