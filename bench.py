@@ -436,7 +436,9 @@ def main() -> int:
     flops = wl.flops()
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
-    traffic = traffic_from_profiles(name)
+    # (the rotary path runs another instantiation plus the K rotation: its own
+    # profile, if one was taken)
+    traffic = traffic_from_profiles(name + ("_rope" if args.rope else ""))
 
     result = {
         "metric": METRIC,
