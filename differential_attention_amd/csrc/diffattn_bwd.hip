@@ -32,12 +32,13 @@
 //           accumulator).
 //  dkdv     key-outer: one workgroup = (sequence, KV head, 128 keys).  Four
 //           waves (32 keys each, both maps) compute S_m = Q_m K_m^T, P_m,
-//           dP = dpre V^T once for both maps, dS_1 = P_1 (dP - D'_1),
-//           dS_2 = P_2 (-lambda dP + lambda D'_2) and dK_m^T += Q_m^T dS_m, and
-//           pass W = P_1 - lambda P_2 (formed in fp32, then rounded) through
-//           LDS to the other four waves, which add dV^T += dpre^T W one
-//           query tile later.  Query tiles (Q, dpre, lse, D') of all G
-//           heads of the group rotate through three LDS stages.
+//           dS_1 = P_1 (dP - D'_1), dS_2 = P_2 (-lambda dP + lambda D'_2)
+//           and dK_m^T += Q_m^T dS_m, and form W = P_1 - lambda P_2 in fp32
+//           (then rounded); the other four waves (same keys) compute
+//           dP = dpre V^T once for both maps one query tile ahead and add
+//           dV^T += dpre^T W one query tile behind, dP and W travelling
+//           through LDS.  Query tiles (Q, dpre, lse, D) of all G heads of
+//           the group rotate through four LDS stages.
 //
 // All contractions run on v_mfma_f32_32x32x16_bf16 with fp32 accumulators;
 // P, W and dS are rounded to bf16 as operands, as is dpre.
