@@ -24,6 +24,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import importlib.util
 import json
 import os
 import re
@@ -53,11 +54,22 @@ BWD_KERNEL_SOURCES = [os.path.join(_CSRC, "diffattn_fwd.hip"),
                       os.path.join(_CSRC, "diffattn_bwd.hip")]
 
 
+def _build_flags() -> bytes:
+    """The compiler flags of the library build (they change the kernels'
+    code as much as their sources do)."""
+    spec = importlib.util.spec_from_file_location(
+        "_diffattn_build", os.path.join(HERE, "differential_attention_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return " ".join(mod.HIPCC_FLAGS).encode()
+
+
 def kernel_digest(sources=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
     for p in sources:
         with open(p, "rb") as f:
             h.update(f.read())
+    h.update(_build_flags())
     return h.hexdigest()[:16]
 
 

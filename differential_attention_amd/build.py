@@ -20,6 +20,11 @@ HIPCC_FLAGS = [
     "-Wall", "-Werror",
     # no packed-fp32 VALU instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the machine scheduler's iterative ILP strategy orders the prefill
+    # loop's MFMAs and VALU work better: +2.3% on the 8 x 4096 prefill,
+    # -1.6% time on the backward, the cache kernels unchanged (and fewer
+    # spills in the fp32 d = 64 prefill)
+    "-mllvm", "-amdgpu-sched-strategy=iterative-ilp",
     "-I", os.path.join(ROOT, "include"),
 ]
 
