@@ -438,7 +438,7 @@ __device__ inline float wave_max(float x)
     return x;
 }
 
-template <int D>
+template <int D, int kChunk>
 __global__ __launch_bounds__(kThreads)
 void diffattn_kv_combine(KvParams p)
 {
@@ -479,12 +479,15 @@ void diffattn_kv_combine(KvParams p)
         lam = expf(d1) - expf(d2) + p.lambda_init;
     }
 
-    // merge the splits of both maps (log-sum-exp in log2 units), up to 16
-    // splits per round: lane j loads split j's (m, l) of both maps in one
-    // 16-byte read while every lane loads its columns of all 16 splits' O
-    // (independent loads, one memory round trip per round); the wave then
-    // reduces the maximum and the weighted sums.
-    constexpr int kChunk = 16;
+    // merge the splits of both maps (log-sum-exp in log2 units), up to
+    // kChunk splits per round: lane j loads split j's (m, l) of both maps in
+    // one 16-byte read while every lane loads its columns of all kChunk
+    // splits' O (independent loads, one memory round trip per round); the
+    // wave then reduces the maximum and the weighted sums.  kChunk is 32
+    // when a row can have more than 16 splits (one round instead of two:
+    // 3.8% on a 4097-key step), else 16 (fewer registers: more waves in
+    // flight when there are many rows).
+    static_assert(kChunk <= 64, "one split's (m, l) per lane");
     float acc[2][CPL];
     float M[2] = {-INFINITY, -INFINITY};
     float L[2] = {0.f, 0.f};
@@ -743,12 +746,21 @@ extern "C" int diffattn_fwd_kv(int dtype, const void *q, const void *k, const vo
     const int64_t blocks2 = (waves2 + kWavesPerBlock - 1) / kWavesPerBlock;
     if (blocks1 > 0x7fffffff || blocks2 > 0x7fffffff)
         return DIFFATTN_EINVAL;
+    // splits of the longest cache
+    const int64_t kmax = cu_seqlens_q ? max_seqlen_k : Tk / nseq;
+    const bool wide = (kmax + pl.ck - 1) / pl.ck > 16;
     if (d == 64) {
         hipLaunchKernelGGL(diffattn_kv_partial<64>, dim3((unsigned)blocks1), dim3(kThreads), 0, st, p);
-        hipLaunchKernelGGL(diffattn_kv_combine<64>, dim3((unsigned)blocks2), dim3(kThreads), 0, st, p);
+        if (wide)
+            hipLaunchKernelGGL((diffattn_kv_combine<64, 32>), dim3((unsigned)blocks2), dim3(kThreads), 0, st, p);
+        else
+            hipLaunchKernelGGL((diffattn_kv_combine<64, 16>), dim3((unsigned)blocks2), dim3(kThreads), 0, st, p);
     } else {
         hipLaunchKernelGGL(diffattn_kv_partial<32>, dim3((unsigned)blocks1), dim3(kThreads), 0, st, p);
-        hipLaunchKernelGGL(diffattn_kv_combine<32>, dim3((unsigned)blocks2), dim3(kThreads), 0, st, p);
+        if (wide)
+            hipLaunchKernelGGL((diffattn_kv_combine<32, 32>), dim3((unsigned)blocks2), dim3(kThreads), 0, st, p);
+        else
+            hipLaunchKernelGGL((diffattn_kv_combine<32, 16>), dim3((unsigned)blocks2), dim3(kThreads), 0, st, p);
     }
     return hipGetLastError() == hipSuccess ? DIFFATTN_OK : DIFFATTN_EHIP;
 }
