@@ -61,7 +61,8 @@ def _build_flags() -> bytes:
         "_diffattn_build", os.path.join(HERE, "differential_attention_amd", "build.py"))
     mod = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(mod)
-    return " ".join(mod.HIPCC_FLAGS).encode()
+    # (without the include path, which depends on where the tree is)
+    return " ".join(f for f in mod.HIPCC_FLAGS if not os.path.isabs(f)).encode()
 
 
 def kernel_digest(sources=KERNEL_SOURCES) -> str:

@@ -82,3 +82,14 @@ def test_copy_calibration_runs():
     assert res.returncode == 0, res.stderr[-2000:]
     out = json.loads(res.stdout.strip().splitlines()[-1])
     assert out["copy_bytes"] == 1 << 20 and out["ms_per_copy"] > 0
+
+
+def test_kernel_digest_does_not_depend_on_the_tree_location():
+    """The profiles' kernel digest hashes the sources and the compiler
+    flags, but no path: the same build gets the same digest wherever the
+    tree is checked out (CPU only)."""
+    sys.path.insert(0, ROOT)
+    import bench
+    flags = bench._build_flags().decode()
+    assert ROOT not in flags
+    assert not any(os.path.isabs(f) for f in flags.split())
