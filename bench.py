@@ -74,6 +74,22 @@ def kernel_digest(sources=KERNEL_SOURCES) -> str:
     return h.hexdigest()[:16]
 
 
+def per_launch_ms(step, stream, n: int):
+    """Median, minimum and maximum of n further launches, each between two
+    events recorded back to back on the launch stream (after the timed
+    region, which they do not touch)."""
+    import torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    with torch.cuda.stream(stream):
+        evs[0].record(stream)
+        for i in range(n):
+            step()
+            evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    t = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(n))
+    return {"median": round(t[n // 2], 4), "min": round(t[0], 4), "max": round(t[-1], 4), "n": n}
+
+
 def traffic_from_profiles(workload: str, sources=KERNEL_SOURCES):
     """HBM bytes per launch from the committed counter summary, if it was
     taken on the current kernel source; else None."""
@@ -242,6 +258,7 @@ def bench_kv(args, name) -> int:
                    "workspace_bytes": need,
                    "launch": f"hip graph of {GRAPH_STEPS} steps" if graph is not None else "eager",
                    "wall_s_timed": round(wall, 4),
+                   "ms_per_launch": per_launch_ms(step, stream, args.steps) if graph is None else None,
                    "kernel_digest": kernel_digest(KV_KERNEL_SOURCES)},
         # both kernels of the step are in the timed duration, so this is a
         # lower bound on the partial kernel's own rate
@@ -332,6 +349,7 @@ def bench_bwd(args, name) -> int:
                    "flops_fwd": fwd_flops, "flops_bwd": bwd_flops,
                    "workspace_bytes": need,
                    "launch": "eager", "wall_s_timed": round(wall, 4),
+                   "ms_per_launch": per_launch_ms(step, stream, args.steps),
                    "kernel_digest": kernel_digest(BWD_KERNEL_SOURCES)},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
                      "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
@@ -473,6 +491,7 @@ def main() -> int:
                    "flops_per_step": flops,
                    "pct_of_bf16_peak": round(100 * tflops / peak, 2),
                    "wall_s_timed": round(wall, 4),
+                   "ms_per_launch": per_launch_ms(step, stream, args.steps),
                    "kernel_digest": kernel_digest()},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
                      "peak": round(peak, 1), "unit": "TFLOP/s",

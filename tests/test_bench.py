@@ -68,6 +68,12 @@ def test_bench_modes_report_the_contract(mode):
         assert key in roof, key
     assert roof["bound"] in ("hbm", "mfma", "alu")
     assert 0 < roof["frac"] < 1
+    launch = out["config"].get("ms_per_launch")
+    if "--graph" in MODES[mode]:
+        assert launch is None
+    else:
+        assert launch["n"] == int(steps)
+        assert 0 < launch["min"] <= launch["median"] <= launch["max"]
     if mode == "tiny_f32_with_cpu_baseline":
         cb = out["cpu_baseline"]
         assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1
