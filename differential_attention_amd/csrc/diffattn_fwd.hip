@@ -284,19 +284,22 @@ template <> struct Rope<float> {
     }
 };
 
-// Rotates every K row once, into a copy: thread = one 16-byte chunk of a
-// (token, KV head) row (whole pairs); the token's position is its offset in
-// its sequence, found by binary search over cu_seqlens.  The prefill kernel
-// then stages the rotated copy.
+// Rotates every K row once, into a copy.  Thread = one 16-byte chunk
+// position (whole pairs) of one token, taken through all 2 Hkv half-heads
+// of that token: the coefficients depend only on the position and the pair
+// index, so each thread reads them once and keeps up to eight chunk loads
+// in flight.  The token's position is its offset in its sequence, found by
+// binary search over cu_seqlens.  The prefill kernel then stages the
+// rotated copy.
 template <typename E, int D>
 __global__ __launch_bounds__(256) void rope_rotate_k(const char *k, char *kr, const int32_t *cu,
                                                      int32_t nseq, int32_t uniform, int32_t T,
                                                      int32_t Hkv, const float *rc, const float *rs)
 {
-    constexpr int CPR = 2 * D * (int)sizeof(E) / 16;    // chunks per (token, KV head) row
+    constexpr int HB = D * (int)sizeof(E);   // bytes per d-wide half-head
+    constexpr int CPH = HB / 16;             // chunks per half-head
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t per_tok = (int64_t)Hkv * CPR;
-    const int t = (int)(idx / per_tok);
+    const int t = (int)(idx / CPH);
     if (t >= T)
         return;
     int s0;
@@ -313,12 +316,23 @@ __global__ __launch_bounds__(256) void rope_rotate_k(const char *k, char *kr, co
     } else {
         s0 = (t / uniform) * uniform;
     }
-    const int c = (int)(idx % CPR);
-    // pair index of the chunk's first element within its d-wide half-head
-    const int j = ((c * 16 / (int)sizeof(E)) % D) / 2;
-    const int64_t off = idx * 16;
-    const u32x4 x = *(const u32x4 *)(k + off);
-    *(u32x4 *)(kr + off) = Rope<E>::rotate(x, Rope<E>::coef(rc, rs, t - s0, j, D));
+    const int c = (int)(idx % CPH);
+    // pair index of the chunk's first element within its half-head
+    const int j = c * (16 / (int)sizeof(E)) / 2;
+    const auto coef = Rope<E>::coef(rc, rs, t - s0, j, D);
+    const int nh = 2 * Hkv;
+    const int64_t base = (int64_t)t * nh * HB + c * 16;
+    for (int h0 = 0; h0 < nh; h0 += 8) {
+        u32x4 x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (h0 + i < nh)
+                x[i] = *(const u32x4 *)(k + base + (int64_t)(h0 + i) * HB);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (h0 + i < nh)
+                *(u32x4 *)(kr + base + (int64_t)(h0 + i) * HB) = Rope<E>::rotate(x[i], coef);
+    }
 }
 
 struct Params {
@@ -915,8 +929,8 @@ int launch(const Params &p, int nblocks, hipStream_t stream)
 {
     if (p.rcos) {
         // K rotated once into the workspace, which the kernel then reads as K
-        const int64_t chunks = (int64_t)p.T * p.Hkv * (2 * D * (int)sizeof(E) / 16);
-        hipLaunchKernelGGL((rope_rotate_k<E, D>), dim3((unsigned)((chunks + 255) / 256)),
+        const int64_t threads = (int64_t)p.T * (D * (int)sizeof(E) / 16);
+        hipLaunchKernelGGL((rope_rotate_k<E, D>), dim3((unsigned)((threads + 255) / 256)),
                            dim3(256), 0, stream, (const char *)p.k_orig, (char *)p.k, p.cu,
                            p.nseq, p.seqlen_uniform, p.T, p.Hkv, p.rcos, p.rsin);
     }
