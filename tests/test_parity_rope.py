@@ -72,6 +72,23 @@ def test_ragged_varlen_rope(dtype, d, H, Hkv, causal):
     assert err <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype,d,H,Hkv", [("bf16", 64, 10, 5), ("bf16", 64, 16, 8),
+                                           ("f32", 16, 8, 8), ("bf16", 32, 9, 3),
+                                           ("f32", 64, 10, 5), ("bf16", 16, 24, 8)])
+def test_many_kv_heads_rope(dtype, d, H, Hkv):
+    """The K rotation takes each chunk position of a token through its
+    2 Hkv half-heads eight at a time: Hkv = 3 leaves a partial group, Hkv = 5
+    and 8 need a second one."""
+    wl = custom("kvheads_rope", dtype, (300, 1, 129, 64), H, Hkv, d, depth=3,
+                causal=True, seed=H * 10 + Hkv + d)
+    inp = make_inputs(wl)
+    inp.w = torch.linspace(0.5, 1.5, 2 * d)
+    rope = rope_tables(320, d, base=50.0)
+    err = max_abs(gpu_run(inp, rope), oracle_full(inp, rope))
+    announce(f"kv heads {dtype} d={d} H={H} Hkv={Hkv}: max-abs {err:.3e}")
+    assert err <= TOL[dtype]
+
+
 def test_identity_tables_bitwise():
     """cos = 1, sin = 0: the rotated path must reproduce the plain one bit
     for bit (x * 1 - y * 0 is exact)."""
