@@ -144,7 +144,7 @@ RAGGED = (1, 0, 31, 32, 33, 63, 64, 65, 127, 200, 0, 7)
 
 @pytest.mark.parametrize("dtype,d", [("f32", 16), ("bf16", 64), ("f32", 64),
                                      ("bf16", 16), ("bf16", 32)])
-@pytest.mark.parametrize("H,Hkv", [(2, 2), (4, 2), (8, 2), (16, 2), (3, 1)])
+@pytest.mark.parametrize("H,Hkv", [(2, 2), (4, 2), (8, 2), (16, 2), (3, 1), (10, 5), (8, 8)])
 @pytest.mark.parametrize("causal", [True, False])
 def test_ragged_varlen(dtype, d, H, Hkv, causal):
     wl = custom("ragged", dtype, RAGGED, H, Hkv, d, depth=5, causal=causal,

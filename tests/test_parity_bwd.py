@@ -112,7 +112,7 @@ RAGGED = (1, 0, 31, 32, 33, 63, 64, 65, 127, 200, 7)
 
 
 @pytest.mark.parametrize("d", [64, 32])
-@pytest.mark.parametrize("H,Hkv", [(4, 2), (8, 2), (3, 1), (16, 4)])
+@pytest.mark.parametrize("H,Hkv", [(4, 2), (8, 2), (3, 1), (16, 4), (10, 5), (8, 8)])
 @pytest.mark.parametrize("causal", [True, False])
 def test_bwd_ragged(d, H, Hkv, causal):
     wl = custom("bwd", "bf16", RAGGED, H, Hkv, d, depth=6, causal=causal,

@@ -141,7 +141,7 @@ RAGGED = [
 ]
 
 
-@pytest.mark.parametrize("H,Hkv", [(8, 2), (4, 4), (16, 1), (12, 4)])
+@pytest.mark.parametrize("H,Hkv", [(8, 2), (4, 4), (16, 1), (12, 4), (10, 5)])
 @pytest.mark.parametrize("d", [64, 32])
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("case", range(len(RAGGED)))
