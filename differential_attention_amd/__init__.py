@@ -18,6 +18,7 @@ from typing import Optional
 import torch
 
 __all__ = ["fwd", "fwd_ptr", "fwd_workspace_size", "fwd_kv", "fwd_kv_ptr", "kv_workspace_size",
+           "fwd_kv_noalloc", "fwd_kv_noalloc_ptr", "KV_SCRATCH_BYTES",
            "fwd_train", "bwd", "bwd_workspace_size", "supported_bwd",
            "lambda_init", "supported", "supported_kv", "check_cu_seqlens",
            "check_cu_seqlens_kv", "library", "LIBRARY", "DiffAttnError",
@@ -26,7 +27,10 @@ __all__ = ["fwd", "fwd_ptr", "fwd_workspace_size", "fwd_kv", "fwd_kv_ptr", "kv_w
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "libdiffattn.so")
 
-OK, EINVAL, EUNSUPPORTED, EHIP = 0, -1, -2, -3
+OK, EINVAL, EUNSUPPORTED, EHIP, ETOOLARGE = 0, -1, -2, -3, -4
+# size of the static device array behind diffattn_fwd_kv_noalloc
+# (DIFFATTN_KV_SCRATCH_BYTES in include/diffattn.h)
+KV_SCRATCH_BYTES = 32 << 20
 BF16, F32 = 0, 1
 _DTYPES = {torch.bfloat16: BF16, torch.float32: F32}
 
@@ -64,6 +68,11 @@ def library() -> ctypes.CDLL:
         f32p, ctypes.c_float, ctypes.c_int, i32p, i32p, i32, i32, i32, i32,
         i32, i32, i32, i32, vp, ctypes.c_size_t, vp, vp]
     lib.diffattn_fwd_kv.restype = ctypes.c_int
+    lib.diffattn_fwd_kv_noalloc.argtypes = [
+        ctypes.c_int, vp, vp, vp, f32p, f32p, f32p, f32p, i32, ctypes.c_float,
+        f32p, ctypes.c_float, ctypes.c_int, i32p, i32p, i32, i32, i32, i32,
+        i32, i32, i32, i32, vp, vp]
+    lib.diffattn_fwd_kv_noalloc.restype = ctypes.c_int
     lib.diffattn_fwd_kv_workspace_size.argtypes = [i32] * 6
     lib.diffattn_fwd_kv_workspace_size.restype = ctypes.c_size_t
     lib.diffattn_supported_kv.argtypes = [ctypes.c_int, ctypes.c_int]
@@ -166,6 +175,24 @@ def fwd_kv_ptr(dtype: int, q: int, k: int, v: int, lq1: int, lk1: int,
         cu_seqlens_k or None, int(nseq), int(max_seqlen_q), int(max_seqlen_k),
         int(Tq), int(Tk), int(H), int(Hkv), int(d), workspace or None,
         int(workspace_bytes), out or None, stream or None)
+
+
+def fwd_kv_noalloc_ptr(dtype: int, q: int, k: int, v: int, lq1: int,
+                       lk1: int, lq2: int, lk2: int, lambda_stride: int,
+                       lambda_init_value: float, subln_weight: int,
+                       eps: float, causal: int, cu_seqlens_q: int,
+                       cu_seqlens_k: int, nseq: int, max_seqlen_q: int,
+                       max_seqlen_k: int, Tq: int, Tk: int, H: int, Hkv: int,
+                       d: int, out: int, stream: int) -> int:
+    """The raw no-allocation cache entry point (static device scratch) on
+    integer device addresses; returns the status."""
+    return library().diffattn_fwd_kv_noalloc(
+        int(dtype), q or None, k or None, v or None, lq1 or None, lk1 or None,
+        lq2 or None, lk2 or None, int(lambda_stride), float(lambda_init_value),
+        subln_weight or None, float(eps), int(causal), cu_seqlens_q or None,
+        cu_seqlens_k or None, int(nseq), int(max_seqlen_q), int(max_seqlen_k),
+        int(Tq), int(Tk), int(H), int(Hkv), int(d), out or None,
+        stream or None)
 
 
 def fwd_ptr(dtype: int, q: int, k: int, v: int, lq1: int, lk1: int, lq2: int,
@@ -333,6 +360,38 @@ def fwd_kv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     at least ``kv_workspace_size(...)`` bytes; one is allocated through
     torch when it is None.  Returns ``out`` [Tq, H, 2d].
     """
+    return _kv_call(q, k, v, (lambda_q1, lambda_k1, lambda_q2, lambda_k2),
+                    lambda_init, subln_weight, eps, causal, cu_seqlens_q,
+                    cu_seqlens_k, max_seqlen_q, max_seqlen_k, nseq, out,
+                    stream, workspace, noalloc=False)
+
+
+def fwd_kv_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                   lambda_q1: torch.Tensor, lambda_k1: torch.Tensor,
+                   lambda_q2: torch.Tensor, lambda_k2: torch.Tensor,
+                   lambda_init: float,
+                   subln_weight: Optional[torch.Tensor] = None,
+                   eps: float = 1e-5, causal: bool = True,
+                   cu_seqlens_q: Optional[torch.Tensor] = None,
+                   cu_seqlens_k: Optional[torch.Tensor] = None,
+                   max_seqlen_q: Optional[int] = None,
+                   max_seqlen_k: Optional[int] = None,
+                   nseq: Optional[int] = None,
+                   out: Optional[torch.Tensor] = None,
+                   stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """``fwd_kv`` through ``diffattn_fwd_kv_noalloc``: the library's static
+    device scratch (``KV_SCRATCH_BYTES`` per GPU) replaces the workspace, so
+    the call allocates nothing when ``out`` and both bounds are given.
+    Calls overlapping in time on one GPU race on that scratch."""
+    return _kv_call(q, k, v, (lambda_q1, lambda_k1, lambda_q2, lambda_k2),
+                    lambda_init, subln_weight, eps, causal, cu_seqlens_q,
+                    cu_seqlens_k, max_seqlen_q, max_seqlen_k, nseq, out,
+                    stream, None, noalloc=True)
+
+
+def _kv_call(q, k, v, lvs, lambda_init, subln_weight, eps, causal,
+             cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, nseq,
+             out, stream, workspace, noalloc):
     if q.dim() != 4 or q.shape[2] != 2:
         raise ValueError("q must be [Tq, H, 2, d]")
     Tq, H, _, d = q.shape
@@ -348,8 +407,7 @@ def fwd_kv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         raise ValueError("q must be a GPU tensor")
     qp, kp, vp_ = (_dev(q, "q", dev), _dev(k, "k", dev, q.dtype),
                    _dev(v, "v", dev, q.dtype))
-    lptrs, lambda_stride = _lambda_args(
-        (lambda_q1, lambda_k1, lambda_q2, lambda_k2), H, d, dev)
+    lptrs, lambda_stride = _lambda_args(lvs, H, d, dev)
     w_ptr = 0
     if subln_weight is not None:
         if subln_weight.numel() != 2 * d:
@@ -374,12 +432,14 @@ def fwd_kv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         nseq = 1 if nseq is None else int(nseq)
         max_seqlen_q = Tq // nseq if nseq > 0 else 0
         max_seqlen_k = Tk // nseq if nseq > 0 else 0
-    need = kv_workspace_size(nseq, max(max_seqlen_q, 1), max(max_seqlen_k, 1),
-                             H, Hkv, d)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
-    ws_ptr = _dev(workspace, "workspace", dev)
-    ws_bytes = workspace.numel() * workspace.element_size()
+    if not noalloc:
+        need = kv_workspace_size(nseq, max(max_seqlen_q, 1),
+                                 max(max_seqlen_k, 1), H, Hkv, d)
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8,
+                                    device=dev)
+        ws_ptr = _dev(workspace, "workspace", dev)
+        ws_bytes = workspace.numel() * workspace.element_size()
     if out is None:
         out = torch.empty((Tq, H, 2 * d), dtype=q.dtype, device=dev)
     elif tuple(out.shape) != (Tq, H, 2 * d):
@@ -387,13 +447,18 @@ def fwd_kv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     out_ptr = _dev(out, "out", dev, q.dtype)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
+    common = (_DTYPES[q.dtype], qp, kp, vp_, *lptrs, lambda_stride,
+              lambda_init, w_ptr, eps, int(bool(causal)), cq_ptr, ck_ptr,
+              nseq, max_seqlen_q, max_seqlen_k, Tq, Tk, H, Hkv, d)
     with torch.cuda.device(dev):
-        st = fwd_kv_ptr(_DTYPES[q.dtype], qp, kp, vp_, *lptrs, lambda_stride,
-                        lambda_init, w_ptr, eps, int(bool(causal)), cq_ptr,
-                        ck_ptr, nseq, max_seqlen_q, max_seqlen_k, Tq, Tk, H,
-                        Hkv, d, ws_ptr, ws_bytes, out_ptr, stream.cuda_stream)
+        if noalloc:
+            st = fwd_kv_noalloc_ptr(*common, out_ptr, stream.cuda_stream)
+        else:
+            st = fwd_kv_ptr(*common, ws_ptr, ws_bytes, out_ptr,
+                            stream.cuda_stream)
     if st != OK:
-        raise DiffAttnError(st, "diffattn_fwd_kv")
+        raise DiffAttnError(st, "diffattn_fwd_kv_noalloc" if noalloc
+                            else "diffattn_fwd_kv")
     return out
 
 

@@ -971,6 +971,8 @@ const char *diffattn_strerror(int status)
     case DIFFATTN_EINVAL: return "invalid argument";
     case DIFFATTN_EUNSUPPORTED: return "unsupported (dtype, d) combination";
     case DIFFATTN_EHIP: return "HIP runtime error (no device or launch failure)";
+    case DIFFATTN_ETOOLARGE:
+        return "sizes need more device scratch than the library's static array holds";
     default: return "unknown status";
     }
 }

@@ -54,6 +54,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 #include <math.h>
 #include <stdint.h>
 
@@ -655,16 +657,19 @@ extern "C" size_t diffattn_fwd_kv_workspace_size(int32_t nseq, int32_t max_seqle
     return pl.ws_o_bytes + pl.ws_ml_bytes;
 }
 
-extern "C" int diffattn_fwd_kv(int dtype, const void *q, const void *k, const void *v,
-                               const float *lambda_q1, const float *lambda_k1,
-                               const float *lambda_q2, const float *lambda_k2,
-                               int32_t lambda_stride, float lambda_init,
-                               const float *subln_weight, float eps, int causal,
-                               const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
-                               int32_t nseq, int32_t max_seqlen_q, int32_t max_seqlen_k,
-                               int32_t Tq, int32_t Tk, int32_t H, int32_t Hkv, int32_t d,
-                               void *workspace, size_t workspace_bytes, void *out,
-                               void *stream)
+namespace {
+
+// Validates the arguments, makes the split plan and launches both kernels
+// with the workspace that `get_ws` returns for the plan's size (it returns
+// a status and sets the pointer, or refuses the size).
+template <typename GetWs>
+int kv_impl(int dtype, const void *q, const void *k, const void *v,
+            const float *lambda_q1, const float *lambda_k1, const float *lambda_q2,
+            const float *lambda_k2, int32_t lambda_stride, float lambda_init,
+            const float *subln_weight, float eps, int causal, const int32_t *cu_seqlens_q,
+            const int32_t *cu_seqlens_k, int32_t nseq, int32_t max_seqlen_q,
+            int32_t max_seqlen_k, int32_t Tq, int32_t Tk, int32_t H, int32_t Hkv, int32_t d,
+            GetWs get_ws, void *out, void *stream)
 {
     if (dtype != DIFFATTN_BF16 && dtype != DIFFATTN_F32)
         return DIFFATTN_EINVAL;
@@ -696,18 +701,19 @@ extern "C" int diffattn_fwd_kv(int dtype, const void *q, const void *k, const vo
         return DIFFATTN_OK;   // no query rows: nothing to write
     if (max_seqlen_k == 0)
         return DIFFATTN_EINVAL;   // queries with no key at all
-    if (!q || !k || !v || !out || !lambda_q1 || !lambda_k1 || !lambda_q2 || !lambda_k2 ||
-        !workspace)
+    if (!q || !k || !v || !out || !lambda_q1 || !lambda_k1 || !lambda_q2 || !lambda_k2)
         return DIFFATTN_EINVAL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
-        !aligned16(workspace) || (subln_weight && !aligned16(subln_weight)))
+        (subln_weight && !aligned16(subln_weight)))
         return DIFFATTN_EINVAL;
     const int G = H / Hkv;
     KvPlan pl;
     if (!make_plan(nseq, max_seqlen_q, max_seqlen_k, G, Hkv, d, Tk, pl))
         return DIFFATTN_EINVAL;
-    if (workspace_bytes < pl.ws_o_bytes + pl.ws_ml_bytes)
-        return DIFFATTN_EINVAL;
+    void *workspace = nullptr;
+    const int wst = get_ws(pl.ws_o_bytes + pl.ws_ml_bytes, workspace);
+    if (wst != DIFFATTN_OK)
+        return wst;
 
     KvParams p;
     p.q = q;
@@ -763,4 +769,85 @@ extern "C" int diffattn_fwd_kv(int dtype, const void *q, const void *k, const vo
             hipLaunchKernelGGL((diffattn_kv_combine<32, 16>), dim3((unsigned)blocks2), dim3(kThreads), 0, st, p);
     }
     return hipGetLastError() == hipSuccess ? DIFFATTN_OK : DIFFATTN_EHIP;
+}
+
+// ---------------------------------------------------------------------------
+// Static scratch of diffattn_fwd_kv_noalloc: the split partials live in this
+// array instead of a caller's workspace.  Every GPU the library runs on holds
+// its own copy (at its own address) until the process ends.  In host code
+// `scratch` names a host-side stand-in, never the device memory: the device
+// address is taken once per device with hipGetSymbolAddress (that device
+// current) and only that address is handed to kernels.
+static __device__ __align__(256) char scratch[DIFFATTN_KV_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 256;
+std::atomic<void *> g_scratch_dev[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch, looked up on the first
+// call on that device.
+int scratch_address(void *&ptr)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return DIFFATTN_EHIP;
+    ptr = g_scratch_dev[dev].load(std::memory_order_acquire);
+    if (ptr)
+        return DIFFATTN_OK;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ptr = g_scratch_dev[dev].load(std::memory_order_relaxed);
+    if (!ptr) {
+        void *addr = nullptr;
+        if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr)
+            return DIFFATTN_EHIP;
+        g_scratch_dev[dev].store(addr, std::memory_order_release);
+        ptr = addr;
+    }
+    return DIFFATTN_OK;
+}
+
+} // namespace
+
+extern "C" int diffattn_fwd_kv(int dtype, const void *q, const void *k, const void *v,
+                               const float *lambda_q1, const float *lambda_k1,
+                               const float *lambda_q2, const float *lambda_k2,
+                               int32_t lambda_stride, float lambda_init,
+                               const float *subln_weight, float eps, int causal,
+                               const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                               int32_t nseq, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                               int32_t Tq, int32_t Tk, int32_t H, int32_t Hkv, int32_t d,
+                               void *workspace, size_t workspace_bytes, void *out,
+                               void *stream)
+{
+    auto caller_ws = [&](size_t need, void *&ws) {
+        if (!workspace || !aligned16(workspace) || workspace_bytes < need)
+            return (int)DIFFATTN_EINVAL;
+        ws = workspace;
+        return (int)DIFFATTN_OK;
+    };
+    return kv_impl(dtype, q, k, v, lambda_q1, lambda_k1, lambda_q2, lambda_k2, lambda_stride,
+                   lambda_init, subln_weight, eps, causal, cu_seqlens_q, cu_seqlens_k, nseq,
+                   max_seqlen_q, max_seqlen_k, Tq, Tk, H, Hkv, d, caller_ws, out, stream);
+}
+
+extern "C" int diffattn_fwd_kv_noalloc(int dtype, const void *q, const void *k, const void *v,
+                                       const float *lambda_q1, const float *lambda_k1,
+                                       const float *lambda_q2, const float *lambda_k2,
+                                       int32_t lambda_stride, float lambda_init,
+                                       const float *subln_weight, float eps, int causal,
+                                       const int32_t *cu_seqlens_q,
+                                       const int32_t *cu_seqlens_k, int32_t nseq,
+                                       int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Tq,
+                                       int32_t Tk, int32_t H, int32_t Hkv, int32_t d,
+                                       void *out, void *stream)
+{
+    // the size check comes first, so an oversized call touches no device
+    auto static_ws = [&](size_t need, void *&ws) {
+        if (need > (size_t)DIFFATTN_KV_SCRATCH_BYTES)
+            return (int)DIFFATTN_ETOOLARGE;
+        return scratch_address(ws);
+    };
+    return kv_impl(dtype, q, k, v, lambda_q1, lambda_k1, lambda_q2, lambda_k2, lambda_stride,
+                   lambda_init, subln_weight, eps, causal, cu_seqlens_q, cu_seqlens_k, nseq,
+                   max_seqlen_q, max_seqlen_k, Tq, Tk, H, Hkv, d, static_ws, out, stream);
 }

@@ -26,7 +26,9 @@
  *
  * Ownership: the caller owns every buffer.  The library allocates no device
  * or host memory, keeps no state between calls, never synchronises, and is
- * safe to call from several threads.  out must not overlap any input.
+ * safe to call from several threads.  out must not overlap any input.  The
+ * one exception is diffattn_fwd_kv_noalloc, whose static device array (one
+ * per GPU, part of the code object) is shared by all of its calls.
  *
  * Errors: every entry point returns a status (DIFFATTN_OK or a negative
  * code) and never aborts or throws.  Argument errors are detected on the host
@@ -44,13 +46,14 @@
 extern "C" {
 #endif
 
-#define DIFFATTN_ABI_VERSION 6
+#define DIFFATTN_ABI_VERSION 7
 
 enum diffattn_status {
     DIFFATTN_OK = 0,
     DIFFATTN_EINVAL = -1,       /* malformed arguments; nothing launched    */
     DIFFATTN_EUNSUPPORTED = -2, /* (dtype, d) pair not compiled in          */
-    DIFFATTN_EHIP = -3          /* HIP runtime error: no device, bad launch */
+    DIFFATTN_EHIP = -3,         /* HIP runtime error: no device, bad launch */
+    DIFFATTN_ETOOLARGE = -4     /* needs more than the static scratch holds */
 };
 
 enum diffattn_dtype {
@@ -186,6 +189,41 @@ int diffattn_fwd_kv(int dtype, const void *q, const void *k, const void *v,
                     int32_t Tq, int32_t Tk, int32_t H, int32_t Hkv, int32_t d,
                     void *workspace, size_t workspace_bytes, void *out,
                     void *stream);
+
+/*
+ * diffattn_fwd_kv without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  The split partials go to a
+ * static device array of DIFFATTN_KV_SCRATCH_BYTES that the library owns:
+ * one per GPU, created with the code object and held until the process
+ * ends.  The call allocates nothing (no hipMalloc or allocating library
+ * routine); the first call on a device looks up that device's array.
+ *
+ * Arguments, results and errors as for diffattn_fwd_kv, minus workspace and
+ * workspace_bytes; the kernels and the split plan are the same, so the
+ * output is bitwise that of diffattn_fwd_kv.  Sizes whose
+ * diffattn_fwd_kv_workspace_size(...) exceeds DIFFATTN_KV_SCRATCH_BYTES are
+ * rejected with DIFFATTN_ETOOLARGE before any device work.
+ *
+ * All calls on one GPU share its array, and it keeps the last call's
+ * partials (nothing needs to start at zero: each call writes every partial
+ * it reads).  Calls that overlap in time on one GPU (several streams, or
+ * several host threads without ordering) race on the array and give wrong
+ * results: order them on one stream, or use diffattn_fwd_kv with separate
+ * workspaces.
+ */
+#define DIFFATTN_KV_SCRATCH_BYTES (32u << 20)
+
+int diffattn_fwd_kv_noalloc(int dtype, const void *q, const void *k,
+                            const void *v, const float *lambda_q1,
+                            const float *lambda_k1, const float *lambda_q2,
+                            const float *lambda_k2, int32_t lambda_stride,
+                            float lambda_init, const float *subln_weight,
+                            float eps, int causal, const int32_t *cu_seqlens_q,
+                            const int32_t *cu_seqlens_k, int32_t nseq,
+                            int32_t max_seqlen_q, int32_t max_seqlen_k,
+                            int32_t Tq, int32_t Tk, int32_t H, int32_t Hkv,
+                            int32_t d, void *out, void *stream);
 
 /* Bytes of workspace diffattn_fwd_kv needs for these sizes (the same split
  * plan the call makes); 0 for sizes it rejects.  Host function. */

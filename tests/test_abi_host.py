@@ -38,7 +38,7 @@ def test_abi_version_matches_header(lib):
 
 
 def test_strerror(lib):
-    for st in (0, -1, -2, -3, 12345):
+    for st in (0, -1, -2, -3, -4, 12345):
         assert isinstance(da.strerror(st), str) and da.strerror(st)
 
 
@@ -184,6 +184,48 @@ def call_kv(**over):
 ])
 def test_kv_validation_before_any_device_work(over, status):
     assert call_kv(**over) == status
+
+
+def call_kv_noalloc(**over):
+    a = dict(dtype=da.BF16, q=FAKE, k=FAKE, v=FAKE, lq1=FAKE, lk1=FAKE,
+             lq2=FAKE, lk2=FAKE, lambda_stride=0, lambda_init_value=0.7,
+             subln_weight=0, eps=1e-5, causal=1, cu_seqlens_q=0,
+             cu_seqlens_k=0, nseq=8, max_seqlen_q=0, max_seqlen_k=0, Tq=8,
+             Tk=8 * 4097, H=16, Hkv=4, d=64, out=FAKE, stream=0)
+    a.update(over)
+    return da.fwd_kv_noalloc_ptr(**a)
+
+
+def test_kv_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define DIFFATTN_KV_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == da.KV_SCRATCH_BYTES
+    # the three decode workloads fit the static scratch
+    for nseq, mq, mk in ((8, 1, 4097), (64, 1, 8192), (32, 4, 31196)):
+        assert 0 < da.kv_workspace_size(nseq, mq, mk, 16, 4, 64) <= da.KV_SCRATCH_BYTES
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(dtype=7), da.EINVAL),
+    (dict(H=6, Hkv=4), da.EINVAL),
+    (dict(causal=2), da.EINVAL),
+    (dict(dtype=da.F32), da.EUNSUPPORTED),
+    (dict(Tq=12), da.EINVAL),                      # Tq % nseq
+    (dict(Tk=0), da.EINVAL),                       # queries without keys
+    (dict(q=0), da.EINVAL),
+    (dict(out=FAKE + 4), da.EINVAL),               # not 16-byte aligned
+    (dict(Tq=0, q=0, out=0), da.OK),               # no query rows
+    # partials beyond the static scratch: 64 sequences x 64 queries x 4 heads
+    (dict(nseq=64, Tq=64 * 64, Tk=64 * 4096), da.ETOOLARGE),
+])
+def test_kv_noalloc_validation_before_any_device_work(over, status):
+    assert call_kv_noalloc(**over) == status
+
+
+def test_kv_noalloc_too_large_matches_workspace_size():
+    need = da.kv_workspace_size(64, 64, 4096, 16, 4, 64)
+    assert need > da.KV_SCRATCH_BYTES
+    assert da.kv_workspace_size(64, 1, 4096, 16, 4, 64) <= da.KV_SCRATCH_BYTES
 
 
 # --------------------------------------------------------------------------
