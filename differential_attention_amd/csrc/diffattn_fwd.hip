@@ -953,6 +953,7 @@ launch_fn find_launcher(int dtype, int d)
         if (d == 16) return launch<bf16, 16>;
     } else if (dtype == DIFFATTN_F32) {
         if (d == 64) return launch<float, 64>;
+        if (d == 32) return launch<float, 32>;
         if (d == 16) return launch<float, 16>;
     }
     return nullptr;

@@ -58,6 +58,7 @@ def test_supported():
     import torch
     assert da.supported(torch.bfloat16, 64)
     assert da.supported(torch.float32, 16)
+    assert da.supported(torch.float32, 32)
     assert not da.supported(torch.bfloat16, 48)
 
 
@@ -92,7 +93,7 @@ def call(**over):
     (dict(lambda_stride=-1), da.EINVAL),
     (dict(lambda_stride=63), da.EINVAL),        # stride below d
     (dict(d=48), da.EUNSUPPORTED),
-    (dict(dtype=da.F32, d=32), da.EUNSUPPORTED),
+    (dict(dtype=da.F32, d=48), da.EUNSUPPORTED),
     (dict(q=0), da.EINVAL),
     (dict(out=0), da.EINVAL),
     (dict(lk2=0), da.EINVAL),

@@ -25,25 +25,67 @@ def test_cancellation_ratio_first_row_closed_form():
             assert abs(cancellation_ratio(inp, t, h) - want) < 1e-9
 
 
-def test_group_floor_equals_rowwise_minimum():
-    """The per-(sequence, KV group) minimum, from whole score matrices, equals
-    the minimum of the row-by-row ratio (CPU only)."""
+def test_bar_factor_is_capped():
+    """Rows that cancel get 0.2 / ratio times the bar, never more than 4x
+    (CPU only)."""
+    from conditioning import CAP, bar_factor
+    assert CAP == 4.0
+    assert bar_factor(0.5) == 1.0 and bar_factor(0.2) == 1.0
+    assert abs(bar_factor(0.1) - 2.0) < 1e-12
+    assert bar_factor(0.05) == 4.0 and bar_factor(1e-9) == 4.0 and bar_factor(0.0) == 4.0
+
+
+def _case(causal, seed):
+    wl = custom("factors", "bf16", (5, 9, 0, 4, 1), 4, 2, 16, depth=3, causal=causal, seed=seed)
+    inp = make_inputs(wl)
+    g = torch.Generator().manual_seed(seed + 1)
+    # vectors at 0.5 scale: heads with lambda near 1, so some rows cancel
+    inp.lq1, inp.lk1, inp.lq2, inp.lk2 = [0.5 * torch.randn(4, 16, generator=g)
+                                          for _ in range(4)]
+    return inp
+
+
+def test_row_factors_equal_rowwise_ratios():
+    """The backward's per-row multipliers, from whole score matrices, equal
+    bar_factor of the row-by-row ratio, and 1 where a row sees one key
+    (CPU only)."""
     import numpy as np
-    from conditioning import group_floor
+    from conditioning import bar_factor, row_factors
+    seen_wide = False
     for causal in (True, False):
-        wl = custom("floor", "bf16", (5, 9, 0, 4), 4, 2, 16, depth=3, causal=causal, seed=2)
-        inp = make_inputs(wl)
-        g = torch.Generator().manual_seed(1)
-        inp.lq1, inp.lk1, inp.lq2, inp.lk2 = [0.5 * torch.randn(4, 16, generator=g)
-                                              for _ in range(4)]
-        floor = group_floor(inp)
+        for seed in (2, 3, 4):
+            inp = _case(causal, seed)
+            rf = row_factors(inp)
+            cu = inp.cu_seqlens.tolist()
+            for s in range(len(cu) - 1):
+                for t in range(cu[s], cu[s + 1]):
+                    single = (t == cu[s]) if causal else (cu[s + 1] - cu[s] == 1)
+                    for h in range(4):
+                        want = 1.0 if single else bar_factor(cancellation_ratio(inp, t, h))
+                        assert abs(rf[t, h] - want) < 1e-9, (causal, seed, t, h)
+                        seen_wide |= want > 1.0
+            assert rf.max() <= 4.0
+    assert seen_wide   # the cases do reach the wider bar
+
+
+def test_key_factors_take_the_worst_row_that_sees_the_key():
+    """dk/dv multiplier of key j = max of the row factors of the group's rows
+    that see j (brute force over rows; CPU only)."""
+    import numpy as np
+    from conditioning import key_factors
+    for causal in (True, False):
+        inp = _case(causal, 7)
+        T = inp.q.shape[0]
+        rng = np.random.default_rng(0)
+        rf = rng.uniform(1.0, 4.0, (T, 4))
+        kf = key_factors(inp, rf)
         cu = inp.cu_seqlens.tolist()
-        brute = np.ones_like(floor)
         for s in range(len(cu) - 1):
-            for t in range(cu[s], cu[s + 1]):
-                for h in range(4):
-                    brute[s, h // 2] = min(brute[s, h // 2], cancellation_ratio(inp, t, h))
-        assert np.abs(floor - brute).max() < 1e-12
+            for j in range(cu[s], cu[s + 1]):
+                for g in range(2):
+                    rows = [(t, h) for t in range(cu[s], cu[s + 1])
+                            for h in (2 * g, 2 * g + 1) if (t >= j or not causal)]
+                    assert kf[j, g] == max(rf[t, h] for t, h in rows)
 
 
 def test_rotated_copy_matches_the_oracle_rotary_path():
