@@ -297,7 +297,7 @@ def bench_bwd(args, name) -> int:
     o12 = torch.empty(wl.T, wl.H, 2, 2 * wl.d, dtype=torch.float32, device=dev)
     grads = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)] + \
             [torch.empty_like(x) for x in lv] + [torch.empty(2 * wl.d, device=dev)]
-    need = da.bwd_workspace_size(wl.T, wl.H, wl.d)
+    need = da.bwd_workspace_size(torch.bfloat16, wl.T, wl.H, wl.d)
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
     stream = torch.cuda.Stream(dev)
     lam0 = da.lambda_init(wl.depth)

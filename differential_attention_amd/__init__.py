@@ -91,7 +91,7 @@ def library() -> ctypes.CDLL:
         f32p, ctypes.c_float, ctypes.c_int, i32p, i32, i32, i32, i32, i32, i32,
         vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.diffattn_bwd.restype = ctypes.c_int
-    lib.diffattn_bwd_workspace_size.argtypes = [i32, i32, i32]
+    lib.diffattn_bwd_workspace_size.argtypes = [ctypes.c_int, i32, i32, i32]
     lib.diffattn_bwd_workspace_size.restype = ctypes.c_size_t
     lib.diffattn_supported_bwd.argtypes = [ctypes.c_int, ctypes.c_int]
     lib.diffattn_supported_bwd.restype = ctypes.c_int
@@ -466,8 +466,8 @@ def supported_bwd(dtype: torch.dtype, d: int) -> bool:
     return bool(library().diffattn_supported_bwd(_DTYPES[dtype], int(d)))
 
 
-def bwd_workspace_size(T: int, H: int, d: int) -> int:
-    return int(library().diffattn_bwd_workspace_size(int(T), int(H), int(d)))
+def bwd_workspace_size(dtype: torch.dtype, T: int, H: int, d: int) -> int:
+    return int(library().diffattn_bwd_workspace_size(_DTYPES[dtype], int(T), int(H), int(d)))
 
 
 def _seq_args(T, cu_seqlens, max_seqlen, nseq, dev):
@@ -534,7 +534,7 @@ def bwd(q, k, v, lambda_q1, lambda_k1, lambda_q2, lambda_k2,
         g[name] = alloc(lv)
     g["dw"] = alloc(torch.empty(2 * d, dtype=torch.float32, device=dev))
     if workspace is None:
-        workspace = torch.empty(max(bwd_workspace_size(T, H, d), 16),
+        workspace = torch.empty(max(bwd_workspace_size(q.dtype, T, H, d), 16),
                                 dtype=torch.uint8, device=dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev)

@@ -42,6 +42,14 @@
 //
 // All contractions run on v_mfma_f32_32x32x16_bf16 with fp32 accumulators;
 // P, W and dS are rounded to bf16 as operands, as is dpre.
+//
+// The exact path serves the (storage, d) pairs the MFMA kernels do not
+// (fp32 storage at d = 16, 32, 64; bf16 at d = 16): the same prep and
+// reduce with dpre kept in fp32, then a dq kernel with one wave per query
+// row and a dk/dv kernel with one wave per key row, lanes over the row's
+// dimensions, every score and dot product a 64-lane fp32 sum.  Nothing is
+// rounded below fp32 before the final store; it is built for correctness at
+// the small scales fp32 training runs at, not for speed.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -206,8 +214,26 @@ template <int N> __device__ inline void store_bf16(bf16 *dst, const bf16 (&x)[N]
         v[k] = x[k];
     *(bv *)dst = v;
 }
+template <int N> __device__ inline void store_f32(float *dst, const float (&x)[N])
+{
+    typedef float fv __attribute__((ext_vector_type(N)));
+    fv v;
+#pragma unroll
+    for (int k = 0; k < N; ++k)
+        v[k] = x[k];
+    *(fv *)dst = v;
+}
+// a row of storage-type values as floats / floats stored in a row of the
+// storage or dpre type
+template <int N> __device__ inline void load_row(float (&x)[N], const bf16 *src) { load_bf16(x, src); }
+template <int N> __device__ inline void load_row(float (&x)[N], const float *src) { load_f32(x, src); }
+template <int N> __device__ inline void store_row(bf16 *dst, const bf16 (&x)[N]) { store_bf16(dst, x); }
+template <int N> __device__ inline void store_row(float *dst, const float (&x)[N]) { store_f32(dst, x); }
 
-template <int D>
+// E: storage type of dout; DP: type of the stored dpre (bf16 as the MFMA
+// operand, whose rounded value then also enters D'_m; fp32 on the exact
+// path)
+template <typename E, typename DP, int D>
 __global__ __launch_bounds__(256) void bwd_prep(BwdParams p)
 {
     // a wave takes four (token, head) rows at a time, 16 lanes per row and
@@ -242,7 +268,7 @@ __global__ __launch_bounds__(256) void bwd_prep(BwdParams p)
             const float *o1 = p.o12 + row * 2 * (2 * D) + CPL * l16;
             load_f32(a1, o1);
             load_f32(a2, o1 + 2 * D);
-            load_bf16(dyv, p.dy + row * (2 * D) + CPL * l16);
+            load_row(dyv, (const E *)p.dy + row * (2 * D) + CPL * l16);
         } else {
 #pragma unroll
             for (int cc = 0; cc < CPL; ++cc)
@@ -262,11 +288,11 @@ __global__ __launch_bounds__(256) void bwd_prep(BwdParams p)
         const float r = rsqrtf(ss / (float)(2 * D) + p.eps);
         const float r3 = r * r * r * gp / (float)(2 * D);
         float d1 = 0.f, d2 = 0.f;
-        bf16 b1[CPL];
+        DP b1[CPL];
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc) {
             const float dpre = r * g[cc] - r3 * pre[cc];
-            b1[cc] = (bf16)dpre;
+            b1[cc] = (DP)dpre;
             d1 += (float)b1[cc] * a1[cc];
             d2 += (float)b1[cc] * a2[cc];
             dlp -= dpre * a2[cc];
@@ -275,7 +301,7 @@ __global__ __launch_bounds__(256) void bwd_prep(BwdParams p)
         d1 = seg16_sum(d1);
         d2 = seg16_sum(d2);
         if (ok) {
-            store_bf16(p.dpre + row * (2 * D) + CPL * l16, b1);
+            store_row((DP *)p.dpre + row * (2 * D) + CPL * l16, b1);
             if (l16 == 0) {
                 p.dd[row * 2] = d1;
                 p.dd[row * 2 + 1] = lam * d2;
@@ -840,15 +866,158 @@ void bwd_dkdv(BwdParams p)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Exact path.  The sequence of token t: the last s with cu[s] <= t (zero-
+// length sequences are skipped over).
+__device__ inline void seq_of(const BwdParams &p, int t, int &s0, int &s1)
+{
+    if (p.cu) {
+        int lo = 0, hi = p.nseq;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (p.cu[mid] <= t)
+                lo = mid;
+            else
+                hi = mid;
+        }
+        s0 = p.cu[lo];
+        s1 = p.cu[lo + 1];
+    } else {
+        s0 = (t / p.seqlen_uniform) * p.seqlen_uniform;
+        s1 = s0 + p.seqlen_uniform;
+    }
+}
+
+// lane's elements of a d-wide half (dim lane, if lane < D) and of a 2d-wide
+// row (dims lane + 64 i)
+template <int D> struct Lanes {
+    static constexpr int NV = (2 * D + 63) / 64;   // 2d-row elements per lane
+};
+
+// dq: one wave per (token t, head h): over the keys j the row sees,
+//   P_m = 2^(<Q_m, K_m[j]> log2(e) / sqrt(d) - lse_m), dP' = <dpre, V[j]>,
+//   dS_1 = P_1 (dP' - D'_1), dS_2 = P_2 (lambda D'_2 - lambda dP'),
+//   dQ_m += dS_m K_m[j] / sqrt(d).
+template <typename E, int D>
+__global__ __launch_bounds__(256) void bwdx_dq(BwdParams p)
+{
+    constexpr int NV = Lanes<D>::NV;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // t H + h
+    if (row >= (int64_t)p.T * p.H)
+        return;
+    const int t = (int)(row / p.H), h = (int)(row % p.H), g = h / p.G;
+    int s0, s1;
+    seq_of(p, t, s0, s1);
+    const int jend = p.causal ? t + 1 : s1;
+    const float c = kLog2e * rsqrtf((float)D);
+    const E *q = (const E *)p.q, *k = (const E *)p.k, *v = (const E *)p.v;
+    const float *dpre = (const float *)p.dpre;
+    const bool cd = lane < D;
+    const float q1 = cd ? (float)q[(row * 2) * D + lane] : 0.f;
+    const float q2 = cd ? (float)q[(row * 2 + 1) * D + lane] : 0.f;
+    float dp[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+        dp[i] = lane + 64 * i < 2 * D ? dpre[row * (2 * D) + lane + 64 * i] : 0.f;
+    const float lse1 = p.lse[row * 2], lse2 = p.lse[row * 2 + 1];
+    const float dd1 = p.dd[row * 2], dd2 = p.dd[row * 2 + 1];   // D'_1, lambda D'_2
+    const float lam = p.lam[h];
+    float a1 = 0.f, a2 = 0.f;
+    for (int j = s0; j < jend; ++j) {
+        const int64_t kr = (int64_t)j * p.Hkv + g;
+        const float k1 = cd ? (float)k[(kr * 2) * D + lane] : 0.f;
+        const float k2 = cd ? (float)k[(kr * 2 + 1) * D + lane] : 0.f;
+        float vd = 0.f;
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            if (lane + 64 * i < 2 * D)
+                vd += dp[i] * (float)v[kr * (2 * D) + lane + 64 * i];
+        const float sa = wave_sum(q1 * k1), sb = wave_sum(q2 * k2), dpv = wave_sum(vd);
+        const float P1 = exp2f(sa * c - lse1), P2 = exp2f(sb * c - lse2);
+        a1 += P1 * (dpv - dd1) * k1;
+        a2 += P2 * (dd2 - lam * dpv) * k2;
+    }
+    if (cd) {
+        const float isd = rsqrtf((float)D);
+        ((E *)p.dq)[(row * 2) * D + lane] = (E)(a1 * isd);
+        ((E *)p.dq)[(row * 2 + 1) * D + lane] = (E)(a2 * isd);
+    }
+}
+
+// dk, dv: one wave per (key token j, KV head g): over the rows (t, h) of the
+// group that see key j, with P_m, dP', dS_m as in bwdx_dq,
+//   dK_m += dS_m Q_m[t, h] / sqrt(d),  dV += (P_1 - lambda_h P_2) dpre[t, h].
+template <typename E, int D>
+__global__ __launch_bounds__(256) void bwdx_dkdv(BwdParams p)
+{
+    constexpr int NV = Lanes<D>::NV;
+    const int lane = threadIdx.x & 63;
+    const int64_t kr = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // j Hkv + g
+    if (kr >= (int64_t)p.T * p.Hkv)
+        return;
+    const int j = (int)(kr / p.Hkv), g = (int)(kr % p.Hkv);
+    int s0, s1;
+    seq_of(p, j, s0, s1);
+    const int tbeg = p.causal ? j : s0;
+    const float c = kLog2e * rsqrtf((float)D);
+    const E *q = (const E *)p.q, *k = (const E *)p.k, *v = (const E *)p.v;
+    const float *dpre = (const float *)p.dpre;
+    const bool cd = lane < D;
+    const float k1 = cd ? (float)k[(kr * 2) * D + lane] : 0.f;
+    const float k2 = cd ? (float)k[(kr * 2 + 1) * D + lane] : 0.f;
+    float vv[NV], dv[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        vv[i] = lane + 64 * i < 2 * D ? (float)v[kr * (2 * D) + lane + 64 * i] : 0.f;
+        dv[i] = 0.f;
+    }
+    float a1 = 0.f, a2 = 0.f;
+    for (int hh = 0; hh < p.G; ++hh) {
+        const int h = g * p.G + hh;
+        const float lam = p.lam[h];
+        for (int t = tbeg; t < s1; ++t) {
+            const int64_t row = (int64_t)t * p.H + h;
+            const float q1 = cd ? (float)q[(row * 2) * D + lane] : 0.f;
+            const float q2 = cd ? (float)q[(row * 2 + 1) * D + lane] : 0.f;
+            float dp[NV], vd = 0.f;
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                dp[i] = lane + 64 * i < 2 * D ? dpre[row * (2 * D) + lane + 64 * i] : 0.f;
+                vd += dp[i] * vv[i];
+            }
+            const float sa = wave_sum(q1 * k1), sb = wave_sum(q2 * k2), dpv = wave_sum(vd);
+            const float P1 = exp2f(sa * c - p.lse[row * 2]);
+            const float P2 = exp2f(sb * c - p.lse[row * 2 + 1]);
+            a1 += P1 * (dpv - p.dd[row * 2]) * q1;
+            a2 += P2 * (p.dd[row * 2 + 1] - lam * dpv) * q2;
+            const float W = P1 - lam * P2;
+#pragma unroll
+            for (int i = 0; i < NV; ++i)
+                dv[i] += W * dp[i];
+        }
+    }
+    const float isd = rsqrtf((float)D);
+    if (cd) {
+        ((E *)p.dk)[(kr * 2) * D + lane] = (E)(a1 * isd);
+        ((E *)p.dk)[(kr * 2 + 1) * D + lane] = (E)(a2 * isd);
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+        if (lane + 64 * i < 2 * D)
+            ((E *)p.dv)[kr * (2 * D) + lane + 64 * i] = (E)dv[i];
+}
+
 struct BwdPlan {
     size_t dpre, dd, lam, part_dw, part_dl, total;
 };
 
-BwdPlan bwd_plan(int64_t T, int H, int d)
+// dpre_bytes: 2 on the MFMA path (bf16 operand), 4 on the exact path
+BwdPlan bwd_plan(int64_t T, int H, int d, int dpre_bytes)
 {
     BwdPlan pl;
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-    pl.dpre = up((size_t)T * H * (2 * d) * 2);
+    pl.dpre = up((size_t)T * H * (2 * d) * dpre_bytes);
     pl.dd = up((size_t)T * H * 2 * 4);
     pl.lam = up((size_t)H * 4);
     pl.part_dw = up((size_t)H * (kPrepPerHead / 4) * 2 * d * 4);
@@ -860,11 +1029,26 @@ BwdPlan bwd_plan(int64_t T, int H, int d)
 template <int D>
 void launch_bwd(const BwdParams &p, int nseq, int Hkv, hipStream_t st)
 {
-    hipLaunchKernelGGL(bwd_prep<D>, dim3(p.H * kPrepBlocksPerHead), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((bwd_prep<bf16, bf16, D>), dim3(p.H * kPrepBlocksPerHead), dim3(256), 0,
+                       st, p);
     hipLaunchKernelGGL(bwd_reduce<D>, dim3(1), dim3(1024), 0, st, p);
     hipLaunchKernelGGL(bwd_dq<D>, dim3(p.ntile * nseq * p.H), dim3(kThreads), 0, st, p);
     hipLaunchKernelGGL(bwd_dkdv<D>, dim3(p.ntile * nseq * Hkv), dim3(kThreads), 0, st, p);
 }
+
+template <typename E, int D>
+void launch_bwd_exact(const BwdParams &p, hipStream_t st)
+{
+    hipLaunchKernelGGL((bwd_prep<E, float, D>), dim3(p.H * kPrepBlocksPerHead), dim3(256), 0,
+                       st, p);
+    hipLaunchKernelGGL(bwd_reduce<D>, dim3(1), dim3(1024), 0, st, p);
+    const int64_t rq = ((int64_t)p.T * p.H + 3) / 4, rk = ((int64_t)p.T * p.Hkv + 3) / 4;
+    hipLaunchKernelGGL((bwdx_dq<E, D>), dim3((unsigned)rq), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((bwdx_dkdv<E, D>), dim3((unsigned)rk), dim3(256), 0, st, p);
+}
+
+// the MFMA kernels serve bf16 at d = 32 and 64; the exact path the rest
+bool mfma_path(int dtype, int d) { return dtype == DIFFATTN_BF16 && (d == 32 || d == 64); }
 
 bool a16(const void *x) { return ((uintptr_t)x & 15u) == 0; }
 
@@ -872,14 +1056,14 @@ bool a16(const void *x) { return ((uintptr_t)x & 15u) == 0; }
 
 extern "C" int diffattn_supported_bwd(int dtype, int d)
 {
-    return dtype == DIFFATTN_BF16 && (d == 32 || d == 64);
+    return (dtype == DIFFATTN_BF16 || dtype == DIFFATTN_F32) && (d == 16 || d == 32 || d == 64);
 }
 
-extern "C" size_t diffattn_bwd_workspace_size(int32_t T, int32_t H, int32_t d)
+extern "C" size_t diffattn_bwd_workspace_size(int dtype, int32_t T, int32_t H, int32_t d)
 {
-    if (T < 0 || H < 1 || d < 1)
+    if (T < 0 || H < 1 || d < 1 || !diffattn_supported_bwd(dtype, d))
         return 0;
-    return bwd_plan(T, H, d).total;
+    return bwd_plan(T, H, d, mfma_path(dtype, d) ? 2 : 4).total;
 }
 
 extern "C" int diffattn_bwd(int dtype, const void *q, const void *k, const void *v,
@@ -918,7 +1102,8 @@ extern "C" int diffattn_bwd(int dtype, const void *q, const void *k, const void 
     } else if (max_seqlen < 0 || max_seqlen > T) {
         return DIFFATTN_EINVAL;
     }
-    const BwdPlan pl = bwd_plan(T, H, d);
+    const bool mfma = mfma_path(dtype, d);
+    const BwdPlan pl = bwd_plan(T, H, d, mfma ? 2 : 4);
     if (T > 0) {
         if (!q || !k || !v || !dout || !lse || !o12 || !dq || !dk || !dv || !workspace)
             return DIFFATTN_EINVAL;
@@ -975,12 +1160,24 @@ extern "C" int diffattn_bwd(int dtype, const void *q, const void *k, const void 
     const int64_t blocks = (int64_t)p.ntile * nseq * H;
     if (blocks > INT32_MAX)
         return DIFFATTN_EINVAL;
+    if (!mfma && ((int64_t)T * H + 3) / 4 > INT32_MAX)   // exact path: a wave per row
+        return DIFFATTN_EINVAL;
     hipStream_t st = (hipStream_t)stream;
     if (T == 0)
         return DIFFATTN_OK;   // no rows: nothing is launched or written
-    if (d == 64)
-        launch_bwd<64>(p, nseq, Hkv, st);
-    else
-        launch_bwd<32>(p, nseq, Hkv, st);
+    if (mfma) {
+        if (d == 64)
+            launch_bwd<64>(p, nseq, Hkv, st);
+        else
+            launch_bwd<32>(p, nseq, Hkv, st);
+    } else if (dtype == DIFFATTN_BF16) {
+        launch_bwd_exact<bf16, 16>(p, st);
+    } else if (d == 64) {
+        launch_bwd_exact<float, 64>(p, st);
+    } else if (d == 32) {
+        launch_bwd_exact<float, 32>(p, st);
+    } else {
+        launch_bwd_exact<float, 16>(p, st);
+    }
     return hipGetLastError() == hipSuccess ? DIFFATTN_OK : DIFFATTN_EHIP;
 }

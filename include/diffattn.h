@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define DIFFATTN_ABI_VERSION 7
+#define DIFFATTN_ABI_VERSION 8
 
 enum diffattn_status {
     DIFFATTN_OK = 0,
@@ -284,7 +284,11 @@ int diffattn_fwd_train(int dtype, const void *q, const void *k, const void *v,
  *   dlq2 = -dlambda e^b lk2, dlk2 = -dlambda e^b lq2
  * (dlambda summed over all heads when the vectors are shared).
  *
- *   dtype        DIFFATTN_BF16 (see diffattn_supported_bwd).
+ *   dtype        DIFFATTN_BF16 or DIFFATTN_F32, d = 16, 32 or 64 (see
+ *                diffattn_supported_bwd).  bf16 at d = 32 and 64 runs the
+ *                MFMA kernels (bf16 operands, fp32 accumulation); the other
+ *                pairs run exact kernels that keep every intermediate in
+ *                fp32 and round only the stored gradients.
  *   q .. max_seqlen, T, H, Hkv, d
  *                exactly as given to diffattn_fwd_train (H <= 256).
  *   dout         device [T, H, 2d], storage type.
@@ -295,7 +299,7 @@ int diffattn_fwd_train(int dtype, const void *q, const void *k, const void *v,
  *                device fp32 outputs laid out like the lambda vectors
  *                (d elements, or H sets lambda_stride apart).
  *   dsubln_weight device fp32 [2d] output, or NULL to skip it.
- *   workspace    device scratch of diffattn_bwd_workspace_size(T, H, d)
+ *   workspace    device scratch of diffattn_bwd_workspace_size(dtype, T, H, d)
  *                bytes, 16-byte aligned, owned by the caller; no
  *                initialisation needed; calls in flight at once need
  *                separate workspaces.
@@ -317,9 +321,9 @@ int diffattn_bwd(int dtype, const void *q, const void *k, const void *v,
                  float *dsubln_weight, void *workspace, size_t workspace_bytes,
                  void *stream);
 
-/* Bytes of workspace diffattn_bwd needs; 0 for sizes it rejects.  Host
- * function. */
-size_t diffattn_bwd_workspace_size(int32_t T, int32_t H, int32_t d);
+/* Bytes of workspace diffattn_bwd needs for (dtype, T, H, d); 0 for sizes
+ * or (dtype, d) pairs it rejects.  Host function. */
+size_t diffattn_bwd_workspace_size(int dtype, int32_t T, int32_t H, int32_t d);
 
 /* 1 if the backward kernels are compiled for (dtype, d), else 0.  Host
  * function. */

@@ -234,11 +234,20 @@ def test_kv_noalloc_too_large_matches_workspace_size():
 
 def test_supported_bwd_and_workspace():
     import torch
-    assert da.supported_bwd(torch.bfloat16, 64)
-    assert da.supported_bwd(torch.bfloat16, 32)
-    assert not da.supported_bwd(torch.float32, 64)
-    assert da.bwd_workspace_size(4096, 16, 64) > da.bwd_workspace_size(1024, 16, 64) > 0
-    assert da.bwd_workspace_size(-1, 16, 64) == 0
+    for dt in (torch.bfloat16, torch.float32):
+        for d in (16, 32, 64):
+            assert da.supported_bwd(dt, d)
+        assert not da.supported_bwd(dt, 48)
+    assert not da.library().diffattn_supported_bwd(9, 64)
+    bf, f32 = torch.bfloat16, torch.float32
+    assert da.bwd_workspace_size(bf, 4096, 16, 64) > da.bwd_workspace_size(bf, 1024, 16, 64) > 0
+    assert da.bwd_workspace_size(bf, -1, 16, 64) == 0
+    assert da.bwd_workspace_size(f32, 1024, 16, 48) == 0
+    # the exact path (fp32, and bf16 at d = 16) keeps dpre [T, H, 2d] in fp32,
+    # the MFMA path in bf16
+    assert (da.bwd_workspace_size(f32, 1024, 16, 64) - da.bwd_workspace_size(bf, 1024, 16, 64)
+            == 1024 * 16 * 128 * 2)
+    assert da.bwd_workspace_size(bf, 1024, 16, 16) == da.bwd_workspace_size(f32, 1024, 16, 16)
 
 
 def call_bwd(**over):
@@ -256,8 +265,9 @@ def call_bwd(**over):
 
 @pytest.mark.parametrize("over,status", [
     (dict(dtype=9), da.EINVAL),
-    (dict(dtype=da.F32), da.EUNSUPPORTED),
-    (dict(d=16), da.EUNSUPPORTED),
+    (dict(dtype=da.F32, d=48), da.EUNSUPPORTED),
+    (dict(d=48), da.EUNSUPPORTED),
+    (dict(d=128), da.EUNSUPPORTED),
     (dict(H=6), da.EINVAL),
     (dict(H=512, Hkv=4), da.EINVAL),            # more heads than supported
     (dict(causal=3), da.EINVAL),

@@ -117,7 +117,7 @@ def test_training_step_graph():
     lam0 = da.lambda_init(wl.depth)
     dy = torch.randn((q.shape[0], wl.H, 2 * wl.d), generator=torch.Generator().manual_seed(8))
     dy = dy.to(q.dtype).to(DEV).contiguous()
-    ws = torch.empty(da.bwd_workspace_size(q.shape[0], wl.H, wl.d), dtype=torch.uint8,
+    ws = torch.empty(da.bwd_workspace_size(q.dtype, q.shape[0], wl.H, wl.d), dtype=torch.uint8,
                      device=DEV)
     kw = dict(subln_weight=w, eps=wl.eps, causal=True, cu_seqlens=cu, max_seqlen=wl.max_seqlen)
     names = ("dq", "dk", "dv", "dlq1", "dlk1", "dlq2", "dlk2", "dw")

@@ -9,7 +9,15 @@ gradients are dlambda times a vector, and dlambda = -sum over rows of
 <dpre, O_2> can cancel to far below its terms, each of which carries the
 forward's bf16 rounding of P; their error is bounded instead by 2^-7 (two
 bf16 roundings) times the oracle's sum over rows of |dpre| |O_2|, times the
-vector factor.  All tests need an MI355X.
+vector factor.
+
+fp32 storage (and bf16 at d = 16) runs the exact kernels, fp32 throughout:
+with fp32 inputs every gradient, the lambda-vector ones included, is held
+to 2e-5 of the same scales (fp32 sums over at most a few thousand terms sit
+near 1e-6).  Every bf16 random case also runs as an fp32 twin (the same
+values in fp32 storage) against that bar, which shows the bf16 cases' error
+is the operand rounding and not a slip of the arithmetic.  All tests need an
+MI355X.
 """
 
 import numpy as np
@@ -24,6 +32,15 @@ pytestmark = pytest.mark.gpu
 
 REL = {"dq": 2e-2, "dk": 2e-2, "dv": 2e-2, "dlq1": 2.0 ** -7, "dlk1": 2.0 ** -7,
        "dlq2": 2.0 ** -7, "dlk2": 2.0 ** -7, "dw": 2e-2}
+REL32 = {name: 2e-5 for name in REL}
+
+
+def fp32_twin(inp, dy):
+    """The same input values in fp32 storage (bf16 -> fp32 is exact)."""
+    import copy
+    twin = copy.copy(inp)
+    twin.q, twin.k, twin.v = inp.q.float(), inp.k.float(), inp.v.float()
+    return twin, dy.float()
 
 
 def announce(msg):
@@ -70,7 +87,7 @@ def conditioning_factors(inp):
     return rf, key_factors(inp, rf)
 
 
-def compare(got, ref, tag, inp=None):
+def compare(got, ref, tag, inp=None, rel=REL):
     """dq, dk, dv, dw: max-abs relative to the tensor's largest magnitude
     (with inp given, dq, dk and dv elementwise against the bar times the
     multiplier of their row or key, conditioning_factors).
@@ -100,14 +117,14 @@ def compare(got, ref, tag, inp=None):
             if fac is not None and name in ("dq", "dk", "dv"):
                 f = fac[0] if name == "dq" else fac[1]           # [T, heads]
                 # elements beyond the plain bar are the ones the wider bar admits
-                widened += int(np.sum(e > REL[name] * scale))
+                widened += int(np.sum(e > rel[name] * scale))
                 e = e / f.reshape(f.shape + (1,) * (e.ndim - 2))
             errs[name] = float(np.max(e)) / scale
     announce(f"{tag}: " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()) +
              (f"; {widened} elements past the plain bar" if widened else ""))
     for name, err in errs.items():
-        assert err <= REL[name], f"{tag}: {name} relative max-abs {err:.3e}"
-    return max(errs[n] / REL[n] for n in errs)
+        assert err <= rel[name], f"{tag}: {name} relative max-abs {err:.3e}"
+    return max(errs[n] / rel[n] for n in errs)
 
 
 RAGGED = (1, 0, 31, 32, 33, 63, 64, 65, 127, 200, 7)
@@ -125,6 +142,50 @@ def test_bwd_ragged(d, H, Hkv, causal):
     _, (got,) = gpu_grads(inp, dy)
     worst = compare(got, oracle_grads(inp, dy), f"d={d} H={H} Hkv={Hkv} causal={causal}")
     announce(f"ragged d={d} H={H} Hkv={Hkv} causal={causal}: worst err / bar {worst:.3f}")
+
+
+# the exact kernels: fp32 storage at every d, bf16 at d = 16
+@pytest.mark.parametrize("dtype,d", [("f32", 16), ("f32", 32), ("f32", 64), ("bf16", 16)])
+@pytest.mark.parametrize("H,Hkv", [(4, 2), (3, 1), (10, 5), (8, 8)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_bwd_exact_path_ragged(dtype, d, H, Hkv, causal):
+    wl = custom("bwd_exact", dtype, RAGGED, H, Hkv, d, depth=5, causal=causal,
+                seed=H * 10 + d + 1)
+    inp = make_inputs(wl)
+    inp.w = torch.linspace(0.5, 1.5, 2 * d)
+    dy = dout_for(inp, 17)
+    _, (got,) = gpu_grads(inp, dy)
+    tag = f"exact {dtype} d={d} H={H} Hkv={Hkv} causal={causal}"
+    worst = compare(got, oracle_grads(inp, dy), tag, inp=inp,
+                    rel=REL32 if dtype == "f32" else REL)
+    announce(f"{tag}: worst err / bar {worst:.3f}")
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_bwd_exact_path_random(i):
+    """Seeded random shapes on the exact kernels, per-head lambda in half of
+    them, longer sequences than the ragged matrix (up to 1500 keys)."""
+    rng = np.random.default_rng(7500 + i)
+    dtype, d = [("f32", 64), ("f32", 32), ("f32", 16), ("bf16", 16)][i % 4]
+    Hkv = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 2, 3, 4]))
+    lens = tuple(int(x) for x in rng.integers(0, 1500, int(rng.integers(1, 4))))
+    if sum(lens) == 0:
+        lens = lens + (9,)
+    causal = bool(rng.integers(0, 2))
+    wl = custom("bwd_exact_random", dtype, lens, Hkv * G, Hkv, d, depth=3 + i,
+                causal=causal, seed=8500 + i)
+    inp = make_inputs(wl)
+    if rng.integers(0, 2):
+        g = torch.Generator().manual_seed(9500 + i)
+        inp.lq1, inp.lk1, inp.lq2, inp.lk2 = [0.3 * torch.randn(Hkv * G, d, generator=g)
+                                              for _ in range(4)]
+    dy = dout_for(inp, 40 + i)
+    _, (got,) = gpu_grads(inp, dy)
+    tag = f"exact random {i}: {dtype} lens {lens} H={Hkv * G} Hkv={Hkv} d={d} causal={causal}"
+    worst = compare(got, oracle_grads(inp, dy), tag, inp=inp,
+                    rel=REL32 if dtype == "f32" else REL)
+    announce(f"{tag}: worst err / bar {worst:.3f}")
 
 
 def test_bwd_embed2048_full():
@@ -278,7 +339,11 @@ def test_bwd_random_shapes(i):
                                               for _ in range(4)]
     dy = dout_for(inp, 10 + i)
     _, (got,) = gpu_grads(inp, dy, w=use_w)
-    worst = compare(got, oracle_grads(inp, dy, w=use_w),
-                    f"random {i}: lens {lens} H={Hkv * G} Hkv={Hkv} d={d} causal={causal}",
-                    inp=inp)
+    ref = oracle_grads(inp, dy, w=use_w)
+    tag = f"random {i}: lens {lens} H={Hkv * G} Hkv={Hkv} d={d} causal={causal}"
+    worst = compare(got, ref, tag, inp=inp)
     announce(f"random case {i}: worst err / bar {worst:.3f}")
+    twin, dy32 = fp32_twin(inp, dy)
+    _, (got32,) = gpu_grads(twin, dy32, w=use_w)
+    worst32 = compare(got32, ref, "fp32 twin of " + tag, inp=twin, rel=REL32)
+    announce(f"random case {i}, fp32 twin: worst err / bar {worst32:.3f}")
