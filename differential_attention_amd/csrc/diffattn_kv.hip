@@ -116,23 +116,6 @@ __device__ inline void seq_bounds(const int32_t *cu, int uniform, int s, int &a,
 // wave-wide scan of cu_seqlens_k, 64 sequences per step (wave-uniform).
 __device__ inline int split_count(int nk, int ck) { return (nk + ck - 1) / ck; }
 
-// base(s) of sequence s
-__device__ inline int split_base(const KvParams &p, int s, int lane)
-{
-    if (!p.cuk)
-        return s * split_count(p.klen_uniform, p.ck);
-    int base = 0;
-    for (int s0 = 0; s0 < s; s0 += 64) {
-        const int si = s0 + lane;
-        int cnt = si < s ? split_count(p.cuk[si + 1] - p.cuk[si], p.ck) : 0;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1)
-            cnt += __shfl_xor(cnt, off, 64);
-        base += cnt;
-    }
-    return base;
-}
-
 // Sequence owning slot j and its base, or false past the last split.
 __device__ inline bool split_owner(const KvParams &p, int j, int lane, int &s, int &base)
 {
@@ -455,31 +438,71 @@ void diffattn_kv_combine(KvParams p)
     const int s = (int)(wid / p.max_q);
     if (s >= p.nseq)
         return;
-    int qa, nq, ka, nk;
-    seq_bounds(p.cuq, p.qlen_uniform, s, qa, nq);
-    seq_bounds(p.cuk, p.klen_uniform, s, ka, nk);
+    // ---- first memory round trip: everything that does not depend on the
+    // partials -- the sequence bounds, the split counts of the sequences
+    // before this one (the first 64 of them, one per lane), the lambda
+    // vectors and the weight -- is loaded before any of it is used, so the
+    // loads travel together (used one by one, each would wait out its own
+    // round trip)
+    // (unconditional loads at clamped indices: a load under a lane mask
+    // would make the compiler wait for it inside the masked block)
+    static_assert(D <= 64 && (D & (D - 1)) == 0, "one lambda-vector element per lane");
+    const int64_t lo = (int64_t)h * p.lstride + (lane & (D - 1));
+    const float lq1 = p.lq1[lo], lk1 = p.lk1[lo], lq2 = p.lq2[lo], lk2 = p.lk2[lo];
+    float wc[CPL];
+#pragma unroll
+    for (int cc = 0; cc < CPL; ++cc)
+        wc[cc] = p.w ? p.w[CPL * lane + cc] : 1.f;
+    int qa, qe, ka, ke;
+    int kb0 = 0, kb1 = 0;   // bounds of sequence `lane`, used if lane < s
+    if (p.cuq) {
+        qa = p.cuq[s];
+        qe = p.cuq[s + 1];
+        ka = p.cuk[s];
+        ke = p.cuk[s + 1];
+        const int li = lane < s ? lane : s;
+        kb0 = p.cuk[li];
+        kb1 = p.cuk[li + 1];
+    } else {
+        qa = s * p.qlen_uniform;
+        qe = qa + p.qlen_uniform;
+        ka = s * p.klen_uniform;
+        ke = ka + p.klen_uniform;
+    }
+    const float d1 = lane < D ? lq1 * lk1 : 0.f;
+    const float d2 = lane < D ? lq2 * lk2 : 0.f;
+
+    const int nq = qe - qa, nk = ke - ka;
     if (i >= nq)
         return;
     const int g = h / p.G;
     const int r = i * p.G + h % p.G;
-    const int sbase = split_base(p, s, lane);
+    // base of this sequence's splits: the sum of the split counts of the
+    // sequences before it (the first 64 already loaded)
+    int sbase;
+    if (!p.cuk) {
+        sbase = s * split_count(p.klen_uniform, p.ck);
+    } else {
+        int cnt = lane < s ? split_count(kb1 - kb0, p.ck) : 0;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1)
+            cnt += __shfl_xor(cnt, off, 64);
+        sbase = cnt;
+        for (int s0 = 64; s0 < s; s0 += 64) {
+            const int si = s0 + lane;
+            int c2 = si < s ? split_count(p.cuk[si + 1] - p.cuk[si], p.ck) : 0;
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1)
+                c2 += __shfl_xor(c2, off, 64);
+            sbase += c2;
+        }
+    }
     // (the clamp only matters when cu_seqlens_k breaks its preconditions:
     // no read past the workspace)
     const int nsp = max(0, min(split_count(nk, p.ck), p.nslots - sbase));
 
     // lambda of this head
-    float lam;
-    {
-        const int64_t lo = (int64_t)h * p.lstride;
-        float d1 = 0.f, d2 = 0.f;
-        for (int cc = lane; cc < D; cc += 64) {
-            d1 += p.lq1[lo + cc] * p.lk1[lo + cc];
-            d2 += p.lq2[lo + cc] * p.lk2[lo + cc];
-        }
-        d1 = wave_sum(d1);
-        d2 = wave_sum(d2);
-        lam = expf(d1) - expf(d2) + p.lambda_init;
-    }
+    const float lam = expf(wave_sum(d1)) - expf(wave_sum(d2)) + p.lambda_init;
 
     // merge the splits of both maps (log-sum-exp in log2 units), up to
     // kChunk splits per round: lane j loads split j's (m, l) of both maps in
@@ -554,10 +577,8 @@ void diffattn_kv_combine(KvParams p)
     const float scale = rsqrtf(ss / (float)(2 * D) + p.eps) * (1.f - p.lambda_init);
     bf16 *dst = (bf16 *)p.out + ((int64_t)(qa + i) * p.H + h) * (2 * D) + CPL * lane;
 #pragma unroll
-    for (int cc = 0; cc < CPL; ++cc) {
-        const float wc = p.w ? p.w[CPL * lane + cc] : 1.f;
-        dst[cc] = (bf16)(pre[cc] * scale * wc);
-    }
+    for (int cc = 0; cc < CPL; ++cc)
+        dst[cc] = (bf16)(pre[cc] * scale * wc[cc]);
 }
 
 // Split policy: keys per split ck chosen from the total number of cache
