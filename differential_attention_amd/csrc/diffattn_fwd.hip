@@ -14,7 +14,10 @@
 //   otherwise  : 1 head   x 256 queries
 // and every slot is served by two waves, one per attention map: wave w
 // computes map (w / 4) of slot (w % 4) for its 64 queries, as two 32-query
-// sub-blocks.  Each K operand read and each V operand read of a wave feeds
+// sub-blocks.  (Grids that would leave fewer than two workgroups per CU run
+// an instantiation with one 32-query sub-block per wave, so twice the
+// workgroups share the work; everything below then holds with 32 queries
+// per slot.)  Each K operand read and each V operand read of a wave feeds
 // two MFMAs (one per sub-block), and each K/V tile staged in LDS serves 256
 // query rows of the GQA group, which keeps LDS traffic per MFMA low (the
 // transposing V read runs at half the LDS read rate, 16-byte LDS writes at a
@@ -81,10 +84,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 8;    // two maps x four slots
+constexpr int kCUs = 256;    // compute units of the part
 constexpr int kSlots = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kSub = 2;   // 32-query sub-blocks per wave
-constexpr int kQB = 32 * kSub;   // query rows per slot
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleLog2 = 8.0f;   // lazy-max threshold, log2 units
 constexpr float kRescaleSum = 256.0f;  // the same threshold as a probability
@@ -356,14 +358,20 @@ struct Params {
     int32_t ntile_q;   // query tiles per sequence (of the longest one)
     int32_t hpw;       // heads per workgroup (1, 2 or 4)
     int32_t hblocks;   // head blocks per KV group: G / hpw
+    int32_t sub;       // 32-query sub-blocks per wave (the kernel's SUB)
 };
 
 // Every CU runs one workgroup of 8 waves (two per SIMD); the register
-// budget per lane is the 256 that two waves per SIMD leave.
-template <typename E, int D, bool ROPE>
+// budget per lane is the 256 that two waves per SIMD leave.  SUB: 32-query
+// sub-blocks per wave -- 2 (each K/V operand read feeds two MFMAs), or 1 for
+// grids too small to fill the chip, which doubles the workgroups.
+template <typename E, int D, bool ROPE, int SUB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void diffattn_fwd_kernel(Params p)
 {
+    constexpr int kSub = SUB;
+    constexpr int kQB = 32 * kSub;   // query rows per slot
+    static_assert(SUB == 1 || SUB == 2, "one or two sub-blocks per wave");
     typedef Geo<E, D> GEO;
     typedef Mfma<E> M;
     typedef typename M::Frag Frag;
@@ -764,15 +772,16 @@ void diffattn_fwd_kernel(Params p)
     __syncthreads();
 
     // ---- epilogue: combine through LDS, RMSNorm, scale, store -------------
-    // The two waves of a slot split the epilogue by query sub-block: the
-    // map-1 wave finishes sub-block 0, the map-2 wave sub-block 1.  Each
-    // publishes the term the other needs (map 1: O_1/l_1 of sub-block 1;
-    // map 2: lambda O_2/l_2 of sub-block 0) in its accumulator layout (four
-    // consecutive elements of a lane as one 16-byte entry, lanes adjacent);
-    // the partner's lanes hold the same (query, dim) elements.
+    // With two sub-blocks the two waves of a slot split the epilogue by
+    // query sub-block: the map-1 wave finishes sub-block 0, the map-2 wave
+    // sub-block 1.  Each publishes the term the other needs (map 1: O_1/l_1
+    // of sub-block 1; map 2: lambda O_2/l_2 of sub-block 0) in its
+    // accumulator layout (four consecutive elements of a lane as one 16-byte
+    // entry, lanes adjacent); the partner's lanes hold the same (query, dim)
+    // elements.  With one sub-block the map-2 wave publishes and the map-1
+    // wave finishes.
     float *xch = (float *)((slot < 2 ? stage0 : stage1)) + (slot & 1) * XCH;
     constexpr int XHALF = XCH / kSub;   // floats per published sub-block
-    static_assert(kSub == 2, "one sub-block per map wave");
     float lsum[kSub];
 #pragma unroll
     for (int u = 0; u < kSub; ++u)
@@ -816,10 +825,15 @@ void diffattn_fwd_kernel(Params p)
                     make_float4(acc[db][4 * i] * scale, acc[db][4 * i + 1] * scale,
                                 acc[db][4 * i + 2] * scale, acc[db][4 * i + 3] * scale);
     };
-    if (map == 0)
-        publish(o[1], own[1], xch + XHALF);
-    else
-        publish(o[0], own[0], xch);
+    if constexpr (kSub == 2) {
+        if (map == 0)
+            publish(o[1], own[1], xch + XHALF);
+        else
+            publish(o[0], own[0], xch);
+    } else {
+        if (map == 1)
+            publish(o[0], own[0], xch);
+    }
     // weights of this lane's output dims (loads in flight across the barrier)
     float wv[NDB][16];
 #pragma unroll
@@ -920,8 +934,8 @@ void diffattn_fwd_kernel(Params p)
     };
     if (map == 0)
         finish(o[0], own[0], 0);
-    else
-        finish(o[1], own[1], 1);
+    else if constexpr (kSub == 2)
+        finish(o[kSub - 1], own[kSub - 1], 1);
 }
 
 template <typename E, int D>
@@ -934,12 +948,21 @@ int launch(const Params &p, int nblocks, hipStream_t stream)
                            dim3(256), 0, stream, (const char *)p.k_orig, (char *)p.k, p.cu,
                            p.nseq, p.seqlen_uniform, p.T, p.Hkv, p.rcos, p.rsin);
     }
-    if (p.rcos)
-        hipLaunchKernelGGL((diffattn_fwd_kernel<E, D, true>), dim3(nblocks), dim3(kThreads), 0,
-                           stream, p);
-    else
-        hipLaunchKernelGGL((diffattn_fwd_kernel<E, D, false>), dim3(nblocks), dim3(kThreads), 0,
-                           stream, p);
+    if (p.rcos) {
+        if (p.sub == 2)
+            hipLaunchKernelGGL((diffattn_fwd_kernel<E, D, true, 2>), dim3(nblocks), dim3(kThreads),
+                               0, stream, p);
+        else
+            hipLaunchKernelGGL((diffattn_fwd_kernel<E, D, true, 1>), dim3(nblocks), dim3(kThreads),
+                               0, stream, p);
+    } else {
+        if (p.sub == 2)
+            hipLaunchKernelGGL((diffattn_fwd_kernel<E, D, false, 2>), dim3(nblocks),
+                               dim3(kThreads), 0, stream, p);
+        else
+            hipLaunchKernelGGL((diffattn_fwd_kernel<E, D, false, 1>), dim3(nblocks),
+                               dim3(kThreads), 0, stream, p);
+    }
     return hipGetLastError() == hipSuccess ? DIFFATTN_OK : DIFFATTN_EHIP;
 }
 
@@ -1060,9 +1083,18 @@ int fwd_impl(int dtype, const void *q, const void *k, const void *v,
     // byte offsets of K/V rows are formed in 64 bits; the grid in 32 bits
     const int G = H / Hkv;
     const int hpw = (G % 4 == 0) ? 4 : (G % 2 == 0 ? 2 : 1);
-    const int bm = kQB * (kSlots / hpw);
-    const int64_t ntile_q = ((int64_t)max_seqlen + bm - 1) / bm;
-    const int64_t nblocks = ntile_q * nseq * Hkv * (G / hpw);
+    // 64 queries per wave; 32 when that leaves fewer than two workgroups per
+    // CU (256 CUs), so small problems spread over twice the workgroups
+    int sub = 2;
+    int64_t ntile_q = 0, nblocks = 0;
+    for (;;) {
+        const int bm = 32 * sub * (kSlots / hpw);
+        ntile_q = ((int64_t)max_seqlen + bm - 1) / bm;
+        nblocks = ntile_q * nseq * Hkv * (G / hpw);
+        if (sub == 1 || nblocks >= 2 * kCUs)
+            break;
+        sub = 1;
+    }
     if (nblocks > INT32_MAX)
         return DIFFATTN_EINVAL;
 
@@ -1095,6 +1127,7 @@ int fwd_impl(int dtype, const void *q, const void *k, const void *v,
     p.max_seqlen = max_seqlen;
     p.hpw = hpw;
     p.hblocks = G / hpw;
+    p.sub = sub;
 
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess)

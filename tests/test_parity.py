@@ -13,6 +13,7 @@ import torch
 import oracle
 import workloads
 from conditioning import rows_within_bar
+from launch_shape import prefill_sub_blocks
 from workloads import WORKLOADS, custom, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -159,6 +160,34 @@ def test_ragged_varlen(dtype, d, H, Hkv, causal):
     out = gpu_run(inp)
     err = max_abs(out, oracle_full(inp))
     assert err <= TOL[dtype], f"max-abs {err:.3e}"
+
+
+# Small shapes launch the 32-query instantiation (fewer than 512 workgroups
+# of 64-query slots); many short ragged sequences keep the 64-query one at
+# sizes the oracle finishes at once.
+RAGGED_MANY = RAGGED * 11
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 16), ("bf16", 64), ("f32", 64),
+                                     ("bf16", 16), ("bf16", 32), ("f32", 32)])
+@pytest.mark.parametrize("H,Hkv", [(4, 4), (16, 4), (6, 2)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_ragged_varlen_64_query_slots(dtype, d, H, Hkv, causal):
+    assert prefill_sub_blocks(H, Hkv, len(RAGGED_MANY), max(RAGGED_MANY)) == 2
+    wl = custom("ragged_many", dtype, RAGGED_MANY, H, Hkv, d, depth=7, causal=causal,
+                seed=H * 100 + d + 1)
+    announce(f"ragged x11 {dtype} d={d} H={H} Hkv={Hkv} causal={causal}")
+    inp = make_inputs(wl)
+    inp.w = torch.linspace(1.5, 0.5, 2 * d)
+    out = gpu_run(inp)
+    err = max_abs(out, oracle_full(inp))
+    assert err <= TOL[dtype], f"max-abs {err:.3e}"
+
+
+def test_ragged_shapes_take_32_query_slots():
+    """The ragged matrix above runs on the other instantiation."""
+    for H, Hkv in [(2, 2), (4, 2), (8, 2), (16, 2), (3, 1), (10, 5), (8, 8)]:
+        assert prefill_sub_blocks(H, Hkv, len(RAGGED), max(RAGGED)) == 1
 
 
 def test_fp32_path_at_d64_gqa4():

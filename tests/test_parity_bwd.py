@@ -26,6 +26,7 @@ import torch
 
 import oracle
 from conditioning import key_factors, row_factors
+from launch_shape import prefill_sub_blocks
 from workloads import WORKLOADS, custom, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -142,6 +143,23 @@ def test_bwd_ragged(d, H, Hkv, causal):
     _, (got,) = gpu_grads(inp, dy)
     worst = compare(got, oracle_grads(inp, dy), f"d={d} H={H} Hkv={Hkv} causal={causal}")
     announce(f"ragged d={d} H={H} Hkv={Hkv} causal={causal}: worst err / bar {worst:.3f}")
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("bf16", 32), ("f32", 32), ("bf16", 16)])
+def test_bwd_ragged_64_query_slots(dtype, d):
+    """Many short sequences: the training forward on its 64-query
+    instantiation, then the backward."""
+    lens = RAGGED * 11
+    assert prefill_sub_blocks(16, 4, len(lens), max(lens)) == 2
+    wl = custom("bwd_many", dtype, lens, 16, 4, d, depth=4, causal=True, seed=d + 90)
+    inp = make_inputs(wl)
+    inp.w = torch.linspace(0.5, 1.5, 2 * d)
+    dy = dout_for(inp, 27)
+    _, (got,) = gpu_grads(inp, dy)
+    tag = f"ragged x11 {dtype} d={d}"
+    worst = compare(got, oracle_grads(inp, dy), tag, inp=inp,
+                    rel=REL32 if dtype == "f32" else REL)
+    announce(f"{tag}: worst err / bar {worst:.3f}")
 
 
 # the exact kernels: fp32 storage at every d, bf16 at d = 16

@@ -17,6 +17,7 @@ import torch
 import oracle
 from conditioning import rotated, rows_within_bar
 from workloads import WORKLOADS, custom, make_inputs, rope_tables
+from launch_shape import prefill_sub_blocks
 
 pytestmark = pytest.mark.gpu
 
@@ -69,6 +70,22 @@ def test_ragged_varlen_rope(dtype, d, H, Hkv, causal):
     rope = rope_tables(256, d, base=50.0)
     err = max_abs(gpu_run(inp, rope), oracle_full(inp, rope))
     announce(f"ragged {dtype} d={d} H={H} Hkv={Hkv} causal={causal}: max-abs {err:.3e}")
+    assert err <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 16), ("bf16", 64), ("bf16", 32), ("f32", 64)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_ragged_varlen_rope_64_query_slots(dtype, d, causal):
+    """Many short sequences: the 64-query instantiation with the rotation."""
+    lens = RAGGED * 11
+    assert prefill_sub_blocks(16, 4, len(lens), max(lens)) == 2
+    wl = custom("ragged_rope_many", dtype, lens, 16, 4, d, depth=9, causal=causal,
+                seed=d + 70)
+    inp = make_inputs(wl)
+    inp.w = torch.linspace(1.5, 0.5, 2 * d)
+    rope = rope_tables(256, d, base=50.0)
+    err = max_abs(gpu_run(inp, rope), oracle_full(inp, rope))
+    announce(f"ragged x11 {dtype} d={d} causal={causal}: max-abs {err:.3e}")
     assert err <= TOL[dtype]
 
 
