@@ -48,9 +48,9 @@ GRAPH_STEPS = 10   # decode steps per captured graph (--graph)
 _CSRC = os.path.join(HERE, "differential_attention_amd", "csrc")
 # the sources whose kernels a stored counter profile measured: a profile
 # counts only while their digest matches
-KERNEL_SOURCES = [os.path.join(_CSRC, "diffattn_fwd.hip")]
-KV_KERNEL_SOURCES = [os.path.join(_CSRC, "diffattn_kv.hip")]
-BWD_KERNEL_SOURCES = [os.path.join(_CSRC, "diffattn_fwd.hip"),
+KERNEL_SOURCES = [os.path.join(_CSRC, "diffattn_fwd.hip"), os.path.join(_CSRC, "rope.h")]
+KV_KERNEL_SOURCES = [os.path.join(_CSRC, "diffattn_kv.hip"), os.path.join(_CSRC, "rope.h")]
+BWD_KERNEL_SOURCES = [os.path.join(_CSRC, "diffattn_fwd.hip"), os.path.join(_CSRC, "rope.h"),
                       os.path.join(_CSRC, "diffattn_bwd.hip")]
 
 
@@ -193,7 +193,7 @@ def bench_kv(args, name) -> int:
             *[x.data_ptr() for x in lv], 0, da.lambda_init(wl.depth),
             w.data_ptr(), wl.eps, int(wl.causal), cq.data_ptr(), ck.data_ptr(),
             wl.nseq, wl.max_q, wl.max_k, wl.Tq, wl.Tk, wl.H, wl.Hkv, wl.d,
-            ws.data_ptr(), need, out.data_ptr(), stream.cuda_stream)
+            0, 0, 0, 0, ws.data_ptr(), need, out.data_ptr(), stream.cuda_stream)
 
     def step():
         st = da.fwd_kv_ptr(*ptrs)
@@ -434,12 +434,12 @@ def main() -> int:
     lam0 = da.lambda_init(wl.depth)
     stream = torch.cuda.Stream(dev)
     dtype_code = da.BF16 if wl.dtype == "bf16" else da.F32
-    rope_args = (0, 0, 0, 0, 0)
+    rope_args = (0, 0, 0, 0, 0, 0)
     if args.rope:
         rc, rs = (c(t) for t in workloads.rope_tables(wl.max_seqlen, wl.d))
         need = da.fwd_workspace_size(q.dtype, wl.T, wl.Hkv, wl.d, True)
         rws = torch.empty(need, dtype=torch.uint8, device=dev)
-        rope_args = (rc.data_ptr(), rs.data_ptr(), wl.max_seqlen, rws.data_ptr(), need)
+        rope_args = (rc.data_ptr(), rs.data_ptr(), wl.max_seqlen, da.F32, rws.data_ptr(), need)
     ptrs = (dtype_code, q.data_ptr(), k.data_ptr(), v.data_ptr(),
             *[x.data_ptr() for x in lv], 0, lam0, w.data_ptr(), wl.eps,
             int(wl.causal), cu.data_ptr(), wl.nseq, wl.max_seqlen, wl.T, wl.H,

@@ -20,6 +20,7 @@ import torch
 __all__ = ["fwd", "fwd_ptr", "fwd_workspace_size", "fwd_kv", "fwd_kv_ptr", "kv_workspace_size",
            "fwd_kv_noalloc", "fwd_kv_noalloc_ptr", "KV_SCRATCH_BYTES",
            "fwd_train", "bwd", "bwd_workspace_size", "supported_bwd",
+           "kv_append", "kv_append_ptr",
            "lambda_init", "supported", "supported_kv", "check_cu_seqlens",
            "check_cu_seqlens_kv", "library", "LIBRARY", "DiffAttnError",
            "BF16", "F32"]
@@ -59,20 +60,25 @@ def library() -> ctypes.CDLL:
     lib.diffattn_fwd.argtypes = [
         ctypes.c_int, vp, vp, vp, f32p, f32p, f32p, f32p, i32, ctypes.c_float,
         f32p, ctypes.c_float, ctypes.c_int, i32p, i32, i32, i32, i32, i32, i32,
-        f32p, f32p, i32, vp, ctypes.c_size_t, vp, vp]
+        vp, vp, i32, ctypes.c_int, vp, ctypes.c_size_t, vp, vp]
     lib.diffattn_fwd_workspace_size.argtypes = [ctypes.c_int, i32, i32, i32, ctypes.c_int]
     lib.diffattn_fwd_workspace_size.restype = ctypes.c_size_t
     lib.diffattn_fwd.restype = ctypes.c_int
     lib.diffattn_fwd_kv.argtypes = [
         ctypes.c_int, vp, vp, vp, f32p, f32p, f32p, f32p, i32, ctypes.c_float,
         f32p, ctypes.c_float, ctypes.c_int, i32p, i32p, i32, i32, i32, i32,
-        i32, i32, i32, i32, vp, ctypes.c_size_t, vp, vp]
+        i32, i32, i32, i32, vp, vp, i32, ctypes.c_int, vp, ctypes.c_size_t,
+        vp, vp]
     lib.diffattn_fwd_kv.restype = ctypes.c_int
     lib.diffattn_fwd_kv_noalloc.argtypes = [
         ctypes.c_int, vp, vp, vp, f32p, f32p, f32p, f32p, i32, ctypes.c_float,
         f32p, ctypes.c_float, ctypes.c_int, i32p, i32p, i32, i32, i32, i32,
-        i32, i32, i32, i32, vp, vp]
+        i32, i32, i32, i32, vp, vp, i32, ctypes.c_int, vp, vp]
     lib.diffattn_fwd_kv_noalloc.restype = ctypes.c_int
+    lib.diffattn_kv_append.argtypes = [
+        ctypes.c_int, vp, vp, i32p, i32p, i32, i32, i32, i32, i32, i32,
+        vp, vp, i32, ctypes.c_int, vp, vp, vp]
+    lib.diffattn_kv_append.restype = ctypes.c_int
     lib.diffattn_fwd_kv_workspace_size.argtypes = [i32] * 6
     lib.diffattn_fwd_kv_workspace_size.restype = ctypes.c_size_t
     lib.diffattn_supported_kv.argtypes = [ctypes.c_int, ctypes.c_int]
@@ -164,7 +170,8 @@ def fwd_kv_ptr(dtype: int, q: int, k: int, v: int, lq1: int, lk1: int,
                lambda_init_value: float, subln_weight: int, eps: float,
                causal: int, cu_seqlens_q: int, cu_seqlens_k: int, nseq: int,
                max_seqlen_q: int, max_seqlen_k: int, Tq: int, Tk: int, H: int,
-               Hkv: int, d: int, workspace: int, workspace_bytes: int,
+               Hkv: int, d: int, rope_cos: int, rope_sin: int, rope_len: int,
+               rope_dtype: int, workspace: int, workspace_bytes: int,
                out: int, stream: int) -> int:
     """The raw cache entry point on integer device addresses; returns the
     status."""
@@ -173,7 +180,8 @@ def fwd_kv_ptr(dtype: int, q: int, k: int, v: int, lq1: int, lk1: int,
         lq2 or None, lk2 or None, int(lambda_stride), float(lambda_init_value),
         subln_weight or None, float(eps), int(causal), cu_seqlens_q or None,
         cu_seqlens_k or None, int(nseq), int(max_seqlen_q), int(max_seqlen_k),
-        int(Tq), int(Tk), int(H), int(Hkv), int(d), workspace or None,
+        int(Tq), int(Tk), int(H), int(Hkv), int(d), rope_cos or None,
+        rope_sin or None, int(rope_len), int(rope_dtype), workspace or None,
         int(workspace_bytes), out or None, stream or None)
 
 
@@ -183,7 +191,8 @@ def fwd_kv_noalloc_ptr(dtype: int, q: int, k: int, v: int, lq1: int,
                        eps: float, causal: int, cu_seqlens_q: int,
                        cu_seqlens_k: int, nseq: int, max_seqlen_q: int,
                        max_seqlen_k: int, Tq: int, Tk: int, H: int, Hkv: int,
-                       d: int, out: int, stream: int) -> int:
+                       d: int, rope_cos: int, rope_sin: int, rope_len: int,
+                       rope_dtype: int, out: int, stream: int) -> int:
     """The raw no-allocation cache entry point (static device scratch) on
     integer device addresses; returns the status."""
     return library().diffattn_fwd_kv_noalloc(
@@ -191,16 +200,31 @@ def fwd_kv_noalloc_ptr(dtype: int, q: int, k: int, v: int, lq1: int,
         lq2 or None, lk2 or None, int(lambda_stride), float(lambda_init_value),
         subln_weight or None, float(eps), int(causal), cu_seqlens_q or None,
         cu_seqlens_k or None, int(nseq), int(max_seqlen_q), int(max_seqlen_k),
-        int(Tq), int(Tk), int(H), int(Hkv), int(d), out or None,
+        int(Tq), int(Tk), int(H), int(Hkv), int(d), rope_cos or None,
+        rope_sin or None, int(rope_len), int(rope_dtype), out or None,
         stream or None)
+
+
+def kv_append_ptr(dtype: int, k_new: int, v_new: int, cu_seqlens_q: int,
+                  cu_seqlens_k: int, nseq: int, max_seqlen_k: int, Tq: int,
+                  Tk: int, Hkv: int, d: int, rope_cos: int, rope_sin: int,
+                  rope_len: int, rope_dtype: int, k_cache: int, v_cache: int,
+                  stream: int) -> int:
+    """The raw cache-update entry point on integer device addresses;
+    returns the status."""
+    return library().diffattn_kv_append(
+        int(dtype), k_new or None, v_new or None, cu_seqlens_q or None,
+        cu_seqlens_k or None, int(nseq), int(max_seqlen_k), int(Tq), int(Tk),
+        int(Hkv), int(d), rope_cos or None, rope_sin or None, int(rope_len),
+        int(rope_dtype), k_cache or None, v_cache or None, stream or None)
 
 
 def fwd_ptr(dtype: int, q: int, k: int, v: int, lq1: int, lk1: int, lq2: int,
             lk2: int, lambda_stride: int, lambda_init_value: float,
             subln_weight: int, eps: float, causal: int, cu_seqlens: int,
             nseq: int, max_seqlen: int, T: int, H: int, Hkv: int, d: int,
-            rope_cos: int, rope_sin: int, rope_len: int, workspace: int,
-            workspace_bytes: int, out: int, stream: int) -> int:
+            rope_cos: int, rope_sin: int, rope_len: int, rope_dtype: int,
+            workspace: int, workspace_bytes: int, out: int, stream: int) -> int:
     """The raw C entry point on integer device addresses; returns the
     status."""
     return library().diffattn_fwd(
@@ -208,8 +232,8 @@ def fwd_ptr(dtype: int, q: int, k: int, v: int, lq1: int, lk1: int, lq2: int,
         lq2 or None, lk2 or None, int(lambda_stride), float(lambda_init_value),
         subln_weight or None, float(eps), int(causal), cu_seqlens or None,
         int(nseq), int(max_seqlen), int(T), int(H), int(Hkv), int(d),
-        rope_cos or None, rope_sin or None, int(rope_len), workspace or None,
-        int(workspace_bytes), out or None, stream or None)
+        rope_cos or None, rope_sin or None, int(rope_len), int(rope_dtype),
+        workspace or None, int(workspace_bytes), out or None, stream or None)
 
 
 def fwd_workspace_size(dtype: torch.dtype, T: int, Hkv: int, d: int,
@@ -295,14 +319,9 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         nseq = 1 if nseq is None else int(nseq)
         if max_seqlen is None:
             max_seqlen = T // nseq if nseq > 0 else 0
-    rc_ptr = rs_ptr = rope_len = ws_ptr = ws_bytes = 0
+    rc_ptr = rs_ptr = rope_len = rope_dtype = ws_ptr = ws_bytes = 0
     if rope is not None:
-        rc, rs = rope
-        if rc.dim() != 2 or rc.shape[1] != d // 2 or tuple(rs.shape) != tuple(rc.shape):
-            raise ValueError("rope tables must be two [len, d/2] tensors")
-        rc_ptr = _dev(rc, "rope cos", dev, torch.float32)
-        rs_ptr = _dev(rs, "rope sin", dev, torch.float32)
-        rope_len = rc.shape[0]
+        rc_ptr, rs_ptr, rope_len, rope_dtype = _rope_args(rope, d, dev)
         if workspace is None:
             workspace = torch.empty(max(fwd_workspace_size(q.dtype, T, Hkv, d, True), 16),
                                     dtype=torch.uint8, device=dev)
@@ -320,11 +339,23 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                      args[4], args[5], args[6], lambda_stride, lambda_init,
                      w_ptr, eps,
                      int(bool(causal)), cu_ptr, nseq, max_seqlen, T, H, Hkv, d,
-                     rc_ptr, rs_ptr, rope_len, ws_ptr, ws_bytes, out_ptr,
-                     stream.cuda_stream)
+                     rc_ptr, rs_ptr, rope_len, rope_dtype, ws_ptr, ws_bytes,
+                     out_ptr, stream.cuda_stream)
     if st != OK:
         raise DiffAttnError(st, "diffattn_fwd")
     return out
+
+
+def _rope_args(rope, d, dev):
+    """(cos, sin) tables [len, d/2], both fp32 or both bf16, on the device:
+    their pointers, length and DIFFATTN dtype."""
+    rc, rs = rope
+    if rc.dim() != 2 or rc.shape[1] != d // 2 or tuple(rs.shape) != tuple(rc.shape):
+        raise ValueError("rope tables must be two [len, d/2] tensors")
+    if rc.dtype not in _DTYPES or rs.dtype != rc.dtype:
+        raise ValueError("rope tables must both be float32 or both bfloat16")
+    return (_dev(rc, "rope cos", dev, rc.dtype), _dev(rs, "rope sin", dev, rc.dtype),
+            rc.shape[0], _DTYPES[rc.dtype])
 
 
 def _lambda_args(lvs, H, d, dev):
@@ -349,7 +380,8 @@ def fwd_kv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
            max_seqlen_k: Optional[int] = None, nseq: Optional[int] = None,
            workspace: Optional[torch.Tensor] = None,
            out: Optional[torch.Tensor] = None,
-           stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+           stream: Optional[torch.cuda.Stream] = None,
+           rope: Optional[tuple] = None) -> torch.Tensor:
     """New queries against a key/value cache on the GPU (bottom-right causal).
 
     q [Tq, H, 2, d]; k [Tk, Hkv, 2, d], v [Tk, Hkv, 2d] (bf16); lambda
@@ -358,12 +390,15 @@ def fwd_kv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     sequences).  When the bounds are not given they are read back from the
     device (a synchronising copy).  ``workspace`` is a device uint8 tensor of
     at least ``kv_workspace_size(...)`` bytes; one is allocated through
-    torch when it is None.  Returns ``out`` [Tq, H, 2d].
+    torch when it is None.  ``rope`` = (cos, sin) device tables [len, d/2]
+    (fp32 or bf16) rotates each new query at its absolute position
+    nk - nq + i; the cached keys are taken as already rotated (``kv_append``
+    writes them so).  Returns ``out`` [Tq, H, 2d].
     """
     return _kv_call(q, k, v, (lambda_q1, lambda_k1, lambda_q2, lambda_k2),
                     lambda_init, subln_weight, eps, causal, cu_seqlens_q,
                     cu_seqlens_k, max_seqlen_q, max_seqlen_k, nseq, out,
-                    stream, workspace, noalloc=False)
+                    stream, workspace, noalloc=False, rope=rope)
 
 
 def fwd_kv_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
@@ -378,7 +413,8 @@ def fwd_kv_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                    max_seqlen_k: Optional[int] = None,
                    nseq: Optional[int] = None,
                    out: Optional[torch.Tensor] = None,
-                   stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+                   stream: Optional[torch.cuda.Stream] = None,
+                   rope: Optional[tuple] = None) -> torch.Tensor:
     """``fwd_kv`` through ``diffattn_fwd_kv_noalloc``: the library's static
     device scratch (``KV_SCRATCH_BYTES`` per GPU) replaces the workspace, so
     the call allocates nothing when ``out`` and both bounds are given.
@@ -386,12 +422,12 @@ def fwd_kv_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     return _kv_call(q, k, v, (lambda_q1, lambda_k1, lambda_q2, lambda_k2),
                     lambda_init, subln_weight, eps, causal, cu_seqlens_q,
                     cu_seqlens_k, max_seqlen_q, max_seqlen_k, nseq, out,
-                    stream, None, noalloc=True)
+                    stream, None, noalloc=True, rope=rope)
 
 
 def _kv_call(q, k, v, lvs, lambda_init, subln_weight, eps, causal,
              cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, nseq,
-             out, stream, workspace, noalloc):
+             out, stream, workspace, noalloc, rope=None):
     if q.dim() != 4 or q.shape[2] != 2:
         raise ValueError("q must be [Tq, H, 2, d]")
     Tq, H, _, d = q.shape
@@ -447,9 +483,10 @@ def _kv_call(q, k, v, lvs, lambda_init, subln_weight, eps, causal,
     out_ptr = _dev(out, "out", dev, q.dtype)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
+    rargs = (0, 0, 0, 0) if rope is None else _rope_args(rope, d, dev)
     common = (_DTYPES[q.dtype], qp, kp, vp_, *lptrs, lambda_stride,
               lambda_init, w_ptr, eps, int(bool(causal)), cq_ptr, ck_ptr,
-              nseq, max_seqlen_q, max_seqlen_k, Tq, Tk, H, Hkv, d)
+              nseq, max_seqlen_q, max_seqlen_k, Tq, Tk, H, Hkv, d, *rargs)
     with torch.cuda.device(dev):
         if noalloc:
             st = fwd_kv_noalloc_ptr(*common, out_ptr, stream.cuda_stream)
@@ -460,6 +497,59 @@ def _kv_call(q, k, v, lvs, lambda_init, subln_weight, eps, causal,
         raise DiffAttnError(st, "diffattn_fwd_kv_noalloc" if noalloc
                             else "diffattn_fwd_kv")
     return out
+
+
+def kv_append(k_new: torch.Tensor, v_new: torch.Tensor,
+              k_cache: torch.Tensor, v_cache: torch.Tensor,
+              cu_seqlens_q: Optional[torch.Tensor] = None,
+              cu_seqlens_k: Optional[torch.Tensor] = None,
+              max_seqlen_k: Optional[int] = None, nseq: Optional[int] = None,
+              rope: Optional[tuple] = None,
+              stream: Optional[torch.cuda.Stream] = None) -> None:
+    """The cache update of a decode step, in place: the nq new tokens of
+    each sequence (k_new [Tq, Hkv, 2, d], v_new [Tq, Hkv, 2d]) go to the
+    last nq rows of its region of k_cache [Tk, Hkv, 2, d] / v_cache
+    [Tk, Hkv, 2d]; with ``rope`` = (cos, sin) the keys are rotated at their
+    positions nk - nq + i.  Boundaries as for ``fwd_kv``."""
+    if k_new.dim() != 4 or k_new.shape[2] != 2:
+        raise ValueError("k_new must be [Tq, Hkv, 2, d]")
+    Tq, Hkv, _, d = k_new.shape
+    if tuple(v_new.shape) != (Tq, Hkv, 2 * d):
+        raise ValueError("v_new must be [Tq, Hkv, 2d]")
+    if k_cache.dim() != 4 or tuple(k_cache.shape[1:]) != (Hkv, 2, d):
+        raise ValueError("k_cache must be [Tk, Hkv, 2, d]")
+    Tk = k_cache.shape[0]
+    if tuple(v_cache.shape) != (Tk, Hkv, 2 * d):
+        raise ValueError("v_cache must be [Tk, Hkv, 2d]")
+    if k_new.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {k_new.dtype}")
+    dev = k_new.device
+    dt = k_new.dtype
+    ptrs = [_dev(k_new, "k_new", dev, dt), _dev(v_new, "v_new", dev, dt)]
+    if (cu_seqlens_q is None) != (cu_seqlens_k is None):
+        raise ValueError("give both cu_seqlens_q and cu_seqlens_k, or neither")
+    cq_ptr = ck_ptr = 0
+    if cu_seqlens_q is not None:
+        if cu_seqlens_q.numel() != cu_seqlens_k.numel():
+            raise ValueError("cu_seqlens_q and cu_seqlens_k differ in length")
+        cq_ptr = _dev(cu_seqlens_q, "cu_seqlens_q", dev, torch.int32)
+        ck_ptr = _dev(cu_seqlens_k, "cu_seqlens_k", dev, torch.int32)
+        nseq = cu_seqlens_q.numel() - 1
+        if max_seqlen_k is None:
+            c = cu_seqlens_k.cpu()
+            max_seqlen_k = int((c[1:] - c[:-1]).max()) if nseq > 0 else 0
+    else:
+        nseq = 1 if nseq is None else int(nseq)
+        max_seqlen_k = Tk // nseq if nseq > 0 else 0
+    rargs = (0, 0, 0, 0) if rope is None else _rope_args(rope, d, dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        st = kv_append_ptr(_DTYPES[dt], *ptrs, cq_ptr, ck_ptr, nseq, max_seqlen_k,
+                           Tq, Tk, Hkv, d, *rargs, _dev(k_cache, "k_cache", dev, dt),
+                           _dev(v_cache, "v_cache", dev, dt), stream.cuda_stream)
+    if st != OK:
+        raise DiffAttnError(st, "diffattn_kv_append")
 
 
 def supported_bwd(dtype: torch.dtype, d: int) -> bool:

@@ -74,6 +74,7 @@
 #include <stdint.h>
 
 #include "diffattn.h"
+#include "rope.h"
 
 namespace {
 
@@ -232,59 +233,7 @@ template <int D> struct VOperand<float, D> {
 // once per call into the caller's workspace (every query tile of a group
 // reads each K row, so rotating it while staging would repeat the work
 // per tile); Q fragments are rotated when each wave loads them.
-template <typename E> struct Rope;
-
-template <> struct Rope<bf16> {
-    struct Coef { float4 c, s; };
-    __device__ static inline Coef coef(const float *rc, const float *rs, int pos, int j, int D)
-    {
-        const int64_t o = (int64_t)pos * (D / 2) + j;
-        return Coef{*(const float4 *)(rc + o), *(const float4 *)(rs + o)};
-    }
-    __device__ static inline u32x4 rotate(u32x4 x, const Coef &k)
-    {
-        const bf16x8 v = __builtin_bit_cast(bf16x8, x);
-        const float cc[4] = {k.c.x, k.c.y, k.c.z, k.c.w};
-        const float ss[4] = {k.s.x, k.s.y, k.s.z, k.s.w};
-        bf16x8 r;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float x0 = (float)v[2 * i], x1 = (float)v[2 * i + 1];
-            r[2 * i] = (bf16)(x0 * cc[i] - x1 * ss[i]);
-            r[2 * i + 1] = (bf16)(x0 * ss[i] + x1 * cc[i]);
-        }
-        return __builtin_bit_cast(u32x4, r);
-    }
-};
-
-template <> struct Rope<float> {
-    struct Coef { float2 c, s; };
-    __device__ static inline Coef coef(const float *rc, const float *rs, int pos, int j, int D)
-    {
-        const int64_t o = (int64_t)pos * (D / 2) + j;
-        return Coef{*(const float2 *)(rc + o), *(const float2 *)(rs + o)};
-    }
-    __device__ static inline u32x4 rotate(u32x4 x, const Coef &k)
-    {
-        const float4 v = __builtin_bit_cast(float4, x);
-        float4 r;
-        r.x = v.x * k.c.x - v.y * k.s.x;
-        r.y = v.x * k.s.x + v.y * k.c.x;
-        r.z = v.z * k.c.y - v.w * k.s.y;
-        r.w = v.z * k.s.y + v.w * k.c.y;
-        return __builtin_bit_cast(u32x4, r);
-    }
-    // B-operand element of dim d0 (= 2j + half) of a query row, rotated: the
-    // lane reads both elements of its pair
-    __device__ static inline float q_frag(const float *row, int d0, int half, const float *rc,
-                                          const float *rs, int pos, int D)
-    {
-        const float2 x = *(const float2 *)(row + (d0 & ~1));
-        const int64_t o = (int64_t)pos * (D / 2) + d0 / 2;
-        const float c = rc[o], sn = rs[o];
-        return half ? x.x * sn + x.y * c : x.x * c - x.y * sn;
-    }
-};
+using diffattn_rope::Rope;
 
 // Rotates every K row once, into a copy.  Thread = one 16-byte chunk
 // position (whole pairs) of one token, taken through all 2 Hkv half-heads
@@ -293,10 +242,10 @@ template <> struct Rope<float> {
 // in flight.  The token's position is its offset in its sequence, found by
 // binary search over cu_seqlens.  The prefill kernel then stages the
 // rotated copy.
-template <typename E, int D>
+template <typename E, int D, int RT>
 __global__ __launch_bounds__(256) void rope_rotate_k(const char *k, char *kr, const int32_t *cu,
                                                      int32_t nseq, int32_t uniform, int32_t T,
-                                                     int32_t Hkv, const float *rc, const float *rs)
+                                                     int32_t Hkv, const void *rc, const void *rs)
 {
     constexpr int HB = D * (int)sizeof(E);   // bytes per d-wide half-head
     constexpr int CPH = HB / 16;             // chunks per half-head
@@ -321,7 +270,7 @@ __global__ __launch_bounds__(256) void rope_rotate_k(const char *k, char *kr, co
     const int c = (int)(idx % CPH);
     // pair index of the chunk's first element within its half-head
     const int j = c * (16 / (int)sizeof(E)) / 2;
-    const auto coef = Rope<E>::coef(rc, rs, t - s0, j, D);
+    const auto coef = Rope<E, RT>::coef(rc, rs, t - s0, j, D);
     const int nh = 2 * Hkv;
     const int64_t base = (int64_t)t * nh * HB + c * 16;
     for (int h0 = 0; h0 < nh; h0 += 8) {
@@ -333,7 +282,7 @@ __global__ __launch_bounds__(256) void rope_rotate_k(const char *k, char *kr, co
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             if (h0 + i < nh)
-                *(u32x4 *)(kr + base + (int64_t)(h0 + i) * HB) = Rope<E>::rotate(x[i], coef);
+                *(u32x4 *)(kr + base + (int64_t)(h0 + i) * HB) = Rope<E, RT>::rotate(x[i], coef);
     }
 }
 
@@ -346,7 +295,8 @@ struct Params {
     int64_t lstride;   // elements between heads' lambda vectors (0: shared)
     const float *w;
     const int32_t *cu;
-    const float *rcos, *rsin;   // rotary tables [len][d/2], or NULL
+    const void *rcos, *rsin;    // rotary tables [len][d/2] (fp32 or bf16), or NULL
+    int32_t rope_dtype;         // element type of the tables
     const void *k_orig;         // unrotated K when rcos is set (k is then its rotated copy)
     int32_t max_seqlen;
     float *lse;                 // training forward: [T][H][2] log2-sum-exp, or NULL
@@ -365,13 +315,14 @@ struct Params {
 // budget per lane is the 256 that two waves per SIMD leave.  SUB: 32-query
 // sub-blocks per wave -- 2 (each K/V operand read feeds two MFMAs), or 1 for
 // grids too small to fill the chip, which doubles the workgroups.
-template <typename E, int D, bool ROPE, int SUB>
+template <typename E, int D, int RT, int SUB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void diffattn_fwd_kernel(Params p)
 {
     constexpr int kSub = SUB;
     constexpr int kQB = 32 * kSub;   // query rows per slot
     static_assert(SUB == 1 || SUB == 2, "one or two sub-blocks per wave");
+    constexpr bool ROPE = RT != diffattn_rope::kOff;   // rotary tables given
     typedef Geo<E, D> GEO;
     typedef Mfma<E> M;
     typedef typename M::Frag Frag;
@@ -452,7 +403,7 @@ void diffattn_fwd_kernel(Params p)
                                   (((int64_t)tq * p.H + head) * 2 + map) * (D * 2) + qc * 16;
                 qv[i] = *(const u32x4 *)src;
                 if constexpr (ROPE)   // pairs 4 qc .. 4 qc + 3 of the half-head
-                    qv[i] = Rope<E>::rotate(qv[i], Rope<E>::coef(p.rcos, p.rsin, tq - s0,
+                    qv[i] = Rope<E, RT>::rotate(qv[i], Rope<E, RT>::coef(p.rcos, p.rsin, tq - s0,
                                                                  4 * qc, D));
             } else {
                 qv[i] = u32x4{0u, 0u, 0u, 0u};
@@ -478,8 +429,8 @@ void diffattn_fwd_kernel(Params p)
                 if (tq < s1) {
                     const E *row = qg + (((int64_t)tq * p.H + head) * 2 + map) * D;
                     if constexpr (ROPE)
-                        qf[u][ks] = Rope<E>::q_frag(row, ks * KSTEP + h * VEC, h,
-                                                    p.rcos, p.rsin, tq - s0, D);
+                        qf[u][ks] = Rope<E, RT>::element(row, ks * KSTEP + h * VEC, h,
+                                                         p.rcos, p.rsin, tq - s0, D);
                     else
                         qf[u][ks] = *(const Frag *)(row + ks * KSTEP + h * VEC);
                 } else {
@@ -938,31 +889,33 @@ void diffattn_fwd_kernel(Params p)
         finish(o[kSub - 1], own[kSub - 1], 1);
 }
 
-template <typename E, int D>
-int launch(const Params &p, int nblocks, hipStream_t stream)
+template <typename E, int D, int RT>
+void launch_rt(const Params &p, int nblocks, hipStream_t stream)
 {
-    if (p.rcos) {
+    if constexpr (RT != diffattn_rope::kOff) {
         // K rotated once into the workspace, which the kernel then reads as K
         const int64_t threads = (int64_t)p.T * (D * (int)sizeof(E) / 16);
-        hipLaunchKernelGGL((rope_rotate_k<E, D>), dim3((unsigned)((threads + 255) / 256)),
+        hipLaunchKernelGGL((rope_rotate_k<E, D, RT>), dim3((unsigned)((threads + 255) / 256)),
                            dim3(256), 0, stream, (const char *)p.k_orig, (char *)p.k, p.cu,
                            p.nseq, p.seqlen_uniform, p.T, p.Hkv, p.rcos, p.rsin);
     }
-    if (p.rcos) {
-        if (p.sub == 2)
-            hipLaunchKernelGGL((diffattn_fwd_kernel<E, D, true, 2>), dim3(nblocks), dim3(kThreads),
-                               0, stream, p);
-        else
-            hipLaunchKernelGGL((diffattn_fwd_kernel<E, D, true, 1>), dim3(nblocks), dim3(kThreads),
-                               0, stream, p);
-    } else {
-        if (p.sub == 2)
-            hipLaunchKernelGGL((diffattn_fwd_kernel<E, D, false, 2>), dim3(nblocks),
-                               dim3(kThreads), 0, stream, p);
-        else
-            hipLaunchKernelGGL((diffattn_fwd_kernel<E, D, false, 1>), dim3(nblocks),
-                               dim3(kThreads), 0, stream, p);
-    }
+    if (p.sub == 2)
+        hipLaunchKernelGGL((diffattn_fwd_kernel<E, D, RT, 2>), dim3(nblocks), dim3(kThreads), 0,
+                           stream, p);
+    else
+        hipLaunchKernelGGL((diffattn_fwd_kernel<E, D, RT, 1>), dim3(nblocks), dim3(kThreads), 0,
+                           stream, p);
+}
+
+template <typename E, int D>
+int launch(const Params &p, int nblocks, hipStream_t stream)
+{
+    if (!p.rcos)
+        launch_rt<E, D, diffattn_rope::kOff>(p, nblocks, stream);
+    else if (p.rope_dtype == DIFFATTN_BF16)
+        launch_rt<E, D, diffattn_rope::kBF16>(p, nblocks, stream);
+    else
+        launch_rt<E, D, diffattn_rope::kF32>(p, nblocks, stream);
     return hipGetLastError() == hipSuccess ? DIFFATTN_OK : DIFFATTN_EHIP;
 }
 
@@ -1031,9 +984,9 @@ int fwd_impl(int dtype, const void *q, const void *k, const void *v,
              const float *subln_weight, float eps,
              int causal, const int32_t *cu_seqlens, int32_t nseq,
              int32_t max_seqlen, int32_t T, int32_t H, int32_t Hkv,
-             int32_t d, const float *rope_cos, const float *rope_sin,
-             int32_t rope_len, void *workspace, size_t workspace_bytes, float *lse,
-             float *o12, void *out, void *stream)
+             int32_t d, const void *rope_cos, const void *rope_sin,
+             int32_t rope_len, int rope_dtype, void *workspace, size_t workspace_bytes,
+             float *lse, float *o12, void *out, void *stream)
 {
     if (dtype != DIFFATTN_BF16 && dtype != DIFFATTN_F32)
         return DIFFATTN_EINVAL;
@@ -1046,6 +999,8 @@ int fwd_impl(int dtype, const void *q, const void *k, const void *v,
     if (lambda_stride != 0 && lambda_stride < d)
         return DIFFATTN_EINVAL;
     if ((rope_cos == nullptr) != (rope_sin == nullptr))
+        return DIFFATTN_EINVAL;
+    if (rope_cos && rope_dtype != DIFFATTN_F32 && rope_dtype != DIFFATTN_BF16)
         return DIFFATTN_EINVAL;
     const launch_fn fn = find_launcher(dtype, d);
     if (!fn)
@@ -1072,8 +1027,8 @@ int fwd_impl(int dtype, const void *q, const void *k, const void *v,
     } else if (max_seqlen < 1 || max_seqlen > T) {
         return DIFFATTN_EINVAL;
     }
-    // rotary tables cover every position and are read in 16-byte vectors;
-    // the workspace holds the rotated copy of K
+    // rotary tables cover every position and are read in aligned vectors
+    // of 2 or 4 entries; the workspace holds the rotated copy of K
     if (rope_cos && (rope_len < max_seqlen ||
                      ((uintptr_t)rope_cos | (uintptr_t)rope_sin) % 16 != 0))
         return DIFFATTN_EINVAL;
@@ -1113,6 +1068,7 @@ int fwd_impl(int dtype, const void *q, const void *k, const void *v,
     p.cu = cu_seqlens;
     p.rcos = rope_cos;
     p.rsin = rope_sin;
+    p.rope_dtype = rope_dtype;
     p.lse = lse;
     p.o12 = o12;
     p.lambda_init = lambda_init;
@@ -1146,13 +1102,13 @@ int diffattn_fwd(int dtype, const void *q, const void *k, const void *v,
                  const float *subln_weight, float eps,
                  int causal, const int32_t *cu_seqlens, int32_t nseq,
                  int32_t max_seqlen, int32_t T, int32_t H, int32_t Hkv,
-                 int32_t d, const float *rope_cos, const float *rope_sin,
-                 int32_t rope_len, void *workspace, size_t workspace_bytes,
+                 int32_t d, const void *rope_cos, const void *rope_sin,
+                 int32_t rope_len, int rope_dtype, void *workspace, size_t workspace_bytes,
                  void *out, void *stream)
 {
     return fwd_impl(dtype, q, k, v, lambda_q1, lambda_k1, lambda_q2, lambda_k2,
                     lambda_stride, lambda_init, subln_weight, eps, causal, cu_seqlens,
-                    nseq, max_seqlen, T, H, Hkv, d, rope_cos, rope_sin, rope_len,
+                    nseq, max_seqlen, T, H, Hkv, d, rope_cos, rope_sin, rope_len, rope_dtype,
                     workspace, workspace_bytes, nullptr, nullptr, out, stream);
 }
 
@@ -1177,7 +1133,7 @@ int diffattn_fwd_train(int dtype, const void *q, const void *k, const void *v,
         return DIFFATTN_EINVAL;
     return fwd_impl(dtype, q, k, v, lambda_q1, lambda_k1, lambda_q2, lambda_k2,
                     lambda_stride, lambda_init, subln_weight, eps, causal, cu_seqlens,
-                    nseq, max_seqlen, T, H, Hkv, d, nullptr, nullptr, 0, nullptr, 0, lse,
+                    nseq, max_seqlen, T, H, Hkv, d, nullptr, nullptr, 0, 0, nullptr, 0, lse,
                     o12, out, stream);
 }
 

@@ -60,6 +60,7 @@
 #include <stdint.h>
 
 #include "diffattn.h"
+#include "rope.h"
 
 namespace {
 
@@ -88,6 +89,8 @@ struct KvParams {
     const int32_t *cuk;   // NULL: uniform lengths klen_uniform
     float *ws_o;          // [split slot][Hkv][rmax][2][2d]
     float *ws_ml;         // [split slot][Hkv][rmax][4]: m, l of map 1, m, l of map 2
+    const void *rcos, *rsin;   // rotary tables of the new queries, or NULL
+    int32_t rope_len;
     float lambda_init;
     float eps;
     int32_t H, Hkv, G, nseq, causal;
@@ -177,7 +180,8 @@ __device__ inline f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int D>
+// RT: rotary tables of the new queries (diffattn_rope::kOff, kF32, kBF16).
+template <int D, int RT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void diffattn_kv_partial(KvParams p)
 {
@@ -241,19 +245,31 @@ void diffattn_kv_partial(KvParams p)
     const int row_lim = p.causal ? min(nk - 1, nk - nq + qi) : nk - 1;
 
     // ---- Q fragments (B operand of S^T = K Q^T) ----------------------------
+    // With rotary tables each fragment (pairs 16 ks + 4 qq .. + 3 of the
+    // half-head) is rotated at the query's absolute position nk - nq + i
+    // (clamped into the tables, which only matters when the preconditions
+    // nq <= nk and rope_len >= nk are broken)
     bf16x8 qf[2][NKS];
     {
         const bf16 *qg = (const bf16 *)p.q;
         const int head = g * p.G + r % p.G;
         const int64_t tok = (int64_t)qa + qi;
+        const int pos = min(max(nk - nq + qi, 0), p.rope_len - 1);
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
-                if (row_ok)
+                if (row_ok) {
                     qf[m][ks] = *(const bf16x8 *)(qg + ((tok * p.H + head) * 2 + m) * D + 32 * ks + 8 * qq);
-                else
+                    if constexpr (RT != diffattn_rope::kOff) {
+                        typedef diffattn_rope::Rope<bf16, RT> R;
+                        qf[m][ks] = __builtin_bit_cast(
+                            bf16x8, R::rotate(__builtin_bit_cast(u32x4, qf[m][ks]),
+                                              R::coef(p.rcos, p.rsin, pos, 16 * ks + 4 * qq, D)));
+                    }
+                } else {
                     qf[m][ks] = bf16x8{};
+                }
             }
     }
 
@@ -680,6 +696,20 @@ extern "C" size_t diffattn_fwd_kv_workspace_size(int32_t nseq, int32_t max_seqle
 
 namespace {
 
+template <int D>
+void launch_partial(int rt, unsigned blocks, hipStream_t st, const KvParams &p)
+{
+    if (rt == diffattn_rope::kBF16)
+        hipLaunchKernelGGL((diffattn_kv_partial<D, diffattn_rope::kBF16>), dim3(blocks),
+                           dim3(kThreads), 0, st, p);
+    else if (rt == diffattn_rope::kF32)
+        hipLaunchKernelGGL((diffattn_kv_partial<D, diffattn_rope::kF32>), dim3(blocks),
+                           dim3(kThreads), 0, st, p);
+    else
+        hipLaunchKernelGGL((diffattn_kv_partial<D, diffattn_rope::kOff>), dim3(blocks),
+                           dim3(kThreads), 0, st, p);
+}
+
 // Validates the arguments, makes the split plan and launches both kernels
 // with the workspace that `get_ws` returns for the plan's size (it returns
 // a status and sets the pointer, or refuses the size).
@@ -690,6 +720,7 @@ int kv_impl(int dtype, const void *q, const void *k, const void *v,
             const float *subln_weight, float eps, int causal, const int32_t *cu_seqlens_q,
             const int32_t *cu_seqlens_k, int32_t nseq, int32_t max_seqlen_q,
             int32_t max_seqlen_k, int32_t Tq, int32_t Tk, int32_t H, int32_t Hkv, int32_t d,
+            const void *rope_cos, const void *rope_sin, int32_t rope_len, int rope_dtype,
             GetWs get_ws, void *out, void *stream)
 {
     if (dtype != DIFFATTN_BF16 && dtype != DIFFATTN_F32)
@@ -703,6 +734,10 @@ int kv_impl(int dtype, const void *q, const void *k, const void *v,
     if (lambda_stride != 0 && lambda_stride < d)
         return DIFFATTN_EINVAL;
     if ((cu_seqlens_q == nullptr) != (cu_seqlens_k == nullptr))
+        return DIFFATTN_EINVAL;
+    if ((rope_cos == nullptr) != (rope_sin == nullptr))
+        return DIFFATTN_EINVAL;
+    if (rope_cos && rope_dtype != DIFFATTN_F32 && rope_dtype != DIFFATTN_BF16)
         return DIFFATTN_EINVAL;
     if (!cu_seqlens_q) {
         if (Tq % nseq != 0 || Tk % nseq != 0)
@@ -726,6 +761,9 @@ int kv_impl(int dtype, const void *q, const void *k, const void *v,
         return DIFFATTN_EINVAL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
         (subln_weight && !aligned16(subln_weight)))
+        return DIFFATTN_EINVAL;
+    // the tables cover every position a new query can have (< nk)
+    if (rope_cos && (rope_len < max_seqlen_k || !aligned16(rope_cos) || !aligned16(rope_sin)))
         return DIFFATTN_EINVAL;
     const int G = H / Hkv;
     KvPlan pl;
@@ -751,6 +789,9 @@ int kv_impl(int dtype, const void *q, const void *k, const void *v,
     p.cuk = cu_seqlens_k;
     p.ws_o = (float *)workspace;
     p.ws_ml = (float *)((char *)workspace + pl.ws_o_bytes);
+    p.rcos = rope_cos;
+    p.rsin = rope_sin;
+    p.rope_len = rope_cos ? rope_len : 1;
     p.lambda_init = lambda_init;
     p.eps = eps;
     p.H = H;
@@ -776,14 +817,16 @@ int kv_impl(int dtype, const void *q, const void *k, const void *v,
     // splits of the longest cache
     const int64_t kmax = cu_seqlens_q ? max_seqlen_k : Tk / nseq;
     const bool wide = (kmax + pl.ck - 1) / pl.ck > 16;
+    const int rt = !rope_cos ? diffattn_rope::kOff
+                             : (rope_dtype == DIFFATTN_BF16 ? diffattn_rope::kBF16 : diffattn_rope::kF32);
     if (d == 64) {
-        hipLaunchKernelGGL(diffattn_kv_partial<64>, dim3((unsigned)blocks1), dim3(kThreads), 0, st, p);
+        launch_partial<64>(rt, (unsigned)blocks1, st, p);
         if (wide)
             hipLaunchKernelGGL((diffattn_kv_combine<64, 32>), dim3((unsigned)blocks2), dim3(kThreads), 0, st, p);
         else
             hipLaunchKernelGGL((diffattn_kv_combine<64, 16>), dim3((unsigned)blocks2), dim3(kThreads), 0, st, p);
     } else {
-        hipLaunchKernelGGL(diffattn_kv_partial<32>, dim3((unsigned)blocks1), dim3(kThreads), 0, st, p);
+        launch_partial<32>(rt, (unsigned)blocks1, st, p);
         if (wide)
             hipLaunchKernelGGL((diffattn_kv_combine<32, 32>), dim3((unsigned)blocks2), dim3(kThreads), 0, st, p);
         else
@@ -837,8 +880,9 @@ extern "C" int diffattn_fwd_kv(int dtype, const void *q, const void *k, const vo
                                const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
                                int32_t nseq, int32_t max_seqlen_q, int32_t max_seqlen_k,
                                int32_t Tq, int32_t Tk, int32_t H, int32_t Hkv, int32_t d,
-                               void *workspace, size_t workspace_bytes, void *out,
-                               void *stream)
+                               const void *rope_cos, const void *rope_sin, int32_t rope_len,
+                               int rope_dtype, void *workspace, size_t workspace_bytes,
+                               void *out, void *stream)
 {
     auto caller_ws = [&](size_t need, void *&ws) {
         if (!workspace || !aligned16(workspace) || workspace_bytes < need)
@@ -848,7 +892,8 @@ extern "C" int diffattn_fwd_kv(int dtype, const void *q, const void *k, const vo
     };
     return kv_impl(dtype, q, k, v, lambda_q1, lambda_k1, lambda_q2, lambda_k2, lambda_stride,
                    lambda_init, subln_weight, eps, causal, cu_seqlens_q, cu_seqlens_k, nseq,
-                   max_seqlen_q, max_seqlen_k, Tq, Tk, H, Hkv, d, caller_ws, out, stream);
+                   max_seqlen_q, max_seqlen_k, Tq, Tk, H, Hkv, d, rope_cos, rope_sin, rope_len,
+                   rope_dtype, caller_ws, out, stream);
 }
 
 extern "C" int diffattn_fwd_kv_noalloc(int dtype, const void *q, const void *k, const void *v,
@@ -860,7 +905,9 @@ extern "C" int diffattn_fwd_kv_noalloc(int dtype, const void *q, const void *k, 
                                        const int32_t *cu_seqlens_k, int32_t nseq,
                                        int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Tq,
                                        int32_t Tk, int32_t H, int32_t Hkv, int32_t d,
-                                       void *out, void *stream)
+                                       const void *rope_cos, const void *rope_sin,
+                                       int32_t rope_len, int rope_dtype, void *out,
+                                       void *stream)
 {
     // the size check comes first, so an oversized call touches no device
     auto static_ws = [&](size_t need, void *&ws) {
@@ -870,5 +917,167 @@ extern "C" int diffattn_fwd_kv_noalloc(int dtype, const void *q, const void *k, 
     };
     return kv_impl(dtype, q, k, v, lambda_q1, lambda_k1, lambda_q2, lambda_k2, lambda_stride,
                    lambda_init, subln_weight, eps, causal, cu_seqlens_q, cu_seqlens_k, nseq,
-                   max_seqlen_q, max_seqlen_k, Tq, Tk, H, Hkv, d, static_ws, out, stream);
+                   max_seqlen_q, max_seqlen_k, Tq, Tk, H, Hkv, d, rope_cos, rope_sin, rope_len,
+                   rope_dtype, static_ws, out, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Cache update of a decode step.  Thread = one 16-byte chunk of one new
+// token's key row (the first half of the grid) or value row (the second
+// half; both rows are Hkv x 2d elements).  The token's sequence comes from
+// a binary search of cu_seqlens_q; its cache row and position from the
+// sequence's bounds.
+namespace {
+
+struct AppendParams {
+    const char *k_new, *v_new;
+    char *k_cache, *v_cache;
+    const int32_t *cuq, *cuk;
+    const void *rcos, *rsin;
+    int32_t nseq, Tq, Hkv, rope_len;
+    int32_t qlen_uniform, klen_uniform;
+};
+
+template <typename E, int D, int RT>
+__global__ __launch_bounds__(256) void diffattn_kv_append_kernel(AppendParams p)
+{
+    constexpr int ES = (int)sizeof(E);
+    constexpr int CPH = D * ES / 16;   // 16-byte chunks per d-wide half-head
+    const int cpt = 2 * p.Hkv * CPH;   // chunks per token row
+    const int64_t per = (int64_t)p.Tq * cpt;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= 2 * per)
+        return;
+    const bool is_v = idx >= per;
+    const int64_t e = is_v ? idx - per : idx;
+    const int t = (int)(e / cpt), c = (int)(e % cpt);
+    int qa, nq, ka, nk;
+    if (p.cuq) {
+        int lo = 0, hi = p.nseq;   // last sequence with cu_q[s] <= t
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (p.cuq[mid] <= t)
+                lo = mid;
+            else
+                hi = mid;
+        }
+        qa = p.cuq[lo];
+        nq = p.cuq[lo + 1] - qa;
+        ka = p.cuk[lo];
+        nk = p.cuk[lo + 1] - ka;
+    } else {
+        const int s = t / p.qlen_uniform;
+        qa = s * p.qlen_uniform;
+        nq = p.qlen_uniform;
+        ka = s * p.klen_uniform;
+        nk = p.klen_uniform;
+    }
+    if (nq > nk)
+        return;   // broken precondition: the new rows would leave the sequence
+    const int i = t - qa;
+    const int64_t rowb = (int64_t)2 * p.Hkv * D * ES;   // bytes per token row
+    const int64_t row = (int64_t)ka + nk - nq + i;
+    u32x4 x = *(const u32x4 *)((is_v ? p.v_new : p.k_new) + (int64_t)t * rowb + c * 16);
+    if constexpr (RT != diffattn_rope::kOff) {
+        if (!is_v) {
+            typedef diffattn_rope::Rope<E, RT> R;
+            const int pos = min(nk - nq + i, p.rope_len - 1);
+            const int j = (c % CPH) * (16 / ES) / 2;   // first pair of the chunk
+            x = R::rotate(x, R::coef(p.rcos, p.rsin, pos, j, D));
+        }
+    }
+    *(u32x4 *)((is_v ? p.v_cache : p.k_cache) + row * rowb + c * 16) = x;
+}
+
+template <typename E, int D>
+void launch_append(int rt, unsigned blocks, hipStream_t st, const AppendParams &p)
+{
+    if (rt == diffattn_rope::kBF16)
+        hipLaunchKernelGGL((diffattn_kv_append_kernel<E, D, diffattn_rope::kBF16>), dim3(blocks),
+                           dim3(256), 0, st, p);
+    else if (rt == diffattn_rope::kF32)
+        hipLaunchKernelGGL((diffattn_kv_append_kernel<E, D, diffattn_rope::kF32>), dim3(blocks),
+                           dim3(256), 0, st, p);
+    else
+        hipLaunchKernelGGL((diffattn_kv_append_kernel<E, D, diffattn_rope::kOff>), dim3(blocks),
+                           dim3(256), 0, st, p);
+}
+
+} // namespace
+
+extern "C" int diffattn_kv_append(int dtype, const void *k_new, const void *v_new,
+                                  const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                                  int32_t nseq, int32_t max_seqlen_k, int32_t Tq, int32_t Tk,
+                                  int32_t Hkv, int32_t d, const void *rope_cos,
+                                  const void *rope_sin, int32_t rope_len, int rope_dtype,
+                                  void *k_cache, void *v_cache, void *stream)
+{
+    if (dtype != DIFFATTN_BF16 && dtype != DIFFATTN_F32)
+        return DIFFATTN_EINVAL;
+    if (Tq < 0 || Tk < 0 || Hkv < 1 || d < 1 || nseq < 1)
+        return DIFFATTN_EINVAL;
+    if ((cu_seqlens_q == nullptr) != (cu_seqlens_k == nullptr))
+        return DIFFATTN_EINVAL;
+    if ((rope_cos == nullptr) != (rope_sin == nullptr))
+        return DIFFATTN_EINVAL;
+    if (rope_cos && rope_dtype != DIFFATTN_F32 && rope_dtype != DIFFATTN_BF16)
+        return DIFFATTN_EINVAL;
+    if (!cu_seqlens_q) {
+        if (Tq % nseq != 0 || Tk % nseq != 0 || Tq / nseq > Tk / nseq)
+            return DIFFATTN_EINVAL;
+        max_seqlen_k = Tk / nseq;
+    } else if (max_seqlen_k < 0 || max_seqlen_k > Tk) {
+        return DIFFATTN_EINVAL;
+    }
+    if (d != 16 && d != 32 && d != 64)
+        return DIFFATTN_EUNSUPPORTED;
+    if (Tq == 0)
+        return DIFFATTN_OK;
+    if (!k_new || !v_new || !k_cache || !v_cache)
+        return DIFFATTN_EINVAL;
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+        return DIFFATTN_EINVAL;
+    if (rope_cos && (rope_len < max_seqlen_k || rope_len < 1 || !aligned16(rope_cos) ||
+                     !aligned16(rope_sin)))
+        return DIFFATTN_EINVAL;
+    const int es = dtype == DIFFATTN_F32 ? 4 : 2;
+    const int64_t threads = (int64_t)2 * Tq * (2 * Hkv * d * es / 16);
+    const int64_t blocks = (threads + 255) / 256;
+    if (blocks > 0x7fffffff)
+        return DIFFATTN_EINVAL;
+    AppendParams p;
+    p.k_new = (const char *)k_new;
+    p.v_new = (const char *)v_new;
+    p.k_cache = (char *)k_cache;
+    p.v_cache = (char *)v_cache;
+    p.cuq = cu_seqlens_q;
+    p.cuk = cu_seqlens_k;
+    p.rcos = rope_cos;
+    p.rsin = rope_sin;
+    p.nseq = nseq;
+    p.Tq = Tq;
+    p.Hkv = Hkv;
+    p.rope_len = rope_cos ? rope_len : 1;
+    p.qlen_uniform = cu_seqlens_q ? 0 : Tq / nseq;
+    p.klen_uniform = cu_seqlens_q ? 0 : Tk / nseq;
+    const int rt = !rope_cos ? diffattn_rope::kOff
+                             : (rope_dtype == DIFFATTN_BF16 ? diffattn_rope::kBF16 : diffattn_rope::kF32);
+    hipStream_t st = (hipStream_t)stream;
+    const unsigned nb = (unsigned)blocks;
+    if (dtype == DIFFATTN_BF16) {
+        if (d == 64)
+            launch_append<bf16, 64>(rt, nb, st, p);
+        else if (d == 32)
+            launch_append<bf16, 32>(rt, nb, st, p);
+        else
+            launch_append<bf16, 16>(rt, nb, st, p);
+    } else {
+        if (d == 64)
+            launch_append<float, 64>(rt, nb, st, p);
+        else if (d == 32)
+            launch_append<float, 32>(rt, nb, st, p);
+        else
+            launch_append<float, 16>(rt, nb, st, p);
+    }
+    return hipGetLastError() == hipSuccess ? DIFFATTN_OK : DIFFATTN_EHIP;
 }

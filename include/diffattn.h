@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define DIFFATTN_ABI_VERSION 8
+#define DIFFATTN_ABI_VERSION 9
 
 enum diffattn_status {
     DIFFATTN_OK = 0,
@@ -92,8 +92,8 @@ enum diffattn_dtype {
  *                diffattn_supported.
  *   rope_cos, rope_sin
  *                NULL (both) when q and k are already rotated; otherwise
- *                device fp32 tables [rope_len, d/2] (16-byte aligned), and
- *                the kernel applies the rotary prologue of the
+ *                device tables [rope_len, d/2] of rope_dtype (16-byte
+ *                aligned), and the kernel applies the rotary prologue of the
  *                FlashDiffAttention pull request's test (apply_rotary_emb
  *                with interleaved=True on every d-wide half-head of q and k):
  *                the pair (x[2j], x[2j+1]) of a row at position p of its
@@ -102,6 +102,10 @@ enum diffattn_dtype {
  *                s = rope_sin[p, j]; computed in fp32, rounded once to the
  *                storage type.  V is not rotated.
  *   rope_len     rows of the tables; >= max_seqlen when they are given.
+ *   rope_dtype   DIFFATTN_F32 or DIFFATTN_BF16: the tables' element type
+ *                (the pull request's test caches them in bf16; a bf16 entry
+ *                enters the fp32 arithmetic exactly).  Ignored without
+ *                tables.
  *   workspace, workspace_bytes
  *                with rotary tables: device scratch of at least
  *                diffattn_fwd_workspace_size(dtype, T, Hkv, d, 1) bytes,
@@ -122,9 +126,9 @@ int diffattn_fwd(int dtype, const void *q, const void *k, const void *v,
                  const float *subln_weight, float eps,
                  int causal, const int32_t *cu_seqlens, int32_t nseq,
                  int32_t max_seqlen, int32_t T, int32_t H, int32_t Hkv,
-                 int32_t d, const float *rope_cos, const float *rope_sin,
-                 int32_t rope_len, void *workspace, size_t workspace_bytes,
-                 void *out, void *stream);
+                 int32_t d, const void *rope_cos, const void *rope_sin,
+                 int32_t rope_len, int rope_dtype, void *workspace,
+                 size_t workspace_bytes, void *out, void *stream);
 
 /* Bytes of workspace diffattn_fwd needs: the rotated copy of k when rope
  * (rotary tables given) is nonzero, else 0.  Host function. */
@@ -166,6 +170,15 @@ size_t diffattn_fwd_workspace_size(int dtype, int32_t T, int32_t Hkv, int32_t d,
  *   Tq, Tk, H, Hkv, d
  *                sizes; H % Hkv == 0.  Compiled (dtype, d) pairs: see
  *                diffattn_supported_kv.
+ *   rope_cos, rope_sin, rope_len, rope_dtype
+ *                NULL (both) when q is already rotated.  Otherwise tables
+ *                as for diffattn_fwd (rope_len >= max_seqlen_k), and each
+ *                new query is rotated in the kernel at its absolute
+ *                position nk - nq + i, as the gist's forward rotates the
+ *                step's queries at their position ids.  The cached keys are
+ *                used as they are: a rotated cache holds each key already
+ *                rotated at its own position (diffattn_kv_append writes
+ *                them so).
  *   workspace    device scratch of at least workspace_bytes =
  *                diffattn_fwd_kv_workspace_size(nseq, max_seqlen_q,
  *                max_seqlen_k, H, Hkv, d) bytes, 16-byte aligned, owned by
@@ -187,8 +200,9 @@ int diffattn_fwd_kv(int dtype, const void *q, const void *k, const void *v,
                     const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
                     int32_t nseq, int32_t max_seqlen_q, int32_t max_seqlen_k,
                     int32_t Tq, int32_t Tk, int32_t H, int32_t Hkv, int32_t d,
-                    void *workspace, size_t workspace_bytes, void *out,
-                    void *stream);
+                    const void *rope_cos, const void *rope_sin, int32_t rope_len,
+                    int rope_dtype, void *workspace, size_t workspace_bytes,
+                    void *out, void *stream);
 
 /*
  * diffattn_fwd_kv without a workspace argument, for callers that cannot
@@ -223,13 +237,54 @@ int diffattn_fwd_kv_noalloc(int dtype, const void *q, const void *k,
                             const int32_t *cu_seqlens_k, int32_t nseq,
                             int32_t max_seqlen_q, int32_t max_seqlen_k,
                             int32_t Tq, int32_t Tk, int32_t H, int32_t Hkv,
-                            int32_t d, void *out, void *stream);
+                            int32_t d, const void *rope_cos,
+                            const void *rope_sin, int32_t rope_len,
+                            int rope_dtype, void *out, void *stream);
 
 /* Bytes of workspace diffattn_fwd_kv needs for these sizes (the same split
  * plan the call makes); 0 for sizes it rejects.  Host function. */
 size_t diffattn_fwd_kv_workspace_size(int32_t nseq, int32_t max_seqlen_q,
                                       int32_t max_seqlen_k, int32_t H,
                                       int32_t Hkv, int32_t d);
+
+/*
+ * The cache update of a decode step, asynchronous on `stream`: the
+ * LlamaDiffSdpaAttention.py gist's forward rotates the step's keys at their
+ * position ids and appends them and the values to the layer's cache
+ * (past_key_value.update) before it attends.  For every sequence s, its nq
+ * new tokens i = 0 .. nq-1 (packed by cu_seqlens_q) go to the last nq rows
+ * of its cache region (packed by cu_seqlens_k, nk rows with the new ones
+ * counted): cache row cu_seqlens_k[s+1] - nq + i, position nk - nq + i.
+ * The key is rotated there as diffattn_fwd rotates keys (interleaved pairs
+ * of each d-wide half-head, fp32 arithmetic, rounded once to the storage
+ * type) when tables are given, else copied; the value is copied.  Every
+ * other cache row is left as it is.
+ *
+ *   dtype        DIFFATTN_BF16 or DIFFATTN_F32: element type of keys and
+ *                values; d = 16, 32 or 64.
+ *   k_new, v_new device [Tq, Hkv, 2, d] and [Tq, Hkv, 2d].
+ *   cu_seqlens_q, cu_seqlens_k, nseq, max_seqlen_k, Tq, Tk
+ *                as for diffattn_fwd_kv (both NULL: nseq sequences of
+ *                Tq / nseq new tokens and Tk / nseq cache rows, and
+ *                max_seqlen_k ignored).  Precondition, not read here:
+ *                nq <= nk for every sequence (a sequence that breaks it is
+ *                left unwritten).
+ *   rope_cos, rope_sin, rope_len, rope_dtype
+ *                as for diffattn_fwd_kv (rope_len >= max_seqlen_k, so the
+ *                tables cover every cache position; NULL tables: no
+ *                rotation, rope_len and rope_dtype ignored).
+ *   k_cache, v_cache
+ *                device [Tk, Hkv, 2, d] and [Tk, Hkv, 2d], written in
+ *                place; they must not overlap k_new or v_new.
+ * All pointers 16-byte aligned.  Returns DIFFATTN_OK (Tq == 0 launches
+ * nothing), DIFFATTN_EINVAL, DIFFATTN_EUNSUPPORTED or DIFFATTN_EHIP.
+ */
+int diffattn_kv_append(int dtype, const void *k_new, const void *v_new,
+                       const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                       int32_t nseq, int32_t max_seqlen_k, int32_t Tq, int32_t Tk,
+                       int32_t Hkv, int32_t d,
+                       const void *rope_cos, const void *rope_sin, int32_t rope_len,
+                       int rope_dtype, void *k_cache, void *v_cache, void *stream);
 
 /* 1 if the cache kernel is compiled for (dtype, d), else 0.  Host
  * function. */

@@ -141,25 +141,29 @@ def key_factors(inp, rf):
     return out
 
 
+def turn(x, pos, rope):
+    """Rows of x ([N, ...heads, d]) turned as the rotary prologue turns
+    them: pair (x[2j], x[2j+1]) of row n by (cos, sin)[pos[n], j], in fp64,
+    stored back in x's type."""
+    cos, sin = (t.double() for t in rope)
+    pos = torch.as_tensor(pos).long()
+    c, s_ = cos[pos], sin[pos]                                   # [N, d/2]
+    xd = x.double()
+    x0, x1 = xd[..., 0::2], xd[..., 1::2]
+    shape = (xd.shape[0],) + (1,) * (xd.dim() - 2) + (c.shape[1],)
+    cc, ss = c.reshape(shape), s_.reshape(shape)
+    y = torch.empty_like(xd)
+    y[..., 0::2] = x0 * cc - x1 * ss
+    y[..., 1::2] = x0 * ss + x1 * cc
+    return y.to(x.dtype)
+
+
 def rotated(inp, rope):
     """A copy of inp whose q and k rows are turned as the rotary prologue
-    turns them: pair (x[2j], x[2j+1]) of the row at position p of its
-    sequence by (cos, sin)[p, j], stored back in the input's type."""
-    cos, sin = (t.double() for t in rope)
+    turns them: the row at position p of its sequence by (cos, sin)[p],
+    stored back in the input's type."""
     cu = inp.cu_seqlens.tolist()
     pos = torch.cat([torch.arange(cu[s + 1] - cu[s]) for s in range(len(cu) - 1)]).long()
-    c, s_ = cos[pos], sin[pos]                                   # [T, d/2]
-
-    def turn(x):
-        x = x.double()
-        x0, x1 = x[..., 0::2], x[..., 1::2]
-        shape = (x.shape[0],) + (1,) * (x.dim() - 2) + (c.shape[1],)
-        cc, ss = c.reshape(shape), s_.reshape(shape)
-        y = torch.empty_like(x)
-        y[..., 0::2] = x0 * cc - x1 * ss
-        y[..., 1::2] = x0 * ss + x1 * cc
-        return y.to(inp.q.dtype)
-
     out = copy.copy(inp)
-    out.q, out.k = turn(inp.q), turn(inp.k)
+    out.q, out.k = turn(inp.q, pos, rope), turn(inp.k, pos, rope)
     return out

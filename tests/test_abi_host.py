@@ -76,7 +76,7 @@ def call(**over):
              subln_weight=0,
              eps=1e-5, causal=1, cu_seqlens=0, nseq=2, max_seqlen=0, T=64,
              H=16, Hkv=4, d=64, rope_cos=0, rope_sin=0, rope_len=0,
-             workspace=0, workspace_bytes=0, out=FAKE, stream=0)
+             rope_dtype=0, workspace=0, workspace_bytes=0, out=FAKE, stream=0)
     a.update(over)
     return da.fwd_ptr(**a)
 
@@ -111,6 +111,8 @@ def call(**over):
     (dict(rope_cos=FAKE, rope_sin=FAKE, rope_len=32), da.EINVAL),   # no workspace
     (dict(rope_cos=FAKE, rope_sin=FAKE, rope_len=32, workspace=FAKE,
           workspace_bytes=100), da.EINVAL),                         # workspace too small
+    (dict(rope_cos=FAKE, rope_sin=FAKE, rope_len=32, rope_dtype=5, workspace=FAKE,
+          workspace_bytes=1 << 20), da.EINVAL),                     # table type
     (dict(T=0, q=0, k=0, v=0, out=0), da.OK),  # empty: nothing launched
 ])
 def test_validation_before_any_device_work(over, status):
@@ -153,7 +155,8 @@ def call_kv(**over):
              lq2=FAKE, lk2=FAKE, lambda_stride=0, lambda_init_value=0.7,
              subln_weight=0, eps=1e-5, causal=1, cu_seqlens_q=0,
              cu_seqlens_k=0, nseq=8, max_seqlen_q=0, max_seqlen_k=0, Tq=8,
-             Tk=8 * 4097, H=16, Hkv=4, d=64, workspace=FAKE,
+             Tk=8 * 4097, H=16, Hkv=4, d=64, rope_cos=0, rope_sin=0,
+             rope_len=0, rope_dtype=0, workspace=FAKE,
              workspace_bytes=1 << 30, out=FAKE, stream=0)
     a.update(over)
     return da.fwd_kv_ptr(**a)
@@ -181,6 +184,10 @@ def call_kv(**over):
     (dict(cu_seqlens_q=FAKE, cu_seqlens_k=FAKE, max_seqlen_q=9), da.EINVAL),
     (dict(cu_seqlens_q=FAKE, cu_seqlens_k=FAKE, max_seqlen_q=1,
           max_seqlen_k=8 * 4097 + 1), da.EINVAL),  # bound beyond Tk
+    (dict(rope_cos=FAKE), da.EINVAL),              # one table only
+    (dict(rope_cos=FAKE, rope_sin=FAKE, rope_len=4097, rope_dtype=7), da.EINVAL),
+    (dict(rope_cos=FAKE, rope_sin=FAKE, rope_len=4096), da.EINVAL),   # < max_seqlen_k
+    (dict(rope_cos=FAKE + 8, rope_sin=FAKE, rope_len=4097), da.EINVAL),
     (dict(Tq=0, q=0, out=0), da.OK),               # no query rows
 ])
 def test_kv_validation_before_any_device_work(over, status):
@@ -192,7 +199,8 @@ def call_kv_noalloc(**over):
              lq2=FAKE, lk2=FAKE, lambda_stride=0, lambda_init_value=0.7,
              subln_weight=0, eps=1e-5, causal=1, cu_seqlens_q=0,
              cu_seqlens_k=0, nseq=8, max_seqlen_q=0, max_seqlen_k=0, Tq=8,
-             Tk=8 * 4097, H=16, Hkv=4, d=64, out=FAKE, stream=0)
+             Tk=8 * 4097, H=16, Hkv=4, d=64, rope_cos=0, rope_sin=0,
+             rope_len=0, rope_dtype=0, out=FAKE, stream=0)
     a.update(over)
     return da.fwd_kv_noalloc_ptr(**a)
 
@@ -215,12 +223,42 @@ def test_kv_scratch_size_matches_header():
     (dict(Tk=0), da.EINVAL),                       # queries without keys
     (dict(q=0), da.EINVAL),
     (dict(out=FAKE + 4), da.EINVAL),               # not 16-byte aligned
+    (dict(rope_cos=FAKE, rope_sin=FAKE, rope_len=100), da.EINVAL),  # < max_seqlen_k
     (dict(Tq=0, q=0, out=0), da.OK),               # no query rows
     # partials beyond the static scratch: 64 sequences x 64 queries x 4 heads
     (dict(nseq=64, Tq=64 * 64, Tk=64 * 4096), da.ETOOLARGE),
 ])
 def test_kv_noalloc_validation_before_any_device_work(over, status):
     assert call_kv_noalloc(**over) == status
+
+
+def call_append(**over):
+    a = dict(dtype=da.BF16, k_new=FAKE, v_new=FAKE, cu_seqlens_q=0,
+             cu_seqlens_k=0, nseq=8, max_seqlen_k=0, Tq=8, Tk=8 * 4097,
+             Hkv=4, d=64, rope_cos=0, rope_sin=0, rope_len=0, rope_dtype=0,
+             k_cache=FAKE, v_cache=FAKE, stream=0)
+    a.update(over)
+    return da.kv_append_ptr(**a)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(dtype=7), da.EINVAL),
+    (dict(Hkv=0), da.EINVAL),
+    (dict(nseq=0), da.EINVAL),
+    (dict(d=48), da.EUNSUPPORTED),
+    (dict(cu_seqlens_q=FAKE), da.EINVAL),          # one boundary array only
+    (dict(Tq=12), da.EINVAL),                      # Tq % nseq
+    (dict(Tq=8 * 5000), da.EINVAL),                # nq > nk
+    (dict(k_cache=0), da.EINVAL),
+    (dict(v_new=FAKE + 4), da.EINVAL),             # not 16-byte aligned
+    (dict(rope_cos=FAKE), da.EINVAL),              # one table only
+    (dict(rope_cos=FAKE, rope_sin=FAKE, rope_len=4096), da.EINVAL),  # < nk
+    (dict(rope_cos=FAKE, rope_sin=FAKE, rope_len=4097, rope_dtype=3), da.EINVAL),
+    (dict(cu_seqlens_q=FAKE, cu_seqlens_k=FAKE, max_seqlen_k=8 * 4097 + 1), da.EINVAL),
+    (dict(Tq=0, k_new=0, v_new=0), da.OK),         # nothing to append
+])
+def test_kv_append_validation_before_any_device_work(over, status):
+    assert call_append(**over) == status
 
 
 def test_kv_noalloc_too_large_matches_workspace_size():

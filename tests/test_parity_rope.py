@@ -73,6 +73,24 @@ def test_ragged_varlen_rope(dtype, d, H, Hkv, causal):
     assert err <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("f32", 16), ("bf16", 32), ("f32", 64),
+                                     ("bf16", 16)])
+@pytest.mark.parametrize("lens", [RAGGED, RAGGED * 11])
+def test_bf16_tables(dtype, d, lens):
+    """Tables stored in bf16 (as the pull request's test caches them): the
+    output equals, bitwise, that of fp32 tables holding the same values, on
+    both instantiations of the prefill, and the oracle's with those values."""
+    wl = custom("rope_bf16_tables", dtype, lens, 16, 4, d, depth=4, seed=d + 51)
+    inp = make_inputs(wl)
+    rb = tuple(t.bfloat16() for t in rope_tables(256, d, base=50.0))
+    rf = tuple(t.float() for t in rb)
+    a, b = gpu_run(inp, rb), gpu_run(inp, rf)
+    assert torch.equal(a, b)
+    err = max_abs(a, oracle_full(inp, rf))
+    announce(f"bf16 tables {dtype} d={d} {len(lens)} sequences: max-abs {err:.3e}")
+    assert err <= TOL[dtype]
+
+
 @pytest.mark.parametrize("dtype,d", [("f32", 16), ("bf16", 64), ("bf16", 32), ("f32", 64)])
 @pytest.mark.parametrize("causal", [True, False])
 def test_ragged_varlen_rope_64_query_slots(dtype, d, causal):
