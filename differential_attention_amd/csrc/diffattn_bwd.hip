@@ -95,19 +95,38 @@ __device__ inline bf16x8 pack8(const f32x16 &s, int a0)
 // A operand X^T for a contraction over 16 rows of a row-major bf16 LDS tile
 // X: lane (column i, half h) gets X[step_row + 8t + 4h + e][i] for t, e in
 // 0..3 (two transposing reads).  col_byte selects the 32 columns.
+// Swizzled tiles (swz): the 16-byte chunk c of tile row r is stored at
+// chunk c ^ ((r >> 2) & 3).  LDS serves 256 bytes per cycle: a plain
+// 16-byte read by 16 lanes (here 16 consecutive rows at one chunk), a
+// transposing 8-byte read by 32 lanes (4 consecutive rows x 64 bytes).
+// With a row pitch of 64 mod 256 bytes the 4 rows of a transposing read
+// tile the 256 bytes (the swizzle only permutes chunks inside each row's
+// aligned group of 4), and the 16 rows of a plain read at one chunk land on
+// 16 distinct 16-byte slots (rows 4 apart share a 64-byte window and the
+// swizzle spreads them across it).  Every reader's swizzle is a lane
+// constant, folded into its base addresses.
 struct TrOperand {
-    int base;
-    __device__ TrOperand(int lane, int rowb)
+    int base[2];   // for the two 8-row halves of a 16-row step
+    __device__ TrOperand(int lane, int rowb, bool swz = false)
     {
         const int j = lane & 15;
-        base = (4 * (lane >> 5) + (j >> 2)) * rowb + 32 * ((lane >> 4) & 1) + 8 * (j & 3);
+        // this lane's 8 bytes: row 8 t + 4 (lane >> 5) + j / 4 of the step,
+        // chunk 2 ((lane >> 4) & 1) + (j & 3) / 2 of the column block (a
+        // multiple of 4 chunks), half j & 1; steps start at multiples of 16
+        // rows, so the row's swizzle bits are (2 t + (lane >> 5)) & 3
+        const int ch = 2 * ((lane >> 4) & 1) + ((j & 3) >> 1);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int sw = swz ? (2 * t + (lane >> 5)) & 3 : 0;
+            base[t] = (8 * t + 4 * (lane >> 5) + (j >> 2)) * rowb + 16 * (ch ^ sw) + 8 * (j & 1);
+        }
     }
     __device__ inline bf16x8 load(const char *tile, int rowb, int step_row, int col_byte) const
     {
         bf16x8 f;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const char *addr = tile + base + (step_row + 8 * t) * rowb + col_byte;
+            const char *addr = tile + base[t] + step_row * rowb + col_byte;
             const bf16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
                 (__attribute__((address_space(3))) bf16x4 *)addr);
 #pragma unroll
@@ -401,7 +420,7 @@ __global__ __launch_bounds__(1024) void bwd_reduce(BwdParams p)
 // chunks spread over the workgroup; rows at or past `valid` read as zero.
 // load() fills this thread's registers (the loads stay in flight), store()
 // writes them to LDS, so a tile can travel while the previous one is used.
-template <int ROWB, int LROW, int ROWS>
+template <int ROWB, int LROW, int ROWS, bool SWZ = false>
 struct Stager {
     static constexpr int CPR = ROWB / 16;
     static constexpr int N = (ROWS * CPR + kThreads - 1) / kThreads;   // chunks per thread
@@ -422,7 +441,7 @@ struct Stager {
 #pragma unroll
         for (int i = 0; i < N; ++i) {
             const int idx = threadIdx.x + i * kThreads;
-            const int row = idx / CPR, c = (idx % CPR) * 16;
+            const int row = idx / CPR, c = ((idx % CPR) ^ (SWZ ? (row >> 2) & 3 : 0)) * 16;
             if (idx < ROWS * CPR)
                 *(u32x4 *)(lds + row * LROW + c) = r[i];
         }
@@ -437,9 +456,9 @@ void bwd_dq(BwdParams p)
 {
     constexpr int ROWB = 2 * D * 2;        // K or V row bytes
     // K rows are read both as plain 16-byte rows and through the transposing
-    // read (4 rows x 64 bytes); a 48-byte pad keeps the plain reads on
-    // distinct banks and starts the transposed rows 48 bytes apart
-    constexpr int LROW = ROWB + 48;
+    // read, V rows plainly: swizzled tiles with a pitch of 64 mod 256 bytes
+    // (TrOperand) keep both on distinct banks (d = 32: 192 = -64 mod 256)
+    constexpr int LROW = ROWB + 64;
     constexpr int NKS = D / 16;            // QK contraction steps
     constexpr int NVS = 2 * D / 16;        // dO V contraction steps
     constexpr int NDB = D / 32;            // 32-dim blocks of dQ
@@ -488,14 +507,19 @@ void bwd_dq(BwdParams p)
     for (int db = 0; db < NDB; ++db)
         dqa[db] = f32x16{};
     const float c = kLog2e * rsqrtf((float)D);
-    const TrOperand tr(lane, LROW);
+    const TrOperand tr(lane, LROW, true);
+    // plain reads of row 32 b + n of a swizzled tile: chunk 2 ks + h lies at
+    // (2 ks + h) ^ a, a = (n >> 2) & 3: bases for even and odd ks
+    const int sa_ = (n >> 2) & 3;
+    const int plain_e = n * LROW + 16 * (h ^ (sa_ & 1)) + 32 * (sa_ >> 1);
+    const int plain_o = n * LROW + 16 * (h ^ (sa_ & 1)) - 32 * (sa_ >> 1);
     const int qhi = min(s1, q0 + kTile);
     const int kend = p.causal ? qhi : s1;
     const int ntiles = (kend - s0 + kInner - 1) / kInner;
     const int64_t kstride = (int64_t)p.Hkv * ROWB;
     const char *kg = (const char *)p.k + (int64_t)g * ROWB;
     const char *vg = (const char *)p.v + (int64_t)g * ROWB;
-    Stager<ROWB, LROW, kInner> sk, sv;
+    Stager<ROWB, LROW, kInner, true> sk, sv;
     auto fetch = [&](int it) __attribute__((always_inline)) {
         const int k0 = s0 + it * kInner;
         sk.load(kg + (int64_t)k0 * kstride, kstride, min(kInner, s1 - k0));
@@ -519,15 +543,16 @@ void bwd_dq(BwdParams p)
             f32x16 sa = f32x16{};
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
-                const bf16x8 ka = *(const bf16x8 *)(kt + (32 * b + n) * LROW +
-                                                    (map * D + 16 * ks + 8 * h) * 2);
+                const bf16x8 ka = *(const bf16x8 *)(kt + 32 * b * LROW + map * D * 2 +
+                                                    ((ks & 1) ? plain_o : plain_e) + 32 * ks);
                 sa = mma(ka, qf[ks], sa);
             }
             // dP^T = V dO^T
             f32x16 dp = f32x16{};
 #pragma unroll
             for (int ks = 0; ks < NVS; ++ks) {
-                const bf16x8 va = *(const bf16x8 *)(vt + (32 * b + n) * LROW + (16 * ks + 8 * h) * 2);
+                const bf16x8 va = *(const bf16x8 *)(vt + 32 * b * LROW +
+                                                    ((ks & 1) ? plain_o : plain_e) + 32 * ks);
                 dp = mma(va, df[ks], dp);
             }
             // P^T and dS^T; lane owns query wq, element a is key kb0 + acc_row(a, h).
@@ -613,11 +638,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 void bwd_dkdv(BwdParams p)
 {
     constexpr int ROWB = 2 * D * 2;          // K, V, Q (both maps) or dpre row bytes
-    // Q and dpre rows are read both ways: plain 16-byte reads of 16 rows and
-    // transposing reads of 4 consecutive rows x 64 bytes.  A pad of 48 keeps
-    // the plain reads on distinct banks (48 r mod 256 differs for r < 16) and
-    // starts the 4 rows of a transposing read 48 bytes apart instead of 16.
-    constexpr int LQROW = ROWB + 48;
+    // Q and dpre rows are read both ways, plain 16-byte reads and
+    // transposing reads: swizzled tiles with a pitch of 64 mod 256 bytes
+    // (TrOperand) keep both on distinct banks
+    // (d = 64: 320 bytes; d = 32: 192, which is -64 mod 256 and works alike)
+    constexpr int LQROW = ROWB + 64;
     constexpr int NKS = D / 16;
     constexpr int NVS = 2 * D / 16;
     constexpr int NKB = D / 32;              // 32-dim blocks of dK (per map)
@@ -661,14 +686,20 @@ void bwd_dkdv(BwdParams p)
     for (int db = 0; db < NVB; ++db)
         acc[db] = f32x16{};
     const float c = kLog2e * rsqrtf((float)D);
-    const TrOperand tr(lane, LQROW);
+    const TrOperand tr(lane, LQROW, true);
+    // this lane's plain reads of its row n of a swizzled tile: chunk
+    // 2 ks + h lies at (2 ks + h) ^ a, a = (n >> 2) & 3, that is at
+    // 2 (ks ^ (a >> 1)) + (h ^ (a & 1)): two bases, for even and odd ks
+    const int sa = (n >> 2) & 3;
+    const int plain_e = n * LQROW + 16 * (h ^ (sa & 1)) + 32 * (sa >> 1);
+    const int plain_o = n * LQROW + 16 * (h ^ (sa & 1)) - 32 * (sa >> 1);
     const int wk_first = k0 + 32 * sub;   // first key of this wave
     // queries before the tile's first key cannot see any of its keys
     const int qstart = p.causal ? k0 : s0;
     const int nqt = (s1 - qstart + kQT - 1) / kQT;   // query tiles per head
     const int total = p.G * nqt;                     // (head, query tile) steps
 
-    Stager<ROWB, LQROW, kQT> sq, sd;
+    Stager<ROWB, LQROW, kQT, true> sq, sd;
     // lse, and D'_1 or lambda D'_2, of the tile as [lse, D][map][row], so
     // that the four rows a lane's accumulator elements cover are one 16-byte
     // read
@@ -710,7 +741,7 @@ void bwd_dkdv(BwdParams p)
         f32x16 dp = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < NVS; ++ks)
-            dp = mma(*(const bf16x8 *)(dt + n * LQROW + (16 * ks + 8 * h) * 2), kv[ks], dp);
+            dp = mma(*(const bf16x8 *)(dt + ((ks & 1) ? plain_o : plain_e) + 32 * ks), kv[ks], dp);
         char *out = px + (stp & 1) * PXB + sub * 4 * 1024 + lane * 16;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -728,7 +759,7 @@ void bwd_dkdv(BwdParams p)
         f32x16 s1a = f32x16{}, s2a = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-            const char *qa = qt + n * LQROW + (16 * ks + 8 * h) * 2;
+            const char *qa = qt + ((ks & 1) ? plain_o : plain_e) + 32 * ks;
             s1a = mma(*(const bf16x8 *)qa, kv[ks], s1a);
             s2a = mma(*(const bf16x8 *)(qa + D * 2), kv[NKS + ks], s2a);
         }
