@@ -189,13 +189,31 @@ def bench_kv(args, name) -> int:
     need = da.kv_workspace_size(wl.nseq, wl.max_q, wl.max_k, wl.H, wl.Hkv, wl.d)
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
     stream = torch.cuda.Stream(dev)
+    # --rope: a rotary decode step -- the step's new keys (and values) turned
+    # into the last rows of each sequence's cache, then the new queries turned
+    # at their positions as they attend (tables of base 10000, fp32)
+    rope_args = (0, 0, 0, 0)
+    append = None
+    if args.rope:
+        rc, rs = (c(t) for t in workloads.rope_tables(wl.max_k, wl.d))
+        gen = torch.Generator().manual_seed(2)
+        k_new = c(torch.randn(wl.Tq, wl.Hkv, 2, wl.d, generator=gen).to(q.dtype))
+        v_new = c(torch.randn(wl.Tq, wl.Hkv, 2 * wl.d, generator=gen).to(q.dtype))
+        rope_args = (rc.data_ptr(), rs.data_ptr(), wl.max_k, da.F32)
+        append = (da.BF16, k_new.data_ptr(), v_new.data_ptr(), cq.data_ptr(), ck.data_ptr(),
+                  wl.nseq, wl.max_k, wl.Tq, wl.Tk, wl.Hkv, wl.d, *rope_args,
+                  k.data_ptr(), v.data_ptr(), stream.cuda_stream)
     ptrs = (da.BF16, q.data_ptr(), k.data_ptr(), v.data_ptr(),
             *[x.data_ptr() for x in lv], 0, da.lambda_init(wl.depth),
             w.data_ptr(), wl.eps, int(wl.causal), cq.data_ptr(), ck.data_ptr(),
             wl.nseq, wl.max_q, wl.max_k, wl.Tq, wl.Tk, wl.H, wl.Hkv, wl.d,
-            0, 0, 0, 0, ws.data_ptr(), need, out.data_ptr(), stream.cuda_stream)
+            *rope_args, ws.data_ptr(), need, out.data_ptr(), stream.cuda_stream)
 
     def step():
+        if append is not None:
+            st = da.kv_append_ptr(*append)
+            if st != 0:
+                raise da.DiffAttnError(st, "diffattn_kv_append")
         st = da.fwd_kv_ptr(*ptrs)
         if st != 0:
             raise da.DiffAttnError(st, "diffattn_fwd_kv")
@@ -249,7 +267,8 @@ def bench_kv(args, name) -> int:
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic (seeded N(0,1) q/k/v, N(0,0.1^2) lambda vectors)",
-        "config": {"workload": name, "nseq": wl.nseq, "Tq": wl.Tq, "Tk": wl.Tk,
+        "config": {"workload": name + ("+rope" if args.rope else ""), "rope": bool(args.rope),
+                   "nseq": wl.nseq, "Tq": wl.Tq, "Tk": wl.Tk,
                    "max_q": wl.max_q, "max_k": wl.max_k, "H": wl.H,
                    "Hkv": wl.Hkv, "d": wl.d, "depth": wl.depth,
                    "causal": wl.causal, "bytes_per_step": nbytes,
@@ -265,9 +284,11 @@ def bench_kv(args, name) -> int:
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4),
-                     "traffic": traffic_from_profiles(name, KV_KERNEL_SOURCES)},
+                     "traffic": traffic_from_profiles(name + ("_rope" if args.rope else ""),
+                                                      KV_KERNEL_SOURCES)},
     }
     result["cpu_baseline"] = (None if args.no_cpu_baseline
+                              else None if args.rope  # (the oracle's cache path takes rotated q)
                               else cpu_baseline_kv(wl, inp))
     print(json.dumps(result), flush=True)
     return 0
@@ -399,7 +420,9 @@ def main() -> int:
                          "the backward pass (bf16, no rotary prologue)")
     ap.add_argument("--rope", action="store_true",
                     help="prefill with the fused rotary prologue (q and k "
-                         "given unrotated, tables of base 10000)")
+                         "given unrotated, tables of base 10000); with a cache "
+                         "workload, a rotary decode step (the new keys turned "
+                         "into the cache, then the new queries turned)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of the workload, time a plain device copy of "
                          "this many bytes (calibrates HBM byte counters)")
