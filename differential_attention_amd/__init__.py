@@ -20,7 +20,7 @@ import torch
 __all__ = ["fwd", "fwd_ptr", "fwd_workspace_size", "fwd_kv", "fwd_kv_ptr", "kv_workspace_size",
            "fwd_kv_noalloc", "fwd_kv_noalloc_ptr", "KV_SCRATCH_BYTES",
            "fwd_train", "bwd", "bwd_workspace_size", "supported_bwd",
-           "kv_append", "kv_append_ptr",
+           "kv_append", "kv_append_ptr", "diff_attention", "DiffAttnFunction",
            "lambda_init", "supported", "supported_kv", "check_cu_seqlens",
            "check_cu_seqlens_kv", "library", "LIBRARY", "DiffAttnError",
            "BF16", "F32"]
@@ -643,3 +643,43 @@ def bwd(q, k, v, lambda_q1, lambda_k1, lambda_q2, lambda_k2,
     if st != OK:
         raise DiffAttnError(st, "diffattn_bwd")
     return g
+
+
+class DiffAttnFunction(torch.autograd.Function):
+    """Differential attention as a differentiable op: the forward through
+    ``diffattn_fwd_train``, the backward through ``diffattn_bwd`` (inputs
+    already rotated; gradients for q, k, v, the four lambda vectors and the
+    RMSNorm weight).  Call it through ``diff_attention``."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, lambda_q1, lambda_k1, lambda_q2, lambda_k2,
+                subln_weight, lambda_init, eps, causal, cu_seqlens, max_seqlen, nseq):
+        kw = dict(subln_weight=subln_weight, eps=eps, causal=causal,
+                  cu_seqlens=cu_seqlens, max_seqlen=max_seqlen, nseq=nseq)
+        out, lse, o12 = fwd_train(q, k, v, lambda_q1, lambda_k1, lambda_q2,
+                                  lambda_k2, lambda_init, **kw)
+        ctx.save_for_backward(q, k, v, lambda_q1, lambda_k1, lambda_q2, lambda_k2, lse, o12)
+        ctx.lambda_init = lambda_init
+        ctx.kw = kw
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, lq1, lk1, lq2, lk2, lse, o12 = ctx.saved_tensors
+        g = bwd(q, k, v, lq1, lk1, lq2, lk2, ctx.lambda_init, dout.contiguous(),
+                lse, o12, **ctx.kw)
+        w = ctx.kw["subln_weight"]
+        dw = g["dw"].view_as(w) if w is not None and ctx.needs_input_grad[7] else None
+        return (g["dq"], g["dk"], g["dv"], g["dlq1"], g["dlk1"], g["dlq2"],
+                g["dlk2"], dw, None, None, None, None, None, None)
+
+
+def diff_attention(q, k, v, lambda_q1, lambda_k1, lambda_q2, lambda_k2,
+                   lambda_init: float, subln_weight=None, eps: float = 1e-5,
+                   causal: bool = True, cu_seqlens=None, max_seqlen=None,
+                   nseq=None) -> torch.Tensor:
+    """Differentiable forward (autograd through ``DiffAttnFunction``); the
+    arguments are those of ``fwd_train`` (q and k post-rotary)."""
+    return DiffAttnFunction.apply(q, k, v, lambda_q1, lambda_k1, lambda_q2,
+                                  lambda_k2, subln_weight, lambda_init, eps,
+                                  causal, cu_seqlens, max_seqlen, nseq)

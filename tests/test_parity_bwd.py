@@ -365,3 +365,36 @@ def test_bwd_random_shapes(i):
     _, (got32,) = gpu_grads(twin, dy32, w=use_w)
     worst32 = compare(got32, ref, "fp32 twin of " + tag, inp=twin, rel=REL32)
     announce(f"random case {i}, fp32 twin: worst err / bar {worst32:.3f}")
+
+
+@pytest.mark.parametrize("w", [True, False])
+def test_autograd_function_matches_the_raw_calls(w):
+    """diff_attention under autograd: its output is the training forward's
+    and its gradients are diffattn_bwd's, bitwise."""
+    import differential_attention_amd as da
+    wl = custom("autograd", "bf16", (300, 65, 129), 8, 2, 64, depth=5, seed=71)
+    inp = make_inputs(wl)
+    dev = torch.device("cuda:0")
+    c = lambda t: t.to(dev).contiguous()
+    q, k, v = (c(x).requires_grad_() for x in (inp.q, inp.k, inp.v))
+    lv = [c(x).requires_grad_() for x in (inp.lq1, inp.lk1, inp.lq2, inp.lk2)]
+    wt = c(inp.w).requires_grad_() if w else None
+    lam0 = da.lambda_init(wl.depth)
+    kw = dict(subln_weight=wt, eps=wl.eps, causal=True, cu_seqlens=c(inp.cu_seqlens),
+              max_seqlen=wl.max_seqlen)
+    out = da.diff_attention(q, k, v, *lv, lam0, **kw)
+    dy = c(dout_for(inp, 72))
+    out.backward(dy)
+    torch.cuda.synchronize()
+    with torch.no_grad():
+        raw = [x.detach() for x in (q, k, v, *lv)]
+        kw2 = dict(kw, subln_weight=None if wt is None else wt.detach())
+        ref_out, lse, o12 = da.fwd_train(*raw, lam0, **kw2)
+        g = da.bwd(*raw, lam0, dy, lse, o12, **kw2)
+    torch.cuda.synchronize()
+    assert torch.equal(out.detach(), ref_out)
+    for name, t in zip(("dq", "dk", "dv", "dlq1", "dlk1", "dlq2", "dlk2"), (q, k, v, *lv)):
+        assert torch.equal(t.grad, g[name]), name
+    if w:
+        assert torch.equal(wt.grad, g["dw"])
+    announce(f"autograd (weight {w}): output and gradients equal the raw calls")
