@@ -390,7 +390,8 @@ def fwd_kv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     sequences).  When the bounds are not given they are read back from the
     device (a synchronising copy).  ``workspace`` is a device uint8 tensor of
     at least ``kv_workspace_size(...)`` bytes; one is allocated through
-    torch when it is None.  ``rope`` = (cos, sin) device tables [len, d/2]
+    torch when it is None and that size is not 0 (it is 0 for long query
+    chunks, which run in one kernel).  ``rope`` = (cos, sin) device tables [len, d/2]
     (fp32 or bf16) rotates each new query at its absolute position
     nk - nq + i; the cached keys are taken as already rotated (``kv_append``
     writes them so).  Returns ``out`` [Tq, H, 2d].
@@ -471,11 +472,13 @@ def _kv_call(q, k, v, lvs, lambda_init, subln_weight, eps, causal,
     if not noalloc:
         need = kv_workspace_size(nseq, max(max_seqlen_q, 1),
                                  max(max_seqlen_k, 1), H, Hkv, d)
-        if workspace is None:
-            workspace = torch.empty(max(need, 16), dtype=torch.uint8,
-                                    device=dev)
-        ws_ptr = _dev(workspace, "workspace", dev)
-        ws_bytes = workspace.numel() * workspace.element_size()
+        if workspace is None and need == 0:
+            ws_ptr, ws_bytes = 0, 0      # the one-kernel path: no workspace
+        else:
+            if workspace is None:
+                workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+            ws_ptr = _dev(workspace, "workspace", dev)
+            ws_bytes = workspace.numel() * workspace.element_size()
     if out is None:
         out = torch.empty((Tq, H, 2 * d), dtype=q.dtype, device=dev)
     elif tuple(out.shape) != (Tq, H, 2 * d):

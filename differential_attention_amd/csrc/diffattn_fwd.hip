@@ -73,6 +73,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "chunk.h"
 #include "diffattn.h"
 #include "rope.h"
 
@@ -295,6 +296,10 @@ struct Params {
     int64_t lstride;   // elements between heads' lambda vectors (0: shared)
     const float *w;
     const int32_t *cu;
+    // query chunks against a longer key range (the CHUNK instantiation):
+    // the keys' own boundaries, or NULL with klen_uniform keys per sequence
+    const int32_t *cuk;
+    int32_t klen_uniform;
     const void *rcos, *rsin;    // rotary tables [len][d/2] (fp32 or bf16), or NULL
     int32_t rope_dtype;         // element type of the tables
     const void *k_orig;         // unrotated K when rcos is set (k is then its rotated copy)
@@ -314,8 +319,12 @@ struct Params {
 // Every CU runs one workgroup of 8 waves (two per SIMD); the register
 // budget per lane is the 256 that two waves per SIMD leave.  SUB: 32-query
 // sub-blocks per wave -- 2 (each K/V operand read feeds two MFMAs), or 1 for
-// grids too small to fill the chip, which doubles the workgroups.
-template <typename E, int D, int RT, int SUB>
+// grids too small to fill the chip, which doubles the workgroups.  CHUNK:
+// each sequence's queries are the last nq of its nk keys (a chunk of new
+// queries against a key/value cache that already holds their keys, aligned
+// bottom-right as in the cache path), packed by their own boundaries; the
+// keys are used as given (a rotary chunk turns only its queries).
+template <typename E, int D, int RT, int SUB, bool CHUNK = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void diffattn_fwd_kernel(Params p)
 {
@@ -360,7 +369,7 @@ void diffattn_fwd_kernel(Params p)
     const int g = grp / p.hblocks;
     const int hb = grp % p.hblocks;
 
-    int s0, s1;
+    int s0, s1;                          // the sequence's query rows
     if (p.cu) {
         s0 = p.cu[seq];
         s1 = p.cu[seq + 1];
@@ -368,6 +377,27 @@ void diffattn_fwd_kernel(Params p)
         s0 = seq * p.seqlen_uniform;
         s1 = s0 + p.seqlen_uniform;
     }
+    // its key rows [ks0, ks1), and dk: the key index of query row tq (its
+    // own key) is tq + dk; without CHUNK the same rows, dk = 0
+    int ks0 = s0, ks1 = s1;
+    if constexpr (CHUNK) {
+        if (p.cuk) {
+            ks0 = p.cuk[seq];
+            ks1 = p.cuk[seq + 1];
+        } else {
+            ks0 = seq * p.klen_uniform;
+            ks1 = ks0 + p.klen_uniform;
+        }
+        if (ks1 <= ks0)
+            return;   // queries without keys: a broken precondition
+    }
+    const int dk = CHUNK ? ks1 - s1 : 0;
+    // rotary position of query row tq: its key's index in the sequence
+    // (clamped at 0 for chunks longer than their keys, a broken precondition
+    // of rotary chunks that must still read inside the tables)
+    auto rope_pos = [&](int tq) __attribute__((always_inline)) {
+        return CHUNK ? max(tq + dk - ks0, 0) : tq - ks0;
+    };
     const int qpw = kSlots / p.hpw;     // query blocks per workgroup
     const int bm = kQB * qpw;           // query rows per workgroup
     const int q0 = s0 + t * bm;
@@ -403,7 +433,7 @@ void diffattn_fwd_kernel(Params p)
                                   (((int64_t)tq * p.H + head) * 2 + map) * (D * 2) + qc * 16;
                 qv[i] = *(const u32x4 *)src;
                 if constexpr (ROPE)   // pairs 4 qc .. 4 qc + 3 of the half-head
-                    qv[i] = Rope<E, RT>::rotate(qv[i], Rope<E, RT>::coef(p.rcos, p.rsin, tq - s0,
+                    qv[i] = Rope<E, RT>::rotate(qv[i], Rope<E, RT>::coef(p.rcos, p.rsin, rope_pos(tq),
                                                                  4 * qc, D));
             } else {
                 qv[i] = u32x4{0u, 0u, 0u, 0u};
@@ -430,7 +460,7 @@ void diffattn_fwd_kernel(Params p)
                     const E *row = qg + (((int64_t)tq * p.H + head) * 2 + map) * D;
                     if constexpr (ROPE)
                         qf[u][ks] = Rope<E, RT>::element(row, ks * KSTEP + h * VEC, h,
-                                                         p.rcos, p.rsin, tq - s0, D);
+                                                         p.rcos, p.rsin, rope_pos(tq), D);
                     else
                         qf[u][ks] = *(const Frag *)(row + ks * KSTEP + h * VEC);
                 } else {
@@ -462,12 +492,12 @@ void diffattn_fwd_kernel(Params p)
     u32x4 kst[MAXL], vst[MAXL];
     // global -> registers: this wave's loads of block slice b of the tile at k0
     auto stage_load = [&](int k0, int b) __attribute__((always_inline)) {
-        const bool tail = k0 + GEO::BN > s1;
+        const bool tail = k0 + GEO::BN > ks1;
 #pragma unroll
         for (int i = b * LPW / GEO::NB; i < (b + 1) * LPW / GEO::NB; ++i) {
             int key = k0 + lrow + i * kWaves * RPL;
             if (tail)   // rows past the sequence repeat its last row
-                key = min(key, s1 - 1);
+                key = min(key, ks1 - 1);
             const int64_t off = (int64_t)key * rowstride;
             kst[i - b * LPW / GEO::NB] = *(const u32x4 *)(kbytes + off);
             vst[i - b * LPW / GEO::NB] = *(const u32x4 *)(vbytes + off);
@@ -498,8 +528,8 @@ void diffattn_fwd_kernel(Params p)
             o[u][db] = f32x16{};
     }
 
-    const int kv_end = p.causal ? qhi : s1;
-    const int ntiles = (kv_end - s0 + GEO::BN - 1) / GEO::BN;
+    const int kv_end = p.causal ? qhi + dk : ks1;
+    const int ntiles = (kv_end - ks0 + GEO::BN - 1) / GEO::BN;
 
     // lambda of this head (needed by the map-2 waves in the epilogue); its
     // loads travel with the first tile's.  The butterfly leaves every lane
@@ -525,12 +555,12 @@ void diffattn_fwd_kernel(Params p)
     // write (slice by slice, each write would wait for its own load)
     {
         u32x4 k0v[LPW], v0v[LPW];
-        const bool tail = s0 + GEO::BN > s1;
+        const bool tail = ks0 + GEO::BN > ks1;
 #pragma unroll
         for (int i = 0; i < LPW; ++i) {
-            int key = s0 + lrow + i * kWaves * RPL;
+            int key = ks0 + lrow + i * kWaves * RPL;
             if (tail)   // rows past the sequence repeat its last row
-                key = min(key, s1 - 1);
+                key = min(key, ks1 - 1);
             const int64_t off = (int64_t)key * rowstride;
             k0v[i] = *(const u32x4 *)(kbytes + off);
             v0v[i] = *(const u32x4 *)(vbytes + off);
@@ -569,7 +599,7 @@ void diffattn_fwd_kernel(Params p)
     };
     // One tile: compute from `cur` while the next tile is staged into `nxt`.
     auto tile = [&](int it, const char *cur, char *nxt) __attribute__((always_inline)) {
-        const int k0 = s0 + it * GEO::BN;
+        const int k0 = ks0 + it * GEO::BN;
         const char *kt = cur + k_lane;
         const bool more = it + 1 < ntiles;
 #pragma unroll
@@ -587,8 +617,8 @@ void diffattn_fwd_kernel(Params p)
             const int kb0 = k0 + 32 * b;
             // wave-uniform: can this wave see any key of the block, and does
             // any key need the index mask?
-            if (!(kb0 >= s1 || (p.causal && kb0 > wq_last))) {
-            const bool masked = kb0 + 32 > s1 || (p.causal && kb0 + 31 > wq0);
+            if (!(kb0 >= ks1 || (p.causal && kb0 > wq_last + dk))) {
+            const bool masked = kb0 + 32 > ks1 || (p.causal && kb0 + 31 > wq0 + dk);
             // ---- S^T = K Q^T ------------------------------------------------
             Frag ka[NKS];
 #pragma unroll
@@ -608,12 +638,12 @@ void diffattn_fwd_kernel(Params p)
                 for (int u = 0; u < kSub; ++u) {
                     // wave-uniform: does this sub-block straddle the diagonal
                     // or the end of the sequence?
-                    if (kb0 + 32 > s1 || (p.causal && kb0 + 31 > wq0 + 32 * u)) {
+                    if (kb0 + 32 > ks1 || (p.causal && kb0 + 31 > wq0 + dk + 32 * u)) {
                         // key kb0 + acc_row(a, h) is visible iff its offset
                         // acc_row(a, 0) is at most lim (one compare per key)
-                        int lim = s1 - 1 - kb0;
+                        int lim = ks1 - 1 - kb0;
                         if (p.causal)
-                            lim = min(lim, wq0 + 32 * u + n - kb0);
+                            lim = min(lim, wq0 + dk + 32 * u + n - kb0);
                         lim -= 4 * h;
 #pragma unroll
                         for (int a = 0; a < 16; ++a)
@@ -919,6 +949,51 @@ int launch(const Params &p, int nblocks, hipStream_t stream)
     return hipGetLastError() == hipSuccess ? DIFFATTN_OK : DIFFATTN_EHIP;
 }
 
+// Query chunks against a key/value cache: the keys are used as given, so a
+// rotary chunk turns only its queries (no K rotation).
+template <typename E, int D, int RT>
+void launch_chunk_rt(const Params &p, int nblocks, hipStream_t stream)
+{
+    if (p.sub == 2)
+        hipLaunchKernelGGL((diffattn_fwd_kernel<E, D, RT, 2, true>), dim3(nblocks), dim3(kThreads),
+                           0, stream, p);
+    else
+        hipLaunchKernelGGL((diffattn_fwd_kernel<E, D, RT, 1, true>), dim3(nblocks), dim3(kThreads),
+                           0, stream, p);
+}
+
+template <typename E, int D>
+int launch_chunk(const Params &p, int nblocks, hipStream_t stream)
+{
+    if (!p.rcos)
+        launch_chunk_rt<E, D, diffattn_rope::kOff>(p, nblocks, stream);
+    else if (p.rope_dtype == DIFFATTN_BF16)
+        launch_chunk_rt<E, D, diffattn_rope::kBF16>(p, nblocks, stream);
+    else
+        launch_chunk_rt<E, D, diffattn_rope::kF32>(p, nblocks, stream);
+    return hipGetLastError() == hipSuccess ? DIFFATTN_OK : DIFFATTN_EHIP;
+}
+
+// Grid of a launch: 64 queries per wave, or 32 when that leaves fewer than
+// two workgroups per CU (256 CUs), so small problems spread over twice the
+// workgroups.  Returns false when the grid would not fit 32 bits.
+bool grid_shape(int max_seqlen, int nseq, int H, int Hkv, int &hpw, int &sub, int64_t &ntile_q,
+                int64_t &nblocks)
+{
+    const int G = H / Hkv;
+    hpw = (G % 4 == 0) ? 4 : (G % 2 == 0 ? 2 : 1);
+    sub = 2;
+    for (;;) {
+        const int bm = 32 * sub * (kSlots / hpw);
+        ntile_q = ((int64_t)max_seqlen + bm - 1) / bm;
+        nblocks = ntile_q * nseq * Hkv * (G / hpw);
+        if (sub == 1 || nblocks >= 2 * kCUs)
+            break;
+        sub = 1;
+    }
+    return nblocks <= INT32_MAX;
+}
+
 typedef int (*launch_fn)(const Params &, int, hipStream_t);
 
 launch_fn find_launcher(int dtype, int d)
@@ -1037,20 +1112,9 @@ int fwd_impl(int dtype, const void *q, const void *k, const void *v,
         return DIFFATTN_EINVAL;
     // byte offsets of K/V rows are formed in 64 bits; the grid in 32 bits
     const int G = H / Hkv;
-    const int hpw = (G % 4 == 0) ? 4 : (G % 2 == 0 ? 2 : 1);
-    // 64 queries per wave; 32 when that leaves fewer than two workgroups per
-    // CU (256 CUs), so small problems spread over twice the workgroups
-    int sub = 2;
+    int hpw = 0, sub = 0;
     int64_t ntile_q = 0, nblocks = 0;
-    for (;;) {
-        const int bm = 32 * sub * (kSlots / hpw);
-        ntile_q = ((int64_t)max_seqlen + bm - 1) / bm;
-        nblocks = ntile_q * nseq * Hkv * (G / hpw);
-        if (sub == 1 || nblocks >= 2 * kCUs)
-            break;
-        sub = 1;
-    }
-    if (nblocks > INT32_MAX)
+    if (!grid_shape(max_seqlen, nseq, H, Hkv, hpw, sub, ntile_q, nblocks))
         return DIFFATTN_EINVAL;
 
     Params p;
@@ -1066,6 +1130,8 @@ int fwd_impl(int dtype, const void *q, const void *k, const void *v,
     p.lstride = lambda_stride;
     p.w = subln_weight;
     p.cu = cu_seqlens;
+    p.cuk = nullptr;
+    p.klen_uniform = 0;
     p.rcos = rope_cos;
     p.rsin = rope_sin;
     p.rope_dtype = rope_dtype;
@@ -1092,6 +1158,74 @@ int fwd_impl(int dtype, const void *q, const void *k, const void *v,
 }
 
 } // namespace
+
+double diffattn_chunk_prefill_us(int32_t nseq, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                 int32_t H, int32_t Hkv)
+{
+    int hpw = 0, sub = 0;
+    int64_t ntile_q = 0, nblocks = 0;
+    if (!grid_shape(max_seqlen_q, nseq, H, Hkv, hpw, sub, ntile_q, nblocks))
+        return INFINITY;
+    // one workgroup per CU at a time; a workgroup takes about 24 ns per key
+    // with 32-query sub-blocks and 47 ns with 64 (measured, d = 64, keys of
+    // one sequence streaming through a 128-key tile)
+    const double ns_per_key = sub == 2 ? 47.0 : 24.0;
+    const int64_t rounds = (nblocks + kCUs - 1) / kCUs;
+    return 1e-3 * ns_per_key * (double)rounds * (double)max_seqlen_k;
+}
+
+int diffattn_chunk_prefill(const void *q, const void *k, const void *v, const float *lambda_q1,
+                           const float *lambda_k1, const float *lambda_q2,
+                           const float *lambda_k2, int32_t lambda_stride, float lambda_init,
+                           const float *subln_weight, float eps, int causal,
+                           const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                           int32_t nseq, int32_t max_seqlen_q, int32_t Tq, int32_t Tk, int32_t H,
+                           int32_t Hkv, int32_t d, const void *rope_cos, const void *rope_sin,
+                           int rope_dtype, void *out, void *stream)
+{
+    if (d != 64 && d != 32)
+        return DIFFATTN_EUNSUPPORTED;
+    int hpw = 0, sub = 0;
+    int64_t ntile_q = 0, nblocks = 0;
+    if (!grid_shape(max_seqlen_q, nseq, H, Hkv, hpw, sub, ntile_q, nblocks))
+        return DIFFATTN_EINVAL;
+    Params p;
+    p.q = q;
+    p.k = k;
+    p.k_orig = k;
+    p.v = v;
+    p.out = out;
+    p.lq1 = lambda_q1;
+    p.lk1 = lambda_k1;
+    p.lq2 = lambda_q2;
+    p.lk2 = lambda_k2;
+    p.lstride = lambda_stride;
+    p.w = subln_weight;
+    p.cu = cu_seqlens_q;
+    p.cuk = cu_seqlens_k;
+    p.klen_uniform = cu_seqlens_q ? 0 : Tk / nseq;
+    p.rcos = rope_cos;
+    p.rsin = rope_sin;
+    p.rope_dtype = rope_dtype;
+    p.lse = nullptr;
+    p.o12 = nullptr;
+    p.lambda_init = lambda_init;
+    p.eps = eps;
+    p.T = Tq;
+    p.H = H;
+    p.Hkv = Hkv;
+    p.nseq = nseq;
+    p.seqlen_uniform = cu_seqlens_q ? 0 : Tq / nseq;
+    p.causal = causal;
+    p.ntile_q = (int32_t)ntile_q;
+    p.max_seqlen = max_seqlen_q;
+    p.hpw = hpw;
+    p.hblocks = H / Hkv / hpw;
+    p.sub = sub;
+    hipStream_t st = (hipStream_t)stream;
+    return d == 64 ? launch_chunk<bf16, 64>(p, (int)nblocks, st)
+                   : launch_chunk<bf16, 32>(p, (int)nblocks, st);
+}
 
 extern "C" {
 

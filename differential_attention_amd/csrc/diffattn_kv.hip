@@ -59,6 +59,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "chunk.h"
 #include "diffattn.h"
 #include "rope.h"
 
@@ -618,6 +619,26 @@ struct KvPlan {
 
 constexpr int64_t kTargetWaves = 1024;
 
+// Long query chunks (chunked prefill, a context-parallel shard) run on the
+// prefill kernel, which reads each key tile once for 32 or 64 query rows of
+// four heads, when its estimated time beats the split-KV pair's.  The pair
+// costs about 4.3 ps per (query row x key) once rows outnumber what one K/V
+// read can feed, plus about 10 us of fixed cost (measured, d = 64, against
+// caches of 2048 to 32768 keys).  The sizes are taken as uniform (nseq
+// sequences of max_seqlen_q queries and max_seqlen_k keys), so the choice,
+// like the split plan, depends on the bounds alone.  Below 32 rows the pair
+// always wins.
+constexpr int kChunkMinRows = 32;
+
+bool use_chunk(int nseq, int max_q, int max_k, int H, int Hkv, int d)
+{
+    if (max_q < kChunkMinRows || nseq < 1 || max_k < 1 || H < 1 || Hkv < 1 || H % Hkv != 0 ||
+        !diffattn_supported_kv(DIFFATTN_BF16, d))
+        return false;
+    const double split_us = 4.3e-6 * H * (double)max_q * (double)nseq * (double)max_k + 10.0;
+    return diffattn_chunk_prefill_us(nseq, max_q, max_k, H, Hkv) < split_us;
+}
+
 // Tk < 0: the workspace bound only (ck left 0)
 bool make_plan(int nseq, int max_q, int max_k, int G, int Hkv, int d, int64_t Tk, KvPlan &pl)
 {
@@ -688,6 +709,8 @@ extern "C" size_t diffattn_fwd_kv_workspace_size(int32_t nseq, int32_t max_seqle
 {
     if (H < 1 || Hkv < 1 || H % Hkv != 0 || d < 1)
         return 0;
+    if (use_chunk(nseq, max_seqlen_q, max_seqlen_k, H, Hkv, d))
+        return 0;   // the prefill kernel: no workspace
     KvPlan pl;
     if (!make_plan(nseq, max_seqlen_q, max_seqlen_k, H / Hkv, Hkv, d, -1, pl))
         return 0;
@@ -765,6 +788,12 @@ int kv_impl(int dtype, const void *q, const void *k, const void *v,
     // the tables cover every position a new query can have (< nk)
     if (rope_cos && (rope_len < max_seqlen_k || !aligned16(rope_cos) || !aligned16(rope_sin)))
         return DIFFATTN_EINVAL;
+    // long query chunks: the prefill kernel, with no split and no workspace
+    if (use_chunk(nseq, max_seqlen_q, max_seqlen_k, H, Hkv, d))
+        return diffattn_chunk_prefill(q, k, v, lambda_q1, lambda_k1, lambda_q2, lambda_k2,
+                                      lambda_stride, lambda_init, subln_weight, eps, causal,
+                                      cu_seqlens_q, cu_seqlens_k, nseq, max_seqlen_q, Tq, Tk, H,
+                                      Hkv, d, rope_cos, rope_sin, rope_dtype, out, stream);
     const int G = H / Hkv;
     KvPlan pl;
     if (!make_plan(nseq, max_seqlen_q, max_seqlen_k, G, Hkv, d, Tk, pl))

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define DIFFATTN_ABI_VERSION 9
+#define DIFFATTN_ABI_VERSION 10
 
 enum diffattn_status {
     DIFFATTN_OK = 0,
@@ -145,7 +145,17 @@ size_t diffattn_fwd_workspace_size(int dtype, int32_t T, int32_t Hkv, int32_t d,
  * and nk cached keys (the new tokens' own keys being the last nq of them),
  * query i (0-based) sees keys j <= nk - nq + i when causal == 1 and all nk
  * keys when causal == 0; everything else is as in diffattn_fwd.  With
- * nq == nk this is diffattn_fwd's causal prefill.
+ * nq == nk this is diffattn_fwd's causal prefill; a prompt cut into chunks
+ * (each chunk's keys appended before its queries attend) gives, chunk by
+ * chunk, the rows of its one-shot prefill.
+ *
+ * Two kernel paths, chosen from the size bounds alone (nseq, max_seqlen_q,
+ * max_seqlen_k, H, Hkv, d): few query rows per sequence (decoding) split
+ * the keys over many workgroups and merge the partial results in a second
+ * kernel, through the workspace; long query chunks (32 rows or more, when
+ * the library's cost estimate favours it) run on diffattn_fwd's prefill
+ * kernel with the keys' own boundaries, in one kernel and with no
+ * workspace.  diffattn_fwd_kv_workspace_size returns 0 for the latter.
  *
  *   q            device [Tq, H, 2, d]: the new queries, packed by
  *                cu_seqlens_q.
@@ -164,8 +174,9 @@ size_t diffattn_fwd_workspace_size(int dtype, int32_t T, int32_t Hkv, int32_t d,
  *                causal (see diffattn_check_cu_seqlens_kv).
  *   max_seqlen_q, max_seqlen_k
  *                upper bounds on every nq and nk (ignored when the
- *                boundaries are NULL); max_seqlen_q sizes the grid and the
- *                workspace.  Keys are split into chunks of one size for all
+ *                boundaries are NULL); with H, Hkv and d they choose the
+ *                path, and max_seqlen_q sizes the grid and the workspace.
+ *                The split path cuts keys into pieces of one size for all
  *                sequences, chosen from Tk.
  *   Tq, Tk, H, Hkv, d
  *                sizes; H % Hkv == 0.  Compiled (dtype, d) pairs: see
@@ -186,6 +197,7 @@ size_t diffattn_fwd_workspace_size(int dtype, int32_t T, int32_t Hkv, int32_t d,
  *                kernels of one call; its contents need no initialisation
  *                and are meaningless afterwards.  Two calls in flight at
  *                once (on different streams) need different workspaces.
+ *                Not read (and may be NULL) when that size is 0.
  *   out          device [Tq, H, 2d], same element type as q.
  *
  * Returns DIFFATTN_OK (also when there is no query row, which launches
@@ -241,8 +253,10 @@ int diffattn_fwd_kv_noalloc(int dtype, const void *q, const void *k,
                             const void *rope_sin, int32_t rope_len,
                             int rope_dtype, void *out, void *stream);
 
-/* Bytes of workspace diffattn_fwd_kv needs for these sizes (the same split
- * plan the call makes); 0 for sizes it rejects.  Host function. */
+/* Bytes of workspace diffattn_fwd_kv needs for these sizes (the same path
+ * choice and split plan the call makes); 0 when the call runs on the
+ * prefill kernel, which needs none, and for sizes it rejects.  Host
+ * function. */
 size_t diffattn_fwd_kv_workspace_size(int32_t nseq, int32_t max_seqlen_q,
                                       int32_t max_seqlen_k, int32_t H,
                                       int32_t Hkv, int32_t d);

@@ -225,8 +225,9 @@ def test_kv_scratch_size_matches_header():
     (dict(out=FAKE + 4), da.EINVAL),               # not 16-byte aligned
     (dict(rope_cos=FAKE, rope_sin=FAKE, rope_len=100), da.EINVAL),  # < max_seqlen_k
     (dict(Tq=0, q=0, out=0), da.OK),               # no query rows
-    # partials beyond the static scratch: 64 sequences x 64 queries x 4 heads
-    (dict(nseq=64, Tq=64 * 64, Tk=64 * 4096), da.ETOOLARGE),
+    # split partials beyond the static scratch: 4096 sequences x 4 queries x
+    # 16 heads against 128 keys each (a decode-sized call)
+    (dict(nseq=4096, Tq=4096 * 4, Tk=4096 * 128), da.ETOOLARGE),
 ])
 def test_kv_noalloc_validation_before_any_device_work(over, status):
     assert call_kv_noalloc(**over) == status
@@ -262,9 +263,39 @@ def test_kv_append_validation_before_any_device_work(over, status):
 
 
 def test_kv_noalloc_too_large_matches_workspace_size():
-    need = da.kv_workspace_size(64, 64, 4096, 16, 4, 64)
+    need = da.kv_workspace_size(4096, 4, 128, 16, 4, 64)
     assert need > da.KV_SCRATCH_BYTES
     assert da.kv_workspace_size(64, 1, 4096, 16, 4, 64) <= da.KV_SCRATCH_BYTES
+
+
+@pytest.mark.parametrize("nseq,mq,mk,H,Hkv,d", [
+    (8, 64, 4096, 16, 4, 64),      # chunked prefill of the 8 x 4096 prompts
+    (8, 1024, 4096, 16, 4, 64),
+    (8, 4096, 4096, 16, 4, 64),    # the whole prompt as one chunk
+    (1, 1024, 32768, 16, 4, 64),
+    (32, 32, 2048, 16, 4, 64),
+    (8, 128, 4096, 8, 8, 64),      # G = 1
+    (8, 64, 4096, 16, 4, 32),
+    (5, 257, 1100, 12, 4, 64),     # G = 3
+])
+def test_long_chunks_take_the_one_kernel_path(nseq, mq, mk, H, Hkv, d):
+    """Query chunks whose split-KV cost (rows x keys) outweighs one pass of
+    the prefill kernel over the keys need no workspace."""
+    assert da.kv_workspace_size(nseq, mq, mk, H, Hkv, d) == 0
+
+
+@pytest.mark.parametrize("nseq,mq,mk,H,Hkv,d", [
+    (8, 1, 4097, 16, 4, 64),       # decode steps
+    (64, 1, 8192, 16, 4, 64),
+    (32, 4, 32768, 16, 4, 64),
+    (8, 16, 4096, 16, 4, 64),      # below 32 rows
+    (8, 31, 4096, 16, 4, 64),
+    (8, 32, 4096, 16, 4, 64),      # one grid round of 4096 keys: no gain
+    (1, 256, 32768, 16, 4, 64),    # 32 workgroups over 32768 keys
+    (4096, 4, 128, 16, 4, 64),
+])
+def test_decode_shapes_keep_the_split_path(nseq, mq, mk, H, Hkv, d):
+    assert da.kv_workspace_size(nseq, mq, mk, H, Hkv, d) > 0
 
 
 # --------------------------------------------------------------------------
