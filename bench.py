@@ -18,6 +18,8 @@ sample of the same workload.
 step = one diffattn_fwd_kv call: the split-KV partial kernel and the
 combine kernel); its ``value`` is GB/s of the bytes the step must move (q,
 k, v read once, out written once) against MI355X's 8 TB/s HBM peak.
+``--workload chunk_...`` is a chunked prefill through the same call, which
+runs on the prefill kernel: TFLOP/s against the bf16 MFMA peak.
 """
 
 from __future__ import annotations
@@ -44,12 +46,15 @@ PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 METRIC = "diff-attention fwd TFLOP/s & % bf16 MFMA peak, 1 MI355X, N=4096 causal"
 METRIC_KV = "diff-attention KV-cache decode GB/s & % HBM peak, 1 MI355X"
+METRIC_CHUNK = "diff-attention chunked prefill TFLOP/s & % bf16 MFMA peak, 1 MI355X"
 GRAPH_STEPS = 10   # decode steps per captured graph (--graph)
 _CSRC = os.path.join(HERE, "differential_attention_amd", "csrc")
 # the sources whose kernels a stored counter profile measured: a profile
 # counts only while their digest matches
 KERNEL_SOURCES = [os.path.join(_CSRC, "diffattn_fwd.hip"), os.path.join(_CSRC, "rope.h")]
 KV_KERNEL_SOURCES = [os.path.join(_CSRC, "diffattn_kv.hip"), os.path.join(_CSRC, "rope.h")]
+CHUNK_KERNEL_SOURCES = KERNEL_SOURCES + [os.path.join(_CSRC, "diffattn_kv.hip"),
+                                         os.path.join(_CSRC, "chunk.h")]
 BWD_KERNEL_SOURCES = [os.path.join(_CSRC, "diffattn_fwd.hip"), os.path.join(_CSRC, "rope.h"),
                       os.path.join(_CSRC, "diffattn_bwd.hip")]
 
@@ -141,13 +146,19 @@ def cpu_baseline(wl, inp, flop_budget: float = 1.0e12, rope=None):
                        "convention); fp64 C oracle, OpenMP over rows")}
 
 
-def cpu_baseline_kv(wl, inp, min_seconds: float = 2.0):
-    """The fp64 oracle on the whole cache workload (every sequence, query
-    and head), repeated until ``min_seconds`` of host time have passed;
-    reported in GB/s of the bytes a step must move (q, k, v, out in the
-    storage type)."""
-    import numpy as np
+def cpu_baseline_kv(wl, inp, min_seconds: float = 2.0, flops: bool = False):
+    """The fp64 oracle on the cache workload, repeated until ``min_seconds``
+    of host time have passed; reported in GB/s of the bytes a step must move
+    (q, k, v, out in the storage type), or with ``flops`` in TFLOP/s on the
+    first sequence alone (a chunk's compute, sampled)."""
     import oracle
+    import workloads
+    if flops:   # one sequence of the chunk workload
+        wl = workloads.custom_kv(wl.name, wl.dtype, wl.q_lens[:1], wl.k_lens[:1], H=wl.H,
+                                 Hkv=wl.Hkv, d=wl.d, depth=wl.depth, causal=wl.causal,
+                                 eps=wl.eps)
+        nq, nk = wl.Tq, wl.Tk
+        inp = type(inp)(**{**inp.__dict__, "q": inp.q[:nq], "k": inp.k[:nk], "v": inp.v[:nk]})
     q, k, v = (oracle._f32(x) for x in (inp.q, inp.k, inp.v))
     lv = [oracle._f32(x) for x in (inp.lq1, inp.lk1, inp.lq2, inp.lk2)]
     w = oracle._f32(inp.w)
@@ -162,6 +173,13 @@ def cpu_baseline_kv(wl, inp, min_seconds: float = 2.0):
         dt = time.perf_counter() - t0
         if dt >= min_seconds:
             break
+    if flops:
+        return {"value": wl.flops() * runs / dt / 1e12, "unit": "TFLOP/s",
+                "cores": oracle.max_threads(), "kind": "oracle",
+                "seconds": round(dt, 3),
+                "sample": (f"one sequence of the workload ({wl.Tq} queries x {wl.H} heads "
+                           f"against {wl.Tk} keys, {wl.flops() / 1e9:.1f} GFLOP), {runs} "
+                           "run(s); fp64 C oracle, OpenMP over output rows")}
     nbytes = wl.bytes()
     return {"value": nbytes * runs / dt / 1e9, "unit": "GB/s",
             "cores": oracle.max_threads(), "kind": "oracle",
@@ -187,6 +205,9 @@ def bench_kv(args, name) -> int:
     w, cq, ck = c(inp.w), c(inp.cu_q), c(inp.cu_k)
     out = torch.empty((wl.Tq, wl.H, 2 * wl.d), dtype=q.dtype, device=dev)
     need = da.kv_workspace_size(wl.nseq, wl.max_q, wl.max_k, wl.H, wl.Hkv, wl.d)
+    # no workspace: a chunk that runs on the prefill kernel, bound by MFMA
+    # throughput rather than by reading the cache
+    chunk = need == 0
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
     stream = torch.cuda.Stream(dev)
     # --rope: a rotary decode step -- the step's new keys (and values) turned
@@ -207,7 +228,7 @@ def bench_kv(args, name) -> int:
             *[x.data_ptr() for x in lv], 0, da.lambda_init(wl.depth),
             w.data_ptr(), wl.eps, int(wl.causal), cq.data_ptr(), ck.data_ptr(),
             wl.nseq, wl.max_q, wl.max_k, wl.Tq, wl.Tk, wl.H, wl.Hkv, wl.d,
-            *rope_args, ws.data_ptr(), need, out.data_ptr(), stream.cuda_stream)
+            *rope_args, ws.data_ptr() if need else 0, need, out.data_ptr(), stream.cuda_stream)
 
     def step():
         if append is not None:
@@ -254,10 +275,11 @@ def bench_kv(args, name) -> int:
     ms = ev0.elapsed_time(ev1) / args.steps
     nbytes = wl.bytes()
     gbs = nbytes / (ms * 1e-3) / 1e9
+    tflops = wl.flops() / (ms * 1e-3) / 1e12
     result = {
-        "metric": METRIC_KV,
-        "value": round(gbs, 1),
-        "unit": "GB/s",
+        "metric": METRIC_CHUNK if chunk else METRIC_KV,
+        "value": round(tflops, 2) if chunk else round(gbs, 1),
+        "unit": "TFLOP/s" if chunk else "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -273,23 +295,29 @@ def bench_kv(args, name) -> int:
                    "Hkv": wl.Hkv, "d": wl.d, "depth": wl.depth,
                    "causal": wl.causal, "bytes_per_step": nbytes,
                    "tokens_per_s": round(wl.Tq / (ms * 1e-3), 1),
-                   "tflops": round(wl.flops() / (ms * 1e-3) / 1e12, 2),
+                   "tflops": round(tflops, 2), "gb_per_s": round(gbs, 1),
+                   "path": "one kernel (prefill)" if chunk else "split-KV + combine",
                    "workspace_bytes": need,
                    "launch": f"hip graph of {GRAPH_STEPS} steps" if graph is not None else "eager",
                    "wall_s_timed": round(wall, 4),
                    "ms_per_launch": per_launch_ms(step, stream, args.steps) if graph is None else None,
                    "kernel_digest": kernel_digest(KV_KERNEL_SOURCES)},
-        # both kernels of the step are in the timed duration, so this is a
-        # lower bound on the partial kernel's own rate
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
-                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(gbs / PEAK_HBM_GBS, 4),
-                     "traffic": traffic_from_profiles(name + ("_rope" if args.rope else ""),
-                                                      KV_KERNEL_SOURCES)},
+        # split path: both kernels of the step are in the timed duration, so
+        # this is a lower bound on the partial kernel's own rate
+        "roofline": ({"bound": "mfma", "achieved": round(tflops, 2),
+                      "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
+                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4)} if chunk else
+                     {"bound": "hbm", "achieved": round(gbs, 1),
+                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                      "frac": round(gbs / PEAK_HBM_GBS, 4)}),
     }
+    result["roofline"]["traffic"] = traffic_from_profiles(
+        name + ("_rope" if args.rope else ""), CHUNK_KERNEL_SOURCES if chunk else KV_KERNEL_SOURCES)
+    result["config"]["kernel_digest"] = kernel_digest(CHUNK_KERNEL_SOURCES if chunk
+                                                      else KV_KERNEL_SOURCES)
     result["cpu_baseline"] = (None if args.no_cpu_baseline
                               else None if args.rope  # (the oracle's cache path takes rotated q)
-                              else cpu_baseline_kv(wl, inp))
+                              else cpu_baseline_kv(wl, inp, flops=chunk))
     print(json.dumps(result), flush=True)
     return 0
 

@@ -263,6 +263,13 @@ KV_WORKLOADS = {
         description="bf16 multi-token decode: 32 sequences, 4 new queries "
                     "each, cache lengths uniform in [1024, 32768], 16 diff "
                     "heads, 4 KV heads, d=64"),
+    "chunk_b8_q1024_kv4096": KvWorkload(
+        "chunk_b8_q1024_kv4096", "bf16", (1024,) * 8, (4096,) * 8, H=16, Hkv=4,
+        d=64, depth=8,
+        description="bf16 chunked prefill: the last 1024 tokens of each of "
+                    "the 8 x 4096 prompts as one chunk against its 4096 "
+                    "keys (bottom-right causal), 16 diff heads, 4 KV heads, "
+                    "d=64"),
 }
 
 KV_HEADLINE = "decode_b64_kv8192"
