@@ -204,10 +204,13 @@ def bench_kv(args, name) -> int:
     lv = [c(x) for x in (inp.lq1, inp.lk1, inp.lq2, inp.lk2)]
     w, cq, ck = c(inp.w), c(inp.cu_q), c(inp.cu_k)
     out = torch.empty((wl.Tq, wl.H, 2 * wl.d), dtype=q.dtype, device=dev)
-    need = da.kv_workspace_size(wl.nseq, wl.max_q, wl.max_k, wl.H, wl.Hkv, wl.d)
-    # no workspace: a chunk that runs on the prefill kernel, bound by MFMA
-    # throughput rather than by reading the cache
-    chunk = need == 0
+    # the path the call takes: a chunk on the prefill kernel is bound by MFMA
+    # throughput rather than by reading the cache (and alone needs no
+    # workspace)
+    path = da.kv_path(wl.nseq, wl.max_q, wl.max_k, wl.H, wl.Hkv, wl.d, Tq=wl.Tq, Tk=wl.Tk)
+    chunk = path in (da.KV_PATH_PREFILL, da.KV_PATH_PREFILL_SPLIT)
+    need = (0 if path == da.KV_PATH_PREFILL
+            else da.kv_workspace_size(wl.nseq, wl.max_q, wl.max_k, wl.H, wl.Hkv, wl.d))
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
     stream = torch.cuda.Stream(dev)
     # --rope: a rotary decode step -- the step's new keys (and values) turned
@@ -296,7 +299,9 @@ def bench_kv(args, name) -> int:
                    "causal": wl.causal, "bytes_per_step": nbytes,
                    "tokens_per_s": round(wl.Tq / (ms * 1e-3), 1),
                    "tflops": round(tflops, 2), "gb_per_s": round(gbs, 1),
-                   "path": "one kernel (prefill)" if chunk else "split-KV + combine",
+                   "path": {da.KV_PATH_SPLIT_KV: "split-KV + combine",
+                            da.KV_PATH_PREFILL: "prefill kernel",
+                            da.KV_PATH_PREFILL_SPLIT: "prefill kernel on key splits + combine"}[path],
                    "workspace_bytes": need,
                    "launch": f"hip graph of {GRAPH_STEPS} steps" if graph is not None else "eager",
                    "wall_s_timed": round(wall, 4),

@@ -18,6 +18,8 @@ from typing import Optional
 import torch
 
 __all__ = ["fwd", "fwd_ptr", "fwd_workspace_size", "fwd_kv", "fwd_kv_ptr", "kv_workspace_size",
+           "kv_path", "KV_PATH_SPLIT_KV", "KV_PATH_PREFILL", "KV_PATH_PREFILL_SPLIT",
+           "fwd_kv_on_path_ptr", "kv_path_workspace_size",
            "fwd_kv_noalloc", "fwd_kv_noalloc_ptr", "KV_SCRATCH_BYTES",
            "fwd_train", "bwd", "bwd_workspace_size", "supported_bwd",
            "kv_append", "kv_append_ptr", "diff_attention", "DiffAttnFunction",
@@ -70,6 +72,10 @@ def library() -> ctypes.CDLL:
         i32, i32, i32, i32, vp, vp, i32, ctypes.c_int, vp, ctypes.c_size_t,
         vp, vp]
     lib.diffattn_fwd_kv.restype = ctypes.c_int
+    lib.diffattn_fwd_kv_on_path.argtypes = [ctypes.c_int] + lib.diffattn_fwd_kv.argtypes
+    lib.diffattn_fwd_kv_on_path.restype = ctypes.c_int
+    lib.diffattn_fwd_kv_path_workspace_size.argtypes = [ctypes.c_int] + [i32] * 6
+    lib.diffattn_fwd_kv_path_workspace_size.restype = ctypes.c_size_t
     lib.diffattn_fwd_kv_noalloc.argtypes = [
         ctypes.c_int, vp, vp, vp, f32p, f32p, f32p, f32p, i32, ctypes.c_float,
         f32p, ctypes.c_float, ctypes.c_int, i32p, i32p, i32, i32, i32, i32,
@@ -81,6 +87,8 @@ def library() -> ctypes.CDLL:
     lib.diffattn_kv_append.restype = ctypes.c_int
     lib.diffattn_fwd_kv_workspace_size.argtypes = [i32] * 6
     lib.diffattn_fwd_kv_workspace_size.restype = ctypes.c_size_t
+    lib.diffattn_fwd_kv_path.argtypes = [i32] * 8
+    lib.diffattn_fwd_kv_path.restype = ctypes.c_int
     lib.diffattn_supported_kv.argtypes = [ctypes.c_int, ctypes.c_int]
     lib.diffattn_supported_kv.restype = ctypes.c_int
     lib.diffattn_check_cu_seqlens_kv.argtypes = [
@@ -165,6 +173,23 @@ def kv_workspace_size(nseq: int, max_seqlen_q: int, max_seqlen_k: int,
         int(d)))
 
 
+# the kernels fwd_kv runs (kv_path)
+KV_PATH_SPLIT_KV = 0       # split-KV partial kernel + combine kernel
+KV_PATH_PREFILL = 1        # the prefill kernel alone (no workspace)
+KV_PATH_PREFILL_SPLIT = 2  # the prefill kernel on key splits + combine kernel
+
+
+def kv_path(nseq: int, max_seqlen_q: int, max_seqlen_k: int, H: int, Hkv: int,
+            d: int, Tq: Optional[int] = None, Tk: Optional[int] = None) -> int:
+    """Which kernels ``fwd_kv`` runs for these bounds and totals (KV_PATH_*;
+    -1: sizes rejected).  Tq and Tk default to nseq equal sequences."""
+    Tq = nseq * max_seqlen_q if Tq is None else Tq
+    Tk = nseq * max_seqlen_k if Tk is None else Tk
+    return int(library().diffattn_fwd_kv_path(
+        int(nseq), int(max_seqlen_q), int(max_seqlen_k), int(Tq), int(Tk), int(H), int(Hkv),
+        int(d)))
+
+
 def fwd_kv_ptr(dtype: int, q: int, k: int, v: int, lq1: int, lk1: int,
                lq2: int, lk2: int, lambda_stride: int,
                lambda_init_value: float, subln_weight: int, eps: float,
@@ -183,6 +208,35 @@ def fwd_kv_ptr(dtype: int, q: int, k: int, v: int, lq1: int, lk1: int,
         int(Tq), int(Tk), int(H), int(Hkv), int(d), rope_cos or None,
         rope_sin or None, int(rope_len), int(rope_dtype), workspace or None,
         int(workspace_bytes), out or None, stream or None)
+
+
+def fwd_kv_on_path_ptr(path: int, dtype: int, q: int, k: int, v: int, lq1: int, lk1: int,
+                       lq2: int, lk2: int, lambda_stride: int,
+                       lambda_init_value: float, subln_weight: int, eps: float,
+                       causal: int, cu_seqlens_q: int, cu_seqlens_k: int, nseq: int,
+                       max_seqlen_q: int, max_seqlen_k: int, Tq: int, Tk: int, H: int,
+                       Hkv: int, d: int, rope_cos: int, rope_sin: int, rope_len: int,
+                       rope_dtype: int, workspace: int, workspace_bytes: int,
+                       out: int, stream: int) -> int:
+    """diffattn_fwd_kv_on_path on integer device addresses; returns the
+    status."""
+    return library().diffattn_fwd_kv_on_path(
+        int(path), int(dtype), q or None, k or None, v or None, lq1 or None, lk1 or None,
+        lq2 or None, lk2 or None, int(lambda_stride), float(lambda_init_value),
+        subln_weight or None, float(eps), int(causal), cu_seqlens_q or None,
+        cu_seqlens_k or None, int(nseq), int(max_seqlen_q), int(max_seqlen_k),
+        int(Tq), int(Tk), int(H), int(Hkv), int(d), rope_cos or None,
+        rope_sin or None, int(rope_len), int(rope_dtype), workspace or None,
+        int(workspace_bytes), out or None, stream or None)
+
+
+def kv_path_workspace_size(path: int, nseq: int, max_seqlen_q: int, max_seqlen_k: int,
+                           H: int, Hkv: int, d: int) -> int:
+    """Bytes of device workspace ``fwd_kv(path=...)`` needs (0: path 1, or
+    sizes rejected)."""
+    return int(library().diffattn_fwd_kv_path_workspace_size(
+        int(path), int(nseq), int(max_seqlen_q), int(max_seqlen_k), int(H), int(Hkv),
+        int(d)))
 
 
 def fwd_kv_noalloc_ptr(dtype: int, q: int, k: int, v: int, lq1: int,
@@ -381,7 +435,7 @@ def fwd_kv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
            workspace: Optional[torch.Tensor] = None,
            out: Optional[torch.Tensor] = None,
            stream: Optional[torch.cuda.Stream] = None,
-           rope: Optional[tuple] = None) -> torch.Tensor:
+           rope: Optional[tuple] = None, path: Optional[int] = None) -> torch.Tensor:
     """New queries against a key/value cache on the GPU (bottom-right causal).
 
     q [Tq, H, 2, d]; k [Tk, Hkv, 2, d], v [Tk, Hkv, 2d] (bf16); lambda
@@ -390,16 +444,17 @@ def fwd_kv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     sequences).  When the bounds are not given they are read back from the
     device (a synchronising copy).  ``workspace`` is a device uint8 tensor of
     at least ``kv_workspace_size(...)`` bytes; one is allocated through
-    torch when it is None and that size is not 0 (it is 0 for long query
-    chunks, which run in one kernel).  ``rope`` = (cos, sin) device tables [len, d/2]
+    torch when it is None and the call needs one (``kv_path``: not on the
+    prefill kernel alone).  ``rope`` = (cos, sin) device tables [len, d/2]
     (fp32 or bf16) rotates each new query at its absolute position
     nk - nq + i; the cached keys are taken as already rotated (``kv_append``
-    writes them so).  Returns ``out`` [Tq, H, 2d].
+    writes them so).  ``path`` (KV_PATH_*) runs those kernels instead of the
+    library's choice (diffattn_fwd_kv_on_path).  Returns ``out`` [Tq, H, 2d].
     """
     return _kv_call(q, k, v, (lambda_q1, lambda_k1, lambda_q2, lambda_k2),
                     lambda_init, subln_weight, eps, causal, cu_seqlens_q,
                     cu_seqlens_k, max_seqlen_q, max_seqlen_k, nseq, out,
-                    stream, workspace, noalloc=False, rope=rope)
+                    stream, workspace, noalloc=False, rope=rope, path=path)
 
 
 def fwd_kv_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
@@ -428,7 +483,7 @@ def fwd_kv_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
 
 def _kv_call(q, k, v, lvs, lambda_init, subln_weight, eps, causal,
              cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, nseq,
-             out, stream, workspace, noalloc, rope=None):
+             out, stream, workspace, noalloc, rope=None, path=None):
     if q.dim() != 4 or q.shape[2] != 2:
         raise ValueError("q must be [Tq, H, 2, d]")
     Tq, H, _, d = q.shape
@@ -469,11 +524,20 @@ def _kv_call(q, k, v, lvs, lambda_init, subln_weight, eps, causal,
         nseq = 1 if nseq is None else int(nseq)
         max_seqlen_q = Tq // nseq if nseq > 0 else 0
         max_seqlen_k = Tk // nseq if nseq > 0 else 0
-    if not noalloc:
+    if not noalloc and path is not None:
+        need = kv_path_workspace_size(path, nseq, max(max_seqlen_q, 1),
+                                      max(max_seqlen_k, 1), H, Hkv, d)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        ws_ptr = 0 if workspace is None else _dev(workspace, "workspace", dev)
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    elif not noalloc:
         need = kv_workspace_size(nseq, max(max_seqlen_q, 1),
                                  max(max_seqlen_k, 1), H, Hkv, d)
-        if workspace is None and need == 0:
-            ws_ptr, ws_bytes = 0, 0      # the one-kernel path: no workspace
+        if workspace is None and (need == 0 or kv_path(
+                nseq, max(max_seqlen_q, 1), max(max_seqlen_k, 1), H, Hkv, d,
+                max(Tq, 1), max(Tk, 1)) == KV_PATH_PREFILL):
+            ws_ptr, ws_bytes = 0, 0      # the prefill kernel alone: no workspace
         else:
             if workspace is None:
                 workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -493,11 +557,15 @@ def _kv_call(q, k, v, lvs, lambda_init, subln_weight, eps, causal,
     with torch.cuda.device(dev):
         if noalloc:
             st = fwd_kv_noalloc_ptr(*common, out_ptr, stream.cuda_stream)
+        elif path is not None:
+            st = fwd_kv_on_path_ptr(path, *common, ws_ptr, ws_bytes, out_ptr,
+                                    stream.cuda_stream)
         else:
             st = fwd_kv_ptr(*common, ws_ptr, ws_bytes, out_ptr,
                             stream.cuda_stream)
     if st != OK:
         raise DiffAttnError(st, "diffattn_fwd_kv_noalloc" if noalloc
+                            else "diffattn_fwd_kv_on_path" if path is not None
                             else "diffattn_fwd_kv")
     return out
 

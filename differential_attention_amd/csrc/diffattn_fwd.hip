@@ -70,6 +70,8 @@
 // first) so the causal tail is short.
 
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #include <math.h>
 #include <stdint.h>
 
@@ -87,6 +89,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 8;    // two maps x four slots
 constexpr int kCUs = 256;    // compute units of the part
+constexpr float kUnseen = 1e30f;   // floor of a key split's running maximum
 constexpr int kSlots = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -300,6 +303,13 @@ struct Params {
     // the keys' own boundaries, or NULL with klen_uniform keys per sequence
     const int32_t *cuk;
     int32_t klen_uniform;
+    // key splits of a chunk (ck > 0): the grid's first index runs over
+    // nslots split slots (sequence s owns ceil(nk_s / ck) consecutive ones),
+    // and each workgroup writes its rows' partial (maximum in log2 units,
+    // sum, unnormalised O) per map to ws_ml [slot][Hkv][rmax][4] and ws_o
+    // [slot][Hkv][rmax][2][2d] for a merge kernel, row r = i G + gh
+    float *ws_o, *ws_ml;
+    int32_t ck, nslots, rmax;
     const void *rcos, *rsin;    // rotary tables [len][d/2] (fp32 or bf16), or NULL
     int32_t rope_dtype;         // element type of the tables
     const void *k_orig;         // unrotated K when rcos is set (k is then its rotated copy)
@@ -315,6 +325,43 @@ struct Params {
     int32_t hblocks;   // head blocks per KV group: G / hpw
     int32_t sub;       // 32-query sub-blocks per wave (the kernel's SUB)
 };
+
+// Split slot j of a chunk with key splits: its sequence and the sequence's
+// first slot, or false past the last split.  The slots of all sequences
+// share one index space (sequence s owns ceil(nk_s / ck) consecutive ones),
+// found with a wave-wide scan of the key boundaries, 64 sequences per step.
+__device__ inline bool chunk_split_owner(const Params &p, int j, int lane, int &s, int &base)
+{
+    if (!p.cuk) {
+        const int cnt = (p.klen_uniform + p.ck - 1) / p.ck;
+        if (cnt == 0 || j >= cnt * p.nseq)
+            return false;
+        s = j / cnt;
+        base = s * cnt;
+        return true;
+    }
+    int run = 0;
+    for (int s0 = 0; s0 < p.nseq; s0 += 64) {
+        const int si = s0 + lane;
+        const int cnt = si < p.nseq ? (p.cuk[si + 1] - p.cuk[si] + p.ck - 1) / p.ck : 0;
+        int incl = cnt;   // inclusive prefix over the lanes
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int t = __shfl_up(incl, off, 64);
+            if (lane >= off)
+                incl += t;
+        }
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(j >= run + incl - cnt && j < run + incl);
+        if (hit) {
+            const int l = __builtin_ctzll(hit);
+            s = s0 + l;
+            base = run + __builtin_amdgcn_readlane(incl - cnt, l);
+            return true;
+        }
+        run += __builtin_amdgcn_readlane(incl, 63);
+    }
+    return false;
+}
 
 // Every CU runs one workgroup of 8 waves (two per SIMD); the register
 // budget per lane is the 256 that two waves per SIMD leave.  SUB: 32-query
@@ -360,14 +407,25 @@ void diffattn_fwd_kernel(Params p)
     const int map = wave / kSlots;     // 0: map 1 (Q1, K1), 1: map 2 (Q2, K2)
 
     // ---- tile scheduler: longest query tiles first ------------------------
-    const int pairs = p.nseq * p.Hkv * p.hblocks;
+    // (units: sequences, or a chunk's key splits)
+    const int units = CHUNK ? p.nslots : p.nseq;
+    const int pairs = units * p.Hkv * p.hblocks;
     const int id = blockIdx.x;
     const int t = p.ntile_q - 1 - id / pairs;
     const int rem = id % pairs;
-    const int seq = rem / (p.Hkv * p.hblocks);
+    const int unit = rem / (p.Hkv * p.hblocks);
     const int grp = rem % (p.Hkv * p.hblocks);
     const int g = grp / p.hblocks;
     const int hb = grp % p.hblocks;
+    int seq = unit, split = 0;
+    if constexpr (CHUNK) {
+        if (p.ck > 0) {
+            int base = 0;
+            if (!chunk_split_owner(p, unit, lane, seq, base))
+                return;   // past the last split
+            split = unit - base;
+        }
+    }
 
     int s0, s1;                          // the sequence's query rows
     if (p.cu) {
@@ -392,6 +450,16 @@ void diffattn_fwd_kernel(Params p)
             return;   // queries without keys: a broken precondition
     }
     const int dk = CHUNK ? ks1 - s1 : 0;
+    // this workgroup's keys [kr0, kr1): the sequence's, or one split of them
+    int kr0 = ks0, kr1 = ks1;
+    if constexpr (CHUNK) {
+        if (p.ck > 0) {
+            kr0 = ks0 + split * p.ck;
+            kr1 = min(kr0 + p.ck, ks1);
+            if (kr0 >= ks1)
+                return;
+        }
+    }
     // rotary position of query row tq: its key's index in the sequence
     // (clamped at 0 for chunks longer than their keys, a broken precondition
     // of rotary chunks that must still read inside the tables)
@@ -492,12 +560,12 @@ void diffattn_fwd_kernel(Params p)
     u32x4 kst[MAXL], vst[MAXL];
     // global -> registers: this wave's loads of block slice b of the tile at k0
     auto stage_load = [&](int k0, int b) __attribute__((always_inline)) {
-        const bool tail = k0 + GEO::BN > ks1;
+        const bool tail = k0 + GEO::BN > kr1;
 #pragma unroll
         for (int i = b * LPW / GEO::NB; i < (b + 1) * LPW / GEO::NB; ++i) {
             int key = k0 + lrow + i * kWaves * RPL;
-            if (tail)   // rows past the sequence repeat its last row
-                key = min(key, ks1 - 1);
+            if (tail)   // rows past the key range repeat its last row
+                key = min(key, kr1 - 1);
             const int64_t off = (int64_t)key * rowstride;
             kst[i - b * LPW / GEO::NB] = *(const u32x4 *)(kbytes + off);
             vst[i - b * LPW / GEO::NB] = *(const u32x4 *)(vbytes + off);
@@ -521,15 +589,18 @@ void diffattn_fwd_kernel(Params p)
     f32x16 o[kSub][NDB];
 #pragma unroll
     for (int u = 0; u < kSub; ++u) {
-        m_run[u] = -INFINITY;
+        // (a key split can hold no key of a row: a finite floor keeps its
+        // probabilities 0 instead of exp2(-inf + inf), and the first visible
+        // key still overflows the lazy test and raises the maximum)
+        m_run[u] = CHUNK ? -kUnseen : -INFINITY;
         l_run[u] = 0.f;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
             o[u][db] = f32x16{};
     }
 
-    const int kv_end = p.causal ? qhi + dk : ks1;
-    const int ntiles = (kv_end - ks0 + GEO::BN - 1) / GEO::BN;
+    const int kv_end = p.causal ? (CHUNK ? min(qhi + dk, kr1) : qhi) : kr1;
+    const int ntiles = (kv_end - kr0 + GEO::BN - 1) / GEO::BN;   // (<= 0: none visible)
 
     // lambda of this head (needed by the map-2 waves in the epilogue); its
     // loads travel with the first tile's.  The butterfly leaves every lane
@@ -555,12 +626,12 @@ void diffattn_fwd_kernel(Params p)
     // write (slice by slice, each write would wait for its own load)
     {
         u32x4 k0v[LPW], v0v[LPW];
-        const bool tail = ks0 + GEO::BN > ks1;
+        const bool tail = kr0 + GEO::BN > kr1;
 #pragma unroll
         for (int i = 0; i < LPW; ++i) {
-            int key = ks0 + lrow + i * kWaves * RPL;
-            if (tail)   // rows past the sequence repeat its last row
-                key = min(key, ks1 - 1);
+            int key = kr0 + lrow + i * kWaves * RPL;
+            if (tail)   // rows past the key range repeat its last row
+                key = min(key, kr1 - 1);
             const int64_t off = (int64_t)key * rowstride;
             k0v[i] = *(const u32x4 *)(kbytes + off);
             v0v[i] = *(const u32x4 *)(vbytes + off);
@@ -599,7 +670,7 @@ void diffattn_fwd_kernel(Params p)
     };
     // One tile: compute from `cur` while the next tile is staged into `nxt`.
     auto tile = [&](int it, const char *cur, char *nxt) __attribute__((always_inline)) {
-        const int k0 = ks0 + it * GEO::BN;
+        const int k0 = kr0 + it * GEO::BN;
         const char *kt = cur + k_lane;
         const bool more = it + 1 < ntiles;
 #pragma unroll
@@ -617,8 +688,8 @@ void diffattn_fwd_kernel(Params p)
             const int kb0 = k0 + 32 * b;
             // wave-uniform: can this wave see any key of the block, and does
             // any key need the index mask?
-            if (!(kb0 >= ks1 || (p.causal && kb0 > wq_last + dk))) {
-            const bool masked = kb0 + 32 > ks1 || (p.causal && kb0 + 31 > wq0 + dk);
+            if (!(kb0 >= kr1 || (p.causal && kb0 > wq_last + dk))) {
+            const bool masked = kb0 + 32 > kr1 || (p.causal && kb0 + 31 > wq0 + dk);
             // ---- S^T = K Q^T ------------------------------------------------
             Frag ka[NKS];
 #pragma unroll
@@ -638,10 +709,10 @@ void diffattn_fwd_kernel(Params p)
                 for (int u = 0; u < kSub; ++u) {
                     // wave-uniform: does this sub-block straddle the diagonal
                     // or the end of the sequence?
-                    if (kb0 + 32 > ks1 || (p.causal && kb0 + 31 > wq0 + dk + 32 * u)) {
+                    if (kb0 + 32 > kr1 || (p.causal && kb0 + 31 > wq0 + dk + 32 * u)) {
                         // key kb0 + acc_row(a, h) is visible iff its offset
                         // acc_row(a, 0) is at most lim (one compare per key)
-                        int lim = ks1 - 1 - kb0;
+                        int lim = kr1 - 1 - kb0;
                         if (p.causal)
                             lim = min(lim, wq0 + dk + 32 * u + n - kb0);
                         lim -= 4 * h;
@@ -655,7 +726,8 @@ void diffattn_fwd_kernel(Params p)
 
             // ---- online softmax with a lazily raised maximum ---------------
             // (a query row whose keys of this block are all masked keeps its
-            // maximum: its first block always has a visible key)
+            // maximum: its first block always has a visible key, except in a
+            // key split, where the maximum starts at the finite floor)
 #pragma unroll
             for (int u = 0; u < kSub; ++u) {
                 // the row maximum of the block, then a raised running maximum
@@ -767,6 +839,32 @@ void diffattn_fwd_kernel(Params p)
 #pragma unroll
     for (int u = 0; u < kSub; ++u)
         lsum[u] = pair_sum(l_run[u]);
+    if constexpr (CHUNK) {
+        if (p.ws_o) {
+            // key split: this map's partial per row for the merge (a row that
+            // saw no key of the split leaves the floor, a zero sum and zeros)
+            const int G = p.H / p.Hkv;
+#pragma unroll
+            for (int u = 0; u < kSub; ++u) {
+                const int tq = wq0 + 32 * u + n;
+                if (tq >= s1 || tq - s0 >= p.max_seqlen)
+                    continue;
+                const int64_t r = (int64_t)(tq - s0) * G + (head - g * G);
+                const int64_t row = ((int64_t)unit * p.Hkv + g) * p.rmax + r;
+                float *dst = p.ws_o + (row * 2 + map) * (2 * D);
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        *(float4 *)(dst + 32 * db + 8 * i + 4 * h) =
+                            make_float4(o[u][db][4 * i], o[u][db][4 * i + 1], o[u][db][4 * i + 2],
+                                        o[u][db][4 * i + 3]);
+                if (h == 0)
+                    *(float2 *)(p.ws_ml + row * 4 + 2 * map) = make_float2(m_run[u] * c, lsum[u]);
+            }
+            return;
+        }
+    }
     if (p.lse) {
         // training forward: each map's log2-sum-exp of the scaled scores and
         // its normalised output, for the backward pass
@@ -1132,6 +1230,10 @@ int fwd_impl(int dtype, const void *q, const void *k, const void *v,
     p.cu = cu_seqlens;
     p.cuk = nullptr;
     p.klen_uniform = 0;
+    p.ws_o = p.ws_ml = nullptr;
+    p.ck = 0;
+    p.nslots = nseq;
+    p.rmax = 0;
     p.rcos = rope_cos;
     p.rsin = rope_sin;
     p.rope_dtype = rope_dtype;
@@ -1159,19 +1261,59 @@ int fwd_impl(int dtype, const void *q, const void *k, const void *v,
 
 } // namespace
 
-double diffattn_chunk_prefill_us(int32_t nseq, int32_t max_seqlen_q, int32_t max_seqlen_k,
-                                 int32_t H, int32_t Hkv)
+int diffattn_chunk_plan(int32_t nseq, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t H,
+                        int32_t Hkv, int32_t d, int splits, DiffattnChunkPlan *plan)
 {
     int hpw = 0, sub = 0;
     int64_t ntile_q = 0, nblocks = 0;
-    if (!grid_shape(max_seqlen_q, nseq, H, Hkv, hpw, sub, ntile_q, nblocks))
-        return INFINITY;
-    // one workgroup per CU at a time; a workgroup takes about 24 ns per key
-    // with 32-query sub-blocks and 47 ns with 64 (measured, d = 64, keys of
-    // one sequence streaming through a 128-key tile)
-    const double ns_per_key = sub == 2 ? 47.0 : 24.0;
-    const int64_t rounds = (nblocks + kCUs - 1) / kCUs;
-    return 1e-3 * ns_per_key * (double)rounds * (double)max_seqlen_k;
+    if (nseq < 1 || max_seqlen_q < 1 || max_seqlen_k < 1 ||
+        !grid_shape(max_seqlen_q, nseq, H, Hkv, hpw, sub, ntile_q, nblocks))
+        return 0;
+    const int64_t per_unit = nblocks / nseq;   // workgroups per sequence or split
+    const int64_t rmax = (int64_t)(H / Hkv) * max_seqlen_q;
+    // Estimated duration with units of ck keys each (sequences, or splits):
+    // rounds of at most one workgroup per CU, each as long as a workgroup
+    // streaming ck keys, plus, for splits, the merge kernel.  The constants
+    // are fitted to measured calls on this part (d = 64; d = 32 about 0.72
+    // of the per-key time): per key 21 ns with 32-query sub-blocks and 27
+    // with 64, 48% more when every CU is busy (the clock under load), 7 us
+    // per round, and the merge 0.46 us per MB of partials plus 8 us.
+    const double fd = d == 32 ? 0.72 : 1.0;
+    const double ns_per_key = (sub == 2 ? 26.9 : 21.1) * fd;
+    auto estimate = [&](int64_t blocks, int64_t keys, size_t ws_bytes) {
+        const double occ = (double)std::min<int64_t>(blocks, kCUs) / kCUs;
+        double us = (double)((blocks + kCUs - 1) / kCUs) *
+                    (1e-3 * ns_per_key * (double)keys * (1.0 + 0.48 * occ) + 7.0);
+        if (ws_bytes)
+            us += 0.46e-6 * (double)ws_bytes + 8.0;
+        return us;
+    };
+    DiffattnChunkPlan pl{};
+    pl.rmax = (int32_t)std::min<int64_t>(rmax, INT32_MAX);
+    pl.nslots = nseq;
+    pl.est_us = splits == 2 ? INFINITY : estimate(nblocks, max_seqlen_k, 0);
+    // key splits of 256, 512, 1024, ... keys (whole 128-key tiles), the
+    // cheapest estimate winning
+    for (int64_t ck = 256; splits && ck < max_seqlen_k; ck *= 2) {
+        const int64_t slots = (int64_t)nseq * ((max_seqlen_k + ck - 1) / ck);
+        const int64_t rows = slots * Hkv * rmax;
+        if (slots > INT32_MAX || per_unit * slots > INT32_MAX || rmax > (1 << 24) ||
+            rows > ((int64_t)1 << 36))
+            continue;
+        const size_t ws_o = (size_t)rows * 2 * (2 * d) * 4, ws_ml = (size_t)rows * 4 * 4;
+        const double us = estimate(per_unit * slots, ck, ws_o + ws_ml);
+        if (us < pl.est_us) {
+            pl.ck = (int32_t)ck;
+            pl.nslots = (int32_t)slots;
+            pl.ws_o_bytes = ws_o;
+            pl.ws_ml_bytes = ws_ml;
+            pl.est_us = us;
+        }
+    }
+    if (splits == 2 && pl.ck == 0)
+        return 0;   // no split fits
+    *plan = pl;
+    return 1;
 }
 
 int diffattn_chunk_prefill(const void *q, const void *k, const void *v, const float *lambda_q1,
@@ -1181,13 +1323,19 @@ int diffattn_chunk_prefill(const void *q, const void *k, const void *v, const fl
                            const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
                            int32_t nseq, int32_t max_seqlen_q, int32_t Tq, int32_t Tk, int32_t H,
                            int32_t Hkv, int32_t d, const void *rope_cos, const void *rope_sin,
-                           int rope_dtype, void *out, void *stream)
+                           int rope_dtype, const DiffattnChunkPlan *plan, float *ws_o,
+                           float *ws_ml, void *out, void *stream)
 {
     if (d != 64 && d != 32)
         return DIFFATTN_EUNSUPPORTED;
+    // (the grid's first index runs over the split slots, or the sequences)
+    const int units = plan->ck > 0 ? plan->nslots : nseq;
     int hpw = 0, sub = 0;
     int64_t ntile_q = 0, nblocks = 0;
     if (!grid_shape(max_seqlen_q, nseq, H, Hkv, hpw, sub, ntile_q, nblocks))
+        return DIFFATTN_EINVAL;
+    nblocks = nblocks / nseq * units;
+    if (nblocks > INT32_MAX)
         return DIFFATTN_EINVAL;
     Params p;
     p.q = q;
@@ -1204,6 +1352,11 @@ int diffattn_chunk_prefill(const void *q, const void *k, const void *v, const fl
     p.cu = cu_seqlens_q;
     p.cuk = cu_seqlens_k;
     p.klen_uniform = cu_seqlens_q ? 0 : Tk / nseq;
+    p.ck = plan->ck;
+    p.nslots = units;
+    p.rmax = plan->rmax;
+    p.ws_o = plan->ck > 0 ? ws_o : nullptr;
+    p.ws_ml = plan->ck > 0 ? ws_ml : nullptr;
     p.rcos = rope_cos;
     p.rsin = rope_sin;
     p.rope_dtype = rope_dtype;

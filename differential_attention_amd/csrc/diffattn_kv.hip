@@ -619,24 +619,56 @@ struct KvPlan {
 
 constexpr int64_t kTargetWaves = 1024;
 
-// Long query chunks (chunked prefill, a context-parallel shard) run on the
-// prefill kernel, which reads each key tile once for 32 or 64 query rows of
-// four heads, when its estimated time beats the split-KV pair's.  The pair
-// costs about 4.3 ps per (query row x key) once rows outnumber what one K/V
-// read can feed, plus about 10 us of fixed cost (measured, d = 64, against
-// caches of 2048 to 32768 keys).  The sizes are taken as uniform (nseq
-// sequences of max_seqlen_q queries and max_seqlen_k keys), so the choice,
-// like the split plan, depends on the bounds alone.  Below 32 rows the pair
-// always wins.
-constexpr int kChunkMinRows = 32;
+// Long query chunks (chunked prefill, a context-parallel shard, many
+// speculative tokens) run on the prefill kernel, which reads each key tile
+// once for 32 or 64 query rows of up to four heads -- over the sequences'
+// whole key ranges, or over key splits whose partials the combine kernel
+// below merges -- when its estimated time beats the split-KV pair's.  The
+// prefill plan (split size and estimate) depends on the bounds alone,
+// taken as uniform sequences; the pair's estimate uses the totals Tq and Tk
+// too, since its time follows the keys actually cached: about 3.6 ps per
+// (query row x head x key) at d = 64, 0.26 us per MB of K/V, 0.12 us per
+// split of a row and 6.3 us (fitted to measured calls on this part).
+// Below kChunkMinRows query rows per sequence the pair always runs.
+constexpr int kChunkMinRows = 4;
 
-bool use_chunk(int nseq, int max_q, int max_k, int H, int Hkv, int d)
+enum KvPath { kPathSplitKv = 0, kPathChunk = 1, kPathChunkSplit = 2 };
+
+// Tk < 0: the workspace bound only (ck left 0)
+bool make_plan(int nseq, int max_q, int max_k, int G, int Hkv, int d, int64_t Tk, KvPlan &pl);
+
+double split_kv_us(int nseq, int max_q, int max_k, int64_t Tq, int64_t Tk, int H, int Hkv,
+                   int d)
+{
+    KvPlan pl;
+    if (!make_plan(nseq, max_q, max_k, H / Hkv, Hkv, d, Tk, pl))
+        return INFINITY;
+    const double rowkeys = (double)H * std::min((double)max_q * Tk, (double)Tq * max_k);
+    const double kv_mb = (double)Tk * Hkv * 4 * d * 2 / 1e6;
+    const int splits = (max_k + pl.ck - 1) / pl.ck;
+    return 3.62e-6 * rowkeys * d / 64 + 0.262 * kv_mb + 0.119 * splits + 6.3;
+}
+
+// The path of a call with these bounds and totals (Tq, Tk < 0: taken as
+// uniform); cp receives the prefill plan when a prefill path wins.
+int kv_path(int nseq, int max_q, int max_k, int64_t Tq, int64_t Tk, int H, int Hkv, int d,
+            DiffattnChunkPlan *cp)
 {
     if (max_q < kChunkMinRows || nseq < 1 || max_k < 1 || H < 1 || Hkv < 1 || H % Hkv != 0 ||
         !diffattn_supported_kv(DIFFATTN_BF16, d))
-        return false;
-    const double split_us = 4.3e-6 * H * (double)max_q * (double)nseq * (double)max_k + 10.0;
-    return diffattn_chunk_prefill_us(nseq, max_q, max_k, H, Hkv) < split_us;
+        return kPathSplitKv;
+    DiffattnChunkPlan pl;
+    if (!diffattn_chunk_plan(nseq, max_q, max_k, H, Hkv, d, 1, &pl))
+        return kPathSplitKv;
+    if (Tq < 0 || Tk < 0) {
+        Tq = (int64_t)nseq * max_q;
+        Tk = (int64_t)nseq * max_k;
+    }
+    if (!(pl.est_us < split_kv_us(nseq, max_q, max_k, Tq, Tk, H, Hkv, d)))
+        return kPathSplitKv;
+    if (cp)
+        *cp = pl;
+    return pl.ck > 0 ? kPathChunkSplit : kPathChunk;
 }
 
 // Tk < 0: the workspace bound only (ck left 0)
@@ -703,18 +735,32 @@ extern "C" int diffattn_check_cu_seqlens_kv(const int32_t *host_cu_q, const int3
     return DIFFATTN_OK;
 }
 
+extern "C" int diffattn_fwd_kv_path(int32_t nseq, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                    int32_t Tq, int32_t Tk, int32_t H, int32_t Hkv, int32_t d)
+{
+    if (nseq < 1 || max_seqlen_q < 1 || max_seqlen_k < 1 || Tq < 1 || Tk < 1 || H < 1 ||
+        Hkv < 1 || H % Hkv != 0 || !diffattn_supported_kv(DIFFATTN_BF16, d))
+        return -1;
+    return kv_path(nseq, max_seqlen_q, max_seqlen_k, Tq, Tk, H, Hkv, d, nullptr);
+}
+
 extern "C" size_t diffattn_fwd_kv_workspace_size(int32_t nseq, int32_t max_seqlen_q,
                                                  int32_t max_seqlen_k, int32_t H, int32_t Hkv,
                                                  int32_t d)
 {
     if (H < 1 || Hkv < 1 || H % Hkv != 0 || d < 1)
         return 0;
-    if (use_chunk(nseq, max_seqlen_q, max_seqlen_k, H, Hkv, d))
-        return 0;   // the prefill kernel: no workspace
     KvPlan pl;
     if (!make_plan(nseq, max_seqlen_q, max_seqlen_k, H / Hkv, Hkv, d, -1, pl))
         return 0;
-    return pl.ws_o_bytes + pl.ws_ml_bytes;
+    size_t need = pl.ws_o_bytes + pl.ws_ml_bytes;
+    // (a call within these bounds may take the prefill kernel on key splits
+    // instead, whose plan depends on the bounds alone)
+    DiffattnChunkPlan cp;
+    if (max_seqlen_q >= kChunkMinRows && diffattn_supported_kv(DIFFATTN_BF16, d) &&
+        diffattn_chunk_plan(nseq, max_seqlen_q, max_seqlen_k, H, Hkv, d, 1, &cp) && cp.ck > 0)
+        need = std::max(need, cp.ws_o_bytes + cp.ws_ml_bytes);
+    return need;
 }
 
 namespace {
@@ -744,8 +790,10 @@ int kv_impl(int dtype, const void *q, const void *k, const void *v,
             const int32_t *cu_seqlens_k, int32_t nseq, int32_t max_seqlen_q,
             int32_t max_seqlen_k, int32_t Tq, int32_t Tk, int32_t H, int32_t Hkv, int32_t d,
             const void *rope_cos, const void *rope_sin, int32_t rope_len, int rope_dtype,
-            GetWs get_ws, void *out, void *stream)
+            int force_path, GetWs get_ws, void *out, void *stream)
 {
+    if (force_path < -1 || force_path > kPathChunkSplit)
+        return DIFFATTN_EINVAL;
     if (dtype != DIFFATTN_BF16 && dtype != DIFFATTN_F32)
         return DIFFATTN_EINVAL;
     if (Tq < 0 || Tk < 0 || H < 1 || Hkv < 1 || d < 1 || H % Hkv != 0 || nseq < 1)
@@ -788,21 +836,7 @@ int kv_impl(int dtype, const void *q, const void *k, const void *v,
     // the tables cover every position a new query can have (< nk)
     if (rope_cos && (rope_len < max_seqlen_k || !aligned16(rope_cos) || !aligned16(rope_sin)))
         return DIFFATTN_EINVAL;
-    // long query chunks: the prefill kernel, with no split and no workspace
-    if (use_chunk(nseq, max_seqlen_q, max_seqlen_k, H, Hkv, d))
-        return diffattn_chunk_prefill(q, k, v, lambda_q1, lambda_k1, lambda_q2, lambda_k2,
-                                      lambda_stride, lambda_init, subln_weight, eps, causal,
-                                      cu_seqlens_q, cu_seqlens_k, nseq, max_seqlen_q, Tq, Tk, H,
-                                      Hkv, d, rope_cos, rope_sin, rope_dtype, out, stream);
     const int G = H / Hkv;
-    KvPlan pl;
-    if (!make_plan(nseq, max_seqlen_q, max_seqlen_k, G, Hkv, d, Tk, pl))
-        return DIFFATTN_EINVAL;
-    void *workspace = nullptr;
-    const int wst = get_ws(pl.ws_o_bytes + pl.ws_ml_bytes, workspace);
-    if (wst != DIFFATTN_OK)
-        return wst;
-
     KvParams p;
     p.q = q;
     p.k = k;
@@ -816,8 +850,6 @@ int kv_impl(int dtype, const void *q, const void *k, const void *v,
     p.w = subln_weight;
     p.cuq = cu_seqlens_q;
     p.cuk = cu_seqlens_k;
-    p.ws_o = (float *)workspace;
-    p.ws_ml = (float *)((char *)workspace + pl.ws_o_bytes);
     p.rcos = rope_cos;
     p.rsin = rope_sin;
     p.rope_len = rope_cos ? rope_len : 1;
@@ -831,36 +863,96 @@ int kv_impl(int dtype, const void *q, const void *k, const void *v,
     p.qlen_uniform = cu_seqlens_q ? 0 : Tq / nseq;
     p.klen_uniform = cu_seqlens_q ? 0 : Tk / nseq;
     p.max_q = max_seqlen_q;
+    hipStream_t st = (hipStream_t)stream;
+    const int64_t waves2 = (int64_t)nseq * max_seqlen_q * H;   // combine: one wave per row
+    const int64_t blocks2 = (waves2 + kWavesPerBlock - 1) / kWavesPerBlock;
+    if (blocks2 > 0x7fffffff)
+        return DIFFATTN_EINVAL;
+    // merge the splits of every row: up to 32 per round when a row can have
+    // more than 16 (splits of ck keys of the longest cache)
+    auto combine = [&](int ck) {
+        const int64_t kmax = cu_seqlens_q ? max_seqlen_k : Tk / nseq;
+        const bool wide = (kmax + ck - 1) / ck > 16;
+        if (d == 64) {
+            if (wide)
+                hipLaunchKernelGGL((diffattn_kv_combine<64, 32>), dim3((unsigned)blocks2), dim3(kThreads), 0, st, p);
+            else
+                hipLaunchKernelGGL((diffattn_kv_combine<64, 16>), dim3((unsigned)blocks2), dim3(kThreads), 0, st, p);
+        } else {
+            if (wide)
+                hipLaunchKernelGGL((diffattn_kv_combine<32, 32>), dim3((unsigned)blocks2), dim3(kThreads), 0, st, p);
+            else
+                hipLaunchKernelGGL((diffattn_kv_combine<32, 16>), dim3((unsigned)blocks2), dim3(kThreads), 0, st, p);
+        }
+    };
+
+    // long query chunks: the prefill kernel, on whole key ranges (no
+    // workspace) or on key splits merged by the combine kernel
+    DiffattnChunkPlan cp;
+    int path = force_path;
+    if (path == -1) {
+        path = kv_path(nseq, max_seqlen_q, max_seqlen_k, Tq, Tk, H, Hkv, d, &cp);
+    } else if (path != kPathSplitKv) {
+        // (the grid of the prefill kernel must fit, and for splits, a split
+        // size must)
+        if (!diffattn_chunk_plan(nseq, max_seqlen_q, max_seqlen_k, H, Hkv, d,
+                                 path == kPathChunkSplit ? 2 : 0, &cp))
+            return DIFFATTN_EINVAL;
+    }
+    if (path != kPathSplitKv) {
+        void *workspace = nullptr;
+        if (path == kPathChunkSplit) {
+            const int wst = get_ws(cp.ws_o_bytes + cp.ws_ml_bytes, workspace);
+            if (wst == DIFFATTN_ETOOLARGE) {
+                // (only the static scratch refuses a size: run unsplit)
+                if (!diffattn_chunk_plan(nseq, max_seqlen_q, max_seqlen_k, H, Hkv, d, 0, &cp))
+                    return DIFFATTN_EINVAL;
+            } else if (wst != DIFFATTN_OK) {
+                return wst;
+            }
+        }
+        float *ws_o = (float *)workspace;
+        float *ws_ml = cp.ck > 0 ? (float *)((char *)workspace + cp.ws_o_bytes) : nullptr;
+        const int cst = diffattn_chunk_prefill(
+            q, k, v, lambda_q1, lambda_k1, lambda_q2, lambda_k2, lambda_stride, lambda_init,
+            subln_weight, eps, causal, cu_seqlens_q, cu_seqlens_k, nseq, max_seqlen_q, Tq, Tk,
+            H, Hkv, d, rope_cos, rope_sin, rope_dtype, &cp, ws_o, ws_ml, out, stream);
+        if (cst != DIFFATTN_OK || cp.ck == 0)
+            return cst;
+        p.ws_o = ws_o;
+        p.ws_ml = ws_ml;
+        p.rmax = cp.rmax;
+        p.nslots = cp.nslots;
+        p.ck = cp.ck;
+        p.nrb = 0;   // (the partial kernel's; unused by the combine)
+        combine(cp.ck);
+        return hipGetLastError() == hipSuccess ? DIFFATTN_OK : DIFFATTN_EHIP;
+    }
+
+    KvPlan pl;
+    if (!make_plan(nseq, max_seqlen_q, max_seqlen_k, G, Hkv, d, Tk, pl))
+        return DIFFATTN_EINVAL;
+    void *workspace = nullptr;
+    const int wst = get_ws(pl.ws_o_bytes + pl.ws_ml_bytes, workspace);
+    if (wst != DIFFATTN_OK)
+        return wst;
+    p.ws_o = (float *)workspace;
+    p.ws_ml = (float *)((char *)workspace + pl.ws_o_bytes);
     p.rmax = pl.rmax;
     p.nrb = pl.nrb;
     p.nslots = pl.nslots;
     p.ck = pl.ck;
-
-    hipStream_t st = (hipStream_t)stream;
     const int64_t waves1 = (int64_t)pl.nslots * Hkv * pl.nrb;
-    const int64_t waves2 = (int64_t)nseq * max_seqlen_q * H;
     const int64_t blocks1 = (waves1 + kWavesPerBlock - 1) / kWavesPerBlock;
-    const int64_t blocks2 = (waves2 + kWavesPerBlock - 1) / kWavesPerBlock;
-    if (blocks1 > 0x7fffffff || blocks2 > 0x7fffffff)
+    if (blocks1 > 0x7fffffff)
         return DIFFATTN_EINVAL;
-    // splits of the longest cache
-    const int64_t kmax = cu_seqlens_q ? max_seqlen_k : Tk / nseq;
-    const bool wide = (kmax + pl.ck - 1) / pl.ck > 16;
     const int rt = !rope_cos ? diffattn_rope::kOff
                              : (rope_dtype == DIFFATTN_BF16 ? diffattn_rope::kBF16 : diffattn_rope::kF32);
-    if (d == 64) {
+    if (d == 64)
         launch_partial<64>(rt, (unsigned)blocks1, st, p);
-        if (wide)
-            hipLaunchKernelGGL((diffattn_kv_combine<64, 32>), dim3((unsigned)blocks2), dim3(kThreads), 0, st, p);
-        else
-            hipLaunchKernelGGL((diffattn_kv_combine<64, 16>), dim3((unsigned)blocks2), dim3(kThreads), 0, st, p);
-    } else {
+    else
         launch_partial<32>(rt, (unsigned)blocks1, st, p);
-        if (wide)
-            hipLaunchKernelGGL((diffattn_kv_combine<32, 32>), dim3((unsigned)blocks2), dim3(kThreads), 0, st, p);
-        else
-            hipLaunchKernelGGL((diffattn_kv_combine<32, 16>), dim3((unsigned)blocks2), dim3(kThreads), 0, st, p);
-    }
+    combine(pl.ck);
     return hipGetLastError() == hipSuccess ? DIFFATTN_OK : DIFFATTN_EHIP;
 }
 
@@ -922,7 +1014,7 @@ extern "C" int diffattn_fwd_kv(int dtype, const void *q, const void *k, const vo
     return kv_impl(dtype, q, k, v, lambda_q1, lambda_k1, lambda_q2, lambda_k2, lambda_stride,
                    lambda_init, subln_weight, eps, causal, cu_seqlens_q, cu_seqlens_k, nseq,
                    max_seqlen_q, max_seqlen_k, Tq, Tk, H, Hkv, d, rope_cos, rope_sin, rope_len,
-                   rope_dtype, caller_ws, out, stream);
+                   rope_dtype, -1, caller_ws, out, stream);
 }
 
 extern "C" int diffattn_fwd_kv_noalloc(int dtype, const void *q, const void *k, const void *v,
@@ -947,7 +1039,55 @@ extern "C" int diffattn_fwd_kv_noalloc(int dtype, const void *q, const void *k, 
     return kv_impl(dtype, q, k, v, lambda_q1, lambda_k1, lambda_q2, lambda_k2, lambda_stride,
                    lambda_init, subln_weight, eps, causal, cu_seqlens_q, cu_seqlens_k, nseq,
                    max_seqlen_q, max_seqlen_k, Tq, Tk, H, Hkv, d, rope_cos, rope_sin, rope_len,
-                   rope_dtype, static_ws, out, stream);
+                   rope_dtype, -1, static_ws, out, stream);
+}
+
+extern "C" int diffattn_fwd_kv_on_path(int path, int dtype, const void *q, const void *k,
+                                       const void *v, const float *lambda_q1,
+                                       const float *lambda_k1, const float *lambda_q2,
+                                       const float *lambda_k2, int32_t lambda_stride,
+                                       float lambda_init, const float *subln_weight, float eps,
+                                       int causal, const int32_t *cu_seqlens_q,
+                                       const int32_t *cu_seqlens_k, int32_t nseq,
+                                       int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Tq,
+                                       int32_t Tk, int32_t H, int32_t Hkv, int32_t d,
+                                       const void *rope_cos, const void *rope_sin,
+                                       int32_t rope_len, int rope_dtype, void *workspace,
+                                       size_t workspace_bytes, void *out, void *stream)
+{
+    if (path < 0)
+        return DIFFATTN_EINVAL;
+    auto caller_ws = [&](size_t need, void *&ws) {
+        if (!workspace || !aligned16(workspace) || workspace_bytes < need)
+            return (int)DIFFATTN_EINVAL;
+        ws = workspace;
+        return (int)DIFFATTN_OK;
+    };
+    return kv_impl(dtype, q, k, v, lambda_q1, lambda_k1, lambda_q2, lambda_k2, lambda_stride,
+                   lambda_init, subln_weight, eps, causal, cu_seqlens_q, cu_seqlens_k, nseq,
+                   max_seqlen_q, max_seqlen_k, Tq, Tk, H, Hkv, d, rope_cos, rope_sin, rope_len,
+                   rope_dtype, path, caller_ws, out, stream);
+}
+
+extern "C" size_t diffattn_fwd_kv_path_workspace_size(int path, int32_t nseq,
+                                                      int32_t max_seqlen_q,
+                                                      int32_t max_seqlen_k, int32_t H,
+                                                      int32_t Hkv, int32_t d)
+{
+    if (nseq < 1 || max_seqlen_q < 1 || max_seqlen_k < 1 || H < 1 || Hkv < 1 || H % Hkv != 0 ||
+        !diffattn_supported_kv(DIFFATTN_BF16, d))
+        return 0;
+    if (path == kPathSplitKv) {
+        KvPlan pl;
+        if (!make_plan(nseq, max_seqlen_q, max_seqlen_k, H / Hkv, Hkv, d, -1, pl))
+            return 0;
+        return pl.ws_o_bytes + pl.ws_ml_bytes;
+    }
+    DiffattnChunkPlan cp;
+    if (path == kPathChunkSplit &&
+        diffattn_chunk_plan(nseq, max_seqlen_q, max_seqlen_k, H, Hkv, d, 2, &cp))
+        return cp.ws_o_bytes + cp.ws_ml_bytes;
+    return 0;
 }
 
 // ---------------------------------------------------------------------------

@@ -149,13 +149,14 @@ size_t diffattn_fwd_workspace_size(int dtype, int32_t T, int32_t Hkv, int32_t d,
  * (each chunk's keys appended before its queries attend) gives, chunk by
  * chunk, the rows of its one-shot prefill.
  *
- * Two kernel paths, chosen from the size bounds alone (nseq, max_seqlen_q,
- * max_seqlen_k, H, Hkv, d): few query rows per sequence (decoding) split
- * the keys over many workgroups and merge the partial results in a second
- * kernel, through the workspace; long query chunks (32 rows or more, when
+ * Three kernel paths, chosen on the host from the sizes (see
+ * diffattn_fwd_kv_path): few query rows per sequence (decoding) split the
+ * keys over many workgroups and merge the partial results in a second
+ * kernel, through the workspace; longer query chunks (4 rows or more, when
  * the library's cost estimate favours it) run on diffattn_fwd's prefill
- * kernel with the keys' own boundaries, in one kernel and with no
- * workspace.  diffattn_fwd_kv_workspace_size returns 0 for the latter.
+ * kernel with the keys' own boundaries -- in one kernel and with no
+ * workspace, or, when that grid would leave compute units idle, on key
+ * splits whose partials the second kernel merges through the workspace.
  *
  *   q            device [Tq, H, 2, d]: the new queries, packed by
  *                cu_seqlens_q.
@@ -192,12 +193,14 @@ size_t diffattn_fwd_workspace_size(int dtype, int32_t T, int32_t Hkv, int32_t d,
  *                them so).
  *   workspace    device scratch of at least workspace_bytes =
  *                diffattn_fwd_kv_workspace_size(nseq, max_seqlen_q,
- *                max_seqlen_k, H, Hkv, d) bytes, 16-byte aligned, owned by
- *                the caller.  It holds fp32 partial results between the two
- *                kernels of one call; its contents need no initialisation
- *                and are meaningless afterwards.  Two calls in flight at
- *                once (on different streams) need different workspaces.
- *                Not read (and may be NULL) when that size is 0.
+ *                max_seqlen_k, H, Hkv, d) bytes (enough for either path
+ *                that uses one), 16-byte aligned, owned by the caller.  It
+ *                holds fp32 partial results between the two kernels of one
+ *                call; its contents need no initialisation and are
+ *                meaningless afterwards.  Two calls in flight at once (on
+ *                different streams) need different workspaces.  Not read
+ *                (and may be NULL, with workspace_bytes 0) on the prefill
+ *                kernel alone (diffattn_fwd_kv_path 1).
  *   out          device [Tq, H, 2d], same element type as q.
  *
  * Returns DIFFATTN_OK (also when there is no query row, which launches
@@ -226,10 +229,15 @@ int diffattn_fwd_kv(int dtype, const void *q, const void *k, const void *v,
  * routine); the first call on a device looks up that device's array.
  *
  * Arguments, results and errors as for diffattn_fwd_kv, minus workspace and
- * workspace_bytes; the kernels and the split plan are the same, so the
- * output is bitwise that of diffattn_fwd_kv.  Sizes whose
- * diffattn_fwd_kv_workspace_size(...) exceeds DIFFATTN_KV_SCRATCH_BYTES are
- * rejected with DIFFATTN_ETOOLARGE before any device work.
+ * workspace_bytes; the path, the kernels and the split plan are the same,
+ * so the output is bitwise that of diffattn_fwd_kv, with two exceptions.  A
+ * call on the split-KV path whose partials need more than
+ * DIFFATTN_KV_SCRATCH_BYTES is rejected with DIFFATTN_ETOOLARGE before any
+ * device work.  A call on key splits of the prefill kernel
+ * (diffattn_fwd_kv_path 2) whose partials need more runs unsplit on the
+ * prefill kernel alone instead (no scratch; a different rounding order, so
+ * not bitwise diffattn_fwd_kv's output).  On the prefill kernel alone no
+ * scratch is used.
  *
  * All calls on one GPU share its array, and it keeps the last call's
  * partials (nothing needs to start at zero: each call writes every partial
@@ -253,13 +261,56 @@ int diffattn_fwd_kv_noalloc(int dtype, const void *q, const void *k,
                             const void *rope_sin, int32_t rope_len,
                             int rope_dtype, void *out, void *stream);
 
-/* Bytes of workspace diffattn_fwd_kv needs for these sizes (the same path
- * choice and split plan the call makes); 0 when the call runs on the
- * prefill kernel, which needs none, and for sizes it rejects.  Host
+/* Bytes of workspace diffattn_fwd_kv needs for calls within these bounds:
+ * the split-KV plan's, or the prefill kernel's key-split plan's when that
+ * is larger and such a call may take it; 0 for sizes it rejects.  Host
  * function. */
 size_t diffattn_fwd_kv_workspace_size(int32_t nseq, int32_t max_seqlen_q,
                                       int32_t max_seqlen_k, int32_t H,
                                       int32_t Hkv, int32_t d);
+
+/* The kernels diffattn_fwd_kv runs for these bounds and totals (bf16, the
+ * dtype the cache path supports): 0 the split-KV partial kernel and the
+ * combine kernel, 1 the prefill kernel alone, 2 the prefill kernel on key
+ * splits and the combine kernel; -1 for sizes it rejects (including Tq or
+ * Tk < 1).  The split-KV estimate follows the totals, the prefill kernel's
+ * the bounds.  Host function. */
+int diffattn_fwd_kv_path(int32_t nseq, int32_t max_seqlen_q,
+                         int32_t max_seqlen_k, int32_t Tq, int32_t Tk,
+                         int32_t H, int32_t Hkv, int32_t d);
+
+/*
+ * diffattn_fwd_kv on a path the caller picks (path 0, 1 or 2, numbered as
+ * diffattn_fwd_kv_path numbers them) instead of the library's choice, for
+ * callers that pin the kernels -- the rounding order, and so the bits of a
+ * row, then no longer depend on the rest of the batch -- and for tests of
+ * each path.  Path 2 takes the split size with the lowest estimate.  The
+ * other arguments, results and errors are diffattn_fwd_kv's; the workspace
+ * must hold diffattn_fwd_kv_path_workspace_size(path, ...) bytes (none, and
+ * NULL allowed, for path 1).  Returns DIFFATTN_EINVAL also for a path
+ * outside 0..2, and for path 2 when the keys are too few to split.
+ */
+int diffattn_fwd_kv_on_path(int path, int dtype, const void *q, const void *k,
+                            const void *v, const float *lambda_q1,
+                            const float *lambda_k1, const float *lambda_q2,
+                            const float *lambda_k2, int32_t lambda_stride,
+                            float lambda_init, const float *subln_weight,
+                            float eps, int causal, const int32_t *cu_seqlens_q,
+                            const int32_t *cu_seqlens_k, int32_t nseq,
+                            int32_t max_seqlen_q, int32_t max_seqlen_k,
+                            int32_t Tq, int32_t Tk, int32_t H, int32_t Hkv,
+                            int32_t d, const void *rope_cos,
+                            const void *rope_sin, int32_t rope_len,
+                            int rope_dtype, void *workspace,
+                            size_t workspace_bytes, void *out, void *stream);
+
+/* Bytes of workspace diffattn_fwd_kv_on_path needs on `path` for these
+ * bounds: 0 for path 1, and for sizes or paths it rejects.  Host
+ * function. */
+size_t diffattn_fwd_kv_path_workspace_size(int path, int32_t nseq,
+                                           int32_t max_seqlen_q,
+                                           int32_t max_seqlen_k, int32_t H,
+                                           int32_t Hkv, int32_t d);
 
 /*
  * The cache update of a decode step, asynchronous on `stream`: the

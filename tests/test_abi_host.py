@@ -268,34 +268,81 @@ def test_kv_noalloc_too_large_matches_workspace_size():
     assert da.kv_workspace_size(64, 1, 4096, 16, 4, 64) <= da.KV_SCRATCH_BYTES
 
 
-@pytest.mark.parametrize("nseq,mq,mk,H,Hkv,d", [
-    (8, 64, 4096, 16, 4, 64),      # chunked prefill of the 8 x 4096 prompts
-    (8, 1024, 4096, 16, 4, 64),
-    (8, 4096, 4096, 16, 4, 64),    # the whole prompt as one chunk
-    (1, 1024, 32768, 16, 4, 64),
-    (32, 32, 2048, 16, 4, 64),
-    (8, 128, 4096, 8, 8, 64),      # G = 1
-    (8, 64, 4096, 16, 4, 32),
-    (5, 257, 1100, 12, 4, 64),     # G = 3
+@pytest.mark.parametrize("nseq,mq,mk,H,Hkv,d,path", [
+    (8, 1024, 4096, 16, 4, 64, 1),   # chunked prefill of the 8 x 4096 prompts
+    (8, 4096, 4096, 16, 4, 64, 1),   # the whole prompt as one chunk
+    (5, 257, 1100, 12, 4, 64, 1),    # G = 3
+    (1, 1024, 32768, 16, 4, 64, 2),  # one long context: too few query tiles
+    (1, 64, 32768, 16, 4, 64, 2),
+    (8, 64, 4096, 16, 4, 64, 2),
+    (8, 16, 4096, 16, 4, 64, 2),     # speculative tokens
+    (8, 128, 4096, 8, 8, 64, 2),     # G = 1
 ])
-def test_long_chunks_take_the_one_kernel_path(nseq, mq, mk, H, Hkv, d):
-    """Query chunks whose split-KV cost (rows x keys) outweighs one pass of
-    the prefill kernel over the keys need no workspace."""
-    assert da.kv_workspace_size(nseq, mq, mk, H, Hkv, d) == 0
+def test_long_chunks_take_the_prefill_kernel(nseq, mq, mk, H, Hkv, d, path):
+    """Query chunks whose split-KV cost (rows x keys) outweighs the prefill
+    kernel's run on it: over whole key ranges when the grid fills the GPU,
+    else over key splits."""
+    assert da.kv_path(nseq, mq, mk, H, Hkv, d) == path
 
 
-@pytest.mark.parametrize("nseq,mq,mk,H,Hkv,d", [
-    (8, 1, 4097, 16, 4, 64),       # decode steps
-    (64, 1, 8192, 16, 4, 64),
-    (32, 4, 32768, 16, 4, 64),
-    (8, 16, 4096, 16, 4, 64),      # below 32 rows
-    (8, 31, 4096, 16, 4, 64),
-    (8, 32, 4096, 16, 4, 64),      # one grid round of 4096 keys: no gain
-    (1, 256, 32768, 16, 4, 64),    # 32 workgroups over 32768 keys
-    (4096, 4, 128, 16, 4, 64),
+@pytest.mark.parametrize("nseq,mq,mk,H,Hkv,d,Tq,Tk", [
+    (8, 1, 4097, 16, 4, 64, None, None),     # decode steps
+    (64, 1, 8192, 16, 4, 64, None, None),
+    (32, 4, 31196, 16, 4, 64, 128, 539306),  # the varlen step: its cache total
+    (8, 3, 4096, 16, 4, 64, None, None),     # below 4 query rows
+    (8, 16, 4096, 16, 4, 64, 16, 32768),     # a loose bound on 2 queries each
+    (4096, 4, 128, 16, 4, 64, None, None),
 ])
-def test_decode_shapes_keep_the_split_path(nseq, mq, mk, H, Hkv, d):
+def test_decode_shapes_keep_the_split_path(nseq, mq, mk, H, Hkv, d, Tq, Tk):
+    assert da.kv_path(nseq, mq, mk, H, Hkv, d, Tq=Tq, Tk=Tk) == 0
     assert da.kv_workspace_size(nseq, mq, mk, H, Hkv, d) > 0
+
+
+def test_kv_path_rejects_what_the_call_rejects():
+    assert da.kv_path(8, 64, 4096, 16, 5, 64) == -1    # H % Hkv
+    assert da.kv_path(8, 64, 4096, 16, 4, 16) == -1    # d not compiled
+    assert da.kv_path(0, 64, 4096, 16, 4, 64) == -1
+    assert da.kv_path(8, 64, 4096, 16, 4, 64, Tq=0) == -1
+
+
+def call_kv_on_path(path, **over):
+    a = dict(dtype=da.BF16, q=FAKE, k=FAKE, v=FAKE, lq1=FAKE, lk1=FAKE,
+             lq2=FAKE, lk2=FAKE, lambda_stride=0, lambda_init_value=0.7,
+             subln_weight=0, eps=1e-5, causal=1, cu_seqlens_q=0,
+             cu_seqlens_k=0, nseq=8, max_seqlen_q=0, max_seqlen_k=0, Tq=8 * 64,
+             Tk=8 * 4096, H=16, Hkv=4, d=64, rope_cos=0, rope_sin=0,
+             rope_len=0, rope_dtype=0, workspace=FAKE,
+             workspace_bytes=1 << 30, out=FAKE, stream=0)
+    a.update(over)
+    return da.fwd_kv_on_path_ptr(path, **a)
+
+
+@pytest.mark.parametrize("path,over,status", [
+    (3, {}, da.EINVAL),                      # no such path
+    (-2, {}, da.EINVAL),
+    (2, dict(Tk=8 * 200), da.EINVAL),        # 200 keys: nothing to split
+    (0, dict(workspace_bytes=64), da.EINVAL),
+    (2, dict(workspace_bytes=64), da.EINVAL),
+    (1, dict(dtype=da.F32), da.EUNSUPPORTED),
+    (1, dict(Tq=0, q=0, out=0), da.OK),      # no query rows
+])
+def test_kv_on_path_validation_before_any_device_work(path, over, status):
+    assert call_kv_on_path(path, **over) == status
+
+
+def test_path_workspace_sizes():
+    assert da.kv_path_workspace_size(1, 8, 64, 4096, 16, 4, 64) == 0
+    assert da.kv_path_workspace_size(0, 8, 64, 4096, 16, 4, 64) > 0
+    assert da.kv_path_workspace_size(2, 8, 64, 4096, 16, 4, 64) > 0
+    assert da.kv_path_workspace_size(2, 8, 64, 200, 16, 4, 64) == 0   # nothing to split
+    assert da.kv_path_workspace_size(3, 8, 64, 4096, 16, 4, 64) == 0
+
+
+def test_workspace_bound_covers_either_path():
+    """The workspace bound holds the split-KV plan and, where a call within
+    the bounds may run on key splits, that plan too."""
+    from_split_only = da.kv_workspace_size(8, 3, 4096, 16, 4, 64)
+    assert da.kv_workspace_size(8, 64, 4096, 16, 4, 64) >= from_split_only
 
 
 # --------------------------------------------------------------------------

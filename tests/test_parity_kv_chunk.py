@@ -1,9 +1,9 @@
 """Parity of the cache path on long query chunks with the fp64 oracle:
 diffattn_fwd_kv calls whose bounds make the split-KV kernels' rows x keys
-cost outweigh one pass of the prefill kernel over the keys run on that
-kernel, with the keys' own boundaries and no workspace
-(kv_workspace_size returns 0 for them, which the tests use to check the
-path).
+cost outweigh the prefill kernel's run on that kernel with the keys' own
+boundaries -- over whole key ranges (no workspace), or over key splits
+merged by the combine kernel when whole ranges would leave CUs idle.  The
+tests read the path from diffattn_fwd_kv_path.
 
 A chunk is the method's attention for the nq newest tokens of a sequence of
 nk: query i sees keys 0 .. nk - nq + i under the causal mask, all nk keys
@@ -44,15 +44,28 @@ def c(t):
     return t.to(DEV).contiguous()
 
 
-def one_kernel(inp, max_q=None):
-    """Does the call take the one-kernel (prefill) path?  It alone needs no
-    workspace."""
-    H, d, Hkv = inp.q.shape[1], inp.q.shape[3], inp.k.shape[1]
-    return _da().kv_workspace_size(inp.cu_q.numel() - 1, max_q or inp.max_q, inp.max_k,
-                                   H, Hkv, d) == 0
+def path(inp, max_q=None):
+    """The kernels the call runs: 0 split-KV, 1 prefill kernel, 2 prefill
+    kernel on key splits."""
+    Tq, H, _, d = inp.q.shape
+    Tk, Hkv = inp.k.shape[:2]
+    return _da().kv_path(inp.cu_q.numel() - 1, max_q or inp.max_q, inp.max_k, H, Hkv, d,
+                         Tq=Tq, Tk=Tk)
 
 
-def gpu_kv(inp, lam=None, rope=None, uniform=False, noalloc=False, out=None, max_q=None):
+def on_every_path(inp, ref, what, **kw):
+    """The call on the library's own path and on each forced one (key splits
+    where there are more than 256 keys to split), against ref."""
+    paths = [None, 0, 1] + ([2] if inp.max_k > 256 else [])
+    for pth in paths:
+        err = max_abs(gpu_kv(inp, on_path=pth, **kw), ref)
+        announce(f"{what}, path {'auto ' + str(path(inp)) if pth is None else pth}: "
+                 f"max-abs {err:.3e}")
+        assert err <= TOL
+
+
+def gpu_kv(inp, lam=None, rope=None, uniform=False, noalloc=False, out=None, max_q=None,
+           on_path=None):
     da = _da()
     lv = [c(x) for x in (lam if lam is not None else (inp.lq1, inp.lk1, inp.lq2, inp.lk2))]
     kw = {}
@@ -65,6 +78,8 @@ def gpu_kv(inp, lam=None, rope=None, uniform=False, noalloc=False, out=None, max
         kw["rope"] = tuple(c(t) for t in rope)
     if out is not None:
         kw["out"] = out
+    if on_path is not None:
+        kw["path"] = on_path
     f = da.fwd_kv_noalloc if noalloc else da.fwd_kv
     res = f(c(inp.q), c(inp.k), c(inp.v), *lv, da.lambda_init(inp.depth), c(inp.w),
             inp.eps, inp.causal, **kw)
@@ -111,91 +126,106 @@ CHUNKS = [
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("case", range(len(CHUNKS)))
 def test_chunk_ragged_matrix(H, Hkv, d, causal, case):
+    """Every path on each case (key splits where there are more than 256
+    keys to split), and the library's own choice bitwise equal to running
+    the path it reports."""
     ql, kl = CHUNKS[case]
     wl = custom_kv("chunk", "bf16", ql, kl, H=H, Hkv=Hkv, d=d, depth=5, causal=causal,
                    seed=700 + case)
     inp = make_kv_inputs(wl)
     inp.w.copy_(0.5 + torch.rand(2 * d, generator=torch.Generator().manual_seed(case)))
-    path = "one-kernel" if one_kernel(inp) else "split"
-    if H == 8:
-        assert path == "one-kernel"   # every case is a chunk at 8 heads
-    err = max_abs(gpu_kv(inp), oracle_kv(inp))
-    announce(f"case {case} H={H} Hkv={Hkv} d={d} causal={causal} ({path}): "
-             f"max-abs {err:.3e}")
-    assert err <= TOL
+    ref = oracle_kv(inp)
+    outs = {}
+    for pth in (0, 1, 2):
+        if pth == 2 and max(kl) <= 256:
+            continue
+        outs[pth] = gpu_kv(inp, on_path=pth)
+        err = max_abs(outs[pth], ref)
+        announce(f"case {case} H={H} Hkv={Hkv} d={d} causal={causal} path {pth}: "
+                 f"max-abs {err:.3e}")
+        assert err <= TOL
+    auto = path(inp)
+    assert torch.equal(gpu_kv(inp), outs[auto])
 
 
-def test_both_paths_on_the_same_call():
-    """max_seqlen_q is an upper bound, and with the other bounds it picks
-    the path: 32 queries per sequence under a bound of 32 take the split
-    kernels, under a bound of 200 the prefill kernel.  Both meet the bar."""
-    wl = custom_kv("both", "bf16", (32,) * 8, (4096,) * 8, H=16, Hkv=4, d=64, depth=3,
+def test_paths_on_the_same_call():
+    """max_seqlen_q is an upper bound (at most Tq), and with the other sizes
+    it picks the path: 8 queries per sequence under a bound of 8 take the
+    prefill kernel on key splits, under a loose bound the split-KV kernels.
+    Every path met meets the bar on the same data."""
+    wl = custom_kv("paths", "bf16", (8,) * 8, (4096,) * 8, H=16, Hkv=4, d=64, depth=3,
                    seed=710)
     inp = make_kv_inputs(wl)
-    assert not one_kernel(inp) and one_kernel(inp, max_q=200)
+    bounds = {}
+    for b in (8, 16, 32, 64):
+        bounds.setdefault(path(inp, b), b)
+    assert 0 in bounds and 2 in bounds
     ref = oracle_kv(inp)
-    split, chunk = gpu_kv(inp), gpu_kv(inp, max_q=200)
-    e1, e2 = max_abs(split, ref), max_abs(chunk, ref)
-    announce(f"split {e1:.3e}, one-kernel {e2:.3e}")
-    assert e1 <= TOL and e2 <= TOL
+    for pth, b in sorted(bounds.items()):
+        err = max_abs(gpu_kv(inp, max_q=b), ref)
+        announce(f"bound {b} (path {pth}): max-abs {err:.3e}")
+        assert err <= TOL
 
 
 def test_uniform_chunks_without_boundaries():
     wl = custom_kv("uni", "bf16", (160,) * 3, (500,) * 3, H=16, Hkv=4, d=64, depth=6,
                    seed=711)
     inp = make_kv_inputs(wl)
-    assert one_kernel(inp)
-    a = gpu_kv(inp, uniform=True)
-    b = gpu_kv(inp)
-    assert torch.equal(a, b)
-    err = max_abs(a, oracle_kv(inp))
-    announce(f"uniform chunks: max-abs {err:.3e}")
-    assert err <= TOL
+    ref = oracle_kv(inp)
+    for pth in (None, 0, 1, 2):
+        a = gpu_kv(inp, uniform=True, on_path=pth)
+        assert torch.equal(a, gpu_kv(inp, on_path=pth))
+        err = max_abs(a, ref)
+        announce(f"uniform chunks, path {pth}: max-abs {err:.3e}")
+        assert err <= TOL
 
 
 def test_more_queries_than_keys_noncausal():
     wl = custom_kv("nc", "bf16", (300, 150), (100, 2), H=8, Hkv=2, d=64, causal=False,
                    seed=712)
     inp = make_kv_inputs(wl)
-    assert one_kernel(inp)
-    err = max_abs(gpu_kv(inp), oracle_kv(inp))
-    announce(f"nq > nk, non-causal: max-abs {err:.3e}")
-    assert err <= TOL
+    on_every_path(inp, oracle_kv(inp), "nq > nk, non-causal")
 
 
 def test_large_logits():
     wl = custom_kv("big", "bf16", (600, 140), (3000, 5000), H=8, Hkv=2, d=64, depth=2,
                    seed=713)
     inp = make_kv_inputs(wl, q_scale=30.0)
-    assert one_kernel(inp)
-    err = max_abs(gpu_kv(inp), oracle_kv(inp))
-    announce(f"large logits: max-abs {err:.3e}")
-    assert err <= TOL
+    on_every_path(inp, oracle_kv(inp), "large logits")
 
 
 def test_per_head_lambda():
     wl = custom_kv("ph", "bf16", (400, 2), (900, 70), H=8, Hkv=2, d=64, depth=4, seed=714)
     inp = make_kv_inputs(wl)
-    assert one_kernel(inp)
     g = torch.Generator().manual_seed(715)
     lam = [0.2 * torch.randn(wl.H, wl.d, generator=g) for _ in range(4)]
-    err = max_abs(gpu_kv(inp, lam=lam), oracle_kv(inp, lam=lam))
-    announce(f"per-head lambda: max-abs {err:.3e}")
-    assert err <= TOL
+    on_every_path(inp, oracle_kv(inp, lam=lam), "per-head lambda", lam=lam)
 
 
-def test_deterministic_no_alloc_and_output_bounds():
-    """Bitwise equal on repeated calls and through the no-allocation entry
-    point, which runs a chunk whose split partials would not fit its static
-    scratch (the prefill kernel needs none); rows around a provided output
-    are left untouched."""
-    wl = custom_kv("det", "bf16", (700, 64), (4000, 64), H=16, Hkv=4, d=64, depth=8,
-                   seed=716)
+@pytest.mark.parametrize("ql,kl", [((700, 64), (4000, 64)), ((16,) * 8, (4096,) * 8),
+                                   ((64,) * 8, (4096,) * 8), ((2000,), (2000,))])
+def test_deterministic_no_alloc_and_output_bounds(ql, kl):
+    """Bitwise equal on repeated calls; rows around a provided output are
+    left untouched.  The no-allocation entry point gives the same bits on
+    the prefill kernel alone and when the workspace bound fits its static
+    scratch; when key splits' partials would not fit, it runs unsplit (same
+    bar, another rounding order)."""
+    da = _da()
+    wl = custom_kv("det", "bf16", ql, kl, H=16, Hkv=4, d=64, depth=8, seed=716)
     inp = make_kv_inputs(wl)
-    assert one_kernel(inp)
+    pth = path(inp)
+    assert pth in (1, 2)
     a = gpu_kv(inp)
     assert torch.equal(a, gpu_kv(inp))
-    assert torch.equal(a, gpu_kv(inp, noalloc=True))
+    na = gpu_kv(inp, noalloc=True)
+    need = da.kv_workspace_size(len(ql), max(ql), max(kl), 16, 4, 64)
+    if pth == 1 or need <= da.KV_SCRATCH_BYTES:
+        assert torch.equal(a, na)
+    ref = oracle_kv(inp)
+    e1, e2 = max_abs(a, ref), max_abs(na, ref)
+    announce(f"path {pth}, workspace bound {need / 2**20:.1f} MiB: max-abs {e1:.3e}, "
+             f"no-alloc {e2:.3e}")
+    assert e1 <= TOL and e2 <= TOL
     out = torch.full((inp.q.shape[0] + 2, 16, 128), 7.0, dtype=torch.bfloat16, device=DEV)
     gpu_kv(inp, out=out[1:-1])
     assert torch.all(out[0] == 7.0) and torch.all(out[-1] == 7.0)
@@ -213,25 +243,27 @@ def test_rotary_chunks(kind, H, Hkv, d, causal):
     wl = custom_kv("chunk_rope", "bf16", ql, kl, H=H, Hkv=Hkv, d=d, depth=6, causal=causal,
                    seed=720)
     inp = make_kv_inputs(wl)
-    assert one_kernel(inp)
     rc, rs = rope_tables(max(kl), d, base=50.0)
     rope = (rc.bfloat16(), rs.bfloat16()) if kind == "bf16" else (rc, rs)
-    out = gpu_kv(inp, rope=rope)
     qr = turn(inp.q, positions(inp.cu_q, inp.cu_k), tuple(t.float() for t in rope))
-    err = max_abs(out, oracle_kv(inp, q=qr))
-    announce(f"rotary {kind} H={H} Hkv={Hkv} d={d} causal={causal}: max-abs {err:.3e}")
-    assert err <= TOL
+    ref = oracle_kv(inp, q=qr)
+    for pth in (None, 0, 1, 2):
+        err = max_abs(gpu_kv(inp, rope=rope, on_path=pth), ref)
+        announce(f"rotary {kind} H={H} Hkv={Hkv} d={d} causal={causal} path {pth}: "
+                 f"max-abs {err:.3e}")
+        assert err <= TOL
 
 
+@pytest.mark.parametrize("on_path", [None, 1, 2])
 @pytest.mark.parametrize("kind", ["f32", "bf16"])
-def test_chunked_rotary_prefill_equals_prefill_rows(kind):
+def test_chunked_rotary_prefill_equals_prefill_rows(kind, on_path):
     """A prompt run as a chunked prefill -- each chunk's keys appended
     (turned) to the cache, then its queries against the cache so far --
     gives the rows of the oracle's one-shot causal prefill with its own
     rotary prologue."""
     da = _da()
     lens, H, Hkv, d = (1000, 300, 700), 16, 4, 64
-    cuts = (0, 200, 329, 1000)                   # chunk boundaries per sequence
+    cuts = (0, 300, 429, 1000)                   # chunk boundaries per sequence
     wl = custom("chunked", "bf16", lens, H=H, Hkv=Hkv, d=d, depth=7, seed=721)
     pf = make_inputs(wl)
     rc, rs = rope_tables(max(lens), d, base=50.0)
@@ -251,14 +283,13 @@ def test_chunked_rotary_prefill_equals_prefill_rows(kind):
         cu_k = torch.tensor(np.concatenate([[0], np.cumsum(kl)]), dtype=torch.int32)
         # the cache holds each sequence's first kl tokens, packed
         krows = torch.cat([torch.arange(cu[s], cu[s] + n) for s, n in enumerate(kl)]).long()
-        assert da.kv_workspace_size(len(lens), max(ql), max(kl), H, Hkv, d) == 0
         kcur, vcur = kc[krows.to(DEV)], vc[krows.to(DEV)]
         da.kv_append(c(pf.k[rows]), c(pf.v[rows]), kcur, vcur, cu_seqlens_q=c(cu_q),
                      cu_seqlens_k=c(cu_k), max_seqlen_k=max(kl), rope=rdev)
         kc[krows.to(DEV)], vc[krows.to(DEV)] = kcur, vcur
         o = da.fwd_kv(c(pf.q[rows]), kcur, vcur, *lv, da.lambda_init(wl.depth), c(pf.w),
                       wl.eps, True, cu_seqlens_q=c(cu_q), cu_seqlens_k=c(cu_k),
-                      max_seqlen_q=max(ql), max_seqlen_k=max(kl), rope=rdev)
+                      max_seqlen_q=max(ql), max_seqlen_k=max(kl), rope=rdev, path=on_path)
         out[rows.to(DEV)] = o
     torch.cuda.synchronize()
     toks = np.arange(pf.q.shape[0], dtype=np.int64)
@@ -268,7 +299,7 @@ def test_chunked_rotary_prefill_equals_prefill_rows(kind):
                       np.tile(heads, toks.size), pf.w, wl.eps, True, pf.cu_seqlens,
                       rope=tuple(t.float() for t in rope), rope_round_bf16=True)
     err = max_abs(out.reshape(-1, 2 * d), ref.reshape(-1, 2 * d))
-    announce(f"chunked rotary prefill ({kind} tables): max-abs {err:.3e}")
+    announce(f"chunked rotary prefill ({kind} tables, path {on_path}): max-abs {err:.3e}")
     assert err <= TOL
 
 
@@ -287,7 +318,7 @@ def test_full_size_chunk_of_the_headline_prefill():
     rows = torch.cat([torch.arange(s * N + N - n, s * N + N) for s in range(B)]).long()
     cu_q = torch.arange(0, B + 1, dtype=torch.int32) * n
     lv = [c(x) for x in (pf.lq1, pf.lk1, pf.lq2, pf.lk2)]
-    assert da.kv_workspace_size(B, n, N, wl.H, wl.Hkv, wl.d) == 0
+    assert da.kv_path(B, n, N, wl.H, wl.Hkv, wl.d) in (1, 2)
     announce("8 x (1024 vs 4096) chunk: full-size GPU run")
     out = da.fwd_kv(c(pf.q[rows]), c(pf.k), c(pf.v), *lv, da.lambda_init(wl.depth),
                     c(pf.w), wl.eps, True, cu_seqlens_q=c(cu_q),
@@ -307,4 +338,35 @@ def test_full_size_chunk_of_the_headline_prefill():
               torch.from_numpy(rows_h).long().to(DEV)]
     err = max_abs(got, ref)
     announce(f"8 x (1024 vs 4096) chunk: {rows_t.size} rows, max-abs {err:.3e}")
+    assert err <= TOL
+
+
+def test_full_size_long_context_chunk_on_key_splits():
+    """One 32768-token sequence whose last 1024 tokens form the chunk (16
+    heads, 4 KV heads, d = 64): too few query tiles to fill the GPU, so the
+    keys are split and merged.  Every head of one token in eight, and of the
+    chunk's first and last 64 tokens, against the oracle's prefill rows."""
+    da = _da()
+    N, n, H, Hkv, d = 32768, 1024, 16, 4, 64
+    wl = custom("long_chunk", "bf16", (N,), H=H, Hkv=Hkv, d=d, depth=12, seed=730)
+    pf = make_inputs(wl)
+    assert da.kv_path(1, n, N, H, Hkv, d) == 2
+    rows = torch.arange(N - n, N)
+    lv = [c(x) for x in (pf.lq1, pf.lk1, pf.lq2, pf.lk2)]
+    announce("1 x (1024 vs 32768) chunk on key splits: full-size GPU run")
+    out = da.fwd_kv(c(pf.q[rows]), c(pf.k), c(pf.v), *lv, da.lambda_init(wl.depth),
+                    c(pf.w), wl.eps, True, nseq=1)
+    torch.cuda.synchronize()
+    pick = np.array(sorted(set(range(0, n, 8)) | set(range(64)) | set(range(n - 64, n))),
+                    np.int64)
+    toks = rows.numpy()[pick]
+    rows_t = np.repeat(toks, H)
+    rows_h = np.tile(np.arange(H, dtype=np.int32), toks.size)
+    ref = oracle.rows(pf.q, pf.k, pf.v, pf.lq1, pf.lk1, pf.lq2, pf.lk2,
+                      oracle.lambda_init(wl.depth), rows_t, rows_h, pf.w, wl.eps, True,
+                      pf.cu_seqlens)
+    got = out[torch.from_numpy(np.repeat(pick, H)).to(DEV),
+              torch.from_numpy(rows_h).long().to(DEV)]
+    err = max_abs(got, ref)
+    announce(f"1 x (1024 vs 32768): {rows_t.size} rows, max-abs {err:.3e}")
     assert err <= TOL
