@@ -270,6 +270,13 @@ KV_WORKLOADS = {
                     "the 8 x 4096 prompts as one chunk against its 4096 "
                     "keys (bottom-right causal), 16 diff heads, 4 KV heads, "
                     "d=64"),
+    "chunk_b1_q1024_kv32768": KvWorkload(
+        "chunk_b1_q1024_kv32768", "bf16", (1024,), (32768,), H=16, Hkv=4,
+        d=64, depth=8,
+        description="bf16 chunked prefill of one long context: its last "
+                    "1024 tokens against 32768 keys (bottom-right causal), "
+                    "16 diff heads, 4 KV heads, d=64 -- too few query "
+                    "tiles to fill the GPU, so the keys are split"),
 }
 
 KV_HEADLINE = "decode_b64_kv8192"
