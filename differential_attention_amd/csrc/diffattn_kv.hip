@@ -525,10 +525,11 @@ void diffattn_kv_combine(KvParams p)
     // kChunk splits per round: lane j loads split j's (m, l) of both maps in
     // one 16-byte read while every lane loads its columns of all kChunk
     // splits' O (independent loads, one memory round trip per round); the
-    // wave then reduces the maximum and the weighted sums.  kChunk is 32
-    // when a row can have more than 16 splits (one round instead of two:
-    // 3.8% on a 4097-key step), else 16 (fewer registers: more waves in
-    // flight when there are many rows).
+    // wave then reduces the maximum and the weighted sums.  kChunk (4, 8, 16
+    // or 32) covers the longest row's splits in one round where it can (32
+    // instead of 16: 3.8% on a 4097-key step); a narrower one holds fewer
+    // registers and issues fewer loads (rounds past a row's last split
+    // re-read it).
     static_assert(kChunk <= 64, "one split's (m, l) per lane");
     float acc[2][CPL];
     float M[2] = {-INFINITY, -INFINITY};
@@ -779,6 +780,23 @@ void launch_partial(int rt, unsigned blocks, hipStream_t st, const KvParams &p)
                            dim3(kThreads), 0, st, p);
 }
 
+// The merge of up to `splits` splits per row: as many per memory round as
+// the longest row has, in steps of 4, 8, 16 or 32 (a round of the longest
+// row's width, where fewer would take two; narrower rounds hold fewer
+// registers and issue fewer loads).
+template <int D>
+void launch_combine(int64_t splits, unsigned blocks, hipStream_t st, const KvParams &p)
+{
+    if (splits <= 4)
+        hipLaunchKernelGGL((diffattn_kv_combine<D, 4>), dim3(blocks), dim3(kThreads), 0, st, p);
+    else if (splits <= 8)
+        hipLaunchKernelGGL((diffattn_kv_combine<D, 8>), dim3(blocks), dim3(kThreads), 0, st, p);
+    else if (splits <= 16)
+        hipLaunchKernelGGL((diffattn_kv_combine<D, 16>), dim3(blocks), dim3(kThreads), 0, st, p);
+    else
+        hipLaunchKernelGGL((diffattn_kv_combine<D, 32>), dim3(blocks), dim3(kThreads), 0, st, p);
+}
+
 // Validates the arguments, makes the split plan and launches both kernels
 // with the workspace that `get_ws` returns for the plan's size (it returns
 // a status and sets the pointer, or refuses the size).
@@ -872,18 +890,11 @@ int kv_impl(int dtype, const void *q, const void *k, const void *v,
     // more than 16 (splits of ck keys of the longest cache)
     auto combine = [&](int ck) {
         const int64_t kmax = cu_seqlens_q ? max_seqlen_k : Tk / nseq;
-        const bool wide = (kmax + ck - 1) / ck > 16;
-        if (d == 64) {
-            if (wide)
-                hipLaunchKernelGGL((diffattn_kv_combine<64, 32>), dim3((unsigned)blocks2), dim3(kThreads), 0, st, p);
-            else
-                hipLaunchKernelGGL((diffattn_kv_combine<64, 16>), dim3((unsigned)blocks2), dim3(kThreads), 0, st, p);
-        } else {
-            if (wide)
-                hipLaunchKernelGGL((diffattn_kv_combine<32, 32>), dim3((unsigned)blocks2), dim3(kThreads), 0, st, p);
-            else
-                hipLaunchKernelGGL((diffattn_kv_combine<32, 16>), dim3((unsigned)blocks2), dim3(kThreads), 0, st, p);
-        }
+        const int64_t splits = (kmax + ck - 1) / ck;
+        if (d == 64)
+            launch_combine<64>(splits, (unsigned)blocks2, st, p);
+        else
+            launch_combine<32>(splits, (unsigned)blocks2, st, p);
     };
 
     // long query chunks: the prefill kernel, on whole key ranges (no
