@@ -143,6 +143,44 @@ def test_decode_step_with_rotary_graph():
     replay_and_check(g, static, step, lambda: k_new.mul_(2.0), "rotary decode step")
 
 
+@pytest.mark.parametrize("path", [None, da.KV_PATH_PREFILL, da.KV_PATH_PREFILL_SPLIT])
+def test_chunked_prefill_step_graph(path):
+    """A rotary chunked-prefill step -- the chunk's keys turned into the
+    cache, then its queries attending on the prefill kernel (whole key
+    ranges, or key splits merged by the combine kernel) -- captured as one
+    graph."""
+    from workloads import rope_tables
+    wl = custom_kv("graph_chunk", "bf16", (200, 64, 1), (1200, 300, 900), H=16, Hkv=4, d=64,
+                   depth=5, seed=18)
+    inp = make_kv_inputs(wl)
+    c = lambda t: t.to(DEV).contiguous()
+    q, kc, vc = c(inp.q), c(inp.k), c(inp.v)
+    g_ = torch.Generator().manual_seed(19)
+    k_new = c(torch.randn(q.shape[0], wl.Hkv, 2, wl.d, generator=g_).to(q.dtype))
+    v_new = c(torch.randn(q.shape[0], wl.Hkv, 2 * wl.d, generator=g_).to(q.dtype))
+    lv = [c(x) for x in (inp.lq1, inp.lk1, inp.lq2, inp.lk2)]
+    cq, ck = c(inp.cu_q), c(inp.cu_k)
+    rope = tuple(c(t) for t in rope_tables(inp.max_k, wl.d, base=50.0))
+    lam0 = da.lambda_init(wl.depth)
+    nseq = cq.numel() - 1
+    need = (da.kv_workspace_size(nseq, inp.max_q, inp.max_k, wl.H, wl.Hkv, wl.d) if path is None
+            else da.kv_path_workspace_size(path, nseq, inp.max_q, inp.max_k, wl.H, wl.Hkv,
+                                           wl.d))
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=DEV)
+    out = torch.empty((q.shape[0], wl.H, 2 * wl.d), dtype=q.dtype, device=DEV)
+    kw = dict(subln_weight=c(inp.w), eps=wl.eps, causal=True, cu_seqlens_q=cq,
+              cu_seqlens_k=ck, max_seqlen_q=inp.max_q, max_seqlen_k=inp.max_k, rope=rope,
+              path=path)
+
+    def step(**extra):
+        da.kv_append(k_new, v_new, kc, vc, cu_seqlens_q=cq, cu_seqlens_k=ck,
+                     max_seqlen_k=inp.max_k, rope=rope)
+        return da.fwd_kv(q, kc, vc, *lv, lam0, **kw, **extra)
+
+    g, static = capture(lambda: step(workspace=ws, out=out))
+    replay_and_check(g, static, step, lambda: q.mul_(-1.5), f"chunked prefill step path={path}")
+
+
 def test_training_step_graph():
     wl = custom("graph", "bf16", (300, 65, 129), H=8, Hkv=2, d=64, depth=4, seed=7)
     q, k, v, lv, w, cu, inp = dev_inputs(wl)
