@@ -167,6 +167,23 @@ def test_paths_on_the_same_call():
         assert err <= TOL
 
 
+def test_many_sequences_on_key_splits():
+    """More than 64 sequences, with empty ones and caches of every length up
+    to several splits, on each path: a split slot finds its sequence by the
+    kernels' scan of cu_seqlens_k across 64-sequence steps, and a sequence
+    without keys owns no slot."""
+    rng = np.random.default_rng(740)
+    nseq = 150
+    kl = [int(x) for x in rng.integers(1, 2500, nseq)]
+    ql = [int(min(q, k)) for q, k in zip(rng.integers(0, 40, nseq), kl)]
+    for s in (0, 63, 64, 100, 149):   # empty sequences, on and off step edges
+        ql[s], kl[s] = 0, 0
+    ql[70] = 0                         # keys only
+    wl = custom_kv("many", "bf16", tuple(ql), tuple(kl), H=8, Hkv=2, d=64, depth=4, seed=741)
+    inp = make_kv_inputs(wl)
+    on_every_path(inp, oracle_kv(inp), f"{nseq} sequences, Tk={sum(kl)}")
+
+
 def test_uniform_chunks_without_boundaries():
     wl = custom_kv("uni", "bf16", (160,) * 3, (500,) * 3, H=16, Hkv=4, d=64, depth=6,
                    seed=711)
