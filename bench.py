@@ -51,8 +51,10 @@ GRAPH_STEPS = 10   # decode steps per captured graph (--graph)
 _CSRC = os.path.join(HERE, "differential_attention_amd", "csrc")
 # the sources whose kernels a stored counter profile measured: a profile
 # counts only while their digest matches
-KERNEL_SOURCES = [os.path.join(_CSRC, "diffattn_fwd.hip"), os.path.join(_CSRC, "rope.h")]
-KV_KERNEL_SOURCES = [os.path.join(_CSRC, "diffattn_kv.hip"), os.path.join(_CSRC, "rope.h")]
+KERNEL_SOURCES = [os.path.join(_CSRC, "diffattn_fwd.hip"), os.path.join(_CSRC, "rope.h"),
+                  os.path.join(_CSRC, "splits.h")]
+KV_KERNEL_SOURCES = [os.path.join(_CSRC, "diffattn_kv.hip"), os.path.join(_CSRC, "rope.h"),
+                     os.path.join(_CSRC, "splits.h")]
 CHUNK_KERNEL_SOURCES = KERNEL_SOURCES + [os.path.join(_CSRC, "diffattn_kv.hip"),
                                          os.path.join(_CSRC, "chunk.h")]
 BWD_KERNEL_SOURCES = [os.path.join(_CSRC, "diffattn_fwd.hip"), os.path.join(_CSRC, "rope.h"),

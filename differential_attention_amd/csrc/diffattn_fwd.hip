@@ -78,6 +78,7 @@
 #include "chunk.h"
 #include "diffattn.h"
 #include "rope.h"
+#include "splits.h"
 
 namespace {
 
@@ -326,43 +327,6 @@ struct Params {
     int32_t sub;       // 32-query sub-blocks per wave (the kernel's SUB)
 };
 
-// Split slot j of a chunk with key splits: its sequence and the sequence's
-// first slot, or false past the last split.  The slots of all sequences
-// share one index space (sequence s owns ceil(nk_s / ck) consecutive ones),
-// found with a wave-wide scan of the key boundaries, 64 sequences per step.
-__device__ inline bool chunk_split_owner(const Params &p, int j, int lane, int &s, int &base)
-{
-    if (!p.cuk) {
-        const int cnt = (p.klen_uniform + p.ck - 1) / p.ck;
-        if (cnt == 0 || j >= cnt * p.nseq)
-            return false;
-        s = j / cnt;
-        base = s * cnt;
-        return true;
-    }
-    int run = 0;
-    for (int s0 = 0; s0 < p.nseq; s0 += 64) {
-        const int si = s0 + lane;
-        const int cnt = si < p.nseq ? (p.cuk[si + 1] - p.cuk[si] + p.ck - 1) / p.ck : 0;
-        int incl = cnt;   // inclusive prefix over the lanes
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int t = __shfl_up(incl, off, 64);
-            if (lane >= off)
-                incl += t;
-        }
-        const uint64_t hit = __builtin_amdgcn_ballot_w64(j >= run + incl - cnt && j < run + incl);
-        if (hit) {
-            const int l = __builtin_ctzll(hit);
-            s = s0 + l;
-            base = run + __builtin_amdgcn_readlane(incl - cnt, l);
-            return true;
-        }
-        run += __builtin_amdgcn_readlane(incl, 63);
-    }
-    return false;
-}
-
 // Every CU runs one workgroup of 8 waves (two per SIMD); the register
 // budget per lane is the 256 that two waves per SIMD leave.  SUB: 32-query
 // sub-blocks per wave -- 2 (each K/V operand read feeds two MFMAs), or 1 for
@@ -421,7 +385,7 @@ void diffattn_fwd_kernel(Params p)
     if constexpr (CHUNK) {
         if (p.ck > 0) {
             int base = 0;
-            if (!chunk_split_owner(p, unit, lane, seq, base))
+            if (!diffattn_splits::split_owner(p, unit, lane, seq, base))
                 return;   // past the last split
             split = unit - base;
         }

@@ -62,6 +62,7 @@
 #include "chunk.h"
 #include "diffattn.h"
 #include "rope.h"
+#include "splits.h"
 
 namespace {
 
@@ -114,45 +115,8 @@ __device__ inline void seq_bounds(const int32_t *cu, int uniform, int s, int &a,
     }
 }
 
-// Splits of all sequences share one index space: sequence s owns the
-// ceil(nk_s / ck) consecutive slots starting at base(s) = the sum of the
-// earlier sequences' split counts.  Both kernels find them with a
-// wave-wide scan of cu_seqlens_k, 64 sequences per step (wave-uniform).
-__device__ inline int split_count(int nk, int ck) { return (nk + ck - 1) / ck; }
-
-// Sequence owning slot j and its base, or false past the last split.
-__device__ inline bool split_owner(const KvParams &p, int j, int lane, int &s, int &base)
-{
-    if (!p.cuk) {
-        const int cnt = split_count(p.klen_uniform, p.ck);
-        if (cnt == 0 || j >= cnt * p.nseq)
-            return false;
-        s = j / cnt;
-        base = s * cnt;
-        return true;
-    }
-    int run = 0;
-    for (int s0 = 0; s0 < p.nseq; s0 += 64) {
-        const int si = s0 + lane;
-        const int cnt = si < p.nseq ? split_count(p.cuk[si + 1] - p.cuk[si], p.ck) : 0;
-        int incl = cnt;   // inclusive prefix over the lanes
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int t = __shfl_up(incl, off, 64);
-            if (lane >= off)
-                incl += t;
-        }
-        const uint64_t hit = __builtin_amdgcn_ballot_w64(j >= run + incl - cnt && j < run + incl);
-        if (hit) {
-            const int l = __builtin_ctzll(hit);
-            s = s0 + l;
-            base = run + __builtin_amdgcn_readlane(incl - cnt, l);
-            return true;
-        }
-        run += __builtin_amdgcn_readlane(incl, 63);
-    }
-    return false;
-}
+using diffattn_splits::split_count;
+using diffattn_splits::split_owner;
 
 // Combined value over the four lanes l, l^16, l^32, l^48 (the quarter-waves
 // of one row); the order of combination is fixed, so all four lanes get
