@@ -55,6 +55,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "diffattn.h"
 
 namespace {
@@ -530,57 +532,86 @@ void bwd_dq(BwdParams p)
         sv.store(stage + TILEB);
     };
 
-    auto compute = [&](int it, const char *stage) __attribute__((always_inline)) {
+    // NB consecutive 32-key blocks from block b0 of the tile, their S, dP,
+    // softmax and dS interleaved in one straight-line region (independent
+    // chains for the scheduler), then their dQ products; masked: apply the
+    // index mask (blocks reaching the diagonal or the sequence end)
+    auto blocks = [&](auto nb, int k0, int b0, bool masked, const char *stage)
+        __attribute__((always_inline)) {
+        constexpr int NB = decltype(nb)::value;
         const char *kt = stage, *vt = stage + TILEB;
+        f32x16 sa[NB], dp[NB];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const int b = b0 + j;
+            // S^T = K Q^T (keys x queries)
+            sa[j] = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const bf16x8 ka = *(const bf16x8 *)(kt + 32 * b * LROW + map * D * 2 +
+                                                    ((ks & 1) ? plain_o : plain_e) + 32 * ks);
+                sa[j] = mma(ka, qf[ks], sa[j]);
+            }
+            // dP^T = V dO^T
+            dp[j] = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < NVS; ++ks) {
+                const bf16x8 va = *(const bf16x8 *)(vt + 32 * b * LROW +
+                                                    ((ks & 1) ? plain_o : plain_e) + 32 * ks);
+                dp[j] = mma(va, df[ks], dp[j]);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            // P^T and dS^T; lane owns query wq, element a is key kb0 +
+            // acc_row(a, h).  Keys past the sequence or after the query get
+            // a score of -inf (probability 0).
+            const int kb0 = k0 + 32 * (b0 + j);
+            if (masked) {
+#pragma unroll
+                for (int a = 0; a < 16; ++a) {
+                    const int key = kb0 + acc_row(a, h);
+                    if (!(key < s1 && (!p.causal || key <= wq)))
+                        sa[j][a] = -INFINITY;
+                }
+            }
+#pragma unroll
+            for (int a = 0; a < 16; ++a) {
+                const float pv = __builtin_amdgcn_exp2f(fmaf(sa[j][a], c, -lse));
+                sa[j][a] = pv * fmaf(dpf, dp[j][a], -dval);
+            }
+        }
+        // dQ^T += K^T dS^T
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+            for (int ps = 0; ps < 2; ++ps) {
+                const bf16x8 bs = pack8(sa[j], 8 * ps);
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    dqa[db] = mma(tr.load(kt, LROW, 32 * (b0 + j) + 16 * ps,
+                                          (map * D + 32 * db) * 2),
+                                  bs, dqa[db]);
+            }
+    };
+    auto compute = [&](int it, const char *stage) __attribute__((always_inline)) {
         const int k0 = s0 + it * kInner;
+        static_assert(kInner == 64, "two 32-key blocks per tile");
+        // wave-uniform: both blocks visible and unmasked (the common case:
+        // one region for both), else block by block
+        const int klast = k0 + 32;   // first key of the tile's second block
+        if (klast + 32 <= s1 && (!p.causal || klast + 31 <= q0 + 32 * sub)) {
+            blocks(std::integral_constant<int, 2>{}, k0, 0, false, stage);
+            return;
+        }
 #pragma unroll
         for (int b = 0; b < kInner / 32; ++b) {
             const int kb0 = k0 + 32 * b;
             // wave-uniform: keys of the block this wave's queries can see
             if (kb0 >= s1 || (p.causal && kb0 > q0 + 32 * sub + 31))
                 continue;
-            // S^T = K Q^T (keys x queries)
-            f32x16 sa = f32x16{};
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                const bf16x8 ka = *(const bf16x8 *)(kt + 32 * b * LROW + map * D * 2 +
-                                                    ((ks & 1) ? plain_o : plain_e) + 32 * ks);
-                sa = mma(ka, qf[ks], sa);
-            }
-            // dP^T = V dO^T
-            f32x16 dp = f32x16{};
-#pragma unroll
-            for (int ks = 0; ks < NVS; ++ks) {
-                const bf16x8 va = *(const bf16x8 *)(vt + 32 * b * LROW +
-                                                    ((ks & 1) ? plain_o : plain_e) + 32 * ks);
-                dp = mma(va, df[ks], dp);
-            }
-            // P^T and dS^T; lane owns query wq, element a is key kb0 + acc_row(a, h).
-            // Keys past the sequence or after the query get a score of -inf
-            // (probability 0); wave-uniform: only blocks that reach the end of
-            // the sequence or the diagonal need the test.
-            if (kb0 + 32 > s1 || (p.causal && kb0 + 31 > q0 + 32 * sub)) {
-#pragma unroll
-                for (int a = 0; a < 16; ++a) {
-                    const int key = kb0 + acc_row(a, h);
-                    if (!(key < s1 && (!p.causal || key <= wq)))
-                        sa[a] = -INFINITY;
-                }
-            }
-#pragma unroll
-            for (int a = 0; a < 16; ++a) {
-                const float pv = __builtin_amdgcn_exp2f(fmaf(sa[a], c, -lse));
-                sa[a] = pv * fmaf(dpf, dp[a], -dval);
-            }
-            // dQ^T += K^T dS^T
-#pragma unroll
-            for (int ps = 0; ps < 2; ++ps) {
-                const bf16x8 bs = pack8(sa, 8 * ps);
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-                    dqa[db] = mma(tr.load(kt, LROW, 32 * b + 16 * ps, (map * D + 32 * db) * 2),
-                                  bs, dqa[db]);
-            }
+            const bool masked = kb0 + 32 > s1 || (p.causal && kb0 + 31 > q0 + 32 * sub);
+            blocks(std::integral_constant<int, 1>{}, k0, b, masked, stage);
         }
     };
     auto step = [&](int it, const char *cur, char *nxt) __attribute__((always_inline)) {
