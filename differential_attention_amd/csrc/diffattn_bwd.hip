@@ -35,7 +35,9 @@
 //           dS_1 = P_1 (dP - D'_1), dS_2 = P_2 (-lambda dP + lambda D'_2)
 //           and dK_m^T += Q_m^T dS_m, and form W = P_1 - lambda P_2 in fp32
 //           (then rounded); the other four waves (same keys) compute
-//           dP = dpre V^T once for both maps one query tile ahead and add
+//           dP = dpre V^T once for both maps one query tile ahead (handed
+//           over as dP - D'_1, with lambda D'_2 - lambda D'_1 per row, so
+//           that map 2's factor is one FMA) and add
 //           dV^T += dpre^T W one query tile behind, dP and W travelling
 //           through LDS.  Query tiles (Q, dpre, lse, D) of all G heads of
 //           the group rotate through four LDS stages.
@@ -682,10 +684,13 @@ void bwd_dkdv(BwdParams p)
     constexpr int QB = kQT * LQROW;          // Q tile bytes
     constexpr int STB = 2 * QB + kQT * 4 * 4;   // one stage: Q, dpre, lse[2], D[2]
     constexpr int WXB = kSubs * 2 * 64 * 16;    // one W hand-over buffer (bf16)
-    constexpr int PXB = kSubs * 4 * 64 * 16;    // one dP hand-over buffer (fp32)
+    constexpr int PXB = kSubs * 4 * 64 * 16;    // one dP - D'_1 hand-over buffer (fp32)
     __shared__ __attribute__((aligned(16))) char stg[4 * STB];
     __shared__ __attribute__((aligned(16))) char wx[2 * WXB];
     __shared__ __attribute__((aligned(16))) char px[2 * PXB];
+    // per query row of a tile: lambda D'_2 - lambda D'_1, so that the S role
+    // forms map 2's factor from map 1's hand-over in one FMA
+    __shared__ __attribute__((aligned(16))) float cx[2][kQT];
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int n = lane & 31, h = lane >> 5;
@@ -764,20 +769,29 @@ void bwd_dkdv(BwdParams p)
         return !(q0 >= s1 || (p.causal && q0 + kQT - 1 < wk_first));
     };
     // V role: dP = dpre V^T of step stp (queries x keys; lane owns key wk),
-    // handed over as 16 floats per lane
+    // handed over as dP - D'_1 (the factor of map 1's dS), 16 floats per
+    // lane; the first V wave also tabulates the tile's lambda D'_2 - lambda
+    // D'_1 (map 2's factor is -lambda (dP - D'_1) plus that)
     auto compute_dp = [&](int stp) __attribute__((always_inline)) {
         if (!visible(stp))
             return;
         const char *dt = stage_of(stp) + QB;
+        const float *tab = (const float *)(stage_of(stp) + 2 * QB);
         f32x16 dp = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < NVS; ++ks)
             dp = mma(*(const bf16x8 *)(dt + ((ks & 1) ? plain_o : plain_e) + 32 * ks), kv[ks], dp);
+        if (sub == 0 && lane < kQT) {
+            const float nlam = -p.lam[g * p.G + stp / nqt];
+            cx[stp & 1][lane] = fmaf(nlam, tab[2 * kQT + lane], tab[3 * kQT + lane]);
+        }
         char *out = px + (stp & 1) * PXB + sub * 4 * 1024 + lane * 16;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            *(float4 *)(out + j * 1024) =
-                float4{dp[4 * j], dp[4 * j + 1], dp[4 * j + 2], dp[4 * j + 3]};
+        for (int j = 0; j < 4; ++j) {
+            const float4 e1 = *(const float4 *)(tab + 2 * kQT + 8 * j + 4 * h);
+            *(float4 *)(out + j * 1024) = float4{dp[4 * j] - e1.x, dp[4 * j + 1] - e1.y,
+                                                 dp[4 * j + 2] - e1.z, dp[4 * j + 3] - e1.w};
+        }
     };
     auto compute_s = [&](int stp) __attribute__((always_inline)) {
         if (!visible(stp))
@@ -812,22 +826,22 @@ void bwd_dkdv(BwdParams p)
             const int r0 = 8 * j + 4 * h;
             const float4 l1 = *(const float4 *)(tab + r0);
             const float4 l2 = *(const float4 *)(tab + kQT + r0);
-            const float4 e1 = *(const float4 *)(tab + 2 * kQT + r0);
-            const float4 e2 = *(const float4 *)(tab + 3 * kQT + r0);
+            const float4 c4 = *(const float4 *)(&cx[stp & 1][r0]);
             const float4 d4 = *(const float4 *)(pin + j * 1024);
             const float lr1[4] = {l1.x, l1.y, l1.z, l1.w}, lr2[4] = {l2.x, l2.y, l2.z, l2.w};
-            const float dr1[4] = {e1.x, e1.y, e1.z, e1.w}, dr2[4] = {e2.x, e2.y, e2.z, e2.w};
-            const float dp[4] = {d4.x, d4.y, d4.z, d4.w};
+            const float cr[4] = {c4.x, c4.y, c4.z, c4.w};
+            const float x1[4] = {d4.x, d4.y, d4.z, d4.w};   // dP - D'_1
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int a = 4 * j + e;
                 const float p1 = __builtin_amdgcn_exp2f(fmaf(s1a[a], c, -lr1[e]));
                 const float p2 = __builtin_amdgcn_exp2f(fmaf(s2a[a], c, -lr2[e]));
-                // W = P_1 - lambda P_2; dS_2 = P_2 (-lambda dP + lambda D'_2),
-                // the table holding lambda D'_2
+                // W = P_1 - lambda P_2; dS_1 = P_1 (dP - D'_1);
+                // dS_2 = P_2 (-lambda dP + lambda D'_2)
+                //      = P_2 (-lambda (dP - D'_1) + lambda D'_2 - lambda D'_1)
                 wpk[a / 8][a % 8] = (bf16)fmaf(nlam, p2, p1);
-                s1a[a] = p1 * (dp[e] - dr1[e]);
-                s2a[a] = p2 * fmaf(nlam, dp[e], dr2[e]);
+                s1a[a] = p1 * x1[e];
+                s2a[a] = p2 * fmaf(nlam, x1[e], cr[e]);
             }
         }
         char *wout = wx + (stp & 1) * WXB;
