@@ -5,7 +5,8 @@
 
 #include <stdint.h>
 
-// How a chunk call runs on the prefill kernel: unsplit (ck = 0), or with
+// How a chunk call runs on the prefill kernel (with sub 32-query
+// sub-blocks per wave): unsplit (ck = 0), or with
 // each sequence's keys cut into splits of ck keys (nslots slots in all) whose
 // partials the cache path's combine kernel merges, through a workspace of
 // ws_bytes (fp32 partial O of [nslots][Hkv][rmax][2][2d], then the maxima
@@ -14,6 +15,7 @@ struct DiffattnChunkPlan {
     int32_t ck;
     int32_t nslots;
     int32_t rmax;
+    int32_t sub;   // 32-query sub-blocks per wave (1 or 2)
     size_t ws_o_bytes, ws_ml_bytes;
     double est_us;
 };

@@ -1039,19 +1039,25 @@ int launch_chunk(const Params &p, int nblocks, hipStream_t stream)
 // Grid of a launch: 64 queries per wave, or 32 when that leaves fewer than
 // two workgroups per CU (256 CUs), so small problems spread over twice the
 // workgroups.  Returns false when the grid would not fit 32 bits.
-bool grid_shape(int max_seqlen, int nseq, int H, int Hkv, int &hpw, int &sub, int64_t &ntile_q,
-                int64_t &nblocks)
+// Grid with `sub` 32-query sub-blocks per wave.
+void grid_of(int max_seqlen, int nseq, int H, int Hkv, int sub, int &hpw, int64_t &ntile_q,
+             int64_t &nblocks)
 {
     const int G = H / Hkv;
     hpw = (G % 4 == 0) ? 4 : (G % 2 == 0 ? 2 : 1);
+    const int bm = 32 * sub * (kSlots / hpw);
+    ntile_q = ((int64_t)max_seqlen + bm - 1) / bm;
+    nblocks = ntile_q * nseq * Hkv * (G / hpw);
+}
+
+bool grid_shape(int max_seqlen, int nseq, int H, int Hkv, int &hpw, int &sub, int64_t &ntile_q,
+                int64_t &nblocks)
+{
     sub = 2;
-    for (;;) {
-        const int bm = 32 * sub * (kSlots / hpw);
-        ntile_q = ((int64_t)max_seqlen + bm - 1) / bm;
-        nblocks = ntile_q * nseq * Hkv * (G / hpw);
-        if (sub == 1 || nblocks >= 2 * kCUs)
-            break;
+    grid_of(max_seqlen, nseq, H, Hkv, sub, hpw, ntile_q, nblocks);
+    if (nblocks < 2 * kCUs) {
         sub = 1;
+        grid_of(max_seqlen, nseq, H, Hkv, sub, hpw, ntile_q, nblocks);
     }
     return nblocks <= INT32_MAX;
 }
@@ -1228,50 +1234,59 @@ int fwd_impl(int dtype, const void *q, const void *k, const void *v,
 int diffattn_chunk_plan(int32_t nseq, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t H,
                         int32_t Hkv, int32_t d, int splits, DiffattnChunkPlan *plan)
 {
-    int hpw = 0, sub = 0;
+    int hpw = 0, sub0 = 0;
     int64_t ntile_q = 0, nblocks = 0;
     if (nseq < 1 || max_seqlen_q < 1 || max_seqlen_k < 1 ||
-        !grid_shape(max_seqlen_q, nseq, H, Hkv, hpw, sub, ntile_q, nblocks))
+        !grid_shape(max_seqlen_q, nseq, H, Hkv, hpw, sub0, ntile_q, nblocks))
         return 0;
-    const int64_t per_unit = nblocks / nseq;   // workgroups per sequence or split
     const int64_t rmax = (int64_t)(H / Hkv) * max_seqlen_q;
     // Estimated duration with units of ck keys each (sequences, or splits):
     // rounds of at most one workgroup per CU, each as long as a workgroup
     // streaming ck keys, plus, for splits, the merge kernel.  The constants
-    // are fitted to measured calls on this part (d = 64; d = 32 about 0.72
-    // of the per-key time): per key 21 ns with 32-query sub-blocks and 27
-    // with 64, 48% more when every CU is busy (the clock under load), 7 us
-    // per round, and the merge 0.46 us per MB of partials plus 8 us.
+    // are fitted to 300 measured calls on this part (d = 64; d = 32 about
+    // 0.72 of the per-key time; an 11.5% RMS fit of log time): per key 20.7
+    // ns with 32-query sub-blocks and 33.2 with 64, 45% more when every CU
+    // is busy (the clock under load), 9.8 us per round; the merge 0.28 us
+    // per MB of partials, 0.65 ns per output row and 5.7 us.
     const double fd = d == 32 ? 0.72 : 1.0;
-    const double ns_per_key = (sub == 2 ? 26.9 : 21.1) * fd;
-    auto estimate = [&](int64_t blocks, int64_t keys, size_t ws_bytes) {
+    const double out_rows = (double)nseq * max_seqlen_q * H;
+    auto estimate = [&](int sub, int64_t blocks, int64_t keys, size_t ws_bytes) {
+        const double ns_per_key = (sub == 2 ? 33.2 : 20.7) * fd;
         const double occ = (double)std::min<int64_t>(blocks, kCUs) / kCUs;
         double us = (double)((blocks + kCUs - 1) / kCUs) *
-                    (1e-3 * ns_per_key * (double)keys * (1.0 + 0.48 * occ) + 7.0);
+                    (1e-3 * ns_per_key * (double)keys * (1.0 + 0.455 * occ) + 9.8);
         if (ws_bytes)
-            us += 0.46e-6 * (double)ws_bytes + 8.0;
+            us += 0.275e-6 * (double)ws_bytes + 0.647e-3 * out_rows + 5.7;
         return us;
     };
+    // unsplit: the prefill's own choice of sub-blocks
     DiffattnChunkPlan pl{};
     pl.rmax = (int32_t)std::min<int64_t>(rmax, INT32_MAX);
     pl.nslots = nseq;
-    pl.est_us = splits == 2 ? INFINITY : estimate(nblocks, max_seqlen_k, 0);
-    // key splits of 256, 512, 1024, ... keys (whole 128-key tiles), the
-    // cheapest estimate winning
-    for (int64_t ck = 256; splits && ck < max_seqlen_k; ck *= 2) {
-        const int64_t slots = (int64_t)nseq * ((max_seqlen_k + ck - 1) / ck);
-        const int64_t rows = slots * Hkv * rmax;
-        if (slots > INT32_MAX || per_unit * slots > INT32_MAX || rmax > (1 << 24) ||
-            rows > ((int64_t)1 << 36))
-            continue;
-        const size_t ws_o = (size_t)rows * 2 * (2 * d) * 4, ws_ml = (size_t)rows * 4 * 4;
-        const double us = estimate(per_unit * slots, ck, ws_o + ws_ml);
-        if (us < pl.est_us) {
-            pl.ck = (int32_t)ck;
-            pl.nslots = (int32_t)slots;
-            pl.ws_o_bytes = ws_o;
-            pl.ws_ml_bytes = ws_ml;
-            pl.est_us = us;
+    pl.sub = sub0;
+    pl.est_us = splits == 2 ? INFINITY : estimate(sub0, nblocks, max_seqlen_k, 0);
+    // key splits of 256, 512, 1024, ... keys (whole 128-key tiles), with 64-
+    // or 32-query sub-blocks, the cheapest estimate winning
+    for (int sub = 2; splits && sub >= 1; --sub) {
+        int64_t nb = 0;
+        grid_of(max_seqlen_q, nseq, H, Hkv, sub, hpw, ntile_q, nb);
+        const int64_t per_unit = nb / nseq;   // workgroups per sequence or split
+        for (int64_t ck = 256; ck < max_seqlen_k; ck *= 2) {
+            const int64_t slots = (int64_t)nseq * ((max_seqlen_k + ck - 1) / ck);
+            const int64_t rows = slots * Hkv * rmax;
+            if (slots > INT32_MAX || per_unit * slots > INT32_MAX || rmax > (1 << 24) ||
+                rows > ((int64_t)1 << 36))
+                continue;
+            const size_t ws_o = (size_t)rows * 2 * (2 * d) * 4, ws_ml = (size_t)rows * 4 * 4;
+            const double us = estimate(sub, per_unit * slots, ck, ws_o + ws_ml);
+            if (us < pl.est_us) {
+                pl.ck = (int32_t)ck;
+                pl.nslots = (int32_t)slots;
+                pl.sub = sub;
+                pl.ws_o_bytes = ws_o;
+                pl.ws_ml_bytes = ws_ml;
+                pl.est_us = us;
+            }
         }
     }
     if (splits == 2 && pl.ck == 0)
@@ -1294,10 +1309,12 @@ int diffattn_chunk_prefill(const void *q, const void *k, const void *v, const fl
         return DIFFATTN_EUNSUPPORTED;
     // (the grid's first index runs over the split slots, or the sequences)
     const int units = plan->ck > 0 ? plan->nslots : nseq;
-    int hpw = 0, sub = 0;
-    int64_t ntile_q = 0, nblocks = 0;
-    if (!grid_shape(max_seqlen_q, nseq, H, Hkv, hpw, sub, ntile_q, nblocks))
+    const int sub = plan->sub;
+    if (sub != 1 && sub != 2)
         return DIFFATTN_EINVAL;
+    int hpw = 0;
+    int64_t ntile_q = 0, nblocks = 0;
+    grid_of(max_seqlen_q, nseq, H, Hkv, sub, hpw, ntile_q, nblocks);
     nblocks = nblocks / nseq * units;
     if (nblocks > INT32_MAX)
         return DIFFATTN_EINVAL;
