@@ -18,8 +18,8 @@ from typing import Optional
 import torch
 
 __all__ = ["fwd", "fwd_ptr", "fwd_workspace_size", "fwd_kv", "fwd_kv_ptr", "kv_workspace_size",
-           "kv_path", "KV_PATH_SPLIT_KV", "KV_PATH_PREFILL", "KV_PATH_PREFILL_SPLIT",
-           "fwd_kv_on_path_ptr", "kv_path_workspace_size",
+           "kv_path", "kv_plan", "KV_PATH_SPLIT_KV", "KV_PATH_PREFILL",
+           "KV_PATH_PREFILL_SPLIT", "fwd_kv_on_path_ptr", "kv_path_workspace_size",
            "fwd_kv_noalloc", "fwd_kv_noalloc_ptr", "KV_SCRATCH_BYTES",
            "fwd_train", "bwd", "bwd_workspace_size", "supported_bwd",
            "kv_append", "kv_append_ptr", "diff_attention", "DiffAttnFunction",
@@ -87,7 +87,8 @@ def library() -> ctypes.CDLL:
     lib.diffattn_kv_append.restype = ctypes.c_int
     lib.diffattn_fwd_kv_workspace_size.argtypes = [i32] * 6
     lib.diffattn_fwd_kv_workspace_size.restype = ctypes.c_size_t
-    lib.diffattn_fwd_kv_path.argtypes = [i32] * 8
+    lib.diffattn_fwd_kv_path.argtypes = [i32] * 8 + [ctypes.c_size_t,
+                                                     ctypes.POINTER(ctypes.c_size_t)]
     lib.diffattn_fwd_kv_path.restype = ctypes.c_int
     lib.diffattn_supported_kv.argtypes = [ctypes.c_int, ctypes.c_int]
     lib.diffattn_supported_kv.restype = ctypes.c_int
@@ -179,15 +180,29 @@ KV_PATH_PREFILL = 1        # the prefill kernel alone (no workspace)
 KV_PATH_PREFILL_SPLIT = 2  # the prefill kernel on key splits + combine kernel
 
 
-def kv_path(nseq: int, max_seqlen_q: int, max_seqlen_k: int, H: int, Hkv: int,
-            d: int, Tq: Optional[int] = None, Tk: Optional[int] = None) -> int:
-    """Which kernels ``fwd_kv`` runs for these bounds and totals (KV_PATH_*;
-    -1: sizes rejected).  Tq and Tk default to nseq equal sequences."""
+def kv_plan(nseq: int, max_seqlen_q: int, max_seqlen_k: int, H: int, Hkv: int,
+            d: int, Tq: Optional[int] = None, Tk: Optional[int] = None,
+            workspace_bytes: Optional[int] = None) -> tuple:
+    """(path, bytes): the kernels ``fwd_kv`` runs for these bounds and totals
+    given a workspace of ``workspace_bytes`` (None: as large as the
+    library's first choice needs), and the workspace bytes that plan uses
+    (KV_PATH_*; path -1: sizes rejected).  Tq and Tk default to nseq equal
+    sequences."""
     Tq = nseq * max_seqlen_q if Tq is None else Tq
     Tk = nseq * max_seqlen_k if Tk is None else Tk
-    return int(library().diffattn_fwd_kv_path(
+    cap = (1 << 64) - 1 if workspace_bytes is None else int(workspace_bytes)
+    need = ctypes.c_size_t(0)
+    path = int(library().diffattn_fwd_kv_path(
         int(nseq), int(max_seqlen_q), int(max_seqlen_k), int(Tq), int(Tk), int(H), int(Hkv),
-        int(d)))
+        int(d), cap, ctypes.byref(need)))
+    return path, int(need.value)
+
+
+def kv_path(nseq: int, max_seqlen_q: int, max_seqlen_k: int, H: int, Hkv: int,
+            d: int, Tq: Optional[int] = None, Tk: Optional[int] = None,
+            workspace_bytes: Optional[int] = None) -> int:
+    """Which kernels ``fwd_kv`` runs (the path of ``kv_plan``)."""
+    return kv_plan(nseq, max_seqlen_q, max_seqlen_k, H, Hkv, d, Tq, Tk, workspace_bytes)[0]
 
 
 def fwd_kv_ptr(dtype: int, q: int, k: int, v: int, lq1: int, lk1: int,

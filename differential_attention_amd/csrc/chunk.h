@@ -3,6 +3,7 @@
 // (diffattn_kv.hip) when the chunks are long.  Not part of the C ABI.
 #pragma once
 
+#include <stddef.h>
 #include <stdint.h>
 
 // How a chunk call runs on the prefill kernel (with sub 32-query
@@ -22,11 +23,13 @@ struct DiffattnChunkPlan {
 
 // The plan for uniform sequences of these sizes: splits = 1 takes the
 // split size (or none) with the lowest estimate, 0 the unsplit plan, 2 the
-// cheapest split size.  Returns 0 when the grid does not fit (or, for 2, no
+// cheapest split size; only split sizes whose partials fit in ws_cap bytes
+// are candidates.  Returns 0 when the grid does not fit (or, for 2, no
 // split size does).
 __attribute__((visibility("hidden"))) int
 diffattn_chunk_plan(int32_t nseq, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t H,
-                    int32_t Hkv, int32_t d, int splits, DiffattnChunkPlan *plan);
+                    int32_t Hkv, int32_t d, int splits, size_t ws_cap,
+                    DiffattnChunkPlan *plan);
 
 // Arguments as validated by diffattn_fwd_kv (bf16, d = 32 or 64); the
 // sequences' queries are the last nq of their nk keys, aligned bottom-right.

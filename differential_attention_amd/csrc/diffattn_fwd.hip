@@ -1232,7 +1232,8 @@ int fwd_impl(int dtype, const void *q, const void *k, const void *v,
 } // namespace
 
 int diffattn_chunk_plan(int32_t nseq, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t H,
-                        int32_t Hkv, int32_t d, int splits, DiffattnChunkPlan *plan)
+                        int32_t Hkv, int32_t d, int splits, size_t ws_cap,
+                        DiffattnChunkPlan *plan)
 {
     int hpw = 0, sub0 = 0;
     int64_t ntile_q = 0, nblocks = 0;
@@ -1266,7 +1267,8 @@ int diffattn_chunk_plan(int32_t nseq, int32_t max_seqlen_q, int32_t max_seqlen_k
     pl.sub = sub0;
     pl.est_us = splits == 2 ? INFINITY : estimate(sub0, nblocks, max_seqlen_k, 0);
     // key splits of 256, 512, 1024, ... keys (whole 128-key tiles), with 64-
-    // or 32-query sub-blocks, the cheapest estimate winning
+    // or 32-query sub-blocks, the cheapest estimate among those that fit the
+    // workspace winning
     for (int sub = 2; splits && sub >= 1; --sub) {
         int64_t nb = 0;
         grid_of(max_seqlen_q, nseq, H, Hkv, sub, hpw, ntile_q, nb);
@@ -1278,6 +1280,8 @@ int diffattn_chunk_plan(int32_t nseq, int32_t max_seqlen_q, int32_t max_seqlen_k
                 rows > ((int64_t)1 << 36))
                 continue;
             const size_t ws_o = (size_t)rows * 2 * (2 * d) * 4, ws_ml = (size_t)rows * 4 * 4;
+            if (ws_o + ws_ml > ws_cap)
+                continue;   // (the partials would not fit the workspace)
             const double us = estimate(sub, per_unit * slots, ck, ws_o + ws_ml);
             if (us < pl.est_us) {
                 pl.ck = (int32_t)ck;

@@ -615,24 +615,38 @@ double split_kv_us(int nseq, int max_q, int max_k, int64_t Tq, int64_t Tk, int H
 }
 
 // The path of a call with these bounds and totals (Tq, Tk < 0: taken as
-// uniform); cp receives the prefill plan when a prefill path wins.
+// uniform) and a workspace of ws_cap bytes: the lowest estimate among the
+// paths whose partials fit, the split-KV path when none does (the call then
+// refuses the workspace).  cp receives the prefill plan when a prefill path
+// wins; need, when given, the workspace bytes of the chosen plan.
 int kv_path(int nseq, int max_q, int max_k, int64_t Tq, int64_t Tk, int H, int Hkv, int d,
-            DiffattnChunkPlan *cp)
+            size_t ws_cap, DiffattnChunkPlan *cp, size_t *need)
 {
+    KvPlan sk;
+    const bool sk_ok = nseq >= 1 && H >= 1 && Hkv >= 1 && H % Hkv == 0 &&
+                       make_plan(nseq, max_q, max_k, H / Hkv, Hkv, d, -1, sk);
+    const size_t sk_need = sk_ok ? sk.ws_o_bytes + sk.ws_ml_bytes : SIZE_MAX;
+    auto split_kv = [&]() {
+        if (need)
+            *need = sk_need;
+        return (int)kPathSplitKv;
+    };
     if (max_q < kChunkMinRows || nseq < 1 || max_k < 1 || H < 1 || Hkv < 1 || H % Hkv != 0 ||
         !diffattn_supported_kv(DIFFATTN_BF16, d))
-        return kPathSplitKv;
+        return split_kv();
     DiffattnChunkPlan pl;
-    if (!diffattn_chunk_plan(nseq, max_q, max_k, H, Hkv, d, 1, &pl))
-        return kPathSplitKv;
+    if (!diffattn_chunk_plan(nseq, max_q, max_k, H, Hkv, d, 1, ws_cap, &pl))
+        return split_kv();
     if (Tq < 0 || Tk < 0) {
         Tq = (int64_t)nseq * max_q;
         Tk = (int64_t)nseq * max_k;
     }
-    if (!(pl.est_us < split_kv_us(nseq, max_q, max_k, Tq, Tk, H, Hkv, d)))
-        return kPathSplitKv;
+    if (sk_need <= ws_cap && !(pl.est_us < split_kv_us(nseq, max_q, max_k, Tq, Tk, H, Hkv, d)))
+        return split_kv();
     if (cp)
         *cp = pl;
+    if (need)
+        *need = pl.ck > 0 ? pl.ws_o_bytes + pl.ws_ml_bytes : 0;
     return pl.ck > 0 ? kPathChunkSplit : kPathChunk;
 }
 
@@ -701,12 +715,14 @@ extern "C" int diffattn_check_cu_seqlens_kv(const int32_t *host_cu_q, const int3
 }
 
 extern "C" int diffattn_fwd_kv_path(int32_t nseq, int32_t max_seqlen_q, int32_t max_seqlen_k,
-                                    int32_t Tq, int32_t Tk, int32_t H, int32_t Hkv, int32_t d)
+                                    int32_t Tq, int32_t Tk, int32_t H, int32_t Hkv, int32_t d,
+                                    size_t workspace_bytes, size_t *workspace_needed)
 {
     if (nseq < 1 || max_seqlen_q < 1 || max_seqlen_k < 1 || Tq < 1 || Tk < 1 || H < 1 ||
         Hkv < 1 || H % Hkv != 0 || !diffattn_supported_kv(DIFFATTN_BF16, d))
         return -1;
-    return kv_path(nseq, max_seqlen_q, max_seqlen_k, Tq, Tk, H, Hkv, d, nullptr);
+    return kv_path(nseq, max_seqlen_q, max_seqlen_k, Tq, Tk, H, Hkv, d, workspace_bytes, nullptr,
+                   workspace_needed);
 }
 
 extern "C" size_t diffattn_fwd_kv_workspace_size(int32_t nseq, int32_t max_seqlen_q,
@@ -723,7 +739,8 @@ extern "C" size_t diffattn_fwd_kv_workspace_size(int32_t nseq, int32_t max_seqle
     // instead, whose plan depends on the bounds alone)
     DiffattnChunkPlan cp;
     if (max_seqlen_q >= kChunkMinRows && diffattn_supported_kv(DIFFATTN_BF16, d) &&
-        diffattn_chunk_plan(nseq, max_seqlen_q, max_seqlen_k, H, Hkv, d, 1, &cp) && cp.ck > 0)
+        diffattn_chunk_plan(nseq, max_seqlen_q, max_seqlen_k, H, Hkv, d, 1, SIZE_MAX, &cp) &&
+        cp.ck > 0)
         need = std::max(need, cp.ws_o_bytes + cp.ws_ml_bytes);
     return need;
 }
@@ -763,7 +780,8 @@ void launch_combine(int64_t splits, unsigned blocks, hipStream_t st, const KvPar
 
 // Validates the arguments, makes the split plan and launches both kernels
 // with the workspace that `get_ws` returns for the plan's size (it returns
-// a status and sets the pointer, or refuses the size).
+// a status and sets the pointer, or refuses the size).  ws_cap is the
+// workspace's size: the path and plan are chosen among those that fit it.
 template <typename GetWs>
 int kv_impl(int dtype, const void *q, const void *k, const void *v,
             const float *lambda_q1, const float *lambda_k1, const float *lambda_q2,
@@ -772,7 +790,7 @@ int kv_impl(int dtype, const void *q, const void *k, const void *v,
             const int32_t *cu_seqlens_k, int32_t nseq, int32_t max_seqlen_q,
             int32_t max_seqlen_k, int32_t Tq, int32_t Tk, int32_t H, int32_t Hkv, int32_t d,
             const void *rope_cos, const void *rope_sin, int32_t rope_len, int rope_dtype,
-            int force_path, GetWs get_ws, void *out, void *stream)
+            int force_path, size_t ws_cap, GetWs get_ws, void *out, void *stream)
 {
     if (force_path < -1 || force_path > kPathChunkSplit)
         return DIFFATTN_EINVAL;
@@ -866,25 +884,21 @@ int kv_impl(int dtype, const void *q, const void *k, const void *v,
     DiffattnChunkPlan cp;
     int path = force_path;
     if (path == -1) {
-        path = kv_path(nseq, max_seqlen_q, max_seqlen_k, Tq, Tk, H, Hkv, d, &cp);
+        path = kv_path(nseq, max_seqlen_q, max_seqlen_k, Tq, Tk, H, Hkv, d, ws_cap, &cp,
+                       nullptr);
     } else if (path != kPathSplitKv) {
         // (the grid of the prefill kernel must fit, and for splits, a split
-        // size must)
+        // size whose partials fit the workspace must)
         if (!diffattn_chunk_plan(nseq, max_seqlen_q, max_seqlen_k, H, Hkv, d,
-                                 path == kPathChunkSplit ? 2 : 0, &cp))
+                                 path == kPathChunkSplit ? 2 : 0, ws_cap, &cp))
             return DIFFATTN_EINVAL;
     }
     if (path != kPathSplitKv) {
         void *workspace = nullptr;
-        if (path == kPathChunkSplit) {
+        if (cp.ck > 0) {
             const int wst = get_ws(cp.ws_o_bytes + cp.ws_ml_bytes, workspace);
-            if (wst == DIFFATTN_ETOOLARGE) {
-                // (only the static scratch refuses a size: run unsplit)
-                if (!diffattn_chunk_plan(nseq, max_seqlen_q, max_seqlen_k, H, Hkv, d, 0, &cp))
-                    return DIFFATTN_EINVAL;
-            } else if (wst != DIFFATTN_OK) {
+            if (wst != DIFFATTN_OK)
                 return wst;
-            }
         }
         float *ws_o = (float *)workspace;
         float *ws_ml = cp.ck > 0 ? (float *)((char *)workspace + cp.ws_o_bytes) : nullptr;
@@ -980,8 +994,10 @@ extern "C" int diffattn_fwd_kv(int dtype, const void *q, const void *k, const vo
                                int rope_dtype, void *workspace, size_t workspace_bytes,
                                void *out, void *stream)
 {
+    if (workspace && !aligned16(workspace))
+        return DIFFATTN_EINVAL;
     auto caller_ws = [&](size_t need, void *&ws) {
-        if (!workspace || !aligned16(workspace) || workspace_bytes < need)
+        if (!workspace || workspace_bytes < need)
             return (int)DIFFATTN_EINVAL;
         ws = workspace;
         return (int)DIFFATTN_OK;
@@ -989,7 +1005,7 @@ extern "C" int diffattn_fwd_kv(int dtype, const void *q, const void *k, const vo
     return kv_impl(dtype, q, k, v, lambda_q1, lambda_k1, lambda_q2, lambda_k2, lambda_stride,
                    lambda_init, subln_weight, eps, causal, cu_seqlens_q, cu_seqlens_k, nseq,
                    max_seqlen_q, max_seqlen_k, Tq, Tk, H, Hkv, d, rope_cos, rope_sin, rope_len,
-                   rope_dtype, -1, caller_ws, out, stream);
+                   rope_dtype, -1, workspace ? workspace_bytes : 0, caller_ws, out, stream);
 }
 
 extern "C" int diffattn_fwd_kv_noalloc(int dtype, const void *q, const void *k, const void *v,
@@ -1014,7 +1030,7 @@ extern "C" int diffattn_fwd_kv_noalloc(int dtype, const void *q, const void *k, 
     return kv_impl(dtype, q, k, v, lambda_q1, lambda_k1, lambda_q2, lambda_k2, lambda_stride,
                    lambda_init, subln_weight, eps, causal, cu_seqlens_q, cu_seqlens_k, nseq,
                    max_seqlen_q, max_seqlen_k, Tq, Tk, H, Hkv, d, rope_cos, rope_sin, rope_len,
-                   rope_dtype, -1, static_ws, out, stream);
+                   rope_dtype, -1, (size_t)DIFFATTN_KV_SCRATCH_BYTES, static_ws, out, stream);
 }
 
 extern "C" int diffattn_fwd_kv_on_path(int path, int dtype, const void *q, const void *k,
@@ -1030,10 +1046,10 @@ extern "C" int diffattn_fwd_kv_on_path(int path, int dtype, const void *q, const
                                        int32_t rope_len, int rope_dtype, void *workspace,
                                        size_t workspace_bytes, void *out, void *stream)
 {
-    if (path < 0)
+    if (path < 0 || (workspace && !aligned16(workspace)))
         return DIFFATTN_EINVAL;
     auto caller_ws = [&](size_t need, void *&ws) {
-        if (!workspace || !aligned16(workspace) || workspace_bytes < need)
+        if (!workspace || workspace_bytes < need)
             return (int)DIFFATTN_EINVAL;
         ws = workspace;
         return (int)DIFFATTN_OK;
@@ -1041,7 +1057,7 @@ extern "C" int diffattn_fwd_kv_on_path(int path, int dtype, const void *q, const
     return kv_impl(dtype, q, k, v, lambda_q1, lambda_k1, lambda_q2, lambda_k2, lambda_stride,
                    lambda_init, subln_weight, eps, causal, cu_seqlens_q, cu_seqlens_k, nseq,
                    max_seqlen_q, max_seqlen_k, Tq, Tk, H, Hkv, d, rope_cos, rope_sin, rope_len,
-                   rope_dtype, path, caller_ws, out, stream);
+                   rope_dtype, path, workspace ? workspace_bytes : 0, caller_ws, out, stream);
 }
 
 extern "C" size_t diffattn_fwd_kv_path_workspace_size(int path, int32_t nseq,
@@ -1060,7 +1076,7 @@ extern "C" size_t diffattn_fwd_kv_path_workspace_size(int path, int32_t nseq,
     }
     DiffattnChunkPlan cp;
     if (path == kPathChunkSplit &&
-        diffattn_chunk_plan(nseq, max_seqlen_q, max_seqlen_k, H, Hkv, d, 2, &cp))
+        diffattn_chunk_plan(nseq, max_seqlen_q, max_seqlen_k, H, Hkv, d, 2, SIZE_MAX, &cp))
         return cp.ws_o_bytes + cp.ws_ml_bytes;
     return 0;
 }

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define DIFFATTN_ABI_VERSION 10
+#define DIFFATTN_ABI_VERSION 11
 
 enum diffattn_status {
     DIFFATTN_OK = 0,
@@ -191,16 +191,22 @@ size_t diffattn_fwd_workspace_size(int dtype, int32_t T, int32_t Hkv, int32_t d,
  *                used as they are: a rotated cache holds each key already
  *                rotated at its own position (diffattn_kv_append writes
  *                them so).
- *   workspace    device scratch of at least workspace_bytes =
- *                diffattn_fwd_kv_workspace_size(nseq, max_seqlen_q,
- *                max_seqlen_k, H, Hkv, d) bytes (enough for either path
- *                that uses one), 16-byte aligned, owned by the caller.  It
- *                holds fp32 partial results between the two kernels of one
- *                call; its contents need no initialisation and are
+ *   workspace, workspace_bytes
+ *                device scratch (16-byte aligned, owned by the caller) for
+ *                the fp32 partial results passed between the two kernels of
+ *                one call; its contents need no initialisation and are
  *                meaningless afterwards.  Two calls in flight at once (on
- *                different streams) need different workspaces.  Not read
- *                (and may be NULL, with workspace_bytes 0) on the prefill
- *                kernel alone (diffattn_fwd_kv_path 1).
+ *                different streams) need different workspaces.  The call
+ *                takes the path and split plan with the lowest estimate
+ *                among those whose partials fit workspace_bytes (0 when
+ *                workspace is NULL; the prefill kernel alone needs none).
+ *                diffattn_fwd_kv_workspace_size(nseq, max_seqlen_q,
+ *                max_seqlen_k, H, Hkv, d) bytes are enough for the
+ *                library's first choice at these bounds, and a workspace of
+ *                that size serves every call within them; with less, a call
+ *                may run a slower plan (different rounding order), and one
+ *                whose only path does not fit (fewer than 4 query rows in
+ *                the longest sequence) returns DIFFATTN_EINVAL.
  *   out          device [Tq, H, 2d], same element type as q.
  *
  * Returns DIFFATTN_OK (also when there is no query row, which launches
@@ -229,15 +235,14 @@ int diffattn_fwd_kv(int dtype, const void *q, const void *k, const void *v,
  * routine); the first call on a device looks up that device's array.
  *
  * Arguments, results and errors as for diffattn_fwd_kv, minus workspace and
- * workspace_bytes; the path, the kernels and the split plan are the same,
- * so the output is bitwise that of diffattn_fwd_kv, with two exceptions.  A
- * call on the split-KV path whose partials need more than
- * DIFFATTN_KV_SCRATCH_BYTES is rejected with DIFFATTN_ETOOLARGE before any
- * device work.  A call on key splits of the prefill kernel
- * (diffattn_fwd_kv_path 2) whose partials need more runs unsplit on the
- * prefill kernel alone instead (no scratch; a different rounding order, so
- * not bitwise diffattn_fwd_kv's output).  On the prefill kernel alone no
- * scratch is used.
+ * workspace_bytes: the call takes the path and plan diffattn_fwd_kv takes
+ * with a workspace of DIFFATTN_KV_SCRATCH_BYTES, and its output is bitwise
+ * that call's (which is the output with diffattn_fwd_kv_workspace_size
+ * bytes whenever that size is no larger than the scratch).  When no path
+ * fits the scratch (fewer than 4 query rows in the longest sequence and
+ * split-KV partials larger than DIFFATTN_KV_SCRATCH_BYTES) the call returns
+ * DIFFATTN_ETOOLARGE before any device work.  On the prefill kernel alone
+ * no scratch is used.
  *
  * All calls on one GPU share its array, and it keeps the last call's
  * partials (nothing needs to start at zero: each call writes every partial
@@ -261,34 +266,42 @@ int diffattn_fwd_kv_noalloc(int dtype, const void *q, const void *k,
                             const void *rope_sin, int32_t rope_len,
                             int rope_dtype, void *out, void *stream);
 
-/* Bytes of workspace diffattn_fwd_kv needs for calls within these bounds:
- * the split-KV plan's, or the prefill kernel's key-split plan's when that
- * is larger and such a call may take it; 0 for sizes it rejects.  Host
- * function. */
+/* Bytes of workspace for diffattn_fwd_kv at these bounds: the split-KV
+ * plan's, or the prefill kernel's key-split plan's when that is larger and
+ * the library may choose it; 0 for sizes it rejects.  A call within these
+ * bounds (smaller max_seqlen_q, max_seqlen_k or totals) given this many
+ * bytes always finds a path that fits.  Host function. */
 size_t diffattn_fwd_kv_workspace_size(int32_t nseq, int32_t max_seqlen_q,
                                       int32_t max_seqlen_k, int32_t H,
                                       int32_t Hkv, int32_t d);
 
 /* The kernels diffattn_fwd_kv runs for these bounds and totals (bf16, the
- * dtype the cache path supports): 0 the split-KV partial kernel and the
- * combine kernel, 1 the prefill kernel alone, 2 the prefill kernel on key
- * splits and the combine kernel; -1 for sizes it rejects (including Tq or
- * Tk < 1).  The split-KV estimate follows the totals, the prefill kernel's
- * the bounds.  Host function. */
+ * dtype the cache path supports) given a workspace of workspace_bytes
+ * (SIZE_MAX: the library's first choice): 0 the split-KV partial kernel and
+ * the combine kernel, 1 the prefill kernel alone, 2 the prefill kernel on
+ * key splits and the combine kernel; -1 for sizes it rejects (including Tq
+ * or Tk < 1).  The split-KV estimate follows the totals, the prefill
+ * kernel's the bounds.  workspace_needed (may be NULL) receives the bytes
+ * of workspace the chosen plan uses; on path 0 they can exceed
+ * workspace_bytes, and the call then returns DIFFATTN_EINVAL.  Host
+ * function. */
 int diffattn_fwd_kv_path(int32_t nseq, int32_t max_seqlen_q,
                          int32_t max_seqlen_k, int32_t Tq, int32_t Tk,
-                         int32_t H, int32_t Hkv, int32_t d);
+                         int32_t H, int32_t Hkv, int32_t d,
+                         size_t workspace_bytes, size_t *workspace_needed);
 
 /*
  * diffattn_fwd_kv on a path the caller picks (path 0, 1 or 2, numbered as
  * diffattn_fwd_kv_path numbers them) instead of the library's choice, for
  * callers that pin the kernels -- the rounding order, and so the bits of a
  * row, then no longer depend on the rest of the batch -- and for tests of
- * each path.  Path 2 takes the split size with the lowest estimate.  The
- * other arguments, results and errors are diffattn_fwd_kv's; the workspace
- * must hold diffattn_fwd_kv_path_workspace_size(path, ...) bytes (none, and
- * NULL allowed, for path 1).  Returns DIFFATTN_EINVAL also for a path
- * outside 0..2, and for path 2 when the keys are too few to split.
+ * each path.  Path 2 takes the split size with the lowest estimate among
+ * those whose partials fit workspace_bytes.  The other arguments, results
+ * and errors are diffattn_fwd_kv's; with
+ * diffattn_fwd_kv_path_workspace_size(path, ...) bytes path 2 gets its
+ * first choice, path 0 needs that many, path 1 none (NULL allowed).
+ * Returns DIFFATTN_EINVAL also for a path outside 0..2, and for path 2 when
+ * the keys are too few to split or no split's partials fit.
  */
 int diffattn_fwd_kv_on_path(int path, int dtype, const void *q, const void *k,
                             const void *v, const float *lambda_q1,

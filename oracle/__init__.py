@@ -27,10 +27,13 @@ LIBRARY = os.path.join(_HERE, "libdiffattn_ref.so")
 
 def build(source: str = SOURCE, output: str = LIBRARY, extra=()) -> str:
     """Compile the oracle with gcc (IEEE semantics: no fast-math)."""
+    # (a temporary of this process's own, so concurrent builds -- parallel
+    # test workers -- each replace the library whole)
+    tmp = f"{output}.{os.getpid()}.tmp"
     cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
-           "-Wall", "-Werror", *extra, source, "-o", output + ".tmp", "-lm"]
+           "-Wall", "-Werror", *extra, source, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(output + ".tmp", output)
+    os.replace(tmp, output)
     return output
 
 

@@ -225,9 +225,10 @@ def test_kv_scratch_size_matches_header():
     (dict(out=FAKE + 4), da.EINVAL),               # not 16-byte aligned
     (dict(rope_cos=FAKE, rope_sin=FAKE, rope_len=100), da.EINVAL),  # < max_seqlen_k
     (dict(Tq=0, q=0, out=0), da.OK),               # no query rows
-    # split partials beyond the static scratch: 4096 sequences x 4 queries x
-    # 16 heads against 128 keys each (a decode-sized call)
-    (dict(nseq=4096, Tq=4096 * 4, Tk=4096 * 128), da.ETOOLARGE),
+    # split partials beyond the static scratch: 4096 sequences x 2 queries x
+    # 16 heads against 128 keys each (a decode-sized call, too few query rows
+    # for the prefill kernel)
+    (dict(nseq=4096, Tq=4096 * 2, Tk=4096 * 128), da.ETOOLARGE),
 ])
 def test_kv_noalloc_validation_before_any_device_work(over, status):
     assert call_kv_noalloc(**over) == status
@@ -263,9 +264,15 @@ def test_kv_append_validation_before_any_device_work(over, status):
 
 
 def test_kv_noalloc_too_large_matches_workspace_size():
-    need = da.kv_workspace_size(4096, 4, 128, 16, 4, 64)
+    need = da.kv_workspace_size(4096, 2, 128, 16, 4, 64)
     assert need > da.KV_SCRATCH_BYTES
+    # no path fits the scratch: the split-KV path is the only one below 4
+    # query rows
+    assert da.kv_plan(4096, 2, 128, 16, 4, 64, workspace_bytes=da.KV_SCRATCH_BYTES) == (0, need)
     assert da.kv_workspace_size(64, 1, 4096, 16, 4, 64) <= da.KV_SCRATCH_BYTES
+    # with 4 query rows the prefill kernel alone (no scratch) takes over
+    assert da.kv_workspace_size(4096, 4, 128, 16, 4, 64) > da.KV_SCRATCH_BYTES
+    assert da.kv_plan(4096, 4, 128, 16, 4, 64, workspace_bytes=da.KV_SCRATCH_BYTES) == (1, 0)
 
 
 @pytest.mark.parametrize("nseq,mq,mk,H,Hkv,d,path", [
@@ -336,6 +343,48 @@ def test_path_workspace_sizes():
     assert da.kv_path_workspace_size(2, 8, 64, 4096, 16, 4, 64) > 0
     assert da.kv_path_workspace_size(2, 8, 64, 200, 16, 4, 64) == 0   # nothing to split
     assert da.kv_path_workspace_size(3, 8, 64, 4096, 16, 4, 64) == 0
+
+
+@pytest.mark.parametrize("d", [64, 32])
+def test_workspace_of_the_bounds_serves_every_call_within_them(d):
+    """A workspace of kv_workspace_size(bounds) bytes fits the plan of
+    every call with smaller bounds: the call takes the cheapest plan whose
+    partials fit, which is its first choice whenever that fits."""
+    H, Hkv = 16, 4
+    changed = 0
+    for nseq in (1, 2, 3, 8):
+        for Mq, Mk in ((4, 4096), (64, 8192), (100, 8192), (100, 32768), (1024, 4096),
+                       (2048, 32768)):
+            W = da.kv_workspace_size(nseq, Mq, Mk, H, Hkv, d)
+            for mq in (1, 3, 4, 5, 16, 33, 64, 100, 512, 1024, 2048):
+                for mk in (mq, 256, 257, 1000, 4096, 4097, 8192, 16384, 32768):
+                    if mq > Mq or mk > Mk or mk < mq:
+                        continue
+                    path, need = da.kv_plan(nseq, mq, mk, H, Hkv, d, workspace_bytes=W)
+                    first = da.kv_plan(nseq, mq, mk, H, Hkv, d)
+                    assert path in (0, 1, 2) and need <= W, (nseq, Mq, Mk, mq, mk)
+                    if first[1] <= W:
+                        assert (path, need) == first
+                    else:
+                        changed += 1
+    # (some calls within the bounds do want more than the bounds' own plan)
+    assert changed > 0
+
+
+def test_plan_follows_the_workspace_given():
+    # one 32768-key context's last 1024 queries: key splits first choice
+    first = da.kv_plan(1, 1024, 32768, 16, 4, 64)
+    assert first[0] == 2 and first[1] > 0
+    # with no workspace: the prefill kernel alone
+    assert da.kv_plan(1, 1024, 32768, 16, 4, 64, workspace_bytes=0) == (1, 0)
+    # with half the first choice's bytes: another split plan that fits
+    path, need = da.kv_plan(1, 1024, 32768, 16, 4, 64, workspace_bytes=first[1] // 2)
+    assert path in (1, 2) and need <= first[1] // 2
+    # decode keeps the split-KV path whatever the workspace; its need is
+    # reported even when the workspace is smaller (the call refuses it)
+    dec = da.kv_plan(8, 1, 4097, 16, 4, 64)
+    assert dec[0] == 0 and dec[1] == da.kv_workspace_size(8, 1, 4097, 16, 4, 64)
+    assert da.kv_plan(8, 1, 4097, 16, 4, 64, workspace_bytes=0) == dec
 
 
 def test_workspace_bound_covers_either_path():

@@ -65,7 +65,7 @@ def on_every_path(inp, ref, what, **kw):
 
 
 def gpu_kv(inp, lam=None, rope=None, uniform=False, noalloc=False, out=None, max_q=None,
-           on_path=None):
+           on_path=None, workspace=None, max_k=None):
     da = _da()
     lv = [c(x) for x in (lam if lam is not None else (inp.lq1, inp.lk1, inp.lq2, inp.lk2))]
     kw = {}
@@ -73,13 +73,15 @@ def gpu_kv(inp, lam=None, rope=None, uniform=False, noalloc=False, out=None, max
         kw["nseq"] = inp.cu_q.numel() - 1
     else:
         kw.update(cu_seqlens_q=c(inp.cu_q), cu_seqlens_k=c(inp.cu_k),
-                  max_seqlen_q=max_q or inp.max_q, max_seqlen_k=inp.max_k)
+                  max_seqlen_q=max_q or inp.max_q, max_seqlen_k=max_k or inp.max_k)
     if rope is not None:
         kw["rope"] = tuple(c(t) for t in rope)
     if out is not None:
         kw["out"] = out
     if on_path is not None:
         kw["path"] = on_path
+    if workspace is not None:
+        kw["workspace"] = workspace
     f = da.fwd_kv_noalloc if noalloc else da.fwd_kv
     res = f(c(inp.q), c(inp.k), c(inp.v), *lv, da.lambda_init(inp.depth), c(inp.w),
             inp.eps, inp.causal, **kw)
@@ -225,8 +227,9 @@ def test_deterministic_no_alloc_and_output_bounds(ql, kl):
     """Bitwise equal on repeated calls; rows around a provided output are
     left untouched.  The no-allocation entry point gives the same bits on
     the prefill kernel alone and when the workspace bound fits its static
-    scratch; when key splits' partials would not fit, it runs unsplit (same
-    bar, another rounding order)."""
+    scratch; when key splits' partials would not fit, it takes the plan of a
+    call given a workspace of the scratch's size (same bar, another
+    rounding order), and those bits."""
     da = _da()
     wl = custom_kv("det", "bf16", ql, kl, H=16, Hkv=4, d=64, depth=8, seed=716)
     inp = make_kv_inputs(wl)
@@ -238,6 +241,9 @@ def test_deterministic_no_alloc_and_output_bounds(ql, kl):
     need = da.kv_workspace_size(len(ql), max(ql), max(kl), 16, 4, 64)
     if pth == 1 or need <= da.KV_SCRATCH_BYTES:
         assert torch.equal(a, na)
+    else:
+        ws = torch.empty(da.KV_SCRATCH_BYTES, dtype=torch.uint8, device=DEV)
+        assert torch.equal(gpu_kv(inp, workspace=ws), na)
     ref = oracle_kv(inp)
     e1, e2 = max_abs(a, ref), max_abs(na, ref)
     announce(f"path {pth}, workspace bound {need / 2**20:.1f} MiB: max-abs {e1:.3e}, "
@@ -251,6 +257,32 @@ def test_deterministic_no_alloc_and_output_bounds(ql, kl):
 
 # ---------------------------------------------------------------------------
 # rotary chunks: the queries turn at their absolute positions nk - nq + i
+
+@pytest.mark.parametrize("nq,nk,bq,bk", [(64, 8192, 100, 8192), (512, 4096, 1024, 4096),
+                                         (100, 4097, 100, 8192)])
+def test_workspace_of_larger_bounds_serves_a_smaller_call(nq, nk, bq, bk):
+    """A workspace sized for larger bounds (a serving loop's one
+    allocation) runs a call whose own first choice of key splits would need
+    more: the call takes the cheapest split plan that fits, which is what
+    the forced key-split path gives with the same workspace."""
+    da = _da()
+    nseq, H, Hkv, d = 2, 16, 4, 64
+    W = da.kv_workspace_size(nseq, bq, bk, H, Hkv, d)
+    first = da.kv_plan(nseq, nq, nk, H, Hkv, d)
+    capped = da.kv_plan(nseq, nq, nk, H, Hkv, d, workspace_bytes=W)
+    announce(f"{nseq} x ({nq} vs {nk}) in a workspace for ({bq} vs {bk}): {W / 2**20:.1f} MiB; "
+             f"first choice {first}, with it {capped}")
+    assert first[1] > W >= capped[1] and capped[0] in (1, 2)
+    wl = custom_kv("wsbound", "bf16", (nq,) * nseq, (nk,) * nseq, H=H, Hkv=Hkv, d=d, depth=6,
+                   seed=731)
+    inp = make_kv_inputs(wl)
+    ws = torch.empty(W, dtype=torch.uint8, device=DEV)
+    got = gpu_kv(inp, workspace=ws)
+    assert torch.equal(got, gpu_kv(inp, workspace=ws, on_path=capped[0]))
+    err = max_abs(got, oracle_kv(inp))
+    announce(f"max-abs vs oracle {err:.3e}")
+    assert err <= TOL
+
 
 @pytest.mark.parametrize("kind", ["f32", "bf16"])
 @pytest.mark.parametrize("H,Hkv,d", [(8, 2, 64), (4, 4, 32), (12, 4, 64)])

@@ -85,7 +85,9 @@ def test_noalloc_equals_workspace_path_on_two_calls():
 def test_noalloc_rejects_oversized_without_writing():
     import differential_attention_amd as da
     dev = torch.device("cuda:0")
-    nseq, nq, nk, H, Hkv, d = 4096, 4, 128, 16, 4, 64
+    # (2 query rows: the split-KV path is the only one, and its partials do
+    # not fit the scratch)
+    nseq, nq, nk, H, Hkv, d = 4096, 2, 128, 16, 4, 64
     assert da.kv_workspace_size(nseq, nq, nk, H, Hkv, d) > da.KV_SCRATCH_BYTES
     q = torch.zeros(nseq * nq, H, 2, d, dtype=torch.bfloat16, device=dev)
     k = torch.zeros(nseq * nk, Hkv, 2, d, dtype=torch.bfloat16, device=dev)
