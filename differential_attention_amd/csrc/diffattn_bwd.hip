@@ -220,6 +220,24 @@ template <int N> __device__ inline void load_f32(float (&x)[N], const float *src
         }
     }
 }
+template <int N> __device__ inline void load_f32_nt(float (&x)[N], const float *src)
+{
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    if constexpr (N % 4 == 0) {
+#pragma unroll
+        for (int k = 0; k < N / 4; ++k) {
+            const f4 v = __builtin_nontemporal_load((const f4 *)(src + 4 * k));
+            x[4 * k] = v.x, x[4 * k + 1] = v.y, x[4 * k + 2] = v.z, x[4 * k + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < N / 2; ++k) {
+            const f2 v = __builtin_nontemporal_load((const f2 *)(src + 2 * k));
+            x[2 * k] = v.x, x[2 * k + 1] = v.y;
+        }
+    }
+}
 template <int N> __device__ inline void load_bf16(float (&x)[N], const bf16 *src)
 {
     typedef __bf16 bv __attribute__((ext_vector_type(N)));
@@ -288,9 +306,10 @@ __global__ __launch_bounds__(256) void bwd_prep(BwdParams p)
         const int64_t row = (int64_t)(ok ? t : 0) * p.H + h;
         float a1[CPL], a2[CPL], dyv[CPL];
         if (ok) {
+            // (the saved maps are read once: nontemporal loads)
             const float *o1 = p.o12 + row * 2 * (2 * D) + CPL * l16;
-            load_f32(a1, o1);
-            load_f32(a2, o1 + 2 * D);
+            load_f32_nt(a1, o1);
+            load_f32_nt(a2, o1 + 2 * D);
             load_row(dyv, (const E *)p.dy + row * (2 * D) + CPL * l16);
         } else {
 #pragma unroll
