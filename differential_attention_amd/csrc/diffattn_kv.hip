@@ -44,9 +44,10 @@
 //
 // Combine kernel
 // --------------
-// One wave per output row (token, head): merges the splits' partials of
-// both maps by log-sum-exp, then applies the epilogue that the prefill
-// kernel fuses -- lambda from the four vectors, O_1/l_1 - lambda O_2/l_2,
+// One or more thread groups per output row (token, head), as many as the
+// longest row's split count asks for: merges the splits' partials of both
+// maps by log-sum-exp, then applies the epilogue that the prefill kernel
+// fuses -- lambda from the four vectors, O_1/l_1 - lambda O_2/l_2,
 // RMSNorm over 2d, the weight and the (1 - lambda_init) scale -- and stores
 // in the input dtype.  Partial outputs cannot simply be summed: the
 // combination is nonlinear in the two maps' normalisers.
@@ -56,6 +57,7 @@
 #include <algorithm>
 #include <atomic>
 #include <mutex>
+#include <type_traits>
 #include <math.h>
 #include <stdint.h>
 
@@ -389,178 +391,172 @@ void diffattn_kv_partial(KvParams p)
         *(f32x4 *)(p.ws_ml + slot * 4) = f32x4{mrun[0], l0, mrun[1], l1};
 }
 
-__device__ inline float wave_sum(float x)
-{
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-        x += __shfl_xor(x, off, 64);
-    return x;
-}
-__device__ inline float wave_max(float x)
-{
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-        x = fmaxf(x, __shfl_xor(x, off, 64));
-    return x;
-}
 
-template <int D, int kChunk>
-__global__ __launch_bounds__(kThreads)
+// Combine kernel: NG thread groups per output row.  A row's columns are
+// NCH chunks of 16 bytes per map; thread (row, j, c) owns chunk c and the
+// splits j, j + NG, j + 2 NG, ... of its row, four per round, and issues
+// their (m, l) and O loads together, then merges them by log-sum-exp.  The
+// NG groups of a row meet in LDS, where the row's first NCH threads merge
+// them, combine the two maps, normalise and store.  NG grows with the
+// longest row's split count (one round of loads per thread where it can):
+// rows with few splits pack 256 / (NCH NG) rows into a workgroup, rows with
+// many spread one row over more threads, so a small step's few rows still
+// reach their partials in one memory round trip.
+template <int D, int NG>
+__global__ __launch_bounds__(256)
 void diffattn_kv_combine(KvParams p)
 {
-    constexpr int CPL = 2 * D / 64;   // output columns per lane
-    static_assert(CPL == 1 || CPL == 2, "unsupported d");
-    const int wave = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
-    int64_t wid = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+    constexpr int W = 2 * D;          // columns of one map's row
+    constexpr int NCH = W / 4;        // 16-byte chunks per row
+    constexpr int TPR = NCH * NG;     // threads per row
+    constexpr int RW = 256 / TPR;     // rows per workgroup
+    constexpr int SW = TPR < 64 ? TPR : 64;   // lanes of one row in a wave
+    constexpr int U = 4;              // splits per thread per round
+    constexpr int LPC = D / NCH;      // lambda-vector elements per merging thread
+    static_assert(RW * TPR == 256 && NCH <= 32 && LPC >= 1 && D % NCH == 0, "chunking");
+    __shared__ f32x4 s_ml[RW][NG];
+    __shared__ f32x4 s_o[RW][2][NG][NCH];
+    const int t = threadIdx.x;
+    const int rw = t / TPR, j = (t / NCH) % NG, c = t % NCH, sl = t % SW;
+    int64_t wid = (int64_t)blockIdx.x * RW + rw;
     const int h = (int)(wid % p.H);
     wid /= p.H;
     const int i = (int)(wid % p.max_q);
-    const int s = (int)(wid / p.max_q);
-    if (s >= p.nseq)
-        return;
-    // ---- first memory round trip: everything that does not depend on the
-    // partials -- the sequence bounds, the split counts of the sequences
-    // before this one (the first 64 of them, one per lane), the lambda
-    // vectors and the weight -- is loaded before any of it is used, so the
-    // loads travel together (used one by one, each would wait out its own
-    // round trip)
-    // (unconditional loads at clamped indices: a load under a lane mask
-    // would make the compiler wait for it inside the masked block)
-    static_assert(D <= 64 && (D & (D - 1)) == 0, "one lambda-vector element per lane");
-    const int64_t lo = (int64_t)h * p.lstride + (lane & (D - 1));
-    const float lq1 = p.lq1[lo], lk1 = p.lk1[lo], lq2 = p.lq2[lo], lk2 = p.lk2[lo];
-    float wc[CPL];
+    const int s_raw = (int)(wid / p.max_q);
+    const int s = min(s_raw, p.nseq - 1);   // (clamped: loads stay in bounds)
+    // everything that does not depend on the partials, loaded before any of
+    // it is used (clamped indices, no loads under lane masks)
+    const int64_t lo = (int64_t)h * p.lstride + c * LPC;
+    float lq1[LPC], lk1[LPC], lq2[LPC], lk2[LPC];
 #pragma unroll
-    for (int cc = 0; cc < CPL; ++cc)
-        wc[cc] = p.w ? p.w[CPL * lane + cc] : 1.f;
+    for (int e = 0; e < LPC; ++e) {
+        lq1[e] = p.lq1[lo + e];
+        lk1[e] = p.lk1[lo + e];
+        lq2[e] = p.lq2[lo + e];
+        lk2[e] = p.lk2[lo + e];
+    }
+    const f32x4 wc = p.w ? *(const f32x4 *)(p.w + 4 * c) : f32x4{1.f, 1.f, 1.f, 1.f};
     int qa, qe, ka, ke;
-    int kb0 = 0, kb1 = 0;   // bounds of sequence `lane`, used if lane < s
     if (p.cuq) {
         qa = p.cuq[s];
         qe = p.cuq[s + 1];
         ka = p.cuk[s];
         ke = p.cuk[s + 1];
-        const int li = lane < s ? lane : s;
-        kb0 = p.cuk[li];
-        kb1 = p.cuk[li + 1];
     } else {
         qa = s * p.qlen_uniform;
         qe = qa + p.qlen_uniform;
         ka = s * p.klen_uniform;
         ke = ka + p.klen_uniform;
     }
-    const float d1 = lane < D ? lq1 * lk1 : 0.f;
-    const float d2 = lane < D ? lq2 * lk2 : 0.f;
-
     const int nq = qe - qa, nk = ke - ka;
-    if (i >= nq)
-        return;
+    const bool live = s_raw < p.nseq && i < nq;
     const int g = h / p.G;
     const int r = i * p.G + h % p.G;
-    // base of this sequence's splits: the sum of the split counts of the
-    // sequences before it (the first 64 already loaded)
+    // base of this sequence's splits: the split counts of the sequences
+    // before it, summed over the SW lanes of the row in this wave
     int sbase;
     if (!p.cuk) {
         sbase = s * split_count(p.klen_uniform, p.ck);
     } else {
-        int cnt = lane < s ? split_count(kb1 - kb0, p.ck) : 0;
+        int cnt = 0;
+        for (int si = sl; si < s; si += SW)
+            cnt += split_count(p.cuk[si + 1] - p.cuk[si], p.ck);
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1)
+        for (int off = SW / 2; off >= 1; off >>= 1)
             cnt += __shfl_xor(cnt, off, 64);
         sbase = cnt;
-        for (int s0 = 64; s0 < s; s0 += 64) {
-            const int si = s0 + lane;
-            int c2 = si < s ? split_count(p.cuk[si + 1] - p.cuk[si], p.ck) : 0;
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1)
-                c2 += __shfl_xor(c2, off, 64);
-            sbase += c2;
-        }
     }
     // (the clamp only matters when cu_seqlens_k breaks its preconditions:
     // no read past the workspace)
-    const int nsp = max(0, min(split_count(nk, p.ck), p.nslots - sbase));
-
-    // lambda of this head
-    const float lam = expf(wave_sum(d1)) - expf(wave_sum(d2)) + p.lambda_init;
-
-    // merge the splits of both maps (log-sum-exp in log2 units), up to
-    // kChunk splits per round: lane j loads split j's (m, l) of both maps in
-    // one 16-byte read while every lane loads its columns of all kChunk
-    // splits' O (independent loads, one memory round trip per round); the
-    // wave then reduces the maximum and the weighted sums.  kChunk (4, 8, 16
-    // or 32) covers the longest row's splits in one round where it can (32
-    // instead of 16: 3.8% on a 4097-key step); a narrower one holds fewer
-    // registers and issues fewer loads (rounds past a row's last split
-    // re-read it).
-    static_assert(kChunk <= 64, "one split's (m, l) per lane");
-    float acc[2][CPL];
-    float M[2] = {-INFINITY, -INFINITY};
-    float L[2] = {0.f, 0.f};
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int cc = 0; cc < CPL; ++cc)
-            acc[m][cc] = 0.f;
+    const int nsp = live ? max(0, min(split_count(nk, p.ck), p.nslots - sbase)) : 0;
     const int64_t slot0 = ((int64_t)sbase * p.Hkv + g) * p.rmax + r;
     const int64_t sstride = (int64_t)p.Hkv * p.rmax;   // between a row's splits
-    for (int j0 = 0; j0 < nsp; j0 += kChunk) {
-        const int nj = min(kChunk, nsp - j0);
-        f32x4 ml = f32x4{-INFINITY, 0.f, -INFINITY, 0.f};
-        if (lane < nj)
-            ml = *(const f32x4 *)(p.ws_ml + (slot0 + (int64_t)(j0 + lane) * sstride) * 4);
-        // past the last split the round re-reads the last one (weight 0)
-        float ob[kChunk][2][CPL];
+
+    // this thread's splits, U per round, merged online per map
+    float M[2] = {-INFINITY, -INFINITY}, L[2] = {0.f, 0.f};
+    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    for (int j0 = j; j0 < nsp; j0 += U * NG) {
+        f32x4 ml[U], ob[U][2];
 #pragma unroll
-        for (int u = 0; u < kChunk; ++u) {
-            const int jc = j0 + min(u, nj - 1);
-            const float *op = p.ws_o + (slot0 + (int64_t)jc * sstride) * 2 * (2 * D) + CPL * lane;
-#pragma unroll
-            for (int m = 0; m < 2; ++m)
-#pragma unroll
-                for (int cc = 0; cc < CPL; ++cc)
-                    ob[u][m][cc] = op[m * 2 * D + cc];
+        for (int u = 0; u < U; ++u) {
+            // past the row's last split: re-read split j0 (weight 0 below)
+            const int js = j0 + u * NG < nsp ? j0 + u * NG : j0;
+            const int64_t slot = slot0 + (int64_t)js * sstride;
+            ml[u] = *(const f32x4 *)(p.ws_ml + slot * 4);
+            const float *op = p.ws_o + slot * 2 * W + 4 * c;
+            ob[u][0] = *(const f32x4 *)op;
+            ob[u][1] = *(const f32x4 *)(op + W);
         }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool in = j0 + u * NG < nsp;
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const float mj = in ? ml[u][2 * m] : -INFINITY;
+                const float mn = fmaxf(M[m], mj);
+                // (0 for what is not there yet, and for splits no key of
+                // the row reached)
+                const float fa = M[m] == -INFINITY ? 0.f : exp2f(M[m] - mn);
+                const float wj = mj == -INFINITY ? 0.f : exp2f(mj - mn);
+                L[m] = L[m] * fa + ml[u][2 * m + 1] * wj;
+                acc[m] = acc[m] * fa + ob[u][m] * wj;
+                M[m] = mn;
+            }
+        }
+    }
+    if (c == 0)
+        s_ml[rw][j] = f32x4{M[0], L[0], M[1], L[1]};
+    s_o[rw][0][j][c] = acc[0];
+    s_o[rw][1][j][c] = acc[1];
+    __syncthreads();
+    if (j != 0 || !live)
+        return;
+
+    // the row's first NCH threads: merge the groups, lambda, combine the
+    // maps, RMSNorm over 2d, weight, (1 - lambda_init), store
+    float Mg[2] = {-INFINITY, -INFINITY};
+#pragma unroll
+    for (int q = 0; q < NG; ++q) {
+        const f32x4 mlq = s_ml[rw][q];
+        Mg[0] = fmaxf(Mg[0], mlq[0]);
+        Mg[1] = fmaxf(Mg[1], mlq[2]);
+    }
+    float Lg[2] = {0.f, 0.f};
+    f32x4 og[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int q = 0; q < NG; ++q) {
+        const f32x4 mlq = s_ml[rw][q];
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-            const float mj = ml[2 * m];
-            const float mn = fmaxf(M[m], wave_max(mj));
-            // rescale what earlier rounds accumulated (0 before any)
-            const float fa = M[m] == -INFINITY ? 0.f : exp2f(M[m] - mn);
-            const float wgt = mj == -INFINITY ? 0.f : exp2f(mj - mn);
-            L[m] = L[m] * fa + wave_sum(ml[2 * m + 1] * wgt);
-#pragma unroll
-            for (int cc = 0; cc < CPL; ++cc)
-                acc[m][cc] *= fa;
-#pragma unroll
-            for (int u = 0; u < kChunk; ++u) {
-                const float wj = u < nj ? __int_as_float(__builtin_amdgcn_readlane(
-                                              __float_as_int(wgt), u))
-                                        : 0.f;
-#pragma unroll
-                for (int cc = 0; cc < CPL; ++cc)
-                    acc[m][cc] += wj * ob[u][m][cc];
-            }
-            M[m] = mn;
+            const float wq = mlq[2 * m] == -INFINITY ? 0.f : exp2f(mlq[2 * m] - Mg[m]);
+            Lg[m] += mlq[2 * m + 1] * wq;
+            og[m] += s_o[rw][m][q][c] * wq;
         }
     }
-
-    // epilogue: combine the maps, RMSNorm over 2d, weight, scale, store
-    float pre[CPL];
-    float ss = 0.f;
-    const float i1 = 1.f / L[0], i2 = lam / L[1];
+    float d1 = 0.f, d2 = 0.f;
 #pragma unroll
-    for (int cc = 0; cc < CPL; ++cc) {
-        pre[cc] = acc[0][cc] * i1 - acc[1][cc] * i2;
-        ss += pre[cc] * pre[cc];
+    for (int e = 0; e < LPC; ++e) {
+        d1 += lq1[e] * lk1[e];
+        d2 += lq2[e] * lk2[e];
     }
-    ss = wave_sum(ss);
-    const float scale = rsqrtf(ss / (float)(2 * D) + p.eps) * (1.f - p.lambda_init);
-    bf16 *dst = (bf16 *)p.out + ((int64_t)(qa + i) * p.H + h) * (2 * D) + CPL * lane;
 #pragma unroll
-    for (int cc = 0; cc < CPL; ++cc)
-        dst[cc] = (bf16)(pre[cc] * scale * wc[cc]);
+    for (int off = NCH / 2; off >= 1; off >>= 1) {
+        d1 += __shfl_xor(d1, off, 64);
+        d2 += __shfl_xor(d2, off, 64);
+    }
+    const float lam = expf(d1) - expf(d2) + p.lambda_init;
+    const float i1 = 1.f / Lg[0], i2 = lam / Lg[1];
+    const f32x4 pre = og[0] * i1 - og[1] * i2;
+    float ss = (pre[0] * pre[0] + pre[1] * pre[1]) + (pre[2] * pre[2] + pre[3] * pre[3]);
+#pragma unroll
+    for (int off = NCH / 2; off >= 1; off >>= 1)
+        ss += __shfl_xor(ss, off, 64);
+    const float scale = rsqrtf(ss / (float)W + p.eps) * (1.f - p.lambda_init);
+    bf16x4 o4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        o4[e] = (bf16)(pre[e] * scale * wc[e]);
+    *(bf16x4 *)((bf16 *)p.out + ((int64_t)(qa + i) * p.H + h) * W + 4 * c) = o4;
 }
 
 // Split policy: keys per split ck chosen from the total number of cache
@@ -766,16 +762,23 @@ void launch_partial(int rt, unsigned blocks, hipStream_t st, const KvParams &p)
 // row's width, where fewer would take two; narrower rounds hold fewer
 // registers and issue fewer loads).
 template <int D>
-void launch_combine(int64_t splits, unsigned blocks, hipStream_t st, const KvParams &p)
+void launch_combine(int64_t splits, int64_t rows, hipStream_t st, const KvParams &p)
 {
+    constexpr int NCH = D / 2;   // 16-byte chunks of a 2d-wide fp32 row
+    auto go = [&](auto ng) {
+        constexpr int NG = decltype(ng)::value;
+        const int64_t rw = 256 / (NCH * NG);
+        hipLaunchKernelGGL((diffattn_kv_combine<D, NG>), dim3((unsigned)((rows + rw - 1) / rw)),
+                           dim3(256), 0, st, p);
+    };
     if (splits <= 4)
-        hipLaunchKernelGGL((diffattn_kv_combine<D, 4>), dim3(blocks), dim3(kThreads), 0, st, p);
+        go(std::integral_constant<int, 1>{});
     else if (splits <= 8)
-        hipLaunchKernelGGL((diffattn_kv_combine<D, 8>), dim3(blocks), dim3(kThreads), 0, st, p);
+        go(std::integral_constant<int, 2>{});
     else if (splits <= 16)
-        hipLaunchKernelGGL((diffattn_kv_combine<D, 16>), dim3(blocks), dim3(kThreads), 0, st, p);
+        go(std::integral_constant<int, 4>{});
     else
-        hipLaunchKernelGGL((diffattn_kv_combine<D, 32>), dim3(blocks), dim3(kThreads), 0, st, p);
+        go(std::integral_constant<int, 8>{});
 }
 
 // Validates the arguments, makes the split plan and launches both kernels
@@ -864,19 +867,18 @@ int kv_impl(int dtype, const void *q, const void *k, const void *v,
     p.klen_uniform = cu_seqlens_q ? 0 : Tk / nseq;
     p.max_q = max_seqlen_q;
     hipStream_t st = (hipStream_t)stream;
-    const int64_t waves2 = (int64_t)nseq * max_seqlen_q * H;   // combine: one wave per row
-    const int64_t blocks2 = (waves2 + kWavesPerBlock - 1) / kWavesPerBlock;
-    if (blocks2 > 0x7fffffff)
+    const int64_t rows2 = (int64_t)nseq * max_seqlen_q * H;   // output rows of the combine
+    if (rows2 > 0x7fffffff)
         return DIFFATTN_EINVAL;
-    // merge the splits of every row: up to 32 per round when a row can have
-    // more than 16 (splits of ck keys of the longest cache)
+    // merge the splits of every row (at most those of ck keys of the
+    // longest cache)
     auto combine = [&](int ck) {
         const int64_t kmax = cu_seqlens_q ? max_seqlen_k : Tk / nseq;
         const int64_t splits = (kmax + ck - 1) / ck;
         if (d == 64)
-            launch_combine<64>(splits, (unsigned)blocks2, st, p);
+            launch_combine<64>(splits, rows2, st, p);
         else
-            launch_combine<32>(splits, (unsigned)blocks2, st, p);
+            launch_combine<32>(splits, rows2, st, p);
     };
 
     // long query chunks: the prefill kernel, on whole key ranges (no

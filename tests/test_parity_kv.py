@@ -196,14 +196,16 @@ def test_one_split_per_sequence():
     assert err <= TOL
 
 
-def test_long_cache_many_splits():
+@pytest.mark.parametrize("d", [64, 32])
+def test_long_cache_many_splits(d):
     """One long sequence with several new queries: many key splits per row
-    block, and the causal limit inside the last split."""
-    wl = custom_kv("long", "bf16", (7,), (20000,), H=16, Hkv=4, d=64, depth=3,
+    block (over a hundred: the combine kernel's widest grouping, several
+    rounds per thread), and the causal limit inside the last split."""
+    wl = custom_kv("long", "bf16", (7,), (20000,), H=16, Hkv=4, d=d, depth=3,
                    seed=7)
     inp = make_kv_inputs(wl)
     err = max_abs(gpu_kv(inp), oracle_kv(inp))
-    announce(f"long cache: max-abs {err:.3e}")
+    announce(f"long cache d={d}: max-abs {err:.3e}")
     assert err <= TOL
 
 
