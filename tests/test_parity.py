@@ -13,7 +13,7 @@ import torch
 import oracle
 import workloads
 from conditioning import rows_within_bar
-from launch_shape import prefill_sub_blocks
+from launch_shape import compact_list, prefill_sub_blocks
 from workloads import WORKLOADS, custom, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -173,7 +173,8 @@ RAGGED_MANY = RAGGED * 11
 @pytest.mark.parametrize("H,Hkv", [(4, 4), (16, 4), (6, 2)])
 @pytest.mark.parametrize("causal", [True, False])
 def test_ragged_varlen_64_query_slots(dtype, d, H, Hkv, causal):
-    assert prefill_sub_blocks(H, Hkv, len(RAGGED_MANY), max(RAGGED_MANY)) == 2
+    assert prefill_sub_blocks(H, Hkv, len(RAGGED_MANY), max(RAGGED_MANY),
+                              sum(RAGGED_MANY)) == 2
     wl = custom("ragged_many", dtype, RAGGED_MANY, H, Hkv, d, depth=7, causal=causal,
                 seed=H * 100 + d + 1)
     announce(f"ragged x11 {dtype} d={d} H={H} Hkv={Hkv} causal={causal}")
@@ -184,10 +185,30 @@ def test_ragged_varlen_64_query_slots(dtype, d, H, Hkv, causal):
     assert err <= TOL[dtype], f"max-abs {err:.3e}"
 
 
+# Sequences long and short, a few empty: the compact tile list over more
+# than 64 query-tile levels (its level search runs over several 64-lane
+# chunks), on both instantiations.
+COMPACT = (6000, 1, 100, 0, 3000, 70, 2049, 64, 0, 65)
+
+
+@pytest.mark.parametrize("H,Hkv,sub", [(16, 4, 2), (4, 1, 1)])
+def test_compact_tile_list(H, Hkv, sub):
+    T = sum(COMPACT)
+    assert compact_list(H, Hkv, len(COMPACT), max(COMPACT), T)
+    assert prefill_sub_blocks(H, Hkv, len(COMPACT), max(COMPACT), T) == sub
+    wl = custom("compact", "bf16", COMPACT, H, Hkv, 64, depth=6, causal=True,
+                seed=H + 300)
+    announce(f"compact tile list H={H} Hkv={Hkv}: every row")
+    inp = make_inputs(wl)
+    err, relaxed = rows_within_bar(gpu_run(inp), oracle_full(inp), TOL["bf16"], True, inp,
+                                   announce)
+    announce(f"compact tile list H={H}: max-abs {err:.3e}, {relaxed} rows on the wider bar")
+
+
 def test_ragged_shapes_take_32_query_slots():
     """The ragged matrix above runs on the other instantiation."""
     for H, Hkv in [(2, 2), (4, 2), (8, 2), (16, 2), (3, 1), (10, 5), (8, 8)]:
-        assert prefill_sub_blocks(H, Hkv, len(RAGGED), max(RAGGED)) == 1
+        assert prefill_sub_blocks(H, Hkv, len(RAGGED), max(RAGGED), sum(RAGGED)) == 1
 
 
 def test_fp32_path_at_d64_gqa4():

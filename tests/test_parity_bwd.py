@@ -150,7 +150,7 @@ def test_bwd_ragged_64_query_slots(dtype, d):
     """Many short sequences: the training forward on its 64-query
     instantiation, then the backward."""
     lens = RAGGED * 11
-    assert prefill_sub_blocks(16, 4, len(lens), max(lens)) == 2
+    assert prefill_sub_blocks(16, 4, len(lens), max(lens), sum(lens)) == 2
     wl = custom("bwd_many", dtype, lens, 16, 4, d, depth=4, causal=True, seed=d + 90)
     inp = make_inputs(wl)
     inp.w = torch.linspace(0.5, 1.5, 2 * d)

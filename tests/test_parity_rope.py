@@ -96,7 +96,7 @@ def test_bf16_tables(dtype, d, lens):
 def test_ragged_varlen_rope_64_query_slots(dtype, d, causal):
     """Many short sequences: the 64-query instantiation with the rotation."""
     lens = RAGGED * 11
-    assert prefill_sub_blocks(16, 4, len(lens), max(lens)) == 2
+    assert prefill_sub_blocks(16, 4, len(lens), max(lens), sum(lens)) == 2
     wl = custom("ragged_rope_many", dtype, lens, 16, 4, d, depth=9, causal=causal,
                 seed=d + 70)
     inp = make_inputs(wl)
