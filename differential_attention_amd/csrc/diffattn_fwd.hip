@@ -67,7 +67,9 @@
 // Causal tiles above the diagonal are never visited; on the diagonal,
 // 32-key blocks a wave cannot see are skipped and the rest are masked by
 // index.  Workgroups are numbered longest-first (largest query tile index
-// first) so the causal tail is short.
+// first) so the causal tail is short; for packed sequences of mixed
+// lengths the grid lists only the tiles that exist, in that order, each
+// workgroup finding its tile from cu_seqlens in its prologue.
 
 #include <hip/hip_runtime.h>
 
@@ -1092,7 +1094,8 @@ int launch_chunk(const Params &p, int nblocks, hipStream_t stream)
 // the padded grid's ntile_q * nseq tiles: the list costs each workgroup a
 // few dozen instructions more in its prologue (1% on eight 4096-token
 // sequences, whose padded grid has no empty tile), and saves the empty
-// workgroups of a length mix (3.4% on 30 sequences of 128 to 4096 tokens).
+// workgroups of a length mix (about 3% on 30 sequences of 128 to 4096
+// tokens).
 void grid_of(int max_seqlen, int nseq, int H, int Hkv, int sub, int &hpw, int64_t &ntile_q,
              int64_t &nblocks, int64_t T = -1, bool *compact = nullptr)
 {
