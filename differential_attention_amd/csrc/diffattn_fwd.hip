@@ -1000,9 +1000,13 @@ void diffattn_fwd_kernel(Params p)
                 const char *a = stg + row * PITCH + cc;
                 const uint2 lo = *(const uint2 *)a, hi = *(const uint2 *)(a + 8);
                 const int tq = qbase + row;
+                // (nontemporal: the output is not read again here, and
+                // keeping it out of L2 leaves room for the K/V tiles that
+                // other workgroups re-read; 0.9% on 8 x 4096 tokens)
                 if (tq < s1)
-                    *(u32x4 *)((char *)p.out + ((int64_t)tq * p.H + head) * ROW + cc) =
-                        u32x4{lo.x, lo.y, hi.x, hi.y};
+                    __builtin_nontemporal_store(
+                        u32x4{lo.x, lo.y, hi.x, hi.y},
+                        (u32x4 *)((char *)p.out + ((int64_t)tq * p.H + head) * ROW + cc));
             }
         } else {
             const int tq = qbase + n;
