@@ -69,7 +69,10 @@ def _build_flags() -> bytes:
     mod = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(mod)
     # (without the include path, which depends on where the tree is)
-    return " ".join(f for f in mod.HIPCC_FLAGS if not os.path.isabs(f)).encode()
+    flags = " ".join(f for f in mod.HIPCC_FLAGS if not os.path.isabs(f))
+    for src, extra in sorted(getattr(mod, "FILE_FLAGS", {}).items()):
+        flags += f" [{src}: {' '.join(extra)}]"
+    return flags.encode()
 
 
 def kernel_digest(sources=KERNEL_SOURCES) -> str:
